@@ -1,0 +1,406 @@
+// CPU oracle for the per-layer sparse decode offload step.
+//
+// TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+// benchmark's CPU-baseline leg may load this library.  It shares no code,
+// header, table or constant with the HIP path under sparse_kv_offload_amd/.
+//
+// It is a plain, slow, single-threaded brute force of what the step computes,
+// following the order of the decode-step list in "Layerwise and Sparse KV
+// Cache Offloading Design" (vLLM-Ascend design doc), section 4 "Sparse Decode
+// Offload", subsection "Decode step", together with the hot-shelf mechanics
+// described in the FlashOffloading explainer on learnaivisually.com
+// ("FlashOffloading offloads all KV cache ..."), decode paragraphs: tokens on
+// the shelf are hits, misses replace evicted tokens so the shelf size never
+// changes, MTP position lists are merged and deduplicated before loading, a
+// reverse index (cache_slots, -1 when absent) answers hit-or-miss, and each
+// top-k candidate carries its token index and residency in one int32.
+//
+// Where the pages leave a step open, the oracle takes one plain reading:
+//   * score: single 64-d dot product q . k, accumulated in binary32 with
+//     fused multiply-add in index order j = 0..63 starting from +0 (exact
+//     bf16 products, one rounding per term); a zero result is stored as +0;
+//   * candidates: every token present after this step's append;
+//   * top-k order: larger score first, equal scores -> smaller token index;
+//     min(k, L_t) winners;
+//   * packed value: bit 31 set <=> cache_slots[token] == -1 at step start,
+//     bits 0..30 = token index;
+//   * merged list U ascending by token index; misses M ascending;
+//   * LRU: per (layer, seq) table stamped with the layer's step counter t;
+//     hits are stamped t first; victims are the slots not stamped t, taken in
+//     ascending (last_use, slot) order; the r-th miss takes the r-th victim;
+//     an eviction is a victim whose previous owner is a token (>= 0);
+//   * attention: K = all 576 columns of a main-KV row, V = its first 512
+//     (latent) columns, softmax(scale * q.K) over the selected rows, in
+//     float64 from the bf16 values.
+//
+// Parity status: every function below is pinned by tests/test_oracle_pins.py
+// (closed forms, brute force, a hand-simulated LRU trace and invariants);
+// the per-step statistics (hit rate, miss count) have no printed values on
+// the pages and are pinned only by the invariants.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <utility>
+#include <vector>
+
+namespace {
+
+constexpr int IDX_DIM = 64;
+constexpr int KV_DIM = 576;
+constexpr int V_DIM = 512;
+
+// Planted-mistake switch.  Zero in every real use; the pin tests set it to
+// show that each pin rejects a plausible slip in this file.
+int g_mutation = 0;
+enum Mutation {
+    MUT_NONE = 0,
+    MUT_SCORE_DROP_LAST_TERM = 1,
+    MUT_TIE_LARGER_INDEX = 2,
+    MUT_NO_DEDUPE = 3,
+    MUT_VICTIM_SLOT_DESC = 4,
+    MUT_VICTIM_IGNORE_STAMP = 5,
+    MUT_SCALE_512 = 6,
+    MUT_V_WRONG_SLICE = 7,
+    MUT_HITS_NOT_STAMPED = 8,
+    MUT_EVICT_KEEPS_OLD = 9,
+    MUT_FLAG_INVERTED = 10,
+    MUT_SCORE_SWAP_OPERAND = 11,
+};
+
+inline float bf16_to_f32(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+inline uint32_t f32_bits(float f) {
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return u;
+}
+
+// Monotone map from binary32 (finite, non-NaN) to uint32: a < b <=> ord(a) < ord(b).
+inline uint32_t ordered_key(float s) {
+    uint32_t u = f32_bits(s);
+    return (u & 0x80000000u) ? ~u : (u ^ 0x80000000u);
+}
+
+struct Chain {
+    int64_t ntok = 0;
+    std::vector<uint16_t> kidx;      // [cap][64]  device indexer cache contents
+    std::vector<uint16_t> pool;      // [cap][576] host main-KV pool
+    std::vector<int32_t> cache_slots;  // [cap] token -> hot slot, -1 when absent
+    std::vector<int32_t> slot_token;   // [S] hot slot -> token, -1 when empty
+    std::vector<int32_t> last_use;     // [S] step stamp, -1 = never used
+    std::vector<uint16_t> hot;       // [S][576] hot buffer contents
+};
+
+struct Oracle {
+    int L, B, k, S, D, H;
+    int64_t cap;
+    float scale;
+    std::vector<Chain> chains;       // [L][B]
+    std::vector<int64_t> layer_step; // t per layer
+    Chain& at(int l, int b) { return chains[(size_t)l * B + b]; }
+};
+
+// ---- step 3 of the decode-step list: the indexer scores every token --------
+// s_i = sum_j q_j * K_i[j], binary32 FMA chain in index order from +0.
+float indexer_score(const uint16_t* q, const uint16_t* krow) {
+    float acc = 0.0f;
+    int n = (g_mutation == MUT_SCORE_DROP_LAST_TERM) ? IDX_DIM - 1 : IDX_DIM;
+    for (int j = 0; j < n; ++j) {
+        float a = bf16_to_f32(q[j]);
+        float b = bf16_to_f32(krow[(g_mutation == MUT_SCORE_SWAP_OPERAND) ? (IDX_DIM - 1 - j) : j]);
+        acc = std::fma(a, b, acc);
+    }
+    if (acc == 0.0f) acc = 0.0f;  // store a zero as +0
+    return acc;
+}
+
+// Top-k over (score desc, index asc); returns min(k, n) token indices.
+std::vector<int32_t> topk_indices(const std::vector<float>& s, int k) {
+    std::vector<int32_t> idx(s.size());
+    for (size_t i = 0; i < s.size(); ++i) idx[i] = (int32_t)i;
+    auto better = [&](int32_t a, int32_t b) {
+        uint32_t ka = ordered_key(s[a]), kb = ordered_key(s[b]);
+        if (ka != kb) return ka > kb;
+        return (g_mutation == MUT_TIE_LARGER_INDEX) ? a > b : a < b;
+    };
+    std::sort(idx.begin(), idx.end(), better);
+    idx.resize(std::min<size_t>((size_t)k, idx.size()));
+    return idx;
+}
+
+// Packed int32 candidate: token index with the residency read from cache_slots.
+inline int32_t pack_candidate(int32_t token, const std::vector<int32_t>& cache_slots) {
+    bool miss = cache_slots[token] == -1;
+    if (g_mutation == MUT_FLAG_INVERTED) miss = !miss;
+    return (int32_t)((uint32_t)token | (miss ? 0x80000000u : 0u));
+}
+
+// Step 7: softmax attention over the selected rows (fp64).
+void sparse_attention(const Oracle& o, const uint16_t* qa /*[H][576]*/,
+                      const std::vector<const uint16_t*>& rows, double* out /*[H][512]*/) {
+    const int n = (int)rows.size();
+    double scale = (g_mutation == MUT_SCALE_512) ? 1.0 / std::sqrt(512.0) : (double)o.scale;
+    int voff = (g_mutation == MUT_V_WRONG_SLICE) ? KV_DIM - V_DIM : 0;
+    std::vector<double> z(n), w(n);
+    for (int h = 0; h < o.H; ++h) {
+        const uint16_t* q = qa + (size_t)h * KV_DIM;
+        double* oh = out + (size_t)h * V_DIM;
+        for (int c = 0; c < V_DIM; ++c) oh[c] = 0.0;
+        if (n == 0) continue;
+        double m = -INFINITY;
+        for (int j = 0; j < n; ++j) {
+            double acc = 0.0;
+            for (int c = 0; c < KV_DIM; ++c) acc += (double)bf16_to_f32(q[c]) * (double)bf16_to_f32(rows[j][c]);
+            z[j] = scale * acc;
+            m = std::max(m, z[j]);
+        }
+        double l = 0.0;
+        for (int j = 0; j < n; ++j) { w[j] = std::exp(z[j] - m); l += w[j]; }
+        for (int j = 0; j < n; ++j) {
+            double p = w[j] / l;
+            for (int c = 0; c < V_DIM; ++c) oh[c] += p * (double)bf16_to_f32(rows[j][voff + c]);
+        }
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+void oracle_set_mutation(int m) { g_mutation = m; }
+
+void* oracle_create(int L, int B, int64_t cap, int k, int S, int D, int H, float scale) {
+    if (L < 1 || B < 1 || cap < 1 || k < 1 || D < 1 || H < 1 || S < (int64_t)D * k) return nullptr;
+    Oracle* o = new Oracle();
+    o->L = L; o->B = B; o->cap = cap; o->k = k; o->S = S; o->D = D; o->H = H; o->scale = scale;
+    o->chains.resize((size_t)L * B);
+    for (auto& c : o->chains) {
+        c.kidx.assign((size_t)cap * IDX_DIM, 0);
+        c.pool.assign((size_t)cap * KV_DIM, 0);
+        c.cache_slots.assign((size_t)cap, -1);
+        c.slot_token.assign((size_t)S, -1);
+        c.last_use.assign((size_t)S, -1);
+        c.hot.assign((size_t)S * KV_DIM, 0);
+    }
+    o->layer_step.assign((size_t)L, 0);
+    return o;
+}
+
+void oracle_destroy(void* h) { delete static_cast<Oracle*>(h); }
+
+// Steps 1-2: the new token's rows go to their logical slots: the main-KV row
+// to the host pool, the indexer row to the indexer cache.
+int oracle_append(void* h, int layer, int seq, const uint16_t* idx_rows, const uint16_t* kv_rows, int64_t n) {
+    Oracle* o = static_cast<Oracle*>(h);
+    if (layer < 0 || layer >= o->L || seq < 0 || seq >= o->B || n < 0) return -1;
+    Chain& c = o->at(layer, seq);
+    if (c.ntok + n > o->cap) return -4;
+    std::memcpy(&c.kidx[(size_t)c.ntok * IDX_DIM], idx_rows, (size_t)n * IDX_DIM * 2);
+    std::memcpy(&c.pool[(size_t)c.ntok * KV_DIM], kv_rows, (size_t)n * KV_DIM * 2);
+    c.ntok += n;
+    return 0;
+}
+
+// One decode step of one layer for all sequences.
+//   q_idx  [B][D][64]     bf16 indexer queries
+//   q_attn [B][D][H][576] bf16 attention queries
+int oracle_decode_step(void* h, int layer, const uint16_t* q_idx, const uint16_t* q_attn,
+                       int32_t* topk, int32_t* phys, uint32_t* keys, int32_t* counts,
+                       int32_t* misses, int32_t* victims, int32_t* evict_old,
+                       double* out, double* out_pool) {
+    Oracle* o = static_cast<Oracle*>(h);
+    if (layer < 0 || layer >= o->L) return -1;
+    const int B = o->B, D = o->D, k = o->k, S = o->S, H = o->H;
+    const int32_t t = (int32_t)o->layer_step[layer];
+    for (int b = 0; b < B; ++b) {
+        Chain& c = o->at(layer, b);
+        const int64_t Lt = c.ntok;
+        const int kk = (int)std::min<int64_t>(k, Lt);
+
+        // Step 3: score all tokens and select the top-k per position.  The
+        // residency of every winner is packed in with it, read from the
+        // reverse index as it stands before this step's LRU update.
+        std::vector<std::vector<int32_t>> W(D);
+        for (int p = 0; p < D; ++p) {
+            const uint16_t* q = q_idx + ((size_t)b * D + p) * IDX_DIM;
+            std::vector<float> s((size_t)Lt);
+            for (int64_t i = 0; i < Lt; ++i) s[i] = indexer_score(q, &c.kidx[(size_t)i * IDX_DIM]);
+            if (keys)
+                for (int64_t i = 0; i < Lt; ++i) keys[((size_t)b * D + p) * o->cap + i] = ordered_key(s[i]);
+            std::vector<int32_t> sel = topk_indices(s, k);
+            for (int32_t tok : sel) W[p].push_back(pack_candidate(tok, c.cache_slots));
+            if (topk) {
+                int32_t* dst = topk + ((size_t)b * D + p) * k;
+                for (int j = 0; j < k; ++j) dst[j] = j < kk ? W[p][j] : 0;
+            }
+        }
+
+        // Merge the D position lists and deduplicate: U ascending; split by
+        // the packed flag into hits H and misses M (both ascending).
+        std::vector<int32_t> U;
+        for (int p = 0; p < D; ++p)
+            for (int32_t v : W[p]) U.push_back(v);
+        std::sort(U.begin(), U.end(), [](int32_t a, int32_t x) {
+            return (a & 0x7FFFFFFF) < (x & 0x7FFFFFFF);
+        });
+        if (g_mutation != MUT_NO_DEDUPE)
+            U.erase(std::unique(U.begin(), U.end(), [](int32_t a, int32_t x) {
+                        return (a & 0x7FFFFFFF) == (x & 0x7FFFFFFF);
+                    }), U.end());
+        std::vector<int32_t> Hs, Ms;
+        for (int32_t v : U) {
+            int32_t tok = v & 0x7FFFFFFF;
+            if (v < 0) Ms.push_back(tok); else Hs.push_back(tok);
+        }
+
+        // Step 4: LRU residency update.  Hits keep their slot and are stamped
+        // with t; the misses take the least recently used other slots.
+        if (g_mutation != MUT_HITS_NOT_STAMPED)
+            for (int32_t tok : Hs) c.last_use[c.cache_slots[tok]] = t;
+        std::vector<std::pair<int32_t, int32_t>> order;  // (last_use, slot)
+        for (int s = 0; s < S; ++s)
+            if (c.last_use[s] < t) order.push_back({c.last_use[s], s});
+        if (g_mutation == MUT_VICTIM_SLOT_DESC)
+            std::sort(order.begin(), order.end(), [](auto a, auto x) {
+                return a.first != x.first ? a.first < x.first : a.second > x.second;
+            });
+        else if (g_mutation == MUT_VICTIM_IGNORE_STAMP)
+            std::sort(order.begin(), order.end(), [](auto a, auto x) { return a.second < x.second; });
+        else
+            std::sort(order.begin(), order.end());
+        int nEv = 0;
+        const int nM = (int)Ms.size();
+        if ((size_t)nM > order.size()) return -5;  // cannot happen when S >= D*k
+        for (int r = 0; r < nM; ++r) {
+            int32_t v = order[r].second, m = Ms[r], old = c.slot_token[v];
+            if (old >= 0) {
+                if (g_mutation != MUT_EVICT_KEEPS_OLD) c.cache_slots[old] = -1;
+                ++nEv;
+            }
+            c.cache_slots[m] = v;
+            c.slot_token[v] = m;
+            c.last_use[v] = t;
+            // Step 5: copy only the missed row, host pool -> hot buffer.
+            std::memcpy(&c.hot[(size_t)v * KV_DIM], &c.pool[(size_t)m * KV_DIM], KV_DIM * 2);
+            if (misses) misses[(size_t)b * D * k + r] = m;
+            if (victims) victims[(size_t)b * D * k + r] = v;
+            if (evict_old) evict_old[(size_t)b * D * k + r] = old;
+        }
+        if (counts) {
+            int32_t* cn = counts + (size_t)b * 8;
+            cn[0] = (int32_t)U.size(); cn[1] = (int32_t)Hs.size(); cn[2] = nM; cn[3] = nEv;
+            cn[4] = kk; cn[5] = (int32_t)Lt; cn[6] = t; cn[7] = 0;
+        }
+
+        // Step 6: remap each position's logical winners to physical slots;
+        // step 7: attention over those hot-buffer rows.  The same attention
+        // over the pool rows is computed alongside: offload moves data, it
+        // must not change the result.
+        for (int p = 0; p < D; ++p) {
+            std::vector<const uint16_t*> hot_rows, pool_rows;
+            for (int j = 0; j < kk; ++j) {
+                int32_t tok = W[p][j] & 0x7FFFFFFF;
+                int32_t slot = c.cache_slots[tok];
+                if (phys) phys[((size_t)b * D + p) * k + j] = slot;
+                if (slot < 0) return -6;  // a winner must be resident after the update
+                hot_rows.push_back(&c.hot[(size_t)slot * KV_DIM]);
+                pool_rows.push_back(&c.pool[(size_t)tok * KV_DIM]);
+            }
+            const uint16_t* qa = q_attn + ((size_t)b * D + p) * H * KV_DIM;
+            if (out) sparse_attention(*o, qa, hot_rows, out + ((size_t)b * D + p) * H * V_DIM);
+            if (out_pool) sparse_attention(*o, qa, pool_rows, out_pool + ((size_t)b * D + p) * H * V_DIM);
+        }
+    }
+    o->layer_step[layer] += 1;
+    return 0;
+}
+
+// Table readers (copies of one (layer, seq) chain's state).
+int oracle_read_state(void* h, int layer, int seq, int32_t* cache_slots, int32_t* slot_token,
+                      int32_t* last_use, uint16_t* hot, int64_t* ntok) {
+    Oracle* o = static_cast<Oracle*>(h);
+    if (layer < 0 || layer >= o->L || seq < 0 || seq >= o->B) return -1;
+    Chain& c = o->at(layer, seq);
+    if (cache_slots) std::memcpy(cache_slots, c.cache_slots.data(), c.cache_slots.size() * 4);
+    if (slot_token) std::memcpy(slot_token, c.slot_token.data(), c.slot_token.size() * 4);
+    if (last_use) std::memcpy(last_use, c.last_use.data(), c.last_use.size() * 4);
+    if (hot) std::memcpy(hot, c.hot.data(), c.hot.size() * 2);
+    if (ntok) *ntok = c.ntok;
+    return 0;
+}
+
+// Direct access to one function at a time, for the pin tests.
+float oracle_score_one(const uint16_t* q, const uint16_t* krow) { return indexer_score(q, krow); }
+
+uint32_t oracle_ordered_key(float s) { return ordered_key(s); }
+
+// Top-k of n given scores; writes min(k, n) indices.
+int oracle_topk(const float* s, int64_t n, int k, int32_t* out_idx) {
+    std::vector<float> v(s, s + n);
+    std::vector<int32_t> sel = topk_indices(v, k);
+    for (size_t i = 0; i < sel.size(); ++i) out_idx[i] = sel[i];
+    return (int)sel.size();
+}
+
+// LRU unit driven by scripted selections.  State arrays are caller-owned.
+//   sel: n packed winners (already carrying flags is not required: the
+//   flags are recomputed from cache_slots here), returns nM and fills the
+//   miss / victim / old-owner lists.
+int oracle_lru_apply(int32_t* cache_slots, int64_t cap, int32_t* slot_token, int32_t* last_use,
+                     int S, int32_t t, const int32_t* sel, int n,
+                     int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* n_hits) {
+    std::vector<int32_t> cs(cache_slots, cache_slots + cap);
+    std::vector<int32_t> U;
+    for (int i = 0; i < n; ++i) U.push_back(pack_candidate(sel[i] & 0x7FFFFFFF, cs));
+    std::sort(U.begin(), U.end(), [](int32_t a, int32_t x) { return (a & 0x7FFFFFFF) < (x & 0x7FFFFFFF); });
+    if (g_mutation != MUT_NO_DEDUPE)
+        U.erase(std::unique(U.begin(), U.end(), [](int32_t a, int32_t x) {
+                    return (a & 0x7FFFFFFF) == (x & 0x7FFFFFFF);
+                }), U.end());
+    std::vector<int32_t> Hs, Ms;
+    for (int32_t v : U) (v < 0 ? Ms : Hs).push_back(v & 0x7FFFFFFF);
+    if (g_mutation != MUT_HITS_NOT_STAMPED)
+        for (int32_t tok : Hs) last_use[cache_slots[tok]] = t;
+    std::vector<std::pair<int32_t, int32_t>> order;
+    for (int s = 0; s < S; ++s)
+        if (last_use[s] < t) order.push_back({last_use[s], s});
+    if (g_mutation == MUT_VICTIM_SLOT_DESC)
+        std::sort(order.begin(), order.end(), [](auto a, auto x) {
+            return a.first != x.first ? a.first < x.first : a.second > x.second;
+        });
+    else if (g_mutation == MUT_VICTIM_IGNORE_STAMP)
+        std::sort(order.begin(), order.end(), [](auto a, auto x) { return a.second < x.second; });
+    else
+        std::sort(order.begin(), order.end());
+    if (Ms.size() > order.size()) return -5;
+    for (size_t r = 0; r < Ms.size(); ++r) {
+        int32_t v = order[r].second, m = Ms[r], old = slot_token[v];
+        if (old >= 0 && g_mutation != MUT_EVICT_KEEPS_OLD) cache_slots[old] = -1;
+        cache_slots[m] = v;
+        slot_token[v] = m;
+        last_use[v] = t;
+        misses[r] = m;
+        victims[r] = v;
+        evict_old[r] = old;
+    }
+    if (n_hits) *n_hits = (int32_t)Hs.size();
+    return (int)Ms.size();
+}
+
+// Attention over explicit rows (for the closed-form pins).
+void oracle_attention(const uint16_t* qa, int H, const uint16_t* rows, int n, float scale, double* out) {
+    Oracle o;
+    o.H = H;
+    o.scale = scale;
+    std::vector<const uint16_t*> r;
+    for (int j = 0; j < n; ++j) r.push_back(rows + (size_t)j * KV_DIM);
+    sparse_attention(o, qa, r, out);
+}
+
+}  // extern "C"
