@@ -1,0 +1,219 @@
+/*
+ * sko.h — C ABI of the sparse decode offload step (libsko.so, gfx950).
+ *
+ * The operation is the per-layer decode step of "Layerwise and Sparse KV
+ * Cache Offloading Design" (vLLM-Ascend design doc), section 4 "Sparse
+ * Decode Offload": the full main-KV history lives in a pinned host pool; the
+ * device holds the indexer cache and a fixed-size per-layer hot buffer; each
+ * step appends the new token's rows, selects top-k tokens with the indexer,
+ * updates an LRU residency table, copies only the missed rows host->device,
+ * remaps the winners to hot-buffer slots and runs sparse attention over them.
+ * The hot-shelf mechanics (hits need no fetch, misses take evicted slots,
+ * fixed shelf size, a cache_slots reverse index that is -1 for absent
+ * tokens, index and residency packed into one int32 per top-k winner, MTP
+ * position lists merged and deduplicated before loading) follow the
+ * decode paragraphs of the FlashOffloading explainer on learnaivisually.com.
+ *
+ * Data types: bf16 values are passed as raw 16-bit patterns (uint16_t).
+ * Row shapes are fixed: indexer row = 64 bf16 (128 B); main-KV row = 576
+ * bf16 (1152 B: 512 latent + 64 rope); attention K = all 576 columns,
+ * V = the first 512.
+ *
+ * Conventions for every call:
+ *  - Return 0 (SKO_OK) or a negative SKO_E_* code; sko_last_error() gives a
+ *    message for the calling thread's last failure.
+ *  - Arguments are validated completely before anything is changed or
+ *    enqueued: a rejected call leaves the handle and all buffers untouched
+ *    (the pages' design fails a transfer on a layout mismatch instead of
+ *    leaving partial data; section 7 of the same page).
+ *  - A HIP runtime failure after validation marks the handle FAILED; every
+ *    later call except sko_destroy returns SKO_E_STATE (no silent
+ *    corruption, no retry).
+ *  - A handle is not thread-safe: drive it from one host thread.
+ *  - All device work is enqueued on the stream given at create (or set by
+ *    sko_set_stream), in call order.
+ */
+#ifndef SKO_H
+#define SKO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKO_OK 0
+#define SKO_E_INVAL (-1)       /* bad argument or configuration */
+#define SKO_E_NOMEM (-2)       /* host pinned or device allocation failed */
+#define SKO_E_DEVICE (-3)      /* HIP runtime error (handle is now FAILED) */
+#define SKO_E_CAPACITY (-4)    /* append beyond max_tokens */
+#define SKO_E_STATE (-5)       /* handle FAILED by an earlier device error */
+#define SKO_E_UNSUPPORTED (-6) /* valid but outside what the kernels support */
+
+#define SKO_ALL_SEQS (-1)
+
+#define SKO_INDEX_DIM 64
+#define SKO_KV_DIM 576
+#define SKO_V_DIM 512
+#define SKO_MAX_MERGE 8192 /* limit on mtp_positions * top_k */
+
+typedef struct sko_handle sko_handle;
+
+typedef struct sko_config {
+    int32_t num_layers;    /* L >= 1 */
+    int32_t batch;         /* B >= 1 sequences */
+    int64_t max_tokens;    /* per-sequence capacity, 1 <= cap < 2^31 - 1 */
+    int32_t index_dim;     /* must be 64 */
+    int32_t kv_dim;        /* must be 576 */
+    int32_t v_dim;         /* must be 512 */
+    int32_t num_heads;     /* H >= 1 attention heads sharing the latent rows */
+    int32_t top_k;         /* k >= 1 winners per query position */
+    int32_t hot_slots;     /* S per (layer, seq); S >= mtp_positions * top_k */
+    int32_t mtp_positions; /* D >= 1 query positions per step (MTP3 = 4) */
+    float attn_scale;      /* finite, > 0; usually 1/sqrt(576) */
+    int32_t device;        /* HIP device ordinal */
+    uint32_t flags;        /* must be 0 */
+} sko_config;
+
+/* Per-sequence counters of the most recent sko_decode_step on a layer. */
+typedef struct sko_seq_counts {
+    int32_t unique;    /* |U|: distinct winners over all positions */
+    int32_t hits;      /* winners already resident */
+    int32_t misses;    /* unique misses = rows copied host -> device */
+    int32_t evictions; /* victims that held a token */
+    int32_t selected;  /* min(top_k, tokens present) */
+    int32_t tokens;    /* tokens present (L_t) */
+    int32_t step;      /* the layer's step stamp t used */
+    int32_t reserved;
+} sko_seq_counts;
+
+/* Cumulative counters of one layer since create. */
+typedef struct sko_layer_stats {
+    int64_t steps;
+    int64_t unique;
+    int64_t hits;
+    int64_t misses;
+    int64_t evictions;
+    int64_t h2d_bytes; /* misses * 1152 */
+} sko_layer_stats;
+
+/*
+ * sko_create — validate cfg, then allocate and own every buffer of the
+ * offload state:
+ *   host pool     pinned, device-mapped  [L][B][cap][576] bf16
+ *   indexer cache device                 [L][B][cap][64]  bf16
+ *   hot buffer    device                 [L][B][S][576]   bf16 (zeroed)
+ *   cache_slots   device                 [L][B][cap] int32 = -1
+ *   slot_token    device                 [L][B][S]   int32 = -1
+ *   last_use      device                 [L][B][S]   int32 = -1
+ * plus per-step scratch.  `stream` is a hipStream_t (NULL = null stream)
+ * owned by the caller.  On error *out = NULL and nothing leaks.
+ * Errors: SKO_E_INVAL (NULL pointer, a dimension other than 64/576/512,
+ * L/B/H/k/D < 1, S < D*k, cap out of range, bad scale, flags != 0),
+ * SKO_E_UNSUPPORTED (D*k > SKO_MAX_MERGE), SKO_E_NOMEM, SKO_E_DEVICE.
+ */
+int sko_create(const sko_config* cfg, void* stream, sko_handle** out);
+
+/* Replace the stream used for later calls (caller-owned hipStream_t). */
+int sko_set_stream(sko_handle* h, void* stream);
+
+/*
+ * sko_append_token — write n new tokens per sequence at the end of each
+ * selected sequence: the main-KV rows go to their logical slots in the host
+ * pool, the indexer rows to the device indexer cache ([LSO] §4 "Decode
+ * step", first two items; the "Decode current KV to Decode host" row of the
+ * transfer-granularity table: token rows).  A prefix load is one call with
+ * n = context length.
+ *   seq       0 <= seq < B, or SKO_ALL_SEQS (rows for sequence b start at
+ *             row b*n of both inputs)
+ *   idx_rows  [rows][64] bf16, kv_rows [rows][576] bf16, row-major,
+ *             rows = n or B*n
+ *   src_on_device  0: host memory (read before the call returns);
+ *                  1: device memory, read in stream order (keep it live
+ *                     until the stream passes this call)
+ * Errors: SKO_E_INVAL, SKO_E_CAPACITY (any selected sequence would exceed
+ * max_tokens; checked for all before any write), SKO_E_STATE.
+ */
+int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_rows,
+                     const void* kv_rows, int64_t n, int32_t src_on_device);
+
+/*
+ * sko_decode_step — one sparse decode step of `layer` for all B sequences
+ * and D positions, enqueued on the stream (asynchronous; no host sync):
+ * score -> packed top-k -> merge/dedupe -> LRU update -> miss-only gather
+ * -> remap -> attention ([LSO] §4 "Decode step" items 3-7).
+ *   q_idx   device [B][D][64] bf16 indexer queries
+ *   q_attn  device [B][D][H][576] bf16 attention queries
+ *   out     device [B][D][H][512] fp32 attention output
+ * A sequence with no tokens selects nothing and gets a zero output.
+ * The layer's step stamp advances by one per call.
+ * Errors: SKO_E_INVAL (bad layer or NULL pointer), SKO_E_STATE, SKO_E_DEVICE.
+ */
+int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void* q_attn,
+                     float* out);
+
+/* Buffers of the most recent sko_decode_step (any layer), for inspection. */
+enum sko_step_buffer {
+    SKO_BUF_TOPK = 1,      /* int32 [B][D][k]: packed winners (bit31 = miss), first `selected` valid, any order */
+    SKO_BUF_PHYS = 2,      /* int32 [B][D][k]: hot slot of each TOPK entry, same order */
+    SKO_BUF_COUNTS = 3,    /* sko_seq_counts [B] */
+    SKO_BUF_MISSES = 4,    /* int32 [B][D*k]: miss tokens ascending, first `misses` valid */
+    SKO_BUF_VICTIMS = 5,   /* int32 [B][D*k]: slot given to MISSES[r] */
+    SKO_BUF_EVICT_OLD = 6, /* int32 [B][D*k]: previous owner of VICTIMS[r] or -1 */
+    SKO_BUF_KEYS = 7       /* uint32 [B][D][cap]: ordered score keys, first `tokens` valid */
+};
+
+/*
+ * sko_read_step — synchronize the stream and copy one step buffer to host
+ * memory `dst` of `bytes` (must equal the buffer's size).
+ */
+int sko_read_step(sko_handle* h, int32_t which, void* dst, int64_t bytes);
+
+/* Per-(layer, seq) state tables, for inspection. */
+enum sko_table {
+    SKO_TAB_CACHE_SLOTS = 1, /* int32 [cap] */
+    SKO_TAB_SLOT_TOKEN = 2,  /* int32 [S] */
+    SKO_TAB_LAST_USE = 3,    /* int32 [S] */
+    SKO_TAB_HOT = 4,         /* bf16 [S][576] */
+    SKO_TAB_INDEXER = 5,     /* bf16 [cap][64] */
+    SKO_TAB_POOL = 6,        /* bf16 [cap][576] (host pool) */
+    SKO_TAB_NTOK = 7         /* int64 [1] tokens present */
+};
+
+/*
+ * sko_read_table — synchronize the stream and copy one table of
+ * (layer, seq) to host memory `dst` of `bytes` (must equal its size).
+ */
+int sko_read_table(sko_handle* h, int32_t layer, int32_t seq, int32_t which, void* dst,
+                   int64_t bytes);
+
+/* Cumulative counters of `layer` (synchronizes the stream). */
+int sko_get_stats(sko_handle* h, int32_t layer, sko_layer_stats* out);
+
+/*
+ * Kernel timing: when enabled, every stage launch of sko_decode_step is
+ * bracketed by HIP events on the handle's stream and the elapsed times are
+ * accumulated per stage.  sko_set_timing (either value) synchronizes and
+ * clears the totals.  sko_get_timing synchronizes and returns the totals
+ * (ms) and launch counts for up to `n` stages; stage names come from
+ * sko_stage_name.
+ */
+int sko_set_timing(sko_handle* h, int32_t enable);
+int sko_get_timing(sko_handle* h, double* total_ms, int64_t* launches, int32_t n);
+const char* sko_stage_name(int32_t stage);
+int32_t sko_num_stages(void);
+
+/* Destroy: synchronize the stream, free everything. NULL is a no-op. */
+void sko_destroy(sko_handle* h);
+
+/* Message for the calling thread's last failure ("" if none). */
+const char* sko_last_error(void);
+
+/* Library version string. */
+const char* sko_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKO_H */

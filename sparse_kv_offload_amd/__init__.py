@@ -1,0 +1,301 @@
+"""Python binding of libsko, the sparse decode offload step for MI355X.
+
+Argument marshalling only: every stage of the step runs in the HIP kernels of
+``libsko.so`` (built from ``csrc/`` by ``build.py``).  The functions carry the
+names of the C ABI in ``include/sko.h``; :class:`SparseKVOffload` is a small
+convenience wrapper over them.  Buffers may be given as torch tensors (device
+or host), numpy arrays (host) or raw integer addresses.  PyTorch only
+provides device memory and the stream.
+
+There is no fallback: if the library is missing, importing this package
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsko.so")
+
+SKO_OK = 0
+SKO_E_INVAL = -1
+SKO_E_NOMEM = -2
+SKO_E_DEVICE = -3
+SKO_E_CAPACITY = -4
+SKO_E_STATE = -5
+SKO_E_UNSUPPORTED = -6
+SKO_ALL_SEQS = -1
+SKO_INDEX_DIM, SKO_KV_DIM, SKO_V_DIM = 64, 576, 512
+SKO_MAX_MERGE = 8192
+
+SKO_BUF_TOPK, SKO_BUF_PHYS, SKO_BUF_COUNTS = 1, 2, 3
+SKO_BUF_MISSES, SKO_BUF_VICTIMS, SKO_BUF_EVICT_OLD, SKO_BUF_KEYS = 4, 5, 6, 7
+SKO_TAB_CACHE_SLOTS, SKO_TAB_SLOT_TOKEN, SKO_TAB_LAST_USE = 1, 2, 3
+SKO_TAB_HOT, SKO_TAB_INDEXER, SKO_TAB_POOL, SKO_TAB_NTOK = 4, 5, 6, 7
+
+EXPORTED = (
+    "sko_create", "sko_set_stream", "sko_append_token", "sko_decode_step", "sko_read_step",
+    "sko_read_table", "sko_get_stats", "sko_set_timing", "sko_get_timing", "sko_stage_name",
+    "sko_num_stages", "sko_destroy", "sko_last_error", "sko_version",
+)
+
+
+class SkoConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int64),
+        ("index_dim", ctypes.c_int32),
+        ("kv_dim", ctypes.c_int32),
+        ("v_dim", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("hot_slots", ctypes.c_int32),
+        ("mtp_positions", ctypes.c_int32),
+        ("attn_scale", ctypes.c_float),
+        ("device", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class SkoSeqCounts(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("unique", "hits", "misses", "evictions", "selected", "tokens", "step", "reserved")]
+
+
+class SkoLayerStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("steps", "unique", "hits", "misses", "evictions", "h2d_bytes")]
+
+
+class SkoError(RuntimeError):
+    def __init__(self, code: int, where: str, msg: str):
+        super().__init__(f"{where} failed ({code}): {msg}")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libsko.so not found at {LIB_PATH}; build it first "
+            "(python sparse_kv_offload_amd/build.py or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    sig = {
+        "sko_create": (ctypes.c_int, [ctypes.POINTER(SkoConfig), vp, ctypes.POINTER(vp)]),
+        "sko_set_stream": (ctypes.c_int, [vp, vp]),
+        "sko_append_token": (ctypes.c_int, [vp, i32, i32, vp, vp, i64, i32]),
+        "sko_decode_step": (ctypes.c_int, [vp, i32, vp, vp, vp]),
+        "sko_read_step": (ctypes.c_int, [vp, i32, vp, i64]),
+        "sko_read_table": (ctypes.c_int, [vp, i32, i32, i32, vp, i64]),
+        "sko_get_stats": (ctypes.c_int, [vp, i32, ctypes.POINTER(SkoLayerStats)]),
+        "sko_set_timing": (ctypes.c_int, [vp, i32]),
+        "sko_get_timing": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_int64), i32]),
+        "sko_stage_name": (ctypes.c_char_p, [i32]),
+        "sko_num_stages": (i32, []),
+        "sko_destroy": (None, [vp]),
+        "sko_last_error": (ctypes.c_char_p, []),
+        "sko_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _addr(x) -> Optional[int]:
+    """Raw address of a torch tensor, numpy array or integer."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, np.ndarray):
+        if not x.flags["C_CONTIGUOUS"]:
+            raise ValueError("numpy buffers must be C-contiguous")
+        return x.ctypes.data
+    if hasattr(x, "data_ptr"):
+        if not x.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        return x.data_ptr()
+    raise TypeError(f"cannot take the address of {type(x)!r}")
+
+
+def _is_device(x) -> bool:
+    return hasattr(x, "is_cuda") and bool(x.is_cuda)
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != SKO_OK:
+        raise SkoError(rc, where, sko_last_error())
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+# --------------------------------------------------------------- C ABI names
+
+def sko_last_error() -> str:
+    return (_lib.sko_last_error() or b"").decode()
+
+
+def sko_version() -> str:
+    return _lib.sko_version().decode()
+
+
+def sko_num_stages() -> int:
+    return int(_lib.sko_num_stages())
+
+
+def sko_stage_name(stage: int) -> str:
+    return (_lib.sko_stage_name(stage) or b"").decode()
+
+
+def sko_create(cfg: SkoConfig, stream=None) -> int:
+    h = ctypes.c_void_p()
+    _check(_lib.sko_create(ctypes.byref(cfg), _stream_handle(stream), ctypes.byref(h)), "sko_create")
+    return int(h.value)
+
+
+def sko_set_stream(h: int, stream) -> None:
+    _check(_lib.sko_set_stream(h, _stream_handle(stream)), "sko_set_stream")
+
+
+def sko_append_token(h: int, layer: int, seq: int, idx_rows, kv_rows, n: int,
+                     src_on_device: Optional[bool] = None) -> None:
+    dev = _is_device(idx_rows) if src_on_device is None else bool(src_on_device)
+    _check(_lib.sko_append_token(h, layer, seq, _addr(idx_rows), _addr(kv_rows), n, int(dev)),
+           "sko_append_token")
+
+
+def sko_decode_step(h: int, layer: int, q_idx, q_attn, out) -> None:
+    _check(_lib.sko_decode_step(h, layer, _addr(q_idx), _addr(q_attn), _addr(out)), "sko_decode_step")
+
+
+def sko_read_step(h: int, which: int, dst: np.ndarray) -> np.ndarray:
+    _check(_lib.sko_read_step(h, which, _addr(dst), dst.nbytes), "sko_read_step")
+    return dst
+
+
+def sko_read_table(h: int, layer: int, seq: int, which: int, dst: np.ndarray) -> np.ndarray:
+    _check(_lib.sko_read_table(h, layer, seq, which, _addr(dst), dst.nbytes), "sko_read_table")
+    return dst
+
+
+def sko_get_stats(h: int, layer: int) -> SkoLayerStats:
+    st = SkoLayerStats()
+    _check(_lib.sko_get_stats(h, layer, ctypes.byref(st)), "sko_get_stats")
+    return st
+
+
+def sko_set_timing(h: int, enable: bool) -> None:
+    _check(_lib.sko_set_timing(h, int(bool(enable))), "sko_set_timing")
+
+
+def sko_get_timing(h: int) -> dict:
+    n = sko_num_stages()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(_lib.sko_get_timing(h, ms, cnt, n), "sko_get_timing")
+    return {sko_stage_name(i): (float(ms[i]), int(cnt[i])) for i in range(n)}
+
+
+def sko_destroy(h: int) -> None:
+    if h:
+        _lib.sko_destroy(h)
+
+
+def make_config(*, num_layers: int, batch: int, max_tokens: int, num_heads: int, top_k: int,
+                hot_slots: int, mtp_positions: int = 1, attn_scale: float = 1.0 / 24.0,
+                device: int = 0, index_dim: int = SKO_INDEX_DIM, kv_dim: int = SKO_KV_DIM,
+                v_dim: int = SKO_V_DIM, flags: int = 0) -> SkoConfig:
+    return SkoConfig(num_layers, batch, max_tokens, index_dim, kv_dim, v_dim, num_heads, top_k,
+                     hot_slots, mtp_positions, attn_scale, device, flags)
+
+
+class SparseKVOffload:
+    """Owner of one libsko handle (thin convenience over the C ABI)."""
+
+    def __init__(self, cfg: SkoConfig, stream=None):
+        self.cfg = cfg
+        self.handle = sko_create(cfg, stream)
+
+    def close(self) -> None:
+        if self.handle:
+            sko_destroy(self.handle)
+            self.handle = 0
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def append(self, layer: int, seq: int, idx_rows, kv_rows, n: Optional[int] = None) -> None:
+        if n is None:
+            rows = idx_rows.shape[0]
+            n = rows if seq != SKO_ALL_SEQS else rows // self.cfg.batch
+        sko_append_token(self.handle, layer, seq, idx_rows, kv_rows, n)
+
+    def decode_step(self, layer: int, q_idx, q_attn, out) -> None:
+        sko_decode_step(self.handle, layer, q_idx, q_attn, out)
+
+    # ---- inspection ----
+    def step_buffer(self, which: int) -> np.ndarray:
+        c = self.cfg
+        B, D, k = c.batch, c.mtp_positions, c.top_k
+        if which == SKO_BUF_COUNTS:
+            a = np.zeros((B, 8), dtype=np.int32)
+        elif which in (SKO_BUF_TOPK, SKO_BUF_PHYS):
+            a = np.zeros((B, D, k), dtype=np.int32)
+        elif which == SKO_BUF_KEYS:
+            a = np.zeros((B, D, c.max_tokens), dtype=np.uint32)
+        else:
+            a = np.zeros((B, D * k), dtype=np.int32)
+        return sko_read_step(self.handle, which, a)
+
+    def table(self, layer: int, seq: int, which: int) -> np.ndarray:
+        c = self.cfg
+        shapes = {
+            SKO_TAB_CACHE_SLOTS: ((c.max_tokens,), np.int32),
+            SKO_TAB_SLOT_TOKEN: ((c.hot_slots,), np.int32),
+            SKO_TAB_LAST_USE: ((c.hot_slots,), np.int32),
+            SKO_TAB_HOT: ((c.hot_slots, SKO_KV_DIM), np.uint16),
+            SKO_TAB_INDEXER: ((c.max_tokens, SKO_INDEX_DIM), np.uint16),
+            SKO_TAB_POOL: ((c.max_tokens, SKO_KV_DIM), np.uint16),
+            SKO_TAB_NTOK: ((1,), np.int64),
+        }
+        shape, dt = shapes[which]
+        return sko_read_table(self.handle, layer, seq, which, np.zeros(shape, dtype=dt))
+
+    def stats(self, layer: int) -> SkoLayerStats:
+        return sko_get_stats(self.handle, layer)
+
+    def set_timing(self, enable: bool) -> None:
+        sko_set_timing(self.handle, enable)
+
+    def timing(self) -> dict:
+        return sko_get_timing(self.handle)
+
+
+__all__ = [n for n in globals() if n.startswith(("sko_", "SKO_", "Sko"))] + [
+    "SparseKVOffload", "make_config", "LIB_PATH", "EXPORTED"]

@@ -1,0 +1,243 @@
+// Remap + sparse attention over the resident rows (split over rows).
+//
+// [LSO] section 4 "Decode step": the logical top-k positions are remapped
+// to physical hot-buffer slots and sparse attention consumes the resident
+// K/V (the Copy-SFA operator of the Chinese revision, section 4, fused
+// Copy-SFA sub-section).  For every (seq, position, head):
+//     z_j = scale * (q . K_j)  over the 576 columns of row j,
+//     out = sum_j softmax(z)_j * V_j  over the first 512 (latent) columns,
+// j running over the min(k, L_t) winners of that position.
+//
+// Layout of the work: a block takes one (seq, position), one group of 16
+// heads and a chunk of winners.  Rows are staged 32 at a time in LDS (one
+// coalesced 1152-byte read each, gathered by slot).  Every wave computes
+// S^T = K Q^T for the 32 rows with v_mfma_f32_16x16x32_bf16 (M = 16 rows,
+// N = 16 heads, K = 576), runs the online softmax, and accumulates
+// O^T = V^T P^T for its own 128 of the 512 output columns (M = 16 columns,
+// N = 16 heads, K = 32 rows).  P enters the MFMA in bf16; accumulation is
+// fp32.  Each block writes (m, l, acc) partials; k_attn_combine merges them.
+#include "sko_common.cuh"
+#include "sko_internal.h"
+
+namespace sko {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRowStrideU4 = kKvRowU4 + 1;  // 16-byte pad per staged row
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// dword holding bf16 element m (0..7) of a 16-byte vector
+__device__ __forceinline__ uint32_t dword_of(uint4 v, int m) {
+    return (m >> 1) == 0 ? v.x : (m >> 1) == 1 ? v.y : (m >> 1) == 2 ? v.z : v.w;
+}
+
+__global__ __launch_bounds__(256) void k_attn_partial(
+    const int32_t* __restrict__ topk, const int32_t* __restrict__ cache_slots_layer,
+    const uint4* __restrict__ hot_layer, const uint4* __restrict__ q_attn,
+    const int32_t* __restrict__ ntok_layer, float* __restrict__ part_acc,
+    float* __restrict__ part_ml, int32_t* __restrict__ phys, int D, int H, int HG, int top_k,
+    int S, int64_t cap, int rows_per_block, int nchunk, float scale_log2) {
+    __shared__ uint4 rows[kAttnTileRows * kRowStrideU4];
+    __shared__ int32_t slot_s[kAttnTileRows];
+
+    const int chunk = blockIdx.x, bp = blockIdx.y, hg = blockIdx.z;
+    const int b = bp / D;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t Lt = ntok_layer[b];
+    const int kk = (int)std::min<int64_t>(top_k, Lt);
+    const int r0 = chunk * rows_per_block;
+    const int r1 = std::min(r0 + rows_per_block, kk);
+    const size_t pidx = ((size_t)bp * HG + hg) * nchunk + chunk;
+    float* __restrict__ acc_out = part_acc + pidx * kAttnHeadGroup * kVDim;
+    float* __restrict__ ml_out = part_ml + pidx * kAttnHeadGroup * 2;
+    if (r0 >= r1) {
+        if (tid < kAttnHeadGroup) {
+            ml_out[2 * tid] = -INFINITY;
+            ml_out[2 * tid + 1] = 0.0f;
+        }
+        return;
+    }
+    const int n16 = lane & 15, g = lane >> 4;
+    const int h = hg * kAttnHeadGroup + n16;
+
+    // B operand of S^T = K Q^T: lane (n16, g) holds Q[h][32ks + 8g .. +7]
+    uint4 qv[kKvDim / 32];
+    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int ks = 0; ks < kKvDim / 32; ++ks)
+        qv[ks] = (h < H) ? q_attn[((size_t)bp * H + h) * kKvRowU4 + 4 * ks + g] : zero4;
+
+    f32x4_t acc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.0f;
+    const int32_t* __restrict__ w = topk + (size_t)bp * top_k;
+    const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
+    const uint4* __restrict__ hb = hot_layer + (size_t)b * S * kKvRowU4;
+
+    for (int r = r0; r < r1; r += kAttnTileRows) {
+        // remap: logical winner -> hot slot
+        if (tid < kAttnTileRows) {
+            const int j = r + tid;
+            int32_t slot = -1;
+            if (j < r1) {
+                const int32_t tok = w[j] & 0x7FFFFFFF;
+                slot = (tok < cap) ? cs[tok] : -1;
+                if (slot >= S) slot = -1;
+                if (hg == 0) phys[(size_t)bp * top_k + j] = slot;
+            }
+            slot_s[tid] = slot;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < kAttnTileRows * kKvRowU4; idx += 256) {
+            const int rr = idx / kKvRowU4;
+            const int part = idx - rr * kKvRowU4;
+            const int32_t slot = slot_s[rr];
+            rows[rr * kRowStrideU4 + part] = (slot >= 0) ? hb[(size_t)slot * kKvRowU4 + part] : zero4;
+        }
+        __syncthreads();
+
+        // S^T tiles for rows r..r+15 and r+16..r+31; lane holds head n16,
+        // rows 4g+i (+16)
+        float s[2][4];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+            const uint4* rp = rows + (half * 16 + n16) * kRowStrideU4 + g;
+#pragma unroll
+            for (int ks = 0; ks < kKvDim / 32; ++ks)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rp[4 * ks]), as_bf16x8(qv[ks]), c, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = r + half * 16 + 4 * g + i;
+                s[half][i] = (j < r1) ? c[i] * scale_log2 : -INFINITY;
+            }
+        }
+        // online softmax per head over the 32 rows (lane groups g share a head)
+        float mt = s[0][0];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[half][i]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = exp2f(m_run - m_new);
+        float p[2][4];
+        float ls = 0.0f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[half][i] = exp2f(s[half][i] - m_new);
+                ls += p[half][i];
+            }
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m] *= alpha;
+
+        // B operand of O^T = V^T P^T: k-slot s of group g is row 4g+s (s<4)
+        // or 16+4g+s-4 (s>=4), i.e. exactly the rows this lane's p covers
+        uint4 pb;
+        pb.x = f32_to_bf16_bits(p[0][0]) | (f32_to_bf16_bits(p[0][1]) << 16);
+        pb.y = f32_to_bf16_bits(p[0][2]) | (f32_to_bf16_bits(p[0][3]) << 16);
+        pb.z = f32_to_bf16_bits(p[1][0]) | (f32_to_bf16_bits(p[1][1]) << 16);
+        pb.w = f32_to_bf16_bits(p[1][2]) | (f32_to_bf16_bits(p[1][3]) << 16);
+
+        // A operand: V^T.  Lane reads 8 columns (cb + 8*n16 .. +7) of each of
+        // its 8 rows; column cb + 8*n16 + m feeds MFMA m.
+        uint4 vr[8];
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+            const int R = (sl < 4) ? (4 * g + sl) : (16 + 4 * g + sl - 4);
+            vr[sl] = rows[R * kRowStrideU4 + wave * 16 + n16];
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            // element m of each row: low half of dword m/2 for even m, high half for odd m
+            uint32_t d[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t w0 = dword_of(vr[2 * q], m), w1 = dword_of(vr[2 * q + 1], m);
+                d[q] = (m & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
+            }
+            const uint4 a = make_uint4(d[0], d[1], d[2], d[3]);
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pb), acc[m], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    float lt = l_run + __shfl_xor(l_run, 16);
+    lt += __shfl_xor(lt, 32);
+    const int cb = wave * 128;
+    if (h < H) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc_out[n16 * kVDim + cb + 8 * (4 * g + i) + m] = acc[m][i];
+    }
+    if (wave == 0 && g == 0) {
+        ml_out[2 * n16] = m_run;
+        ml_out[2 * n16 + 1] = lt;
+    }
+}
+
+__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_acc,
+                                                      const float* __restrict__ part_ml,
+                                                      float* __restrict__ out, int H, int HG,
+                                                      int nchunk) {
+    const int bp = blockIdx.x, h = blockIdx.y;
+    const int hg = h / kAttnHeadGroup, hl = h - hg * kAttnHeadGroup;
+    const size_t pbase = ((size_t)bp * HG + hg) * nchunk;
+    float M = -INFINITY;
+    for (int c = 0; c < nchunk; ++c) {
+        const float l = part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2 + 1];
+        if (l > 0.0f) M = fmaxf(M, part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2]);
+    }
+    const int col = threadIdx.x * 4;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.0f;
+    for (int c = 0; c < nchunk; ++c) {
+        const float l = part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2 + 1];
+        if (!(l > 0.0f)) continue;
+        const float wgt = exp2f(part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2] - M);
+        L += wgt * l;
+        const float4 a = *reinterpret_cast<const float4*>(
+            part_acc + ((pbase + c) * kAttnHeadGroup + hl) * kVDim + col);
+        o.x += wgt * a.x;
+        o.y += wgt * a.y;
+        o.z += wgt * a.z;
+        o.w += wgt * a.w;
+    }
+    const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+    *reinterpret_cast<float4*>(out + ((size_t)bp * H + h) * kVDim + col) =
+        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+}
+
+hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_t* cache_slots_layer,
+                               const uint16_t* hot_layer, const uint16_t* q_attn,
+                               const int32_t* ntok_layer, float* part_acc, float* part_ml,
+                               int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
+                               int rows_per_block, float scale) {
+    const int HG = (H + kAttnHeadGroup - 1) / kAttnHeadGroup;
+    const int nchunk = (top_k + rows_per_block - 1) / rows_per_block;
+    const float scale_log2 = scale * 1.4426950408889634f;
+    hipLaunchKernelGGL(k_attn_partial, dim3(nchunk, B * D, HG), dim3(256), 0, st, topk,
+                       cache_slots_layer, reinterpret_cast<const uint4*>(hot_layer),
+                       reinterpret_cast<const uint4*>(q_attn), ntok_layer, part_acc, part_ml, phys,
+                       D, H, HG, top_k, S, cap, rows_per_block, nchunk, scale_log2);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(hipStream_t st, const float* part_acc, const float* part_ml,
+                               float* out, int B, int D, int H, int nchunk) {
+    const int HG = (H + kAttnHeadGroup - 1) / kAttnHeadGroup;
+    hipLaunchKernelGGL(k_attn_combine, dim3(B * D, H), dim3(kVDim / 4), 0, st, part_acc, part_ml,
+                       out, H, HG, nchunk);
+    return hipGetLastError();
+}
+
+}  // namespace sko

@@ -1,0 +1,590 @@
+// Host runtime of libsko: the C ABI declared in include/sko.h.
+//
+// Owns the offload state of "Layerwise and Sparse KV Cache Offloading
+// Design" section 4 ("Memory layout"): the full main-KV history in a pinned,
+// device-mapped host pool; the indexer cache and the per-layer hot buffers
+// in device memory; and the residency tables.  Every call validates all of
+// its arguments before touching state (section 7 of the same page: a layout
+// mismatch fails instead of leaving partial data); a HIP failure marks the
+// handle FAILED so that later calls refuse instead of computing on corrupt
+// state.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/sko.h"
+#include "sko_internal.h"
+
+using namespace sko;
+
+namespace {
+
+thread_local std::string g_err;
+
+int set_err(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int set_err(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+enum Stage {
+    ST_APPEND = 0,
+    ST_INIT,
+    ST_SCORE,
+    ST_THRESH,
+    ST_FILTER,
+    ST_REFINE,
+    ST_MERGE_LRU,
+    ST_GATHER,
+    ST_ATTN,
+    ST_COMBINE,
+    ST_COUNT
+};
+const char* const kStageNames[ST_COUNT] = {"append_rows",  "step_init",     "score_hist",
+                                           "topk_threshold", "topk_filter", "topk_refine",
+                                           "merge_lru",    "gather_misses", "attn_partial",
+                                           "attn_combine"};
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+}  // namespace
+
+struct sko_handle {
+    sko_config cfg{};
+    hipStream_t stream = nullptr;
+    bool failed = false;
+    int L = 0, B = 0, k = 0, S = 0, D = 0, H = 0, HG = 0;
+    int64_t cap = 0;
+
+    // offload state
+    uint16_t* pool_host = nullptr;  // pinned [L][B][cap][576]
+    uint16_t* pool_dev = nullptr;   // device mapping of pool_host
+    uint16_t* idx = nullptr;        // [L][B][cap][64]
+    uint16_t* hot = nullptr;        // [L][B][S][576]
+    int32_t* cache_slots = nullptr; // [L][B][cap]
+    int32_t* slot_token = nullptr;  // [L][B][S]
+    int32_t* last_use = nullptr;    // [L][B][S]
+    int32_t* ntok_dev = nullptr;    // [L][B]
+    unsigned long long* stats = nullptr;  // [L][8]
+    std::vector<int64_t> ntok;      // host mirror [L][B]
+    std::vector<int32_t> step;      // [L]
+
+    // per-step scratch (shared by all layers; steps are stream-ordered)
+    uint32_t* keys = nullptr;       // [B][D][cap]
+    uint32_t* hist = nullptr;       // [B][D][4096]
+    RowMeta* meta = nullptr;        // [B][D]
+    uint2* cand = nullptr;          // [B][D][cap]
+    int32_t* topk = nullptr;        // [B][D][k]
+    int32_t* phys = nullptr;        // [B][D][k]
+    int32_t* misses = nullptr;      // [B][D*k]
+    int32_t* victims = nullptr;     // [B][D*k]
+    int32_t* evict_old = nullptr;   // [B][D*k]
+    int32_t* counts = nullptr;      // [B][8]
+    GatherEntry* glist = nullptr;   // [B*D*k]
+    uint32_t* gtotal = nullptr;     // [1]
+    float* part_acc = nullptr;      // [B*D][HG][nchunk][16][512]
+    float* part_ml = nullptr;       // [B*D][HG][nchunk][16][2]
+    int rows_per_block = 32, nchunk = 1;
+    int last_layer = -1;
+
+    // timing
+    bool timing = false;
+    struct Pending {
+        int stage;
+        hipEvent_t a, b;
+    };
+    std::vector<Pending> pending;
+    std::vector<hipEvent_t> spare;
+    double total_ms[ST_COUNT] = {};
+    int64_t launches[ST_COUNT] = {};
+
+    std::vector<void*> dev_allocs;
+
+    size_t lb(int layer, int b) const { return (size_t)layer * B + b; }
+};
+
+namespace {
+
+int device_fail(sko_handle* h, hipError_t e, const char* what) {
+    if (h) h->failed = true;
+    return set_err(SKO_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dev_alloc(sko_handle* h, void** p, size_t bytes) {
+    *p = nullptr;
+    if (bytes == 0) bytes = 16;
+    if (hipMalloc(p, bytes) != hipSuccess) {
+        *p = nullptr;
+        (void)hipGetLastError();
+        return false;
+    }
+    h->dev_allocs.push_back(*p);
+    return true;
+}
+
+void free_all(sko_handle* h) {
+    for (auto& p : h->pending) {
+        (void)hipEventDestroy(p.a);
+        (void)hipEventDestroy(p.b);
+    }
+    for (auto e : h->spare) (void)hipEventDestroy(e);
+    for (void* p : h->dev_allocs) (void)hipFree(p);
+    if (h->pool_host) (void)hipHostFree(h->pool_host);
+    h->dev_allocs.clear();
+    h->pool_host = nullptr;
+}
+
+hipEvent_t take_event(sko_handle* h) {
+    if (!h->spare.empty()) {
+        hipEvent_t e = h->spare.back();
+        h->spare.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Launch one stage, bracketed by events when timing is on.
+template <typename F>
+int run_stage(sko_handle* h, int stage, F&& launch) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (h->timing) {
+        a = take_event(h);
+        b = take_event(h);
+        if (a) (void)hipEventRecord(a, h->stream);
+    }
+    hipError_t e = launch();
+    if (e != hipSuccess) return device_fail(h, e, kStageNames[stage]);
+    if (h->timing && a && b) {
+        (void)hipEventRecord(b, h->stream);
+        h->pending.push_back({stage, a, b});
+    }
+    return SKO_OK;
+}
+
+int check_handle(sko_handle* h) {
+    if (!h) return set_err(SKO_E_INVAL, "NULL handle");
+    if (h->failed) return set_err(SKO_E_STATE, "handle is FAILED after an earlier device error");
+    return SKO_OK;
+}
+
+int validate_config(const sko_config* c) {
+    if (!c) return set_err(SKO_E_INVAL, "NULL config");
+    if (c->index_dim != SKO_INDEX_DIM || c->kv_dim != SKO_KV_DIM || c->v_dim != SKO_V_DIM)
+        return set_err(SKO_E_INVAL, "row shapes must be index_dim=64, kv_dim=576, v_dim=512 (got %d/%d/%d)",
+                       c->index_dim, c->kv_dim, c->v_dim);
+    if (c->num_layers < 1 || c->batch < 1 || c->num_heads < 1 || c->top_k < 1 || c->mtp_positions < 1)
+        return set_err(SKO_E_INVAL, "num_layers, batch, num_heads, top_k, mtp_positions must be >= 1");
+    if (c->max_tokens < 1 || c->max_tokens >= 0x7FFFFFFFLL)
+        return set_err(SKO_E_INVAL, "max_tokens must be in [1, 2^31-1)");
+    if ((int64_t)c->hot_slots < (int64_t)c->mtp_positions * c->top_k)
+        return set_err(SKO_E_INVAL, "hot_slots (%d) must be >= mtp_positions*top_k (%lld)", c->hot_slots,
+                       (long long)c->mtp_positions * c->top_k);
+    if (!(c->attn_scale > 0.0f) || !std::isfinite(c->attn_scale))
+        return set_err(SKO_E_INVAL, "attn_scale must be finite and > 0");
+    if (c->flags != 0) return set_err(SKO_E_INVAL, "flags must be 0");
+    if (c->device < 0) return set_err(SKO_E_INVAL, "device must be >= 0");
+    if ((int64_t)c->mtp_positions * c->top_k > SKO_MAX_MERGE)
+        return set_err(SKO_E_UNSUPPORTED, "mtp_positions*top_k above %d", SKO_MAX_MERGE);
+    if ((int64_t)c->batch * c->max_tokens >= 0xFFFFFFFFLL || (int64_t)c->batch * c->hot_slots >= 0xFFFFFFFFLL)
+        return set_err(SKO_E_UNSUPPORTED, "batch*max_tokens and batch*hot_slots must stay below 2^32");
+    return SKO_OK;
+}
+
+int attn_rows_per_block(int k, int rows_total_pairs) {
+    // aim for >= ~1024 blocks across the chip; tiles of 32 rows
+    int rpb = kAttnTileRows;
+    while (rpb < 512 && (int64_t)((k + rpb * 2 - 1) / (rpb * 2)) * rows_total_pairs >= 1024) rpb *= 2;
+    return rpb;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sko_last_error(void) { return g_err.c_str(); }
+
+const char* sko_version(void) { return "sko 0.1 (gfx950)"; }
+
+int32_t sko_num_stages(void) { return ST_COUNT; }
+
+const char* sko_stage_name(int32_t stage) {
+    return (stage >= 0 && stage < ST_COUNT) ? kStageNames[stage] : "";
+}
+
+int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
+    if (!out) return set_err(SKO_E_INVAL, "NULL out pointer");
+    *out = nullptr;
+    int rc = validate_config(cfg);
+    if (rc != SKO_OK) return rc;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= cfg->device)
+        return set_err(SKO_E_DEVICE, "HIP device %d not available", cfg->device);
+    DeviceGuard guard(cfg->device);
+    if (!guard.ok) return set_err(SKO_E_DEVICE, "hipSetDevice(%d) failed", cfg->device);
+
+    sko_handle* h = new sko_handle();
+    h->cfg = *cfg;
+    h->stream = (hipStream_t)stream;
+    h->L = cfg->num_layers;
+    h->B = cfg->batch;
+    h->k = cfg->top_k;
+    h->S = cfg->hot_slots;
+    h->D = cfg->mtp_positions;
+    h->H = cfg->num_heads;
+    h->HG = (h->H + kAttnHeadGroup - 1) / kAttnHeadGroup;
+    h->cap = cfg->max_tokens;
+    h->ntok.assign((size_t)h->L * h->B, 0);
+    h->step.assign((size_t)h->L, 0);
+    h->rows_per_block = attn_rows_per_block(h->k, h->B * h->D * h->HG);
+    h->nchunk = (h->k + h->rows_per_block - 1) / h->rows_per_block;
+
+    const size_t LB = (size_t)h->L * h->B;
+    const size_t BD = (size_t)h->B * h->D;
+    const size_t pool_bytes = LB * (size_t)h->cap * kKvRowBytes;
+    if (hipHostMalloc((void**)&h->pool_host, pool_bytes, hipHostMallocMapped) != hipSuccess) {
+        (void)hipGetLastError();
+        h->pool_host = nullptr;
+        free_all(h);
+        delete h;
+        return set_err(SKO_E_NOMEM, "pinned host pool of %zu bytes", pool_bytes);
+    }
+    if (hipHostGetDevicePointer((void**)&h->pool_dev, h->pool_host, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        free_all(h);
+        delete h;
+        return set_err(SKO_E_DEVICE, "hipHostGetDevicePointer on the host pool failed");
+    }
+    bool ok = true;
+    ok = ok && dev_alloc(h, (void**)&h->idx, LB * h->cap * kIdxDim * 2);
+    ok = ok && dev_alloc(h, (void**)&h->hot, LB * h->S * (size_t)kKvRowBytes);
+    ok = ok && dev_alloc(h, (void**)&h->cache_slots, LB * h->cap * 4);
+    ok = ok && dev_alloc(h, (void**)&h->slot_token, LB * h->S * 4);
+    ok = ok && dev_alloc(h, (void**)&h->last_use, LB * h->S * 4);
+    ok = ok && dev_alloc(h, (void**)&h->ntok_dev, LB * 4);
+    ok = ok && dev_alloc(h, (void**)&h->stats, (size_t)h->L * 8 * 8);
+    ok = ok && dev_alloc(h, (void**)&h->keys, BD * h->cap * 4);
+    ok = ok && dev_alloc(h, (void**)&h->hist, BD * kHistBins * 4);
+    ok = ok && dev_alloc(h, (void**)&h->meta, BD * sizeof(RowMeta));
+    ok = ok && dev_alloc(h, (void**)&h->cand, BD * h->cap * sizeof(uint2));
+    ok = ok && dev_alloc(h, (void**)&h->topk, BD * h->k * 4);
+    ok = ok && dev_alloc(h, (void**)&h->phys, BD * h->k * 4);
+    ok = ok && dev_alloc(h, (void**)&h->misses, BD * h->k * 4);
+    ok = ok && dev_alloc(h, (void**)&h->victims, BD * h->k * 4);
+    ok = ok && dev_alloc(h, (void**)&h->evict_old, BD * h->k * 4);
+    ok = ok && dev_alloc(h, (void**)&h->counts, (size_t)h->B * 8 * 4);
+    ok = ok && dev_alloc(h, (void**)&h->glist, BD * h->k * sizeof(GatherEntry));
+    ok = ok && dev_alloc(h, (void**)&h->gtotal, 4);
+    ok = ok && dev_alloc(h, (void**)&h->part_acc, BD * h->HG * h->nchunk * kAttnHeadGroup * kVDim * 4);
+    ok = ok && dev_alloc(h, (void**)&h->part_ml, BD * h->HG * h->nchunk * kAttnHeadGroup * 2 * 4);
+    if (!ok) {
+        free_all(h);
+        delete h;
+        return set_err(SKO_E_NOMEM, "device allocation failed");
+    }
+    // initial state: empty shelf, empty reverse index, no tokens
+    hipError_t e = hipSuccess;
+    if (e == hipSuccess) e = hipMemsetAsync(h->cache_slots, 0xFF, LB * h->cap * 4, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->slot_token, 0xFF, LB * h->S * 4, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->last_use, 0xFF, LB * h->S * 4, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->ntok_dev, 0, LB * 4, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->hot, 0, LB * h->S * (size_t)kKvRowBytes, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->stats, 0, (size_t)h->L * 8 * 8, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->topk, 0, BD * h->k * 4, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->counts, 0, (size_t)h->B * 8 * 4, h->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+    if (e != hipSuccess) {
+        set_err(SKO_E_DEVICE, "initialising state: %s", hipGetErrorString(e));
+        free_all(h);
+        delete h;
+        return SKO_E_DEVICE;
+    }
+    *out = h;
+    return SKO_OK;
+}
+
+int sko_set_stream(sko_handle* h, void* stream) {
+    int rc = check_handle(h);
+    if (rc != SKO_OK) return rc;
+    h->stream = (hipStream_t)stream;
+    return SKO_OK;
+}
+
+int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_rows,
+                     const void* kv_rows, int64_t n, int32_t src_on_device) {
+    int rc = check_handle(h);
+    if (rc != SKO_OK) return rc;
+    if (layer < 0 || layer >= h->L) return set_err(SKO_E_INVAL, "layer %d out of range [0, %d)", layer, h->L);
+    if (seq != SKO_ALL_SEQS && (seq < 0 || seq >= h->B))
+        return set_err(SKO_E_INVAL, "seq %d out of range", seq);
+    if (n < 0) return set_err(SKO_E_INVAL, "n must be >= 0");
+    if (n > 0 && (!idx_rows || !kv_rows)) return set_err(SKO_E_INVAL, "NULL row pointer");
+    if (src_on_device != 0 && src_on_device != 1) return set_err(SKO_E_INVAL, "src_on_device must be 0 or 1");
+    const int seq0 = seq == SKO_ALL_SEQS ? 0 : seq;
+    const int nseq = seq == SKO_ALL_SEQS ? h->B : 1;
+    for (int s = 0; s < nseq; ++s)
+        if (h->ntok[h->lb(layer, seq0 + s)] + n > h->cap)
+            return set_err(SKO_E_CAPACITY, "seq %d: %lld + %lld tokens exceed max_tokens %lld", seq0 + s,
+                           (long long)h->ntok[h->lb(layer, seq0 + s)], (long long)n, (long long)h->cap);
+    if (n == 0) return SKO_OK;
+    DeviceGuard guard(h->cfg.device);
+    if (!guard.ok) return device_fail(h, hipErrorInvalidDevice, "hipSetDevice");
+
+    uint16_t* idx_layer = h->idx + (size_t)layer * h->B * h->cap * kIdxDim;
+    uint16_t* pool_layer_dev = h->pool_dev + (size_t)layer * h->B * h->cap * kKvDim;
+    int32_t* ntok_layer = h->ntok_dev + (size_t)layer * h->B;
+    const uint16_t* isrc = static_cast<const uint16_t*>(idx_rows);
+    const uint16_t* ksrc = static_cast<const uint16_t*>(kv_rows);
+
+    if (src_on_device) {
+        // one launch per run of sequences that share a start position
+        int s = 0;
+        while (s < nseq) {
+            const int64_t base = h->ntok[h->lb(layer, seq0 + s)];
+            int e = s + 1;
+            while (e < nseq && h->ntok[h->lb(layer, seq0 + e)] == base) ++e;
+            rc = run_stage(h, ST_APPEND, [&] {
+                return launch_append_rows(h->stream, isrc + (size_t)s * n * kIdxDim, ksrc + (size_t)s * n * kKvDim,
+                                          idx_layer, pool_layer_dev, ntok_layer, seq0 + s, e - s, n, h->cap,
+                                          (int32_t)base);
+            });
+            if (rc != SKO_OK) return rc;
+            s = e;
+        }
+    } else {
+        for (int s = 0; s < nseq; ++s) {
+            const int b = seq0 + s;
+            const int64_t base = h->ntok[h->lb(layer, b)];
+            std::memcpy(h->pool_host + (h->lb(layer, b) * h->cap + base) * kKvDim, ksrc + (size_t)s * n * kKvDim,
+                        (size_t)n * kKvRowBytes);
+            hipError_t e = hipMemcpyAsync(idx_layer + ((size_t)b * h->cap + base) * kIdxDim,
+                                          isrc + (size_t)s * n * kIdxDim, (size_t)n * kIdxDim * 2,
+                                          hipMemcpyHostToDevice, h->stream);
+            if (e != hipSuccess) return device_fail(h, e, "indexer rows host->device");
+            e = launch_set_ntok(h->stream, ntok_layer, b, 1, (int32_t)(base + n));
+            if (e != hipSuccess) return device_fail(h, e, "set token count");
+        }
+        // the caller may reuse its host rows once the call returns
+        hipError_t e = hipStreamSynchronize(h->stream);
+        if (e != hipSuccess) return device_fail(h, e, "append sync");
+    }
+    for (int s = 0; s < nseq; ++s) h->ntok[h->lb(layer, seq0 + s)] += n;
+    return SKO_OK;
+}
+
+int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void* q_attn, float* out) {
+    int rc = check_handle(h);
+    if (rc != SKO_OK) return rc;
+    if (layer < 0 || layer >= h->L) return set_err(SKO_E_INVAL, "layer %d out of range [0, %d)", layer, h->L);
+    if (!q_idx || !q_attn || !out) return set_err(SKO_E_INVAL, "NULL query or output pointer");
+    DeviceGuard guard(h->cfg.device);
+    if (!guard.ok) return device_fail(h, hipErrorInvalidDevice, "hipSetDevice");
+
+    const int B = h->B, D = h->D, k = h->k, S = h->S, H = h->H;
+    const int64_t cap = h->cap;
+    int64_t max_now = 0;
+    for (int b = 0; b < B; ++b) max_now = std::max(max_now, h->ntok[h->lb(layer, b)]);
+    const int32_t t = h->step[layer];
+    const size_t LBc = (size_t)layer * B * cap;
+    const size_t LBs = (size_t)layer * B * S;
+    const uint16_t* idx_layer = h->idx + LBc * kIdxDim;
+    const uint16_t* pool_layer = h->pool_dev + LBc * kKvDim;
+    uint16_t* hot_layer = h->hot + LBs * kKvDim;
+    int32_t* cs = h->cache_slots + LBc;
+    int32_t* st = h->slot_token + LBs;
+    int32_t* lu = h->last_use + LBs;
+    const int32_t* ntok = h->ntok_dev + (size_t)layer * B;
+    const uint16_t* qi = static_cast<const uint16_t*>(q_idx);
+    const uint16_t* qa = static_cast<const uint16_t*>(q_attn);
+
+    if ((rc = run_stage(h, ST_INIT, [&] { return launch_step_init(h->stream, h->hist, h->meta, h->gtotal, B * D); })))
+        return rc;
+    if ((rc = run_stage(h, ST_SCORE, [&] {
+             return launch_score_hist(h->stream, idx_layer, qi, ntok, h->keys, h->hist, B, D, cap, max_now, k);
+         })))
+        return rc;
+    if ((rc = run_stage(h, ST_THRESH, [&] { return launch_topk_threshold(h->stream, h->hist, h->meta, ntok, B, D, k); })))
+        return rc;
+    if ((rc = run_stage(h, ST_FILTER, [&] {
+             return launch_topk_filter(h->stream, h->keys, h->meta, h->cand, h->topk, cs, ntok, B, D, cap, k, max_now);
+         })))
+        return rc;
+    if ((rc = run_stage(h, ST_REFINE, [&] {
+             return launch_topk_refine(h->stream, h->cand, h->meta, h->topk, cs, B, D, cap, k);
+         })))
+        return rc;
+    if ((rc = run_stage(h, ST_MERGE_LRU, [&] {
+             return launch_merge_lru(h->stream, h->topk, ntok, cs, st, lu, B, D, k, S, cap, t, h->misses,
+                                     h->victims, h->evict_old, h->counts, h->glist, h->gtotal,
+                                     h->stats + (size_t)layer * 8);
+         })))
+        return rc;
+    if ((rc = run_stage(h, ST_GATHER, [&] {
+             return launch_gather_misses(h->stream, h->glist, h->gtotal, pool_layer, hot_layer, B * D * k);
+         })))
+        return rc;
+    if ((rc = run_stage(h, ST_ATTN, [&] {
+             return launch_attn_partial(h->stream, h->topk, cs, hot_layer, qa, ntok, h->part_acc, h->part_ml,
+                                        h->phys, B, D, H, k, S, cap, h->rows_per_block, h->cfg.attn_scale);
+         })))
+        return rc;
+    if ((rc = run_stage(h, ST_COMBINE, [&] {
+             return launch_attn_combine(h->stream, h->part_acc, h->part_ml, out, B, D, H, h->nchunk);
+         })))
+        return rc;
+    h->step[layer] += 1;
+    h->last_layer = layer;
+    return SKO_OK;
+}
+
+int sko_read_step(sko_handle* h, int32_t which, void* dst, int64_t bytes) {
+    int rc = check_handle(h);
+    if (rc != SKO_OK) return rc;
+    if (!dst) return set_err(SKO_E_INVAL, "NULL destination");
+    const size_t BD = (size_t)h->B * h->D;
+    const void* src = nullptr;
+    size_t size = 0;
+    switch (which) {
+        case SKO_BUF_TOPK: src = h->topk; size = BD * h->k * 4; break;
+        case SKO_BUF_PHYS: src = h->phys; size = BD * h->k * 4; break;
+        case SKO_BUF_COUNTS: src = h->counts; size = (size_t)h->B * sizeof(sko_seq_counts); break;
+        case SKO_BUF_MISSES: src = h->misses; size = BD * h->k * 4; break;
+        case SKO_BUF_VICTIMS: src = h->victims; size = BD * h->k * 4; break;
+        case SKO_BUF_EVICT_OLD: src = h->evict_old; size = BD * h->k * 4; break;
+        case SKO_BUF_KEYS: src = h->keys; size = BD * h->cap * 4; break;
+        default: return set_err(SKO_E_INVAL, "unknown step buffer %d", which);
+    }
+    if ((size_t)bytes != size) return set_err(SKO_E_INVAL, "buffer %d holds %zu bytes, got %lld", which, size, (long long)bytes);
+    DeviceGuard guard(h->cfg.device);
+    hipError_t e = hipStreamSynchronize(h->stream);
+    if (e == hipSuccess) e = hipMemcpy(dst, src, size, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return device_fail(h, e, "read step buffer");
+    return SKO_OK;
+}
+
+int sko_read_table(sko_handle* h, int32_t layer, int32_t seq, int32_t which, void* dst, int64_t bytes) {
+    int rc = check_handle(h);
+    if (rc != SKO_OK) return rc;
+    if (layer < 0 || layer >= h->L || seq < 0 || seq >= h->B) return set_err(SKO_E_INVAL, "layer/seq out of range");
+    if (!dst) return set_err(SKO_E_INVAL, "NULL destination");
+    const size_t lb = h->lb(layer, seq);
+    const void* src = nullptr;
+    size_t size = 0;
+    bool host = false;
+    switch (which) {
+        case SKO_TAB_CACHE_SLOTS: src = h->cache_slots + lb * h->cap; size = (size_t)h->cap * 4; break;
+        case SKO_TAB_SLOT_TOKEN: src = h->slot_token + lb * h->S; size = (size_t)h->S * 4; break;
+        case SKO_TAB_LAST_USE: src = h->last_use + lb * h->S; size = (size_t)h->S * 4; break;
+        case SKO_TAB_HOT: src = h->hot + lb * h->S * kKvDim; size = (size_t)h->S * kKvRowBytes; break;
+        case SKO_TAB_INDEXER: src = h->idx + lb * h->cap * kIdxDim; size = (size_t)h->cap * kIdxDim * 2; break;
+        case SKO_TAB_POOL: src = h->pool_host + lb * h->cap * kKvDim; size = (size_t)h->cap * kKvRowBytes; host = true; break;
+        case SKO_TAB_NTOK: size = 8; break;
+        default: return set_err(SKO_E_INVAL, "unknown table %d", which);
+    }
+    if ((size_t)bytes != size) return set_err(SKO_E_INVAL, "table %d holds %zu bytes, got %lld", which, size, (long long)bytes);
+    DeviceGuard guard(h->cfg.device);
+    hipError_t e = hipStreamSynchronize(h->stream);
+    if (e != hipSuccess) return device_fail(h, e, "read table sync");
+    if (which == SKO_TAB_NTOK) {
+        int64_t v = h->ntok[lb];
+        std::memcpy(dst, &v, 8);
+    } else if (host) {
+        std::memcpy(dst, src, size);
+    } else {
+        e = hipMemcpy(dst, src, size, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return device_fail(h, e, "read table");
+    }
+    return SKO_OK;
+}
+
+int sko_get_stats(sko_handle* h, int32_t layer, sko_layer_stats* out) {
+    int rc = check_handle(h);
+    if (rc != SKO_OK) return rc;
+    if (layer < 0 || layer >= h->L || !out) return set_err(SKO_E_INVAL, "bad layer or NULL output");
+    DeviceGuard guard(h->cfg.device);
+    unsigned long long v[8];
+    hipError_t e = hipStreamSynchronize(h->stream);
+    if (e == hipSuccess) e = hipMemcpy(v, h->stats + (size_t)layer * 8, sizeof(v), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return device_fail(h, e, "read stats");
+    out->steps = (int64_t)v[0];
+    out->unique = (int64_t)v[1];
+    out->hits = (int64_t)v[2];
+    out->misses = (int64_t)v[3];
+    out->evictions = (int64_t)v[4];
+    out->h2d_bytes = (int64_t)v[3] * kKvRowBytes;
+    return SKO_OK;
+}
+
+int sko_set_timing(sko_handle* h, int32_t enable) {
+    int rc = check_handle(h);
+    if (rc != SKO_OK) return rc;
+    DeviceGuard guard(h->cfg.device);
+    (void)hipStreamSynchronize(h->stream);
+    for (auto& p : h->pending) {
+        h->spare.push_back(p.a);
+        h->spare.push_back(p.b);
+    }
+    h->pending.clear();
+    for (int i = 0; i < ST_COUNT; ++i) {
+        h->total_ms[i] = 0.0;
+        h->launches[i] = 0;
+    }
+    h->timing = enable != 0;
+    return SKO_OK;
+}
+
+int sko_get_timing(sko_handle* h, double* total_ms, int64_t* launches, int32_t n) {
+    int rc = check_handle(h);
+    if (rc != SKO_OK) return rc;
+    if (n < 0 || (n > 0 && (!total_ms || !launches))) return set_err(SKO_E_INVAL, "bad timing output");
+    DeviceGuard guard(h->cfg.device);
+    hipError_t e = hipStreamSynchronize(h->stream);
+    if (e != hipSuccess) return device_fail(h, e, "timing sync");
+    for (auto& p : h->pending) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+            h->total_ms[p.stage] += ms;
+            h->launches[p.stage] += 1;
+        }
+        h->spare.push_back(p.a);
+        h->spare.push_back(p.b);
+    }
+    h->pending.clear();
+    for (int i = 0; i < n && i < ST_COUNT; ++i) {
+        total_ms[i] = h->total_ms[i];
+        launches[i] = h->launches[i];
+    }
+    return SKO_OK;
+}
+
+void sko_destroy(sko_handle* h) {
+    if (!h) return;
+    {
+        DeviceGuard guard(h->cfg.device);
+        (void)hipStreamSynchronize(h->stream);
+        free_all(h);
+    }
+    delete h;
+}
+
+}  // extern "C"
