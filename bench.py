@@ -89,6 +89,8 @@ def main() -> int:
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="time without per-stage events")
+    ap.add_argument("--pool", choices=["default", "coherent", "noncoherent"], default="default",
+                    help="host-pool allocation mode")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -110,8 +112,10 @@ def main() -> int:
     B, D, H, k = w.batch, w.positions, w.heads, w.top_k
 
     t_setup = time.perf_counter()
+    flags = {"default": 0, "coherent": sko.SKO_FLAG_POOL_COHERENT,
+             "noncoherent": sko.SKO_FLAG_POOL_NONCOHERENT}[args.pool]
     cfg = sko.make_config(num_layers=L, batch=B, max_tokens=w.capacity, num_heads=H, top_k=k,
-                          hot_slots=w.hot_slots, mtp_positions=D)
+                          hot_slots=w.hot_slots, mtp_positions=D, flags=flags)
     h = sko.SparseKVOffload(cfg, stream)
     chunk = 65536
     for l in range(L):
@@ -212,7 +216,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "layers": L, "batch": B, "context": w.context,
                    "top_k": k, "hot_slots": w.hot_slots, "mtp_positions": D, "heads": H,
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)", "pool": args.pool},
         "tokens_per_s": round(B * K / elapsed, 2),
         "indexer_scan_GBps": rooflines.get("score_hist", {}).get("achieved"),
         "miss_gather_GBps": rooflines.get("gather_misses", {}).get("achieved"),

@@ -57,6 +57,11 @@ extern "C" {
 #define SKO_V_DIM 512
 #define SKO_MAX_MERGE 8192 /* limit on mtp_positions * top_k */
 
+/* sko_config.flags: host-pool allocation mode (at most one). Default: the
+ * HIP runtime's default coherence for mapped pinned memory. */
+#define SKO_FLAG_POOL_COHERENT 0x1u    /* fine-grained: device reads bypass its caches */
+#define SKO_FLAG_POOL_NONCOHERENT 0x2u /* coarse-grained: device may cache pool lines */
+
 typedef struct sko_handle sko_handle;
 
 typedef struct sko_config {
@@ -72,7 +77,7 @@ typedef struct sko_config {
     int32_t mtp_positions; /* D >= 1 query positions per step (MTP3 = 4) */
     float attn_scale;      /* finite, > 0; usually 1/sqrt(576) */
     int32_t device;        /* HIP device ordinal */
-    uint32_t flags;        /* must be 0 */
+    uint32_t flags;        /* SKO_FLAG_* bits, 0 = defaults */
 } sko_config;
 
 /* Per-sequence counters of the most recent sko_decode_step on a layer. */
@@ -109,7 +114,8 @@ typedef struct sko_layer_stats {
  * plus per-step scratch.  `stream` is a hipStream_t (NULL = null stream)
  * owned by the caller.  On error *out = NULL and nothing leaks.
  * Errors: SKO_E_INVAL (NULL pointer, a dimension other than 64/576/512,
- * L/B/H/k/D < 1, S < D*k, cap out of range, bad scale, flags != 0),
+ * L/B/H/k/D < 1, S < D*k, cap out of range, bad scale, unknown or
+ * conflicting flags),
  * SKO_E_UNSUPPORTED (D*k > SKO_MAX_MERGE), SKO_E_NOMEM, SKO_E_DEVICE.
  */
 int sko_create(const sko_config* cfg, void* stream, sko_handle** out);

@@ -31,6 +31,8 @@ SKO_E_UNSUPPORTED = -6
 SKO_ALL_SEQS = -1
 SKO_INDEX_DIM, SKO_KV_DIM, SKO_V_DIM = 64, 576, 512
 SKO_MAX_MERGE = 8192
+SKO_FLAG_POOL_COHERENT = 0x1
+SKO_FLAG_POOL_NONCOHERENT = 0x2
 
 SKO_BUF_TOPK, SKO_BUF_PHYS, SKO_BUF_COUNTS = 1, 2, 3
 SKO_BUF_MISSES, SKO_BUF_VICTIMS, SKO_BUF_EVICT_OLD, SKO_BUF_KEYS = 4, 5, 6, 7

@@ -185,36 +185,60 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     }
 }
 
-__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_acc,
-                                                      const float* __restrict__ part_ml,
-                                                      float* __restrict__ out, int H, int HG,
-                                                      int nchunk) {
-    const int bp = blockIdx.x, h = blockIdx.y;
+// Merge of the per-chunk partials (m, l, acc) of one (seq, position, head):
+// out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c.  Grid (B*D*H, 4):
+// a block takes 128 output columns; the chunk weights are computed once in
+// LDS and every thread then sums its column over the chunks.
+constexpr int kCombineThreads = 128;
+constexpr int kMaxChunks = 1024;
+
+__global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* __restrict__ part_acc,
+                                                                  const float* __restrict__ part_ml,
+                                                                  float* __restrict__ out, int H,
+                                                                  int HG, int nchunk) {
+    __shared__ float wgt[kMaxChunks];
+    __shared__ float red[2 * kCombineThreads / 64];
+    const int bph = blockIdx.x;
+    const int bp = bph / H, h = bph - bp * H;
     const int hg = h / kAttnHeadGroup, hl = h - hg * kAttnHeadGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const size_t pbase = ((size_t)bp * HG + hg) * nchunk;
-    float M = -INFINITY;
-    for (int c = 0; c < nchunk; ++c) {
+    float mloc = -INFINITY;
+    for (int c = tid; c < nchunk; c += kCombineThreads) {
+        const float m = part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2];
         const float l = part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2 + 1];
-        if (l > 0.0f) M = fmaxf(M, part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2]);
+        if (l > 0.0f) mloc = fmaxf(mloc, m);
     }
-    const int col = threadIdx.x * 4;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    float L = 0.0f;
-    for (int c = 0; c < nchunk; ++c) {
+    for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+    if (lane == 0) red[wid] = mloc;
+    __syncthreads();
+    const float M = fmaxf(red[0], red[1]);
+    float lsum = 0.0f;
+    for (int c = tid; c < nchunk; c += kCombineThreads) {
+        const float m = part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2];
         const float l = part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2 + 1];
-        if (!(l > 0.0f)) continue;
-        const float wgt = exp2f(part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2] - M);
-        L += wgt * l;
-        const float4 a = *reinterpret_cast<const float4*>(
-            part_acc + ((pbase + c) * kAttnHeadGroup + hl) * kVDim + col);
-        o.x += wgt * a.x;
-        o.y += wgt * a.y;
-        o.z += wgt * a.z;
-        o.w += wgt * a.w;
+        const float wc = (l > 0.0f) ? exp2f(m - M) : 0.0f;
+        wgt[c] = wc;
+        lsum += wc * l;
     }
-    const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
-    *reinterpret_cast<float4*>(out + ((size_t)bp * H + h) * kVDim + col) =
-        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+    if (lane == 0) red[2 + wid] = lsum;
+    __syncthreads();
+    const float L = red[2] + red[3];
+    const int col = blockIdx.y * kCombineThreads + tid;
+    const float* __restrict__ src = part_acc + (pbase * kAttnHeadGroup + hl) * kVDim + col;
+    const size_t cstride = (size_t)kAttnHeadGroup * kVDim;
+    float acc = 0.0f;
+    int c = 0;
+    for (; c + 8 <= nchunk; c += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(c + u) * cstride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += wgt[c + u] * v[u];
+    }
+    for (; c < nchunk; ++c) acc += wgt[c] * src[(size_t)c * cstride];
+    out[((size_t)bp * H + h) * kVDim + col] = (L > 0.0f) ? acc / L : 0.0f;
 }
 
 hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_t* cache_slots_layer,
@@ -235,8 +259,9 @@ hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_
 hipError_t launch_attn_combine(hipStream_t st, const float* part_acc, const float* part_ml,
                                float* out, int B, int D, int H, int nchunk) {
     const int HG = (H + kAttnHeadGroup - 1) / kAttnHeadGroup;
-    hipLaunchKernelGGL(k_attn_combine, dim3(B * D, H), dim3(kVDim / 4), 0, st, part_acc, part_ml,
-                       out, H, HG, nchunk);
+    if (nchunk > kMaxChunks) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_attn_combine, dim3(B * D * H, kVDim / kCombineThreads), dim3(kCombineThreads), 0,
+                       st, part_acc, part_ml, out, H, HG, nchunk);
     return hipGetLastError();
 }
 

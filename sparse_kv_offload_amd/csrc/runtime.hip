@@ -23,6 +23,8 @@ using namespace sko;
 
 namespace {
 
+constexpr int64_t kStagingRows = 65536;  // indexer rows per host-append piece
+
 thread_local std::string g_err;
 
 int set_err(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -38,21 +40,16 @@ int set_err(int code, const char* fmt, ...) {
 
 enum Stage {
     ST_APPEND = 0,
-    ST_INIT,
     ST_SCORE,
-    ST_THRESH,
     ST_FILTER,
-    ST_REFINE,
     ST_MERGE_LRU,
     ST_GATHER,
     ST_ATTN,
     ST_COMBINE,
     ST_COUNT
 };
-const char* const kStageNames[ST_COUNT] = {"append_rows",  "step_init",     "score_hist",
-                                           "topk_threshold", "topk_filter", "topk_refine",
-                                           "merge_lru",    "gather_misses", "attn_partial",
-                                           "attn_combine"};
+const char* const kStageNames[ST_COUNT] = {"append_rows",   "score_hist",   "topk_filter", "merge_lru",
+                                           "gather_misses", "attn_partial", "attn_combine"};
 
 struct DeviceGuard {
     int prev = -1;
@@ -74,25 +71,32 @@ struct sko_handle {
     bool failed = false;
     int L = 0, B = 0, k = 0, S = 0, D = 0, H = 0, HG = 0;
     int64_t cap = 0;
+    int64_t ntiles = 0;  // indexer tiles of 64 tokens per sequence
+    int64_t kcap = 0;    // key row stride (cap rounded up to 16)
+    int64_t Sp = 0;      // recency-order row stride (S rounded up to 4)
+    int64_t wpr = 0;     // winner-bitmap words per sequence
 
     // offload state
     uint16_t* pool_host = nullptr;  // pinned [L][B][cap][576]
     uint16_t* pool_dev = nullptr;   // device mapping of pool_host
-    uint16_t* idx = nullptr;        // [L][B][cap][64]
+    uint16_t* idx = nullptr;        // [L][B][ntiles][8][64] x 16 B (tiled)
+    uint16_t* staging = nullptr;    // device rows for host-source appends
     uint16_t* hot = nullptr;        // [L][B][S][576]
     int32_t* cache_slots = nullptr; // [L][B][cap]
     int32_t* slot_token = nullptr;  // [L][B][S]
     int32_t* last_use = nullptr;    // [L][B][S]
+    int32_t* order[2] = {nullptr, nullptr};  // [L][B][Sp] recency order, double-buffered
     int32_t* ntok_dev = nullptr;    // [L][B]
     unsigned long long* stats = nullptr;  // [L][8]
     std::vector<int64_t> ntok;      // host mirror [L][B]
     std::vector<int32_t> step;      // [L]
 
     // per-step scratch (shared by all layers; steps are stream-ordered)
-    uint32_t* keys = nullptr;       // [B][D][cap]
+    uint32_t* keys = nullptr;       // [B][D][kcap]
     uint32_t* hist = nullptr;       // [B][D][4096]
     RowMeta* meta = nullptr;        // [B][D]
     uint2* cand = nullptr;          // [B][D][cap]
+    uint32_t* winners = nullptr;    // [B][wpr] bitmap of this step's winners
     int32_t* topk = nullptr;        // [B][D][k]
     int32_t* phys = nullptr;        // [B][D][k]
     int32_t* misses = nullptr;      // [B][D*k]
@@ -100,7 +104,6 @@ struct sko_handle {
     int32_t* evict_old = nullptr;   // [B][D*k]
     int32_t* counts = nullptr;      // [B][8]
     GatherEntry* glist = nullptr;   // [B*D*k]
-    uint32_t* gtotal = nullptr;     // [1]
     float* part_acc = nullptr;      // [B*D][HG][nchunk][16][512]
     float* part_ml = nullptr;       // [B*D][HG][nchunk][16][2]
     int rows_per_block = 32, nchunk = 1;
@@ -202,8 +205,13 @@ int validate_config(const sko_config* c) {
                        (long long)c->mtp_positions * c->top_k);
     if (!(c->attn_scale > 0.0f) || !std::isfinite(c->attn_scale))
         return set_err(SKO_E_INVAL, "attn_scale must be finite and > 0");
-    if (c->flags != 0) return set_err(SKO_E_INVAL, "flags must be 0");
+    if ((c->flags & ~(SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT)) != 0 ||
+        (c->flags & (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT)) ==
+            (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT))
+        return set_err(SKO_E_INVAL, "unknown or conflicting flags 0x%x", c->flags);
     if (c->device < 0) return set_err(SKO_E_INVAL, "device must be >= 0");
+    if (c->hot_slots > kMaxHotSlots)
+        return set_err(SKO_E_UNSUPPORTED, "hot_slots above %d", kMaxHotSlots);
     if ((int64_t)c->mtp_positions * c->top_k > SKO_MAX_MERGE)
         return set_err(SKO_E_UNSUPPORTED, "mtp_positions*top_k above %d", SKO_MAX_MERGE);
     if ((int64_t)c->batch * c->max_tokens >= 0xFFFFFFFFLL || (int64_t)c->batch * c->hot_slots >= 0xFFFFFFFFLL)
@@ -254,6 +262,10 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     h->H = cfg->num_heads;
     h->HG = (h->H + kAttnHeadGroup - 1) / kAttnHeadGroup;
     h->cap = cfg->max_tokens;
+    h->ntiles = (h->cap + kIdxTile - 1) / kIdxTile;
+    h->kcap = (h->cap + 15) / 16 * 16;
+    h->Sp = ((int64_t)h->S + 3) / 4 * 4;
+    h->wpr = (h->cap + 31) / 32;
     h->ntok.assign((size_t)h->L * h->B, 0);
     h->step.assign((size_t)h->L, 0);
     h->rows_per_block = attn_rows_per_block(h->k, h->B * h->D * h->HG);
@@ -262,7 +274,10 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     const size_t LB = (size_t)h->L * h->B;
     const size_t BD = (size_t)h->B * h->D;
     const size_t pool_bytes = LB * (size_t)h->cap * kKvRowBytes;
-    if (hipHostMalloc((void**)&h->pool_host, pool_bytes, hipHostMallocMapped) != hipSuccess) {
+    unsigned pool_flags = hipHostMallocMapped;
+    if (cfg->flags & SKO_FLAG_POOL_COHERENT) pool_flags |= hipHostMallocCoherent;
+    if (cfg->flags & SKO_FLAG_POOL_NONCOHERENT) pool_flags |= hipHostMallocNonCoherent;
+    if (hipHostMalloc((void**)&h->pool_host, pool_bytes, pool_flags) != hipSuccess) {
         (void)hipGetLastError();
         h->pool_host = nullptr;
         free_all(h);
@@ -276,14 +291,18 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
         return set_err(SKO_E_DEVICE, "hipHostGetDevicePointer on the host pool failed");
     }
     bool ok = true;
-    ok = ok && dev_alloc(h, (void**)&h->idx, LB * h->cap * kIdxDim * 2);
+    ok = ok && dev_alloc(h, (void**)&h->idx, LB * h->ntiles * kIdxTile * kIdxDim * 2);
+    ok = ok && dev_alloc(h, (void**)&h->staging, (size_t)kStagingRows * kIdxDim * 2);
     ok = ok && dev_alloc(h, (void**)&h->hot, LB * h->S * (size_t)kKvRowBytes);
     ok = ok && dev_alloc(h, (void**)&h->cache_slots, LB * h->cap * 4);
     ok = ok && dev_alloc(h, (void**)&h->slot_token, LB * h->S * 4);
     ok = ok && dev_alloc(h, (void**)&h->last_use, LB * h->S * 4);
+    ok = ok && dev_alloc(h, (void**)&h->order[0], LB * h->Sp * 4);
+    ok = ok && dev_alloc(h, (void**)&h->order[1], LB * h->Sp * 4);
     ok = ok && dev_alloc(h, (void**)&h->ntok_dev, LB * 4);
     ok = ok && dev_alloc(h, (void**)&h->stats, (size_t)h->L * 8 * 8);
-    ok = ok && dev_alloc(h, (void**)&h->keys, BD * h->cap * 4);
+    ok = ok && dev_alloc(h, (void**)&h->keys, BD * h->kcap * 4);
+    ok = ok && dev_alloc(h, (void**)&h->winners, (size_t)h->B * h->wpr * 4);
     ok = ok && dev_alloc(h, (void**)&h->hist, BD * kHistBins * 4);
     ok = ok && dev_alloc(h, (void**)&h->meta, BD * sizeof(RowMeta));
     ok = ok && dev_alloc(h, (void**)&h->cand, BD * h->cap * sizeof(uint2));
@@ -294,7 +313,6 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     ok = ok && dev_alloc(h, (void**)&h->evict_old, BD * h->k * 4);
     ok = ok && dev_alloc(h, (void**)&h->counts, (size_t)h->B * 8 * 4);
     ok = ok && dev_alloc(h, (void**)&h->glist, BD * h->k * sizeof(GatherEntry));
-    ok = ok && dev_alloc(h, (void**)&h->gtotal, 4);
     ok = ok && dev_alloc(h, (void**)&h->part_acc, BD * h->HG * h->nchunk * kAttnHeadGroup * kVDim * 4);
     ok = ok && dev_alloc(h, (void**)&h->part_ml, BD * h->HG * h->nchunk * kAttnHeadGroup * 2 * 4);
     if (!ok) {
@@ -312,6 +330,12 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     if (e == hipSuccess) e = hipMemsetAsync(h->stats, 0, (size_t)h->L * 8 * 8, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->topk, 0, BD * h->k * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->counts, 0, (size_t)h->B * 8 * 4, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->winners, 0, (size_t)h->B * h->wpr * 4, h->stream);
+    // selection scratch starts cleared; every step's merge clears it again
+    if (e == hipSuccess) e = hipMemsetAsync(h->hist, 0, BD * kHistBins * 4, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->meta, 0, BD * sizeof(RowMeta), h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->idx, 0, LB * h->ntiles * kIdxTile * kIdxDim * 2, h->stream);
+    if (e == hipSuccess) e = launch_init_order(h->stream, h->order[0], (int64_t)LB, h->S);
     if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
     if (e != hipSuccess) {
         set_err(SKO_E_DEVICE, "initialising state: %s", hipGetErrorString(e));
@@ -350,7 +374,7 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
     DeviceGuard guard(h->cfg.device);
     if (!guard.ok) return device_fail(h, hipErrorInvalidDevice, "hipSetDevice");
 
-    uint16_t* idx_layer = h->idx + (size_t)layer * h->B * h->cap * kIdxDim;
+    uint16_t* idx_layer = h->idx + (size_t)layer * h->B * h->ntiles * kIdxTile * kIdxDim;
     uint16_t* pool_layer_dev = h->pool_dev + (size_t)layer * h->B * h->cap * kKvDim;
     int32_t* ntok_layer = h->ntok_dev + (size_t)layer * h->B;
     const uint16_t* isrc = static_cast<const uint16_t*>(idx_rows);
@@ -366,7 +390,7 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
             rc = run_stage(h, ST_APPEND, [&] {
                 return launch_append_rows(h->stream, isrc + (size_t)s * n * kIdxDim, ksrc + (size_t)s * n * kKvDim,
                                           idx_layer, pool_layer_dev, ntok_layer, seq0 + s, e - s, n, h->cap,
-                                          (int32_t)base);
+                                          h->ntiles, (int32_t)base);
             });
             if (rc != SKO_OK) return rc;
             s = e;
@@ -377,12 +401,16 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
             const int64_t base = h->ntok[h->lb(layer, b)];
             std::memcpy(h->pool_host + (h->lb(layer, b) * h->cap + base) * kKvDim, ksrc + (size_t)s * n * kKvDim,
                         (size_t)n * kKvRowBytes);
-            hipError_t e = hipMemcpyAsync(idx_layer + ((size_t)b * h->cap + base) * kIdxDim,
-                                          isrc + (size_t)s * n * kIdxDim, (size_t)n * kIdxDim * 2,
-                                          hipMemcpyHostToDevice, h->stream);
-            if (e != hipSuccess) return device_fail(h, e, "indexer rows host->device");
-            e = launch_set_ntok(h->stream, ntok_layer, b, 1, (int32_t)(base + n));
-            if (e != hipSuccess) return device_fail(h, e, "set token count");
+            // indexer rows: host -> staging rows -> tiled cache, in pieces
+            for (int64_t r0 = 0; r0 < n; r0 += kStagingRows) {
+                const int64_t m = std::min<int64_t>(kStagingRows, n - r0);
+                hipError_t e = hipMemcpyAsync(h->staging, isrc + ((size_t)s * n + r0) * kIdxDim,
+                                              (size_t)m * kIdxDim * 2, hipMemcpyHostToDevice, h->stream);
+                if (e != hipSuccess) return device_fail(h, e, "indexer rows host->device");
+                e = launch_append_rows(h->stream, h->staging, nullptr, idx_layer, nullptr, ntok_layer, b, 1, m,
+                                       h->cap, h->ntiles, (int32_t)(base + r0));
+                if (e != hipSuccess) return device_fail(h, e, "indexer rows to tiles");
+            }
         }
         // the caller may reuse its host rows once the call returns
         hipError_t e = hipStreamSynchronize(h->stream);
@@ -407,7 +435,7 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
     const int32_t t = h->step[layer];
     const size_t LBc = (size_t)layer * B * cap;
     const size_t LBs = (size_t)layer * B * S;
-    const uint16_t* idx_layer = h->idx + LBc * kIdxDim;
+    const uint16_t* idx_layer = h->idx + (size_t)layer * B * h->ntiles * kIdxTile * kIdxDim;
     const uint16_t* pool_layer = h->pool_dev + LBc * kKvDim;
     uint16_t* hot_layer = h->hot + LBs * kKvDim;
     int32_t* cs = h->cache_slots + LBc;
@@ -417,30 +445,27 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
     const uint16_t* qi = static_cast<const uint16_t*>(q_idx);
     const uint16_t* qa = static_cast<const uint16_t*>(q_attn);
 
-    if ((rc = run_stage(h, ST_INIT, [&] { return launch_step_init(h->stream, h->hist, h->meta, h->gtotal, B * D); })))
-        return rc;
+    const int32_t* order_cur = h->order[t & 1] + (size_t)layer * B * h->Sp;
+    int32_t* order_next = h->order[(t & 1) ^ 1] + (size_t)layer * B * h->Sp;
+
     if ((rc = run_stage(h, ST_SCORE, [&] {
-             return launch_score_hist(h->stream, idx_layer, qi, ntok, h->keys, h->hist, B, D, cap, max_now, k);
+             return launch_score_hist(h->stream, idx_layer, qi, ntok, h->keys, h->hist, B, D, h->kcap, h->ntiles,
+                                      max_now);
          })))
-        return rc;
-    if ((rc = run_stage(h, ST_THRESH, [&] { return launch_topk_threshold(h->stream, h->hist, h->meta, ntok, B, D, k); })))
         return rc;
     if ((rc = run_stage(h, ST_FILTER, [&] {
-             return launch_topk_filter(h->stream, h->keys, h->meta, h->cand, h->topk, cs, ntok, B, D, cap, k, max_now);
-         })))
-        return rc;
-    if ((rc = run_stage(h, ST_REFINE, [&] {
-             return launch_topk_refine(h->stream, h->cand, h->meta, h->topk, cs, B, D, cap, k);
+             return launch_topk_filter(h->stream, h->keys, h->hist, h->meta, h->cand, h->topk, cs, ntok, h->winners,
+                                       B, D, cap, k, max_now);
          })))
         return rc;
     if ((rc = run_stage(h, ST_MERGE_LRU, [&] {
-             return launch_merge_lru(h->stream, h->topk, ntok, cs, st, lu, B, D, k, S, cap, t, h->misses,
-                                     h->victims, h->evict_old, h->counts, h->glist, h->gtotal,
-                                     h->stats + (size_t)layer * 8);
+             return launch_merge_lru(h->stream, h->winners, h->hist, h->meta, h->cand, h->topk, ntok, cs, st, lu,
+                                     order_cur, order_next, B, D, k, S, cap, t, h->misses, h->victims,
+                                     h->evict_old, h->counts, h->glist, h->stats + (size_t)layer * 8);
          })))
         return rc;
     if ((rc = run_stage(h, ST_GATHER, [&] {
-             return launch_gather_misses(h->stream, h->glist, h->gtotal, pool_layer, hot_layer, B * D * k);
+             return launch_gather_misses(h->stream, h->glist, h->counts, pool_layer, hot_layer, B, D * k, B * D * k);
          })))
         return rc;
     if ((rc = run_stage(h, ST_ATTN, [&] {
@@ -471,13 +496,17 @@ int sko_read_step(sko_handle* h, int32_t which, void* dst, int64_t bytes) {
         case SKO_BUF_MISSES: src = h->misses; size = BD * h->k * 4; break;
         case SKO_BUF_VICTIMS: src = h->victims; size = BD * h->k * 4; break;
         case SKO_BUF_EVICT_OLD: src = h->evict_old; size = BD * h->k * 4; break;
-        case SKO_BUF_KEYS: src = h->keys; size = BD * h->cap * 4; break;
+        case SKO_BUF_KEYS: src = h->keys; size = BD * h->cap * 4; break;  // de-strided below
         default: return set_err(SKO_E_INVAL, "unknown step buffer %d", which);
     }
     if ((size_t)bytes != size) return set_err(SKO_E_INVAL, "buffer %d holds %zu bytes, got %lld", which, size, (long long)bytes);
     DeviceGuard guard(h->cfg.device);
     hipError_t e = hipStreamSynchronize(h->stream);
-    if (e == hipSuccess) e = hipMemcpy(dst, src, size, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && which == SKO_BUF_KEYS)
+        e = hipMemcpy2D(dst, (size_t)h->cap * 4, src, (size_t)h->kcap * 4, (size_t)h->cap * 4, BD,
+                        hipMemcpyDeviceToHost);
+    else if (e == hipSuccess)
+        e = hipMemcpy(dst, src, size, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return device_fail(h, e, "read step buffer");
     return SKO_OK;
 }
@@ -496,7 +525,7 @@ int sko_read_table(sko_handle* h, int32_t layer, int32_t seq, int32_t which, voi
         case SKO_TAB_SLOT_TOKEN: src = h->slot_token + lb * h->S; size = (size_t)h->S * 4; break;
         case SKO_TAB_LAST_USE: src = h->last_use + lb * h->S; size = (size_t)h->S * 4; break;
         case SKO_TAB_HOT: src = h->hot + lb * h->S * kKvDim; size = (size_t)h->S * kKvRowBytes; break;
-        case SKO_TAB_INDEXER: src = h->idx + lb * h->cap * kIdxDim; size = (size_t)h->cap * kIdxDim * 2; break;
+        case SKO_TAB_INDEXER: src = h->idx + lb * h->ntiles * kIdxTile * kIdxDim; size = (size_t)h->cap * kIdxDim * 2; break;
         case SKO_TAB_POOL: src = h->pool_host + lb * h->cap * kKvDim; size = (size_t)h->cap * kKvRowBytes; host = true; break;
         case SKO_TAB_NTOK: size = 8; break;
         default: return set_err(SKO_E_INVAL, "unknown table %d", which);
@@ -508,6 +537,14 @@ int sko_read_table(sko_handle* h, int32_t layer, int32_t seq, int32_t which, voi
     if (which == SKO_TAB_NTOK) {
         int64_t v = h->ntok[lb];
         std::memcpy(dst, &v, 8);
+    } else if (which == SKO_TAB_INDEXER) {
+        // undo the 64-token tiling: [tile][chunk][token] x 16 B -> [token][chunk] x 16 B
+        std::vector<uint4> tiles((size_t)h->ntiles * kIdxRowU4 * kIdxTile);
+        e = hipMemcpy(tiles.data(), src, tiles.size() * sizeof(uint4), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return device_fail(h, e, "read table");
+        uint4* o = static_cast<uint4*>(dst);
+        for (int64_t tok = 0; tok < h->cap; ++tok)
+            for (int c = 0; c < kIdxRowU4; ++c) o[tok * kIdxRowU4 + c] = tiles[idx_tile_u4(0, tok, c)];
     } else if (host) {
         std::memcpy(dst, src, size);
     } else {

@@ -13,11 +13,23 @@ constexpr int kVDim = 512;
 constexpr int kIdxRowU4 = kIdxDim * 2 / 16;  // 8 x 16 B per indexer row
 constexpr int kKvRowU4 = kKvDim * 2 / 16;    // 72 x 16 B per main-KV row
 constexpr int kKvRowBytes = kKvDim * 2;      // 1152
+constexpr int kIdxTile = 64;                 // tokens per indexer tile (one wave)
 constexpr int kHistBits = 12;                // first radix digit of the top-k
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kMaxMerge = 8192;              // D * k limit of the merge/LRU kernel
+constexpr int kMaxHotSlots = 1 << 18;        // S limit (LDS bitmap of touched slots)
 constexpr int kAttnHeadGroup = 16;           // heads per MFMA tile (M = 16)
 constexpr int kAttnTileRows = 32;            // rows per attention tile
+constexpr int kFilterKeysPerThread = 16;
+constexpr int kFilterSpan = 256 * kFilterKeysPerThread;  // keys per block pass
+
+// Indexer cache layout in HBM (per layer): [B][ntiles][8 chunks][64 tokens]
+// x 16 bytes, so that chunk c of 64 consecutive tokens is one contiguous
+// 1 KB run: a wave reading one chunk for its 64 tokens is fully coalesced.
+__host__ __device__ inline size_t idx_tile_u4(size_t seq_tiles_base, int64_t token, int chunk) {
+    return ((seq_tiles_base + (size_t)(token / kIdxTile)) * kIdxRowU4 + chunk) * kIdxTile +
+           (size_t)(token % kIdxTile);
+}
 
 // Per (seq, position) row of the top-k selection.
 struct RowMeta {
@@ -38,32 +50,28 @@ struct GatherEntry {
 // Launchers.  All enqueue on `st`; none synchronizes.
 hipError_t launch_append_rows(hipStream_t st, const uint16_t* idx_src, const uint16_t* kv_src,
                               uint16_t* idx_layer, uint16_t* pool_layer, int32_t* ntok_layer,
-                              int seq0, int nseq, int64_t n, int64_t cap, int32_t base);
-hipError_t launch_set_ntok(hipStream_t st, int32_t* ntok_layer, int seq0, int nseq, int32_t value);
-
-hipError_t launch_step_init(hipStream_t st, uint32_t* hist, RowMeta* meta, uint32_t* gather_total,
-                            int rows);
+                              int seq0, int nseq, int64_t n, int64_t cap, int64_t ntiles,
+                              int32_t base);
 hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const uint16_t* q_idx,
-                             const int32_t* ntok_layer, uint32_t* keys, uint32_t* hist, int B,
-                             int D, int64_t cap, int64_t max_tokens_now, int top_k);
-hipError_t launch_topk_threshold(hipStream_t st, const uint32_t* hist, RowMeta* meta,
-                                 const int32_t* ntok_layer, int B, int D, int top_k);
-hipError_t launch_topk_filter(hipStream_t st, const uint32_t* keys, RowMeta* meta,
+                             const int32_t* ntok_layer, uint32_t* keys, uint32_t* hist, int B, int D,
+                             int64_t kcap, int64_t ntiles, int64_t max_tokens_now);
+hipError_t launch_topk_filter(hipStream_t st, const uint32_t* keys, const uint32_t* hist, RowMeta* meta,
                               uint2* cand, int32_t* topk, const int32_t* cache_slots_layer,
-                              const int32_t* ntok_layer, int B, int D, int64_t cap, int top_k,
-                              int64_t max_tokens_now);
-hipError_t launch_topk_refine(hipStream_t st, const uint2* cand, RowMeta* meta, int32_t* topk,
-                              const int32_t* cache_slots_layer, int B, int D, int64_t cap,
-                              int top_k);
-hipError_t launch_merge_lru(hipStream_t st, const int32_t* topk, const int32_t* ntok_layer,
+                              const int32_t* ntok_layer, uint32_t* winners, int B, int D,
+                              int64_t cap, int top_k, int64_t max_tokens_now);
+// Also finishes the top-k (split buckets) and clears the histograms and row
+// records for the next step.
+hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, RowMeta* meta,
+                            const uint2* cand, int32_t* topk, const int32_t* ntok_layer,
                             int32_t* cache_slots_layer, int32_t* slot_token_layer,
-                            int32_t* last_use_layer, int B, int D, int top_k, int S,
-                            int64_t cap, int32_t t, int32_t* misses, int32_t* victims,
-                            int32_t* evict_old, int32_t* counts, GatherEntry* glist,
-                            uint32_t* gather_total, unsigned long long* layer_stats);
-hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist,
-                                const uint32_t* gather_total, const uint16_t* pool_layer,
-                                uint16_t* hot_layer, int max_entries);
+                            int32_t* last_use_layer, const int32_t* order_cur, int32_t* order_next,
+                            int B, int D, int top_k, int S, int64_t cap, int32_t t,
+                            int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
+                            GatherEntry* glist, unsigned long long* layer_stats);
+// Work list: sequence b's entries are glist[b * D*k + r], r < counts[b][2].
+hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const int32_t* counts,
+                                const uint16_t* pool_layer, uint16_t* hot_layer, int B, int mstride,
+                                int max_entries);
 hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_t* cache_slots_layer,
                                const uint16_t* hot_layer, const uint16_t* q_attn,
                                const int32_t* ntok_layer, float* part_acc, float* part_ml,
@@ -71,5 +79,6 @@ hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_
                                int rows_per_block, float scale);
 hipError_t launch_attn_combine(hipStream_t st, const float* part_acc, const float* part_ml,
                                float* out, int B, int D, int H, int nchunk);
+hipError_t launch_init_order(hipStream_t st, int32_t* order, int64_t n_seqs, int S);
 
 }  // namespace sko

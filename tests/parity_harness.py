@@ -67,14 +67,14 @@ class GpuSide:
     """The HIP path through the C ABI (all sequences of the workload)."""
 
     def __init__(self, w: synth.Workload, layers: int, device_append: bool = True,
-                 prefix_chunk: int = 65536):
+                 prefix_chunk: int = 65536, flags: int = 0):
         import sparse_kv_offload_amd as sko
         torch = torch_mod()
         self.sko, self.torch, self.w = sko, torch, w
         self.L = layers
         cfg = sko.make_config(num_layers=layers, batch=w.batch, max_tokens=w.capacity,
                               num_heads=w.heads, top_k=w.top_k, hot_slots=w.hot_slots,
-                              mtp_positions=w.positions, attn_scale=SCALE)
+                              mtp_positions=w.positions, attn_scale=SCALE, flags=flags)
         self.stream = torch.cuda.current_stream()
         self.h = sko.SparseKVOffload(cfg, self.stream)
         self.device_append = device_append
@@ -202,13 +202,13 @@ def compare_tables(gt: Dict[str, np.ndarray], ot: Dict[str, np.ndarray], where: 
 def run_parity(w: synth.Workload, layers: Optional[int] = None, steps: Optional[int] = None,
                chains: Optional[List[tuple]] = None, check_tables_every: int = 1,
                check_keys: bool = False, device_append: bool = True, out_steps=None,
-               log=None) -> Dict[str, float]:
+               log=None, flags: int = 0) -> Dict[str, float]:
     """Run the full workload on the GPU; check the sampled chains on the CPU."""
     L = w.layers if layers is None else layers
     T = w.steps if steps is None else steps
     chains = [(l, b) for l in range(L) for b in range(w.batch)] if chains is None else chains
     inputs = Inputs(w, sorted({c[0] for c in chains} | set(range(L))), T)
-    gpu = GpuSide(w, L, device_append=device_append)
+    gpu = GpuSide(w, L, device_append=device_append, flags=flags)
     ora = OracleSide(w, chains)
     worst = {"abs": 0.0, "rel_rms": 0.0}
     try:

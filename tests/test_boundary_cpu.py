@@ -47,7 +47,8 @@ def good_cfg(sko, **kw):
     dict(index_dim=32), dict(kv_dim=512), dict(v_dim=576), dict(num_layers=0), dict(batch=0),
     dict(num_heads=0), dict(top_k=0), dict(mtp_positions=0), dict(max_tokens=0),
     dict(max_tokens=2 ** 31), dict(hot_slots=127), dict(attn_scale=0.0),
-    dict(attn_scale=float("inf")), dict(attn_scale=float("nan")), dict(flags=1), dict(device=-1),
+    dict(attn_scale=float("inf")), dict(attn_scale=float("nan")), dict(flags=4), dict(flags=3),
+    dict(device=-1),
 ])
 def test_create_rejects_bad_config(bad):
     import sparse_kv_offload_amd as sko
@@ -81,7 +82,7 @@ def test_calls_on_null_handle_fail_cleanly():
 def test_stage_names():
     import sparse_kv_offload_amd as sko
     names = [sko.sko_stage_name(i) for i in range(sko.sko_num_stages())]
-    assert names[:3] == ["append_rows", "step_init", "score_hist"]
+    assert names[:3] == ["append_rows", "score_hist", "topk_filter"]
     assert "gather_misses" in names and "attn_partial" in names
     assert sko.sko_stage_name(99) == ""
     assert "gfx950" in sko.sko_version()

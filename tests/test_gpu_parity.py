@@ -61,11 +61,28 @@ def test_ragged_batch(device_append):
     run_parity(w, check_keys=True, device_append=device_append, log=log)
 
 
+@pytest.mark.parametrize("pool", ["coherent", "noncoherent"])
+def test_pool_modes(pool):
+    """Both host-pool allocation modes give identical results."""
+    import sparse_kv_offload_amd as sko
+    flags = {"coherent": sko.SKO_FLAG_POOL_COHERENT, "noncoherent": sko.SKO_FLAG_POOL_NONCOHERENT}[pool]
+    w = case("pool", batch=3, context=2500, steps=10, top_k=128, hot_slots=300, positions=2, heads=16)
+    log(f"case pool={pool}")
+    run_parity(w, check_keys=True, flags=flags, log=log)
+
+
 def test_minimum_shelf():
     """S == D*k: every non-hit slot is a victim candidate each step."""
     w = case("minshelf", batch=2, context=900, steps=20, top_k=64, hot_slots=128, positions=2, heads=3)
     log("case minshelf")
     run_parity(w, log=log)
+
+
+def test_five_positions():
+    """D = 5: the score runs two position groups (4 + 1)."""
+    w = case("d5", batch=2, context=1200, steps=8, top_k=40, hot_slots=230, positions=5, heads=7)
+    log("case d5")
+    run_parity(w, check_keys=True, log=log)
 
 
 def test_k_equals_one():
