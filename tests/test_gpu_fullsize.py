@@ -1,0 +1,67 @@
+"""Parity at the full workload sizes, in the benchmark's launch configuration.
+
+The GPU runs every sequence of the workload at its real per-layer shape (the
+same kernels and grids the benchmark times); the oracle replays sampled
+(layer, seq) chains one by one (chains are independent, so a chain replayed
+alone is the full workload restricted to it).  Every step is compared
+bit-exactly on selection, counts, misses and evictions; attention is checked
+on a few steps; residency tables and hot-buffer bytes every few steps.
+
+Layer counts are reduced where the full count only repeats identical
+launches on more memory (mtp3: 2 of 4, shelf: 2 of 8); step counts are cut
+to what the oracle replays in well under a minute, always including the
+cold first step.
+"""
+import pytest
+
+import synth
+from parity_harness import run_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_kv_offload_amd  # noqa: F401
+    yield
+
+
+def _run(w, layers, steps, chains, out_steps, tables_every):
+    log(f"fullsize {w.name}: layers={layers} batch={w.batch} context={w.context} k={w.top_k} "
+        f"S={w.hot_slots} D={w.positions} H={w.heads} steps={steps} chains={chains}")
+    worst = run_parity(w, layers=layers, steps=steps, chains=chains, out_steps=set(out_steps),
+                       check_tables_every=tables_every, log=log)
+    log(f"fullsize {w.name}: ok, attention worst {worst}")
+
+
+def test_small_full():
+    w = synth.SMALL
+    _run(w, layers=4, steps=w.steps, chains=[(0, 0), (3, 7)], out_steps=[0, 1, 31, 63],
+         tables_every=16)
+
+
+def test_mtp3_full_shape():
+    w = synth.MTP3
+    _run(w, layers=2, steps=24, chains=[(0, 3), (1, 15)], out_steps=[0, 23], tables_every=8)
+
+
+def test_shelf_ctx8_across_topic_jump():
+    w = synth.SHELF8
+    _run(w, layers=2, steps=70, chains=[(1, 31)], out_steps=[0, 64, 69], tables_every=32)
+
+
+def test_shelf_ctx4_full_shape():
+    w = synth.SHELF4
+    _run(w, layers=1, steps=20, chains=[(0, 5)], out_steps=[0, 19], tables_every=10)
+
+
+def test_long_full_shape():
+    w = synth.LONG
+    _run(w, layers=2, steps=10, chains=[(1, 1)], out_steps=[0, 9], tables_every=5)
