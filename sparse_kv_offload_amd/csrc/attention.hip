@@ -10,12 +10,14 @@
 //
 // Layout of the work: a block takes one (seq, position), one group of 16
 // heads and a chunk of winners.  Rows are staged 32 at a time in LDS (one
-// coalesced 1152-byte read each, gathered by slot).  Every wave computes
-// S^T = K Q^T for the 32 rows with v_mfma_f32_16x16x32_bf16 (M = 16 rows,
-// N = 16 heads, K = 576), runs the online softmax, and accumulates
-// O^T = V^T P^T for its own 128 of the 512 output columns (M = 16 columns,
-// N = 16 heads, K = 32 rows).  P enters the MFMA in bf16; accumulation is
-// fp32.  Each block writes (m, l, acc) partials; k_attn_combine merges them.
+// coalesced 1152-byte read each, gathered by slot); the next tile is fetched
+// into registers while the current one is computed.  The four waves split
+// the 576-deep contraction S^T = K Q^T (v_mfma_f32_16x16x32_bf16, M = 16
+// rows, N = 16 heads) and add their partial tiles through LDS; each wave
+// then runs the online softmax and accumulates O^T = V^T P^T for its own
+// 128 of the 512 output columns (M = 16 columns, N = 16 heads, K = 32
+// rows).  P enters the MFMA in bf16; accumulation is fp32.  Each block
+// writes (m, l, acc) partials; k_attn_combine merges them.
 #include "sko_common.cuh"
 #include "sko_internal.h"
 
@@ -40,7 +42,8 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     float* __restrict__ part_ml, int32_t* __restrict__ phys, int D, int H, int HG, int top_k,
     int S, int64_t cap, int rows_per_block, int nchunk, float scale_log2) {
     __shared__ uint4 rows[kAttnTileRows * kRowStrideU4];
-    __shared__ int32_t slot_s[kAttnTileRows];
+    __shared__ int32_t slot_s[kAttnMaxRowsPerBlock];
+    __shared__ f32x4_t sp[4][2][64];  // per-wave partial S^T tiles
 
     const int chunk = blockIdx.x, bp = blockIdx.y, hg = blockIdx.z;
     const int b = bp / D;
@@ -61,54 +64,90 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     }
     const int n16 = lane & 15, g = lane >> 4;
     const int h = hg * kAttnHeadGroup + n16;
+    const int32_t* __restrict__ w = topk + (size_t)bp * top_k;
+    const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
+    const uint4* __restrict__ hb = hot_layer + (size_t)b * S * kKvRowU4;
 
-    // B operand of S^T = K Q^T: lane (n16, g) holds Q[h][32ks + 8g .. +7]
-    uint4 qv[kKvDim / 32];
-    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+    // remap: logical winner -> hot slot, for the whole chunk
+    for (int j = tid; j < r1 - r0; j += 256) {
+        const int32_t tok = w[r0 + j] & 0x7FFFFFFF;
+        int32_t slot = (tok < cap) ? cs[tok] : -1;
+        if (slot >= S) slot = -1;
+        slot_s[j] = slot;
+        if (hg == 0) phys[(size_t)bp * top_k + r0 + j] = slot;
+    }
+
+    // The 18 k-steps (32 columns each) of S^T = K Q^T are split over the 4
+    // waves (5, 5, 4, 4); wave w holds the B operand Q^T of its k-steps:
+    // lane (n16, g) holds Q[h][32ks + 8g .. +7].
+    const int ks0 = wave < 2 ? 5 * wave : 10 + 4 * (wave - 2);
+    const int nks = wave < 2 ? 5 : 4;
+    uint4 qv[5];
 #pragma unroll
-    for (int ks = 0; ks < kKvDim / 32; ++ks)
-        qv[ks] = (h < H) ? q_attn[((size_t)bp * H + h) * kKvRowU4 + 4 * ks + g] : zero4;
+    for (int q = 0; q < 5; ++q) {
+        // loads stay in bounds (clamped head and step); the select zeroes
+        // padding heads and the fifth step of waves that own four
+        const int hq = h < H ? h : H - 1;
+        const int kq = q < nks ? ks0 + q : ks0;
+        const uint4 v = q_attn[((size_t)bp * H + hq) * kKvRowU4 + 4 * kq + g];
+        qv[q] = (h < H && q < nks) ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
 
     f32x4_t acc[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
-    const int32_t* __restrict__ w = topk + (size_t)bp * top_k;
-    const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
-    const uint4* __restrict__ hb = hot_layer + (size_t)b * S * kKvRowU4;
+    __syncthreads();
+
+    // rows of a tile: 32 x 72 chunks of 16 bytes, 9 per thread; the next
+    // tile is fetched into registers while the current one is computed
+    constexpr int kPer = kAttnTileRows * kKvRowU4 / 256;
+    uint4 pre[kPer];
+    // 16-byte chunk u of this thread: row rr_u, part pt_u of the tile
+#define SKO_FETCH(rbase)                                                             \
+    _Pragma("unroll") for (int u = 0; u < kPer; ++u) {                              \
+        const int idx = tid + 256 * u;                                              \
+        const int rr = idx / kKvRowU4;                                              \
+        const int j = (rbase) + rr;                                                 \
+        const int32_t slot = (j < r1) ? slot_s[j - r0] : -1;                        \
+        const uint4 v = hb[(size_t)(slot >= 0 ? slot : 0) * kKvRowU4 + (idx - rr * kKvRowU4)]; \
+        pre[u] = (slot >= 0) ? v : make_uint4(0u, 0u, 0u, 0u);                      \
+    }
+#define SKO_STASH()                                                   \
+    _Pragma("unroll") for (int u = 0; u < kPer; ++u) {               \
+        const int idx = tid + 256 * u;                               \
+        const int rr = idx / kKvRowU4;                               \
+        rows[rr * kRowStrideU4 + (idx - rr * kKvRowU4)] = pre[u];    \
+    }
+    SKO_FETCH(r0)
+    SKO_STASH()
+    __syncthreads();
 
     for (int r = r0; r < r1; r += kAttnTileRows) {
-        // remap: logical winner -> hot slot
-        if (tid < kAttnTileRows) {
-            const int j = r + tid;
-            int32_t slot = -1;
-            if (j < r1) {
-                const int32_t tok = w[j] & 0x7FFFFFFF;
-                slot = (tok < cap) ? cs[tok] : -1;
-                if (slot >= S) slot = -1;
-                if (hg == 0) phys[(size_t)bp * top_k + j] = slot;
-            }
-            slot_s[tid] = slot;
+        const bool more = r + kAttnTileRows < r1;
+        if (more) {
+            SKO_FETCH(r + kAttnTileRows)
         }
-        __syncthreads();
-        for (int idx = tid; idx < kAttnTileRows * kKvRowU4; idx += 256) {
-            const int rr = idx / kKvRowU4;
-            const int part = idx - rr * kKvRowU4;
-            const int32_t slot = slot_s[rr];
-            rows[rr * kRowStrideU4 + part] = (slot >= 0) ? hb[(size_t)slot * kKvRowU4 + part] : zero4;
-        }
-        __syncthreads();
 
         // S^T tiles for rows r..r+15 and r+16..r+31; lane holds head n16,
-        // rows 4g+i (+16)
-        float s[2][4];
+        // rows 4g+i (+16).  Each wave forms its k-steps' partial sums; the
+        // four partials are added in wave order (the same in every wave).
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             f32x4_t c = {0.f, 0.f, 0.f, 0.f};
             const uint4* rp = rows + (half * 16 + n16) * kRowStrideU4 + g;
 #pragma unroll
-            for (int ks = 0; ks < kKvDim / 32; ++ks)
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rp[4 * ks]), as_bf16x8(qv[ks]), c, 0, 0, 0);
+            for (int q = 0; q < 5; ++q)
+                if (q < nks)
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rp[4 * (ks0 + q)]), as_bf16x8(qv[q]), c,
+                                                                0, 0, 0);
+            sp[wave][half][lane] = c;
+        }
+        __syncthreads();
+        float s[2][4];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const f32x4_t c = ((sp[0][half][lane] + sp[1][half][lane]) + sp[2][half][lane]) + sp[3][half][lane];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = r + half * 16 + 4 * g + i;
@@ -168,7 +207,13 @@ __global__ __launch_bounds__(256) void k_attn_partial(
             acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pb), acc[m], 0, 0, 0);
         }
         __syncthreads();
+        if (more) {
+            SKO_STASH()
+            __syncthreads();
+        }
     }
+#undef SKO_FETCH
+#undef SKO_STASH
 
     float lt = l_run + __shfl_xor(l_run, 16);
     lt += __shfl_xor(lt, 32);
@@ -230,14 +275,16 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* _
     const size_t cstride = (size_t)kAttnHeadGroup * kVDim;
     float acc = 0.0f;
     int c = 0;
+    // chunks without rows (weight 0) never wrote their accumulators: they
+    // are skipped, not scaled by zero
     for (; c + 8 <= nchunk; c += 8) {
         float v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(c + u) * cstride];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc += wgt[c + u] * v[u];
+        for (int u = 0; u < 8; ++u) acc = (wgt[c + u] > 0.0f) ? fmaf(wgt[c + u], v[u], acc) : acc;
     }
-    for (; c < nchunk; ++c) acc += wgt[c] * src[(size_t)c * cstride];
+    for (; c < nchunk; ++c) acc = (wgt[c] > 0.0f) ? fmaf(wgt[c], src[(size_t)c * cstride], acc) : acc;
     out[((size_t)bp * H + h) * kVDim + col] = (L > 0.0f) ? acc / L : 0.0f;
 }
 

@@ -8,18 +8,22 @@
 // reverse index cache_slots maps a token to its slot or -1.
 //
 // Per (layer, seq) state: cache_slots[cap], slot_token[S], last_use[S]
-// (step stamp, -1 = never used) and the recency order of the slots: every
-// slot once, ascending by (last_use, slot).  At step t, for one sequence:
+// (step stamp, -1 = never used) and the recency list of the slots: every
+// slot once, ascending by (last_use, slot), kept as a ring of slot ids.  At
+// step t, for one sequence:
 //   U = the tokens whose bit is set in the winner bitmap (the union of the
 //       D position lists, already deduplicated and in token order);
-//   hits are stamped t; misses M are listed in token order;
-//   victims = the first |M| slots of the recency order that were not hit;
+//   hits are stamped t and their ring entries become tombstones (-1);
+//   misses M are listed in token order;
+//   victims = the first |M| live entries from the ring head (the least
+//       recently used slots that were not hit); the head moves past them;
 //   the r-th miss takes the r-th victim; a victim's previous owner (if any)
 //   is evicted: cache_slots[old] = -1;
-//   the new order keeps every untouched slot in place and appends the slots
-//   stamped t (hits and victims) in slot order, so it stays sorted by
-//   (last_use, slot) without any sort.
-// The order lives in two buffers; the step reads one and writes the other.
+//   the slots stamped t (hits and victims) are appended at the tail in slot
+//   order, so the live entries stay sorted by (last_use, slot) without any
+//   sort, and a step touches O(|U| + S/32) entries instead of all S.
+// When the ring would overflow, its live entries are compacted into the
+// other ring buffer first (at most every ~S/|hits| steps).
 //
 // One 1024-thread block per sequence.  Before the merge it finishes the
 // top-k of its D rows whose threshold bucket had to be split (exact radix
@@ -45,7 +49,7 @@ __device__ __forceinline__ uint64_t refine_composite(uint2 e) {
 // (low 20 key bits) << 32 | (0xFFFFFFFF - token), which is unique per
 // candidate (so equal scores go to the smaller token); ends with the
 // threshold composite T and appends the candidates with composite >= T.
-__device__ void refine_row(const uint2* __restrict__ cr, int c, int need, int32_t* __restrict__ out_count,
+__device__ __forceinline__ void refine_row(const uint2* cr, int c, int need, int32_t* __restrict__ out_count,
                            int32_t* __restrict__ w, const int32_t* __restrict__ cs,
                            uint32_t* __restrict__ wb, int top_k, uint32_t* h, int* scratch,
                            int* s_digit, int* s_above) {
@@ -94,21 +98,39 @@ __device__ void refine_row(const uint2* __restrict__ cr, int c, int need, int32_
     __syncthreads();
 }
 
+constexpr int kBatch = 8;  // 16-byte loads in flight per thread per batch
+
+// Per-thread contiguous run [r0, r1) of n items over the block, with the run
+// length rounded up to a multiple of `align`.
+__device__ __forceinline__ void thread_run(int64_t n, int align, int64_t* r0, int64_t* r1) {
+    int64_t per = (n + kLruThreads - 1) / kLruThreads;
+    per = (per + align - 1) / align * align;
+    *r0 = std::min<int64_t>(n, (int64_t)threadIdx.x * per);
+    *r1 = std::min<int64_t>(n, *r0 + per);
+}
+
 __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     uint32_t* __restrict__ winners, uint32_t* __restrict__ hist, RowMeta* __restrict__ meta,
     const uint2* __restrict__ cand, int32_t* __restrict__ topk, const int32_t* __restrict__ ntok_layer,
     int32_t* __restrict__ cache_slots_layer, int32_t* __restrict__ slot_token_layer,
-    int32_t* __restrict__ last_use_layer, const int32_t* __restrict__ order_cur,
-    int32_t* __restrict__ order_next, int D, int top_k, int S, int64_t Sp, int64_t cap, int64_t wpr,
+    int32_t* __restrict__ last_use_layer, int32_t* __restrict__ ring0_layer, int32_t* __restrict__ ring1_layer,
+    int32_t* __restrict__ pos_layer, RingState* __restrict__ ring_state_layer, int D, int top_k, int S,
+    int64_t C, int64_t cap, int64_t wpr,
     int32_t t, int32_t* __restrict__ misses, int32_t* __restrict__ victims,
     int32_t* __restrict__ evict_old, int32_t* __restrict__ counts, GatherEntry* __restrict__ glist,
     unsigned long long* __restrict__ layer_stats) {
     __shared__ uint32_t touched[kMaxHotSlots / 32];
-    __shared__ int32_t mlist[kMaxMerge];
-    __shared__ int32_t vlist[kMaxMerge];
+    // [0, kMaxMerge): misses; [kMaxMerge, 2 kMaxMerge): the union, later the
+    // victims.  Before the merge the whole area stages refine candidates.
+    __shared__ int32_t lists[2 * kMaxMerge];
     __shared__ uint32_t h[256];
     __shared__ int scratch[kLruThreads / 64 + 1];
     __shared__ int s_digit, s_above;
+    __shared__ int64_t s_newhead;
+    int32_t* mlist = lists;
+    int32_t* ulist = lists + kMaxMerge;
+    int32_t* vlist = lists + kMaxMerge;
+    uint2* cstage = reinterpret_cast<uint2*>(lists);
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
@@ -117,91 +139,136 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
     int32_t* __restrict__ st = slot_token_layer + (size_t)b * S;
     int32_t* __restrict__ lu = last_use_layer + (size_t)b * S;
-    const int32_t* __restrict__ oc = order_cur + (size_t)b * Sp;
-    int32_t* __restrict__ on = order_next + (size_t)b * Sp;
+    int32_t* __restrict__ pos = pos_layer + (size_t)b * S;
+    const RingState rs = ring_state_layer[b];
+    int32_t* __restrict__ ring = (rs.cur ? ring1_layer : ring0_layer) + (size_t)b * C;
+    int32_t* __restrict__ ring_other = (rs.cur ? ring0_layer : ring1_layer) + (size_t)b * C;
     uint32_t* __restrict__ wb = winners + (size_t)b * wpr;
     int32_t* __restrict__ cnt = counts + (size_t)b * 8;
     const int mstride = D * top_k;
     const int SW = (S + 31) / 32;
 
-    // 0. finish the top-k of rows whose threshold bucket is split
+    // 0. finish the top-k of rows whose threshold bucket is split; the
+    //    staged candidates are copied to LDS when they fit
     for (int p = 0; p < D; ++p) {
         const int row = b * D + p;
         const RowMeta m = meta[row];
         if (m.bucket < 0 || m.need == 0 || m.need == m.bucket_count) continue;
         const int c = (int)std::min<int64_t>(m.cand_count, cap);
-        refine_row(cand + (size_t)row * cap, c, m.need, &meta[row].out_count, topk + (size_t)row * top_k, cs, wb,
-                   top_k, h, scratch, &s_digit, &s_above);
+        const uint2* cr = cand + (size_t)row * cap;
+        int32_t* w = topk + (size_t)row * top_k;
+        if (c <= kMaxMerge) {
+            for (int i = tid; i < c; i += kLruThreads) cstage[i] = cr[i];
+            __syncthreads();
+            refine_row(cstage, c, m.need, &meta[row].out_count, w, cs, wb, top_k, h, scratch, &s_digit, &s_above);
+        } else {
+            refine_row(cr, c, m.need, &meta[row].out_count, w, cs, wb, top_k, h, scratch, &s_digit, &s_above);
+        }
     }
 
     for (int i = tid; i < SW; i += kLruThreads) touched[i] = 0u;
     if (tid == 0) cnt[7] = 0;
     __syncthreads();
 
-    // 1. the union U in token order: count hits and misses per run of words
+    // 1. the union U in token order from the winner bitmap: each thread owns
+    //    a contiguous run of words (16-byte loads, batched); one scan places
+    //    every thread's tokens; the bitmap is cleared for the next step
     const int64_t nwords = (Lt + 31) / 32;
-    const int64_t wper = (nwords + kLruThreads - 1) / kLruThreads;
-    const int64_t w0 = std::min<int64_t>(nwords, (int64_t)tid * wper);
-    const int64_t w1 = std::min<int64_t>(nwords, w0 + wper);
-    int nh_loc = 0, nm_loc = 0;
-    for (int64_t w = w0; w < w1; ++w) {
-        uint32_t bits = wb[w];
-        while (bits) {
-            const int e = __ffs((int)bits) - 1;
-            bits &= bits - 1u;
-            if (cs[w * 32 + e] < 0) ++nm_loc; else ++nh_loc;
-        }
+    int64_t w0, w1;
+    thread_run(nwords, 4, &w0, &w1);
+    int nu_loc = 0;
+    for (int64_t w = w0; w < w1; w += 4 * kBatch) {
+        uint4 v[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            v[q] = (w + 4 * q < w1) ? *reinterpret_cast<const uint4*>(wb + w + 4 * q) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) nu_loc += __popc(v[q].x) + __popc(v[q].y) + __popc(v[q].z) + __popc(v[q].w);
     }
-    int nH, nM;
-    (void)block_exclusive_scan<kLruThreads>(nh_loc, &nH, scratch);
-    const int m_off = block_exclusive_scan<kLruThreads>(nm_loc, &nM, scratch);
-    // misses listed in token order; hits stamped and marked; bitmap cleared
-    {
-        int o = m_off;
-        for (int64_t w = w0; w < w1; ++w) {
-            uint32_t bits = wb[w];
-            if (!bits) continue;
-            wb[w] = 0u;
-            while (bits) {
-                const int e = __ffs((int)bits) - 1;
-                bits &= bits - 1u;
-                const int32_t tok = (int32_t)(w * 32 + e);
-                const int32_t slot = cs[tok];
-                if (slot < 0) {
-                    if (o < kMaxMerge) mlist[o] = tok;
-                    ++o;
-                } else if (slot < S) {
-                    atomicOr(&touched[slot >> 5], 1u << (slot & 31));
-                    lu[slot] = t;
+    int nU;
+    int uo = block_exclusive_scan<kLruThreads>(nu_loc, &nU, scratch);
+    if (nu_loc) {
+        for (int64_t w = w0; w < w1; w += 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(wb + w);
+            if ((v.x | v.y | v.z | v.w) == 0u) continue;
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                for (uint32_t x = wv[q]; x; x &= x - 1u) {
+                    if (uo < kMaxMerge) ulist[uo] = (int32_t)((w + q) * 32 + (__ffs((int)x) - 1));
+                    ++uo;
                 }
-            }
+            *reinterpret_cast<uint4*>(wb + w) = make_uint4(0u, 0u, 0u, 0u);
         }
     }
     __syncthreads();
+    nU = std::min(nU, kMaxMerge);
+
+    // 2. hits and misses: every thread looks up its contiguous run of U at
+    //    once; misses listed in token order, hits stamped t and marked
+    int64_t u0, u1;
+    thread_run(nU, 1, &u0, &u1);
+    constexpr int kMaxPer = kMaxMerge / kLruThreads;
+    int32_t slot_of[kMaxPer];
+    int nm_loc = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) {
+        slot_of[q] = (u0 + q < u1) ? cs[ulist[u0 + q]] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) nm_loc += (u0 + q < u1 && slot_of[q] < 0) ? 1 : 0;
+    int nM;
+    int mo = block_exclusive_scan<kLruThreads>(nm_loc, &nM, scratch);
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) {
+        if (u0 + q >= u1) continue;
+        const int32_t slot = slot_of[q];
+        if (slot < 0) {
+            mlist[mo++] = ulist[u0 + q];
+        } else if (slot < S) {
+            atomicOr(&touched[slot >> 5], 1u << (slot & 31));
+            lu[slot] = t;
+            const int32_t rp = pos[slot];
+            if (rp >= 0 && rp < C) ring[rp] = -1;  // the hit leaves its place in the list
+        }
+    }
+    const int nH = nU - nM;
+    __syncthreads();
 
     int nEv = 0;
-    const bool sane = nM <= kMaxMerge && nH + nM <= S;
+    int avail = 0;
+    const bool sane = nH + nM <= S;
     if (nM > 0 && sane) {
-        // 2. victims: the first nM slots of the recency order not hit at t;
-        //    they lie within its first nM + nH entries
-        const int P = std::min(S, nM + nH);
-        const int per = (P + kLruThreads - 1) / kLruThreads;
-        const int p0 = std::min(P, tid * per), p1 = std::min(P, p0 + per);
-        int c = 0;
-        for (int i = p0; i < p1; ++i) c += !is_touched(touched, oc[i]);
-        int avail;
-        int vpos = block_exclusive_scan<kLruThreads>(c, &avail, scratch);
-        for (int i = p0; i < p1 && vpos < nM; ++i) {
-            const int32_t s = oc[i];
-            if (!is_touched(touched, s)) vlist[vpos++] = s;
+        // 3. victims: the first nM live ring entries from the head, scanned
+        //    in windows of 8 consecutive entries per thread
+        int found = 0;
+        for (int64_t base = rs.head; found < nM && base < rs.tail; base += 8 * kLruThreads) {
+            const int64_t e0 = base + 8 * (int64_t)tid;
+            int32_t ent[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) ent[q] = (e0 + q < rs.tail) ? ring[(e0 + q) % C] : -1;
+            int c = 0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) c += ent[q] >= 0 ? 1 : 0;
+            int tot;
+            int rank = found + block_exclusive_scan<kLruThreads>(c, &tot, scratch);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if (ent[q] < 0) continue;
+                if (rank < nM) vlist[rank] = ent[q];
+                if (rank == nM - 1) s_newhead = e0 + q + 1;
+                ++rank;
+            }
+            found += tot;
         }
+        avail = found;
         __syncthreads();
         for (int r = tid; r < nM; r += kLruThreads) {
             const int32_t s = vlist[r];
             if (s >= 0 && s < S) atomicOr(&touched[s >> 5], 1u << (s & 31));
         }
         __syncthreads();
-        // 3. assignment: r-th miss -> r-th victim
+        // 4. assignment: r-th miss -> r-th victim
         int ev_loc = 0;
         for (int r = tid; r < nM; r += kLruThreads) {
             const int32_t v = vlist[r];
@@ -231,50 +298,62 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     }
     __syncthreads();
 
-    // 4. next recency order: untouched slots in their order, then the slots
-    //    stamped t in slot order.  Runs are multiples of 4 entries (rows are
-    //    padded to Sp, a multiple of 4) and read as 16-byte vectors.
+    // 5. ring maintenance: compact if the append would overflow, then append
+    //    the slots stamped t (hits and victims) at the tail in slot order
     {
-        const int per = ((S + kLruThreads - 1) / kLruThreads + 3) & ~3;
-        const int s0 = std::min(S, tid * per), s1 = std::min(S, s0 + per);
-        int keep = 0;
-        for (int i = s0; i < s1; i += 4) {
-            const int4 v = *reinterpret_cast<const int4*>(oc + i);
-            keep += !is_touched(touched, v.x);
-            if (i + 1 < s1) keep += !is_touched(touched, v.y);
-            if (i + 2 < s1) keep += !is_touched(touched, v.z);
-            if (i + 3 < s1) keep += !is_touched(touched, v.w);
+        const bool took = nM > 0 && sane && avail >= nM;
+        const int nT = took ? nH + nM : nH;
+        int64_t head = took ? s_newhead : rs.head;
+        int64_t tail = rs.tail;
+        int32_t cur = rs.cur;
+        int32_t* rg = ring;
+        if ((tail + nT) - head > C) {
+            // live entries of [head, tail) -> ring_other[0 ..), in order
+            const int64_t R = tail - head;
+            int64_t i0, i1;
+            thread_run(R, 1, &i0, &i1);
+            int lc = 0;
+            for (int64_t i = i0; i < i1; ++i) lc += ring[(head + i) % C] >= 0 ? 1 : 0;
+            int nlive;
+            int64_t lp = block_exclusive_scan<kLruThreads>(lc, &nlive, scratch);
+            for (int64_t i = i0; i < i1; ++i) {
+                const int32_t sl = ring[(head + i) % C];
+                if (sl >= 0 && sl < S && lp < C) {
+                    ring_other[lp] = sl;
+                    pos[sl] = (int32_t)lp;
+                    ++lp;
+                }
+            }
+            head = 0;
+            tail = nlive;
+            cur ^= 1;
+            rg = ring_other;
         }
-        int nkeep;
-        int kpos = block_exclusive_scan<kLruThreads>(keep, &nkeep, scratch);
-        for (int i = s0; i < s1; i += 4) {
-            const int4 v = *reinterpret_cast<const int4*>(oc + i);
-            const int32_t e4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (i + q < s1 && !is_touched(touched, e4[q]) && kpos < S) on[kpos++] = e4[q];
-        }
-        const int tw = (SW + kLruThreads - 1) / kLruThreads;
-        const int q0 = std::min(SW, tid * tw), q1 = std::min(SW, q0 + tw);
+        int64_t q0, q1;
+        thread_run(SW, 1, &q0, &q1);
         int ct = 0;
-        for (int q = q0; q < q1; ++q) ct += __popc(touched[q]);
+        for (int64_t q = q0; q < q1; ++q) ct += __popc(touched[q]);
         int ntouched;
-        int tpos = nkeep + block_exclusive_scan<kLruThreads>(ct, &ntouched, scratch);
-        for (int q = q0; q < q1; ++q) {
+        int64_t tp = tail + block_exclusive_scan<kLruThreads>(ct, &ntouched, scratch);
+        for (int64_t q = q0; q < q1; ++q) {
             uint32_t bits = touched[q];
             while (bits) {
                 const int e = __ffs((int)bits) - 1;
                 bits &= bits - 1u;
-                if (tpos < S) on[tpos++] = q * 32 + e;
+                const int32_t sl = (int32_t)(q * 32 + e);
+                const int64_t ri = tp % C;
+                rg[ri] = sl;
+                pos[sl] = (int32_t)ri;
+                ++tp;
             }
         }
+        if (tid == 0) ring_state_layer[b] = RingState{head, tail + ntouched, cur, {0, 0, 0}};
     }
 
-    // 5. counters; clear this sequence's selection scratch for the next step
+    // 6. counters; clear this sequence's selection scratch for the next step
     for (int i = tid; i < D * kHistBins; i += kLruThreads) hist[(size_t)b * D * kHistBins + i] = 0u;
     if (tid < D) meta[b * D + tid] = RowMeta{-1, 0, 0, 0, 0, 0, {0, 0}};
     if (tid == 0) {
-        const int nU = nH + nM;
         cnt[0] = nU; cnt[1] = nH; cnt[2] = nM; cnt[3] = nEv;
         cnt[4] = kk; cnt[5] = (int32_t)Lt; cnt[6] = t;
         atomicAdd(&layer_stats[1], (unsigned long long)nU);
@@ -288,33 +367,36 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
 hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, RowMeta* meta,
                             const uint2* cand, int32_t* topk, const int32_t* ntok_layer,
                             int32_t* cache_slots_layer, int32_t* slot_token_layer,
-                            int32_t* last_use_layer, const int32_t* order_cur, int32_t* order_next,
+                            int32_t* last_use_layer, int32_t* ring0_layer, int32_t* ring1_layer,
+                            int32_t* pos_layer, RingState* ring_state_layer,
                             int B, int D, int top_k, int S, int64_t cap, int32_t t,
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
                             GatherEntry* glist, unsigned long long* layer_stats) {
-    const int64_t Sp = ((int64_t)S + 3) / 4 * 4;
-    const int64_t wpr = (cap + 31) / 32;
+    const int64_t C = ring_capacity(S, D, top_k);
+    const int64_t wpr = winner_words(cap);
     hipLaunchKernelGGL(k_merge_lru, dim3(B), dim3(kLruThreads), 0, st, winners, hist, meta, cand, topk,
-                       ntok_layer, cache_slots_layer, slot_token_layer, last_use_layer, order_cur,
-                       order_next, D, top_k, S, Sp, cap, wpr, t, misses, victims, evict_old, counts,
-                       glist, layer_stats);
+                       ntok_layer, cache_slots_layer, slot_token_layer, last_use_layer, ring0_layer,
+                       ring1_layer, pos_layer, ring_state_layer, D, top_k, S, C, cap, wpr, t, misses, victims,
+                       evict_old, counts, glist, layer_stats);
     return hipGetLastError();
 }
 
-__global__ void k_init_order(int32_t* __restrict__ order, int64_t n_seqs, int S, int64_t Sp) {
-    const int64_t total = n_seqs * Sp;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t s = i % Sp;
-        order[i] = s < S ? (int32_t)s : -1;
+__global__ void k_init_rings(int32_t* __restrict__ ring0, int32_t* __restrict__ pos,
+                             RingState* __restrict__ state, int64_t n_seqs, int S, int64_t C) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t i = i0; i < n_seqs * C; i += stride) {
+        const int64_t e = i % C;
+        ring0[i] = e < S ? (int32_t)e : -1;
     }
+    for (int64_t i = i0; i < n_seqs * S; i += stride) pos[i] = (int32_t)(i % S);
+    for (int64_t i = i0; i < n_seqs; i += stride) state[i] = RingState{0, S, 0, {0, 0, 0}};
 }
 
-hipError_t launch_init_order(hipStream_t st, int32_t* order, int64_t n_seqs, int S) {
-    const int64_t Sp = ((int64_t)S + 3) / 4 * 4;
-    const int64_t total = n_seqs * Sp;
-    const int g = (int)std::min<int64_t>((total + 255) / 256, 4096);
-    hipLaunchKernelGGL(k_init_order, dim3(std::max(g, 1)), dim3(256), 0, st, order, n_seqs, S, Sp);
+hipError_t launch_init_rings(hipStream_t st, int32_t* ring0, int32_t* pos, RingState* state, int64_t n_seqs,
+                             int S, int64_t C) {
+    const int g = (int)std::min<int64_t>((n_seqs * C + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_init_rings, dim3(std::max(g, 1)), dim3(256), 0, st, ring0, pos, state, n_seqs, S, C);
     return hipGetLastError();
 }
 

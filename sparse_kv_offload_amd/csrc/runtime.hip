@@ -73,7 +73,7 @@ struct sko_handle {
     int64_t cap = 0;
     int64_t ntiles = 0;  // indexer tiles of 64 tokens per sequence
     int64_t kcap = 0;    // key row stride (cap rounded up to 16)
-    int64_t Sp = 0;      // recency-order row stride (S rounded up to 4)
+    int64_t C = 0;       // recency ring capacity per sequence
     int64_t wpr = 0;     // winner-bitmap words per sequence
 
     // offload state
@@ -85,7 +85,9 @@ struct sko_handle {
     int32_t* cache_slots = nullptr; // [L][B][cap]
     int32_t* slot_token = nullptr;  // [L][B][S]
     int32_t* last_use = nullptr;    // [L][B][S]
-    int32_t* order[2] = {nullptr, nullptr};  // [L][B][Sp] recency order, double-buffered
+    int32_t* ring[2] = {nullptr, nullptr};  // [L][B][C] recency rings (one live per sequence)
+    int32_t* ring_pos = nullptr;            // [L][B][S] ring index of each slot
+    RingState* ring_state = nullptr;        // [L][B]
     int32_t* ntok_dev = nullptr;    // [L][B]
     unsigned long long* stats = nullptr;  // [L][8]
     std::vector<int64_t> ntok;      // host mirror [L][B]
@@ -264,8 +266,8 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     h->cap = cfg->max_tokens;
     h->ntiles = (h->cap + kIdxTile - 1) / kIdxTile;
     h->kcap = (h->cap + 15) / 16 * 16;
-    h->Sp = ((int64_t)h->S + 3) / 4 * 4;
-    h->wpr = (h->cap + 31) / 32;
+    h->C = ring_capacity(h->S, h->D, h->k);
+    h->wpr = winner_words(h->cap);
     h->ntok.assign((size_t)h->L * h->B, 0);
     h->step.assign((size_t)h->L, 0);
     h->rows_per_block = attn_rows_per_block(h->k, h->B * h->D * h->HG);
@@ -297,8 +299,10 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     ok = ok && dev_alloc(h, (void**)&h->cache_slots, LB * h->cap * 4);
     ok = ok && dev_alloc(h, (void**)&h->slot_token, LB * h->S * 4);
     ok = ok && dev_alloc(h, (void**)&h->last_use, LB * h->S * 4);
-    ok = ok && dev_alloc(h, (void**)&h->order[0], LB * h->Sp * 4);
-    ok = ok && dev_alloc(h, (void**)&h->order[1], LB * h->Sp * 4);
+    ok = ok && dev_alloc(h, (void**)&h->ring[0], LB * h->C * 4);
+    ok = ok && dev_alloc(h, (void**)&h->ring[1], LB * h->C * 4);
+    ok = ok && dev_alloc(h, (void**)&h->ring_pos, LB * h->S * 4);
+    ok = ok && dev_alloc(h, (void**)&h->ring_state, LB * sizeof(RingState));
     ok = ok && dev_alloc(h, (void**)&h->ntok_dev, LB * 4);
     ok = ok && dev_alloc(h, (void**)&h->stats, (size_t)h->L * 8 * 8);
     ok = ok && dev_alloc(h, (void**)&h->keys, BD * h->kcap * 4);
@@ -335,7 +339,7 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     if (e == hipSuccess) e = hipMemsetAsync(h->hist, 0, BD * kHistBins * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->meta, 0, BD * sizeof(RowMeta), h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->idx, 0, LB * h->ntiles * kIdxTile * kIdxDim * 2, h->stream);
-    if (e == hipSuccess) e = launch_init_order(h->stream, h->order[0], (int64_t)LB, h->S);
+    if (e == hipSuccess) e = launch_init_rings(h->stream, h->ring[0], h->ring_pos, h->ring_state, (int64_t)LB, h->S, h->C);
     if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
     if (e != hipSuccess) {
         set_err(SKO_E_DEVICE, "initialising state: %s", hipGetErrorString(e));
@@ -445,8 +449,10 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
     const uint16_t* qi = static_cast<const uint16_t*>(q_idx);
     const uint16_t* qa = static_cast<const uint16_t*>(q_attn);
 
-    const int32_t* order_cur = h->order[t & 1] + (size_t)layer * B * h->Sp;
-    int32_t* order_next = h->order[(t & 1) ^ 1] + (size_t)layer * B * h->Sp;
+    int32_t* ring0 = h->ring[0] + (size_t)layer * B * h->C;
+    int32_t* ring1 = h->ring[1] + (size_t)layer * B * h->C;
+    int32_t* ring_pos = h->ring_pos + LBs;
+    RingState* ring_state = h->ring_state + (size_t)layer * B;
 
     if ((rc = run_stage(h, ST_SCORE, [&] {
              return launch_score_hist(h->stream, idx_layer, qi, ntok, h->keys, h->hist, B, D, h->kcap, h->ntiles,
@@ -460,7 +466,7 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
         return rc;
     if ((rc = run_stage(h, ST_MERGE_LRU, [&] {
              return launch_merge_lru(h->stream, h->winners, h->hist, h->meta, h->cand, h->topk, ntok, cs, st, lu,
-                                     order_cur, order_next, B, D, k, S, cap, t, h->misses, h->victims,
+                                     ring0, ring1, ring_pos, ring_state, B, D, k, S, cap, t, h->misses, h->victims,
                                      h->evict_old, h->counts, h->glist, h->stats + (size_t)layer * 8);
          })))
         return rc;

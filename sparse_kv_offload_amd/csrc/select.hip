@@ -143,47 +143,58 @@ __global__ __launch_bounds__(256) void k_score_hist(const uint4* __restrict__ id
         uint32_t* __restrict__ keyrow = keys + ((size_t)b * D + p0) * kcap;
         const int64_t tile_end = std::min<int64_t>(tile0 + tiles_per_block, (Lt + kIdxTile - 1) / kIdxTile);
         const uint4* __restrict__ seq_tiles = idx_layer + (size_t)b * ntiles * kIdxRowU4 * kIdxTile + lane;
-        // double-buffered: the next tile's 8 loads are in flight while this
-        // tile's FMA chains run
-        uint4 cur[kIdxRowU4], nxt[kIdxRowU4];
-        int64_t tile = tile0 + wave;
-        if (tile < tile_end) {
+        // Ping-pong over two register tiles: the next tile's 8 loads are in
+        // flight while this tile's FMA chains run.  Loads are unconditional
+        // (the tile index is clamped to the last valid tile) so that the
+        // compiler's wait counts stay "all but the newest 8 loads".
+        const int64_t last = tile_end - 1;
+        auto load_tile = [&](uint4* r, int64_t tile) {
+            const int64_t tl = tile < last ? tile : last;
 #pragma unroll
-            for (int c = 0; c < kIdxRowU4; ++c) cur[c] = seq_tiles[(tile * kIdxRowU4 + c) * kIdxTile];
-        }
-        for (; tile < tile_end; tile += 4) {
-            if (tile + 4 < tile_end) {
-#pragma unroll
-                for (int c = 0; c < kIdxRowU4; ++c) nxt[c] = seq_tiles[((tile + 4) * kIdxRowU4 + c) * kIdxTile];
-            }
+            for (int c = 0; c < kIdxRowU4; ++c) r[c] = seq_tiles[(tl * kIdxRowU4 + c) * kIdxTile];
+        };
+        // the chains run for every lane (lanes past the last token compute on
+        // a clamped in-bounds row and store nothing), so every loaded
+        // register is consumed on every path
+        auto score_tile = [&](const uint4* r, int64_t tile) {
             const int64_t i = tile * kIdxTile + lane;
-            if (i < Lt) {
-                uint32_t w[32];
+            const bool valid = i < Lt;
+            uint32_t w[32];
 #pragma unroll
-                for (int c = 0; c < kIdxRowU4; ++c) {
-                    w[4 * c + 0] = cur[c].x;
-                    w[4 * c + 1] = cur[c].y;
-                    w[4 * c + 2] = cur[c].z;
-                    w[4 * c + 3] = cur[c].w;
+            for (int c = 0; c < kIdxRowU4; ++c) {
+                w[4 * c + 0] = r[c].x;
+                w[4 * c + 1] = r[c].y;
+                w[4 * c + 2] = r[c].z;
+                w[4 * c + 3] = r[c].w;
+            }
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    const uint32_t qw = qb[p * 32 + j];
+                    acc = __builtin_fmaf(bf16_lo(qw), bf16_lo(w[j]), acc);
+                    acc = __builtin_fmaf(bf16_hi(qw), bf16_hi(w[j]), acc);
                 }
-#pragma unroll
-                for (int p = 0; p < NP; ++p) {
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < 32; ++j) {
-                        const uint32_t qw = qb[p * 32 + j];
-                        acc = __builtin_fmaf(bf16_lo(qw), bf16_lo(w[j]), acc);
-                        acc = __builtin_fmaf(bf16_hi(qw), bf16_hi(w[j]), acc);
-                    }
-                    if (acc == 0.0f) acc = 0.0f;  // store a zero as +0
-                    const uint32_t key = score_key(acc);
+                if (acc == 0.0f) acc = 0.0f;  // store a zero as +0
+                uint32_t key = score_key(acc);
+                asm volatile("" : "+v"(key));  // keep the chain outside the branch below
+                if (valid) {
                     keyrow[(size_t)p * kcap + i] = key;
                     const uint32_t bin = key >> (32 - kHistBits);
                     atomicAdd(&sh[p * HW + (bin >> 1)], 1u << ((bin & 1u) << 4));
                 }
             }
-#pragma unroll
-            for (int c = 0; c < kIdxRowU4; ++c) cur[c] = nxt[c];
+        };
+        uint4 ra[kIdxRowU4], rb[kIdxRowU4];
+        int64_t tile = tile0 + wave;
+        load_tile(ra, tile);
+        for (; tile < tile_end; tile += 8) {
+            load_tile(rb, tile + 4);
+            score_tile(ra, tile);
+            if (tile + 4 >= tile_end) break;
+            load_tile(ra, tile + 8);
+            score_tile(rb, tile + 4);
         }
         __syncthreads();
         for (int i = threadIdx.x; i < NP * HW; i += blockDim.x) {
@@ -313,7 +324,7 @@ hipError_t launch_topk_filter(hipStream_t st, const uint32_t* keys, const uint32
                               const int32_t* ntok_layer, uint32_t* winners, int B, int D,
                               int64_t cap, int top_k, int64_t max_tokens_now) {
     const int64_t kcap = (cap + 15) / 16 * 16;
-    const int64_t wpr = (cap + 31) / 32;
+    const int64_t wpr = winner_words(cap);
     const int64_t now = std::max<int64_t>(1, max_tokens_now);
     int chunk = kFilterSpan;
     while (chunk < (1 << 20) && (int64_t)B * D * ((now + 2 * chunk - 1) / (2 * chunk)) >= 1024) chunk *= 2;

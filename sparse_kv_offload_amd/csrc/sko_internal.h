@@ -20,6 +20,7 @@ constexpr int kMaxMerge = 8192;              // D * k limit of the merge/LRU ker
 constexpr int kMaxHotSlots = 1 << 18;        // S limit (LDS bitmap of touched slots)
 constexpr int kAttnHeadGroup = 16;           // heads per MFMA tile (M = 16)
 constexpr int kAttnTileRows = 32;            // rows per attention tile
+constexpr int kAttnMaxRowsPerBlock = 512;    // rows of one attention block (remap table)
 constexpr int kFilterKeysPerThread = 16;
 constexpr int kFilterSpan = 256 * kFilterKeysPerThread;  // keys per block pass
 
@@ -41,6 +42,23 @@ struct RowMeta {
     int32_t cand_count;    // bucket keys staged for refinement
     int32_t pad[2];
 };
+
+// Words of the per-sequence winner bitmap (padded to 16 bytes).
+__host__ __device__ inline int64_t winner_words(int64_t cap) { return ((cap + 31) / 32 + 3) / 4 * 4; }
+
+// Recency list of one (layer, seq) hot buffer: a ring of slot ids (two
+// buffers, `cur` selects the live one), -1 marking entries that moved.
+// Live entries in [head, tail) are every slot once, ascending by
+// (last_use, slot); pos[slot] is the ring index of its live entry.
+struct RingState {
+    int64_t head;
+    int64_t tail;
+    int32_t cur;
+    int32_t pad[3];
+};
+__host__ __device__ inline int64_t ring_capacity(int S, int D, int k) {
+    return ((2 * (int64_t)S + (int64_t)D * k) + 3) / 4 * 4;
+}
 
 struct GatherEntry {
     uint32_t src_row;  // b * cap + token  (within the layer's pool)
@@ -64,7 +82,8 @@ hipError_t launch_topk_filter(hipStream_t st, const uint32_t* keys, const uint32
 hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, RowMeta* meta,
                             const uint2* cand, int32_t* topk, const int32_t* ntok_layer,
                             int32_t* cache_slots_layer, int32_t* slot_token_layer,
-                            int32_t* last_use_layer, const int32_t* order_cur, int32_t* order_next,
+                            int32_t* last_use_layer, int32_t* ring0_layer, int32_t* ring1_layer,
+                            int32_t* pos_layer, RingState* ring_state_layer,
                             int B, int D, int top_k, int S, int64_t cap, int32_t t,
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
                             GatherEntry* glist, unsigned long long* layer_stats);
@@ -79,6 +98,8 @@ hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_
                                int rows_per_block, float scale);
 hipError_t launch_attn_combine(hipStream_t st, const float* part_acc, const float* part_ml,
                                float* out, int B, int D, int H, int nchunk);
-hipError_t launch_init_order(hipStream_t st, int32_t* order, int64_t n_seqs, int S);
+// Rings of n_seqs sequences: ring0 = 0..S-1, pos = identity, head 0, tail S.
+hipError_t launch_init_rings(hipStream_t st, int32_t* ring0, int32_t* pos, RingState* state, int64_t n_seqs,
+                             int S, int64_t C);
 
 }  // namespace sko
