@@ -6,20 +6,20 @@
 // table).  The pool is pinned, device-mapped host memory; this kernel reads
 // it directly over the host link (zero-copy) and writes the 1152-byte rows
 // into their victim slots of the hot buffer.  The work list (source row,
-// destination row) for all sequences of the layer comes from the LRU kernel,
-// whose device-side counter gives the total, so no host sync is needed.
+// destination row) of every sequence comes from the LRU kernel, with the
+// per-sequence miss counts on the device, so no host sync is needed.
 #include "sko_common.cuh"
 #include "sko_internal.h"
 
 namespace sko {
 
-constexpr int kGatherUnroll = 4;
 constexpr int kGatherThreads = 256;
+constexpr int kRowsPerWave = 4;  // rows in flight per wave
+constexpr int kGatherMaxBlocks = 512;
 
 // Sequence b's entries are glist[b * mstride + r] for r < counts[b][2].
 // Each block first builds the prefix of the per-sequence miss counts in LDS;
-// a flat 16-byte chunk index c then maps to entry e = c / 72 and, by binary
-// search in the prefix, to (sequence, r).
+// a flat entry index e then maps to (sequence, r) by binary search.
 __device__ __forceinline__ int find_seq(const int* pre, int B, int64_t e) {
     int lo = 0, hi = B;  // pre[lo] <= e < pre[hi]
     while (hi - lo > 1) {
@@ -29,6 +29,9 @@ __device__ __forceinline__ int find_seq(const int* pre, int B, int64_t e) {
     return lo;
 }
 
+// One wave copies whole rows: lanes 0..63 read chunks 0..63 of a 1152-byte
+// row (one contiguous 1 KB read), lanes 0..7 the last 8 chunks; each wave
+// keeps kRowsPerWave rows in flight before storing them.
 __global__ __launch_bounds__(kGatherThreads) void k_gather_misses(const GatherEntry* __restrict__ glist,
                                                                   const int32_t* __restrict__ counts,
                                                                   const uint4* __restrict__ pool_layer,
@@ -49,41 +52,38 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_misses(const GatherEn
     if (threadIdx.x == 0) pre[B] = total;
     __syncthreads();
 
-    const int64_t chunks = (int64_t)total * kKvRowU4;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    // several 16-byte host reads in flight per thread before the stores
-    for (; c + (kGatherUnroll - 1) * stride < chunks; c += kGatherUnroll * stride) {
-        uint4 v[kGatherUnroll];
-        int64_t dst[kGatherUnroll];
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t e0 = wave * kRowsPerWave; e0 < total; e0 += nwaves * kRowsPerWave) {
+        uint4 a[kRowsPerWave], t8[kRowsPerWave];
+        int64_t dst[kRowsPerWave];
 #pragma unroll
-        for (int u = 0; u < kGatherUnroll; ++u) {
-            const int64_t cc = c + u * stride;
-            const int64_t e = cc / kKvRowU4;
-            const int part = (int)(cc - e * kKvRowU4);
+        for (int r = 0; r < kRowsPerWave; ++r) {
+            const int64_t e = std::min<int64_t>(e0 + r, total - 1);  // in range; duplicates are not stored
             const int b = find_seq(pre, B, e);
             const GatherEntry g = glist[(size_t)b * mstride + (e - pre[b])];
-            v[u] = pool_layer[(int64_t)g.src_row * kKvRowU4 + part];
-            dst[u] = (int64_t)g.dst_row * kKvRowU4 + part;
+            const uint4* src = pool_layer + (int64_t)g.src_row * kKvRowU4;
+            a[r] = src[lane];
+            t8[r] = make_uint4(0u, 0u, 0u, 0u);
+            if (lane < kKvRowU4 - 64) t8[r] = src[64 + lane];
+            dst[r] = (int64_t)g.dst_row * kKvRowU4;
         }
 #pragma unroll
-        for (int u = 0; u < kGatherUnroll; ++u) hot_layer[dst[u]] = v[u];
-    }
-    for (; c < chunks; c += stride) {
-        const int64_t e = c / kKvRowU4;
-        const int part = (int)(c - e * kKvRowU4);
-        const int b = find_seq(pre, B, e);
-        const GatherEntry g = glist[(size_t)b * mstride + (e - pre[b])];
-        hot_layer[(int64_t)g.dst_row * kKvRowU4 + part] = pool_layer[(int64_t)g.src_row * kKvRowU4 + part];
+        for (int r = 0; r < kRowsPerWave; ++r) {
+            if (e0 + r >= total) break;
+            hot_layer[dst[r] + lane] = a[r];
+            if (lane < kKvRowU4 - 64) hot_layer[dst[r] + 64 + lane] = t8[r];
+        }
     }
 }
 
 hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const int32_t* counts,
                                 const uint16_t* pool_layer, uint16_t* hot_layer, int B, int mstride,
                                 int max_entries) {
-    const int64_t max_chunks = (int64_t)max_entries * kKvRowU4;
-    int grid = (int)std::min<int64_t>((max_chunks + kGatherThreads * kGatherUnroll - 1) /
-                                          (kGatherThreads * kGatherUnroll), 2048);
+    const int rows_per_block = (kGatherThreads / 64) * kRowsPerWave;
+    int grid = (int)std::min<int64_t>(((int64_t)max_entries + rows_per_block - 1) / rows_per_block,
+                                      kGatherMaxBlocks);
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(k_gather_misses, dim3(grid), dim3(kGatherThreads), (size_t)(B + 1) * sizeof(int), st,
                        glist, counts, reinterpret_cast<const uint4*>(pool_layer),

@@ -44,58 +44,137 @@ __device__ __forceinline__ uint64_t refine_composite(uint2 e) {
     return ((uint64_t)(e.x & 0xFFFFFu) << 32) | (uint64_t)(0xFFFFFFFFu - e.y);
 }
 
-// Exact selection of `need` winners among the c staged bucket keys of one
-// row.  Radix select, 8 bits per pass from the top, on the 52-bit composite
+// Exact selection inside split threshold buckets.  For each row whose
+// bucket must be split, `need` winners are chosen among its c staged bucket
+// keys by radix select, from the top, on the 52-bit composite
 // (low 20 key bits) << 32 | (0xFFFFFFFF - token), which is unique per
-// candidate (so equal scores go to the smaller token); ends with the
-// threshold composite T and appends the candidates with composite >= T.
-__device__ __forceinline__ void refine_row(const uint2* cr, int c, int need, int32_t* __restrict__ out_count,
-                           int32_t* __restrict__ w, const int32_t* __restrict__ cs,
-                           uint32_t* __restrict__ wb, int top_k, uint32_t* h, int* scratch,
-                           int* s_digit, int* s_above) {
-    uint64_t prefix = 0;
-    int rem = need;
-    uint64_t T = 0;
-    for (int shift = 48;; shift -= 8) {
-        if (threadIdx.x < 256) h[threadIdx.x] = 0u;
-        __syncthreads();
-        for (int i = threadIdx.x; i < c; i += blockDim.x) {
-            const uint64_t comp = refine_composite(cr[i]);
-            if ((comp >> (shift + 8)) == prefix) atomicAdd(&h[(comp >> shift) & 255u], 1u);
+// candidate (so equal scores go to the smaller token); the result is the
+// threshold composite T, and the candidates with composite >= T are
+// appended to the row's winners.  Up to 4 rows run at once, one thread
+// group each (the block's barriers are shared, every group has its own
+// histogram and state; one wave per group scans the 256 bins).
+struct RefineGroup {
+    uint64_t prefix;
+    uint64_t T;
+    int rem;
+    int done;
+    int row;
+    int c;
+};
+
+__device__ __forceinline__ void refine_rows(int b, int D, RowMeta* __restrict__ meta, const uint2* __restrict__ cand,
+                                            int32_t* __restrict__ topk, const int32_t* __restrict__ cs,
+                                            uint32_t* __restrict__ wb, int top_k, int64_t cap, uint2* stage,
+                                            uint32_t (*hg)[256], RefineGroup* gs) {
+    const int NG = D < 4 ? D : 4;
+    const int gsize = (kLruThreads / NG) & ~63;  // whole waves per group
+    const int tid = threadIdx.x;
+    const int g = tid / gsize;  // < NG, except for leftover threads when NG = 3
+    const int gt = tid - g * gsize;
+    const int gl = gt & 63;
+    const bool in_group = g < NG;
+    const int gi = in_group ? g : 0;  // a valid index for threads outside any group
+    const int stage_per = kMaxMerge / NG;
+    for (int p0 = 0; p0 < D; p0 += NG) {
+        if (in_group && gt == 0) {
+            const int p = p0 + g;
+            RefineGroup G{0, 0, 0, 1, -1, 0};
+            if (p < D) {
+                const int row = b * D + p;
+                const RowMeta m = meta[row];
+                G.row = row;
+                if (m.bucket >= 0 && m.need > 0 && m.need != m.bucket_count) {
+                    G.rem = m.need;
+                    G.done = 0;
+                    G.c = (int)std::min<int64_t>(m.cand_count, cap);
+                }
+            }
+            gs[g] = G;
         }
         __syncthreads();
-        // thread t < 256 holds bin 255 - t; scan in descending bin order
-        const int v = threadIdx.x < 256 ? (int)h[255 - threadIdx.x] : 0;
-        int total;
-        const int excl = block_exclusive_scan<kLruThreads>(v, &total, scratch);
-        if (threadIdx.x < 256 && excl < rem && excl + v >= rem) {
-            *s_digit = 255 - (int)threadIdx.x;
-            *s_above = excl;
+        const RefineGroup G = gs[gi];
+        const bool active = in_group && !G.done;
+        const uint2* __restrict__ cg = cand + (size_t)(active ? G.row : 0) * cap;
+        const bool staged = active && G.c <= stage_per;
+        uint2* sg = stage + (size_t)gi * stage_per;
+        if (staged)
+            for (int i = gt; i < G.c; i += gsize) sg[i] = cg[i];
+        __syncthreads();
+        int width = 8;
+        for (int shift = 44;; shift -= width) {
+            if (shift < 0) { width += shift; shift = 0; }
+            if (active && gt < 256) hg[g][gt] = 0u;
+            __syncthreads();
+            const uint64_t gprefix = gs[gi].prefix;
+            const int grem = gs[gi].rem;
+            const bool gdone = !in_group || gs[gi].done;
+            if (!gdone) {
+                for (int i = gt; i < G.c; i += gsize) {
+                    const uint64_t comp = refine_composite(staged ? sg[i] : cg[i]);
+                    if ((comp >> (shift + width)) == gprefix)
+                        atomicAdd(&hg[g][(comp >> shift) & ((1u << width) - 1u)], 1u);
+                }
+            }
+            __syncthreads();
+            if (gt < 64 && !gdone) {
+                // lane gl holds bins 255-4gl .. 252-4gl (descending order)
+                uint32_t v[4];
+                int sum = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[j] = hg[g][255 - 4 * gl - j];
+                    sum += (int)v[j];
+                }
+                int incl = sum;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_up(incl, o);
+                    if (gl >= o) incl += y;
+                }
+                const int excl = incl - sum;
+                if (excl < grem && incl >= grem) {
+                    int cacc = excl;
+                    for (int j = 0; j < 4; ++j) {
+                        const int cnt = (int)v[j];
+                        if (cacc + cnt >= grem) {
+                            const int d = 255 - 4 * gl - j;
+                            const int rem = grem - cacc;
+                            const uint64_t prefix = (gprefix << width) | (uint64_t)d;
+                            gs[g].prefix = prefix;
+                            gs[g].rem = rem;
+                            if (cnt == rem || shift == 0) {
+                                gs[g].done = 1;
+                                gs[g].T = prefix << shift;
+                            }
+                            break;
+                        }
+                        cacc += cnt;
+                    }
+                }
+            }
+            __syncthreads();
+            bool all_done = true;
+            for (int q = 0; q < NG; ++q) all_done = all_done && gs[q].done;
+            if (all_done || shift == 0) break;
+        }
+        // emit the bucket winners of each active row
+        if (active) {
+            const uint64_t T = gs[gi].T;
+            for (int base = 0; base < G.c; base += gsize) {
+                const int i = base + gt;
+                const bool valid = i < G.c;
+                const uint2 e = valid ? (staged ? sg[i] : cg[i]) : make_uint2(0u, 0u);
+                const bool win = valid && refine_composite(e) >= T;
+                const int pw = wave_append(&meta[G.row].out_count, win);
+                if (win && pw < top_k) {
+                    const bool miss = cs[e.y] == -1;
+                    topk[(size_t)G.row * top_k + pw] = (int32_t)(e.y | (miss ? 0x80000000u : 0u));
+                    atomicOr(&wb[e.y >> 5], 1u << (e.y & 31u));
+                }
+            }
         }
         __syncthreads();
-        const int d = *s_digit;
-        rem -= *s_above;
-        prefix = (prefix << 8) | (uint64_t)d;
-        const bool done = ((int)h[d] == rem) || shift == 0;
-        __syncthreads();
-        if (done) {
-            T = prefix << shift;
-            break;
-        }
     }
-    for (int base = 0; base < c; base += blockDim.x) {
-        const int i = base + threadIdx.x;
-        const bool valid = i < c;
-        const uint2 e = valid ? cr[i] : make_uint2(0u, 0u);
-        const bool win = valid && refine_composite(e) >= T;
-        const int pw = wave_append(out_count, win);
-        if (win && pw < top_k) {
-            const bool miss = cs[e.y] == -1;
-            w[pw] = (int32_t)(e.y | (miss ? 0x80000000u : 0u));
-            atomicOr(&wb[e.y >> 5], 1u << (e.y & 31u));
-        }
-    }
-    __syncthreads();
 }
 
 constexpr int kBatch = 8;  // 16-byte loads in flight per thread per batch
@@ -123,9 +202,9 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     // [0, kMaxMerge): misses; [kMaxMerge, 2 kMaxMerge): the union, later the
     // victims.  Before the merge the whole area stages refine candidates.
     __shared__ int32_t lists[2 * kMaxMerge];
-    __shared__ uint32_t h[256];
+    __shared__ uint32_t hgrp[4][256];
+    __shared__ RefineGroup rgrp[4];
     __shared__ int scratch[kLruThreads / 64 + 1];
-    __shared__ int s_digit, s_above;
     __shared__ int64_t s_newhead;
     int32_t* mlist = lists;
     int32_t* ulist = lists + kMaxMerge;
@@ -148,23 +227,8 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     const int mstride = D * top_k;
     const int SW = (S + 31) / 32;
 
-    // 0. finish the top-k of rows whose threshold bucket is split; the
-    //    staged candidates are copied to LDS when they fit
-    for (int p = 0; p < D; ++p) {
-        const int row = b * D + p;
-        const RowMeta m = meta[row];
-        if (m.bucket < 0 || m.need == 0 || m.need == m.bucket_count) continue;
-        const int c = (int)std::min<int64_t>(m.cand_count, cap);
-        const uint2* cr = cand + (size_t)row * cap;
-        int32_t* w = topk + (size_t)row * top_k;
-        if (c <= kMaxMerge) {
-            for (int i = tid; i < c; i += kLruThreads) cstage[i] = cr[i];
-            __syncthreads();
-            refine_row(cstage, c, m.need, &meta[row].out_count, w, cs, wb, top_k, h, scratch, &s_digit, &s_above);
-        } else {
-            refine_row(cr, c, m.need, &meta[row].out_count, w, cs, wb, top_k, h, scratch, &s_digit, &s_above);
-        }
-    }
+    // 0. finish the top-k of rows whose threshold bucket is split
+    refine_rows(b, D, meta, cand, topk, cs, wb, top_k, cap, cstage, hgrp, rgrp);
 
     for (int i = tid; i < SW; i += kLruThreads) touched[i] = 0u;
     if (tid == 0) cnt[7] = 0;
