@@ -10,8 +10,11 @@ first of which is the all-miss cold step).  All inputs (prefix history,
 per-step token rows and queries) are generated from the seeded synthetic
 recipe and are resident on the device / in the pinned pool before timing.
 
-Prints one JSON line.  Per-kernel durations come from HIP events recorded on
-the library's stream around every stage launch inside the timed region.
+Prints one JSON line.  Per-kernel durations come from HIP events that the
+library records on its own stream: around every stage during the warm-up
+steps after the cold one (the per-stage breakdown), and around the dominant
+stage only during the timed steps (its roofline), since every event pair
+costs device time.
 """
 from __future__ import annotations
 
@@ -27,7 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor figure
-PCIE5_X16_GBPS = 63.0         # PCIe 5.0 x16 per direction, theoretical
+HOST_LINK_PEAK_GBPS = 64.0    # MI355X host interface, PCIe 5.0 x16: 128 GB/s both ways
+CALIB_COPY_BYTES = 256 << 20  # plain device copy run once for counter calibration
 IDX_ROW, KV_ROW = 128, 1152
 
 
@@ -49,6 +53,45 @@ def measure_h2d_ceiling(torch, nbytes: int = 1 << 30, reps: int = 5) -> float:
         best = max(best, nbytes / (time.perf_counter() - t0) / 1e9)
     del src, dst
     return best
+
+
+def calibration_copy(torch) -> None:
+    """One plain device-to-device copy of CALIB_COPY_BYTES, so that a counter
+    run of this script also holds a kernel with known bytes read and written
+    (the scale factor between the FETCH_SIZE / WRITE_SIZE counters and bytes)."""
+    src = torch.ones(CALIB_COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+# Kernel source file that each modelled stage is compiled from.
+KERNEL_SOURCE = {"score_hist": "select.hip", "gather_misses": "gather.hip",
+                 "attn_partial": "attention.hip"}
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary of this kernel
+    and workload, or None when there is none or the kernel's source changed
+    since the counters were taken (the summary records the source digest)."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    src = os.path.join(ROOT, "sparse_kv_offload_amd", "csrc", KERNEL_SOURCE.get(kernel, ""))
+    if not os.path.isfile(path) or not os.path.isfile(src):
+        return None
+    m = re.search(r"```json\n(.*?)```", open(path).read(), re.S)
+    if not m:
+        return None
+    entry = json.loads(m.group(1)).get(kernel)
+    if not entry:
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if entry.get("source_sha256_16") != digest:
+        return None
+    return entry.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(w, target_s: float) -> dict:
@@ -148,58 +191,86 @@ def main() -> int:
             sko.sko_append_token(h.handle, l, sko.SKO_ALL_SEQS, new_idx[t][l], new_kv[t][l], 1, True)
             sko.sko_decode_step(h.handle, l, q_idx[t][l], q_attn[t][l], out)
 
-    for t in range(args.warmup):
+    # Warm-up: the cold step untimed, then the remaining warm-up steps with
+    # every stage bracketed by events (the per-stage breakdown; each event
+    # pair costs device time, so the timed steps bracket only one stage).
+    nstage = sko.sko_num_stages()
+    run_step(0)
+    torch.cuda.synchronize()
+    calib_stats0 = [h.stats(l) for l in range(L)]
+    h.set_timing(0 if args.no_timing else (1 << nstage) - 1)
+    for t in range(1, args.warmup):
         run_step(t)
     torch.cuda.synchronize()
+    calib = h.timing() if (not args.no_timing and args.warmup > 1) else {}
     stats0 = [h.stats(l) for l in range(L)]
-    lt0 = w.context + args.warmup  # tokens present at the first timed step (after its append)
+    calib_steps = args.warmup - 1
 
-    h.set_timing(not args.no_timing)
+    dominant = None
+    if calib:
+        dominant = max(calib.items(), key=lambda kv: kv[1][0])[0]
+    timed_mask = 0 if dominant is None else (1 << sko.sko_stage_index(dominant))
+    h.set_timing(timed_mask)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for t in range(args.warmup, T):
         run_step(t)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    timing = h.timing() if not args.no_timing else {}
-    h.set_timing(False)
+    timing = h.timing() if timed_mask else {}
+    h.set_timing(0)
     stats1 = [h.stats(l) for l in range(L)]
 
     K = args.steps
     layer_steps = L * K
     value = layer_steps / elapsed
-    d = {f: sum(getattr(s1, f) - getattr(s0, f) for s0, s1 in zip(stats0, stats1))
-         for f in ("unique", "hits", "misses", "evictions", "h2d_bytes")}
-    # algorithmic bytes per launch (averaged over the timed launches)
-    avg_lt = lt0 + (K - 1) / 2.0
-    scan_bytes = IDX_ROW * B * avg_lt + IDX_ROW * B * D
-    gather_bytes = d["h2d_bytes"] / layer_steps
-    attn_bytes = KV_ROW * B * D * min(k, avg_lt)
+
+    def deltas(s0, s1):
+        return {f: sum(getattr(b, f) - getattr(a, f) for a, b in zip(s0, s1))
+                for f in ("unique", "hits", "misses", "evictions", "h2d_bytes")}
+
+    d = deltas(stats0, stats1)
+
+    def alg_bytes(first_step, nsteps, h2d_bytes):
+        """Algorithmic bytes per launch of the modelled kernels, averaged over
+        decode steps first_step .. first_step + nsteps - 1."""
+        avg_lt = w.context + first_step + (nsteps + 1) / 2.0  # tokens present after each append
+        ls = L * nsteps
+        return {"score_hist": (IDX_ROW * B * avg_lt + IDX_ROW * B * D, "hbm", HBM_PEAK_GBPS),
+                "gather_misses": (h2d_bytes / ls if ls else 0.0, "host-link", HOST_LINK_PEAK_GBPS),
+                "attn_partial": (KV_ROW * B * D * min(k, avg_lt), "hbm", HBM_PEAK_GBPS)}
 
     h2d_ceiling = measure_h2d_ceiling(torch)
+    calibration_copy(torch)
+
+    def roof_entry(name, ms, n, model):
+        nbytes, bound, peak = model[name]
+        avg = ms / n
+        ach = nbytes / (avg * 1e-3) / 1e9 if avg > 0 else 0.0
+        e = {"bound": bound, "achieved": round(ach, 2), "peak": round(peak, 2), "unit": "GB/s",
+             "frac": round(ach / peak, 4), "traffic": traffic_for(name, w.name), "kernel": name,
+             "avg_ms": round(avg, 5), "launches": n, "bytes_per_launch": int(nbytes)}
+        if bound == "host-link":
+            e["measured_ceiling"] = round(h2d_ceiling, 2)
+            e["frac_of_measured"] = round(ach / h2d_ceiling, 4)
+        return e
 
     rooflines = {}
-    if timing:
-        def kernel_avg_ms(name):
-            ms, n = timing.get(name, (0.0, 0))
-            return ms / n if n else float("nan")
-        for name, nbytes, bound, peak in (
-                ("score_hist", scan_bytes, "hbm", HBM_PEAK_GBPS),
-                ("gather_misses", gather_bytes, "host-link", h2d_ceiling),
-                ("attn_partial", attn_bytes, "hbm", HBM_PEAK_GBPS)):
-            avg = kernel_avg_ms(name)
-            ach = nbytes / (avg * 1e-3) / 1e9 if avg > 0 else 0.0
-            rooflines[name] = {"bound": bound, "achieved": round(ach, 2), "peak": round(peak, 2),
-                               "unit": "GB/s", "frac": round(ach / peak, 4), "traffic": None,
-                               "avg_ms": round(avg, 5), "bytes_per_launch": int(nbytes)}
-        dominant = max(timing.items(), key=lambda kv: kv[1][0])[0]
-        roof = rooflines.get(dominant)
-        if roof is None:  # a kernel without a bandwidth model dominates
+    if calib:
+        model = alg_bytes(1, calib_steps, deltas(calib_stats0, stats0)["h2d_bytes"])
+        for name in model:
+            ms, n = calib.get(name, (0.0, 0))
+            if n:
+                rooflines[name] = roof_entry(name, ms, n, model)
+    roof = None
+    if timing and dominant in timing:
+        model = alg_bytes(args.warmup, K, d["h2d_bytes"])
+        ms, n = timing[dominant]
+        if dominant in model:
+            roof = roof_entry(dominant, ms, n, model)
+        else:  # a kernel without a byte model dominates: report its time only
             roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": None, "traffic": None}
-        roof = dict(roof, kernel=dominant)
-    else:
-        roof, dominant = None, None
+                    "frac": None, "traffic": None, "kernel": dominant, "avg_ms": round(ms / n, 5)}
 
     result = {
         "metric": "sparse-offload decode layer-steps/s",
@@ -219,14 +290,18 @@ def main() -> int:
                    "parallelism": "none (1 GPU)", "pool": args.pool},
         "tokens_per_s": round(B * K / elapsed, 2),
         "indexer_scan_GBps": rooflines.get("score_hist", {}).get("achieved"),
-        "miss_gather_GBps": rooflines.get("gather_misses", {}).get("achieved"),
+        "miss_gather_GBps": (roof or {}).get("achieved") if dominant == "gather_misses"
+        else rooflines.get("gather_misses", {}).get("achieved"),
         "h2d_ceiling_GBps": round(h2d_ceiling, 2),
         "hit_rate": round(d["hits"] / max(1, d["unique"]), 4),
         "unique_misses_per_layer_step": round(d["misses"] / layer_steps, 1),
         "h2d_bytes_per_layer_step": int(d["h2d_bytes"] / layer_steps),
         "roofline": roof,
         "rooflines": rooflines,
-        "stage_ms_per_launch": {n: round(ms / c, 5) for n, (ms, c) in timing.items() if c},
+        "stage_ms_per_launch": {n: round(ms / c, 5) for n, (ms, c) in calib.items() if c},
+        "stage_timing_note": (f"stage breakdown from warm-up steps 1..{args.warmup - 1} with every stage "
+                              f"event-timed; the timed steps bracket only '{dominant}'")
+        if calib else None,
     }
     h.close()
     del new_idx, new_kv, q_idx, q_attn

@@ -197,14 +197,15 @@ int sko_read_table(sko_handle* h, int32_t layer, int32_t seq, int32_t which, voi
 int sko_get_stats(sko_handle* h, int32_t layer, sko_layer_stats* out);
 
 /*
- * Kernel timing: when enabled, every stage launch of sko_decode_step is
- * bracketed by HIP events on the handle's stream and the elapsed times are
- * accumulated per stage.  sko_set_timing (either value) synchronizes and
- * clears the totals.  sko_get_timing synchronizes and returns the totals
- * (ms) and launch counts for up to `n` stages; stage names come from
- * sko_stage_name.
+ * Kernel timing: stages whose bit is set in `stage_mask` (bit i = stage i,
+ * names from sko_stage_name) are bracketed by HIP events on the handle's
+ * stream, and the elapsed times are accumulated per stage.  Each event pair
+ * costs device time, so time only the stages of interest.  sko_set_timing
+ * (any mask, 0 disables) synchronizes and clears the totals.
+ * sko_get_timing synchronizes and returns the totals (ms) and launch counts
+ * for up to `n` stages.
  */
-int sko_set_timing(sko_handle* h, int32_t enable);
+int sko_set_timing(sko_handle* h, uint32_t stage_mask);
 int sko_get_timing(sko_handle* h, double* total_ms, int64_t* launches, int32_t n);
 const char* sko_stage_name(int32_t stage);
 int32_t sko_num_stages(void);

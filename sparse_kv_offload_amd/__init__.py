@@ -95,7 +95,7 @@ def _load() -> ctypes.CDLL:
         "sko_read_step": (ctypes.c_int, [vp, i32, vp, i64]),
         "sko_read_table": (ctypes.c_int, [vp, i32, i32, i32, vp, i64]),
         "sko_get_stats": (ctypes.c_int, [vp, i32, ctypes.POINTER(SkoLayerStats)]),
-        "sko_set_timing": (ctypes.c_int, [vp, i32]),
+        "sko_set_timing": (ctypes.c_int, [vp, ctypes.c_uint32]),
         "sko_get_timing": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int64), i32]),
         "sko_stage_name": (ctypes.c_char_p, [i32]),
@@ -203,8 +203,18 @@ def sko_get_stats(h: int, layer: int) -> SkoLayerStats:
     return st
 
 
-def sko_set_timing(h: int, enable: bool) -> None:
-    _check(_lib.sko_set_timing(h, int(bool(enable))), "sko_set_timing")
+def sko_set_timing(h: int, stage_mask) -> None:
+    """stage_mask: int bit mask, True (all stages) or False/0 (off)."""
+    if stage_mask is True:
+        stage_mask = 0xFFFFFFFF
+    _check(_lib.sko_set_timing(h, int(stage_mask) & 0xFFFFFFFF), "sko_set_timing")
+
+
+def sko_stage_index(name: str) -> int:
+    for i in range(sko_num_stages()):
+        if sko_stage_name(i) == name:
+            return i
+    raise KeyError(name)
 
 
 def sko_get_timing(h: int) -> dict:
@@ -292,8 +302,8 @@ class SparseKVOffload:
     def stats(self, layer: int) -> SkoLayerStats:
         return sko_get_stats(self.handle, layer)
 
-    def set_timing(self, enable: bool) -> None:
-        sko_set_timing(self.handle, enable)
+    def set_timing(self, stage_mask) -> None:
+        sko_set_timing(self.handle, stage_mask)
 
     def timing(self) -> dict:
         return sko_get_timing(self.handle)

@@ -109,10 +109,11 @@ struct sko_handle {
     float* part_acc = nullptr;      // [B*D][HG][nchunk][16][512]
     float* part_ml = nullptr;       // [B*D][HG][nchunk][16][2]
     int rows_per_block = 32, nchunk = 1;
+    int cu_count = 256;  // compute units of the device (launch sizing)
     int last_layer = -1;
 
     // timing
-    bool timing = false;
+    uint32_t timing_mask = 0;
     struct Pending {
         int stage;
         hipEvent_t a, b;
@@ -164,8 +165,11 @@ hipEvent_t take_event(sko_handle* h) {
         h->spare.pop_back();
         return e;
     }
+    // Timing-only events: the totals are read after a stream synchronize, so
+    // the event needs no system-scope fence (which would write back and
+    // invalidate caches between the kernels it brackets).
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
 }
 
@@ -173,14 +177,15 @@ hipEvent_t take_event(sko_handle* h) {
 template <typename F>
 int run_stage(sko_handle* h, int stage, F&& launch) {
     hipEvent_t a = nullptr, b = nullptr;
-    if (h->timing) {
+    const bool timed = (h->timing_mask >> stage) & 1u;
+    if (timed) {
         a = take_event(h);
         b = take_event(h);
         if (a) (void)hipEventRecord(a, h->stream);
     }
     hipError_t e = launch();
     if (e != hipSuccess) return device_fail(h, e, kStageNames[stage]);
-    if (h->timing && a && b) {
+    if (timed && a && b) {
         (void)hipEventRecord(b, h->stream);
         h->pending.push_back({stage, a, b});
     }
@@ -270,6 +275,11 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     h->wpr = winner_words(h->cap);
     h->ntok.assign((size_t)h->L * h->B, 0);
     h->step.assign((size_t)h->L, 0);
+    {
+        int ncu = 0;
+        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, cfg->device) == hipSuccess && ncu > 0)
+            h->cu_count = ncu;
+    }
     h->rows_per_block = attn_rows_per_block(h->k, h->B * h->D * h->HG);
     h->nchunk = (h->k + h->rows_per_block - 1) / h->rows_per_block;
 
@@ -456,7 +466,7 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
 
     if ((rc = run_stage(h, ST_SCORE, [&] {
              return launch_score_hist(h->stream, idx_layer, qi, ntok, h->keys, h->hist, B, D, h->kcap, h->ntiles,
-                                      max_now);
+                                      max_now, h->cu_count);
          })))
         return rc;
     if ((rc = run_stage(h, ST_FILTER, [&] {
@@ -578,7 +588,7 @@ int sko_get_stats(sko_handle* h, int32_t layer, sko_layer_stats* out) {
     return SKO_OK;
 }
 
-int sko_set_timing(sko_handle* h, int32_t enable) {
+int sko_set_timing(sko_handle* h, uint32_t stage_mask) {
     int rc = check_handle(h);
     if (rc != SKO_OK) return rc;
     DeviceGuard guard(h->cfg.device);
@@ -592,7 +602,7 @@ int sko_set_timing(sko_handle* h, int32_t enable) {
         h->total_ms[i] = 0.0;
         h->launches[i] = 0;
     }
-    h->timing = enable != 0;
+    h->timing_mask = stage_mask;
     return SKO_OK;
 }
 

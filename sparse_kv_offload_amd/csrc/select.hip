@@ -114,13 +114,18 @@ __device__ void threshold_row(const uint32_t* __restrict__ h, RowMeta* __restric
 
 // ---------------------------------------------------------------- score
 
-// A block scores `tiles_per_block` tiles of 64 tokens of one sequence for NP
-// query positions (p0 .. p0+NP-1).  Wave w takes tiles w, w+4, ...; lane l
-// owns token 64*tile + l and reads its row as 8 loads of 16 bytes, each a
-// coalesced 1 KB run of the tiled layout.  Every position runs its 64-term
-// FMA chain in index order.  The first-digit histogram is counted in LDS
-// with two 16-bit counters per word (< 65536 tokens per block) and flushed
-// with one global atomic per non-empty bin.
+// Score pass over the flattened (sequence, tile) space of B * tiles_now
+// tiles of 64 tokens: block j takes the contiguous range
+// [j * total / nblocks, (j + 1) * total / nblocks), and the launch holds at
+// most as many blocks as the chip keeps resident at once, so every block
+// gets the same share and no second round of blocks forms a tail.  A range
+// is cut at sequence boundaries into segments; within a segment wave w takes
+// tiles w, w+4, ...; lane l owns token 64*tile + l and reads its row as 8
+// loads of 16 bytes, each a coalesced 1 KB run of the tiled layout.  Every
+// position p0 .. p0+NP-1 runs its 64-term FMA chain in index order.  The
+// first-digit histogram of a segment is counted in LDS with two 16-bit
+// counters per word (a range holds fewer than 65536 tokens) and flushed with
+// one global atomic per non-empty bin.
 template <int NP>
 __global__ __launch_bounds__(256) void k_score_hist(const uint4* __restrict__ idx_layer,
                                                     const uint32_t* __restrict__ q_idx,
@@ -128,20 +133,25 @@ __global__ __launch_bounds__(256) void k_score_hist(const uint4* __restrict__ id
                                                     uint32_t* __restrict__ keys,
                                                     uint32_t* __restrict__ hist,
                                                     int D, int p0, int64_t kcap, int64_t ntiles,
-                                                    int tiles_per_block) {
+                                                    int64_t tiles_now, int64_t total_tiles) {
     constexpr int HW = kHistBins / 2;  // packed words per position
     __shared__ uint32_t sh[NP * HW];
-    const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t Lt = ntok_layer[b];
-    const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_block;
-    if (tile0 * kIdxTile >= Lt) return;
-    {
-        for (int i = threadIdx.x; i < NP * HW; i += blockDim.x) sh[i] = 0u;
-        __syncthreads();
+    const int64_t r_begin = (int64_t)blockIdx.x * total_tiles / gridDim.x;
+    const int64_t r_end = ((int64_t)blockIdx.x + 1) * total_tiles / gridDim.x;
+    for (int i = threadIdx.x; i < NP * HW; i += blockDim.x) sh[i] = 0u;
+    __syncthreads();
+    for (int64_t seg = r_begin; seg < r_end;) {
+        const int b = (int)(seg / tiles_now);
+        const int64_t seg_end = std::min<int64_t>(r_end, ((int64_t)b + 1) * tiles_now);
+        const int64_t Lt = ntok_layer[b];
+        const int64_t tile0 = seg - (int64_t)b * tiles_now;
+        const int64_t tile_end = std::min<int64_t>(seg_end - (int64_t)b * tiles_now,
+                                                   (Lt + kIdxTile - 1) / kIdxTile);
+        seg = seg_end;
+        if (tile0 >= tile_end) continue;  // block-uniform: nothing of this sequence here
         const uint32_t* __restrict__ qb = q_idx + ((size_t)b * D + p0) * (kIdxDim / 2);
         uint32_t* __restrict__ keyrow = keys + ((size_t)b * D + p0) * kcap;
-        const int64_t tile_end = std::min<int64_t>(tile0 + tiles_per_block, (Lt + kIdxTile - 1) / kIdxTile);
         const uint4* __restrict__ seq_tiles = idx_layer + (size_t)b * ntiles * kIdxRowU4 * kIdxTile + lane;
         // Ping-pong over two register tiles: the next tile's 8 loads are in
         // flight while this tile's FMA chains run.  Loads are unconditional
@@ -188,45 +198,67 @@ __global__ __launch_bounds__(256) void k_score_hist(const uint4* __restrict__ id
         };
         uint4 ra[kIdxRowU4], rb[kIdxRowU4];
         int64_t tile = tile0 + wave;
-        load_tile(ra, tile);
-        for (; tile < tile_end; tile += 8) {
-            load_tile(rb, tile + 4);
-            score_tile(ra, tile);
-            if (tile + 4 >= tile_end) break;
-            load_tile(ra, tile + 8);
-            score_tile(rb, tile + 4);
+        if (tile < tile_end) {
+            load_tile(ra, tile);
+            for (; tile < tile_end; tile += 8) {
+                load_tile(rb, tile + 4);
+                score_tile(ra, tile);
+                if (tile + 4 >= tile_end) break;
+                load_tile(ra, tile + 8);
+                score_tile(rb, tile + 4);
+            }
         }
         __syncthreads();
         for (int i = threadIdx.x; i < NP * HW; i += blockDim.x) {
             const uint32_t v = sh[i];
             if (v == 0u) continue;
+            sh[i] = 0u;
             const int p = i / HW;
             const int bin = (i - p * HW) * 2;
             uint32_t* h = hist + ((size_t)b * D + p0 + p) * kHistBins;
             if (v & 0xFFFFu) atomicAdd(&h[bin], v & 0xFFFFu);
             if (v >> 16) atomicAdd(&h[bin + 1], v >> 16);
         }
+        __syncthreads();
     }
 }
 
+namespace {
+template <int NP>
+int score_blocks_per_cu() {
+    static const int n = [] {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void*>(&k_score_hist<NP>), 256, 0) !=
+                hipSuccess || v < 1)
+            v = 1;
+        return v;
+    }();
+    return n;
+}
+}  // namespace
+
 hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const uint16_t* q_idx,
                              const int32_t* ntok_layer, uint32_t* keys, uint32_t* hist, int B, int D,
-                             int64_t kcap, int64_t ntiles, int64_t max_tokens_now) {
+                             int64_t kcap, int64_t ntiles, int64_t max_tokens_now, int cu_count) {
     const int64_t tiles_now = std::max<int64_t>(1, (max_tokens_now + kIdxTile - 1) / kIdxTile);
-    // about a thousand blocks with several tiles per wave; at most 1023
-    // tiles (65472 tokens) per block for the 16-bit LDS counters
-    int tpb = 8;
-    while (tpb < 512 && (int64_t)B * ((tiles_now + 2 * tpb - 1) / (2 * tpb)) >= 1024) tpb *= 2;
-    const dim3 grid((unsigned)((tiles_now + tpb - 1) / tpb), (unsigned)B);
+    const int64_t total = (int64_t)B * tiles_now;
     const uint4* kb = reinterpret_cast<const uint4*>(idx_layer);
     const uint32_t* q = reinterpret_cast<const uint32_t*>(q_idx);
     for (int p0 = 0; p0 < D; p0 += 4) {
         const int np = std::min(4, D - p0);
+        const int per_cu = np == 1 ? score_blocks_per_cu<1>() : np == 2 ? score_blocks_per_cu<2>()
+                         : np == 3 ? score_blocks_per_cu<3>() : score_blocks_per_cu<4>();
+        // one resident round of blocks, at least 4 tiles (one per wave) per
+        // block, and fewer than 1024 tiles per block for the 16-bit counters
+        int64_t nb = std::min<int64_t>((int64_t)cu_count * per_cu, (total + 3) / 4);
+        nb = std::max<int64_t>(nb, (total + 1000) / 1001);
+        nb = std::max<int64_t>(nb, 1);
+        const dim3 grid((unsigned)nb);
         switch (np) {
-            case 1: hipLaunchKernelGGL(k_score_hist<1>, grid, dim3(256), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tpb); break;
-            case 2: hipLaunchKernelGGL(k_score_hist<2>, grid, dim3(256), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tpb); break;
-            case 3: hipLaunchKernelGGL(k_score_hist<3>, grid, dim3(256), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tpb); break;
-            default: hipLaunchKernelGGL(k_score_hist<4>, grid, dim3(256), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tpb); break;
+            case 1: hipLaunchKernelGGL(k_score_hist<1>, grid, dim3(256), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
+            case 2: hipLaunchKernelGGL(k_score_hist<2>, grid, dim3(256), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
+            case 3: hipLaunchKernelGGL(k_score_hist<3>, grid, dim3(256), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
+            default: hipLaunchKernelGGL(k_score_hist<4>, grid, dim3(256), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -72,7 +72,7 @@ hipError_t launch_append_rows(hipStream_t st, const uint16_t* idx_src, const uin
                               int32_t base);
 hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const uint16_t* q_idx,
                              const int32_t* ntok_layer, uint32_t* keys, uint32_t* hist, int B, int D,
-                             int64_t kcap, int64_t ntiles, int64_t max_tokens_now);
+                             int64_t kcap, int64_t ntiles, int64_t max_tokens_now, int cu_count);
 hipError_t launch_topk_filter(hipStream_t st, const uint32_t* keys, const uint32_t* hist, RowMeta* meta,
                               uint2* cand, int32_t* topk, const int32_t* cache_slots_layer,
                               const int32_t* ntok_layer, uint32_t* winners, int B, int D,
