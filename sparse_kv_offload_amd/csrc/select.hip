@@ -119,15 +119,21 @@ __device__ void threshold_row(const uint32_t* __restrict__ h, RowMeta* __restric
 // [j * total / nblocks, (j + 1) * total / nblocks), and the launch holds at
 // most as many blocks as the chip keeps resident at once, so every block
 // gets the same share and no second round of blocks forms a tail.  A range
-// is cut at sequence boundaries into segments; within a segment wave w takes
-// tiles w, w+4, ...; lane l owns token 64*tile + l and reads its row as 8
+// is cut at sequence boundaries into segments; within a segment wave w of
+// the block's nw waves takes tiles w, w+nw, ...; lane l owns token
+// 64*tile + l and reads its row as 8
 // loads of 16 bytes, each a coalesced 1 KB run of the tiled layout.  Every
 // position p0 .. p0+NP-1 runs its 64-term FMA chain in index order.  The
 // first-digit histogram of a segment is counted in LDS with two 16-bit
 // counters per word (a range holds fewer than 65536 tokens) and flushed with
-// one global atomic per non-empty bin.
+// one 64-bit global atomic per non-empty pair of bins.  Blocks are large
+// (all the waves one CU holds at this kernel's register use), so a row is
+// split over few blocks and its bins receive few atomics.
 template <int NP>
-__global__ __launch_bounds__(256) void k_score_hist(const uint4* __restrict__ idx_layer,
+constexpr int score_threads() { return NP == 1 ? 640 : 768; }
+
+template <int NP>
+__global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(const uint4* __restrict__ idx_layer,
                                                     const uint32_t* __restrict__ q_idx,
                                                     const int32_t* __restrict__ ntok_layer,
                                                     uint32_t* __restrict__ keys,
@@ -137,6 +143,7 @@ __global__ __launch_bounds__(256) void k_score_hist(const uint4* __restrict__ id
     constexpr int HW = kHistBins / 2;  // packed words per position
     __shared__ uint32_t sh[NP * HW];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int nw = score_threads<NP>() / 64;
     const int64_t r_begin = (int64_t)blockIdx.x * total_tiles / gridDim.x;
     const int64_t r_end = ((int64_t)blockIdx.x + 1) * total_tiles / gridDim.x;
     for (int i = threadIdx.x; i < NP * HW; i += blockDim.x) sh[i] = 0u;
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(256) void k_score_hist(const uint4* __restrict__ id
         auto load_tile = [&](uint4* r, int64_t tile) {
             const int64_t tl = tile < last ? tile : last;
 #pragma unroll
-            for (int c = 0; c < kIdxRowU4; ++c) r[c] = seq_tiles[(tl * kIdxRowU4 + c) * kIdxTile];
+            for (int c = 0; c < kIdxRowU4; ++c) r[c] = load_nt_u4(seq_tiles + (tl * kIdxRowU4 + c) * kIdxTile);
         };
         // the chains run for every lane (lanes past the last token compute on
         // a clamped in-bounds row and store nothing), so every loaded
@@ -200,12 +207,12 @@ __global__ __launch_bounds__(256) void k_score_hist(const uint4* __restrict__ id
         int64_t tile = tile0 + wave;
         if (tile < tile_end) {
             load_tile(ra, tile);
-            for (; tile < tile_end; tile += 8) {
-                load_tile(rb, tile + 4);
+            for (; tile < tile_end; tile += 2 * nw) {
+                load_tile(rb, tile + nw);
                 score_tile(ra, tile);
-                if (tile + 4 >= tile_end) break;
-                load_tile(ra, tile + 8);
-                score_tile(rb, tile + 4);
+                if (tile + nw >= tile_end) break;
+                load_tile(ra, tile + 2 * nw);
+                score_tile(rb, tile + nw);
             }
         }
         __syncthreads();
@@ -215,9 +222,12 @@ __global__ __launch_bounds__(256) void k_score_hist(const uint4* __restrict__ id
             sh[i] = 0u;
             const int p = i / HW;
             const int bin = (i - p * HW) * 2;
+            // bins 2m and 2m+1 are adjacent 32-bit counters: one 64-bit
+            // atomic adds both (a row holds fewer than 2^31 tokens, so the
+            // low counter never carries into the high one)
             uint32_t* h = hist + ((size_t)b * D + p0 + p) * kHistBins;
-            if (v & 0xFFFFu) atomicAdd(&h[bin], v & 0xFFFFu);
-            if (v >> 16) atomicAdd(&h[bin + 1], v >> 16);
+            const unsigned long long add = (unsigned long long)(v & 0xFFFFu) | ((unsigned long long)(v >> 16) << 32);
+            atomicAdd(reinterpret_cast<unsigned long long*>(h + bin), add);
         }
         __syncthreads();
     }
@@ -228,7 +238,8 @@ template <int NP>
 int score_blocks_per_cu() {
     static const int n = [] {
         int v = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void*>(&k_score_hist<NP>), 256, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void*>(&k_score_hist<NP>),
+                                                         score_threads<NP>(), 0) !=
                 hipSuccess || v < 1)
             v = 1;
         return v;
@@ -248,17 +259,18 @@ hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const ui
         const int np = std::min(4, D - p0);
         const int per_cu = np == 1 ? score_blocks_per_cu<1>() : np == 2 ? score_blocks_per_cu<2>()
                          : np == 3 ? score_blocks_per_cu<3>() : score_blocks_per_cu<4>();
-        // one resident round of blocks, at least 4 tiles (one per wave) per
-        // block, and fewer than 1024 tiles per block for the 16-bit counters
-        int64_t nb = std::min<int64_t>((int64_t)cu_count * per_cu, (total + 3) / 4);
+        const int nw = (np == 1 ? score_threads<1>() : np == 2 ? score_threads<2>() : score_threads<4>()) / 64;
+        // one resident round of blocks, at least one tile per wave, and
+        // fewer than 1024 tiles per block for the 16-bit counters
+        int64_t nb = std::min<int64_t>((int64_t)cu_count * per_cu, (total + nw - 1) / nw);
         nb = std::max<int64_t>(nb, (total + 1000) / 1001);
         nb = std::max<int64_t>(nb, 1);
         const dim3 grid((unsigned)nb);
         switch (np) {
-            case 1: hipLaunchKernelGGL(k_score_hist<1>, grid, dim3(256), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
-            case 2: hipLaunchKernelGGL(k_score_hist<2>, grid, dim3(256), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
-            case 3: hipLaunchKernelGGL(k_score_hist<3>, grid, dim3(256), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
-            default: hipLaunchKernelGGL(k_score_hist<4>, grid, dim3(256), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
+            case 1: hipLaunchKernelGGL(k_score_hist<1>, grid, dim3(score_threads<1>()), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
+            case 2: hipLaunchKernelGGL(k_score_hist<2>, grid, dim3(score_threads<2>()), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
+            case 3: hipLaunchKernelGGL(k_score_hist<3>, grid, dim3(score_threads<3>()), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
+            default: hipLaunchKernelGGL(k_score_hist<4>, grid, dim3(score_threads<4>()), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
