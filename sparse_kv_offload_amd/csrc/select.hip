@@ -24,6 +24,8 @@
 // Winners are written packed (bit 31 = absent from the hot buffer at step
 // start) and also marked in a per-sequence bitmap over tokens, which the
 // merge stage reads in token order (union and dedupe of the D positions).
+#include <utility>
+
 #include "sko_common.cuh"
 #include "sko_internal.h"
 
@@ -114,6 +116,29 @@ __device__ void threshold_row(const uint32_t* __restrict__ h, RowMeta* __restric
 
 // ---------------------------------------------------------------- score
 
+// acc = fma(q, k, acc) with q taken from lane E % 16 of the 16-lane row of
+// qv (every row of qv holds the same 16 query values): the broadcast rides
+// on the DPP source operand of the fused multiply-add, so the query costs
+// no scalar or extra vector instruction.
+template <int E>
+__device__ __forceinline__ float fma_row_bcast(float qv, float k, float acc) {
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc)
+        : "v"(qv), "v"(k), "n"(E % 16));
+    return acc;
+}
+
+// One position's 64-term chain over the 32 packed key words of this lane's
+// token, terms in index order e = 0..63 (e even: low half of word e/2, odd:
+// high half); vq[e / 16] holds query terms 16*(e/16) .. +15 as above.
+template <int... E>
+__device__ __forceinline__ float score_chain(const float (&vq)[4], const uint32_t (&w)[32],
+                                             std::integer_sequence<int, E...>) {
+    float acc = 0.0f;
+    ((acc = fma_row_bcast<E>(vq[E / 16], (E & 1) ? bf16_hi(w[E / 2]) : bf16_lo(w[E / 2]), acc)), ...);
+    return acc;
+}
+
 // Score pass over the flattened (sequence, tile) space of B * tiles_now
 // tiles of 64 tokens: block j takes the contiguous range
 // [j * total / nblocks, (j + 1) * total / nblocks), and the launch holds at
@@ -157,7 +182,19 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(const uint4*
                                                    (Lt + kIdxTile - 1) / kIdxTile);
         seg = seg_end;
         if (tile0 >= tile_end) continue;  // block-uniform: nothing of this sequence here
+        // query terms of positions p0.. as binary32, 16 per register
+        // (replicated in the four 16-lane rows): vq[p][m] lane l holds term
+        // 16*m + (l % 16) of position p0 + p
         const uint32_t* __restrict__ qb = q_idx + ((size_t)b * D + p0) * (kIdxDim / 2);
+        float vq[NP][4];
+        if constexpr (NP > 1) {
+            const uint16_t* qh = reinterpret_cast<const uint16_t*>(q_idx) + ((size_t)b * D + p0) * kIdxDim;
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    vq[p][m] = __uint_as_float((uint32_t)qh[p * kIdxDim + 16 * m + (lane & 15)] << 16);
+        }
         uint32_t* __restrict__ keyrow = keys + ((size_t)b * D + p0) * kcap;
         const uint4* __restrict__ seq_tiles = idx_layer + (size_t)b * ntiles * kIdxRowU4 * kIdxTile + lane;
         // Ping-pong over two register tiles: the next tile's 8 loads are in
@@ -186,12 +223,18 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(const uint4*
             }
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                float acc = 0.0f;
+                float acc;
+                if constexpr (NP == 1) {
+                    // one position: its 32 query words fit in scalar registers
+                    acc = 0.0f;
 #pragma unroll
-                for (int j = 0; j < 32; ++j) {
-                    const uint32_t qw = qb[p * 32 + j];
-                    acc = __builtin_fmaf(bf16_lo(qw), bf16_lo(w[j]), acc);
-                    acc = __builtin_fmaf(bf16_hi(qw), bf16_hi(w[j]), acc);
+                    for (int j = 0; j < 32; ++j) {
+                        const uint32_t qw = qb[j];
+                        acc = __builtin_fmaf(bf16_lo(qw), bf16_lo(w[j]), acc);
+                        acc = __builtin_fmaf(bf16_hi(qw), bf16_hi(w[j]), acc);
+                    }
+                } else {
+                    acc = score_chain(vq[p], w, std::make_integer_sequence<int, 64>{});
                 }
                 if (acc == 0.0f) acc = 0.0f;  // store a zero as +0
                 uint32_t key = score_key(acc);
