@@ -227,7 +227,7 @@ def main() -> int:
 
     def deltas(s0, s1):
         return {f: sum(getattr(b, f) - getattr(a, f) for a, b in zip(s0, s1))
-                for f in ("unique", "hits", "misses", "evictions", "h2d_bytes")}
+                for f in ("unique", "hits", "misses", "evictions", "h2d_bytes", "rescans")}
 
     d = deltas(stats0, stats1)
 
@@ -296,6 +296,7 @@ def main() -> int:
         "hit_rate": round(d["hits"] / max(1, d["unique"]), 4),
         "unique_misses_per_layer_step": round(d["misses"] / layer_steps, 1),
         "h2d_bytes_per_layer_step": int(d["h2d_bytes"] / layer_steps),
+        "selection_rescans": d["rescans"],
         "roofline": roof,
         "rooflines": rooflines,
         "stage_ms_per_launch": {n: round(ms / c, 5) for n, (ms, c) in calib.items() if c},

@@ -61,6 +61,12 @@ extern "C" {
  * HIP runtime's default coherence for mapped pinned memory. */
 #define SKO_FLAG_POOL_COHERENT 0x1u    /* fine-grained: device reads bypass its caches */
 #define SKO_FLAG_POOL_NONCOHERENT 0x2u /* coarse-grained: device may cache pool lines */
+/* Also store every score key of each step (readable with SKO_BUF_KEYS);
+ * costs 4 bytes per token and position of HBM writes in the score pass. */
+#define SKO_FLAG_KEEP_KEYS 0x4u
+/* Testing: no candidate floor, so every step selects through the rescan
+ * path (same results, slower). */
+#define SKO_FLAG_SELECT_RESCAN 0x8u
 
 typedef struct sko_handle sko_handle;
 
@@ -100,6 +106,8 @@ typedef struct sko_layer_stats {
     int64_t misses;
     int64_t evictions;
     int64_t h2d_bytes; /* misses * 1152 */
+    int64_t rescans;   /* (seq, position) rows whose threshold fell below the
+                          candidate floor, so the filter rescanned the row */
 } sko_layer_stats;
 
 /*
@@ -153,6 +161,10 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
  *   out     device [B][D][H][512] fp32 attention output
  * A sequence with no tokens selects nothing and gets a zero output.
  * The layer's step stamp advances by one per call.
+ * Selection keeps, per (seq, position), the scored keys at or above a floor
+ * set half an octave of score below the previous step's threshold; when
+ * fewer than k keys reach it the row is rescanned from the indexer.  Both
+ * paths give the same winners (the first step of a layer keeps every key).
  * Errors: SKO_E_INVAL (bad layer or NULL pointer), SKO_E_STATE, SKO_E_DEVICE.
  */
 int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void* q_attn,
@@ -166,7 +178,8 @@ enum sko_step_buffer {
     SKO_BUF_MISSES = 4,    /* int32 [B][D*k]: miss tokens ascending, first `misses` valid */
     SKO_BUF_VICTIMS = 5,   /* int32 [B][D*k]: slot given to MISSES[r] */
     SKO_BUF_EVICT_OLD = 6, /* int32 [B][D*k]: previous owner of VICTIMS[r] or -1 */
-    SKO_BUF_KEYS = 7       /* uint32 [B][D][cap]: ordered score keys, first `tokens` valid */
+    SKO_BUF_KEYS = 7       /* uint32 [B][D][cap]: ordered score keys, first `tokens` valid;
+                              only with SKO_FLAG_KEEP_KEYS, else SKO_E_STATE */
 };
 
 /*

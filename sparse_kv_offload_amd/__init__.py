@@ -33,6 +33,8 @@ SKO_INDEX_DIM, SKO_KV_DIM, SKO_V_DIM = 64, 576, 512
 SKO_MAX_MERGE = 8192
 SKO_FLAG_POOL_COHERENT = 0x1
 SKO_FLAG_POOL_NONCOHERENT = 0x2
+SKO_FLAG_KEEP_KEYS = 0x4
+SKO_FLAG_SELECT_RESCAN = 0x8
 
 SKO_BUF_TOPK, SKO_BUF_PHYS, SKO_BUF_COUNTS = 1, 2, 3
 SKO_BUF_MISSES, SKO_BUF_VICTIMS, SKO_BUF_EVICT_OLD, SKO_BUF_KEYS = 4, 5, 6, 7
@@ -71,7 +73,7 @@ class SkoSeqCounts(ctypes.Structure):
 
 class SkoLayerStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
-                ("steps", "unique", "hits", "misses", "evictions", "h2d_bytes")]
+                ("steps", "unique", "hits", "misses", "evictions", "h2d_bytes", "rescans")]
 
 
 class SkoError(RuntimeError):

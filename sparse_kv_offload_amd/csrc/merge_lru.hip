@@ -40,8 +40,10 @@ __device__ __forceinline__ bool is_touched(const uint32_t* touched, int32_t s) {
     return (touched[s >> 5] >> (s & 31)) & 1u;
 }
 
+// Staged bucket entries are (key, token | miss << 31): the low word is the
+// packed winner value, the token is its low 31 bits.
 __device__ __forceinline__ uint64_t refine_composite(uint2 e) {
-    return ((uint64_t)(e.x & 0xFFFFFu) << 32) | (uint64_t)(0xFFFFFFFFu - e.y);
+    return ((uint64_t)(e.x & 0xFFFFFu) << 32) | (uint64_t)(0xFFFFFFFFu - (e.y & 0x7FFFFFFFu));
 }
 
 // Exact selection inside split threshold buckets.  For each row whose
@@ -63,7 +65,7 @@ struct RefineGroup {
 };
 
 __device__ __forceinline__ void refine_rows(int b, int D, RowMeta* __restrict__ meta, const uint2* __restrict__ cand,
-                                            int32_t* __restrict__ topk, const int32_t* __restrict__ cs,
+                                            int32_t* __restrict__ topk,
                                             uint32_t* __restrict__ wb, int top_k, int64_t cap, uint2* stage,
                                             uint32_t (*hg)[256], RefineGroup* gs) {
     const int NG = D < 4 ? D : 4;
@@ -167,9 +169,9 @@ __device__ __forceinline__ void refine_rows(int b, int D, RowMeta* __restrict__ 
                 const bool win = valid && refine_composite(e) >= T;
                 const int pw = wave_append(&meta[G.row].out_count, win);
                 if (win && pw < top_k) {
-                    const bool miss = cs[e.y] == -1;
-                    topk[(size_t)G.row * top_k + pw] = (int32_t)(e.y | (miss ? 0x80000000u : 0u));
-                    atomicOr(&wb[e.y >> 5], 1u << (e.y & 31u));
+                    const uint32_t tok = e.y & 0x7FFFFFFFu;
+                    topk[(size_t)G.row * top_k + pw] = (int32_t)e.y;
+                    atomicOr(&wb[tok >> 5], 1u << (tok & 31u));
                 }
             }
         }
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     const int SW = (S + 31) / 32;
 
     // 0. finish the top-k of rows whose threshold bucket is split
-    refine_rows(b, D, meta, cand, topk, cs, wb, top_k, cap, cstage, hgrp, rgrp);
+    refine_rows(b, D, meta, cand, topk, wb, top_k, cap, cstage, hgrp, rgrp);
 
     for (int i = tid; i < SW; i += kLruThreads) touched[i] = 0u;
     if (tid == 0) cnt[7] = 0;
@@ -414,10 +416,17 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
         if (tid == 0) ring_state_layer[b] = RingState{head, tail + ntouched, cur, {0, 0, 0}};
     }
 
-    // 6. counters; clear this sequence's selection scratch for the next step
+    // 6. counters (rows that were rescanned); clear this sequence's selection
+    // scratch for the next step
+    __shared__ int s_rescans;
+    if (tid == 0) s_rescans = 0;
+    __syncthreads();
+    if (tid < D && meta[b * D + tid].pre_count < kk) atomicAdd(&s_rescans, 1);
+    __syncthreads();
     for (int i = tid; i < D * kHistBins; i += kLruThreads) hist[(size_t)b * D * kHistBins + i] = 0u;
-    if (tid < D) meta[b * D + tid] = RowMeta{-1, 0, 0, 0, 0, 0, {0, 0}};
+    if (tid < D) meta[b * D + tid] = RowMeta{-1, 0, 0, 0, 0, 0, 0, 0};
     if (tid == 0) {
+        if (s_rescans) atomicAdd(&layer_stats[5], (unsigned long long)s_rescans);
         cnt[0] = nU; cnt[1] = nH; cnt[2] = nM; cnt[3] = nEv;
         cnt[4] = kk; cnt[5] = (int32_t)Lt; cnt[6] = t;
         atomicAdd(&layer_stats[1], (unsigned long long)nU);

@@ -94,7 +94,9 @@ struct sko_handle {
     std::vector<int32_t> step;      // [L]
 
     // per-step scratch (shared by all layers; steps are stream-ordered)
-    uint32_t* keys = nullptr;       // [B][D][kcap]
+    uint32_t* keys = nullptr;       // [B][D][kcap], only with SKO_FLAG_KEEP_KEYS
+    uint2* pre = nullptr;           // [B][D][cap] candidates at or above the floor
+    int32_t* floor = nullptr;       // [L][B][D] candidate floor (first-digit bin)
     uint32_t* hist = nullptr;       // [B][D][4096]
     RowMeta* meta = nullptr;        // [B][D]
     uint2* cand = nullptr;          // [B][D][cap]
@@ -212,7 +214,8 @@ int validate_config(const sko_config* c) {
                        (long long)c->mtp_positions * c->top_k);
     if (!(c->attn_scale > 0.0f) || !std::isfinite(c->attn_scale))
         return set_err(SKO_E_INVAL, "attn_scale must be finite and > 0");
-    if ((c->flags & ~(SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT)) != 0 ||
+    if ((c->flags & ~(SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT | SKO_FLAG_KEEP_KEYS |
+                      SKO_FLAG_SELECT_RESCAN)) != 0 ||
         (c->flags & (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT)) ==
             (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT))
         return set_err(SKO_E_INVAL, "unknown or conflicting flags 0x%x", c->flags);
@@ -315,7 +318,9 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     ok = ok && dev_alloc(h, (void**)&h->ring_state, LB * sizeof(RingState));
     ok = ok && dev_alloc(h, (void**)&h->ntok_dev, LB * 4);
     ok = ok && dev_alloc(h, (void**)&h->stats, (size_t)h->L * 8 * 8);
-    ok = ok && dev_alloc(h, (void**)&h->keys, BD * h->kcap * 4);
+    if (cfg->flags & SKO_FLAG_KEEP_KEYS) ok = ok && dev_alloc(h, (void**)&h->keys, BD * h->kcap * 4);
+    ok = ok && dev_alloc(h, (void**)&h->pre, BD * h->cap * sizeof(uint2));
+    ok = ok && dev_alloc(h, (void**)&h->floor, LB * h->D * 4);
     ok = ok && dev_alloc(h, (void**)&h->winners, (size_t)h->B * h->wpr * 4);
     ok = ok && dev_alloc(h, (void**)&h->hist, BD * kHistBins * 4);
     ok = ok && dev_alloc(h, (void**)&h->meta, BD * sizeof(RowMeta));
@@ -348,6 +353,12 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     // selection scratch starts cleared; every step's merge clears it again
     if (e == hipSuccess) e = hipMemsetAsync(h->hist, 0, BD * kHistBins * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->meta, 0, BD * sizeof(RowMeta), h->stream);
+    if (e == hipSuccess) {
+        // first step: every key is a candidate (or none, to force the rescan path)
+        const std::vector<int32_t> fl(LB * h->D, (cfg->flags & SKO_FLAG_SELECT_RESCAN) ? kFloorRescanAll : 0);
+        e = hipMemcpyAsync(h->floor, fl.data(), fl.size() * 4, hipMemcpyHostToDevice, h->stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+    }
     if (e == hipSuccess) e = hipMemsetAsync(h->idx, 0, LB * h->ntiles * kIdxTile * kIdxDim * 2, h->stream);
     if (e == hipSuccess) e = launch_init_rings(h->stream, h->ring[0], h->ring_pos, h->ring_state, (int64_t)LB, h->S, h->C);
     if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
@@ -463,15 +474,17 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
     int32_t* ring1 = h->ring[1] + (size_t)layer * B * h->C;
     int32_t* ring_pos = h->ring_pos + LBs;
     RingState* ring_state = h->ring_state + (size_t)layer * B;
+    int32_t* floor_layer = h->floor + (size_t)layer * B * D;
 
     if ((rc = run_stage(h, ST_SCORE, [&] {
-             return launch_score_hist(h->stream, idx_layer, qi, ntok, h->keys, h->hist, B, D, h->kcap, h->ntiles,
-                                      max_now, h->cu_count);
+             return launch_score_hist(h->stream, idx_layer, qi, ntok, h->keys, h->hist, floor_layer, h->pre,
+                                      h->meta, cs, B, D, h->kcap, cap, h->ntiles, max_now, h->cu_count);
          })))
         return rc;
     if ((rc = run_stage(h, ST_FILTER, [&] {
-             return launch_topk_filter(h->stream, h->keys, h->hist, h->meta, h->cand, h->topk, cs, ntok, h->winners,
-                                       B, D, cap, k, max_now);
+             return launch_topk_filter(h->stream, h->hist, h->meta, h->pre, h->cand, h->topk, cs, ntok, h->winners,
+                                       idx_layer, qi, floor_layer, (h->cfg.flags & SKO_FLAG_SELECT_RESCAN) != 0, B,
+                                       D, cap, h->ntiles, k, max_now);
          })))
         return rc;
     if ((rc = run_stage(h, ST_MERGE_LRU, [&] {
@@ -512,7 +525,11 @@ int sko_read_step(sko_handle* h, int32_t which, void* dst, int64_t bytes) {
         case SKO_BUF_MISSES: src = h->misses; size = BD * h->k * 4; break;
         case SKO_BUF_VICTIMS: src = h->victims; size = BD * h->k * 4; break;
         case SKO_BUF_EVICT_OLD: src = h->evict_old; size = BD * h->k * 4; break;
-        case SKO_BUF_KEYS: src = h->keys; size = BD * h->cap * 4; break;  // de-strided below
+        case SKO_BUF_KEYS:  // de-strided below
+            if (!h->keys) return set_err(SKO_E_STATE, "score keys are kept only with SKO_FLAG_KEEP_KEYS");
+            src = h->keys;
+            size = BD * h->cap * 4;
+            break;
         default: return set_err(SKO_E_INVAL, "unknown step buffer %d", which);
     }
     if ((size_t)bytes != size) return set_err(SKO_E_INVAL, "buffer %d holds %zu bytes, got %lld", which, size, (long long)bytes);
@@ -585,6 +602,7 @@ int sko_get_stats(sko_handle* h, int32_t layer, sko_layer_stats* out) {
     out->misses = (int64_t)v[3];
     out->evictions = (int64_t)v[4];
     out->h2d_bytes = (int64_t)v[3] * kKvRowBytes;
+    out->rescans = (int64_t)v[5];
     return SKO_OK;
 }
 

@@ -10,11 +10,14 @@
 //
 // Selection is a radix select over the monotone 32-bit key of the score:
 //   1. k_score_hist: one coalesced pass over the tiled indexer cache (the HBM
-//      stream) that writes the keys and a 12-bit first-digit histogram per
-//      row;
+//      stream) that builds a 12-bit first-digit histogram per row and keeps
+//      the (key, token) candidates whose first digit is at or above the
+//      row's floor (set from the previous step's histogram);
 //   2. k_topk_filter: every block finds the bucket holding the k-th largest
 //      key of its row; keys above it are winners; keys in it are staged (or
-//      taken whole when the bucket fits exactly).  Appends are aggregated
+//      taken whole when the bucket fits exactly).  It reads the candidates
+//      when they hold every winner and rescans the row's tokens otherwise,
+//      and sets the rows' floors for the next step.  Appends are aggregated
 //      per block;
 //   3. the merge kernel (merge_lru.hip) resolves a split bucket exactly on
 //      the composite (low 20 key bits, inverted index), so ties go to
@@ -79,9 +82,11 @@ hipError_t launch_append_rows(hipStream_t st, const uint16_t* idx_src, const uin
 
 // ---------------------------------------------------------------- threshold
 
-// Block of 256 threads: bucket of the kk-th largest key of one row.
+// Block of 256 threads: bucket of the kk-th largest key of one row, and the
+// candidate floor for the next step: one bin below the highest bin at which
+// the count from the top reaches kFloorCover * kk (0 when it never does).
 __device__ void threshold_row(const uint32_t* __restrict__ h, RowMeta* __restrict__ meta, int kk,
-                              int* scratch, RowMeta* s_res) {
+                              int* scratch, RowMeta* s_res, int* s_floor) {
     const int hi_bin = kHistBins - 1 - 16 * (int)threadIdx.x;  // thread 0 owns the top bins
     uint32_t loc[16];
     int sum = 0;
@@ -90,7 +95,10 @@ __device__ void threshold_row(const uint32_t* __restrict__ h, RowMeta* __restric
         loc[j] = h[hi_bin - j];
         sum += (int)loc[j];
     }
-    if (threadIdx.x == 0) *s_res = RowMeta{-1, 0, 0, 0, 0, 0, {0, 0}};
+    if (threadIdx.x == 0) {
+        *s_res = RowMeta{-1, 0, 0, 0, 0, 0, 0, 0};
+        *s_floor = 0;
+    }
     int total;
     const int excl = block_exclusive_scan<256>(sum, &total, scratch);
     if (kk > 0 && excl < kk && excl + sum >= kk) {
@@ -98,10 +106,21 @@ __device__ void threshold_row(const uint32_t* __restrict__ h, RowMeta* __restric
         for (int j = 0; j < 16; ++j) {
             const int cnt = (int)loc[j];
             if (c + cnt >= kk) {
-                *s_res = RowMeta{hi_bin - j, c, kk - c, cnt, 0, 0, {0, 0}};
+                *s_res = RowMeta{hi_bin - j, c, kk - c, cnt, 0, 0, 0, 0};
                 break;
             }
             c += cnt;
+        }
+    }
+    const int cover = kFloorCover * kk;
+    if (kk > 0 && excl < cover && excl + sum >= cover) {
+        int c = excl;
+        for (int j = 0; j < 16; ++j) {
+            c += (int)loc[j];
+            if (c >= cover) {
+                *s_floor = hi_bin - j > 0 ? hi_bin - j - 1 : 0;
+                break;
+            }
         }
     }
     __syncthreads();
@@ -139,6 +158,33 @@ __device__ __forceinline__ float score_chain(const float (&vq)[4], const uint32_
     return acc;
 }
 
+// A staged candidate (key, token) with the token's residency at step start
+// packed in: the low word becomes the packed winner value token | miss << 31.
+__device__ __forceinline__ uint2 with_residency(uint2 v, const int32_t* __restrict__ cs) {
+    return make_uint2(v.x, v.y | (cs[v.y] == -1 ? 0x80000000u : 0u));
+}
+
+// Key of token `token` for one query row, computed exactly as the score pass
+// does (64-term binary32 FMA chain in index order from +0; a zero is +0).
+// Used by the rescan path of the filter.
+__device__ __forceinline__ uint32_t token_key(const uint4* __restrict__ idx_layer, size_t seq_tiles_base,
+                                              int64_t token, const uint32_t* __restrict__ qrow) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kIdxRowU4; ++c) {
+        const uint4 v = idx_layer[idx_tile_u4(seq_tiles_base, token, c)];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t qw = qrow[4 * c + m];
+            acc = __builtin_fmaf(bf16_lo(qw), bf16_lo(w4[m]), acc);
+            acc = __builtin_fmaf(bf16_hi(qw), bf16_hi(w4[m]), acc);
+        }
+    }
+    if (acc == 0.0f) acc = 0.0f;
+    return score_key(acc);
+}
+
 // Score pass over the flattened (sequence, tile) space of B * tiles_now
 // tiles of 64 tokens: block j takes the contiguous range
 // [j * total / nblocks, (j + 1) * total / nblocks), and the launch holds at
@@ -146,29 +192,41 @@ __device__ __forceinline__ float score_chain(const float (&vq)[4], const uint32_
 // gets the same share and no second round of blocks forms a tail.  A range
 // is cut at sequence boundaries into segments; within a segment wave w of
 // the block's nw waves takes tiles w, w+nw, ...; lane l owns token
-// 64*tile + l and reads its row as 8
-// loads of 16 bytes, each a coalesced 1 KB run of the tiled layout.  Every
-// position p0 .. p0+NP-1 runs its 64-term FMA chain in index order.  The
-// first-digit histogram of a segment is counted in LDS with two 16-bit
-// counters per word (a range holds fewer than 65536 tokens) and flushed with
-// one 64-bit global atomic per non-empty pair of bins.  Blocks are large
-// (all the waves one CU holds at this kernel's register use), so a row is
-// split over few blocks and its bins receive few atomics.
+// 64*tile + l and reads its row as 8 loads of 16 bytes, each a coalesced
+// 1 KB run of the tiled layout.  Every position p0 .. p0+NP-1 runs its
+// 64-term FMA chain in index order.
+//
+// Outputs per row (seq, position):
+//   * the first-digit histogram of all keys, counted in LDS with two 16-bit
+//     counters per word (a range holds fewer than 65536 tokens) and flushed
+//     with one 64-bit global atomic per non-empty pair of bins.  Blocks are
+//     large (all the waves one CU holds at this kernel's register use), so a
+//     row is split over few blocks and its bins receive few atomics;
+//   * the candidates: (key, token | miss << 31) of every key whose first digit is at or
+//     above the row's floor (set from the previous step's threshold), staged
+//     per wave in LDS and appended to pre[row] with one reservation per block
+//     and row at the end of a segment (a wave whose staging fills up
+//     reserves for itself).  Writing all keys
+//     instead would add 4 bytes per token and position to a read-only
+//     stream, which costs far more than its size in HBM time;
+//   * all keys, only when `keys` is not null (kept for inspection).
 template <int NP>
 constexpr int score_threads() { return NP == 1 ? 640 : 768; }
 
 template <int NP>
-__global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(const uint4* __restrict__ idx_layer,
-                                                    const uint32_t* __restrict__ q_idx,
-                                                    const int32_t* __restrict__ ntok_layer,
-                                                    uint32_t* __restrict__ keys,
-                                                    uint32_t* __restrict__ hist,
-                                                    int D, int p0, int64_t kcap, int64_t ntiles,
-                                                    int64_t tiles_now, int64_t total_tiles) {
+__global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
+    const uint4* __restrict__ idx_layer, const uint32_t* __restrict__ q_idx,
+    const int32_t* __restrict__ ntok_layer, uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
+    const int32_t* __restrict__ floor_layer, uint2* __restrict__ pre, RowMeta* __restrict__ meta,
+    const int32_t* __restrict__ cache_slots_layer, int D, int p0, int64_t kcap, int64_t cap, int64_t ntiles,
+    int64_t tiles_now, int64_t total_tiles) {
     constexpr int HW = kHistBins / 2;  // packed words per position
-    __shared__ uint32_t sh[NP * HW];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     constexpr int nw = score_threads<NP>() / 64;
+    __shared__ uint32_t sh[NP * HW];
+    __shared__ uint2 stage[nw][NP][kPreStage];
+    __shared__ int s_cnt[nw][NP];
+    __shared__ int s_base[NP];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t r_begin = (int64_t)blockIdx.x * total_tiles / gridDim.x;
     const int64_t r_end = ((int64_t)blockIdx.x + 1) * total_tiles / gridDim.x;
     for (int i = threadIdx.x; i < NP * HW; i += blockDim.x) sh[i] = 0u;
@@ -182,21 +240,39 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(const uint4*
                                                    (Lt + kIdxTile - 1) / kIdxTile);
         seg = seg_end;
         if (tile0 >= tile_end) continue;  // block-uniform: nothing of this sequence here
+        const size_t row0 = (size_t)b * D + p0;
+        const uint32_t* __restrict__ qb = q_idx + row0 * (kIdxDim / 2);
+        uint32_t* __restrict__ keyrow = keys ? keys + row0 * kcap : nullptr;
+        const uint4* __restrict__ seq_tiles = idx_layer + (size_t)b * ntiles * kIdxRowU4 * kIdxTile + lane;
+        const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
         // query terms of positions p0.. as binary32, 16 per register
         // (replicated in the four 16-lane rows): vq[p][m] lane l holds term
         // 16*m + (l % 16) of position p0 + p
-        const uint32_t* __restrict__ qb = q_idx + ((size_t)b * D + p0) * (kIdxDim / 2);
         float vq[NP][4];
         if constexpr (NP > 1) {
-            const uint16_t* qh = reinterpret_cast<const uint16_t*>(q_idx) + ((size_t)b * D + p0) * kIdxDim;
+            const uint16_t* qh = reinterpret_cast<const uint16_t*>(q_idx) + row0 * kIdxDim;
 #pragma unroll
             for (int p = 0; p < NP; ++p)
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
                     vq[p][m] = __uint_as_float((uint32_t)qh[p * kIdxDim + 16 * m + (lane & 15)] << 16);
         }
-        uint32_t* __restrict__ keyrow = keys + ((size_t)b * D + p0) * kcap;
-        const uint4* __restrict__ seq_tiles = idx_layer + (size_t)b * ntiles * kIdxRowU4 * kIdxTile + lane;
+        uint32_t floor_bin[NP];
+        int nstage[NP];  // wave-uniform
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            floor_bin[p] = (uint32_t)floor_layer[row0 + p];
+            nstage[p] = 0;
+        }
+        // append this wave's staged candidates of position p to pre[row]
+        auto flush = [&](int p) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&meta[row0 + p].pre_count, nstage[p]);
+            base = __shfl(base, 0);
+            uint2* __restrict__ dst = pre + (row0 + p) * (size_t)cap + base;
+            for (int e = lane; e < nstage[p]; e += 64) dst[e] = with_residency(stage[wave][p][e], cs);
+            nstage[p] = 0;
+        };
         // Ping-pong over two register tiles: the next tile's 8 loads are in
         // flight while this tile's FMA chains run.  Loads are unconditional
         // (the tile index is clamped to the last valid tile) so that the
@@ -238,11 +314,22 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(const uint4*
                 }
                 if (acc == 0.0f) acc = 0.0f;  // store a zero as +0
                 uint32_t key = score_key(acc);
-                asm volatile("" : "+v"(key));  // keep the chain outside the branch below
+                asm volatile("" : "+v"(key));  // keep the chain outside the branches below
+                const uint32_t bin = key >> (32 - kHistBits);
                 if (valid) {
-                    keyrow[(size_t)p * kcap + i] = key;
-                    const uint32_t bin = key >> (32 - kHistBits);
+                    if (keyrow) keyrow[(size_t)p * kcap + i] = key;
                     atomicAdd(&sh[p * HW + (bin >> 1)], 1u << ((bin & 1u) << 4));
+                }
+                const bool take = valid && bin >= floor_bin[p];
+                const unsigned long long bal = __ballot(take);
+                if (bal != 0ull) {
+                    const int n = (int)__popcll(bal);
+                    if (nstage[p] + n > kPreStage) flush(p);
+                    if (take) {
+                        const unsigned long long below = lane == 0 ? 0ull : (bal & (~0ull >> (64 - lane)));
+                        stage[wave][p][nstage[p] + (int)__popcll(below)] = make_uint2(key, (uint32_t)i);
+                    }
+                    nstage[p] += n;
                 }
             }
         };
@@ -258,7 +345,26 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(const uint4*
                 score_tile(rb, tile + nw);
             }
         }
+        // end of segment: one reservation per row for the whole block
+        if (lane == 0) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) s_cnt[wave][p] = nstage[p];
+        }
         __syncthreads();
+        if (threadIdx.x < NP) {
+            const int p = threadIdx.x;
+            int tot = 0;
+            for (int v = 0; v < nw; ++v) tot += s_cnt[v][p];
+            s_base[p] = tot > 0 ? atomicAdd(&meta[row0 + p].pre_count, tot) : 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            int off = s_base[p];
+            for (int v = 0; v < wave; ++v) off += s_cnt[v][p];
+            uint2* __restrict__ dst = pre + (row0 + p) * (size_t)cap + off;
+            for (int e = lane; e < nstage[p]; e += 64) dst[e] = with_residency(stage[wave][p][e], cs);
+        }
         for (int i = threadIdx.x; i < NP * HW; i += blockDim.x) {
             const uint32_t v = sh[i];
             if (v == 0u) continue;
@@ -268,7 +374,7 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(const uint4*
             // bins 2m and 2m+1 are adjacent 32-bit counters: one 64-bit
             // atomic adds both (a row holds fewer than 2^31 tokens, so the
             // low counter never carries into the high one)
-            uint32_t* h = hist + ((size_t)b * D + p0 + p) * kHistBins;
+            uint32_t* h = hist + (row0 + p) * kHistBins;
             const unsigned long long add = (unsigned long long)(v & 0xFFFFu) | ((unsigned long long)(v >> 16) << 32);
             atomicAdd(reinterpret_cast<unsigned long long*>(h + bin), add);
         }
@@ -282,8 +388,8 @@ int score_blocks_per_cu() {
     static const int n = [] {
         int v = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void*>(&k_score_hist<NP>),
-                                                         score_threads<NP>(), 0) !=
-                hipSuccess || v < 1)
+                                                         score_threads<NP>(), 0) != hipSuccess ||
+            v < 1)
             v = 1;
         return v;
     }();
@@ -292,8 +398,10 @@ int score_blocks_per_cu() {
 }  // namespace
 
 hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const uint16_t* q_idx,
-                             const int32_t* ntok_layer, uint32_t* keys, uint32_t* hist, int B, int D,
-                             int64_t kcap, int64_t ntiles, int64_t max_tokens_now, int cu_count) {
+                             const int32_t* ntok_layer, uint32_t* keys, uint32_t* hist,
+                             const int32_t* floor_layer, uint2* pre, RowMeta* meta,
+                             const int32_t* cache_slots_layer, int B, int D, int64_t kcap, int64_t cap,
+                             int64_t ntiles, int64_t max_tokens_now, int cu_count) {
     const int64_t tiles_now = std::max<int64_t>(1, (max_tokens_now + kIdxTile - 1) / kIdxTile);
     const int64_t total = (int64_t)B * tiles_now;
     const uint4* kb = reinterpret_cast<const uint4*>(idx_layer);
@@ -302,19 +410,23 @@ hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const ui
         const int np = std::min(4, D - p0);
         const int per_cu = np == 1 ? score_blocks_per_cu<1>() : np == 2 ? score_blocks_per_cu<2>()
                          : np == 3 ? score_blocks_per_cu<3>() : score_blocks_per_cu<4>();
-        const int nw = (np == 1 ? score_threads<1>() : np == 2 ? score_threads<2>() : score_threads<4>()) / 64;
+        const int nw = (np == 1 ? score_threads<1>() : score_threads<4>()) / 64;
         // one resident round of blocks, at least one tile per wave, and
         // fewer than 1024 tiles per block for the 16-bit counters
         int64_t nb = std::min<int64_t>((int64_t)cu_count * per_cu, (total + nw - 1) / nw);
         nb = std::max<int64_t>(nb, (total + 1000) / 1001);
         nb = std::max<int64_t>(nb, 1);
         const dim3 grid((unsigned)nb);
+#define SKO_SCORE_LAUNCH(N)                                                                              \
+    hipLaunchKernelGGL(k_score_hist<N>, grid, dim3(score_threads<N>()), 0, st, kb, q, ntok_layer, keys, hist, \
+                       floor_layer, pre, meta, cache_slots_layer, D, p0, kcap, cap, ntiles, tiles_now, total)
         switch (np) {
-            case 1: hipLaunchKernelGGL(k_score_hist<1>, grid, dim3(score_threads<1>()), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
-            case 2: hipLaunchKernelGGL(k_score_hist<2>, grid, dim3(score_threads<2>()), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
-            case 3: hipLaunchKernelGGL(k_score_hist<3>, grid, dim3(score_threads<3>()), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
-            default: hipLaunchKernelGGL(k_score_hist<4>, grid, dim3(score_threads<4>()), 0, st, kb, q, ntok_layer, keys, hist, D, p0, kcap, ntiles, tiles_now, total); break;
+            case 1: SKO_SCORE_LAUNCH(1); break;
+            case 2: SKO_SCORE_LAUNCH(2); break;
+            case 3: SKO_SCORE_LAUNCH(3); break;
+            default: SKO_SCORE_LAUNCH(4); break;
         }
+#undef SKO_SCORE_LAUNCH
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -323,63 +435,95 @@ hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const ui
 
 // ---------------------------------------------------------------- filter
 
-__device__ __forceinline__ int32_t pack_winner(int64_t token, const int32_t* __restrict__ cs) {
+__device__ __forceinline__ uint32_t pack_winner(int64_t token, const int32_t* __restrict__ cs) {
     const bool miss = cs[token] == -1;
-    return (int32_t)((uint32_t)token | (miss ? 0x80000000u : 0u));
+    return (uint32_t)token | (miss ? 0x80000000u : 0u);
 }
 
-// Grid (chunks, rows).  Every block first finds the row's threshold bucket
-// from the finished histogram (block 0 records it for the refinement);
-// then each thread judges 16 consecutive keys per pass and the block makes
-// one atomic reservation per list per pass.
-__global__ __launch_bounds__(256) void k_topk_filter(const uint32_t* __restrict__ keys,
-                                                     const uint32_t* __restrict__ hist,
-                                                     RowMeta* __restrict__ meta,
-                                                     uint2* __restrict__ cand,
-                                                     int32_t* __restrict__ topk,
-                                                     const int32_t* __restrict__ cache_slots_layer,
-                                                     const int32_t* __restrict__ ntok_layer,
-                                                     uint32_t* __restrict__ winners, int D,
-                                                     int64_t cap, int64_t kcap, int64_t wpr,
-                                                     int top_k, int chunk) {
+// Grid (blocks per row, rows), 256 threads.  Every block finds the row's
+// threshold bucket from the finished histogram; block 0 records it for the
+// refinement and sets the row's candidate floor for the next step.
+//   * At least kk candidates: the floor was at or below the threshold bucket,
+//     so the candidates hold every winner.  Blocks take spans of kFilterSpanC
+//     candidate entries (4 per thread, coalesced; the first span's loads are
+//     issued with the histogram's).  The entries already carry the packed
+//     winner value (token | miss << 31).
+//   * Fewer: the threshold fell below the floor, and blocks rescan spans of
+//     kFilterSpan tokens of the row, recomputing their keys.
+// In both, a key above the bucket (or in it, when the bucket is taken
+// whole) is a winner: written packed to topk and marked in the sequence's
+// winner bitmap; a key in a split bucket is staged (packed) in cand.  Each
+// pass makes one reservation per list for the block.
+constexpr int kFilterSpanC = 256 * 4;
+
+__global__ __launch_bounds__(256) void k_topk_filter(
+    const uint32_t* __restrict__ hist, RowMeta* __restrict__ meta, const uint2* __restrict__ pre,
+    uint2* __restrict__ cand, int32_t* __restrict__ topk, const int32_t* __restrict__ cache_slots_layer,
+    const int32_t* __restrict__ ntok_layer, uint32_t* __restrict__ winners, const uint4* __restrict__ idx_layer,
+    const uint32_t* __restrict__ q_idx, int32_t* __restrict__ floor_layer, int rescan_all, int D, int64_t cap,
+    int64_t ntiles, int64_t wpr, int top_k) {
     __shared__ int scratch[8];
-    __shared__ int s_bw, s_bs;
+    __shared__ int s_bw, s_bs, s_floor;
     __shared__ RowMeta s_res;
     const int row = blockIdx.y;
     const int b = row / D;
     const int64_t Lt = ntok_layer[b];
-    const int64_t start = (int64_t)blockIdx.x * chunk;
-    if (start >= Lt && blockIdx.x != 0) return;
     const int kk = (int)std::min<int64_t>(top_k, Lt);
-    threshold_row(hist + (size_t)row * kHistBins, blockIdx.x == 0 ? meta + row : nullptr, kk,
-                  scratch, &s_res);
+    const int64_t npre = meta[row].pre_count;
+    const uint2* __restrict__ pr = pre + (size_t)row * cap;
+    // first candidate span, loaded before it is known to be needed (rows
+    // hold cap entries, so clamped indexes stay in bounds)
+    uint2 e0[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t j = (int64_t)blockIdx.x * kFilterSpanC + 256 * u + threadIdx.x;
+        e0[u] = pr[j < cap ? j : cap - 1];
+    }
+    threshold_row(hist + (size_t)row * kHistBins, blockIdx.x == 0 ? meta + row : nullptr, kk, scratch, &s_res,
+                  &s_floor);
+    if (blockIdx.x == 0 && threadIdx.x == 0) floor_layer[row] = rescan_all ? kFloorRescanAll : s_floor;
     const RowMeta m = s_res;
-    const int64_t end = std::min<int64_t>(start + chunk, Lt);
-    if (m.bucket < 0 || start >= end) return;
+    if (m.bucket < 0) return;
+    const bool rescan = npre < kk;
+    const bool take_bucket = m.need == m.bucket_count;
     const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
     uint32_t* __restrict__ wb = winners + (size_t)b * wpr;
     int32_t* __restrict__ w = topk + (size_t)row * top_k;
     uint2* __restrict__ cr = cand + (size_t)row * cap;
-    const bool take_bucket = m.need == m.bucket_count;
-    const uint32_t* __restrict__ krow = keys + (size_t)row * kcap;
-    for (int64_t base = start; base < end; base += kFilterSpan) {
-        const int64_t i0 = base + (int64_t)kFilterKeysPerThread * threadIdx.x;
-        uint32_t kv[kFilterKeysPerThread];
-        if (i0 < end) {
-            const uint4* p = reinterpret_cast<const uint4*>(krow + i0);
-#pragma unroll
-            for (int q = 0; q < kFilterKeysPerThread / 4; ++q) {
-                const uint4 v = p[q];
-                kv[4 * q] = v.x; kv[4 * q + 1] = v.y; kv[4 * q + 2] = v.z; kv[4 * q + 3] = v.w;
-            }
-        }
+    const uint32_t* __restrict__ qrow = q_idx + (size_t)row * (kIdxDim / 2);
+    const int64_t n_items = rescan ? Lt : npre;
+    const int span = rescan ? kFilterSpan : kFilterSpanC;
+    for (int64_t base = (int64_t)blockIdx.x * span; base < n_items; base += (int64_t)gridDim.x * span) {
+        uint32_t kv[kFilterKeysPerThread], tk[kFilterKeysPerThread];  // tk: packed winner value
         uint32_t wmask = 0, smask = 0;
+        if (rescan) {
+            // tokens i0 .. i0+15 of the row, keys recomputed
+            const int64_t i0 = base + (int64_t)kFilterKeysPerThread * threadIdx.x;
+            for (int e = 0; e < kFilterKeysPerThread; ++e) {
+                kv[e] = 0u;
+                tk[e] = 0u;
+                if (i0 + e < n_items) {
+                    kv[e] = token_key(idx_layer, (size_t)b * ntiles, i0 + e, qrow);
+                    const int bin = (int)(kv[e] >> (32 - kHistBits));
+                    if (bin > m.bucket || (bin == m.bucket && take_bucket)) wmask |= 1u << e;
+                    else if (bin == m.bucket) smask |= 1u << e;
+                    if ((wmask | smask) >> e & 1u) tk[e] = pack_winner(i0 + e, cs);
+                }
+            }
+        } else {
+            // candidate entries base + 256 u + thread
 #pragma unroll
-        for (int e = 0; e < kFilterKeysPerThread; ++e) {
-            if (i0 + e < end) {
-                const int bin = (int)(kv[e] >> (32 - kHistBits));
-                if (bin > m.bucket || (bin == m.bucket && take_bucket)) wmask |= 1u << e;
-                else if (bin == m.bucket) smask |= 1u << e;
+            for (int u = 0; u < 4; ++u) {
+                const int64_t j = base + 256 * u + threadIdx.x;
+                uint2 v = e0[u];
+                if (base != (int64_t)blockIdx.x * kFilterSpanC) v = pr[j < cap ? j : cap - 1];
+                kv[u] = v.x;
+                tk[u] = v.y;
+                if (j < n_items) {
+                    const int bin = (int)(v.x >> (32 - kHistBits));
+                    if (bin > m.bucket || (bin == m.bucket && take_bucket)) wmask |= 1u << u;
+                    else if (bin == m.bucket) smask |= 1u << u;
+                }
             }
         }
         const int nw = __popc(wmask), ns = __popc(smask);
@@ -392,32 +536,35 @@ __global__ __launch_bounds__(256) void k_topk_filter(const uint32_t* __restrict_
         __syncthreads();
         int pw = s_bw + (excl & 0xFFFF);
         int ps = s_bs + (excl >> 16);
-#pragma unroll
-        for (int e = 0; e < kFilterKeysPerThread; ++e) {
+        const int ne = rescan ? kFilterKeysPerThread : 4;
+        for (int e = 0; e < ne; ++e) {
             if ((wmask >> e) & 1u) {
-                if (pw < top_k) w[pw] = pack_winner(i0 + e, cs);
+                if (pw < top_k) w[pw] = (int32_t)tk[e];
                 ++pw;
+                const uint32_t tok = tk[e] & 0x7FFFFFFFu;
+                atomicOr(&wb[tok >> 5], 1u << (tok & 31u));
             } else if ((smask >> e) & 1u) {
-                if (ps < cap) cr[ps] = make_uint2(kv[e], (uint32_t)(i0 + e));
+                if (ps < cap) cr[ps] = make_uint2(kv[e], tk[e]);
                 ++ps;
             }
         }
-        if (wmask) atomicOr(&wb[i0 >> 5], wmask << (i0 & 31));
+        __syncthreads();  // s_bw / s_bs are reused by the next pass
     }
 }
 
-hipError_t launch_topk_filter(hipStream_t st, const uint32_t* keys, const uint32_t* hist, RowMeta* meta,
+hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* meta, const uint2* pre,
                               uint2* cand, int32_t* topk, const int32_t* cache_slots_layer,
-                              const int32_t* ntok_layer, uint32_t* winners, int B, int D,
-                              int64_t cap, int top_k, int64_t max_tokens_now) {
-    const int64_t kcap = (cap + 15) / 16 * 16;
+                              const int32_t* ntok_layer, uint32_t* winners, const uint16_t* idx_layer,
+                              const uint16_t* q_idx, int32_t* floor_layer, bool rescan_all, int B, int D,
+                              int64_t cap, int64_t ntiles, int top_k, int64_t max_tokens_now) {
     const int64_t wpr = winner_words(cap);
     const int64_t now = std::max<int64_t>(1, max_tokens_now);
-    int chunk = kFilterSpan;
-    while (chunk < (1 << 20) && (int64_t)B * D * ((now + 2 * chunk - 1) / (2 * chunk)) >= 1024) chunk *= 2;
-    const dim3 grid((unsigned)((now + chunk - 1) / chunk), (unsigned)(B * D));
-    hipLaunchKernelGGL(k_topk_filter, grid, dim3(256), 0, st, keys, hist, meta, cand, topk,
-                       cache_slots_layer, ntok_layer, winners, D, cap, kcap, wpr, top_k, chunk);
+    const int per_row = (int)std::min<int64_t>(32, std::max<int64_t>(4, (now + kFilterSpan - 1) / kFilterSpan));
+    const dim3 grid((unsigned)per_row, (unsigned)(B * D));
+    hipLaunchKernelGGL(k_topk_filter, grid, dim3(256), 0, st, hist, meta, pre, cand, topk, cache_slots_layer,
+                       ntok_layer, winners, reinterpret_cast<const uint4*>(idx_layer),
+                       reinterpret_cast<const uint32_t*>(q_idx), floor_layer, rescan_all ? 1 : 0, D, cap, ntiles,
+                       wpr, top_k);
     return hipGetLastError();
 }
 

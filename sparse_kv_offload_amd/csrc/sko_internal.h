@@ -23,6 +23,14 @@ constexpr int kAttnTileRows = 32;            // rows per attention tile
 constexpr int kAttnMaxRowsPerBlock = 512;    // rows of one attention block (remap table)
 constexpr int kFilterKeysPerThread = 16;
 constexpr int kFilterSpan = 256 * kFilterKeysPerThread;  // keys per block pass
+constexpr int kPreStage = 128;               // per-wave LDS staging of candidates
+// The candidate floor of a row for the next step is one first-digit bin
+// below the highest bin at which the row's count from the top reaches
+// kFloorCover * k (so the floor admits well over k keys at the next step if
+// the score distribution holds, and the next threshold has room to fall).
+constexpr int kFloorCover = 2;
+constexpr int kFloorRescanAll = kHistBins;   // a floor no key reaches
+
 
 // Indexer cache layout in HBM (per layer): [B][ntiles][8 chunks][64 tokens]
 // x 16 bytes, so that chunk c of 64 consecutive tokens is one contiguous
@@ -40,7 +48,8 @@ struct RowMeta {
     int32_t bucket_count;  // keys in the bucket
     int32_t out_count;     // winners written so far
     int32_t cand_count;    // bucket keys staged for refinement
-    int32_t pad[2];
+    int32_t pre_count;     // scored keys at or above the row's candidate floor
+    int32_t pad;
 };
 
 // Words of the per-sequence winner bitmap (padded to 16 bytes).
@@ -70,13 +79,20 @@ hipError_t launch_append_rows(hipStream_t st, const uint16_t* idx_src, const uin
                               uint16_t* idx_layer, uint16_t* pool_layer, int32_t* ntok_layer,
                               int seq0, int nseq, int64_t n, int64_t cap, int64_t ntiles,
                               int32_t base);
+// keys may be null (keys are then not stored); candidates (key, token |
+// miss << 31) with first digit >= floor_layer[row] go to
+// pre[row][0 .. meta[row].pre_count).
 hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const uint16_t* q_idx,
-                             const int32_t* ntok_layer, uint32_t* keys, uint32_t* hist, int B, int D,
-                             int64_t kcap, int64_t ntiles, int64_t max_tokens_now, int cu_count);
-hipError_t launch_topk_filter(hipStream_t st, const uint32_t* keys, const uint32_t* hist, RowMeta* meta,
+                             const int32_t* ntok_layer, uint32_t* keys, uint32_t* hist,
+                             const int32_t* floor_layer, uint2* pre, RowMeta* meta,
+                             const int32_t* cache_slots_layer, int B, int D, int64_t kcap, int64_t cap,
+                             int64_t ntiles, int64_t max_tokens_now, int cu_count);
+// Also sets floor_layer for the next step (kFloorRescanAll when rescan_all).
+hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* meta, const uint2* pre,
                               uint2* cand, int32_t* topk, const int32_t* cache_slots_layer,
-                              const int32_t* ntok_layer, uint32_t* winners, int B, int D,
-                              int64_t cap, int top_k, int64_t max_tokens_now);
+                              const int32_t* ntok_layer, uint32_t* winners, const uint16_t* idx_layer,
+                              const uint16_t* q_idx, int32_t* floor_layer, bool rescan_all, int B, int D,
+                              int64_t cap, int64_t ntiles, int top_k, int64_t max_tokens_now);
 // Also finishes the top-k (split buckets) and clears the histograms and row
 // records for the next step.
 hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, RowMeta* meta,

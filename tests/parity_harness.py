@@ -208,9 +208,11 @@ def run_parity(w: synth.Workload, layers: Optional[int] = None, steps: Optional[
     T = w.steps if steps is None else steps
     chains = [(l, b) for l in range(L) for b in range(w.batch)] if chains is None else chains
     inputs = Inputs(w, sorted({c[0] for c in chains} | set(range(L))), T)
-    gpu = GpuSide(w, L, device_append=device_append, flags=flags)
+    import sparse_kv_offload_amd as sko
+    gpu = GpuSide(w, L, device_append=device_append,
+                  flags=flags | (sko.SKO_FLAG_KEEP_KEYS if check_keys else 0))
     ora = OracleSide(w, chains)
-    worst = {"abs": 0.0, "rel_rms": 0.0}
+    worst = {"abs": 0.0, "rel_rms": 0.0, "rescans": 0}
     try:
         for l in range(L):
             for b in range(w.batch):
@@ -237,6 +239,11 @@ def run_parity(w: synth.Workload, layers: Optional[int] = None, steps: Optional[
                         compare_tables(gpu.tables(l, b), ora.tables(l, b), where=f"[{w.name} l={l} b={b} t={t}]")
             if log:
                 log(f"{w.name}: step {t + 1}/{T} ok")
+        worst["rescans"] = sum(gpu.h.stats(l).rescans for l in range(L))
+        if flags & sko.SKO_FLAG_SELECT_RESCAN:
+            # every row with at least one token took the rescan path
+            rows = sum(1 for b in range(w.batch) for t in range(T) if w.seq_context(b) + t + 1 > 0) * w.positions
+            assert worst["rescans"] == L * rows, (worst["rescans"], L * rows)
     finally:
         gpu.close()
     return worst

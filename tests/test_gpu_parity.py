@@ -174,3 +174,61 @@ def test_append_capacity_and_validation_on_device():
         assert np.array_equal(pool[:90], w.kv_rows(0, 1, 0, 90))
         idx = h.table(0, 1, sko.SKO_TAB_INDEXER)
         assert np.array_equal(idx[:90], w.index_rows(0, 1, 0, 90))
+
+
+@pytest.mark.parametrize("name", ["tiles", "ragged", "ties", "zeroq"])
+def test_rescan_path(name):
+    """The selection's rescan path (forced for every row) gives the same
+    winners as the oracle."""
+    import sparse_kv_offload_amd as sko
+    if name == "tiles":
+        w = case("tiles_rescan", batch=3, context=9000, steps=6, top_k=256, hot_slots=600, positions=2,
+                 heads=4)
+    elif name == "ragged":
+        w = case("ragged_rescan", batch=3, contexts=(3001, 1, 777), context=3001, steps=6, top_k=100,
+                 hot_slots=337, positions=3, heads=5)
+    elif name == "ties":
+        w = TiedRows("ties_rescan", layers=1, batch=2, context=2000, steps=4, top_k=300, hot_slots=700,
+                     positions=2, heads=2, seed=99)
+    else:
+        w = ZeroQuery("zeroq_rescan", layers=1, batch=2, context=5000, steps=3, top_k=200, hot_slots=400,
+                      positions=2, heads=16, seed=5)
+    log(f"case rescan {name}")
+    worst = run_parity(w, check_keys=(name != "zeroq"), flags=sko.SKO_FLAG_SELECT_RESCAN, log=log)
+    log(f"rescans {worst['rescans']}")
+
+
+@dataclasses.dataclass(frozen=True)
+class ScaledQuery(synth.Workload):
+    """Indexer queries alternate between scale 1 and 1/16 (exact in bf16):
+    the score threshold drops four octaves on every other step, below the
+    candidate floor set from the step before."""
+
+    def index_queries(self, layer, seq, steps=None):
+        q = synth.Workload.index_queries(self, layer, seq, steps)
+        f = (q.astype(np.uint32) << 16).view(np.float32).copy()
+        f[1::2] *= np.float32(1.0 / 16.0)
+        return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_floor_below_threshold_rescans():
+    """A threshold that falls below the floor takes the rescan path on its
+    own; the results still match the oracle."""
+    w = ScaledQuery("scaledq", layers=1, batch=2, context=6000, steps=6, top_k=128, hot_slots=300,
+                    positions=2, heads=4, seed=17)
+    log("case scaled query")
+    worst = run_parity(w, check_keys=True, log=log)
+    rows = w.batch * w.positions
+    log(f"rescans {worst['rescans']} of {w.steps * rows} rows")
+    assert rows <= worst["rescans"] < w.steps * rows
+
+
+def test_keys_need_keep_flag():
+    import torch
+    import sparse_kv_offload_amd as sko
+    cfg = sko.make_config(num_layers=1, batch=1, max_tokens=100, num_heads=1, top_k=8, hot_slots=8,
+                          mtp_positions=1)
+    with sko.SparseKVOffload(cfg, torch.cuda.current_stream()) as h:
+        with pytest.raises(sko.SkoError) as e:
+            h.step_buffer(sko.SKO_BUF_KEYS)
+        assert e.value.code == sko.SKO_E_STATE
