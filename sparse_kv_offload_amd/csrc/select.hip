@@ -209,11 +209,11 @@ __device__ __forceinline__ uint32_t token_key(const uint4* __restrict__ idx_laye
 //     reserves for itself).  Writing all keys
 //     instead would add 4 bytes per token and position to a read-only
 //     stream, which costs far more than its size in HBM time;
-//   * all keys, only when `keys` is not null (kept for inspection).
+//   * all keys, only in the KEEP instantiation (kept for inspection).
 template <int NP>
 constexpr int score_threads() { return NP == 1 ? 640 : 768; }
 
-template <int NP>
+template <int NP, bool KEEP>
 __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
     const uint4* __restrict__ idx_layer, const uint32_t* __restrict__ q_idx,
     const int32_t* __restrict__ ntok_layer, uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
@@ -225,6 +225,7 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
     __shared__ uint32_t sh[NP * HW];
     __shared__ uint2 stage[nw][NP][kPreStage];
     __shared__ int s_cnt[nw][NP];
+    __shared__ float sq[NP > 1 ? NP * kIdxDim : 1];
     __shared__ int s_base[NP];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t r_begin = (int64_t)blockIdx.x * total_tiles / gridDim.x;
@@ -242,20 +243,17 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
         if (tile0 >= tile_end) continue;  // block-uniform: nothing of this sequence here
         const size_t row0 = (size_t)b * D + p0;
         const uint32_t* __restrict__ qb = q_idx + row0 * (kIdxDim / 2);
-        uint32_t* __restrict__ keyrow = keys ? keys + row0 * kcap : nullptr;
+        uint32_t* __restrict__ keyrow = keys + row0 * kcap;
         const uint4* __restrict__ seq_tiles = idx_layer + (size_t)b * ntiles * kIdxRowU4 * kIdxTile + lane;
         const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
-        // query terms of positions p0.. as binary32, 16 per register
-        // (replicated in the four 16-lane rows): vq[p][m] lane l holds term
-        // 16*m + (l % 16) of position p0 + p
-        float vq[NP][4];
+        // query terms of positions p0.. as binary32 in LDS; each chain loads
+        // its position's terms 16 per register (replicated in the four
+        // 16-lane rows): register m, lane l holds term 16*m + (l % 16)
         if constexpr (NP > 1) {
             const uint16_t* qh = reinterpret_cast<const uint16_t*>(q_idx) + row0 * kIdxDim;
-#pragma unroll
-            for (int p = 0; p < NP; ++p)
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    vq[p][m] = __uint_as_float((uint32_t)qh[p * kIdxDim + 16 * m + (lane & 15)] << 16);
+            for (int i = threadIdx.x; i < NP * kIdxDim; i += blockDim.x)
+                sq[i] = __uint_as_float((uint32_t)qh[i] << 16);
+            __syncthreads();
         }
         uint32_t floor_bin[NP];
         int nstage[NP];  // wave-uniform
@@ -310,14 +308,17 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
                         acc = __builtin_fmaf(bf16_hi(qw), bf16_hi(w[j]), acc);
                     }
                 } else {
-                    acc = score_chain(vq[p], w, std::make_integer_sequence<int, 64>{});
+                    float vq[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) vq[m] = sq[p * kIdxDim + 16 * m + (lane & 15)];
+                    acc = score_chain(vq, w, std::make_integer_sequence<int, 64>{});
                 }
                 if (acc == 0.0f) acc = 0.0f;  // store a zero as +0
                 uint32_t key = score_key(acc);
                 asm volatile("" : "+v"(key));  // keep the chain outside the branches below
                 const uint32_t bin = key >> (32 - kHistBits);
                 if (valid) {
-                    if (keyrow) keyrow[(size_t)p * kcap + i] = key;
+                    if constexpr (KEEP) keyrow[(size_t)p * kcap + i] = key;
                     atomicAdd(&sh[p * HW + (bin >> 1)], 1u << ((bin & 1u) << 4));
                 }
                 const bool take = valid && bin >= floor_bin[p];
@@ -387,7 +388,7 @@ template <int NP>
 int score_blocks_per_cu() {
     static const int n = [] {
         int v = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void*>(&k_score_hist<NP>),
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void*>(&k_score_hist<NP, false>),
                                                          score_threads<NP>(), 0) != hipSuccess ||
             v < 1)
             v = 1;
@@ -417,9 +418,17 @@ hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const ui
         nb = std::max<int64_t>(nb, (total + 1000) / 1001);
         nb = std::max<int64_t>(nb, 1);
         const dim3 grid((unsigned)nb);
-#define SKO_SCORE_LAUNCH(N)                                                                              \
-    hipLaunchKernelGGL(k_score_hist<N>, grid, dim3(score_threads<N>()), 0, st, kb, q, ntok_layer, keys, hist, \
-                       floor_layer, pre, meta, cache_slots_layer, D, p0, kcap, cap, ntiles, tiles_now, total)
+#define SKO_SCORE_LAUNCH(N)                                                                                \
+    do {                                                                                                   \
+        if (keys)                                                                                          \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_score_hist<N, true>), grid, dim3(score_threads<N>()), 0, st, kb, \
+                               q, ntok_layer, keys, hist, floor_layer, pre, meta, cache_slots_layer, D, p0, kcap, \
+                               cap, ntiles, tiles_now, total);                                               \
+        else                                                                                               \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_score_hist<N, false>), grid, dim3(score_threads<N>()), 0, st, kb,\
+                               q, ntok_layer, keys, hist, floor_layer, pre, meta, cache_slots_layer, D, p0, kcap, \
+                               cap, ntiles, tiles_now, total);                                               \
+    } while (0)
         switch (np) {
             case 1: SKO_SCORE_LAUNCH(1); break;
             case 2: SKO_SCORE_LAUNCH(2); break;
