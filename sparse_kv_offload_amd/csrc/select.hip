@@ -197,9 +197,8 @@ __device__ __forceinline__ uint32_t token_key(const uint4* __restrict__ idx_laye
 // 64-term FMA chain in index order.
 //
 // Outputs per row (seq, position):
-//   * the first-digit histogram of all keys, counted in LDS with two 16-bit
-//     counters per word (a range holds fewer than 65536 tokens) and flushed
-//     with one 64-bit global atomic per non-empty pair of bins.  Blocks are
+//   * the first-digit histogram of all keys, counted in LDS and flushed with
+//     one 64-bit global atomic per non-empty pair of bins.  Blocks are
 //     large (all the waves one CU holds at this kernel's register use), so a
 //     row is split over few blocks and its bins receive few atomics;
 //   * the candidates: (key, token | miss << 31) of every key whose first digit is at or
@@ -220,9 +219,8 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
     const int32_t* __restrict__ floor_layer, uint2* __restrict__ pre, RowMeta* __restrict__ meta,
     const int32_t* __restrict__ cache_slots_layer, int D, int p0, int64_t kcap, int64_t cap, int64_t ntiles,
     int64_t tiles_now, int64_t total_tiles) {
-    constexpr int HW = kHistBins / 2;  // packed words per position
     constexpr int nw = score_threads<NP>() / 64;
-    __shared__ uint32_t sh[NP * HW];
+    __shared__ uint32_t sh[NP * kHistBins];
     __shared__ uint2 stage[nw][NP][kPreStage];
     __shared__ int s_cnt[nw][NP];
     __shared__ float sq[NP > 1 ? NP * kIdxDim : 1];
@@ -230,7 +228,7 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t r_begin = (int64_t)blockIdx.x * total_tiles / gridDim.x;
     const int64_t r_end = ((int64_t)blockIdx.x + 1) * total_tiles / gridDim.x;
-    for (int i = threadIdx.x; i < NP * HW; i += blockDim.x) sh[i] = 0u;
+    for (int i = threadIdx.x; i < NP * kHistBins; i += blockDim.x) sh[i] = 0u;
     __syncthreads();
     for (int64_t seg = r_begin; seg < r_end;) {
         const int b = (int)(seg / tiles_now);
@@ -313,13 +311,13 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
                     for (int m = 0; m < 4; ++m) vq[m] = sq[p * kIdxDim + 16 * m + (lane & 15)];
                     acc = score_chain(vq, w, std::make_integer_sequence<int, 64>{});
                 }
-                if (acc == 0.0f) acc = 0.0f;  // store a zero as +0
+                acc += 0.0f;  // a zero becomes +0 (one add instead of compare and select)
                 uint32_t key = score_key(acc);
                 asm volatile("" : "+v"(key));  // keep the chain outside the branches below
                 const uint32_t bin = key >> (32 - kHistBits);
                 if (valid) {
                     if constexpr (KEEP) keyrow[(size_t)p * kcap + i] = key;
-                    atomicAdd(&sh[p * HW + (bin >> 1)], 1u << ((bin & 1u) << 4));
+                    atomicAdd(&sh[p * kHistBins + bin], 1u);
                 }
                 const bool take = valid && bin >= floor_bin[p];
                 const unsigned long long bal = __ballot(take);
@@ -366,18 +364,19 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
             uint2* __restrict__ dst = pre + (row0 + p) * (size_t)cap + off;
             for (int e = lane; e < nstage[p]; e += 64) dst[e] = with_residency(stage[wave][p][e], cs);
         }
-        for (int i = threadIdx.x; i < NP * HW; i += blockDim.x) {
-            const uint32_t v = sh[i];
-            if (v == 0u) continue;
-            sh[i] = 0u;
-            const int p = i / HW;
-            const int bin = (i - p * HW) * 2;
+        for (int i = threadIdx.x; i < NP * kHistBins / 2; i += blockDim.x) {
+            uint2* const pair = reinterpret_cast<uint2*>(sh) + i;
+            const uint2 v = *pair;
+            if ((v.x | v.y) == 0u) continue;
+            *pair = make_uint2(0u, 0u);
             // bins 2m and 2m+1 are adjacent 32-bit counters: one 64-bit
             // atomic adds both (a row holds fewer than 2^31 tokens, so the
             // low counter never carries into the high one)
+            const int p = (2 * i) / kHistBins;
+            const int bin = 2 * i - p * kHistBins;
             uint32_t* h = hist + (row0 + p) * kHistBins;
-            const unsigned long long add = (unsigned long long)(v & 0xFFFFu) | ((unsigned long long)(v >> 16) << 32);
-            atomicAdd(reinterpret_cast<unsigned long long*>(h + bin), add);
+            atomicAdd(reinterpret_cast<unsigned long long*>(h + bin),
+                      (unsigned long long)v.x | ((unsigned long long)v.y << 32));
         }
         __syncthreads();
     }
@@ -412,10 +411,8 @@ hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const ui
         const int per_cu = np == 1 ? score_blocks_per_cu<1>() : np == 2 ? score_blocks_per_cu<2>()
                          : np == 3 ? score_blocks_per_cu<3>() : score_blocks_per_cu<4>();
         const int nw = (np == 1 ? score_threads<1>() : score_threads<4>()) / 64;
-        // one resident round of blocks, at least one tile per wave, and
-        // fewer than 1024 tiles per block for the 16-bit counters
+        // one resident round of blocks, at least one tile per wave
         int64_t nb = std::min<int64_t>((int64_t)cu_count * per_cu, (total + nw - 1) / nw);
-        nb = std::max<int64_t>(nb, (total + 1000) / 1001);
         nb = std::max<int64_t>(nb, 1);
         const dim3 grid((unsigned)nb);
 #define SKO_SCORE_LAUNCH(N)                                                                                \
@@ -449,9 +446,9 @@ __device__ __forceinline__ uint32_t pack_winner(int64_t token, const int32_t* __
     return (uint32_t)token | (miss ? 0x80000000u : 0u);
 }
 
-// Grid (blocks per row, rows), 256 threads.  Every block finds the row's
-// threshold bucket from the finished histogram; block 0 records it for the
-// refinement and sets the row's candidate floor for the next step.
+// Grid (blocks per row, rows), 256 threads.  Every block with items finds
+// the row's threshold bucket from the finished histogram; block 0 records it
+// for the refinement and sets the row's candidate floor for the next step.
 //   * At least kk candidates: the floor was at or below the threshold bucket,
 //     so the candidates hold every winner.  Blocks take spans of kFilterSpanC
 //     candidate entries (4 per thread, coalesced; the first span's loads are
@@ -488,35 +485,39 @@ __global__ __launch_bounds__(256) void k_topk_filter(
         const int64_t j = (int64_t)blockIdx.x * kFilterSpanC + 256 * u + threadIdx.x;
         e0[u] = pr[j < cap ? j : cap - 1];
     }
+    const bool rescan = npre < kk;
+    const int64_t n_items = rescan ? Lt : npre;
+    const int span = rescan ? kFilterSpan : kFilterSpanC;
+    // a block without items leaves at once (block 0 stays: it records the
+    // threshold and the floor)
+    if (blockIdx.x != 0 && (int64_t)blockIdx.x * span >= n_items) return;
     threshold_row(hist + (size_t)row * kHistBins, blockIdx.x == 0 ? meta + row : nullptr, kk, scratch, &s_res,
                   &s_floor);
     if (blockIdx.x == 0 && threadIdx.x == 0) floor_layer[row] = rescan_all ? kFloorRescanAll : s_floor;
     const RowMeta m = s_res;
     if (m.bucket < 0) return;
-    const bool rescan = npre < kk;
     const bool take_bucket = m.need == m.bucket_count;
     const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
     uint32_t* __restrict__ wb = winners + (size_t)b * wpr;
     int32_t* __restrict__ w = topk + (size_t)row * top_k;
     uint2* __restrict__ cr = cand + (size_t)row * cap;
     const uint32_t* __restrict__ qrow = q_idx + (size_t)row * (kIdxDim / 2);
-    const int64_t n_items = rescan ? Lt : npre;
-    const int span = rescan ? kFilterSpan : kFilterSpanC;
     for (int64_t base = (int64_t)blockIdx.x * span; base < n_items; base += (int64_t)gridDim.x * span) {
         uint32_t kv[kFilterKeysPerThread], tk[kFilterKeysPerThread];  // tk: packed winner value
         uint32_t wmask = 0, smask = 0;
         if (rescan) {
-            // tokens i0 .. i0+15 of the row, keys recomputed
-            const int64_t i0 = base + (int64_t)kFilterKeysPerThread * threadIdx.x;
+            // tokens base + 256 e + thread of the row (a wave reads whole
+            // 1 KB runs of the tiled indexer), keys recomputed
             for (int e = 0; e < kFilterKeysPerThread; ++e) {
+                const int64_t i = base + 256 * e + threadIdx.x;
                 kv[e] = 0u;
                 tk[e] = 0u;
-                if (i0 + e < n_items) {
-                    kv[e] = token_key(idx_layer, (size_t)b * ntiles, i0 + e, qrow);
+                if (i < n_items) {
+                    kv[e] = token_key(idx_layer, (size_t)b * ntiles, i, qrow);
                     const int bin = (int)(kv[e] >> (32 - kHistBits));
                     if (bin > m.bucket || (bin == m.bucket && take_bucket)) wmask |= 1u << e;
                     else if (bin == m.bucket) smask |= 1u << e;
-                    if ((wmask | smask) >> e & 1u) tk[e] = pack_winner(i0 + e, cs);
+                    if ((wmask | smask) >> e & 1u) tk[e] = pack_winner(i, cs);
                 }
             }
         } else {
