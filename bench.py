@@ -231,14 +231,21 @@ def main() -> int:
 
     d = deltas(stats0, stats1)
 
-    def alg_bytes(first_step, nsteps, h2d_bytes):
+    def alg_bytes(first_step, nsteps, h2d_bytes, fused):
         """Algorithmic bytes per launch of the modelled kernels, averaged over
-        decode steps first_step .. first_step + nsteps - 1."""
+        decode steps first_step .. first_step + nsteps - 1.  With the miss
+        copy done by the attention launch (fused), that launch is bound by
+        the host link and its bytes are the copied rows."""
         avg_lt = w.context + first_step + (nsteps + 1) / 2.0  # tokens present after each append
         ls = L * nsteps
-        return {"score_hist": (IDX_ROW * B * avg_lt + IDX_ROW * B * D, "hbm", HBM_PEAK_GBPS),
-                "gather_misses": (h2d_bytes / ls if ls else 0.0, "host-link", HOST_LINK_PEAK_GBPS),
-                "attn_partial": (KV_ROW * B * D * min(k, avg_lt), "hbm", HBM_PEAK_GBPS)}
+        copy = (h2d_bytes / ls if ls else 0.0, "host-link", HOST_LINK_PEAK_GBPS)
+        m = {"score_hist": (IDX_ROW * B * avg_lt + IDX_ROW * B * D, "hbm", HBM_PEAK_GBPS)}
+        if fused:
+            m["attn_partial"] = copy
+        else:
+            m["gather_misses"] = copy
+            m["attn_partial"] = (KV_ROW * B * D * min(k, avg_lt), "hbm", HBM_PEAK_GBPS)
+        return m
 
     h2d_ceiling = measure_h2d_ceiling(torch)
     calibration_copy(torch)
@@ -257,14 +264,16 @@ def main() -> int:
 
     rooflines = {}
     if calib:
-        model = alg_bytes(1, calib_steps, deltas(calib_stats0, stats0)["h2d_bytes"])
+        fused = calib.get("gather_misses", (0.0, 0))[1] == 0
+        model = alg_bytes(1, calib_steps, deltas(calib_stats0, stats0)["h2d_bytes"], fused)
         for name in model:
             ms, n = calib.get(name, (0.0, 0))
             if n:
                 rooflines[name] = roof_entry(name, ms, n, model)
     roof = None
     if timing and dominant in timing:
-        model = alg_bytes(args.warmup, K, d["h2d_bytes"])
+        model = alg_bytes(args.warmup, K, d["h2d_bytes"], timing.get("gather_misses", (0.0, 0))[1] == 0
+                          and calib.get("gather_misses", (0.0, 0))[1] == 0)
         ms, n = timing[dominant]
         if dominant in model:
             roof = roof_entry(dominant, ms, n, model)
@@ -290,8 +299,9 @@ def main() -> int:
                    "parallelism": "none (1 GPU)", "pool": args.pool},
         "tokens_per_s": round(B * K / elapsed, 2),
         "indexer_scan_GBps": rooflines.get("score_hist", {}).get("achieved"),
-        "miss_gather_GBps": (roof or {}).get("achieved") if dominant == "gather_misses"
-        else rooflines.get("gather_misses", {}).get("achieved"),
+        "miss_gather_GBps": next((e["achieved"] for e in [roof or {}] + list(rooflines.values())
+                                  if e.get("bound") == "host-link"), None),
+        "miss_copy_in_attention": calib.get("gather_misses", (0.0, 0))[1] == 0 if calib else None,
         "h2d_ceiling_GBps": round(h2d_ceiling, 2),
         "hit_rate": round(d["hits"] / max(1, d["unique"]), 4),
         "unique_misses_per_layer_step": round(d["misses"] / layer_steps, 1),

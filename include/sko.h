@@ -67,6 +67,11 @@ extern "C" {
 /* Testing: no candidate floor, so every step selects through the rescan
  * path (same results, slower). */
 #define SKO_FLAG_SELECT_RESCAN 0x8u
+/* Copy the misses in their own kernel before the attention even where the
+ * attention could copy them itself (one position, at most 16 heads: each
+ * row is then read by one attention block, which reads a missed row from
+ * the pool and stores it into its slot).  Same results. */
+#define SKO_FLAG_SEPARATE_COPY 0x10u
 
 typedef struct sko_handle sko_handle;
 
@@ -155,7 +160,10 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
  * sko_decode_step — one sparse decode step of `layer` for all B sequences
  * and D positions, enqueued on the stream (asynchronous; no host sync):
  * score -> packed top-k -> merge/dedupe -> LRU update -> miss-only gather
- * -> remap -> attention ([LSO] §4 "Decode step" items 3-7).
+ * -> remap -> attention ([LSO] §4 "Decode step" items 3-7).  With one
+ * position and at most 16 heads the gather is done by the attention launch
+ * itself (the fused Copy-SFA operator of [LSO-zh] §4), unless
+ * SKO_FLAG_SEPARATE_COPY is set.
  *   q_idx   device [B][D][64] bf16 indexer queries
  *   q_attn  device [B][D][H][576] bf16 attention queries
  *   out     device [B][D][H][512] fp32 attention output

@@ -8,6 +8,14 @@
 //     out = sum_j softmax(z)_j * V_j  over the first 512 (latent) columns,
 // j running over the min(k, L_t) winners of that position.
 //
+// With one query position and one group of 16 heads, every winner row is
+// read by exactly one block, and the launch can also do the miss copy of
+// the step (the Copy-SFA fusion of the Chinese revision): a row that missed
+// is read straight from the pinned host pool (device-mapped) by the block
+// that attends to it and written into its victim slot, so the host-link
+// transfer of one block overlaps the attention of the others and no
+// separate copy kernel runs.
+//
 // Layout of the work: a block takes one (seq, position), one group of 16
 // heads and a chunk of winners.  Rows are staged 32 at a time in LDS (one
 // coalesced 1152-byte read each, gathered by slot); the next tile is fetched
@@ -37,12 +45,13 @@ __device__ __forceinline__ uint32_t dword_of(uint4 v, int m) {
 
 __global__ __launch_bounds__(256) void k_attn_partial(
     const int32_t* __restrict__ topk, const int32_t* __restrict__ cache_slots_layer,
-    const uint4* __restrict__ hot_layer, const uint4* __restrict__ q_attn,
+    uint4* __restrict__ hot_layer, const uint4* __restrict__ q_attn, const uint4* __restrict__ pool_layer,
     const int32_t* __restrict__ ntok_layer, float* __restrict__ part_acc,
     float* __restrict__ part_ml, int32_t* __restrict__ phys, int D, int H, int HG, int top_k,
     int S, int64_t cap, int rows_per_block, int nchunk, float scale_log2) {
     __shared__ uint4 rows[kAttnTileRows * kRowStrideU4];
     __shared__ int32_t slot_s[kAttnMaxRowsPerBlock];
+    __shared__ int32_t src_s[kAttnMaxRowsPerBlock];  // token of a miss copied here, else -1
     __shared__ f32x4_t sp[4][2][64];  // per-wave partial S^T tiles
 
     const int chunk = blockIdx.x, bp = blockIdx.y, hg = blockIdx.z;
@@ -66,15 +75,55 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     const int h = hg * kAttnHeadGroup + n16;
     const int32_t* __restrict__ w = topk + (size_t)bp * top_k;
     const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
-    const uint4* __restrict__ hb = hot_layer + (size_t)b * S * kKvRowU4;
+    uint4* __restrict__ hb = hot_layer + (size_t)b * S * kKvRowU4;
+    const bool copy_misses = pool_layer != nullptr;
 
     // remap: logical winner -> hot slot, for the whole chunk
     for (int j = tid; j < r1 - r0; j += 256) {
-        const int32_t tok = w[r0 + j] & 0x7FFFFFFF;
+        const int32_t packed = w[r0 + j];
+        const int32_t tok = packed & 0x7FFFFFFF;
         int32_t slot = (tok < cap) ? cs[tok] : -1;
         if (slot >= S) slot = -1;
         slot_s[j] = slot;
+        src_s[j] = (copy_misses && packed < 0 && slot >= 0) ? tok : -1;
         if (hg == 0) phys[(size_t)bp * top_k + r0 + j] = slot;
+    }
+
+    // The rows of this chunk that missed: copy them from the pool into their
+    // victim slots first (wave w takes rows w, w+4, ...; lanes 0..63 move
+    // 16-byte chunks 0..63 of a row, lanes 0..7 chunks 64..71), then read
+    // every row from the hot buffer below.
+    if (copy_misses) {
+        __syncthreads();
+        // one row in flight per wave: more outstanding host reads lowered
+        // the link rate of this scattered access pattern
+        constexpr int kCopyRows = 1;
+        for (int j0 = kCopyRows * wave; j0 < r1 - r0; j0 += 4 * kCopyRows) {
+            uint4 a[kCopyRows], c[kCopyRows];
+            int32_t dst[kCopyRows];
+#pragma unroll
+            for (int q = 0; q < kCopyRows; ++q) {
+                const int j = j0 + q;
+                const int32_t src = j < r1 - r0 ? src_s[j] : -1;
+                dst[q] = src >= 0 ? slot_s[j] : -1;
+                const uint4* sp = pool_layer + ((size_t)b * cap + (src >= 0 ? src : 0)) * kKvRowU4;
+                a[q] = make_uint4(0u, 0u, 0u, 0u);
+                c[q] = make_uint4(0u, 0u, 0u, 0u);
+                if (src >= 0) {
+                    a[q] = sp[lane];
+                    if (lane < kKvRowU4 - 64) c[q] = sp[64 + lane];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kCopyRows; ++q) {
+                if (dst[q] >= 0) {
+                    uint4* dp = hb + (size_t)dst[q] * kKvRowU4;
+                    dp[lane] = a[q];
+                    if (lane < kKvRowU4 - 64) dp[64 + lane] = c[q];
+                }
+            }
+        }
+        __threadfence_block();
     }
 
     // The 18 k-steps (32 columns each) of S^T = K Q^T are split over the 4
@@ -289,7 +338,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* _
 }
 
 hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_t* cache_slots_layer,
-                               const uint16_t* hot_layer, const uint16_t* q_attn,
+                               uint16_t* hot_layer, const uint16_t* q_attn, const uint16_t* pool_layer,
                                const int32_t* ntok_layer, float* part_acc, float* part_ml,
                                int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
                                int rows_per_block, float scale) {
@@ -297,8 +346,9 @@ hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_
     const int nchunk = (top_k + rows_per_block - 1) / rows_per_block;
     const float scale_log2 = scale * 1.4426950408889634f;
     hipLaunchKernelGGL(k_attn_partial, dim3(nchunk, B * D, HG), dim3(256), 0, st, topk,
-                       cache_slots_layer, reinterpret_cast<const uint4*>(hot_layer),
-                       reinterpret_cast<const uint4*>(q_attn), ntok_layer, part_acc, part_ml, phys,
+                       cache_slots_layer, reinterpret_cast<uint4*>(hot_layer),
+                       reinterpret_cast<const uint4*>(q_attn), reinterpret_cast<const uint4*>(pool_layer),
+                       ntok_layer, part_acc, part_ml, phys,
                        D, H, HG, top_k, S, cap, rows_per_block, nchunk, scale_log2);
     return hipGetLastError();
 }

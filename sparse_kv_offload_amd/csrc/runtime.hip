@@ -215,7 +215,7 @@ int validate_config(const sko_config* c) {
     if (!(c->attn_scale > 0.0f) || !std::isfinite(c->attn_scale))
         return set_err(SKO_E_INVAL, "attn_scale must be finite and > 0");
     if ((c->flags & ~(SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT | SKO_FLAG_KEEP_KEYS |
-                      SKO_FLAG_SELECT_RESCAN)) != 0 ||
+                      SKO_FLAG_SELECT_RESCAN | SKO_FLAG_SEPARATE_COPY)) != 0 ||
         (c->flags & (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT)) ==
             (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT))
         return set_err(SKO_E_INVAL, "unknown or conflicting flags 0x%x", c->flags);
@@ -493,13 +493,18 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
                                      h->evict_old, h->counts, h->glist, h->stats + (size_t)layer * 8);
          })))
         return rc;
-    if ((rc = run_stage(h, ST_GATHER, [&] {
+    // One position and one head group: the attention launch copies the
+    // misses itself (each row is read by one block), overlapping the
+    // host-link transfer with the attention over resident rows.
+    const bool fused_copy = D == 1 && h->HG == 1 && !(h->cfg.flags & SKO_FLAG_SEPARATE_COPY);
+    if (!fused_copy && (rc = run_stage(h, ST_GATHER, [&] {
              return launch_gather_misses(h->stream, h->glist, h->counts, pool_layer, hot_layer, B, D * k, B * D * k);
          })))
         return rc;
     if ((rc = run_stage(h, ST_ATTN, [&] {
-             return launch_attn_partial(h->stream, h->topk, cs, hot_layer, qa, ntok, h->part_acc, h->part_ml,
-                                        h->phys, B, D, H, k, S, cap, h->rows_per_block, h->cfg.attn_scale);
+             return launch_attn_partial(h->stream, h->topk, cs, hot_layer, qa, fused_copy ? pool_layer : nullptr,
+                                        ntok, h->part_acc, h->part_ml, h->phys, B, D, H, k, S, cap,
+                                        h->rows_per_block, h->cfg.attn_scale);
          })))
         return rc;
     if ((rc = run_stage(h, ST_COMBINE, [&] {

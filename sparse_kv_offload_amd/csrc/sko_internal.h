@@ -107,8 +107,11 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
 hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const int32_t* counts,
                                 const uint16_t* pool_layer, uint16_t* hot_layer, int B, int mstride,
                                 int max_entries);
+// pool_layer non-null: the launch also copies the rows that missed (packed
+// topk entries < 0) from the pool into their slots; only valid when each
+// row is read by one block (one position, at most 16 heads).
 hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_t* cache_slots_layer,
-                               const uint16_t* hot_layer, const uint16_t* q_attn,
+                               uint16_t* hot_layer, const uint16_t* q_attn, const uint16_t* pool_layer,
                                const int32_t* ntok_layer, float* part_acc, float* part_ml,
                                int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
                                int rows_per_block, float scale);

@@ -232,3 +232,14 @@ def test_keys_need_keep_flag():
         with pytest.raises(sko.SkoError) as e:
             h.step_buffer(sko.SKO_BUF_KEYS)
         assert e.value.code == sko.SKO_E_STATE
+
+
+@pytest.mark.parametrize("separate", [False, True])
+def test_copy_in_attention_or_separate(separate):
+    """One position, at most 16 heads: the attention launch copies the misses
+    itself unless SKO_FLAG_SEPARATE_COPY asks for the copy kernel; both give
+    the oracle's results, hot-buffer bytes included."""
+    import sparse_kv_offload_amd as sko
+    w = case("copy", batch=3, context=12000, steps=8, top_k=300, hot_slots=700, positions=1, heads=16)
+    log(f"case copy separate={separate}")
+    run_parity(w, check_keys=False, flags=sko.SKO_FLAG_SEPARATE_COPY if separate else 0, log=log)
