@@ -72,6 +72,12 @@ extern "C" {
  * row is then read by one attention block, which reads a missed row from
  * the pool and stores it into its slot).  Same results. */
 #define SKO_FLAG_SEPARATE_COPY 0x10u
+/* Where the attention does not copy the misses itself, they are normally
+ * copied from the host into a staging area on a second stream as soon as
+ * the selection is known, while the LRU update runs, and moved into their
+ * slots after it.  This flag copies them from the host after the LRU
+ * update instead (one stream).  Same results. */
+#define SKO_FLAG_LATE_COPY 0x20u
 
 typedef struct sko_handle sko_handle;
 
@@ -163,7 +169,9 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
  * -> remap -> attention ([LSO] §4 "Decode step" items 3-7).  With one
  * position and at most 16 heads the gather is done by the attention launch
  * itself (the fused Copy-SFA operator of [LSO-zh] §4), unless
- * SKO_FLAG_SEPARATE_COPY is set.
+ * SKO_FLAG_SEPARATE_COPY is set; otherwise the copy overlaps the LRU update
+ * on a library-owned stream (see SKO_FLAG_LATE_COPY), joined back into the
+ * caller's stream before the step's attention.
  *   q_idx   device [B][D][64] bf16 indexer queries
  *   q_attn  device [B][D][H][576] bf16 attention queries
  *   out     device [B][D][H][512] fp32 attention output

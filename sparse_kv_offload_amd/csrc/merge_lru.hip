@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     int64_t C, int64_t cap, int64_t wpr,
     int32_t t, int32_t* __restrict__ misses, int32_t* __restrict__ victims,
     int32_t* __restrict__ evict_old, int32_t* __restrict__ counts, GatherEntry* __restrict__ glist,
-    unsigned long long* __restrict__ layer_stats) {
+    unsigned long long* __restrict__ layer_stats, int do_refine) {
     __shared__ uint32_t touched[kMaxHotSlots / 32];
     // [0, kMaxMerge): misses; [kMaxMerge, 2 kMaxMerge): the union, later the
     // victims.  Before the merge the whole area stages refine candidates.
@@ -229,8 +229,9 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     const int mstride = D * top_k;
     const int SW = (S + 31) / 32;
 
-    // 0. finish the top-k of rows whose threshold bucket is split
-    refine_rows(b, D, meta, cand, topk, wb, top_k, cap, cstage, hgrp, rgrp);
+    // 0. finish the top-k of rows whose threshold bucket is split (unless
+    //    k_topk_refine already did)
+    if (do_refine) refine_rows(b, D, meta, cand, topk, wb, top_k, cap, cstage, hgrp, rgrp);
 
     for (int i = tid; i < SW; i += kLruThreads) touched[i] = 0u;
     if (tid == 0) cnt[7] = 0;
@@ -444,13 +445,127 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int32_t* pos_layer, RingState* ring_state_layer,
                             int B, int D, int top_k, int S, int64_t cap, int32_t t,
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
-                            GatherEntry* glist, unsigned long long* layer_stats) {
+                            GatherEntry* glist, unsigned long long* layer_stats, bool do_refine) {
     const int64_t C = ring_capacity(S, D, top_k);
     const int64_t wpr = winner_words(cap);
     hipLaunchKernelGGL(k_merge_lru, dim3(B), dim3(kLruThreads), 0, st, winners, hist, meta, cand, topk,
                        ntok_layer, cache_slots_layer, slot_token_layer, last_use_layer, ring0_layer,
                        ring1_layer, pos_layer, ring_state_layer, D, top_k, S, C, cap, wpr, t, misses, victims,
-                       evict_old, counts, glist, layer_stats);
+                       evict_old, counts, glist, layer_stats, do_refine ? 1 : 0);
+    return hipGetLastError();
+}
+
+// Exact selection inside the split threshold bucket of one row per block
+// (256 threads), as refine_rows does inside the merge kernel: radix select
+// from the top on the 52-bit composite, 8 bits per pass, over the staged
+// bucket entries (in LDS when they fit); the entries with composite >= T
+// are appended to the row's winners and marked in the winner bitmap, and
+// in the miss bitmap when they are absent from the hot buffer.
+constexpr int kRefineThreads = 256;
+constexpr int kRefineStage = 4096;
+
+__global__ __launch_bounds__(kRefineThreads) void k_topk_refine(RowMeta* __restrict__ meta,
+                                                                const uint2* __restrict__ cand,
+                                                                int32_t* __restrict__ topk,
+                                                                uint32_t* __restrict__ winners,
+                                                                uint32_t* __restrict__ miss_bits, int D,
+                                                                int top_k, int64_t cap, int64_t wpr) {
+    __shared__ uint2 sg[kRefineStage];
+    __shared__ uint32_t hg[256];
+    __shared__ uint64_t s_prefix, s_T;
+    __shared__ int s_rem, s_done;
+    const int row = blockIdx.x;
+    const int b = row / D;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const RowMeta m = meta[row];
+    if (m.bucket < 0 || m.need <= 0 || m.need == m.bucket_count) return;  // block-uniform
+    const int c = (int)std::min<int64_t>(m.cand_count, cap);
+    const uint2* __restrict__ cg = cand + (size_t)row * cap;
+    const bool staged = c <= kRefineStage;
+    if (staged)
+        for (int i = tid; i < c; i += kRefineThreads) sg[i] = cg[i];
+    if (tid == 0) {
+        s_prefix = 0;
+        s_T = 0;
+        s_rem = m.need;
+        s_done = 0;
+    }
+    __syncthreads();
+    int width = 8;
+    for (int shift = 44;; shift -= width) {
+        if (shift < 0) {
+            width += shift;
+            shift = 0;
+        }
+        hg[tid] = 0u;
+        __syncthreads();
+        const uint64_t prefix = s_prefix;
+        const int rem = s_rem;
+        for (int i = tid; i < c; i += kRefineThreads) {
+            const uint64_t comp = refine_composite(staged ? sg[i] : cg[i]);
+            if ((comp >> (shift + width)) == prefix) atomicAdd(&hg[(comp >> shift) & ((1u << width) - 1u)], 1u);
+        }
+        __syncthreads();
+        if (tid < 64) {
+            // lane holds bins 255-4l .. 252-4l (descending order)
+            uint32_t v[4];
+            int sum = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[j] = hg[255 - 4 * lane - j];
+                sum += (int)v[j];
+            }
+            int incl = sum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            const int excl = incl - sum;
+            if (excl < rem && incl >= rem) {
+                int cacc = excl;
+                for (int j = 0; j < 4; ++j) {
+                    const int cnt = (int)v[j];
+                    if (cacc + cnt >= rem) {
+                        const int d = 255 - 4 * lane - j;
+                        const uint64_t np = (prefix << width) | (uint64_t)d;
+                        s_prefix = np;
+                        s_rem = rem - cacc;
+                        if (cnt == rem - cacc || shift == 0) {
+                            s_done = 1;
+                            s_T = np << shift;
+                        }
+                        break;
+                    }
+                    cacc += cnt;
+                }
+            }
+        }
+        __syncthreads();
+        if (s_done || shift == 0) break;
+    }
+    const uint64_t T = s_T;
+    uint32_t* __restrict__ wb = winners + (size_t)b * wpr;
+    uint32_t* __restrict__ mb = miss_bits ? miss_bits + (size_t)b * wpr : nullptr;
+    for (int base = 0; base < c; base += kRefineThreads) {
+        const int i = base + tid;
+        const bool valid = i < c;
+        const uint2 e = valid ? (staged ? sg[i] : cg[i]) : make_uint2(0u, 0u);
+        const bool win = valid && refine_composite(e) >= T;
+        const int pw = wave_append(&meta[row].out_count, win);
+        if (win && pw < top_k) {
+            const uint32_t tok = e.y & 0x7FFFFFFFu;
+            topk[(size_t)row * top_k + pw] = (int32_t)e.y;
+            atomicOr(&wb[tok >> 5], 1u << (tok & 31u));
+            if (mb && (e.y & 0x80000000u)) atomicOr(&mb[tok >> 5], 1u << (tok & 31u));
+        }
+    }
+}
+
+hipError_t launch_topk_refine(hipStream_t st, RowMeta* meta, const uint2* cand, int32_t* topk, uint32_t* winners,
+                              uint32_t* miss_bits, int B, int D, int top_k, int64_t cap) {
+    hipLaunchKernelGGL(k_topk_refine, dim3(B * D), dim3(kRefineThreads), 0, st, meta, cand, topk, winners,
+                       miss_bits, D, top_k, cap, winner_words(cap));
     return hipGetLastError();
 }
 

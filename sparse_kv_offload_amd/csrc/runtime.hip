@@ -46,10 +46,13 @@ enum Stage {
     ST_GATHER,
     ST_ATTN,
     ST_COMBINE,
+    ST_REFINE,
+    ST_STAGE,
     ST_COUNT
 };
-const char* const kStageNames[ST_COUNT] = {"append_rows",   "score_hist",   "topk_filter", "merge_lru",
-                                           "gather_misses", "attn_partial", "attn_combine"};
+const char* const kStageNames[ST_COUNT] = {"append_rows",  "score_hist",  "topk_filter",  "merge_lru",
+                                           "gather_misses", "attn_partial", "attn_combine", "topk_refine",
+                                           "stage_misses"};
 
 struct DeviceGuard {
     int prev = -1;
@@ -96,6 +99,16 @@ struct sko_handle {
     // per-step scratch (shared by all layers; steps are stream-ordered)
     uint32_t* keys = nullptr;       // [B][D][kcap], only with SKO_FLAG_KEEP_KEYS
     uint2* pre = nullptr;           // [B][D][cap] candidates at or above the floor
+    // early miss copy (several positions or head groups): a second stream
+    // copies the misses into staging while the LRU update runs
+    bool fused_copy = false;        // the attention launch copies the misses
+    bool staged_copy = false;       // early copy into staging
+    hipStream_t side = nullptr;
+    hipEvent_t ev_sel = nullptr, ev_copy = nullptr;
+    uint32_t* miss_bits = nullptr;  // [B][wpr]
+    uint16_t* stage_rows = nullptr; // [B][D*k][576] miss rows copied early
+    int32_t* stage_idx = nullptr;   // [B][cap]
+    int32_t* stage_cnt = nullptr;   // [B]
     int32_t* floor = nullptr;       // [L][B][D] candidate floor (first-digit bin)
     uint32_t* hist = nullptr;       // [B][D][4096]
     RowMeta* meta = nullptr;        // [B][D]
@@ -155,6 +168,11 @@ void free_all(sko_handle* h) {
         (void)hipEventDestroy(p.b);
     }
     for (auto e : h->spare) (void)hipEventDestroy(e);
+    if (h->ev_sel) (void)hipEventDestroy(h->ev_sel);
+    if (h->ev_copy) (void)hipEventDestroy(h->ev_copy);
+    if (h->side) (void)hipStreamDestroy(h->side);
+    h->ev_sel = h->ev_copy = nullptr;
+    h->side = nullptr;
     for (void* p : h->dev_allocs) (void)hipFree(p);
     if (h->pool_host) (void)hipHostFree(h->pool_host);
     h->dev_allocs.clear();
@@ -175,23 +193,28 @@ hipEvent_t take_event(sko_handle* h) {
     return e;
 }
 
-// Launch one stage, bracketed by events when timing is on.
+// Launch one stage on `st` (default: the handle's stream), bracketed by
+// events when timing is on.
 template <typename F>
-int run_stage(sko_handle* h, int stage, F&& launch) {
+int run_stage(sko_handle* h, int stage, F&& launch, hipStream_t st) {
     hipEvent_t a = nullptr, b = nullptr;
     const bool timed = (h->timing_mask >> stage) & 1u;
     if (timed) {
         a = take_event(h);
         b = take_event(h);
-        if (a) (void)hipEventRecord(a, h->stream);
+        if (a) (void)hipEventRecord(a, st);
     }
     hipError_t e = launch();
     if (e != hipSuccess) return device_fail(h, e, kStageNames[stage]);
     if (timed && a && b) {
-        (void)hipEventRecord(b, h->stream);
+        (void)hipEventRecord(b, st);
         h->pending.push_back({stage, a, b});
     }
     return SKO_OK;
+}
+template <typename F>
+int run_stage(sko_handle* h, int stage, F&& launch) {
+    return run_stage(h, stage, static_cast<F&&>(launch), h->stream);
 }
 
 int check_handle(sko_handle* h) {
@@ -215,7 +238,7 @@ int validate_config(const sko_config* c) {
     if (!(c->attn_scale > 0.0f) || !std::isfinite(c->attn_scale))
         return set_err(SKO_E_INVAL, "attn_scale must be finite and > 0");
     if ((c->flags & ~(SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT | SKO_FLAG_KEEP_KEYS |
-                      SKO_FLAG_SELECT_RESCAN | SKO_FLAG_SEPARATE_COPY)) != 0 ||
+                      SKO_FLAG_SELECT_RESCAN | SKO_FLAG_SEPARATE_COPY | SKO_FLAG_LATE_COPY)) != 0 ||
         (c->flags & (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT)) ==
             (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT))
         return set_err(SKO_E_INVAL, "unknown or conflicting flags 0x%x", c->flags);
@@ -285,6 +308,12 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     }
     h->rows_per_block = attn_rows_per_block(h->k, h->B * h->D * h->HG);
     h->nchunk = (h->k + h->rows_per_block - 1) / h->rows_per_block;
+    // One position and one head group: every winner row is read by one
+    // attention block, which then copies the row itself if it missed.
+    // Otherwise the misses known after the selection are copied into a
+    // staging area on a second stream while the LRU update runs.
+    h->fused_copy = h->D == 1 && h->HG == 1 && !(cfg->flags & SKO_FLAG_SEPARATE_COPY);
+    h->staged_copy = !h->fused_copy && !(cfg->flags & SKO_FLAG_LATE_COPY);
 
     const size_t LB = (size_t)h->L * h->B;
     const size_t BD = (size_t)h->B * h->D;
@@ -321,6 +350,16 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     if (cfg->flags & SKO_FLAG_KEEP_KEYS) ok = ok && dev_alloc(h, (void**)&h->keys, BD * h->kcap * 4);
     ok = ok && dev_alloc(h, (void**)&h->pre, BD * h->cap * sizeof(uint2));
     ok = ok && dev_alloc(h, (void**)&h->floor, LB * h->D * 4);
+    if (h->staged_copy) {
+        ok = ok && dev_alloc(h, (void**)&h->miss_bits, (size_t)h->B * h->wpr * 4);
+        ok = ok && dev_alloc(h, (void**)&h->stage_rows, BD * h->k * (size_t)kKvRowBytes);
+        ok = ok && dev_alloc(h, (void**)&h->stage_idx, (size_t)h->B * h->cap * 4);
+        ok = ok && dev_alloc(h, (void**)&h->stage_cnt, (size_t)h->B * 4);
+        // default priority (no other priority is used anywhere)
+        ok = ok && hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&h->ev_sel, hipEventDisableTiming) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&h->ev_copy, hipEventDisableTiming) == hipSuccess;
+    }
     ok = ok && dev_alloc(h, (void**)&h->winners, (size_t)h->B * h->wpr * 4);
     ok = ok && dev_alloc(h, (void**)&h->hist, BD * kHistBins * 4);
     ok = ok && dev_alloc(h, (void**)&h->meta, BD * sizeof(RowMeta));
@@ -353,6 +392,9 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     // selection scratch starts cleared; every step's merge clears it again
     if (e == hipSuccess) e = hipMemsetAsync(h->hist, 0, BD * kHistBins * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->meta, 0, BD * sizeof(RowMeta), h->stream);
+    if (e == hipSuccess && h->staged_copy) e = hipMemsetAsync(h->miss_bits, 0, (size_t)h->B * h->wpr * 4, h->stream);
+    if (e == hipSuccess && h->staged_copy) e = hipMemsetAsync(h->stage_cnt, 0, (size_t)h->B * 4, h->stream);
+    if (e == hipSuccess && h->staged_copy) e = hipMemsetAsync(h->stage_idx, 0, (size_t)h->B * h->cap * 4, h->stream);
     if (e == hipSuccess) {
         // first step: every key is a candidate (or none, to force the rescan path)
         const std::vector<int32_t> fl(LB * h->D, (cfg->flags & SKO_FLAG_SELECT_RESCAN) ? kFloorRescanAll : 0);
@@ -481,24 +523,51 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
                                       h->meta, cs, B, D, h->kcap, cap, h->ntiles, max_now, h->cu_count);
          })))
         return rc;
+    const bool fused_copy = h->fused_copy;
+    const bool staged = h->staged_copy;
     if ((rc = run_stage(h, ST_FILTER, [&] {
              return launch_topk_filter(h->stream, h->hist, h->meta, h->pre, h->cand, h->topk, cs, ntok, h->winners,
-                                       idx_layer, qi, floor_layer, (h->cfg.flags & SKO_FLAG_SELECT_RESCAN) != 0, B,
-                                       D, cap, h->ntiles, k, max_now);
+                                       staged ? h->miss_bits : nullptr, idx_layer, qi, floor_layer,
+                                       (h->cfg.flags & SKO_FLAG_SELECT_RESCAN) != 0, B, D, cap, h->ntiles, k,
+                                       max_now);
          })))
         return rc;
+    if (staged) {
+        // the split buckets first, so that the miss set is complete; then
+        // the misses go host -> staging on the second stream
+        if ((rc = run_stage(h, ST_REFINE, [&] {
+                 return launch_topk_refine(h->stream, h->meta, h->cand, h->topk, h->winners, h->miss_bits, B, D, k,
+                                           cap);
+             })))
+            return rc;
+        hipError_t e = hipEventRecord(h->ev_sel, h->stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_sel, 0);
+        if (e != hipSuccess) return device_fail(h, e, "fork to the copy stream");
+        if ((rc = run_stage(
+                 h, ST_STAGE,
+                 [&] {
+                     return launch_stage_misses(h->side, h->miss_bits, pool_layer, h->stage_rows, h->stage_idx,
+                                                h->stage_cnt, ntok, B, cap, D * k, max_now);
+                 },
+                 h->side)))
+            return rc;
+        e = hipEventRecord(h->ev_copy, h->side);
+        if (e != hipSuccess) return device_fail(h, e, "copy stream event");
+    }
     if ((rc = run_stage(h, ST_MERGE_LRU, [&] {
              return launch_merge_lru(h->stream, h->winners, h->hist, h->meta, h->cand, h->topk, ntok, cs, st, lu,
                                      ring0, ring1, ring_pos, ring_state, B, D, k, S, cap, t, h->misses, h->victims,
-                                     h->evict_old, h->counts, h->glist, h->stats + (size_t)layer * 8);
+                                     h->evict_old, h->counts, h->glist, h->stats + (size_t)layer * 8, !staged);
          })))
         return rc;
-    // One position and one head group: the attention launch copies the
-    // misses itself (each row is read by one block), overlapping the
-    // host-link transfer with the attention over resident rows.
-    const bool fused_copy = D == 1 && h->HG == 1 && !(h->cfg.flags & SKO_FLAG_SEPARATE_COPY);
+    if (staged) {
+        const hipError_t e = hipStreamWaitEvent(h->stream, h->ev_copy, 0);
+        if (e != hipSuccess) return device_fail(h, e, "join the copy stream");
+    }
     if (!fused_copy && (rc = run_stage(h, ST_GATHER, [&] {
-             return launch_gather_misses(h->stream, h->glist, h->counts, pool_layer, hot_layer, B, D * k, B * D * k);
+             return launch_gather_misses(h->stream, h->glist, h->counts, pool_layer, hot_layer, B, D * k, B * D * k,
+                                         staged ? h->stage_rows : nullptr, staged ? h->stage_idx : nullptr,
+                                         staged ? h->stage_cnt : nullptr);
          })))
         return rc;
     if ((rc = run_stage(h, ST_ATTN, [&] {

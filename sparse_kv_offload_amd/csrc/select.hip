@@ -458,16 +458,17 @@ __device__ __forceinline__ uint32_t pack_winner(int64_t token, const int32_t* __
 //     kFilterSpan tokens of the row, recomputing their keys.
 // In both, a key above the bucket (or in it, when the bucket is taken
 // whole) is a winner: written packed to topk and marked in the sequence's
-// winner bitmap; a key in a split bucket is staged (packed) in cand.  Each
+// winner bitmap (and, if absent from the hot buffer, in the miss bitmap when
+// one is given); a key in a split bucket is staged (packed) in cand.  Each
 // pass makes one reservation per list for the block.
 constexpr int kFilterSpanC = 256 * 4;
 
 __global__ __launch_bounds__(256) void k_topk_filter(
     const uint32_t* __restrict__ hist, RowMeta* __restrict__ meta, const uint2* __restrict__ pre,
     uint2* __restrict__ cand, int32_t* __restrict__ topk, const int32_t* __restrict__ cache_slots_layer,
-    const int32_t* __restrict__ ntok_layer, uint32_t* __restrict__ winners, const uint4* __restrict__ idx_layer,
-    const uint32_t* __restrict__ q_idx, int32_t* __restrict__ floor_layer, int rescan_all, int D, int64_t cap,
-    int64_t ntiles, int64_t wpr, int top_k) {
+    const int32_t* __restrict__ ntok_layer, uint32_t* __restrict__ winners, uint32_t* __restrict__ miss_bits,
+    const uint4* __restrict__ idx_layer, const uint32_t* __restrict__ q_idx, int32_t* __restrict__ floor_layer,
+    int rescan_all, int D, int64_t cap, int64_t ntiles, int64_t wpr, int top_k) {
     __shared__ int scratch[8];
     __shared__ int s_bw, s_bs, s_floor;
     __shared__ RowMeta s_res;
@@ -499,6 +500,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(
     const bool take_bucket = m.need == m.bucket_count;
     const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
     uint32_t* __restrict__ wb = winners + (size_t)b * wpr;
+    uint32_t* __restrict__ mb = miss_bits ? miss_bits + (size_t)b * wpr : nullptr;
     int32_t* __restrict__ w = topk + (size_t)row * top_k;
     uint2* __restrict__ cr = cand + (size_t)row * cap;
     const uint32_t* __restrict__ qrow = q_idx + (size_t)row * (kIdxDim / 2);
@@ -553,6 +555,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(
                 ++pw;
                 const uint32_t tok = tk[e] & 0x7FFFFFFFu;
                 atomicOr(&wb[tok >> 5], 1u << (tok & 31u));
+                if (mb && (tk[e] & 0x80000000u)) atomicOr(&mb[tok >> 5], 1u << (tok & 31u));
             } else if ((smask >> e) & 1u) {
                 if (ps < cap) cr[ps] = make_uint2(kv[e], tk[e]);
                 ++ps;
@@ -564,15 +567,16 @@ __global__ __launch_bounds__(256) void k_topk_filter(
 
 hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* meta, const uint2* pre,
                               uint2* cand, int32_t* topk, const int32_t* cache_slots_layer,
-                              const int32_t* ntok_layer, uint32_t* winners, const uint16_t* idx_layer,
-                              const uint16_t* q_idx, int32_t* floor_layer, bool rescan_all, int B, int D,
-                              int64_t cap, int64_t ntiles, int top_k, int64_t max_tokens_now) {
+                              const int32_t* ntok_layer, uint32_t* winners, uint32_t* miss_bits,
+                              const uint16_t* idx_layer, const uint16_t* q_idx, int32_t* floor_layer,
+                              bool rescan_all, int B, int D, int64_t cap, int64_t ntiles, int top_k,
+                              int64_t max_tokens_now) {
     const int64_t wpr = winner_words(cap);
     const int64_t now = std::max<int64_t>(1, max_tokens_now);
     const int per_row = (int)std::min<int64_t>(32, std::max<int64_t>(4, (now + kFilterSpan - 1) / kFilterSpan));
     const dim3 grid((unsigned)per_row, (unsigned)(B * D));
     hipLaunchKernelGGL(k_topk_filter, grid, dim3(256), 0, st, hist, meta, pre, cand, topk, cache_slots_layer,
-                       ntok_layer, winners, reinterpret_cast<const uint4*>(idx_layer),
+                       ntok_layer, winners, miss_bits, reinterpret_cast<const uint4*>(idx_layer),
                        reinterpret_cast<const uint32_t*>(q_idx), floor_layer, rescan_all ? 1 : 0, D, cap, ntiles,
                        wpr, top_k);
     return hipGetLastError();

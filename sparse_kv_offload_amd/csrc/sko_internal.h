@@ -90,9 +90,10 @@ hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const ui
 // Also sets floor_layer for the next step (kFloorRescanAll when rescan_all).
 hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* meta, const uint2* pre,
                               uint2* cand, int32_t* topk, const int32_t* cache_slots_layer,
-                              const int32_t* ntok_layer, uint32_t* winners, const uint16_t* idx_layer,
-                              const uint16_t* q_idx, int32_t* floor_layer, bool rescan_all, int B, int D,
-                              int64_t cap, int64_t ntiles, int top_k, int64_t max_tokens_now);
+                              const int32_t* ntok_layer, uint32_t* winners, uint32_t* miss_bits,
+                              const uint16_t* idx_layer, const uint16_t* q_idx, int32_t* floor_layer,
+                              bool rescan_all, int B, int D, int64_t cap, int64_t ntiles, int top_k,
+                              int64_t max_tokens_now);
 // Also finishes the top-k (split buckets) and clears the histograms and row
 // records for the next step.
 hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, RowMeta* meta,
@@ -102,11 +103,24 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int32_t* pos_layer, RingState* ring_state_layer,
                             int B, int D, int top_k, int S, int64_t cap, int32_t t,
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
-                            GatherEntry* glist, unsigned long long* layer_stats);
+                            GatherEntry* glist, unsigned long long* layer_stats, bool do_refine);
 // Work list: sequence b's entries are glist[b * D*k + r], r < counts[b][2].
+// staging non-null: rows come from staging[b][stage_idx[b][token]] (see
+// launch_stage_misses), and stage_cnt is reset.
 hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const int32_t* counts,
                                 const uint16_t* pool_layer, uint16_t* hot_layer, int B, int mstride,
-                                int max_entries);
+                                int max_entries, const uint16_t* staging, const int32_t* stage_idx,
+                                int32_t* stage_cnt);
+// Copies the rows whose bits are set in miss_bits [B][wpr] from the pool
+// into staging [B][mstride][576] (any order), records stage_idx[b][token],
+// counts into stage_cnt[b], and clears the bits.
+hipError_t launch_stage_misses(hipStream_t st, uint32_t* miss_bits, const uint16_t* pool_layer, uint16_t* staging,
+                               int32_t* stage_idx, int32_t* stage_cnt, const int32_t* ntok_layer, int B,
+                               int64_t cap, int mstride, int64_t max_tokens_now);
+// Resolves split threshold buckets, one row per block (for the staged copy,
+// so that the miss bitmap is complete before the LRU update).
+hipError_t launch_topk_refine(hipStream_t st, RowMeta* meta, const uint2* cand, int32_t* topk, uint32_t* winners,
+                              uint32_t* miss_bits, int B, int D, int top_k, int64_t cap);
 // pool_layer non-null: the launch also copies the rows that missed (packed
 // topk entries < 0) from the pool into their slots; only valid when each
 // row is read by one block (one position, at most 16 heads).

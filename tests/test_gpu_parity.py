@@ -243,3 +243,18 @@ def test_copy_in_attention_or_separate(separate):
     w = case("copy", batch=3, context=12000, steps=8, top_k=300, hot_slots=700, positions=1, heads=16)
     log(f"case copy separate={separate}")
     run_parity(w, check_keys=False, flags=sko.SKO_FLAG_SEPARATE_COPY if separate else 0, log=log)
+
+
+@pytest.mark.parametrize("flags", ["late", "separate_late"])
+def test_late_copy(flags):
+    """The copy of the misses after the LRU update (one stream) gives the same
+    results as the early copy into staging on the second stream."""
+    import sparse_kv_offload_amd as sko
+    if flags == "late":
+        w = case("late", batch=3, context=9000, steps=6, top_k=256, hot_slots=600, positions=2, heads=20)
+        f = sko.SKO_FLAG_LATE_COPY
+    else:
+        w = case("seplate", batch=3, context=9000, steps=6, top_k=256, hot_slots=600, positions=1, heads=8)
+        f = sko.SKO_FLAG_LATE_COPY | sko.SKO_FLAG_SEPARATE_COPY
+    log(f"case {flags}")
+    run_parity(w, check_keys=True, flags=f, log=log)
