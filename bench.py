@@ -68,7 +68,7 @@ def calibration_copy(torch) -> None:
 
 
 # Kernel source file that each modelled stage is compiled from.
-KERNEL_SOURCE = {"score_hist": "select.hip", "gather_misses": "gather.hip",
+KERNEL_SOURCE = {"score_hist": "select.hip", "gather_misses": "gather.hip", "stage_misses": "gather.hip",
                  "attn_partial": "attention.hip"}
 
 
@@ -134,6 +134,9 @@ def main() -> int:
     ap.add_argument("--no-timing", action="store_true", help="time without per-stage events")
     ap.add_argument("--pool", choices=["default", "coherent", "noncoherent"], default="default",
                     help="host-pool allocation mode")
+    ap.add_argument("--copy", choices=["default", "separate", "late", "early", "separate-late"], default="default",
+                    help="miss-copy arrangement: default (in the attention at one position, else early on a "
+                         "second stream), separate (own kernel), late (after the LRU update, one stream)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -157,6 +160,9 @@ def main() -> int:
     t_setup = time.perf_counter()
     flags = {"default": 0, "coherent": sko.SKO_FLAG_POOL_COHERENT,
              "noncoherent": sko.SKO_FLAG_POOL_NONCOHERENT}[args.pool]
+    flags |= {"default": 0, "separate": sko.SKO_FLAG_SEPARATE_COPY, "late": sko.SKO_FLAG_LATE_COPY,
+              "early": sko.SKO_FLAG_EARLY_COPY,
+              "separate-late": sko.SKO_FLAG_SEPARATE_COPY | sko.SKO_FLAG_LATE_COPY}[args.copy]
     cfg = sko.make_config(num_layers=L, batch=B, max_tokens=w.capacity, num_heads=H, top_k=k,
                           hot_slots=w.hot_slots, mtp_positions=D, flags=flags)
     h = sko.SparseKVOffload(cfg, stream)
@@ -231,21 +237,32 @@ def main() -> int:
 
     d = deltas(stats0, stats1)
 
-    def alg_bytes(first_step, nsteps, h2d_bytes, fused):
+    def alg_bytes(first_step, nsteps, h2d_bytes, mode):
         """Algorithmic bytes per launch of the modelled kernels, averaged over
-        decode steps first_step .. first_step + nsteps - 1.  With the miss
-        copy done by the attention launch (fused), that launch is bound by
-        the host link and its bytes are the copied rows."""
+        decode steps first_step .. first_step + nsteps - 1.  The launch that
+        reads the missed rows over the host link is bound by it: the
+        attention (mode "fused"), the staging copy ("early", whose move into
+        the slots is an HBM copy, read + write), or the gather ("late")."""
         avg_lt = w.context + first_step + (nsteps + 1) / 2.0  # tokens present after each append
         ls = L * nsteps
-        copy = (h2d_bytes / ls if ls else 0.0, "host-link", HOST_LINK_PEAK_GBPS)
+        per = h2d_bytes / ls if ls else 0.0
+        copy = (per, "host-link", HOST_LINK_PEAK_GBPS)
         m = {"score_hist": (IDX_ROW * B * avg_lt + IDX_ROW * B * D, "hbm", HBM_PEAK_GBPS)}
-        if fused:
+        if mode == "fused":
             m["attn_partial"] = copy
+            return m
+        if mode == "early":
+            m["stage_misses"] = copy
+            m["gather_misses"] = (2 * per, "hbm", HBM_PEAK_GBPS)
         else:
             m["gather_misses"] = copy
-            m["attn_partial"] = (KV_ROW * B * D * min(k, avg_lt), "hbm", HBM_PEAK_GBPS)
+        m["attn_partial"] = (KV_ROW * B * D * min(k, avg_lt), "hbm", HBM_PEAK_GBPS)
         return m
+
+    def copy_mode(t):
+        if t.get("stage_misses", (0.0, 0))[1]:
+            return "early"
+        return "late" if t.get("gather_misses", (0.0, 0))[1] else "fused"
 
     h2d_ceiling = measure_h2d_ceiling(torch)
     calibration_copy(torch)
@@ -264,16 +281,14 @@ def main() -> int:
 
     rooflines = {}
     if calib:
-        fused = calib.get("gather_misses", (0.0, 0))[1] == 0
-        model = alg_bytes(1, calib_steps, deltas(calib_stats0, stats0)["h2d_bytes"], fused)
+        model = alg_bytes(1, calib_steps, deltas(calib_stats0, stats0)["h2d_bytes"], copy_mode(calib))
         for name in model:
             ms, n = calib.get(name, (0.0, 0))
             if n:
                 rooflines[name] = roof_entry(name, ms, n, model)
     roof = None
     if timing and dominant in timing:
-        model = alg_bytes(args.warmup, K, d["h2d_bytes"], timing.get("gather_misses", (0.0, 0))[1] == 0
-                          and calib.get("gather_misses", (0.0, 0))[1] == 0)
+        model = alg_bytes(args.warmup, K, d["h2d_bytes"], copy_mode(calib))
         ms, n = timing[dominant]
         if dominant in model:
             roof = roof_entry(dominant, ms, n, model)
@@ -296,12 +311,12 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "layers": L, "batch": B, "context": w.context,
                    "top_k": k, "hot_slots": w.hot_slots, "mtp_positions": D, "heads": H,
-                   "parallelism": "none (1 GPU)", "pool": args.pool},
+                   "parallelism": "none (1 GPU)", "pool": args.pool, "copy": args.copy},
         "tokens_per_s": round(B * K / elapsed, 2),
         "indexer_scan_GBps": rooflines.get("score_hist", {}).get("achieved"),
         "miss_gather_GBps": next((e["achieved"] for e in [roof or {}] + list(rooflines.values())
                                   if e.get("bound") == "host-link"), None),
-        "miss_copy_in_attention": calib.get("gather_misses", (0.0, 0))[1] == 0 if calib else None,
+        "miss_copy": copy_mode(calib) if calib else None,
         "h2d_ceiling_GBps": round(h2d_ceiling, 2),
         "hit_rate": round(d["hits"] / max(1, d["unique"]), 4),
         "unique_misses_per_layer_step": round(d["misses"] / layer_steps, 1),

@@ -72,12 +72,15 @@ extern "C" {
  * row is then read by one attention block, which reads a missed row from
  * the pool and stores it into its slot).  Same results. */
 #define SKO_FLAG_SEPARATE_COPY 0x10u
-/* Where the attention does not copy the misses itself, they are normally
- * copied from the host into a staging area on a second stream as soon as
- * the selection is known, while the LRU update runs, and moved into their
- * slots after it.  This flag copies them from the host after the LRU
- * update instead (one stream).  Same results. */
+/* Where the attention does not copy the misses itself, the misses are
+ * copied from the host either late (after the LRU update, one stream) or
+ * early (into a staging area on a second stream as soon as the selection is
+ * known, while the LRU update runs, then moved into their slots).  The
+ * default is early for batches of at most 4 sequences (where the LRU update
+ * is long next to the copy) and late otherwise; these flags force one.
+ * Same results either way; setting both is SKO_E_INVAL. */
 #define SKO_FLAG_LATE_COPY 0x20u
+#define SKO_FLAG_EARLY_COPY 0x40u
 
 typedef struct sko_handle sko_handle;
 

@@ -37,6 +37,7 @@ SKO_FLAG_KEEP_KEYS = 0x4
 SKO_FLAG_SELECT_RESCAN = 0x8
 SKO_FLAG_SEPARATE_COPY = 0x10
 SKO_FLAG_LATE_COPY = 0x20
+SKO_FLAG_EARLY_COPY = 0x40
 
 SKO_BUF_TOPK, SKO_BUF_PHYS, SKO_BUF_COUNTS = 1, 2, 3
 SKO_BUF_MISSES, SKO_BUF_VICTIMS, SKO_BUF_EVICT_OLD, SKO_BUF_KEYS = 4, 5, 6, 7

@@ -15,7 +15,8 @@ namespace sko {
 
 constexpr int kGatherThreads = 256;
 constexpr int kRowsPerWave = 4;  // rows in flight per wave
-constexpr int kGatherMaxBlocks = 512;
+constexpr int kGatherMaxBlocks = 512;       // rows read over the host link
+constexpr int kGatherMaxBlocksHbm = 4096;   // rows moved from the staging area
 
 // Sequence b's entries are glist[b * mstride + r] for r < counts[b][2].
 // Each block first builds the prefix of the per-sequence miss counts in LDS;
@@ -95,8 +96,10 @@ hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const 
                                 int max_entries, const uint16_t* staging, const int32_t* stage_idx,
                                 int32_t* stage_cnt) {
     const int rows_per_block = (kGatherThreads / 64) * kRowsPerWave;
+    // every row in flight at once when the source is device memory; a
+    // bounded number when it is the host pool
     int grid = (int)std::min<int64_t>(((int64_t)max_entries + rows_per_block - 1) / rows_per_block,
-                                      kGatherMaxBlocks);
+                                      staging ? kGatherMaxBlocksHbm : kGatherMaxBlocks);
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(k_gather_misses, dim3(grid), dim3(kGatherThreads), (size_t)(B + 1) * sizeof(int), st,
                        glist, counts, reinterpret_cast<const uint4*>(pool_layer),
@@ -115,8 +118,15 @@ hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const 
 // staging area (kStageRowsPerWave in flight per wave), recording each
 // token's staging row in stage_idx.  Staging rows are in no particular
 // order; the copy into the victim slots after the LRU update looks them up.
-constexpr int kStageWords = 256;
-constexpr int kStageRowsPerWave = 2;
+#ifndef SKO_STAGE_WORDS
+#define SKO_STAGE_WORDS 256
+#endif
+#ifndef SKO_STAGE_RPW
+#define SKO_STAGE_RPW 2
+#endif
+constexpr int kStageWords = SKO_STAGE_WORDS;  // at most kGatherThreads
+static_assert(kStageWords <= kGatherThreads, "one bitmap word per thread");
+constexpr int kStageRowsPerWave = SKO_STAGE_RPW;
 
 __global__ __launch_bounds__(kGatherThreads) void k_stage_misses(uint32_t* __restrict__ miss_bits,
                                                                  const uint4* __restrict__ pool_layer,
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_stage_misses(uint32_t* __res
     const int64_t wi = (int64_t)blockIdx.x * kStageWords + threadIdx.x;
     uint32_t* __restrict__ mb = miss_bits + (size_t)b * wpr;
     uint32_t bits = 0u;
-    if (wi < words_now) {
+    if (threadIdx.x < kStageWords && wi < words_now) {
         bits = mb[wi];
         if (bits) mb[wi] = 0u;
     }

@@ -30,6 +30,7 @@ constexpr int kPreStage = 128;               // per-wave LDS staging of candidat
 // the score distribution holds, and the next threshold has room to fall).
 constexpr int kFloorCover = 2;
 constexpr int kFloorRescanAll = kHistBins;   // a floor no key reaches
+constexpr int kEarlyCopyMaxBatch = 4;       // default early miss copy up to this batch
 
 
 // Indexer cache layout in HBM (per layer): [B][ntiles][8 chunks][64 tokens]

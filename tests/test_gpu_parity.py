@@ -258,3 +258,11 @@ def test_late_copy(flags):
         f = sko.SKO_FLAG_LATE_COPY | sko.SKO_FLAG_SEPARATE_COPY
     log(f"case {flags}")
     run_parity(w, check_keys=True, flags=f, log=log)
+
+
+def test_early_copy_forced_at_larger_batch():
+    """SKO_FLAG_EARLY_COPY takes the early copy beyond the default batch."""
+    import sparse_kv_offload_amd as sko
+    w = case("early", batch=6, context=5000, steps=5, top_k=128, hot_slots=500, positions=3, heads=4)
+    log("case early copy B=6")
+    run_parity(w, check_keys=False, flags=sko.SKO_FLAG_EARLY_COPY, log=log)
