@@ -68,7 +68,7 @@ def calibration_copy(torch) -> None:
 
 
 # Kernel source file that each modelled stage is compiled from.
-KERNEL_SOURCE = {"score_hist": "select.hip", "gather_misses": "gather.hip", "stage_misses": "gather.hip",
+KERNEL_SOURCE = {"score_hist": "select.hip", "gather_misses": "gather.hip", "merge_lru": "merge_lru.hip",
                  "attn_partial": "attention.hip"}
 
 
@@ -252,7 +252,7 @@ def main() -> int:
             m["attn_partial"] = copy
             return m
         if mode == "early":
-            m["stage_misses"] = copy
+            m["merge_lru"] = copy  # its copy blocks read the missed rows from the host
             m["gather_misses"] = (2 * per, "hbm", HBM_PEAK_GBPS)
         else:
             m["gather_misses"] = copy
@@ -260,7 +260,7 @@ def main() -> int:
         return m
 
     def copy_mode(t):
-        if t.get("stage_misses", (0.0, 0))[1]:
+        if t.get("topk_refine", (0.0, 0))[1]:
             return "early"
         return "late" if t.get("gather_misses", (0.0, 0))[1] else "fused"
 

@@ -73,12 +73,10 @@ extern "C" {
  * the pool and stores it into its slot).  Same results. */
 #define SKO_FLAG_SEPARATE_COPY 0x10u
 /* Where the attention does not copy the misses itself, the misses are
- * copied from the host either late (after the LRU update, one stream) or
- * early (into a staging area on a second stream as soon as the selection is
- * known, while the LRU update runs, then moved into their slots).  The
- * default is early for batches of at most 4 sequences (where the LRU update
- * is long next to the copy) and late otherwise; these flags force one.
- * Same results either way; setting both is SKO_E_INVAL. */
+ * copied from the host either late (after the LRU update) or early (into a
+ * staging area by extra blocks of the LRU-update launch, concurrently with
+ * the update, then moved into their slots).  The default is early; these
+ * flags force one.  Same results either way; setting both is SKO_E_INVAL. */
 #define SKO_FLAG_LATE_COPY 0x20u
 #define SKO_FLAG_EARLY_COPY 0x40u
 
@@ -172,9 +170,9 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
  * -> remap -> attention ([LSO] §4 "Decode step" items 3-7).  With one
  * position and at most 16 heads the gather is done by the attention launch
  * itself (the fused Copy-SFA operator of [LSO-zh] §4), unless
- * SKO_FLAG_SEPARATE_COPY is set; otherwise the copy overlaps the LRU update
- * on a library-owned stream (see SKO_FLAG_LATE_COPY), joined back into the
- * caller's stream before the step's attention.
+ * SKO_FLAG_SEPARATE_COPY is set; otherwise the copy is done late (after the
+ * LRU update) or early (by extra blocks of the LRU-update launch), see
+ * SKO_FLAG_LATE_COPY.  Everything runs on the caller's stream.
  *   q_idx   device [B][D][64] bf16 indexer queries
  *   q_attn  device [B][D][H][576] bf16 attention queries
  *   out     device [B][D][H][512] fp32 attention output

@@ -34,7 +34,8 @@ __device__ __forceinline__ int find_seq(const int* pre, int B, int64_t e) {
 // row (one contiguous 1 KB read), lanes 0..7 the last 8 chunks; each wave
 // keeps kRowsPerWave rows in flight before storing them.
 // With `staging` non-null the rows were already copied from the host into
-// the staging area by k_stage_misses: entry (token, slot) then reads
+// the staging area (by the copy blocks of the merge launch): entry (token,
+// slot) then reads
 // staging row stage_idx[b][token] instead of the pool row, and the launch
 // resets the per-sequence staging counters for the next step.
 __global__ __launch_bounds__(kGatherThreads) void k_gather_misses(const GatherEntry* __restrict__ glist,
@@ -105,90 +106,6 @@ hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const 
                        glist, counts, reinterpret_cast<const uint4*>(pool_layer),
                        reinterpret_cast<uint4*>(hot_layer), B, mstride, reinterpret_cast<const uint4*>(staging),
                        stage_idx, stage_cnt);
-    return hipGetLastError();
-}
-
-// Early host -> device copy of the misses, on a second stream while the LRU
-// update runs: the union of the miss-flagged winners of a sequence is its
-// miss set M (a winner's flag is its absence at step start), marked in a
-// bitmap by the selection.  Grid (blocks, B), 256 threads: block j takes
-// bitmap words [256 j, 256 j + 256) of its sequence, lists their tokens in
-// LDS (and clears the words for the next step), reserves that many staging
-// rows with one atomic, and its waves copy the rows from the pool into the
-// staging area (kStageRowsPerWave in flight per wave), recording each
-// token's staging row in stage_idx.  Staging rows are in no particular
-// order; the copy into the victim slots after the LRU update looks them up.
-#ifndef SKO_STAGE_WORDS
-#define SKO_STAGE_WORDS 256
-#endif
-#ifndef SKO_STAGE_RPW
-#define SKO_STAGE_RPW 2
-#endif
-constexpr int kStageWords = SKO_STAGE_WORDS;  // at most kGatherThreads
-static_assert(kStageWords <= kGatherThreads, "one bitmap word per thread");
-constexpr int kStageRowsPerWave = SKO_STAGE_RPW;
-
-__global__ __launch_bounds__(kGatherThreads) void k_stage_misses(uint32_t* __restrict__ miss_bits,
-                                                                 const uint4* __restrict__ pool_layer,
-                                                                 uint4* __restrict__ staging,
-                                                                 int32_t* __restrict__ stage_idx,
-                                                                 int32_t* __restrict__ stage_cnt,
-                                                                 const int32_t* __restrict__ ntok_layer,
-                                                                 int64_t cap, int64_t wpr, int mstride) {
-    __shared__ int32_t toks[kStageWords * 32];
-    __shared__ int scratch[kGatherThreads / 64 + 1];
-    __shared__ int s_base;
-    const int b = blockIdx.y;
-    const int64_t words_now = (ntok_layer[b] + 31) / 32;
-    const int64_t wi = (int64_t)blockIdx.x * kStageWords + threadIdx.x;
-    uint32_t* __restrict__ mb = miss_bits + (size_t)b * wpr;
-    uint32_t bits = 0u;
-    if (threadIdx.x < kStageWords && wi < words_now) {
-        bits = mb[wi];
-        if (bits) mb[wi] = 0u;
-    }
-    int total;
-    int pos = block_exclusive_scan<kGatherThreads>(__popc(bits), &total, scratch);
-    if (total == 0) return;  // block-uniform
-    while (bits) {
-        const int e = __ffs((int)bits) - 1;
-        bits &= bits - 1u;
-        toks[pos++] = (int32_t)(wi * 32 + e);
-    }
-    if (threadIdx.x == 0) s_base = atomicAdd(&stage_cnt[b], total);
-    __syncthreads();
-    const int base = s_base;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int i0 = wave * kStageRowsPerWave; i0 < total; i0 += (kGatherThreads / 64) * kStageRowsPerWave) {
-        uint4 a[kStageRowsPerWave], t8[kStageRowsPerWave];
-#pragma unroll
-        for (int r = 0; r < kStageRowsPerWave; ++r) {
-            const int i = std::min(i0 + r, total - 1);  // in range; duplicates are not stored
-            const uint4* src = pool_layer + ((int64_t)b * cap + toks[i]) * kKvRowU4;
-            a[r] = src[lane];
-            t8[r] = make_uint4(0u, 0u, 0u, 0u);
-            if (lane < kKvRowU4 - 64) t8[r] = src[64 + lane];
-        }
-#pragma unroll
-        for (int r = 0; r < kStageRowsPerWave; ++r) {
-            const int i = i0 + r;
-            if (i >= total || base + i >= mstride) break;
-            uint4* dst = staging + ((int64_t)b * mstride + base + i) * kKvRowU4;
-            dst[lane] = a[r];
-            if (lane < kKvRowU4 - 64) dst[64 + lane] = t8[r];
-            if (lane == 0) stage_idx[(size_t)b * cap + toks[i]] = base + i;
-        }
-    }
-}
-
-hipError_t launch_stage_misses(hipStream_t st, uint32_t* miss_bits, const uint16_t* pool_layer, uint16_t* staging,
-                               int32_t* stage_idx, int32_t* stage_cnt, const int32_t* ntok_layer, int B,
-                               int64_t cap, int mstride, int64_t max_tokens_now) {
-    const int64_t words = std::max<int64_t>(1, (max_tokens_now + 31) / 32);
-    const dim3 grid((unsigned)((words + kStageWords - 1) / kStageWords), (unsigned)B);
-    hipLaunchKernelGGL(k_stage_misses, grid, dim3(kGatherThreads), 0, st, miss_bits,
-                       reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<uint4*>(staging), stage_idx,
-                       stage_cnt, ntok_layer, cap, winner_words(cap), mstride);
     return hipGetLastError();
 }
 

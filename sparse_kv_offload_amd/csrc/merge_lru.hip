@@ -190,6 +190,73 @@ __device__ __forceinline__ void thread_run(int64_t n, int align, int64_t* r0, in
     *r1 = std::min<int64_t>(n, *r0 + per);
 }
 
+// Early miss copy inside the merge launch: blocks past the B merge blocks
+// copy, from the pool into the staging area, the rows of the misses marked
+// in the miss bitmap (the union of the miss-flagged winners of a sequence is
+// its miss set M; a winner's flag is its absence at step start), so the
+// host-link transfer runs while the merge blocks update the LRU state.
+// Copy block j of sequence b takes bitmap words [W j, W j + W): it
+// lists their tokens in LDS, clears the words for the next step, reserves
+// that many staging rows with one atomic, and its 16 waves copy the rows
+// (kCopyRowsPerWave in flight per wave), recording each token's staging row
+// in stage_idx.  Staging rows are in no particular order; the move into the
+// victim slots after this launch looks them up.
+// The launch holds about kCopyBlocks copy blocks in all (each block a run
+// of up to 1024 bitmap words, one per thread): on this link more blocks,
+// i.e. more host reads in flight, lowered the transfer rate (2x the blocks:
+// -15 %, 4x: -25 % at long context) and fewer left it idle (small).
+constexpr int kCopyBlocks = 64;
+constexpr int kCopyRowsPerWave = 2;
+
+__device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, uint32_t* __restrict__ miss_bits,
+                                           const uint4* __restrict__ pool_layer, uint4* __restrict__ stage_rows,
+                                           int32_t* __restrict__ stage_idx, int32_t* __restrict__ stage_cnt,
+                                           const int32_t* __restrict__ ntok_layer, int64_t cap, int64_t wpr,
+                                           int mstride, int32_t* toks, int* scratch, int* s_base) {
+    const int b = cb / nper;
+    const int part = cb - b * nper;
+    const int64_t words_now = (ntok_layer[b] + 31) / 32;
+    const int64_t wi = (int64_t)part * copy_words + threadIdx.x;
+    uint32_t* __restrict__ mb = miss_bits + (size_t)b * wpr;
+    uint32_t bits = 0u;
+    if ((int)threadIdx.x < copy_words && wi < words_now) {
+        bits = mb[wi];
+        if (bits) mb[wi] = 0u;
+    }
+    int total;
+    int pos = block_exclusive_scan<kLruThreads>(__popc(bits), &total, scratch);
+    if (total == 0) return;  // block-uniform
+    while (bits) {
+        const int e = __ffs((int)bits) - 1;
+        bits &= bits - 1u;
+        toks[pos++] = (int32_t)(wi * 32 + e);
+    }
+    if (threadIdx.x == 0) *s_base = atomicAdd(&stage_cnt[b], total);
+    __syncthreads();
+    const int base = *s_base;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int i0 = wave * kCopyRowsPerWave; i0 < total; i0 += (kLruThreads / 64) * kCopyRowsPerWave) {
+        uint4 a[kCopyRowsPerWave], t8[kCopyRowsPerWave];
+#pragma unroll
+        for (int r = 0; r < kCopyRowsPerWave; ++r) {
+            const int i = min(i0 + r, total - 1);  // in range; duplicates are not stored
+            const uint4* src = pool_layer + ((int64_t)b * cap + toks[i]) * kKvRowU4;
+            a[r] = src[lane];
+            t8[r] = make_uint4(0u, 0u, 0u, 0u);
+            if (lane < kKvRowU4 - 64) t8[r] = src[64 + lane];
+        }
+#pragma unroll
+        for (int r = 0; r < kCopyRowsPerWave; ++r) {
+            const int i = i0 + r;
+            if (i >= total || base + i >= mstride) break;
+            uint4* dst = stage_rows + ((int64_t)b * mstride + base + i) * kKvRowU4;
+            dst[lane] = a[r];
+            if (lane < kKvRowU4 - 64) dst[64 + lane] = t8[r];
+            if (lane == 0) stage_idx[(size_t)b * cap + toks[i]] = base + i;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     uint32_t* __restrict__ winners, uint32_t* __restrict__ hist, RowMeta* __restrict__ meta,
     const uint2* __restrict__ cand, int32_t* __restrict__ topk, const int32_t* __restrict__ ntok_layer,
@@ -199,7 +266,9 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     int64_t C, int64_t cap, int64_t wpr,
     int32_t t, int32_t* __restrict__ misses, int32_t* __restrict__ victims,
     int32_t* __restrict__ evict_old, int32_t* __restrict__ counts, GatherEntry* __restrict__ glist,
-    unsigned long long* __restrict__ layer_stats, int do_refine) {
+    unsigned long long* __restrict__ layer_stats, int do_refine, int nseq, int copy_per_seq, int copy_words,
+    uint32_t* __restrict__ miss_bits, const uint4* __restrict__ pool_layer, uint4* __restrict__ stage_rows,
+    int32_t* __restrict__ stage_idx, int32_t* __restrict__ stage_cnt) {
     __shared__ uint32_t touched[kMaxHotSlots / 32];
     // [0, kMaxMerge): misses; [kMaxMerge, 2 kMaxMerge): the union, later the
     // victims.  Before the merge the whole area stages refine candidates.
@@ -213,6 +282,13 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     int32_t* vlist = lists + kMaxMerge;
     uint2* cstage = reinterpret_cast<uint2*>(lists);
 
+    if ((int)blockIdx.x >= nseq) {
+        __shared__ int s_base;
+        copy_block((int)blockIdx.x - nseq, copy_per_seq, copy_words, miss_bits, pool_layer, stage_rows, stage_idx,
+                   stage_cnt,
+                   ntok_layer, cap, wpr, D * top_k, lists, scratch, &s_base);
+        return;
+    }
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t Lt = ntok_layer[b];
@@ -445,13 +521,24 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int32_t* pos_layer, RingState* ring_state_layer,
                             int B, int D, int top_k, int S, int64_t cap, int32_t t,
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
-                            GatherEntry* glist, unsigned long long* layer_stats, bool do_refine) {
+                            GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
+                            uint32_t* miss_bits, const uint16_t* pool_layer, uint16_t* stage_rows, int32_t* stage_idx,
+                            int32_t* stage_cnt, int64_t max_tokens_now) {
     const int64_t C = ring_capacity(S, D, top_k);
     const int64_t wpr = winner_words(cap);
-    hipLaunchKernelGGL(k_merge_lru, dim3(B), dim3(kLruThreads), 0, st, winners, hist, meta, cand, topk,
+    // B merge blocks, then (early copy) B * copy_per_seq copy blocks of
+    // copy_words bitmap words each, about kCopyBlocks in all
+    const int64_t words = std::max<int64_t>(1, (max_tokens_now + 31) / 32);
+    const int copy_words =
+        (int)std::min<int64_t>(kLruThreads, std::max<int64_t>(32, (B * words + kCopyBlocks - 1) / kCopyBlocks));
+    const int copy_per_seq = miss_bits ? (int)((words + copy_words - 1) / copy_words) : 0;
+    hipLaunchKernelGGL(k_merge_lru, dim3(B + B * copy_per_seq), dim3(kLruThreads), 0, st, winners, hist, meta, cand, topk,
                        ntok_layer, cache_slots_layer, slot_token_layer, last_use_layer, ring0_layer,
                        ring1_layer, pos_layer, ring_state_layer, D, top_k, S, C, cap, wpr, t, misses, victims,
-                       evict_old, counts, glist, layer_stats, do_refine ? 1 : 0);
+                       evict_old, counts, glist, layer_stats, do_refine ? 1 : 0, B, copy_per_seq, copy_words,
+                       miss_bits,
+                       reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<uint4*>(stage_rows), stage_idx,
+                       stage_cnt);
     return hipGetLastError();
 }
 

@@ -47,12 +47,10 @@ enum Stage {
     ST_ATTN,
     ST_COMBINE,
     ST_REFINE,
-    ST_STAGE,
     ST_COUNT
 };
-const char* const kStageNames[ST_COUNT] = {"append_rows",  "score_hist",  "topk_filter",  "merge_lru",
-                                           "gather_misses", "attn_partial", "attn_combine", "topk_refine",
-                                           "stage_misses"};
+const char* const kStageNames[ST_COUNT] = {"append_rows",   "score_hist",   "topk_filter",  "merge_lru",
+                                           "gather_misses", "attn_partial", "attn_combine", "topk_refine"};
 
 struct DeviceGuard {
     int prev = -1;
@@ -99,12 +97,11 @@ struct sko_handle {
     // per-step scratch (shared by all layers; steps are stream-ordered)
     uint32_t* keys = nullptr;       // [B][D][kcap], only with SKO_FLAG_KEEP_KEYS
     uint2* pre = nullptr;           // [B][D][cap] candidates at or above the floor
-    // early miss copy (several positions or head groups): a second stream
-    // copies the misses into staging while the LRU update runs
+    // early miss copy (several positions or head groups, small batch): copy
+    // blocks of the merge launch move the misses into staging while the
+    // merge blocks update the LRU state
     bool fused_copy = false;        // the attention launch copies the misses
     bool staged_copy = false;       // early copy into staging
-    hipStream_t side = nullptr;
-    hipEvent_t ev_sel = nullptr, ev_copy = nullptr;
     uint32_t* miss_bits = nullptr;  // [B][wpr]
     uint16_t* stage_rows = nullptr; // [B][D*k][576] miss rows copied early
     int32_t* stage_idx = nullptr;   // [B][cap]
@@ -168,14 +165,6 @@ void free_all(sko_handle* h) {
         (void)hipEventDestroy(p.b);
     }
     for (auto e : h->spare) (void)hipEventDestroy(e);
-    if (h->ev_sel) (void)hipEventDestroy(h->ev_sel);
-    if (h->ev_copy) (void)hipEventDestroy(h->ev_copy);
-    if (h->side) {
-        (void)hipStreamSynchronize(h->side);
-        (void)hipStreamDestroy(h->side);
-    }
-    h->ev_sel = h->ev_copy = nullptr;
-    h->side = nullptr;
     for (void* p : h->dev_allocs) (void)hipFree(p);
     if (h->pool_host) (void)hipHostFree(h->pool_host);
     h->dev_allocs.clear();
@@ -319,12 +308,9 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     // Otherwise the misses known after the selection are copied into a
     // staging area on a second stream while the LRU update runs.
     h->fused_copy = h->D == 1 && h->HG == 1 && !(cfg->flags & SKO_FLAG_SEPARATE_COPY);
-    // The early copy pays when the LRU update is long next to the copy: the
-    // update runs one block per sequence, so its time hardly grows with B
-    // while the copy grows with B.  Measured: B = 2 (long context) gains 9 %,
-    // B = 16 loses 1 %; the default takes the early copy up to B = 4.
-    h->staged_copy = !h->fused_copy && !(cfg->flags & SKO_FLAG_LATE_COPY) &&
-                     (h->B <= kEarlyCopyMaxBatch || (cfg->flags & SKO_FLAG_EARLY_COPY));
+    // The early copy takes the LRU update off the critical path: measured
+    // +20 % at long context (B = 2), +2.5 % at B = 16 over the late copy.
+    h->staged_copy = !h->fused_copy && !(cfg->flags & SKO_FLAG_LATE_COPY);
 
     const size_t LB = (size_t)h->L * h->B;
     const size_t BD = (size_t)h->B * h->D;
@@ -366,10 +352,6 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
         ok = ok && dev_alloc(h, (void**)&h->stage_rows, BD * h->k * (size_t)kKvRowBytes);
         ok = ok && dev_alloc(h, (void**)&h->stage_idx, (size_t)h->B * h->cap * 4);
         ok = ok && dev_alloc(h, (void**)&h->stage_cnt, (size_t)h->B * 4);
-        // default priority (no other priority is used anywhere)
-        ok = ok && hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) == hipSuccess;
-        ok = ok && hipEventCreateWithFlags(&h->ev_sel, hipEventDisableTiming) == hipSuccess;
-        ok = ok && hipEventCreateWithFlags(&h->ev_copy, hipEventDisableTiming) == hipSuccess;
     }
     ok = ok && dev_alloc(h, (void**)&h->winners, (size_t)h->B * h->wpr * 4);
     ok = ok && dev_alloc(h, (void**)&h->hist, BD * kHistBins * 4);
@@ -543,38 +525,21 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
                                        max_now);
          })))
         return rc;
-    if (staged) {
-        // the split buckets first, so that the miss set is complete; then
-        // the misses go host -> staging on the second stream
-        if ((rc = run_stage(h, ST_REFINE, [&] {
-                 return launch_topk_refine(h->stream, h->meta, h->cand, h->topk, h->winners, h->miss_bits, B, D, k,
-                                           cap);
-             })))
-            return rc;
-        hipError_t e = hipEventRecord(h->ev_sel, h->stream);
-        if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_sel, 0);
-        if (e != hipSuccess) return device_fail(h, e, "fork to the copy stream");
-        if ((rc = run_stage(
-                 h, ST_STAGE,
-                 [&] {
-                     return launch_stage_misses(h->side, h->miss_bits, pool_layer, h->stage_rows, h->stage_idx,
-                                                h->stage_cnt, ntok, B, cap, D * k, max_now);
-                 },
-                 h->side)))
-            return rc;
-        e = hipEventRecord(h->ev_copy, h->side);
-        if (e != hipSuccess) return device_fail(h, e, "copy stream event");
-    }
+    if (staged && (rc = run_stage(h, ST_REFINE, [&] {
+                       // the split buckets first, so that the miss set is complete
+                       // when the merge launch starts copying
+                       return launch_topk_refine(h->stream, h->meta, h->cand, h->topk, h->winners, h->miss_bits, B,
+                                                 D, k, cap);
+                   })))
+        return rc;
     if ((rc = run_stage(h, ST_MERGE_LRU, [&] {
              return launch_merge_lru(h->stream, h->winners, h->hist, h->meta, h->cand, h->topk, ntok, cs, st, lu,
                                      ring0, ring1, ring_pos, ring_state, B, D, k, S, cap, t, h->misses, h->victims,
-                                     h->evict_old, h->counts, h->glist, h->stats + (size_t)layer * 8, !staged);
+                                     h->evict_old, h->counts, h->glist, h->stats + (size_t)layer * 8, !staged,
+                                     staged ? h->miss_bits : nullptr, pool_layer, h->stage_rows, h->stage_idx,
+                                     h->stage_cnt, max_now);
          })))
         return rc;
-    if (staged) {
-        const hipError_t e = hipStreamWaitEvent(h->stream, h->ev_copy, 0);
-        if (e != hipSuccess) return device_fail(h, e, "join the copy stream");
-    }
     if (!fused_copy && (rc = run_stage(h, ST_GATHER, [&] {
              return launch_gather_misses(h->stream, h->glist, h->counts, pool_layer, hot_layer, B, D * k, B * D * k,
                                          staged ? h->stage_rows : nullptr, staged ? h->stage_idx : nullptr,

@@ -30,7 +30,6 @@ constexpr int kPreStage = 128;               // per-wave LDS staging of candidat
 // the score distribution holds, and the next threshold has room to fall).
 constexpr int kFloorCover = 2;
 constexpr int kFloorRescanAll = kHistBins;   // a floor no key reaches
-constexpr int kEarlyCopyMaxBatch = 4;       // default early miss copy up to this batch
 
 
 // Indexer cache layout in HBM (per layer): [B][ntiles][8 chunks][64 tokens]
@@ -104,7 +103,13 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int32_t* pos_layer, RingState* ring_state_layer,
                             int B, int D, int top_k, int S, int64_t cap, int32_t t,
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
-                            GatherEntry* glist, unsigned long long* layer_stats, bool do_refine);
+                            GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
+                            uint32_t* miss_bits, const uint16_t* pool_layer, uint16_t* stage_rows, int32_t* stage_idx,
+                            int32_t* stage_cnt, int64_t max_tokens_now);
+// (miss_bits non-null: the launch also holds copy blocks that move the rows
+// marked in miss_bits [B][wpr] from the pool into stage_rows [B][D*k][576],
+// any order, record stage_idx[b][token], count into stage_cnt[b] and clear
+// the bits: the early miss copy, overlapping the LRU update.)
 // Work list: sequence b's entries are glist[b * D*k + r], r < counts[b][2].
 // staging non-null: rows come from staging[b][stage_idx[b][token]] (see
 // launch_stage_misses), and stage_cnt is reset.
@@ -112,14 +117,8 @@ hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const 
                                 const uint16_t* pool_layer, uint16_t* hot_layer, int B, int mstride,
                                 int max_entries, const uint16_t* staging, const int32_t* stage_idx,
                                 int32_t* stage_cnt);
-// Copies the rows whose bits are set in miss_bits [B][wpr] from the pool
-// into staging [B][mstride][576] (any order), records stage_idx[b][token],
-// counts into stage_cnt[b], and clears the bits.
-hipError_t launch_stage_misses(hipStream_t st, uint32_t* miss_bits, const uint16_t* pool_layer, uint16_t* staging,
-                               int32_t* stage_idx, int32_t* stage_cnt, const int32_t* ntok_layer, int B,
-                               int64_t cap, int mstride, int64_t max_tokens_now);
-// Resolves split threshold buckets, one row per block (for the staged copy,
-// so that the miss bitmap is complete before the LRU update).
+// Resolves split threshold buckets, one row per block (for the early copy,
+// so that the miss bitmap is complete before the merge launch).
 hipError_t launch_topk_refine(hipStream_t st, RowMeta* meta, const uint2* cand, int32_t* topk, uint32_t* winners,
                               uint32_t* miss_bits, int B, int D, int top_k, int64_t cap);
 // pool_layer non-null: the launch also copies the rows that missed (packed
