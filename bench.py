@@ -135,8 +135,9 @@ def main() -> int:
     ap.add_argument("--pool", choices=["default", "coherent", "noncoherent"], default="default",
                     help="host-pool allocation mode")
     ap.add_argument("--copy", choices=["default", "separate", "late", "early", "separate-late"], default="default",
-                    help="miss-copy arrangement: default (in the attention at one position, else early on a "
-                         "second stream), separate (own kernel), late (after the LRU update, one stream)")
+                    help="miss-copy arrangement: default (in the attention at one position, else early, by "
+                         "blocks of the LRU-update launch), separate (not in the attention), late (after the "
+                         "LRU update), early (forced)")
     args = ap.parse_args()
 
     if args.gpus != 1:

@@ -306,7 +306,7 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     // One position and one head group: every winner row is read by one
     // attention block, which then copies the row itself if it missed.
     // Otherwise the misses known after the selection are copied into a
-    // staging area on a second stream while the LRU update runs.
+    // staging area by extra blocks of the LRU-update launch.
     h->fused_copy = h->D == 1 && h->HG == 1 && !(cfg->flags & SKO_FLAG_SEPARATE_COPY);
     // The early copy takes the LRU update off the critical path: measured
     // +20 % at long context (B = 2), +2.5 % at B = 16 over the late copy.

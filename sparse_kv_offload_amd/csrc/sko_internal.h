@@ -112,7 +112,7 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
 // the bits: the early miss copy, overlapping the LRU update.)
 // Work list: sequence b's entries are glist[b * D*k + r], r < counts[b][2].
 // staging non-null: rows come from staging[b][stage_idx[b][token]] (see
-// launch_stage_misses), and stage_cnt is reset.
+// the copy blocks of launch_merge_lru), and stage_cnt is reset.
 hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const int32_t* counts,
                                 const uint16_t* pool_layer, uint16_t* hot_layer, int B, int mstride,
                                 int max_entries, const uint16_t* staging, const int32_t* stage_idx,

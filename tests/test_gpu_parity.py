@@ -248,7 +248,7 @@ def test_copy_in_attention_or_separate(separate):
 @pytest.mark.parametrize("flags", ["late", "separate_late"])
 def test_late_copy(flags):
     """The copy of the misses after the LRU update (one stream) gives the same
-    results as the early copy into staging on the second stream."""
+    results as the early copy into staging beside the update."""
     import sparse_kv_offload_amd as sko
     if flags == "late":
         w = case("late", batch=3, context=9000, steps=6, top_k=256, hot_slots=600, positions=2, heads=20)
