@@ -134,10 +134,10 @@ def main() -> int:
     ap.add_argument("--no-timing", action="store_true", help="time without per-stage events")
     ap.add_argument("--pool", choices=["default", "coherent", "noncoherent"], default="default",
                     help="host-pool allocation mode")
-    ap.add_argument("--copy", choices=["default", "separate", "late", "early", "separate-late"], default="default",
-                    help="miss-copy arrangement: default (in the attention at one position, else early, by "
-                         "blocks of the LRU-update launch), separate (not in the attention), late (after the "
-                         "LRU update), early (forced)")
+    ap.add_argument("--copy", choices=["default", "early", "late", "fused"], default="default",
+                    help="miss-copy arrangement: early (the default: by extra blocks of the LRU-update launch, "
+                         "into staging), late (after the LRU update), fused (inside the attention launch; one "
+                         "position, at most 16 heads)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -161,9 +161,8 @@ def main() -> int:
     t_setup = time.perf_counter()
     flags = {"default": 0, "coherent": sko.SKO_FLAG_POOL_COHERENT,
              "noncoherent": sko.SKO_FLAG_POOL_NONCOHERENT}[args.pool]
-    flags |= {"default": 0, "separate": sko.SKO_FLAG_SEPARATE_COPY, "late": sko.SKO_FLAG_LATE_COPY,
-              "early": sko.SKO_FLAG_EARLY_COPY,
-              "separate-late": sko.SKO_FLAG_SEPARATE_COPY | sko.SKO_FLAG_LATE_COPY}[args.copy]
+    flags |= {"default": 0, "early": sko.SKO_FLAG_EARLY_COPY, "late": sko.SKO_FLAG_LATE_COPY,
+              "fused": sko.SKO_FLAG_FUSED_COPY}[args.copy]
     cfg = sko.make_config(num_layers=L, batch=B, max_tokens=w.capacity, num_heads=H, top_k=k,
                           hot_slots=w.hot_slots, mtp_positions=D, flags=flags)
     h = sko.SparseKVOffload(cfg, stream)
@@ -242,8 +241,10 @@ def main() -> int:
         """Algorithmic bytes per launch of the modelled kernels, averaged over
         decode steps first_step .. first_step + nsteps - 1.  The launch that
         reads the missed rows over the host link is bound by it: the
-        attention (mode "fused"), the staging copy ("early", whose move into
-        the slots is an HBM copy, read + write), or the gather ("late")."""
+        attention (mode "fused"), the staging copy of the merge launch
+        ("early"; the attention then reads missed rows from the staging area
+        and writes each into its slot once, on top of its reads of the
+        winners), or the gather ("late")."""
         avg_lt = w.context + first_step + (nsteps + 1) / 2.0  # tokens present after each append
         ls = L * nsteps
         per = h2d_bytes / ls if ls else 0.0
@@ -252,12 +253,13 @@ def main() -> int:
         if mode == "fused":
             m["attn_partial"] = copy
             return m
+        attn = KV_ROW * B * D * min(k, avg_lt)
         if mode == "early":
             m["merge_lru"] = copy  # its copy blocks read the missed rows from the host
-            m["gather_misses"] = (2 * per, "hbm", HBM_PEAK_GBPS)
+            attn += per
         else:
             m["gather_misses"] = copy
-        m["attn_partial"] = (KV_ROW * B * D * min(k, avg_lt), "hbm", HBM_PEAK_GBPS)
+        m["attn_partial"] = (attn, "hbm", HBM_PEAK_GBPS)
         return m
 
     def copy_mode(t):

@@ -67,16 +67,18 @@ extern "C" {
 /* Testing: no candidate floor, so every step selects through the rescan
  * path (same results, slower). */
 #define SKO_FLAG_SELECT_RESCAN 0x8u
-/* Copy the misses in their own kernel before the attention even where the
- * attention could copy them itself (one position, at most 16 heads: each
- * row is then read by one attention block, which reads a missed row from
- * the pool and stores it into its slot).  Same results. */
-#define SKO_FLAG_SEPARATE_COPY 0x10u
-/* Where the attention does not copy the misses itself, the misses are
- * copied from the host either late (after the LRU update) or early (into a
- * staging area by extra blocks of the LRU-update launch, concurrently with
- * the update, then moved into their slots).  The default is early; these
- * flags force one.  Same results either way; setting both is SKO_E_INVAL. */
+/* How the rows that missed reach the device (at most one of these three;
+ * all give the same results).  Default (SKO_FLAG_EARLY_COPY): as soon as
+ * the selection is known, extra blocks of the LRU-update launch copy the
+ * misses from the pool into a staging area, concurrently with the update;
+ * the attention reads them from there and stores each into its slot.
+ * SKO_FLAG_LATE_COPY: one kernel after the LRU update copies them from the
+ * pool into their slots.  SKO_FLAG_FUSED_COPY: the attention launch reads
+ * each missed row from the pool and stores it into its slot before
+ * attending (the fused Copy-SFA operator of [LSO-zh] §4); only with one
+ * position and at most 16 heads, where each row is read by one attention
+ * block (SKO_E_INVAL otherwise). */
+#define SKO_FLAG_FUSED_COPY 0x10u
 #define SKO_FLAG_LATE_COPY 0x20u
 #define SKO_FLAG_EARLY_COPY 0x40u
 
@@ -167,12 +169,10 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
  * sko_decode_step — one sparse decode step of `layer` for all B sequences
  * and D positions, enqueued on the stream (asynchronous; no host sync):
  * score -> packed top-k -> merge/dedupe -> LRU update -> miss-only gather
- * -> remap -> attention ([LSO] §4 "Decode step" items 3-7).  With one
- * position and at most 16 heads the gather is done by the attention launch
- * itself (the fused Copy-SFA operator of [LSO-zh] §4), unless
- * SKO_FLAG_SEPARATE_COPY is set; otherwise the copy is done late (after the
- * LRU update) or early (by extra blocks of the LRU-update launch), see
- * SKO_FLAG_LATE_COPY.  Everything runs on the caller's stream.
+ * -> remap -> attention ([LSO] §4 "Decode step" items 3-7).  The gather
+ * is done early (by extra blocks of the LRU-update launch), late, or inside
+ * the attention launch, see SKO_FLAG_EARLY_COPY.  Everything runs on the
+ * caller's stream.
  *   q_idx   device [B][D][64] bf16 indexer queries
  *   q_attn  device [B][D][H][576] bf16 attention queries
  *   out     device [B][D][H][512] fp32 attention output

@@ -35,7 +35,7 @@ SKO_FLAG_POOL_COHERENT = 0x1
 SKO_FLAG_POOL_NONCOHERENT = 0x2
 SKO_FLAG_KEEP_KEYS = 0x4
 SKO_FLAG_SELECT_RESCAN = 0x8
-SKO_FLAG_SEPARATE_COPY = 0x10
+SKO_FLAG_FUSED_COPY = 0x10
 SKO_FLAG_LATE_COPY = 0x20
 SKO_FLAG_EARLY_COPY = 0x40
 

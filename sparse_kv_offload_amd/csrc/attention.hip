@@ -8,13 +8,16 @@
 //     out = sum_j softmax(z)_j * V_j  over the first 512 (latent) columns,
 // j running over the min(k, L_t) winners of that position.
 //
-// With one query position and one group of 16 heads, every winner row is
-// read by exactly one block, and the launch can also do the miss copy of
-// the step (the Copy-SFA fusion of the Chinese revision): a row that missed
-// is read straight from the pinned host pool (device-mapped) by the block
-// that attends to it and written into its victim slot, so the host-link
-// transfer of one block overlaps the attention of the others and no
-// separate copy kernel runs.
+// The launch also puts the rows that missed into their victim slots.  With
+// one query position and one group of 16 heads every winner row is read by
+// exactly one block, which can read a missed row straight from the pinned
+// host pool (device-mapped) and write it into its slot (the Copy-SFA fusion
+// of the Chinese revision), so the host-link transfer of one block overlaps
+// the attention of the others and no separate copy kernel runs.  Otherwise
+// the rows were copied early into a staging area that follows the hot
+// buffer in memory: every block reads its missed rows from there, and the
+// first block to claim a row (a flag bit in its staging index) also writes
+// it into its victim slot for later steps.
 //
 // Layout of the work: a block takes one (seq, position), one group of 16
 // heads and a chunk of winners.  Rows are staged 32 at a time in LDS (one
@@ -43,15 +46,20 @@ __device__ __forceinline__ uint32_t dword_of(uint4 v, int m) {
     return (m >> 1) == 0 ? v.x : (m >> 1) == 1 ? v.y : (m >> 1) == 2 ? v.z : v.w;
 }
 
+// How the launch gets the rows that missed into their slots.
+enum AttnCopy { kCopyNone = 0, kCopyPool = 1, kCopyStaged = 2 };
+
+template <int COPY>
 __global__ __launch_bounds__(256) void k_attn_partial(
     const int32_t* __restrict__ topk, const int32_t* __restrict__ cache_slots_layer,
     uint4* __restrict__ hot_layer, const uint4* __restrict__ q_attn, const uint4* __restrict__ pool_layer,
     const int32_t* __restrict__ ntok_layer, float* __restrict__ part_acc,
-    float* __restrict__ part_ml, int32_t* __restrict__ phys, int D, int H, int HG, int top_k,
-    int S, int64_t cap, int rows_per_block, int nchunk, float scale_log2) {
+    float* __restrict__ part_ml, int32_t* __restrict__ phys, const uint4* __restrict__ stage_rows,
+    int32_t* __restrict__ stage_idx, int32_t* __restrict__ stage_cnt, int B, int D, int H, int HG,
+    int top_k, int S, int64_t cap, int rows_per_block, int nchunk, float scale_log2) {
     __shared__ uint4 rows[kAttnTileRows * kRowStrideU4];
-    __shared__ int32_t slot_s[kAttnMaxRowsPerBlock];
-    __shared__ int32_t src_s[kAttnMaxRowsPerBlock];  // token of a miss copied here, else -1
+    __shared__ int32_t slot_s[kAttnMaxRowsPerBlock];  // row read, relative to the sequence's hot rows
+    __shared__ int32_t cp_s[kAttnMaxRowsPerBlock];    // copy: pool token (fused) or victim slot (staged), else -1
     __shared__ f32x4_t sp[4][2][64];  // per-wave partial S^T tiles
 
     const int chunk = blockIdx.x, bp = blockIdx.y, hg = blockIdx.z;
@@ -76,7 +84,13 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     const int32_t* __restrict__ w = topk + (size_t)bp * top_k;
     const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
     uint4* __restrict__ hb = hot_layer + (size_t)b * S * kKvRowU4;
-    const bool copy_misses = pool_layer != nullptr;
+    constexpr bool fused_copy = COPY == kCopyPool;
+    constexpr bool staged = COPY == kCopyStaged;
+    if (staged && chunk == 0 && bp == 0 && hg == 0)
+        for (int i = tid; i < B; i += 256) stage_cnt[i] = 0;  // the next step's staging starts empty
+    // staging rows of this sequence, as row numbers relative to hb (the
+    // staging area lies in the same allocation, after every layer's rows)
+    const int64_t stage_base = staged ? (stage_rows - hb) / kKvRowU4 + (int64_t)b * D * top_k : 0;
 
     // remap: logical winner -> hot slot, for the whole chunk
     for (int j = tid; j < r1 - r0; j += 256) {
@@ -84,43 +98,44 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         const int32_t tok = packed & 0x7FFFFFFF;
         int32_t slot = (tok < cap) ? cs[tok] : -1;
         if (slot >= S) slot = -1;
-        slot_s[j] = slot;
-        src_s[j] = (copy_misses && packed < 0 && slot >= 0) ? tok : -1;
+        int32_t rd = slot, cp = -1;
+        if (packed < 0 && slot >= 0) {
+            if (fused_copy) {
+                cp = tok;
+            } else if (staged) {
+                const int32_t old = atomicOr(&stage_idx[(size_t)b * cap + tok], kStageClaimed);
+                rd = (int32_t)(stage_base + min(max(old & ~kStageClaimed, 0), D * top_k - 1));
+                if (!(old & kStageClaimed)) cp = slot;
+            }
+        }
+        slot_s[j] = rd;
+        cp_s[j] = cp;
         if (hg == 0) phys[(size_t)bp * top_k + r0 + j] = slot;
     }
 
-    // The rows of this chunk that missed: copy them from the pool into their
-    // victim slots first (wave w takes rows w, w+4, ...; lanes 0..63 move
-    // 16-byte chunks 0..63 of a row, lanes 0..7 chunks 64..71), then read
-    // every row from the hot buffer below.
-    if (copy_misses) {
+    // Fused: the missed rows of this chunk are copied from the pool into
+    // their slots first (wave w takes rows w, w+4, ...; lanes 0..63 move
+    // 16-byte chunks 0..63 of a row, lanes 0..7 chunks 64..71), and the
+    // attention below reads the slots.  (Staged: the attention reads the
+    // staging rows, and the tile loads below also store the claimed ones
+    // into their slots.)
+    if (fused_copy) {
         __syncthreads();
         // one row in flight per wave: more outstanding host reads lowered
         // the link rate of this scattered access pattern
-        constexpr int kCopyRows = 1;
-        for (int j0 = kCopyRows * wave; j0 < r1 - r0; j0 += 4 * kCopyRows) {
-            uint4 a[kCopyRows], c[kCopyRows];
-            int32_t dst[kCopyRows];
-#pragma unroll
-            for (int q = 0; q < kCopyRows; ++q) {
-                const int j = j0 + q;
-                const int32_t src = j < r1 - r0 ? src_s[j] : -1;
-                dst[q] = src >= 0 ? slot_s[j] : -1;
-                const uint4* sp = pool_layer + ((size_t)b * cap + (src >= 0 ? src : 0)) * kKvRowU4;
-                a[q] = make_uint4(0u, 0u, 0u, 0u);
-                c[q] = make_uint4(0u, 0u, 0u, 0u);
-                if (src >= 0) {
-                    a[q] = sp[lane];
-                    if (lane < kKvRowU4 - 64) c[q] = sp[64 + lane];
-                }
+        for (int j = wave; j < r1 - r0; j += 4) {
+            const int32_t c = cp_s[j];
+            const int32_t dst = c >= 0 ? slot_s[j] : -1;
+            const uint4* sp = pool_layer + ((size_t)b * cap + (c >= 0 ? c : 0)) * kKvRowU4;
+            uint4 a = make_uint4(0u, 0u, 0u, 0u), e = make_uint4(0u, 0u, 0u, 0u);
+            if (c >= 0) {
+                a = sp[lane];
+                if (lane < kKvRowU4 - 64) e = sp[64 + lane];
             }
-#pragma unroll
-            for (int q = 0; q < kCopyRows; ++q) {
-                if (dst[q] >= 0) {
-                    uint4* dp = hb + (size_t)dst[q] * kKvRowU4;
-                    dp[lane] = a[q];
-                    if (lane < kKvRowU4 - 64) dp[64 + lane] = c[q];
-                }
+            if (dst >= 0) {
+                uint4* dp = hb + (size_t)dst * kKvRowU4;
+                dp[lane] = a;
+                if (lane < kKvRowU4 - 64) dp[64 + lane] = e;
             }
         }
         __threadfence_block();
@@ -168,8 +183,20 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         const int rr = idx / kKvRowU4;                               \
         rows[rr * kRowStrideU4 + (idx - rr * kKvRowU4)] = pre[u];    \
     }
+    // staged: a tile row this block claimed is also stored into its slot
+#define SKO_MOVE(rbase)                                                                   \
+    if (staged) {                                                                         \
+        _Pragma("unroll") for (int u = 0; u < kPer; ++u) {                               \
+            const int idx = tid + 256 * u;                                               \
+            const int rr = idx / kKvRowU4;                                               \
+            const int j = (rbase) + rr;                                                  \
+            const int32_t c = (j < r1) ? cp_s[j - r0] : -1;                              \
+            if (c >= 0) hb[(size_t)c * kKvRowU4 + (idx - rr * kKvRowU4)] = pre[u];       \
+        }                                                                                \
+    }
     SKO_FETCH(r0)
     SKO_STASH()
+    SKO_MOVE(r0)
     __syncthreads();
 
     for (int r = r0; r < r1; r += kAttnTileRows) {
@@ -258,11 +285,13 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         __syncthreads();
         if (more) {
             SKO_STASH()
+            SKO_MOVE(r + kAttnTileRows)
             __syncthreads();
         }
     }
 #undef SKO_FETCH
 #undef SKO_STASH
+#undef SKO_MOVE
 
     float lt = l_run + __shfl_xor(l_run, 16);
     lt += __shfl_xor(lt, 32);
@@ -341,15 +370,26 @@ hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_
                                uint16_t* hot_layer, const uint16_t* q_attn, const uint16_t* pool_layer,
                                const int32_t* ntok_layer, float* part_acc, float* part_ml,
                                int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
-                               int rows_per_block, float scale) {
+                               int rows_per_block, float scale, const uint16_t* stage_rows,
+                               int32_t* stage_idx, int32_t* stage_cnt) {
     const int HG = (H + kAttnHeadGroup - 1) / kAttnHeadGroup;
     const int nchunk = (top_k + rows_per_block - 1) / rows_per_block;
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(k_attn_partial, dim3(nchunk, B * D, HG), dim3(256), 0, st, topk,
-                       cache_slots_layer, reinterpret_cast<uint4*>(hot_layer),
-                       reinterpret_cast<const uint4*>(q_attn), reinterpret_cast<const uint4*>(pool_layer),
-                       ntok_layer, part_acc, part_ml, phys,
-                       D, H, HG, top_k, S, cap, rows_per_block, nchunk, scale_log2);
+#define SKO_ATTN_LAUNCH(C)                                                                                  \
+    hipLaunchKernelGGL(k_attn_partial<C>, dim3(nchunk, B * D, HG), dim3(256), 0, st, topk, cache_slots_layer,  \
+                       reinterpret_cast<uint4*>(hot_layer), reinterpret_cast<const uint4*>(q_attn),             \
+                       reinterpret_cast<const uint4*>(pool_layer), ntok_layer, part_acc, part_ml, phys,         \
+                       reinterpret_cast<const uint4*>(stage_rows), stage_idx, stage_cnt, B, D, H, HG, top_k, S, \
+                       cap, rows_per_block, nchunk, scale_log2)
+    if (pool_layer != nullptr && stage_rows != nullptr) return hipErrorInvalidValue;
+    if (pool_layer != nullptr) {
+        SKO_ATTN_LAUNCH(kCopyPool);
+    } else if (stage_rows != nullptr) {
+        SKO_ATTN_LAUNCH(kCopyStaged);
+    } else {
+        SKO_ATTN_LAUNCH(kCopyNone);
+    }
+#undef SKO_ATTN_LAUNCH
     return hipGetLastError();
 }
 

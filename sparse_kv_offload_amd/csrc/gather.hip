@@ -15,8 +15,7 @@ namespace sko {
 
 constexpr int kGatherThreads = 256;
 constexpr int kRowsPerWave = 4;  // rows in flight per wave
-constexpr int kGatherMaxBlocks = 512;       // rows read over the host link
-constexpr int kGatherMaxBlocksHbm = 4096;   // rows moved from the staging area
+constexpr int kGatherMaxBlocks = 512;  // bounds the host reads in flight
 
 // Sequence b's entries are glist[b * mstride + r] for r < counts[b][2].
 // Each block first builds the prefix of the per-sequence miss counts in LDS;
@@ -33,18 +32,11 @@ __device__ __forceinline__ int find_seq(const int* pre, int B, int64_t e) {
 // One wave copies whole rows: lanes 0..63 read chunks 0..63 of a 1152-byte
 // row (one contiguous 1 KB read), lanes 0..7 the last 8 chunks; each wave
 // keeps kRowsPerWave rows in flight before storing them.
-// With `staging` non-null the rows were already copied from the host into
-// the staging area (by the copy blocks of the merge launch): entry (token,
-// slot) then reads
-// staging row stage_idx[b][token] instead of the pool row, and the launch
-// resets the per-sequence staging counters for the next step.
 __global__ __launch_bounds__(kGatherThreads) void k_gather_misses(const GatherEntry* __restrict__ glist,
                                                                   const int32_t* __restrict__ counts,
                                                                   const uint4* __restrict__ pool_layer,
                                                                   uint4* __restrict__ hot_layer, int B,
-                                                                  int mstride, const uint4* __restrict__ staging,
-                                                                  const int32_t* __restrict__ stage_idx,
-                                                                  int32_t* __restrict__ stage_cnt) {
+                                                                  int mstride) {
     extern __shared__ int pre[];  // B + 1
     __shared__ int scratch[kGatherThreads / 64 + 1];
     const int per = (B + kGatherThreads - 1) / kGatherThreads;
@@ -60,8 +52,6 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_misses(const GatherEn
     if (threadIdx.x == 0) pre[B] = total;
     __syncthreads();
 
-    if (stage_cnt && blockIdx.x == 0)
-        for (int b = threadIdx.x; b < B; b += kGatherThreads) stage_cnt[b] = 0;
     const int lane = threadIdx.x & 63;
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
@@ -73,11 +63,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_misses(const GatherEn
             const int64_t e = std::min<int64_t>(e0 + r, total - 1);  // in range; duplicates are not stored
             const int b = find_seq(pre, B, e);
             const GatherEntry g = glist[(size_t)b * mstride + (e - pre[b])];
-            // (a staging index outside [0, mstride) cannot occur; it is
-            // clamped so that no read leaves the staging area)
-            const int32_t si = staging ? std::min(std::max(stage_idx[g.src_row], 0), mstride - 1) : 0;
-            const uint4* src = staging ? staging + ((int64_t)b * mstride + si) * kKvRowU4
-                                       : pool_layer + (int64_t)g.src_row * kKvRowU4;
+            const uint4* src = pool_layer + (int64_t)g.src_row * kKvRowU4;
             a[r] = src[lane];
             t8[r] = make_uint4(0u, 0u, 0u, 0u);
             if (lane < kKvRowU4 - 64) t8[r] = src[64 + lane];
@@ -94,18 +80,14 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_misses(const GatherEn
 
 hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const int32_t* counts,
                                 const uint16_t* pool_layer, uint16_t* hot_layer, int B, int mstride,
-                                int max_entries, const uint16_t* staging, const int32_t* stage_idx,
-                                int32_t* stage_cnt) {
+                                int max_entries) {
     const int rows_per_block = (kGatherThreads / 64) * kRowsPerWave;
-    // every row in flight at once when the source is device memory; a
-    // bounded number when it is the host pool
     int grid = (int)std::min<int64_t>(((int64_t)max_entries + rows_per_block - 1) / rows_per_block,
-                                      staging ? kGatherMaxBlocksHbm : kGatherMaxBlocks);
+                                      kGatherMaxBlocks);
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(k_gather_misses, dim3(grid), dim3(kGatherThreads), (size_t)(B + 1) * sizeof(int), st,
                        glist, counts, reinterpret_cast<const uint4*>(pool_layer),
-                       reinterpret_cast<uint4*>(hot_layer), B, mstride, reinterpret_cast<const uint4*>(staging),
-                       stage_idx, stage_cnt);
+                       reinterpret_cast<uint4*>(hot_layer), B, mstride);
     return hipGetLastError();
 }
 

@@ -199,8 +199,8 @@ __device__ __forceinline__ void thread_run(int64_t n, int align, int64_t* r0, in
 // lists their tokens in LDS, clears the words for the next step, reserves
 // that many staging rows with one atomic, and its 16 waves copy the rows
 // (kCopyRowsPerWave in flight per wave), recording each token's staging row
-// in stage_idx.  Staging rows are in no particular order; the move into the
-// victim slots after this launch looks them up.
+// in stage_idx.  Staging rows are in no particular order; the attention
+// launch after this one looks them up (and moves each into its victim slot).
 // The launch holds about kCopyBlocks copy blocks in all (each block a run
 // of up to 1024 bitmap words, one per thread): on this link more blocks,
 // i.e. more host reads in flight, lowered the transfer rate (2x the blocks:

@@ -103,7 +103,7 @@ struct sko_handle {
     bool fused_copy = false;        // the attention launch copies the misses
     bool staged_copy = false;       // early copy into staging
     uint32_t* miss_bits = nullptr;  // [B][wpr]
-    uint16_t* stage_rows = nullptr; // [B][D*k][576] miss rows copied early
+    uint16_t* stage_rows = nullptr; // [B][D*k][576] miss rows copied early (inside the hot allocation)
     int32_t* stage_idx = nullptr;   // [B][cap]
     int32_t* stage_cnt = nullptr;   // [B]
     int32_t* floor = nullptr;       // [L][B][D] candidate floor (first-digit bin)
@@ -230,13 +230,19 @@ int validate_config(const sko_config* c) {
     if (!(c->attn_scale > 0.0f) || !std::isfinite(c->attn_scale))
         return set_err(SKO_E_INVAL, "attn_scale must be finite and > 0");
     if ((c->flags & ~(SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT | SKO_FLAG_KEEP_KEYS |
-                      SKO_FLAG_SELECT_RESCAN | SKO_FLAG_SEPARATE_COPY | SKO_FLAG_LATE_COPY |
+                      SKO_FLAG_SELECT_RESCAN | SKO_FLAG_FUSED_COPY | SKO_FLAG_LATE_COPY |
                       SKO_FLAG_EARLY_COPY)) != 0 ||
         (c->flags & (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT)) ==
             (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT))
         return set_err(SKO_E_INVAL, "unknown or conflicting flags 0x%x", c->flags);
-    if ((c->flags & SKO_FLAG_LATE_COPY) && (c->flags & SKO_FLAG_EARLY_COPY))
-        return set_err(SKO_E_INVAL, "SKO_FLAG_LATE_COPY and SKO_FLAG_EARLY_COPY conflict");
+    {
+        const uint32_t modes = c->flags & (SKO_FLAG_FUSED_COPY | SKO_FLAG_LATE_COPY | SKO_FLAG_EARLY_COPY);
+        if (modes & (modes - 1))
+            return set_err(SKO_E_INVAL, "at most one of SKO_FLAG_FUSED_COPY, _LATE_COPY, _EARLY_COPY");
+        if ((modes & SKO_FLAG_FUSED_COPY) && (c->mtp_positions != 1 || c->num_heads > kAttnHeadGroup))
+            return set_err(SKO_E_INVAL, "SKO_FLAG_FUSED_COPY needs mtp_positions == 1 and num_heads <= %d",
+                           kAttnHeadGroup);
+    }
     if (c->device < 0) return set_err(SKO_E_INVAL, "device must be >= 0");
     if (c->hot_slots > kMaxHotSlots)
         return set_err(SKO_E_UNSUPPORTED, "hot_slots above %d", kMaxHotSlots);
@@ -244,6 +250,10 @@ int validate_config(const sko_config* c) {
         return set_err(SKO_E_UNSUPPORTED, "mtp_positions*top_k above %d", SKO_MAX_MERGE);
     if ((int64_t)c->batch * c->max_tokens >= 0xFFFFFFFFLL || (int64_t)c->batch * c->hot_slots >= 0xFFFFFFFFLL)
         return set_err(SKO_E_UNSUPPORTED, "batch*max_tokens and batch*hot_slots must stay below 2^32");
+    // hot rows of every layer plus the staging rows are addressed by int32 row numbers
+    if ((int64_t)c->num_layers * c->batch * c->hot_slots + (int64_t)c->batch * c->mtp_positions * c->top_k >=
+        0x7FFFFFFFLL)
+        return set_err(SKO_E_UNSUPPORTED, "num_layers*batch*hot_slots must stay below 2^31");
     return SKO_OK;
 }
 
@@ -303,13 +313,12 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     }
     h->rows_per_block = attn_rows_per_block(h->k, h->B * h->D * h->HG);
     h->nchunk = (h->k + h->rows_per_block - 1) / h->rows_per_block;
-    // One position and one head group: every winner row is read by one
-    // attention block, which then copies the row itself if it missed.
-    // Otherwise the misses known after the selection are copied into a
-    // staging area by extra blocks of the LRU-update launch.
-    h->fused_copy = h->D == 1 && h->HG == 1 && !(cfg->flags & SKO_FLAG_SEPARATE_COPY);
-    // The early copy takes the LRU update off the critical path: measured
-    // +20 % at long context (B = 2), +2.5 % at B = 16 over the late copy.
+    // Early copy by default: extra blocks of the LRU-update launch read the
+    // misses into staging while the update runs, so neither the update nor
+    // the attention waits on the host link (measured against copying inside
+    // the attention at one position: tiny +18 %, small +4.5 %, shelf even;
+    // against the late copy: long +20 %, mtp3 +2 %).
+    h->fused_copy = (cfg->flags & SKO_FLAG_FUSED_COPY) != 0;
     h->staged_copy = !h->fused_copy && !(cfg->flags & SKO_FLAG_LATE_COPY);
 
     const size_t LB = (size_t)h->L * h->B;
@@ -334,7 +343,11 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     bool ok = true;
     ok = ok && dev_alloc(h, (void**)&h->idx, LB * h->ntiles * kIdxTile * kIdxDim * 2);
     ok = ok && dev_alloc(h, (void**)&h->staging, (size_t)kStagingRows * kIdxDim * 2);
-    ok = ok && dev_alloc(h, (void**)&h->hot, LB * h->S * (size_t)kKvRowBytes);
+    // the staging rows of the early copy follow the hot rows of every layer
+    // in one allocation (the attention addresses both from one base)
+    const size_t stage_rows_n = h->staged_copy ? BD * h->k : 0;
+    ok = ok && dev_alloc(h, (void**)&h->hot, (LB * h->S + stage_rows_n) * (size_t)kKvRowBytes);
+    if (ok && h->staged_copy) h->stage_rows = h->hot + LB * h->S * kKvDim;
     ok = ok && dev_alloc(h, (void**)&h->cache_slots, LB * h->cap * 4);
     ok = ok && dev_alloc(h, (void**)&h->slot_token, LB * h->S * 4);
     ok = ok && dev_alloc(h, (void**)&h->last_use, LB * h->S * 4);
@@ -349,7 +362,6 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     ok = ok && dev_alloc(h, (void**)&h->floor, LB * h->D * 4);
     if (h->staged_copy) {
         ok = ok && dev_alloc(h, (void**)&h->miss_bits, (size_t)h->B * h->wpr * 4);
-        ok = ok && dev_alloc(h, (void**)&h->stage_rows, BD * h->k * (size_t)kKvRowBytes);
         ok = ok && dev_alloc(h, (void**)&h->stage_idx, (size_t)h->B * h->cap * 4);
         ok = ok && dev_alloc(h, (void**)&h->stage_cnt, (size_t)h->B * 4);
     }
@@ -540,16 +552,17 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
                                      h->stage_cnt, max_now);
          })))
         return rc;
-    if (!fused_copy && (rc = run_stage(h, ST_GATHER, [&] {
-             return launch_gather_misses(h->stream, h->glist, h->counts, pool_layer, hot_layer, B, D * k, B * D * k,
-                                         staged ? h->stage_rows : nullptr, staged ? h->stage_idx : nullptr,
-                                         staged ? h->stage_cnt : nullptr);
+    // late copy: its own gather from the pool; fused or early: the attention
+    // launch puts the missed rows into their slots itself
+    if (!fused_copy && !staged && (rc = run_stage(h, ST_GATHER, [&] {
+             return launch_gather_misses(h->stream, h->glist, h->counts, pool_layer, hot_layer, B, D * k, B * D * k);
          })))
         return rc;
     if ((rc = run_stage(h, ST_ATTN, [&] {
              return launch_attn_partial(h->stream, h->topk, cs, hot_layer, qa, fused_copy ? pool_layer : nullptr,
                                         ntok, h->part_acc, h->part_ml, h->phys, B, D, H, k, S, cap,
-                                        h->rows_per_block, h->cfg.attn_scale);
+                                        h->rows_per_block, h->cfg.attn_scale, staged ? h->stage_rows : nullptr,
+                                        staged ? h->stage_idx : nullptr, staged ? h->stage_cnt : nullptr);
          })))
         return rc;
     if ((rc = run_stage(h, ST_COMBINE, [&] {

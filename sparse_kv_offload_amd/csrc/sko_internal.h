@@ -21,6 +21,7 @@ constexpr int kMaxHotSlots = 1 << 18;        // S limit (LDS bitmap of touched s
 constexpr int kAttnHeadGroup = 16;           // heads per MFMA tile (M = 16)
 constexpr int kAttnTileRows = 32;            // rows per attention tile
 constexpr int kAttnMaxRowsPerBlock = 512;    // rows of one attention block (remap table)
+constexpr int32_t kStageClaimed = 1 << 30;   // staging index flag: row already moved into its slot
 constexpr int kFilterKeysPerThread = 16;
 constexpr int kFilterSpan = 256 * kFilterKeysPerThread;  // keys per block pass
 constexpr int kPreStage = 128;               // per-wave LDS staging of candidates
@@ -110,25 +111,28 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
 // marked in miss_bits [B][wpr] from the pool into stage_rows [B][D*k][576],
 // any order, record stage_idx[b][token], count into stage_cnt[b] and clear
 // the bits: the early miss copy, overlapping the LRU update.)
-// Work list: sequence b's entries are glist[b * D*k + r], r < counts[b][2].
-// staging non-null: rows come from staging[b][stage_idx[b][token]] (see
-// the copy blocks of launch_merge_lru), and stage_cnt is reset.
+// Late copy from the pool into the slots.  Work list: sequence b's entries
+// are glist[b * D*k + r], r < counts[b][2].
 hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const int32_t* counts,
                                 const uint16_t* pool_layer, uint16_t* hot_layer, int B, int mstride,
-                                int max_entries, const uint16_t* staging, const int32_t* stage_idx,
-                                int32_t* stage_cnt);
+                                int max_entries);
 // Resolves split threshold buckets, one row per block (for the early copy,
 // so that the miss bitmap is complete before the merge launch).
 hipError_t launch_topk_refine(hipStream_t st, RowMeta* meta, const uint2* cand, int32_t* topk, uint32_t* winners,
                               uint32_t* miss_bits, int B, int D, int top_k, int64_t cap);
 // pool_layer non-null: the launch also copies the rows that missed (packed
 // topk entries < 0) from the pool into their slots; only valid when each
-// row is read by one block (one position, at most 16 heads).
+// row is read by one block (one position, at most 16 heads).  stage_rows
+// non-null instead (it must lie in the allocation of hot_layer, at a row
+// boundary after it): missed rows are read from stage_rows[b][stage_idx[b]
+// [token]], the first block to set kStageClaimed in that index also moves
+// the row into its slot, and stage_cnt is reset.
 hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_t* cache_slots_layer,
                                uint16_t* hot_layer, const uint16_t* q_attn, const uint16_t* pool_layer,
                                const int32_t* ntok_layer, float* part_acc, float* part_ml,
                                int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
-                               int rows_per_block, float scale);
+                               int rows_per_block, float scale, const uint16_t* stage_rows,
+                               int32_t* stage_idx, int32_t* stage_cnt);
 hipError_t launch_attn_combine(hipStream_t st, const float* part_acc, const float* part_ml,
                                float* out, int B, int D, int H, int nchunk);
 // Rings of n_seqs sequences: ring0 = 0..S-1, pos = identity, head 0, tail S.

@@ -47,7 +47,9 @@ def good_cfg(sko, **kw):
     dict(index_dim=32), dict(kv_dim=512), dict(v_dim=576), dict(num_layers=0), dict(batch=0),
     dict(num_heads=0), dict(top_k=0), dict(mtp_positions=0), dict(max_tokens=0),
     dict(max_tokens=2 ** 31), dict(hot_slots=127), dict(attn_scale=0.0),
-    dict(attn_scale=float("inf")), dict(attn_scale=float("nan")), dict(flags=128), dict(flags=0x60), dict(flags=0x80000000), dict(flags=3),
+    dict(attn_scale=float("inf")), dict(attn_scale=float("nan")), dict(flags=128), dict(flags=0x60),
+    dict(flags=0x30), dict(flags=0x50), dict(flags=0x80000000), dict(flags=3),
+    dict(flags=0x10, mtp_positions=2), dict(flags=0x10, mtp_positions=1, num_heads=17),
     dict(device=-1),
 ])
 def test_create_rejects_bad_config(bad):
@@ -62,6 +64,15 @@ def test_create_rejects_unsupported_merge_width():
     import sparse_kv_offload_amd as sko
     with pytest.raises(sko.SkoError) as e:
         sko.sko_create(good_cfg(sko, top_k=4096, mtp_positions=3, hot_slots=3 * 4096))
+    assert e.value.code == sko.SKO_E_UNSUPPORTED
+
+
+def test_create_rejects_hot_rows_beyond_int32():
+    """Hot rows of every layer plus the staging rows are addressed by int32
+    row numbers: 2^14 layers x 2^9 sequences x 2^8 slots is refused."""
+    import sparse_kv_offload_amd as sko
+    with pytest.raises(sko.SkoError) as e:
+        sko.sko_create(good_cfg(sko, num_layers=1 << 14, batch=1 << 9, hot_slots=1 << 8))
     assert e.value.code == sko.SKO_E_UNSUPPORTED
 
 

@@ -234,35 +234,33 @@ def test_keys_need_keep_flag():
         assert e.value.code == sko.SKO_E_STATE
 
 
-@pytest.mark.parametrize("separate", [False, True])
-def test_copy_in_attention_or_separate(separate):
-    """One position, at most 16 heads: the attention launch copies the misses
-    itself unless SKO_FLAG_SEPARATE_COPY asks for the copy kernel; both give
-    the oracle's results, hot-buffer bytes included."""
+@pytest.mark.parametrize("mode", ["early", "fused", "late"])
+def test_copy_modes_one_position(mode):
+    """One position, 16 heads: the early copy (staging, the default), the
+    copy inside the attention launch and the late copy all give the oracle's
+    results, hot-buffer bytes included."""
     import sparse_kv_offload_amd as sko
     w = case("copy", batch=3, context=12000, steps=8, top_k=300, hot_slots=700, positions=1, heads=16)
-    log(f"case copy separate={separate}")
-    run_parity(w, check_keys=False, flags=sko.SKO_FLAG_SEPARATE_COPY if separate else 0, log=log)
+    log(f"case copy mode={mode}")
+    f = {"early": 0, "fused": sko.SKO_FLAG_FUSED_COPY, "late": sko.SKO_FLAG_LATE_COPY}[mode]
+    run_parity(w, check_keys=False, flags=f, log=log)
 
 
-@pytest.mark.parametrize("flags", ["late", "separate_late"])
-def test_late_copy(flags):
-    """The copy of the misses after the LRU update (one stream) gives the same
-    results as the early copy into staging beside the update."""
+@pytest.mark.parametrize("mode", ["late", "early"])
+def test_copy_modes_positions_and_head_groups(mode):
+    """Two positions and two head groups: a missed row is read by several
+    attention blocks.  Late copy, and early copy (forced by its flag), where
+    the blocks read the staging row and exactly one of them moves it into
+    its slot."""
     import sparse_kv_offload_amd as sko
-    if flags == "late":
-        w = case("late", batch=3, context=9000, steps=6, top_k=256, hot_slots=600, positions=2, heads=20)
-        f = sko.SKO_FLAG_LATE_COPY
-    else:
-        w = case("seplate", batch=3, context=9000, steps=6, top_k=256, hot_slots=600, positions=1, heads=8)
-        f = sko.SKO_FLAG_LATE_COPY | sko.SKO_FLAG_SEPARATE_COPY
-    log(f"case {flags}")
+    w = case(mode, batch=3, context=9000, steps=6, top_k=256, hot_slots=600, positions=2, heads=20)
+    log(f"case {mode} D=2 H=20")
+    f = {"late": sko.SKO_FLAG_LATE_COPY, "early": sko.SKO_FLAG_EARLY_COPY}[mode]
     run_parity(w, check_keys=True, flags=f, log=log)
 
 
-def test_early_copy_forced_at_larger_batch():
-    """SKO_FLAG_EARLY_COPY takes the early copy beyond the default batch."""
-    import sparse_kv_offload_amd as sko
+def test_early_copy_three_positions():
+    """Early copy at three positions and a larger batch."""
     w = case("early", batch=6, context=5000, steps=5, top_k=128, hot_slots=500, positions=3, heads=4)
-    log("case early copy B=6")
-    run_parity(w, check_keys=False, flags=sko.SKO_FLAG_EARLY_COPY, log=log)
+    log("case early copy B=6 D=3")
+    run_parity(w, check_keys=False, flags=0, log=log)
