@@ -263,9 +263,7 @@ def main() -> int:
         return m
 
     def copy_mode(t):
-        if t.get("topk_refine", (0.0, 0))[1]:
-            return "early"
-        return "late" if t.get("gather_misses", (0.0, 0))[1] else "fused"
+        return {"late": "late", "fused": "fused"}.get(args.copy, "early")
 
     h2d_ceiling = measure_h2d_ceiling(torch)
     calibration_copy(torch)
@@ -324,6 +322,13 @@ def main() -> int:
         "hit_rate": round(d["hits"] / max(1, d["unique"]), 4),
         "unique_misses_per_layer_step": round(d["misses"] / layer_steps, 1),
         "h2d_bytes_per_layer_step": int(d["h2d_bytes"] / layer_steps),
+        # the host link alone, at the measured bulk rate, would allow this
+        # many layer-steps/s; value / link_bound = share of the layer-step
+        # during which the link carries misses at that rate
+        "link_bound_layer_steps_per_s": round(h2d_ceiling * 1e9 * layer_steps / d["h2d_bytes"], 1)
+        if d["h2d_bytes"] else None,
+        "frac_of_link_bound": round(value * d["h2d_bytes"] / (h2d_ceiling * 1e9 * layer_steps), 4)
+        if d["h2d_bytes"] else None,
         "selection_rescans": d["rescans"],
         "roofline": roof,
         "rooflines": rooflines,

@@ -72,6 +72,12 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     const size_t pidx = ((size_t)bp * HG + hg) * nchunk + chunk;
     float* __restrict__ acc_out = part_acc + pidx * kAttnHeadGroup * kVDim;
     float* __restrict__ ml_out = part_ml + pidx * kAttnHeadGroup * 2;
+    constexpr bool fused_copy = COPY == kCopyPool;
+    constexpr bool staged = COPY == kCopyStaged;
+    // the next step's staging starts empty (reset by the first block, which
+    // may have no rows when sequence 0 holds no tokens)
+    if (staged && chunk == 0 && bp == 0 && hg == 0)
+        for (int i = tid; i < B; i += 256) stage_cnt[i] = 0;
     if (r0 >= r1) {
         if (tid < kAttnHeadGroup) {
             ml_out[2 * tid] = -INFINITY;
@@ -84,10 +90,6 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     const int32_t* __restrict__ w = topk + (size_t)bp * top_k;
     const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
     uint4* __restrict__ hb = hot_layer + (size_t)b * S * kKvRowU4;
-    constexpr bool fused_copy = COPY == kCopyPool;
-    constexpr bool staged = COPY == kCopyStaged;
-    if (staged && chunk == 0 && bp == 0 && hg == 0)
-        for (int i = tid; i < B; i += 256) stage_cnt[i] = 0;  // the next step's staging starts empty
     // staging rows of this sequence, as row numbers relative to hb (the
     // staging area lies in the same allocation, after every layer's rows)
     const int64_t stage_base = staged ? (stage_rows - hb) / kKvRowU4 + (int64_t)b * D * top_k : 0;

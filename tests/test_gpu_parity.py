@@ -153,6 +153,49 @@ def test_empty_sequence_gives_zero_output():
         assert np.all(out.cpu().numpy() == 0.0)
 
 
+def test_early_copy_with_empty_first_sequence():
+    """Early copy while sequence 0 holds no tokens (its attention blocks have
+    no rows): the per-step staging state must still be reset, so over
+    several steps with new misses the results equal the late copy's
+    (selection and hot-buffer rows bit for bit)."""
+    import torch
+    import sparse_kv_offload_amd as sko
+    w = case("empty0", batch=2, context=700, top_k=32)
+    handles = []
+    for f in (0, sko.SKO_FLAG_LATE_COPY):
+        cfg = sko.make_config(num_layers=1, batch=2, max_tokens=700, num_heads=16, top_k=32,
+                              hot_slots=64, mtp_positions=1, flags=f)
+        handles.append(sko.SparseKVOffload(cfg, torch.cuda.current_stream()))
+    try:
+        for h in handles:
+            h.append(0, 1, w.index_rows(0, 1, 0, 400), w.kv_rows(0, 1, 0, 400))
+        gen = torch.Generator().manual_seed(11)
+        for step in range(6):
+            log(f"case empty0 step {step}")
+            lo = 400 + 40 * step
+            qi = (torch.randn((2, 1, 64), generator=gen) * 0.3).to(torch.bfloat16).view(torch.int16).cuda()
+            qa = (torch.randn((2, 1, 16, 576), generator=gen) * 0.3).to(torch.bfloat16).view(torch.int16).cuda()
+            outs = []
+            for h in handles:
+                h.append(0, 1, w.index_rows(0, 1, lo, 40), w.kv_rows(0, 1, lo, 40))
+                out = torch.full((2, 1, 16, 512), 7.0, device="cuda")
+                h.decode_step(0, qi, qa, out)
+                torch.cuda.synchronize()
+                outs.append((out.cpu().numpy(), h.step_buffer(sko.SKO_BUF_COUNTS),
+                             h.step_buffer(sko.SKO_BUF_PHYS), h.table(0, 1, sko.SKO_TAB_HOT)))
+            (oe, ce, pe, he), (ol, cl, pl, hl) = outs
+            assert ce[1, 2] > 0, "every step must miss"
+            assert np.array_equal(ce, cl) and ce[0, 4] == 0 and ce[1, 4] == 32
+            assert np.array_equal(pe[1], pl[1])  # (sequence 0 selects nothing)
+            # same arithmetic on the same rows; only the copy path differs
+            assert np.abs(oe - ol).max() <= 1e-5, f"step {step}: outputs differ"
+            assert np.all(oe[0] == 0.0)
+            assert np.array_equal(he, hl), f"step {step}: hot rows differ"
+    finally:
+        for h in handles:
+            h.close()
+
+
 def test_append_capacity_and_validation_on_device():
     import torch
     import sparse_kv_offload_amd as sko
