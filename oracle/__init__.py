@@ -39,6 +39,11 @@ MUTATIONS = {
     "evict_keeps_old": 9,
     "flag_inverted": 10,
     "score_swap_operand": 11,
+    "c8_hadamard_sign": 12,
+    "c8_truncate": 13,
+    "c8_query_not_rotated": 14,
+    "c8_scale_255": 15,
+    "c8_no_query_scale": 16,
 }
 
 
@@ -82,6 +87,20 @@ def _load():
     lib.oracle_lru_apply.restype = i32
     lib.oracle_attention.argtypes = [vp, i32, vp, i32, f32, vp]
     lib.oracle_attention.restype = None
+    lib.oracle_set_indexer_c8.argtypes = [vp, i32]
+    lib.oracle_set_indexer_c8.restype = i32
+    lib.oracle_read_indexer_c8.argtypes = [vp, i32, i32, vp, vp]
+    lib.oracle_read_indexer_c8.restype = i32
+    lib.oracle_hadamard_rotate.argtypes = [vp, vp]
+    lib.oracle_hadamard_rotate.restype = None
+    lib.oracle_quantize_row.argtypes = [vp, vp, vp]
+    lib.oracle_quantize_row.restype = None
+    lib.oracle_c8_score.argtypes = [vp, ctypes.c_uint16, vp, ctypes.c_uint16]
+    lib.oracle_c8_score.restype = f32
+    lib.oracle_f32_to_f16.argtypes = [f32]
+    lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f32.restype = f32
     _lib = lib
     return lib
 
@@ -127,6 +146,39 @@ def attention(qa: np.ndarray, rows: np.ndarray, scale: float) -> np.ndarray:
     return out
 
 
+def hadamard_rotate(x: np.ndarray) -> np.ndarray:
+    """bf16 [64] -> binary32 [64]: (1/8) H x (int8-indexer rotation)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    assert x.size == IDX_DIM
+    out = np.empty(IDX_DIM, dtype=np.float32)
+    _load().oracle_hadamard_rotate(_p(x), _p(out))
+    return out
+
+
+def quantize_row(xr: np.ndarray):
+    """binary32 [64] -> (int8 codes [64], fp16 scale bits)."""
+    xr = np.ascontiguousarray(xr, dtype=np.float32)
+    assert xr.size == IDX_DIM
+    codes = np.empty(IDX_DIM, dtype=np.int8)
+    sc = np.zeros(1, dtype=np.uint16)
+    _load().oracle_quantize_row(_p(xr), _p(codes), _p(sc))
+    return codes, int(sc[0])
+
+
+def c8_score(q8: np.ndarray, sq: int, k8: np.ndarray, sk: int) -> float:
+    q8 = np.ascontiguousarray(q8, dtype=np.int8)
+    k8 = np.ascontiguousarray(k8, dtype=np.int8)
+    return float(np.float32(_load().oracle_c8_score(_p(q8), int(sq), _p(k8), int(sk))))
+
+
+def f32_to_f16(x: float) -> int:
+    return int(_load().oracle_f32_to_f16(float(np.float32(x))))
+
+
+def f16_to_f32(h: int) -> float:
+    return float(np.float32(_load().oracle_f16_to_f32(int(h))))
+
+
 class LRUState:
     """One (layer, seq) residency table driven by scripted selections."""
 
@@ -158,14 +210,17 @@ class Oracle:
     """Whole-step oracle over [layers][batch] independent chains."""
 
     def __init__(self, layers: int, batch: int, capacity: int, top_k: int, hot_slots: int,
-                 positions: int, heads: int, scale: float):
+                 positions: int, heads: int, scale: float, indexer_c8: bool = False):
         self.L, self.B, self.cap = layers, batch, capacity
         self.k, self.S, self.D, self.H = top_k, hot_slots, positions, heads
         self.scale = float(np.float32(scale))
+        self.c8 = bool(indexer_c8)
         self._h = _load().oracle_create(layers, batch, capacity, top_k, hot_slots,
                                          positions, heads, self.scale)
         if not self._h:
             raise ValueError("oracle_create rejected the configuration")
+        if self.c8 and _load().oracle_set_indexer_c8(self._h, 1) != 0:
+            raise ValueError("oracle_set_indexer_c8 failed")
 
     def close(self):
         if self._h:
@@ -218,6 +273,14 @@ class Oracle:
         if out_pool is not None:
             r["out_pool"] = out_pool
         return r
+
+    def indexer_c8(self, layer: int, seq: int):
+        """(codes int8 [cap][64], scales fp16 bits [cap]) of one chain."""
+        codes = np.empty((self.cap, IDX_DIM), dtype=np.int8)
+        scales = np.empty(self.cap, dtype=np.uint16)
+        if _load().oracle_read_indexer_c8(self._h, layer, seq, _p(codes), _p(scales)) != 0:
+            raise RuntimeError("oracle_read_indexer_c8 failed (not in int8 mode?)")
+        return codes, scales
 
     def state(self, layer: int, seq: int) -> Dict[str, np.ndarray]:
         cs = np.empty(self.cap, dtype=np.int32)

@@ -33,6 +33,23 @@
 //     (latent) columns, softmax(scale * q.K) over the selected rows, in
 //     float64 from the bf16 values.
 //
+// The int8 indexer (LIM C8 in the Chinese revision of the same page,
+// section 4, fused LIM / Copy-SFA sub-section: the indexer applies a
+// Hadamard rotation to query and key, quantizes both to int8, and the
+// selection takes the int8 query with fp16 dequantization scales).  The page
+// fixes no more than that; the oracle takes these readings:
+//   * rotation: x' = (1/8) H x with H the 64 x 64 Sylvester Hadamard matrix,
+//     H[i][j] = (-1)^popcount(i & j); each x'[i] is a binary32 sum over
+//     j = 0..63 in order from +0 of the exact terms +-x_j, then times 1/8;
+//   * quantization of one row: a = max |x'[i]|; a = 0 gives codes 0 and
+//     scale 0; else s = a / 127 (binary32), code[i] = round-half-even of
+//     x'[i] / s (binary32 division) clamped to [-127, 127], and the stored
+//     scale is s rounded to binary16 (nearest-even);
+//   * keys on append (per token row), the query per (seq, position) row;
+//   * score = (float(dot) * s_k) * s_q in binary32, dot = the exact int32
+//     sum of code products; a zero is stored as +0.  Everything after the
+//     score (keys, top-k order, residency, LRU, attention) is unchanged.
+//
 // Parity status: every function below is pinned by tests/test_oracle_pins.py
 // (closed forms, brute force, a hand-simulated LRU trace and invariants);
 // the per-step statistics (hit rate, miss count) have no printed values on
@@ -66,6 +83,11 @@ enum Mutation {
     MUT_EVICT_KEEPS_OLD = 9,
     MUT_FLAG_INVERTED = 10,
     MUT_SCORE_SWAP_OPERAND = 11,
+    MUT_C8_HADAMARD_SIGN = 12,     // (-1)^popcount(i | j) instead of i & j
+    MUT_C8_TRUNCATE = 13,          // codes truncated toward zero
+    MUT_C8_QUERY_NOT_ROTATED = 14, // keys rotated, the query not
+    MUT_C8_SCALE_255 = 15,         // s = a / 255 (codes saturate)
+    MUT_C8_NO_QUERY_SCALE = 16,    // score misses the factor s_q
 };
 
 inline float bf16_to_f32(uint16_t h) {
@@ -87,8 +109,113 @@ inline uint32_t ordered_key(float s) {
     return (u & 0x80000000u) ? ~u : (u ^ 0x80000000u);
 }
 
+// ---- binary16 <-> binary32 (IEEE 754), written from the format definition --
+// binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits.
+inline float f16_to_f32(uint16_t h) {
+    const uint32_t sign = (uint32_t)(h >> 15) << 31;
+    const int e = (h >> 10) & 0x1F;
+    const uint32_t f = h & 0x3FFu;
+    float v;
+    if (e == 0x1F) {
+        uint32_t u = sign | 0x7F800000u | (f << 13);
+        std::memcpy(&v, &u, 4);
+        return v;
+    }
+    // normal: (1 + f / 2^10) 2^(e - 15); subnormal: (f / 2^10) 2^-14 (both exact in binary32)
+    v = (e == 0) ? std::ldexp((float)f, -24) : std::ldexp((float)(f + 1024u), e - 25);
+    return sign ? -v : v;
+}
+
+// Round a binary32 value to the nearest binary16 value, ties to even
+// fraction; beyond the largest finite binary16 (65504) rounding gives inf.
+inline uint16_t f32_to_f16(float x) {
+    uint32_t u = f32_bits(x);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if (std::isnan(x)) return (uint16_t)(sign | 0x7E00u);
+    const double a = std::fabs((double)x);
+    if (std::isinf(x)) return (uint16_t)(sign | 0x7C00u);
+    if (a == 0.0) return sign;
+    // candidates are multiples of the binary16 spacing at a's binade
+    int e2;
+    std::frexp(a, &e2);               // a = m 2^e2, m in [0.5, 1)
+    int ulp_exp = std::max(e2 - 11, -24);  // spacing 2^(e2 - 11) for normals, 2^-24 subnormal
+    const double ulp = std::ldexp(1.0, ulp_exp);
+    const double q = a / ulp;          // exact (power-of-two scaling)
+    double r = std::floor(q);
+    const double frac = q - r;
+    if (frac > 0.5 || (frac == 0.5 && std::fmod(r, 2.0) != 0.0)) r += 1.0;
+    const double v = r * ulp;          // the rounded magnitude
+    if (v > 65504.0) return (uint16_t)(sign | 0x7C00u);
+    // encode v
+    if (v < std::ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)(v / std::ldexp(1.0, -24)));
+    int ev;
+    const double m = std::frexp(v, &ev);  // v = m 2^ev, m in [0.5, 1)
+    const int E = ev - 1 + 15;
+    const uint32_t frac10 = (uint32_t)((m * 2.0 - 1.0) * 1024.0);
+    return (uint16_t)(sign | (uint16_t)(E << 10) | (uint16_t)frac10);
+}
+
+// ---- the int8 indexer (readings in the header) -----------------------------
+inline int hadamard_sign(int i, int j) {
+    const int m = (g_mutation == MUT_C8_HADAMARD_SIGN) ? (i | j) : (i & j);
+    return (__builtin_popcount((unsigned)m) & 1) ? -1 : 1;
+}
+
+// x' = (1/8) H x, each x'[i] a binary32 sum over j in index order from +0.
+void hadamard_rotate(const uint16_t* x, float* out) {
+    for (int i = 0; i < IDX_DIM; ++i) {
+        float acc = 0.0f;
+        for (int j = 0; j < IDX_DIM; ++j) {
+            const float term = bf16_to_f32(x[j]);
+            acc = hadamard_sign(i, j) > 0 ? acc + term : acc - term;
+        }
+        out[i] = acc * 0.125f;
+    }
+}
+
+// Symmetric per-row int8 quantization with an fp16 dequantization scale.
+void quantize_row(const float* xr, int8_t* codes, uint16_t* scale16) {
+    float a = 0.0f;
+    for (int i = 0; i < IDX_DIM; ++i) a = std::max(a, std::fabs(xr[i]));
+    if (a == 0.0f) {
+        for (int i = 0; i < IDX_DIM; ++i) codes[i] = 0;
+        *scale16 = 0;
+        return;
+    }
+    const float s = a / ((g_mutation == MUT_C8_SCALE_255) ? 255.0f : 127.0f);
+    for (int i = 0; i < IDX_DIM; ++i) {
+        const float q = xr[i] / s;
+        float r = (g_mutation == MUT_C8_TRUNCATE) ? std::trunc(q) : std::nearbyint(q);
+        r = std::min(127.0f, std::max(-127.0f, r));
+        codes[i] = (int8_t)r;
+    }
+    *scale16 = f32_to_f16(s);
+}
+
+// Rotation then quantization of one bf16 row (a key on append, a query).
+void quantize_index_row(const uint16_t* x, int8_t* codes, uint16_t* scale16, bool rotate) {
+    float xr[IDX_DIM];
+    if (rotate) {
+        hadamard_rotate(x, xr);
+    } else {
+        for (int i = 0; i < IDX_DIM; ++i) xr[i] = bf16_to_f32(x[i]);
+    }
+    quantize_row(xr, codes, scale16);
+}
+
+float c8_score(const int8_t* q8, uint16_t sq, const int8_t* k8, uint16_t sk) {
+    int32_t dot = 0;
+    for (int j = 0; j < IDX_DIM; ++j) dot += (int32_t)q8[j] * (int32_t)k8[j];
+    float r = (float)dot * f16_to_f32(sk);
+    if (g_mutation != MUT_C8_NO_QUERY_SCALE) r = r * f16_to_f32(sq);
+    if (r == 0.0f) r = 0.0f;  // store a zero as +0
+    return r;
+}
+
 struct Chain {
     int64_t ntok = 0;
+    std::vector<int8_t> kidx8;       // [cap][64]  int8 indexer cache (C8 mode)
+    std::vector<uint16_t> kscale;    // [cap]      its fp16 scales
     std::vector<uint16_t> kidx;      // [cap][64]  device indexer cache contents
     std::vector<uint16_t> pool;      // [cap][576] host main-KV pool
     std::vector<int32_t> cache_slots;  // [cap] token -> hot slot, -1 when absent
@@ -99,6 +226,7 @@ struct Chain {
 
 struct Oracle {
     int L, B, k, S, D, H;
+    bool c8 = false;
     int64_t cap;
     float scale;
     std::vector<Chain> chains;       // [L][B]
@@ -194,6 +322,15 @@ void* oracle_create(int L, int B, int64_t cap, int k, int S, int D, int H, float
 
 void oracle_destroy(void* h) { delete static_cast<Oracle*>(h); }
 
+// Switch a fresh oracle (nothing appended yet) to the int8 indexer.
+int oracle_set_indexer_c8(void* h, int on) {
+    Oracle* o = static_cast<Oracle*>(h);
+    for (const Chain& c : o->chains)
+        if (c.ntok != 0) return -1;
+    o->c8 = on != 0;
+    return 0;
+}
+
 // Steps 1-2: the new token's rows go to their logical slots: the main-KV row
 // to the host pool, the indexer row to the indexer cache.
 int oracle_append(void* h, int layer, int seq, const uint16_t* idx_rows, const uint16_t* kv_rows, int64_t n) {
@@ -202,6 +339,15 @@ int oracle_append(void* h, int layer, int seq, const uint16_t* idx_rows, const u
     Chain& c = o->at(layer, seq);
     if (c.ntok + n > o->cap) return -4;
     std::memcpy(&c.kidx[(size_t)c.ntok * IDX_DIM], idx_rows, (size_t)n * IDX_DIM * 2);
+    if (o->c8) {
+        if (c.kidx8.empty()) {
+            c.kidx8.assign((size_t)o->cap * IDX_DIM, 0);
+            c.kscale.assign((size_t)o->cap, 0);
+        }
+        for (int64_t r = 0; r < n; ++r)
+            quantize_index_row(idx_rows + (size_t)r * IDX_DIM, &c.kidx8[(size_t)(c.ntok + r) * IDX_DIM],
+                               &c.kscale[(size_t)(c.ntok + r)], true);
+    }
     std::memcpy(&c.pool[(size_t)c.ntok * KV_DIM], kv_rows, (size_t)n * KV_DIM * 2);
     c.ntok += n;
     return 0;
@@ -230,7 +376,15 @@ int oracle_decode_step(void* h, int layer, const uint16_t* q_idx, const uint16_t
         for (int p = 0; p < D; ++p) {
             const uint16_t* q = q_idx + ((size_t)b * D + p) * IDX_DIM;
             std::vector<float> s((size_t)Lt);
-            for (int64_t i = 0; i < Lt; ++i) s[i] = indexer_score(q, &c.kidx[(size_t)i * IDX_DIM]);
+            if (o->c8) {
+                int8_t q8[IDX_DIM];
+                uint16_t sq;
+                quantize_index_row(q, q8, &sq, g_mutation != MUT_C8_QUERY_NOT_ROTATED);
+                for (int64_t i = 0; i < Lt; ++i)
+                    s[i] = c8_score(q8, sq, &c.kidx8[(size_t)i * IDX_DIM], c.kscale[(size_t)i]);
+            } else {
+                for (int64_t i = 0; i < Lt; ++i) s[i] = indexer_score(q, &c.kidx[(size_t)i * IDX_DIM]);
+            }
             if (keys)
                 for (int64_t i = 0; i < Lt; ++i) keys[((size_t)b * D + p) * o->cap + i] = ordered_key(s[i]);
             std::vector<int32_t> sel = topk_indices(s, k);
@@ -334,6 +488,33 @@ int oracle_read_state(void* h, int layer, int seq, int32_t* cache_slots, int32_t
     if (ntok) *ntok = c.ntok;
     return 0;
 }
+
+// The int8 indexer rows of one (layer, seq) chain: codes [cap][64], scales [cap].
+int oracle_read_indexer_c8(void* h, int layer, int seq, int8_t* codes, uint16_t* scales) {
+    Oracle* o = static_cast<Oracle*>(h);
+    if (layer < 0 || layer >= o->L || seq < 0 || seq >= o->B || !o->c8) return -1;
+    Chain& c = o->at(layer, seq);
+    if (c.kidx8.empty()) {
+        std::memset(codes, 0, (size_t)o->cap * IDX_DIM);
+        std::memset(scales, 0, (size_t)o->cap * 2);
+        return 0;
+    }
+    std::memcpy(codes, c.kidx8.data(), c.kidx8.size());
+    std::memcpy(scales, c.kscale.data(), c.kscale.size() * 2);
+    return 0;
+}
+
+void oracle_hadamard_rotate(const uint16_t* x, float* out) { hadamard_rotate(x, out); }
+
+void oracle_quantize_row(const float* xr, int8_t* codes, uint16_t* scale16) { quantize_row(xr, codes, scale16); }
+
+float oracle_c8_score(const int8_t* q8, uint16_t sq, const int8_t* k8, uint16_t sk) {
+    return c8_score(q8, sq, k8, sk);
+}
+
+uint16_t oracle_f32_to_f16(float x) { return f32_to_f16(x); }
+
+float oracle_f16_to_f32(uint16_t h) { return f16_to_f32(h); }
 
 // Direct access to one function at a time, for the pin tests.
 float oracle_score_one(const uint16_t* q, const uint16_t* krow) { return indexer_score(q, krow); }

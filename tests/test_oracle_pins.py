@@ -315,10 +315,162 @@ def pin_dedupe():
         assert np.array_equal(a["misses"][0, :a["counts"][0, 2]], b["misses"][0, :b["counts"][0, 2]])
 
 
+# ------------------------------------------------- int8 indexer (LIM C8)
+
+def sylvester(n):
+    """Sylvester's construction: H_1 = [1], H_2m = [[H, H], [H, -H]]."""
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def pin_f16_conversion():
+    """binary32 -> binary16 round-to-nearest-even and back, against numpy's
+    IEEE half conversion, over random magnitudes and the edge cases
+    (largest finite, overflow to inf, subnormals, ties)."""
+    rng = np.random.default_rng(21)
+    xs = np.concatenate([
+        rng.standard_normal(3000) * 10.0 ** rng.integers(-9, 6, 3000),
+        np.array([0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 7e4, 2.0 ** -24, 2.0 ** -25,
+                  3 * 2.0 ** -26, 5 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 1.0 + 2.0 ** -11,
+                  1.0 + 3 * 2.0 ** -11, 2048.0 + 1.0, 2048.0 + 3.0])])
+    for x in xs.astype(np.float32):
+        with np.errstate(over="ignore"):  # overflow to inf is one of the cases
+            want = int(np.array([x], dtype=np.float32).astype(np.float16).view(np.uint16)[0])
+        assert oracle.f32_to_f16(float(x)) == want, (float(x), hex(want))
+    for h in range(0, 0x10000, 7):
+        v = np.array([h], dtype=np.uint16).view(np.float16).astype(np.float32)[0]
+        if np.isnan(v):
+            continue
+        assert oracle.f16_to_f32(h) == v, hex(h)
+
+
+def pin_hadamard_closed_form():
+    """Unit vectors give the columns of H/8 (H from Sylvester's recursion),
+    and the rotation is an involution on exactly representable rows
+    ((H/8)^2 = I)."""
+    H = sylvester(64)
+    for j in (0, 1, 5, 33, 63):
+        e = np.zeros(64, dtype=np.uint16)
+        e[j] = bf([1.0])[0]
+        assert np.array_equal(oracle.hadamard_rotate(e).astype(np.float64), H[:, j] / 8.0), j
+    rng = np.random.default_rng(22)
+    for _ in range(20):
+        x = rng.integers(-4, 5, 64).astype(np.float64)
+        y = oracle.hadamard_rotate(bf(x)).astype(np.float64)
+        assert np.array_equal(y, H @ x / 8.0)
+        assert np.array_equal(oracle.hadamard_rotate(bf(y)).astype(np.float64), x)
+
+
+def pin_hadamard_error_bound():
+    """Random rows: within the recursive-summation bound of (H/8) x in fp64
+    (64 exact terms), and the norm is kept (orthonormal rotation)."""
+    H = sylvester(64)
+    rng = np.random.default_rng(23)
+    g = 63 * U32 / (1 - 63 * U32)
+    for _ in range(200):
+        x = rand_bf16(rng, 64)
+        y = oracle.hadamard_rotate(x).astype(np.float64)
+        exact = H @ f(x) / 8.0
+        assert np.all(np.abs(y - exact) <= g * np.sum(np.abs(f(x))) / 8.0 + 1e-300)
+        assert abs(np.linalg.norm(y) - np.linalg.norm(f(x))) <= 1e-5 * np.linalg.norm(f(x)) + 1e-30
+
+
+def pin_quantize_row():
+    """Codes are round-to-nearest-even of x / s with s = max|x| / 127: the
+    largest entry maps to +-127, every code is within half a step, ties go to
+    the even code, the stored scale is s in binary16, a zero row gives zeros."""
+    rng = np.random.default_rng(24)
+    for _ in range(300):
+        x = (rng.standard_normal(64) * 10.0 ** rng.uniform(-3, 2)).astype(np.float32)
+        codes, sc = oracle.quantize_row(x)
+        a = np.float32(np.max(np.abs(x)))
+        s = np.float32(a / np.float32(127.0))
+        assert np.all(np.abs(codes.astype(np.int32)) <= 127)
+        assert abs(int(codes[np.argmax(np.abs(x))])) == 127
+        err = np.abs(x.astype(np.float64) / float(s) - codes.astype(np.float64))
+        assert np.all(err <= 0.5 + 1e-6), err.max()
+        assert sc == int(np.array([s], np.float32).astype(np.float16).view(np.uint16)[0])
+    codes, sc = oracle.quantize_row(np.zeros(64, np.float32))
+    assert np.all(codes == 0) and sc == 0
+    # exact ties: a = 127 gives s = 1
+    x = np.zeros(64, np.float32)
+    x[:6] = [127.0, 2.5, 3.5, -2.5, -3.5, 0.5]
+    codes, sc = oracle.quantize_row(x)
+    assert codes[:6].tolist() == [127, 2, 4, -2, -4, 0] and sc == 0x3C00
+
+
+def c8_pipeline(q, k):
+    q8, sq = oracle.quantize_row(oracle.hadamard_rotate(q))
+    k8, sk = oracle.quantize_row(oracle.hadamard_rotate(k))
+    return q8, sq, k8, sk
+
+
+def pin_c8_score_bound():
+    """The int8 score approximates q . k (the rotation is orthonormal), with
+    error at most the dequantization error of both rows: per element at most
+    s / 2 plus 127 |s - fp16(s)|, summed against the other row's entries."""
+    rng = np.random.default_rng(25)
+    H = sylvester(64)
+    for _ in range(300):
+        q, k = rand_bf16(rng, 64), rand_bf16(rng, 64)
+        q8, sq, k8, sk = c8_pipeline(q, k)
+        score = oracle.c8_score(q8, sq, k8, sk)
+        exact = float(np.dot(f(q), f(k)))
+        qr, kr = H @ f(q) / 8.0, H @ f(k) / 8.0
+        sq32 = float(np.max(np.abs(qr))) / 127.0
+        sk32 = float(np.max(np.abs(kr))) / 127.0
+        eq = sq32 / 2 + 127 * sq32 * 2.0 ** -11 + 1e-6 * sq32
+        ek = sk32 / 2 + 127 * sk32 * 2.0 ** -11 + 1e-6 * sk32
+        bound = np.sum(np.abs(qr) * ek + np.abs(kr) * eq + eq * ek)
+        assert abs(score - exact) <= bound + 1e-6 * abs(exact), (score, exact, bound)
+    # the integer dot is exact: a zero key scores +0, a scaled copy scales
+    z = np.zeros(64, np.int8)
+    s0 = oracle.c8_score(np.full(64, 3, np.int8), 0x3C00, z, 0x3C00)
+    assert s0 == 0.0 and not np.signbit(np.float32(s0))
+    assert oracle.c8_score(np.full(64, 127, np.int8), 0x3C00, np.full(64, -127, np.int8), 0x3800) == \
+        np.float32(-64 * 127 * 127 * 0.5)
+
+
+def pin_c8_decode_consistent():
+    """The oracle's int8 decode stores the rotated, quantized rows on append,
+    quantizes the rotated query, and ranks by the int8 score of the pinned
+    functions (keys compared for every token, winners by brute force)."""
+    w = small_workload(D=2, B=2, steps=3)
+    o = oracle.Oracle(w.layers, w.batch, w.capacity, w.top_k, w.hot_slots, w.positions, w.heads,
+                      1.0 / 24.0, indexer_c8=True)
+    for b in range(w.batch):
+        o.append(0, b, w.index_rows(0, b, 0, w.context), w.kv_rows(0, b, 0, w.context))
+    for t in range(3):
+        for b in range(w.batch):
+            o.append(0, b, w.index_rows(0, b, w.context + t, 1), w.kv_rows(0, b, w.context + t, 1))
+        qi = np.stack([w.index_queries(0, b)[t] for b in range(w.batch)])
+        qa = np.stack([w.attn_queries(0, b, t) for b in range(w.batch)])
+        r = o.decode_step(0, qi, qa, want_keys=True, want_out=False)
+        for b in range(w.batch):
+            codes, scales = o.indexer_c8(0, b)
+            n = w.context + t + 1
+            rows = w.index_rows(0, b, 0, n)
+            for i in range(0, n, 37):
+                c_i, s_i = oracle.quantize_row(oracle.hadamard_rotate(rows[i]))
+                assert np.array_equal(codes[i], c_i) and scales[i] == s_i
+            for p in range(w.positions):
+                q8, sq = oracle.quantize_row(oracle.hadamard_rotate(qi[b, p]))
+                sc = np.array([oracle.c8_score(q8, sq, codes[i], scales[i]) for i in range(n)], np.float32)
+                keys = np.array([oracle.ordered_key(v) for v in sc], np.uint32)
+                assert np.array_equal(r["keys"][b, p, :n], keys)
+                order = sorted(range(n), key=lambda i: (-int(keys[i]), i))[:min(w.top_k, n)]
+                assert (r["topk"][b, p, :len(order)] & 0x7FFFFFFF).tolist() == order
+    o.close()
+
+
 PINS = [pin_score_error_bound, pin_score_special_cases, pin_score_order, pin_ordered_key_monotone,
         pin_topk_bruteforce, pin_topk_all_equal, pin_lru_golden_trace,
         pin_lru_matches_list_formulation, pin_attention_single_row, pin_attention_uniform_mean,
-        pin_attention_textbook, pin_attention_peaked, pin_step_invariants, pin_dedupe]
+        pin_attention_textbook, pin_attention_peaked, pin_step_invariants, pin_dedupe,
+        pin_f16_conversion, pin_hadamard_closed_form, pin_hadamard_error_bound, pin_quantize_row,
+        pin_c8_score_bound, pin_c8_decode_consistent]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
