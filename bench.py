@@ -33,6 +33,7 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor figure
 HOST_LINK_PEAK_GBPS = 64.0    # MI355X host interface, PCIe 5.0 x16: 128 GB/s both ways
 CALIB_COPY_BYTES = 256 << 20  # plain device copy run once for counter calibration
 IDX_ROW, KV_ROW = 128, 1152
+IDX_ROW_C8 = 64 + 2  # int8 codes + fp16 scale per token
 
 
 def log(msg: str) -> None:
@@ -132,6 +133,8 @@ def main() -> int:
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="time without per-stage events")
+    ap.add_argument("--indexer", choices=["bf16", "c8"], default="bf16",
+                    help="indexer cache: bf16 rows, or int8 codes with fp16 scales after a Hadamard rotation")
     ap.add_argument("--pool", choices=["default", "coherent", "noncoherent"], default="default",
                     help="host-pool allocation mode")
     ap.add_argument("--copy", choices=["default", "early", "late", "fused"], default="default",
@@ -163,6 +166,8 @@ def main() -> int:
              "noncoherent": sko.SKO_FLAG_POOL_NONCOHERENT}[args.pool]
     flags |= {"default": 0, "early": sko.SKO_FLAG_EARLY_COPY, "late": sko.SKO_FLAG_LATE_COPY,
               "fused": sko.SKO_FLAG_FUSED_COPY}[args.copy]
+    if args.indexer == "c8":
+        flags |= sko.SKO_FLAG_INDEXER_C8
     cfg = sko.make_config(num_layers=L, batch=B, max_tokens=w.capacity, num_heads=H, top_k=k,
                           hot_slots=w.hot_slots, mtp_positions=D, flags=flags)
     h = sko.SparseKVOffload(cfg, stream)
@@ -249,7 +254,9 @@ def main() -> int:
         ls = L * nsteps
         per = h2d_bytes / ls if ls else 0.0
         copy = (per, "host-link", HOST_LINK_PEAK_GBPS)
-        m = {"score_hist": (IDX_ROW * B * avg_lt + IDX_ROW * B * D, "hbm", HBM_PEAK_GBPS)}
+        # the query rows are read as bf16 in both modes
+        idx_row = IDX_ROW_C8 if args.indexer == "c8" else IDX_ROW
+        m = {"score_hist": (idx_row * B * avg_lt + IDX_ROW * B * D, "hbm", HBM_PEAK_GBPS)}
         if mode == "fused":
             m["attn_partial"] = copy
             return m
@@ -273,7 +280,7 @@ def main() -> int:
         avg = ms / n
         ach = nbytes / (avg * 1e-3) / 1e9 if avg > 0 else 0.0
         e = {"bound": bound, "achieved": round(ach, 2), "peak": round(peak, 2), "unit": "GB/s",
-             "frac": round(ach / peak, 4), "traffic": traffic_for(name, w.name), "kernel": name,
+             "frac": round(ach / peak, 4), "traffic": traffic_for(name, w.name + ("_c8" if args.indexer == "c8" else "")), "kernel": name,
              "avg_ms": round(avg, 5), "launches": n, "bytes_per_launch": int(nbytes)}
         if bound == "host-link":
             e["measured_ceiling"] = round(h2d_ceiling, 2)
@@ -312,7 +319,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "layers": L, "batch": B, "context": w.context,
                    "top_k": k, "hot_slots": w.hot_slots, "mtp_positions": D, "heads": H,
-                   "parallelism": "none (1 GPU)", "pool": args.pool, "copy": args.copy},
+                   "parallelism": "none (1 GPU)", "pool": args.pool, "copy": args.copy,
+                   "indexer": args.indexer},
         "tokens_per_s": round(B * K / elapsed, 2),
         "indexer_scan_GBps": rooflines.get("score_hist", {}).get("achieved"),
         "miss_gather_GBps": next((e["achieved"] for e in [roof or {}] + list(rooflines.values())

@@ -81,6 +81,18 @@ extern "C" {
 #define SKO_FLAG_FUSED_COPY 0x10u
 #define SKO_FLAG_LATE_COPY 0x20u
 #define SKO_FLAG_EARLY_COPY 0x40u
+/* The int8 indexer (LIM C8 of [LSO-zh] §4: the indexer rotates query and
+ * key by a Hadamard transform and quantizes both to int8, and the selection
+ * takes the int8 query with fp16 dequantization scales).  Appended bf16
+ * indexer rows are rotated, x' = (1/8) H x with H the 64 x 64 Sylvester
+ * Hadamard matrix, each x'[i] a binary32 sum in index order from +0, and
+ * quantized per row: s = max|x'| / 127, code = round-half-even(x' / s)
+ * clamped to [-127, 127], scale stored as binary16 (a zero row: codes and
+ * scale 0).  The query of each (seq, position) is treated the same way at
+ * decode.  Score = (float(dot) * s_k) * s_q in binary32 with dot the exact
+ * int32 sum of code products; the selection, residency, LRU and attention
+ * are unchanged.  Halves the indexer bytes the score pass reads. */
+#define SKO_FLAG_INDEXER_C8 0x80u
 
 typedef struct sko_handle sko_handle;
 
@@ -211,9 +223,10 @@ enum sko_table {
     SKO_TAB_SLOT_TOKEN = 2,  /* int32 [S] */
     SKO_TAB_LAST_USE = 3,    /* int32 [S] */
     SKO_TAB_HOT = 4,         /* bf16 [S][576] */
-    SKO_TAB_INDEXER = 5,     /* bf16 [cap][64] */
+    SKO_TAB_INDEXER = 5,     /* bf16 [cap][64]; with SKO_FLAG_INDEXER_C8 int8 codes [cap][64] */
     SKO_TAB_POOL = 6,        /* bf16 [cap][576] (host pool) */
-    SKO_TAB_NTOK = 7         /* int64 [1] tokens present */
+    SKO_TAB_NTOK = 7,        /* int64 [1] tokens present */
+    SKO_TAB_INDEXER_SCALE = 8 /* fp16 [cap] scales; only with SKO_FLAG_INDEXER_C8, else SKO_E_STATE */
 };
 
 /*

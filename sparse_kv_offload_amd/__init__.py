@@ -38,11 +38,13 @@ SKO_FLAG_SELECT_RESCAN = 0x8
 SKO_FLAG_FUSED_COPY = 0x10
 SKO_FLAG_LATE_COPY = 0x20
 SKO_FLAG_EARLY_COPY = 0x40
+SKO_FLAG_INDEXER_C8 = 0x80
 
 SKO_BUF_TOPK, SKO_BUF_PHYS, SKO_BUF_COUNTS = 1, 2, 3
 SKO_BUF_MISSES, SKO_BUF_VICTIMS, SKO_BUF_EVICT_OLD, SKO_BUF_KEYS = 4, 5, 6, 7
 SKO_TAB_CACHE_SLOTS, SKO_TAB_SLOT_TOKEN, SKO_TAB_LAST_USE = 1, 2, 3
 SKO_TAB_HOT, SKO_TAB_INDEXER, SKO_TAB_POOL, SKO_TAB_NTOK = 4, 5, 6, 7
+SKO_TAB_INDEXER_SCALE = 8
 
 EXPORTED = (
     "sko_create", "sko_set_stream", "sko_append_token", "sko_decode_step", "sko_read_step",
@@ -297,9 +299,11 @@ class SparseKVOffload:
             SKO_TAB_SLOT_TOKEN: ((c.hot_slots,), np.int32),
             SKO_TAB_LAST_USE: ((c.hot_slots,), np.int32),
             SKO_TAB_HOT: ((c.hot_slots, SKO_KV_DIM), np.uint16),
-            SKO_TAB_INDEXER: ((c.max_tokens, SKO_INDEX_DIM), np.uint16),
+            SKO_TAB_INDEXER: ((c.max_tokens, SKO_INDEX_DIM),
+                              np.int8 if c.flags & SKO_FLAG_INDEXER_C8 else np.uint16),
             SKO_TAB_POOL: ((c.max_tokens, SKO_KV_DIM), np.uint16),
             SKO_TAB_NTOK: ((1,), np.int64),
+            SKO_TAB_INDEXER_SCALE: ((c.max_tokens,), np.uint16),
         }
         shape, dt = shapes[which]
         return sko_read_table(self.handle, layer, seq, which, np.zeros(shape, dtype=dt))

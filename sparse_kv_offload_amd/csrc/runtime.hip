@@ -80,7 +80,10 @@ struct sko_handle {
     // offload state
     uint16_t* pool_host = nullptr;  // pinned [L][B][cap][576]
     uint16_t* pool_dev = nullptr;   // device mapping of pool_host
-    uint16_t* idx = nullptr;        // [L][B][ntiles][8][64] x 16 B (tiled)
+    uint16_t* idx = nullptr;        // [L][B][ntiles][8][64] x 16 B (tiled); int8 indexer: [L][B][ntiles][4][64] x 16 B
+    uint16_t* idx_scale = nullptr;  // int8 indexer: fp16 scales [L][B][ntiles * 64]
+    uint32_t* qc8 = nullptr;        // int8 indexer: quantized queries [B][D][kQc8Words]
+    bool c8 = false;                // the int8 indexer (SKO_FLAG_INDEXER_C8)
     uint16_t* staging = nullptr;    // device rows for host-source appends
     uint16_t* hot = nullptr;        // [L][B][S][576]
     int32_t* cache_slots = nullptr; // [L][B][cap]
@@ -138,6 +141,8 @@ struct sko_handle {
     std::vector<void*> dev_allocs;
 
     size_t lb(int layer, int b) const { return (size_t)layer * B + b; }
+    // indexer cache bytes of one (layer, seq): 128 B (bf16) or 64 B (int8) per token slot
+    size_t idx_seq_bytes() const { return (size_t)ntiles * kIdxTile * (c8 ? kIdxDim : kIdxDim * 2); }
 };
 
 namespace {
@@ -231,7 +236,7 @@ int validate_config(const sko_config* c) {
         return set_err(SKO_E_INVAL, "attn_scale must be finite and > 0");
     if ((c->flags & ~(SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT | SKO_FLAG_KEEP_KEYS |
                       SKO_FLAG_SELECT_RESCAN | SKO_FLAG_FUSED_COPY | SKO_FLAG_LATE_COPY |
-                      SKO_FLAG_EARLY_COPY)) != 0 ||
+                      SKO_FLAG_EARLY_COPY | SKO_FLAG_INDEXER_C8)) != 0 ||
         (c->flags & (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT)) ==
             (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT))
         return set_err(SKO_E_INVAL, "unknown or conflicting flags 0x%x", c->flags);
@@ -320,6 +325,7 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     // against the late copy: long +20 %, mtp3 +2 %).
     h->fused_copy = (cfg->flags & SKO_FLAG_FUSED_COPY) != 0;
     h->staged_copy = !h->fused_copy && !(cfg->flags & SKO_FLAG_LATE_COPY);
+    h->c8 = (cfg->flags & SKO_FLAG_INDEXER_C8) != 0;
 
     const size_t LB = (size_t)h->L * h->B;
     const size_t BD = (size_t)h->B * h->D;
@@ -341,7 +347,11 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
         return set_err(SKO_E_DEVICE, "hipHostGetDevicePointer on the host pool failed");
     }
     bool ok = true;
-    ok = ok && dev_alloc(h, (void**)&h->idx, LB * h->ntiles * kIdxTile * kIdxDim * 2);
+    ok = ok && dev_alloc(h, (void**)&h->idx, LB * h->idx_seq_bytes());
+    if (h->c8) {
+        ok = ok && dev_alloc(h, (void**)&h->idx_scale, LB * h->ntiles * kIdxTile * 2);
+        ok = ok && dev_alloc(h, (void**)&h->qc8, (size_t)h->B * h->D * kQc8Words * 4);
+    }
     ok = ok && dev_alloc(h, (void**)&h->staging, (size_t)kStagingRows * kIdxDim * 2);
     // the staging rows of the early copy follow the hot rows of every layer
     // in one allocation (the attention addresses both from one base)
@@ -406,7 +416,9 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
         e = hipMemcpyAsync(h->floor, fl.data(), fl.size() * 4, hipMemcpyHostToDevice, h->stream);
         if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
     }
-    if (e == hipSuccess) e = hipMemsetAsync(h->idx, 0, LB * h->ntiles * kIdxTile * kIdxDim * 2, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->idx, 0, LB * h->idx_seq_bytes(), h->stream);
+    if (e == hipSuccess && h->c8) e = hipMemsetAsync(h->idx_scale, 0, LB * h->ntiles * kIdxTile * 2, h->stream);
+    if (e == hipSuccess && h->c8) e = hipMemsetAsync(h->qc8, 0, (size_t)h->B * h->D * kQc8Words * 4, h->stream);
     if (e == hipSuccess) e = launch_init_rings(h->stream, h->ring[0], h->ring_pos, h->ring_state, (int64_t)LB, h->S, h->C);
     if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
     if (e != hipSuccess) {
@@ -446,9 +458,18 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
     DeviceGuard guard(h->cfg.device);
     if (!guard.ok) return device_fail(h, hipErrorInvalidDevice, "hipSetDevice");
 
-    uint16_t* idx_layer = h->idx + (size_t)layer * h->B * h->ntiles * kIdxTile * kIdxDim;
+    uint8_t* idx_layer = reinterpret_cast<uint8_t*>(h->idx) + (size_t)layer * h->B * h->idx_seq_bytes();
+    uint16_t* scale_layer = h->c8 ? h->idx_scale + (size_t)layer * h->B * h->ntiles * kIdxTile : nullptr;
     uint16_t* pool_layer_dev = h->pool_dev + (size_t)layer * h->B * h->cap * kKvDim;
     int32_t* ntok_layer = h->ntok_dev + (size_t)layer * h->B;
+    // bf16 indexer rows are stored as they are, or rotated and quantized
+    auto append_rows = [&](const uint16_t* is, const uint16_t* ks, uint16_t* pool, int b0, int nb, int64_t m,
+                           int64_t base) {
+        return h->c8 ? launch_append_rows_c8(h->stream, is, ks, idx_layer, scale_layer, pool, ntok_layer, b0, nb, m,
+                                             h->cap, h->ntiles, (int32_t)base)
+                     : launch_append_rows(h->stream, is, ks, reinterpret_cast<uint16_t*>(idx_layer), pool,
+                                          ntok_layer, b0, nb, m, h->cap, h->ntiles, (int32_t)base);
+    };
     const uint16_t* isrc = static_cast<const uint16_t*>(idx_rows);
     const uint16_t* ksrc = static_cast<const uint16_t*>(kv_rows);
 
@@ -460,9 +481,8 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
             int e = s + 1;
             while (e < nseq && h->ntok[h->lb(layer, seq0 + e)] == base) ++e;
             rc = run_stage(h, ST_APPEND, [&] {
-                return launch_append_rows(h->stream, isrc + (size_t)s * n * kIdxDim, ksrc + (size_t)s * n * kKvDim,
-                                          idx_layer, pool_layer_dev, ntok_layer, seq0 + s, e - s, n, h->cap,
-                                          h->ntiles, (int32_t)base);
+                return append_rows(isrc + (size_t)s * n * kIdxDim, ksrc + (size_t)s * n * kKvDim, pool_layer_dev,
+                                   seq0 + s, e - s, n, base);
             });
             if (rc != SKO_OK) return rc;
             s = e;
@@ -479,8 +499,7 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
                 hipError_t e = hipMemcpyAsync(h->staging, isrc + ((size_t)s * n + r0) * kIdxDim,
                                               (size_t)m * kIdxDim * 2, hipMemcpyHostToDevice, h->stream);
                 if (e != hipSuccess) return device_fail(h, e, "indexer rows host->device");
-                e = launch_append_rows(h->stream, h->staging, nullptr, idx_layer, nullptr, ntok_layer, b, 1, m,
-                                       h->cap, h->ntiles, (int32_t)(base + r0));
+                e = append_rows(h->staging, nullptr, nullptr, b, 1, m, base + r0);
                 if (e != hipSuccess) return device_fail(h, e, "indexer rows to tiles");
             }
         }
@@ -507,7 +526,8 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
     const int32_t t = h->step[layer];
     const size_t LBc = (size_t)layer * B * cap;
     const size_t LBs = (size_t)layer * B * S;
-    const uint16_t* idx_layer = h->idx + (size_t)layer * B * h->ntiles * kIdxTile * kIdxDim;
+    const void* idx_layer = reinterpret_cast<const uint8_t*>(h->idx) + (size_t)layer * B * h->idx_seq_bytes();
+    const uint16_t* scale_layer = h->c8 ? h->idx_scale + (size_t)layer * B * h->ntiles * kIdxTile : nullptr;
     const uint16_t* pool_layer = h->pool_dev + LBc * kKvDim;
     uint16_t* hot_layer = h->hot + LBs * kKvDim;
     int32_t* cs = h->cache_slots + LBc;
@@ -525,7 +545,8 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
 
     if ((rc = run_stage(h, ST_SCORE, [&] {
              return launch_score_hist(h->stream, idx_layer, qi, ntok, h->keys, h->hist, floor_layer, h->pre,
-                                      h->meta, cs, B, D, h->kcap, cap, h->ntiles, max_now, h->cu_count);
+                                      h->meta, cs, B, D, h->kcap, cap, h->ntiles, max_now, h->cu_count, scale_layer,
+                                      h->qc8);
          })))
         return rc;
     const bool fused_copy = h->fused_copy;
@@ -534,7 +555,7 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
              return launch_topk_filter(h->stream, h->hist, h->meta, h->pre, h->cand, h->topk, cs, ntok, h->winners,
                                        staged ? h->miss_bits : nullptr, idx_layer, qi, floor_layer,
                                        (h->cfg.flags & SKO_FLAG_SELECT_RESCAN) != 0, B, D, cap, h->ntiles, k,
-                                       max_now);
+                                       max_now, scale_layer, h->c8 ? h->qc8 : nullptr);
          })))
         return rc;
     if (staged && (rc = run_stage(h, ST_REFINE, [&] {
@@ -621,7 +642,15 @@ int sko_read_table(sko_handle* h, int32_t layer, int32_t seq, int32_t which, voi
         case SKO_TAB_SLOT_TOKEN: src = h->slot_token + lb * h->S; size = (size_t)h->S * 4; break;
         case SKO_TAB_LAST_USE: src = h->last_use + lb * h->S; size = (size_t)h->S * 4; break;
         case SKO_TAB_HOT: src = h->hot + lb * h->S * kKvDim; size = (size_t)h->S * kKvRowBytes; break;
-        case SKO_TAB_INDEXER: src = h->idx + lb * h->ntiles * kIdxTile * kIdxDim; size = (size_t)h->cap * kIdxDim * 2; break;
+        case SKO_TAB_INDEXER:
+            src = reinterpret_cast<const uint8_t*>(h->idx) + lb * h->idx_seq_bytes();
+            size = (size_t)h->cap * (h->c8 ? kIdxDim : kIdxDim * 2);
+            break;
+        case SKO_TAB_INDEXER_SCALE:
+            if (!h->c8) return set_err(SKO_E_STATE, "SKO_TAB_INDEXER_SCALE needs SKO_FLAG_INDEXER_C8");
+            src = h->idx_scale + lb * h->ntiles * kIdxTile;
+            size = (size_t)h->cap * 2;
+            break;
         case SKO_TAB_POOL: src = h->pool_host + lb * h->cap * kKvDim; size = (size_t)h->cap * kKvRowBytes; host = true; break;
         case SKO_TAB_NTOK: size = 8; break;
         default: return set_err(SKO_E_INVAL, "unknown table %d", which);
@@ -635,12 +664,14 @@ int sko_read_table(sko_handle* h, int32_t layer, int32_t seq, int32_t which, voi
         std::memcpy(dst, &v, 8);
     } else if (which == SKO_TAB_INDEXER) {
         // undo the 64-token tiling: [tile][chunk][token] x 16 B -> [token][chunk] x 16 B
-        std::vector<uint4> tiles((size_t)h->ntiles * kIdxRowU4 * kIdxTile);
+        const int ru = h->c8 ? kIdxC8RowU4 : kIdxRowU4;
+        std::vector<uint4> tiles((size_t)h->ntiles * ru * kIdxTile);
         e = hipMemcpy(tiles.data(), src, tiles.size() * sizeof(uint4), hipMemcpyDeviceToHost);
         if (e != hipSuccess) return device_fail(h, e, "read table");
         uint4* o = static_cast<uint4*>(dst);
         for (int64_t tok = 0; tok < h->cap; ++tok)
-            for (int c = 0; c < kIdxRowU4; ++c) o[tok * kIdxRowU4 + c] = tiles[idx_tile_u4(0, tok, c)];
+            for (int c = 0; c < ru; ++c)
+                o[tok * ru + c] = tiles[h->c8 ? idx_c8_tile_u4(0, tok, c) : idx_tile_u4(0, tok, c)];
     } else if (host) {
         std::memcpy(dst, src, size);
     } else {

@@ -27,6 +27,8 @@
 // Winners are written packed (bit 31 = absent from the hot buffer at step
 // start) and also marked in a per-sequence bitmap over tokens, which the
 // merge stage reads in token order (union and dedupe of the D positions).
+#include <hip/hip_fp16.h>
+
 #include <utility>
 
 #include "sko_common.cuh"
@@ -77,6 +79,101 @@ hipError_t launch_append_rows(hipStream_t st, const uint16_t* idx_src, const uin
                        reinterpret_cast<const uint4*>(idx_src), reinterpret_cast<const uint4*>(kv_src),
                        reinterpret_cast<uint4*>(idx_layer), reinterpret_cast<uint4*>(pool_layer),
                        ntok_layer, seq0, n, cap, ntiles, base);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------- int8 indexer rows
+
+// One wave rotates and quantizes one bf16 row (LIM C8 of [LSO-zh] section 4:
+// Hadamard rotation, then int8 codes with an fp16 dequantization scale).
+// Lane i holds x_i and gets code i; every lane gets the scale bits.
+//   x'_i = (1/8) sum_j (-1)^popcount(i & j) x_j, a binary32 sum in index
+//          order j = 0..63 from +0 (every term exact);
+//   s = max_i |x'_i| / 127, code_i = round-half-even(x'_i / s) clamped to
+//   [-127, 127]; the scale is s rounded to binary16 (a zero row: all 0).
+__device__ __forceinline__ int quant_row_wave(float xi, uint32_t* scale16) {
+    const int lane = threadIdx.x & 63;
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int j = 0; j < kIdxDim; ++j) {
+        const float xj = __shfl(xi, j);
+        acc = (__popc((unsigned)(lane & j)) & 1) ? acc - xj : acc + xj;
+    }
+    const float xr = acc * 0.125f;
+    float a = fabsf(xr);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+    if (a == 0.0f) {  // wave-uniform
+        *scale16 = 0u;
+        return 0;
+    }
+    const float s = a / 127.0f;  // binary32 division, correctly rounded
+    const float r = fminf(127.0f, fmaxf(-127.0f, rintf(xr / s)));
+    *scale16 = (uint32_t)__half_as_ushort(__float2half_rn(s));
+    return (int)r;
+}
+
+// Four lanes' int8 codes packed little-endian into one word: lane 4w + e
+// holds code e of word w (the result is valid in lanes 4w).
+__device__ __forceinline__ uint32_t pack_codes4(int code) {
+    const uint32_t b = (uint32_t)code & 0xFFu;
+    const uint32_t b1 = __shfl_down(b, 1), b2 = __shfl_down(b, 2), b3 = __shfl_down(b, 3);
+    return b | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+// Append with the int8 indexer: each wave rotates and quantizes rows and
+// writes their codes (tiled) and scales; the threads then copy the
+// main-KV rows to the pool as k_append_rows does.
+__global__ __launch_bounds__(256) void k_append_rows_c8(const uint16_t* __restrict__ idx_src,
+                                                        const uint4* __restrict__ kv_src,
+                                                        uint32_t* __restrict__ codes_layer,
+                                                        uint16_t* __restrict__ scales_layer,
+                                                        uint4* __restrict__ pool_layer,
+                                                        int32_t* __restrict__ ntok_layer, int seq0, int64_t n,
+                                                        int64_t cap, int64_t ntiles, int32_t base) {
+    const int s = blockIdx.y;
+    const int b = seq0 + s;
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / 64);
+    for (int64_t r = gw; r < n; r += nwaves) {
+        const int64_t src_row = (int64_t)s * n + r;
+        const int64_t tok = base + r;
+        const float xi = __uint_as_float((uint32_t)idx_src[src_row * kIdxDim + lane] << 16);
+        uint32_t sc;
+        const int code = quant_row_wave(xi, &sc);
+        const uint32_t word = pack_codes4(code);
+        if ((lane & 3) == 0) {
+            const int w = lane >> 2;  // word w of the row: chunk w / 4, word w % 4 of it
+            codes_layer[idx_c8_tile_u4((size_t)b * ntiles, tok, w >> 2) * 4 + (w & 3)] = word;
+        }
+        if (lane == 0) scales_layer[(size_t)b * ntiles * kIdxTile + tok] = (uint16_t)sc;
+    }
+    if (kv_src) {
+        const int64_t chunks = n * kKvRowU4;
+        for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
+             c += (int64_t)gridDim.x * blockDim.x) {
+            const int64_t r = c / kKvRowU4;
+            const int part = (int)(c - r * kKvRowU4);
+            pool_layer[((int64_t)b * cap + base + r) * kKvRowU4 + part] =
+                kv_src[((int64_t)s * n + r) * kKvRowU4 + part];
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) ntok_layer[b] = base + (int32_t)n;
+}
+
+hipError_t launch_append_rows_c8(hipStream_t st, const uint16_t* idx_src, const uint16_t* kv_src,
+                                 uint8_t* idx_layer, uint16_t* scales_layer, uint16_t* pool_layer,
+                                 int32_t* ntok_layer, int seq0, int nseq, int64_t n, int64_t cap,
+                                 int64_t ntiles, int32_t base) {
+    const int64_t by_rows = (n + 3) / 4;
+    const int64_t by_kv = kv_src ? (n * kKvRowU4 + 255) / 256 : 1;
+    int gx = (int)std::min<int64_t>(std::max(by_rows, by_kv), 4096);
+    if (gx < 1) gx = 1;
+    hipLaunchKernelGGL(k_append_rows_c8, dim3(gx, nseq), dim3(256), 0, st, idx_src,
+                       reinterpret_cast<const uint4*>(kv_src), reinterpret_cast<uint32_t*>(idx_layer),
+                       scales_layer, reinterpret_cast<uint4*>(pool_layer), ntok_layer, seq0, n, cap, ntiles,
+                       base);
     return hipGetLastError();
 }
 
@@ -185,6 +282,29 @@ __device__ __forceinline__ uint32_t token_key(const uint4* __restrict__ idx_laye
     return score_key(acc);
 }
 
+// Key of token `token` with the int8 indexer: the exact int32 dot of the
+// codes (any order gives the same sum), then (dot * s_k) * s_q in binary32.
+__device__ __forceinline__ uint32_t token_key_c8(const uint4* __restrict__ codes_layer,
+                                                 const uint16_t* __restrict__ scales_layer,
+                                                 size_t seq_tiles_base, int64_t token,
+                                                 const uint32_t* __restrict__ q8row) {
+    int dot = 0;
+#pragma unroll
+    for (int c = 0; c < kIdxC8RowU4; ++c) {
+        const uint4 v = codes_layer[idx_c8_tile_u4(seq_tiles_base, token, c)];
+        dot = __builtin_amdgcn_sdot4((int)v.x, (int)q8row[4 * c + 0], dot, false);
+        dot = __builtin_amdgcn_sdot4((int)v.y, (int)q8row[4 * c + 1], dot, false);
+        dot = __builtin_amdgcn_sdot4((int)v.z, (int)q8row[4 * c + 2], dot, false);
+        dot = __builtin_amdgcn_sdot4((int)v.w, (int)q8row[4 * c + 3], dot, false);
+    }
+    const float sk = __half2float(__ushort_as_half(scales_layer[seq_tiles_base * kIdxTile + token]));
+    const float sq = __half2float(__ushort_as_half((uint16_t)q8row[kIdxDim / 4]));
+    float acc = (float)dot * sk;
+    acc = acc * sq;
+    if (acc == 0.0f) acc = 0.0f;
+    return score_key(acc);
+}
+
 // Score pass over the flattened (sequence, tile) space of B * tiles_now
 // tiles of 64 tokens: block j takes the contiguous range
 // [j * total / nblocks, (j + 1) * total / nblocks), and the launch holds at
@@ -212,15 +332,25 @@ __device__ __forceinline__ uint32_t token_key(const uint4* __restrict__ idx_laye
 template <int NP>
 constexpr int score_threads() { return NP == 1 ? 640 : 768; }
 
-template <int NP, bool KEEP>
+// The C8 instantiation reads the int8 indexer instead (4 chunks of codes
+// and one fp16 scale per token): its queries are rotated and quantized at
+// the start of each segment (waves 0..NP-1, one row each, also written to
+// qc8 for the filter), and a score is the exact int32 dot of the codes
+// (dot4 instructions; every order gives the same sum) times s_k, times s_q.
+template <int NP, bool KEEP, bool C8>
 __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
     const uint4* __restrict__ idx_layer, const uint32_t* __restrict__ q_idx,
     const int32_t* __restrict__ ntok_layer, uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
     const int32_t* __restrict__ floor_layer, uint2* __restrict__ pre, RowMeta* __restrict__ meta,
     const int32_t* __restrict__ cache_slots_layer, int D, int p0, int64_t kcap, int64_t cap, int64_t ntiles,
-    int64_t tiles_now, int64_t total_tiles) {
+    int64_t tiles_now, int64_t total_tiles, const uint16_t* __restrict__ scales_layer,
+    uint32_t* __restrict__ qc8) {
     constexpr int nw = score_threads<NP>() / 64;
+    constexpr int RU = C8 ? kIdxC8RowU4 : kIdxRowU4;  // 16-byte loads per token
     __shared__ uint32_t sh[NP * kHistBins];
+    // C8: per position, the query codes (16 words) then the scale bits,
+    // rows of 5 x 16 bytes so the codes are read with 16-byte loads
+    __shared__ uint4 sq8[C8 ? NP : 1][5];
     __shared__ uint2 stage[nw][NP][kPreStage];
     __shared__ int s_cnt[nw][NP];
     __shared__ float sq[NP > 1 ? NP * kIdxDim : 1];
@@ -242,17 +372,37 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
         const size_t row0 = (size_t)b * D + p0;
         const uint32_t* __restrict__ qb = q_idx + row0 * (kIdxDim / 2);
         uint32_t* __restrict__ keyrow = keys + row0 * kcap;
-        const uint4* __restrict__ seq_tiles = idx_layer + (size_t)b * ntiles * kIdxRowU4 * kIdxTile + lane;
+        const uint4* __restrict__ seq_tiles = idx_layer + (size_t)b * ntiles * RU * kIdxTile + lane;
+        const uint16_t* __restrict__ seq_scales = C8 ? scales_layer + (size_t)b * ntiles * kIdxTile + lane : nullptr;
         const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
         // query terms of positions p0.. as binary32 in LDS; each chain loads
         // its position's terms 16 per register (replicated in the four
         // 16-lane rows): register m, lane l holds term 16*m + (l % 16)
-        if constexpr (NP > 1) {
+        if constexpr (C8) {
+            if (wave < NP) {
+                const uint16_t* qh = reinterpret_cast<const uint16_t*>(q_idx) + (row0 + wave) * kIdxDim;
+                uint32_t sc;
+                const int code = quant_row_wave(__uint_as_float((uint32_t)qh[lane] << 16), &sc);
+                const uint32_t word = pack_codes4(code);
+                uint32_t* qg = qc8 + (row0 + wave) * kQc8Words;
+                uint32_t* ql = reinterpret_cast<uint32_t*>(&sq8[wave][0]);
+                if ((lane & 3) == 0) {
+                    ql[lane >> 2] = word;
+                    qg[lane >> 2] = word;
+                }
+                if (lane == 0) {
+                    ql[kIdxDim / 4] = sc;
+                    qg[kIdxDim / 4] = sc;
+                }
+            }
+            __syncthreads();
+        } else if constexpr (NP > 1) {
             const uint16_t* qh = reinterpret_cast<const uint16_t*>(q_idx) + row0 * kIdxDim;
             for (int i = threadIdx.x; i < NP * kIdxDim; i += blockDim.x)
                 sq[i] = __uint_as_float((uint32_t)qh[i] << 16);
             __syncthreads();
         }
+
         uint32_t floor_bin[NP];
         int nstage[NP];  // wave-uniform
 #pragma unroll
@@ -274,20 +424,21 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
         // (the tile index is clamped to the last valid tile) so that the
         // compiler's wait counts stay "all but the newest 8 loads".
         const int64_t last = tile_end - 1;
-        auto load_tile = [&](uint4* r, int64_t tile) {
+        auto load_tile = [&](uint4* r, uint32_t& scv, int64_t tile) {
             const int64_t tl = tile < last ? tile : last;
 #pragma unroll
-            for (int c = 0; c < kIdxRowU4; ++c) r[c] = load_nt_u4(seq_tiles + (tl * kIdxRowU4 + c) * kIdxTile);
+            for (int c = 0; c < RU; ++c) r[c] = load_nt_u4(seq_tiles + (tl * RU + c) * kIdxTile);
+            if constexpr (C8) scv = seq_scales[tl * kIdxTile];
         };
         // the chains run for every lane (lanes past the last token compute on
         // a clamped in-bounds row and store nothing), so every loaded
         // register is consumed on every path
-        auto score_tile = [&](const uint4* r, int64_t tile) {
+        auto score_tile = [&](const uint4* r, uint32_t scv, int64_t tile) {
             const int64_t i = tile * kIdxTile + lane;
             const bool valid = i < Lt;
-            uint32_t w[32];
+            uint32_t w[4 * RU];
 #pragma unroll
-            for (int c = 0; c < kIdxRowU4; ++c) {
+            for (int c = 0; c < RU; ++c) {
                 w[4 * c + 0] = r[c].x;
                 w[4 * c + 1] = r[c].y;
                 w[4 * c + 2] = r[c].z;
@@ -296,7 +447,21 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
                 float acc;
-                if constexpr (NP == 1) {
+                if constexpr (C8) {
+                    // the query row from LDS (same address in every lane)
+                    int dot = 0;
+#pragma unroll
+                    for (int c = 0; c < kIdxC8RowU4; ++c) {
+                        const uint4 qv = sq8[p][c];
+                        dot = __builtin_amdgcn_sdot4((int)w[4 * c + 0], (int)qv.x, dot, false);
+                        dot = __builtin_amdgcn_sdot4((int)w[4 * c + 1], (int)qv.y, dot, false);
+                        dot = __builtin_amdgcn_sdot4((int)w[4 * c + 2], (int)qv.z, dot, false);
+                        dot = __builtin_amdgcn_sdot4((int)w[4 * c + 3], (int)qv.w, dot, false);
+                    }
+                    const float sq = __half2float(__ushort_as_half((uint16_t)sq8[p][4].x));
+                    acc = (float)dot * __half2float(__ushort_as_half((uint16_t)scv));
+                    acc = acc * sq;
+                } else if constexpr (NP == 1) {
                     // one position: its 32 query words fit in scalar registers
                     acc = 0.0f;
 #pragma unroll
@@ -332,16 +497,17 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
                 }
             }
         };
-        uint4 ra[kIdxRowU4], rb[kIdxRowU4];
+        uint4 ra[RU], rb[RU];
+        uint32_t sa = 0u, sb = 0u;  // C8: the lane's token scales
         int64_t tile = tile0 + wave;
         if (tile < tile_end) {
-            load_tile(ra, tile);
+            load_tile(ra, sa, tile);
             for (; tile < tile_end; tile += 2 * nw) {
-                load_tile(rb, tile + nw);
-                score_tile(ra, tile);
+                load_tile(rb, sb, tile + nw);
+                score_tile(ra, sa, tile);
                 if (tile + nw >= tile_end) break;
-                load_tile(ra, tile + 2 * nw);
-                score_tile(rb, tile + nw);
+                load_tile(ra, sa, tile + 2 * nw);
+                score_tile(rb, sb, tile + nw);
             }
         }
         // end of segment: one reservation per row for the whole block
@@ -383,11 +549,11 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
 }
 
 namespace {
-template <int NP>
+template <int NP, bool C8>
 int score_blocks_per_cu() {
     static const int n = [] {
         int v = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void*>(&k_score_hist<NP, false>),
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void*>(&k_score_hist<NP, false, C8>),
                                                          score_threads<NP>(), 0) != hipSuccess ||
             v < 1)
             v = 1;
@@ -397,34 +563,41 @@ int score_blocks_per_cu() {
 }
 }  // namespace
 
-hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const uint16_t* q_idx,
+hipError_t launch_score_hist(hipStream_t st, const void* idx_layer, const uint16_t* q_idx,
                              const int32_t* ntok_layer, uint32_t* keys, uint32_t* hist,
                              const int32_t* floor_layer, uint2* pre, RowMeta* meta,
                              const int32_t* cache_slots_layer, int B, int D, int64_t kcap, int64_t cap,
-                             int64_t ntiles, int64_t max_tokens_now, int cu_count) {
+                             int64_t ntiles, int64_t max_tokens_now, int cu_count,
+                             const uint16_t* scales_layer, uint32_t* qc8) {
     const int64_t tiles_now = std::max<int64_t>(1, (max_tokens_now + kIdxTile - 1) / kIdxTile);
     const int64_t total = (int64_t)B * tiles_now;
     const uint4* kb = reinterpret_cast<const uint4*>(idx_layer);
     const uint32_t* q = reinterpret_cast<const uint32_t*>(q_idx);
     for (int p0 = 0; p0 < D; p0 += 4) {
         const int np = std::min(4, D - p0);
-        const int per_cu = np == 1 ? score_blocks_per_cu<1>() : np == 2 ? score_blocks_per_cu<2>()
-                         : np == 3 ? score_blocks_per_cu<3>() : score_blocks_per_cu<4>();
+        const int per_cu = scales_layer
+                               ? (np == 1 ? score_blocks_per_cu<1, true>() : np == 2 ? score_blocks_per_cu<2, true>()
+                                  : np == 3 ? score_blocks_per_cu<3, true>() : score_blocks_per_cu<4, true>())
+                               : (np == 1 ? score_blocks_per_cu<1, false>() : np == 2 ? score_blocks_per_cu<2, false>()
+                                  : np == 3 ? score_blocks_per_cu<3, false>() : score_blocks_per_cu<4, false>());
         const int nw = (np == 1 ? score_threads<1>() : score_threads<4>()) / 64;
         // one resident round of blocks, at least one tile per wave
         int64_t nb = std::min<int64_t>((int64_t)cu_count * per_cu, (total + nw - 1) / nw);
         nb = std::max<int64_t>(nb, 1);
         const dim3 grid((unsigned)nb);
-#define SKO_SCORE_LAUNCH(N)                                                                                \
-    do {                                                                                                   \
-        if (keys)                                                                                          \
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_score_hist<N, true>), grid, dim3(score_threads<N>()), 0, st, kb, \
-                               q, ntok_layer, keys, hist, floor_layer, pre, meta, cache_slots_layer, D, p0, kcap, \
-                               cap, ntiles, tiles_now, total);                                               \
-        else                                                                                               \
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_score_hist<N, false>), grid, dim3(score_threads<N>()), 0, st, kb,\
-                               q, ntok_layer, keys, hist, floor_layer, pre, meta, cache_slots_layer, D, p0, kcap, \
-                               cap, ntiles, tiles_now, total);                                               \
+#define SKO_SCORE_LAUNCH1(N, K, C)                                                                         \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_score_hist<N, K, C>), grid, dim3(score_threads<N>()), 0, st, kb, q,      \
+                       ntok_layer, keys, hist, floor_layer, pre, meta, cache_slots_layer, D, p0, kcap, cap, ntiles, \
+                       tiles_now, total, scales_layer, qc8)
+#define SKO_SCORE_LAUNCH(N)                                   \
+    do {                                                      \
+        if (scales_layer) {                                   \
+            if (keys) SKO_SCORE_LAUNCH1(N, true, true);       \
+            else SKO_SCORE_LAUNCH1(N, false, true);           \
+        } else {                                              \
+            if (keys) SKO_SCORE_LAUNCH1(N, true, false);      \
+            else SKO_SCORE_LAUNCH1(N, false, false);          \
+        }                                                     \
     } while (0)
         switch (np) {
             case 1: SKO_SCORE_LAUNCH(1); break;
@@ -433,6 +606,7 @@ hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const ui
             default: SKO_SCORE_LAUNCH(4); break;
         }
 #undef SKO_SCORE_LAUNCH
+#undef SKO_SCORE_LAUNCH1
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -468,7 +642,8 @@ __global__ __launch_bounds__(256) void k_topk_filter(
     uint2* __restrict__ cand, int32_t* __restrict__ topk, const int32_t* __restrict__ cache_slots_layer,
     const int32_t* __restrict__ ntok_layer, uint32_t* __restrict__ winners, uint32_t* __restrict__ miss_bits,
     const uint4* __restrict__ idx_layer, const uint32_t* __restrict__ q_idx, int32_t* __restrict__ floor_layer,
-    int rescan_all, int D, int64_t cap, int64_t ntiles, int64_t wpr, int top_k) {
+    int rescan_all, int D, int64_t cap, int64_t ntiles, int64_t wpr, int top_k,
+    const uint16_t* __restrict__ scales_layer, const uint32_t* __restrict__ qc8) {
     __shared__ int scratch[8];
     __shared__ int s_bw, s_bs, s_floor;
     __shared__ RowMeta s_res;
@@ -515,7 +690,9 @@ __global__ __launch_bounds__(256) void k_topk_filter(
                 kv[e] = 0u;
                 tk[e] = 0u;
                 if (i < n_items) {
-                    kv[e] = token_key(idx_layer, (size_t)b * ntiles, i, qrow);
+                    kv[e] = qc8 ? token_key_c8(idx_layer, scales_layer, (size_t)b * ntiles, i,
+                                               qc8 + (size_t)row * kQc8Words)
+                                : token_key(idx_layer, (size_t)b * ntiles, i, qrow);
                     const int bin = (int)(kv[e] >> (32 - kHistBits));
                     if (bin > m.bucket || (bin == m.bucket && take_bucket)) wmask |= 1u << e;
                     else if (bin == m.bucket) smask |= 1u << e;
@@ -568,9 +745,9 @@ __global__ __launch_bounds__(256) void k_topk_filter(
 hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* meta, const uint2* pre,
                               uint2* cand, int32_t* topk, const int32_t* cache_slots_layer,
                               const int32_t* ntok_layer, uint32_t* winners, uint32_t* miss_bits,
-                              const uint16_t* idx_layer, const uint16_t* q_idx, int32_t* floor_layer,
+                              const void* idx_layer, const uint16_t* q_idx, int32_t* floor_layer,
                               bool rescan_all, int B, int D, int64_t cap, int64_t ntiles, int top_k,
-                              int64_t max_tokens_now) {
+                              int64_t max_tokens_now, const uint16_t* scales_layer, const uint32_t* qc8) {
     const int64_t wpr = winner_words(cap);
     const int64_t now = std::max<int64_t>(1, max_tokens_now);
     const int per_row = (int)std::min<int64_t>(32, std::max<int64_t>(4, (now + kFilterSpan - 1) / kFilterSpan));
@@ -578,7 +755,7 @@ hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* met
     hipLaunchKernelGGL(k_topk_filter, grid, dim3(256), 0, st, hist, meta, pre, cand, topk, cache_slots_layer,
                        ntok_layer, winners, miss_bits, reinterpret_cast<const uint4*>(idx_layer),
                        reinterpret_cast<const uint32_t*>(q_idx), floor_layer, rescan_all ? 1 : 0, D, cap, ntiles,
-                       wpr, top_k);
+                       wpr, top_k, scales_layer, qc8);
     return hipGetLastError();
 }
 

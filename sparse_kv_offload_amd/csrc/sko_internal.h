@@ -41,6 +41,17 @@ __host__ __device__ inline size_t idx_tile_u4(size_t seq_tiles_base, int64_t tok
            (size_t)(token % kIdxTile);
 }
 
+// The int8 indexer (LIM C8): per token 64 int8 codes, as 4 chunks of 16
+// bytes in the same tiled order ([B][ntiles][4 chunks][64 tokens] x 16 B),
+// and one fp16 scale in a separate [B][ntiles * 64] array.  A quantized
+// query row is kQc8Words words: 16 words of codes, then its fp16 scale bits.
+constexpr int kIdxC8RowU4 = kIdxDim / 16;  // 4 x 16 B per int8 indexer row
+constexpr int kQc8Words = kIdxDim / 4 + 1;
+__host__ __device__ inline size_t idx_c8_tile_u4(size_t seq_tiles_base, int64_t token, int chunk) {
+    return ((seq_tiles_base + (size_t)(token / kIdxTile)) * kIdxC8RowU4 + chunk) * kIdxTile +
+           (size_t)(token % kIdxTile);
+}
+
 // Per (seq, position) row of the top-k selection.
 struct RowMeta {
     int32_t bucket;        // first-digit bucket holding the k-th largest key (-1: none)
@@ -80,21 +91,31 @@ hipError_t launch_append_rows(hipStream_t st, const uint16_t* idx_src, const uin
                               uint16_t* idx_layer, uint16_t* pool_layer, int32_t* ntok_layer,
                               int seq0, int nseq, int64_t n, int64_t cap, int64_t ntiles,
                               int32_t base);
+// The same for the int8 indexer: each bf16 indexer row is rotated and
+// quantized into its codes (idx_layer in the int8 layout) and fp16 scale.
+hipError_t launch_append_rows_c8(hipStream_t st, const uint16_t* idx_src, const uint16_t* kv_src,
+                                 uint8_t* idx_layer, uint16_t* scales_layer, uint16_t* pool_layer,
+                                 int32_t* ntok_layer, int seq0, int nseq, int64_t n, int64_t cap,
+                                 int64_t ntiles, int32_t base);
 // keys may be null (keys are then not stored); candidates (key, token |
 // miss << 31) with first digit >= floor_layer[row] go to
-// pre[row][0 .. meta[row].pre_count).
-hipError_t launch_score_hist(hipStream_t st, const uint16_t* idx_layer, const uint16_t* q_idx,
+// pre[row][0 .. meta[row].pre_count).  scales_layer non-null: the int8
+// indexer (idx_layer in its layout); the queries are rotated and quantized
+// in the launch and written to qc8 [B*D][kQc8Words] for the filter.
+hipError_t launch_score_hist(hipStream_t st, const void* idx_layer, const uint16_t* q_idx,
                              const int32_t* ntok_layer, uint32_t* keys, uint32_t* hist,
                              const int32_t* floor_layer, uint2* pre, RowMeta* meta,
                              const int32_t* cache_slots_layer, int B, int D, int64_t kcap, int64_t cap,
-                             int64_t ntiles, int64_t max_tokens_now, int cu_count);
+                             int64_t ntiles, int64_t max_tokens_now, int cu_count,
+                             const uint16_t* scales_layer, uint32_t* qc8);
 // Also sets floor_layer for the next step (kFloorRescanAll when rescan_all).
+// scales_layer / qc8 non-null: the int8 indexer (for the rescan path).
 hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* meta, const uint2* pre,
                               uint2* cand, int32_t* topk, const int32_t* cache_slots_layer,
                               const int32_t* ntok_layer, uint32_t* winners, uint32_t* miss_bits,
-                              const uint16_t* idx_layer, const uint16_t* q_idx, int32_t* floor_layer,
+                              const void* idx_layer, const uint16_t* q_idx, int32_t* floor_layer,
                               bool rescan_all, int B, int D, int64_t cap, int64_t ntiles, int top_k,
-                              int64_t max_tokens_now);
+                              int64_t max_tokens_now, const uint16_t* scales_layer, const uint32_t* qc8);
 // Also finishes the top-k (split buckets) and clears the histograms and row
 // records for the next step.
 hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, RowMeta* meta,

@@ -5,7 +5,8 @@ one side is fed to the other.  ``compare_step`` states the parity bar:
   * bit-exact: packed winners (index + miss flag, compared as sets per
     position since the order of winners is free), their hot slots, per-seq
     counts, the miss list, victims and evicted owners (in victim order), and
-    the full residency tables and hot-buffer bytes after the step;
+    the full residency tables and hot-buffer bytes after the step (with the
+    int8 indexer also its codes and fp16 scales);
   * attention: |gpu - oracle| <= 2e-2 absolute for every element, and a
     relative RMS error per (seq, position, head) of at most ATTN_REL_RMS.
 """
@@ -115,19 +116,25 @@ class GpuSide:
 
     def tables(self, layer: int, seq: int) -> Dict[str, np.ndarray]:
         sko = self.sko
-        return {"cache_slots": self.h.table(layer, seq, sko.SKO_TAB_CACHE_SLOTS),
-                "slot_token": self.h.table(layer, seq, sko.SKO_TAB_SLOT_TOKEN),
-                "last_use": self.h.table(layer, seq, sko.SKO_TAB_LAST_USE),
-                "hot": self.h.table(layer, seq, sko.SKO_TAB_HOT)}
+        t = {"cache_slots": self.h.table(layer, seq, sko.SKO_TAB_CACHE_SLOTS),
+             "slot_token": self.h.table(layer, seq, sko.SKO_TAB_SLOT_TOKEN),
+             "last_use": self.h.table(layer, seq, sko.SKO_TAB_LAST_USE),
+             "hot": self.h.table(layer, seq, sko.SKO_TAB_HOT)}
+        if self.h.cfg.flags & sko.SKO_FLAG_INDEXER_C8:
+            t["idx_codes"] = self.h.table(layer, seq, sko.SKO_TAB_INDEXER)
+            t["idx_scales"] = self.h.table(layer, seq, sko.SKO_TAB_INDEXER_SCALE)
+        return t
 
 
 class OracleSide:
     """The CPU oracle over a subset of (layer, seq) chains (each independent)."""
 
-    def __init__(self, w: synth.Workload, chains: List[tuple]):
+    def __init__(self, w: synth.Workload, chains: List[tuple], indexer_c8: bool = False):
         self.w = w
         self.chains = chains
-        self.o = {c: oracle.Oracle(1, 1, w.capacity, w.top_k, w.hot_slots, w.positions, w.heads, SCALE)
+        self.c8 = indexer_c8
+        self.o = {c: oracle.Oracle(1, 1, w.capacity, w.top_k, w.hot_slots, w.positions, w.heads, SCALE,
+                                   indexer_c8=indexer_c8)
                   for c in chains}
 
     def load_prefix(self, layer: int, seq: int) -> None:
@@ -145,7 +152,10 @@ class OracleSide:
                                                 want_out=want_out)
 
     def tables(self, layer: int, seq: int) -> Dict[str, np.ndarray]:
-        return self.o[(layer, seq)].state(0, 0)
+        t = self.o[(layer, seq)].state(0, 0)
+        if self.c8:
+            t["idx_codes"], t["idx_scales"] = self.o[(layer, seq)].indexer_c8(0, 0)
+        return t
 
 
 def _sorted_by_token(packed: np.ndarray, other: Optional[np.ndarray] = None):
@@ -197,6 +207,12 @@ def compare_tables(gt: Dict[str, np.ndarray], ot: Dict[str, np.ndarray], where: 
             bad = np.nonzero(gt[name] != ot[name])[0][:8]
             raise AssertionError(f"{where} table {name} differs at {bad.tolist()}")
     assert np.array_equal(gt["hot"], ot["hot"]), f"{where} hot-buffer bytes differ"
+    if "idx_codes" in ot:
+        # int8 indexer rows: codes and fp16 scale bits exactly
+        for name in ("idx_codes", "idx_scales"):
+            if not np.array_equal(gt[name], ot[name]):
+                bad = np.unique(np.nonzero(gt[name] != ot[name])[0])[:8]
+                raise AssertionError(f"{where} {name} differ at tokens {bad.tolist()}")
 
 
 def run_parity(w: synth.Workload, layers: Optional[int] = None, steps: Optional[int] = None,
@@ -211,7 +227,7 @@ def run_parity(w: synth.Workload, layers: Optional[int] = None, steps: Optional[
     import sparse_kv_offload_amd as sko
     gpu = GpuSide(w, L, device_append=device_append,
                   flags=flags | (sko.SKO_FLAG_KEEP_KEYS if check_keys else 0))
-    ora = OracleSide(w, chains)
+    ora = OracleSide(w, chains, indexer_c8=bool(flags & sko.SKO_FLAG_INDEXER_C8))
     worst = {"abs": 0.0, "rel_rms": 0.0, "rescans": 0}
     try:
         for l in range(L):

@@ -307,3 +307,35 @@ def test_early_copy_three_positions():
     w = case("early", batch=6, context=5000, steps=5, top_k=128, hot_slots=500, positions=3, heads=4)
     log("case early copy B=6 D=3")
     run_parity(w, check_keys=False, flags=0, log=log)
+
+
+@pytest.mark.parametrize("shape", ["d1", "d4_ragged", "host_append", "zeroq", "rescan", "floor_drop"])
+def test_indexer_c8(shape):
+    """The int8 indexer: codes and fp16 scales of every appended row, the
+    score keys of every token, the winners and everything after them match
+    the oracle in its int8 mode."""
+    import sparse_kv_offload_amd as sko
+    f = sko.SKO_FLAG_INDEXER_C8
+    device_append = True
+    if shape == "d1":
+        w = case("c8d1", batch=3, context=5000, steps=6, top_k=256, hot_slots=600, positions=1, heads=16)
+    elif shape == "d4_ragged":
+        w = case("c8d4", batch=3, contexts=(4097, 1, 900), context=4097, steps=5, top_k=128, hot_slots=600,
+                 positions=4, heads=16)
+    elif shape == "host_append":
+        w = case("c8host", batch=2, context=3000, steps=4, top_k=100, hot_slots=300, positions=2, heads=8)
+        device_append = False
+    elif shape == "zeroq":
+        w = ZeroQuery("c8zeroq", layers=1, batch=2, context=3000, steps=3, top_k=150, hot_slots=400,
+                      positions=2, heads=16, seed=5)
+    elif shape == "rescan":
+        w = case("c8rescan", batch=2, context=4000, steps=4, top_k=200, hot_slots=700, positions=3, heads=16)
+        f |= sko.SKO_FLAG_SELECT_RESCAN
+    else:
+        w = ScaledQuery("c8scaledq", layers=1, batch=2, context=6000, steps=6, top_k=128, hot_slots=300,
+                        positions=1, heads=16, seed=9)
+    log(f"case indexer c8 {shape}")
+    worst = run_parity(w, check_keys=True, device_append=device_append, flags=f, log=log)
+    if shape == "floor_drop":
+        assert worst["rescans"] > 0
+    log(f"c8 {shape} worst {worst}")
