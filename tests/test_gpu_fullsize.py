@@ -33,11 +33,11 @@ def _gpu():
     yield
 
 
-def _run(w, layers, steps, chains, out_steps, tables_every):
+def _run(w, layers, steps, chains, out_steps, tables_every, flags=0):
     log(f"fullsize {w.name}: layers={layers} batch={w.batch} context={w.context} k={w.top_k} "
-        f"S={w.hot_slots} D={w.positions} H={w.heads} steps={steps} chains={chains}")
+        f"S={w.hot_slots} D={w.positions} H={w.heads} steps={steps} chains={chains} flags={flags:#x}")
     worst = run_parity(w, layers=layers, steps=steps, chains=chains, out_steps=set(out_steps),
-                       check_tables_every=tables_every, log=log)
+                       check_tables_every=tables_every, log=log, flags=flags)
     log(f"fullsize {w.name}: ok, attention worst {worst}")
 
 
@@ -65,3 +65,19 @@ def test_shelf_ctx4_full_shape():
 def test_long_full_shape():
     w = synth.LONG
     _run(w, layers=2, steps=10, chains=[(1, 1)], out_steps=[0, 9], tables_every=5)
+
+
+def test_long_full_shape_int8_indexer():
+    """The int8 indexer at the long workload's shape (codes, scales and
+    tables of the sampled chain compared too)."""
+    import sparse_kv_offload_amd as sko
+    w = synth.LONG
+    _run(w, layers=1, steps=6, chains=[(0, 1)], out_steps=[0, 5], tables_every=5,
+         flags=sko.SKO_FLAG_INDEXER_C8)
+
+
+def test_mtp3_full_shape_int8_indexer():
+    import sparse_kv_offload_amd as sko
+    w = synth.MTP3
+    _run(w, layers=1, steps=8, chains=[(0, 9)], out_steps=[0, 7], tables_every=7,
+         flags=sko.SKO_FLAG_INDEXER_C8)
