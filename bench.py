@@ -238,7 +238,7 @@ def main() -> int:
 
     def deltas(s0, s1):
         return {f: sum(getattr(b, f) - getattr(a, f) for a, b in zip(s0, s1))
-                for f in ("unique", "hits", "misses", "evictions", "h2d_bytes", "rescans")}
+                for f in ("unique", "hits", "misses", "evictions", "h2d_bytes", "rescans", "direct_rows")}
 
     d = deltas(stats0, stats1)
 
@@ -338,6 +338,7 @@ def main() -> int:
         "frac_of_link_bound": round(value * d["h2d_bytes"] / (h2d_ceiling * 1e9 * layer_steps), 4)
         if d["h2d_bytes"] else None,
         "selection_rescans": d["rescans"],
+        "newest_rows_from_device": d["direct_rows"],
         "roofline": roof,
         "rooflines": rooflines,
         "stage_ms_per_launch": {n: round(ms / c, 5) for n, (ms, c) in calib.items() if c},

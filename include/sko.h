@@ -131,9 +131,12 @@ typedef struct sko_layer_stats {
     int64_t hits;
     int64_t misses;
     int64_t evictions;
-    int64_t h2d_bytes; /* misses * 1152 */
+    int64_t h2d_bytes; /* (misses - direct_rows) * 1152: rows read over the host link */
     int64_t rescans;   /* (seq, position) rows whose threshold fell below the
                           candidate floor, so the filter rescanned the row */
+    int64_t direct_rows; /* misses that were the sequence's newest token: its
+                            row is copied from the device copy kept by
+                            sko_append_token, not read from the host pool */
 } sko_layer_stats;
 
 /*
@@ -163,7 +166,11 @@ int sko_set_stream(sko_handle* h, void* stream);
  * pool, the indexer rows to the device indexer cache ([LSO] §4 "Decode
  * step", first two items; the "Decode current KV to Decode host" row of the
  * transfer-granularity table: token rows).  A prefix load is one call with
- * n = context length.
+ * n = context length.  The last main-KV row of each sequence is also kept
+ * in a device copy: a new token is produced on the device, and when it is
+ * selected at its first step (a miss, since it was never resident) its row
+ * is moved into the hot buffer from that copy instead of over the host
+ * link (counted in sko_layer_stats.direct_rows; results are unchanged).
  *   seq       0 <= seq < B, or SKO_ALL_SEQS (rows for sequence b start at
  *             row b*n of both inputs)
  *   idx_rows  [rows][64] bf16, kv_rows [rows][576] bf16, row-major,

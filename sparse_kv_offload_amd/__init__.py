@@ -78,7 +78,7 @@ class SkoSeqCounts(ctypes.Structure):
 
 class SkoLayerStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
-                ("steps", "unique", "hits", "misses", "evictions", "h2d_bytes", "rescans")]
+                ("steps", "unique", "hits", "misses", "evictions", "h2d_bytes", "rescans", "direct_rows")]
 
 
 class SkoError(RuntimeError):

@@ -53,6 +53,7 @@ template <int COPY>
 __global__ __launch_bounds__(256) void k_attn_partial(
     const int32_t* __restrict__ topk, const int32_t* __restrict__ cache_slots_layer,
     uint4* __restrict__ hot_layer, const uint4* __restrict__ q_attn, const uint4* __restrict__ pool_layer,
+    const uint4* __restrict__ recent_layer,
     const int32_t* __restrict__ ntok_layer, float* __restrict__ part_acc,
     float* __restrict__ part_ml, int32_t* __restrict__ phys, const uint4* __restrict__ stage_rows,
     int32_t* __restrict__ stage_idx, int32_t* __restrict__ stage_cnt, int B, int D, int H, int HG,
@@ -128,7 +129,9 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         for (int j = wave; j < r1 - r0; j += 4) {
             const int32_t c = cp_s[j];
             const int32_t dst = c >= 0 ? slot_s[j] : -1;
-            const uint4* sp = pool_layer + ((size_t)b * cap + (c >= 0 ? c : 0)) * kKvRowU4;
+            // (the newest token's row from its device copy)
+            const uint4* sp = c == Lt - 1 ? recent_layer + (size_t)b * kKvRowU4
+                                          : pool_layer + ((size_t)b * cap + (c >= 0 ? c : 0)) * kKvRowU4;
             uint4 a = make_uint4(0u, 0u, 0u, 0u), e = make_uint4(0u, 0u, 0u, 0u);
             if (c >= 0) {
                 a = sp[lane];
@@ -370,7 +373,8 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* _
 
 hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_t* cache_slots_layer,
                                uint16_t* hot_layer, const uint16_t* q_attn, const uint16_t* pool_layer,
-                               const int32_t* ntok_layer, float* part_acc, float* part_ml,
+                               const uint16_t* recent_layer, const int32_t* ntok_layer, float* part_acc,
+                               float* part_ml,
                                int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
                                int rows_per_block, float scale, const uint16_t* stage_rows,
                                int32_t* stage_idx, int32_t* stage_cnt) {
@@ -380,7 +384,8 @@ hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_
 #define SKO_ATTN_LAUNCH(C)                                                                                  \
     hipLaunchKernelGGL(k_attn_partial<C>, dim3(nchunk, B * D, HG), dim3(256), 0, st, topk, cache_slots_layer,  \
                        reinterpret_cast<uint4*>(hot_layer), reinterpret_cast<const uint4*>(q_attn),             \
-                       reinterpret_cast<const uint4*>(pool_layer), ntok_layer, part_acc, part_ml, phys,         \
+                       reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<const uint4*>(recent_layer), \
+                       ntok_layer, part_acc, part_ml, phys,                                                     \
                        reinterpret_cast<const uint4*>(stage_rows), stage_idx, stage_cnt, B, D, H, HG, top_k, S, \
                        cap, rows_per_block, nchunk, scale_log2)
     if (pool_layer != nullptr && stage_rows != nullptr) return hipErrorInvalidValue;

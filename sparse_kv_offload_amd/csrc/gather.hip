@@ -35,8 +35,10 @@ __device__ __forceinline__ int find_seq(const int* pre, int B, int64_t e) {
 __global__ __launch_bounds__(kGatherThreads) void k_gather_misses(const GatherEntry* __restrict__ glist,
                                                                   const int32_t* __restrict__ counts,
                                                                   const uint4* __restrict__ pool_layer,
+                                                                  const uint4* __restrict__ recent_layer,
+                                                                  const int32_t* __restrict__ ntok_layer,
                                                                   uint4* __restrict__ hot_layer, int B,
-                                                                  int mstride) {
+                                                                  int64_t cap, int mstride) {
     extern __shared__ int pre[];  // B + 1
     __shared__ int scratch[kGatherThreads / 64 + 1];
     const int per = (B + kGatherThreads - 1) / kGatherThreads;
@@ -63,7 +65,9 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_misses(const GatherEn
             const int64_t e = std::min<int64_t>(e0 + r, total - 1);  // in range; duplicates are not stored
             const int b = find_seq(pre, B, e);
             const GatherEntry g = glist[(size_t)b * mstride + (e - pre[b])];
-            const uint4* src = pool_layer + (int64_t)g.src_row * kKvRowU4;
+            // the newest token's row is read from its device copy
+            const bool newest = g.src_row == (int64_t)b * cap + ntok_layer[b] - 1;
+            const uint4* src = newest ? recent_layer + (int64_t)b * kKvRowU4 : pool_layer + (int64_t)g.src_row * kKvRowU4;
             a[r] = src[lane];
             t8[r] = make_uint4(0u, 0u, 0u, 0u);
             if (lane < kKvRowU4 - 64) t8[r] = src[64 + lane];
@@ -79,7 +83,8 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_misses(const GatherEn
 }
 
 hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const int32_t* counts,
-                                const uint16_t* pool_layer, uint16_t* hot_layer, int B, int mstride,
+                                const uint16_t* pool_layer, const uint16_t* recent_layer,
+                                const int32_t* ntok_layer, uint16_t* hot_layer, int B, int64_t cap, int mstride,
                                 int max_entries) {
     const int rows_per_block = (kGatherThreads / 64) * kRowsPerWave;
     int grid = (int)std::min<int64_t>(((int64_t)max_entries + rows_per_block - 1) / rows_per_block,
@@ -87,7 +92,8 @@ hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const 
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(k_gather_misses, dim3(grid), dim3(kGatherThreads), (size_t)(B + 1) * sizeof(int), st,
                        glist, counts, reinterpret_cast<const uint4*>(pool_layer),
-                       reinterpret_cast<uint4*>(hot_layer), B, mstride);
+                       reinterpret_cast<const uint4*>(recent_layer), ntok_layer,
+                       reinterpret_cast<uint4*>(hot_layer), B, cap, mstride);
     return hipGetLastError();
 }
 

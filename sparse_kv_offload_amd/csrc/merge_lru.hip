@@ -209,13 +209,15 @@ constexpr int kCopyBlocks = 64;
 constexpr int kCopyRowsPerWave = 2;
 
 __device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, uint32_t* __restrict__ miss_bits,
-                                           const uint4* __restrict__ pool_layer, uint4* __restrict__ stage_rows,
+                                           const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
+                                           uint4* __restrict__ stage_rows,
                                            int32_t* __restrict__ stage_idx, int32_t* __restrict__ stage_cnt,
                                            const int32_t* __restrict__ ntok_layer, int64_t cap, int64_t wpr,
                                            int mstride, int32_t* toks, int* scratch, int* s_base) {
     const int b = cb / nper;
     const int part = cb - b * nper;
     const int64_t words_now = (ntok_layer[b] + 31) / 32;
+    const int32_t newest = ntok_layer[b] - 1;  // its row is read from the device copy
     const int64_t wi = (int64_t)part * copy_words + threadIdx.x;
     uint32_t* __restrict__ mb = miss_bits + (size_t)b * wpr;
     uint32_t bits = 0u;
@@ -240,7 +242,8 @@ __device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, uin
 #pragma unroll
         for (int r = 0; r < kCopyRowsPerWave; ++r) {
             const int i = min(i0 + r, total - 1);  // in range; duplicates are not stored
-            const uint4* src = pool_layer + ((int64_t)b * cap + toks[i]) * kKvRowU4;
+            const uint4* src = toks[i] == newest ? recent_layer + (int64_t)b * kKvRowU4
+                                                 : pool_layer + ((int64_t)b * cap + toks[i]) * kKvRowU4;
             a[r] = src[lane];
             t8[r] = make_uint4(0u, 0u, 0u, 0u);
             if (lane < kKvRowU4 - 64) t8[r] = src[64 + lane];
@@ -267,8 +270,8 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     int32_t t, int32_t* __restrict__ misses, int32_t* __restrict__ victims,
     int32_t* __restrict__ evict_old, int32_t* __restrict__ counts, GatherEntry* __restrict__ glist,
     unsigned long long* __restrict__ layer_stats, int do_refine, int nseq, int copy_per_seq, int copy_words,
-    uint32_t* __restrict__ miss_bits, const uint4* __restrict__ pool_layer, uint4* __restrict__ stage_rows,
-    int32_t* __restrict__ stage_idx, int32_t* __restrict__ stage_cnt) {
+    uint32_t* __restrict__ miss_bits, const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
+    uint4* __restrict__ stage_rows, int32_t* __restrict__ stage_idx, int32_t* __restrict__ stage_cnt) {
     __shared__ uint32_t touched[kMaxHotSlots / 32];
     // [0, kMaxMerge): misses; [kMaxMerge, 2 kMaxMerge): the union, later the
     // victims.  Before the merge the whole area stages refine candidates.
@@ -284,7 +287,8 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
 
     if ((int)blockIdx.x >= nseq) {
         __shared__ int s_base;
-        copy_block((int)blockIdx.x - nseq, copy_per_seq, copy_words, miss_bits, pool_layer, stage_rows, stage_idx,
+        copy_block((int)blockIdx.x - nseq, copy_per_seq, copy_words, miss_bits, pool_layer, recent_layer,
+                   stage_rows, stage_idx,
                    stage_cnt,
                    ntok_layer, cap, wpr, D * top_k, lists, scratch, &s_base);
         return;
@@ -504,6 +508,10 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     if (tid < D) meta[b * D + tid] = RowMeta{-1, 0, 0, 0, 0, 0, 0, 0};
     if (tid == 0) {
         if (s_rescans) atomicAdd(&layer_stats[5], (unsigned long long)s_rescans);
+        // the newest token is never resident before its first step, so it
+        // holds a slot now exactly when it was a miss; its row comes from
+        // the device copy of the newest row, not over the host link
+        if (Lt > 0 && cs[Lt - 1] >= 0) atomicAdd(&layer_stats[6], 1ull);
         cnt[0] = nU; cnt[1] = nH; cnt[2] = nM; cnt[3] = nEv;
         cnt[4] = kk; cnt[5] = (int32_t)Lt; cnt[6] = t;
         atomicAdd(&layer_stats[1], (unsigned long long)nU);
@@ -522,8 +530,8 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int B, int D, int top_k, int S, int64_t cap, int32_t t,
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
                             GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
-                            uint32_t* miss_bits, const uint16_t* pool_layer, uint16_t* stage_rows, int32_t* stage_idx,
-                            int32_t* stage_cnt, int64_t max_tokens_now) {
+                            uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
+                            uint16_t* stage_rows, int32_t* stage_idx, int32_t* stage_cnt, int64_t max_tokens_now) {
     const int64_t C = ring_capacity(S, D, top_k);
     const int64_t wpr = winner_words(cap);
     // B merge blocks, then (early copy) B * copy_per_seq copy blocks of
@@ -537,8 +545,8 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                        ring1_layer, pos_layer, ring_state_layer, D, top_k, S, C, cap, wpr, t, misses, victims,
                        evict_old, counts, glist, layer_stats, do_refine ? 1 : 0, B, copy_per_seq, copy_words,
                        miss_bits,
-                       reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<uint4*>(stage_rows), stage_idx,
-                       stage_cnt);
+                       reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<const uint4*>(recent_layer),
+                       reinterpret_cast<uint4*>(stage_rows), stage_idx, stage_cnt);
     return hipGetLastError();
 }
 

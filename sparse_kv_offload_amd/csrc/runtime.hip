@@ -86,6 +86,7 @@ struct sko_handle {
     bool c8 = false;                // the int8 indexer (SKO_FLAG_INDEXER_C8)
     uint16_t* staging = nullptr;    // device rows for host-source appends
     uint16_t* hot = nullptr;        // [L][B][S][576]
+    uint16_t* recent = nullptr;     // [L][B][576] device copy of each sequence's newest main-KV row
     int32_t* cache_slots = nullptr; // [L][B][cap]
     int32_t* slot_token = nullptr;  // [L][B][S]
     int32_t* last_use = nullptr;    // [L][B][S]
@@ -358,6 +359,7 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     const size_t stage_rows_n = h->staged_copy ? BD * h->k : 0;
     ok = ok && dev_alloc(h, (void**)&h->hot, (LB * h->S + stage_rows_n) * (size_t)kKvRowBytes);
     if (ok && h->staged_copy) h->stage_rows = h->hot + LB * h->S * kKvDim;
+    ok = ok && dev_alloc(h, (void**)&h->recent, LB * (size_t)kKvRowBytes);
     ok = ok && dev_alloc(h, (void**)&h->cache_slots, LB * h->cap * 4);
     ok = ok && dev_alloc(h, (void**)&h->slot_token, LB * h->S * 4);
     ok = ok && dev_alloc(h, (void**)&h->last_use, LB * h->S * 4);
@@ -461,14 +463,15 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
     uint8_t* idx_layer = reinterpret_cast<uint8_t*>(h->idx) + (size_t)layer * h->B * h->idx_seq_bytes();
     uint16_t* scale_layer = h->c8 ? h->idx_scale + (size_t)layer * h->B * h->ntiles * kIdxTile : nullptr;
     uint16_t* pool_layer_dev = h->pool_dev + (size_t)layer * h->B * h->cap * kKvDim;
+    uint16_t* recent_layer = h->recent + (size_t)layer * h->B * kKvDim;
     int32_t* ntok_layer = h->ntok_dev + (size_t)layer * h->B;
     // bf16 indexer rows are stored as they are, or rotated and quantized
     auto append_rows = [&](const uint16_t* is, const uint16_t* ks, uint16_t* pool, int b0, int nb, int64_t m,
                            int64_t base) {
-        return h->c8 ? launch_append_rows_c8(h->stream, is, ks, idx_layer, scale_layer, pool, ntok_layer, b0, nb, m,
-                                             h->cap, h->ntiles, (int32_t)base)
+        return h->c8 ? launch_append_rows_c8(h->stream, is, ks, idx_layer, scale_layer, pool, recent_layer,
+                                             ntok_layer, b0, nb, m, h->cap, h->ntiles, (int32_t)base)
                      : launch_append_rows(h->stream, is, ks, reinterpret_cast<uint16_t*>(idx_layer), pool,
-                                          ntok_layer, b0, nb, m, h->cap, h->ntiles, (int32_t)base);
+                                          recent_layer, ntok_layer, b0, nb, m, h->cap, h->ntiles, (int32_t)base);
     };
     const uint16_t* isrc = static_cast<const uint16_t*>(idx_rows);
     const uint16_t* ksrc = static_cast<const uint16_t*>(kv_rows);
@@ -493,6 +496,10 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
             const int64_t base = h->ntok[h->lb(layer, b)];
             std::memcpy(h->pool_host + (h->lb(layer, b) * h->cap + base) * kKvDim, ksrc + (size_t)s * n * kKvDim,
                         (size_t)n * kKvRowBytes);
+            // the newest row also to its device copy
+            hipError_t er = hipMemcpyAsync(recent_layer + (size_t)b * kKvDim, ksrc + ((size_t)s * n + n - 1) * kKvDim,
+                                           kKvRowBytes, hipMemcpyHostToDevice, h->stream);
+            if (er != hipSuccess) return device_fail(h, er, "newest row host->device");
             // indexer rows: host -> staging rows -> tiled cache, in pieces
             for (int64_t r0 = 0; r0 < n; r0 += kStagingRows) {
                 const int64_t m = std::min<int64_t>(kStagingRows, n - r0);
@@ -529,6 +536,7 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
     const void* idx_layer = reinterpret_cast<const uint8_t*>(h->idx) + (size_t)layer * B * h->idx_seq_bytes();
     const uint16_t* scale_layer = h->c8 ? h->idx_scale + (size_t)layer * B * h->ntiles * kIdxTile : nullptr;
     const uint16_t* pool_layer = h->pool_dev + LBc * kKvDim;
+    const uint16_t* recent_layer = h->recent + (size_t)layer * B * kKvDim;
     uint16_t* hot_layer = h->hot + LBs * kKvDim;
     int32_t* cs = h->cache_slots + LBc;
     int32_t* st = h->slot_token + LBs;
@@ -569,19 +577,20 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
              return launch_merge_lru(h->stream, h->winners, h->hist, h->meta, h->cand, h->topk, ntok, cs, st, lu,
                                      ring0, ring1, ring_pos, ring_state, B, D, k, S, cap, t, h->misses, h->victims,
                                      h->evict_old, h->counts, h->glist, h->stats + (size_t)layer * 8, !staged,
-                                     staged ? h->miss_bits : nullptr, pool_layer, h->stage_rows, h->stage_idx,
-                                     h->stage_cnt, max_now);
+                                     staged ? h->miss_bits : nullptr, pool_layer, recent_layer, h->stage_rows,
+                                     h->stage_idx, h->stage_cnt, max_now);
          })))
         return rc;
     // late copy: its own gather from the pool; fused or early: the attention
     // launch puts the missed rows into their slots itself
     if (!fused_copy && !staged && (rc = run_stage(h, ST_GATHER, [&] {
-             return launch_gather_misses(h->stream, h->glist, h->counts, pool_layer, hot_layer, B, D * k, B * D * k);
+             return launch_gather_misses(h->stream, h->glist, h->counts, pool_layer, recent_layer, ntok, hot_layer,
+                                         B, cap, D * k, B * D * k);
          })))
         return rc;
     if ((rc = run_stage(h, ST_ATTN, [&] {
              return launch_attn_partial(h->stream, h->topk, cs, hot_layer, qa, fused_copy ? pool_layer : nullptr,
-                                        ntok, h->part_acc, h->part_ml, h->phys, B, D, H, k, S, cap,
+                                        recent_layer, ntok, h->part_acc, h->part_ml, h->phys, B, D, H, k, S, cap,
                                         h->rows_per_block, h->cfg.attn_scale, staged ? h->stage_rows : nullptr,
                                         staged ? h->stage_idx : nullptr, staged ? h->stage_cnt : nullptr);
          })))
@@ -695,7 +704,8 @@ int sko_get_stats(sko_handle* h, int32_t layer, sko_layer_stats* out) {
     out->hits = (int64_t)v[2];
     out->misses = (int64_t)v[3];
     out->evictions = (int64_t)v[4];
-    out->h2d_bytes = (int64_t)v[3] * kKvRowBytes;
+    out->direct_rows = (int64_t)v[6];
+    out->h2d_bytes = ((int64_t)v[3] - (int64_t)v[6]) * kKvRowBytes;
     out->rescans = (int64_t)v[5];
     return SKO_OK;
 }

@@ -40,12 +40,14 @@ namespace sko {
 
 // Rows of new tokens.  16-byte chunks 0..7 of a row are the indexer row
 // (to the tiled device cache); chunks 8..79 the main-KV row (to the host
-// pool through its device mapping; skipped when kv_src is null because the
-// host already wrote it).  Sets the sequence's token count to base + n.
+// pool through its device mapping, and the last row of each sequence also
+// to the device copy of its newest row; skipped when kv_src is null because
+// the host already wrote it).  Sets the sequence's token count to base + n.
 __global__ __launch_bounds__(256) void k_append_rows(const uint4* __restrict__ idx_src,
                                                      const uint4* __restrict__ kv_src,
                                                      uint4* __restrict__ idx_layer,
                                                      uint4* __restrict__ pool_layer,
+                                                     uint4* __restrict__ recent_layer,
                                                      int32_t* __restrict__ ntok_layer, int seq0,
                                                      int64_t n, int64_t cap, int64_t ntiles,
                                                      int32_t base) {
@@ -61,16 +63,18 @@ __global__ __launch_bounds__(256) void k_append_rows(const uint4* __restrict__ i
         const int64_t tok = base + r;
         if (part < kIdxRowU4)
             idx_layer[idx_tile_u4((size_t)b * ntiles, tok, part)] = idx_src[src_row * kIdxRowU4 + part];
-        else
-            pool_layer[((int64_t)b * cap + tok) * kKvRowU4 + (part - kIdxRowU4)] =
-                kv_src[src_row * kKvRowU4 + (part - kIdxRowU4)];
+        else {
+            const uint4 v = kv_src[src_row * kKvRowU4 + (part - kIdxRowU4)];
+            pool_layer[((int64_t)b * cap + tok) * kKvRowU4 + (part - kIdxRowU4)] = v;
+            if (r == n - 1) recent_layer[(int64_t)b * kKvRowU4 + (part - kIdxRowU4)] = v;
+        }
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) ntok_layer[b] = base + (int32_t)n;
 }
 
 hipError_t launch_append_rows(hipStream_t st, const uint16_t* idx_src, const uint16_t* kv_src,
-                              uint16_t* idx_layer, uint16_t* pool_layer, int32_t* ntok_layer,
-                              int seq0, int nseq, int64_t n, int64_t cap, int64_t ntiles,
+                              uint16_t* idx_layer, uint16_t* pool_layer, uint16_t* recent_layer,
+                              int32_t* ntok_layer, int seq0, int nseq, int64_t n, int64_t cap, int64_t ntiles,
                               int32_t base) {
     const int64_t chunks = n * (kv_src ? (kIdxRowU4 + kKvRowU4) : kIdxRowU4);
     int gx = (int)std::min<int64_t>((chunks + 255) / 256, 4096);
@@ -78,7 +82,7 @@ hipError_t launch_append_rows(hipStream_t st, const uint16_t* idx_src, const uin
     hipLaunchKernelGGL(k_append_rows, dim3(gx, nseq), dim3(256), 0, st,
                        reinterpret_cast<const uint4*>(idx_src), reinterpret_cast<const uint4*>(kv_src),
                        reinterpret_cast<uint4*>(idx_layer), reinterpret_cast<uint4*>(pool_layer),
-                       ntok_layer, seq0, n, cap, ntiles, base);
+                       reinterpret_cast<uint4*>(recent_layer), ntok_layer, seq0, n, cap, ntiles, base);
     return hipGetLastError();
 }
 
@@ -129,6 +133,7 @@ __global__ __launch_bounds__(256) void k_append_rows_c8(const uint16_t* __restri
                                                         uint32_t* __restrict__ codes_layer,
                                                         uint16_t* __restrict__ scales_layer,
                                                         uint4* __restrict__ pool_layer,
+                                                        uint4* __restrict__ recent_layer,
                                                         int32_t* __restrict__ ntok_layer, int seq0, int64_t n,
                                                         int64_t cap, int64_t ntiles, int32_t base) {
     const int s = blockIdx.y;
@@ -155,8 +160,9 @@ __global__ __launch_bounds__(256) void k_append_rows_c8(const uint16_t* __restri
              c += (int64_t)gridDim.x * blockDim.x) {
             const int64_t r = c / kKvRowU4;
             const int part = (int)(c - r * kKvRowU4);
-            pool_layer[((int64_t)b * cap + base + r) * kKvRowU4 + part] =
-                kv_src[((int64_t)s * n + r) * kKvRowU4 + part];
+            const uint4 v = kv_src[((int64_t)s * n + r) * kKvRowU4 + part];
+            pool_layer[((int64_t)b * cap + base + r) * kKvRowU4 + part] = v;
+            if (r == n - 1) recent_layer[(int64_t)b * kKvRowU4 + part] = v;
         }
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) ntok_layer[b] = base + (int32_t)n;
@@ -164,16 +170,16 @@ __global__ __launch_bounds__(256) void k_append_rows_c8(const uint16_t* __restri
 
 hipError_t launch_append_rows_c8(hipStream_t st, const uint16_t* idx_src, const uint16_t* kv_src,
                                  uint8_t* idx_layer, uint16_t* scales_layer, uint16_t* pool_layer,
-                                 int32_t* ntok_layer, int seq0, int nseq, int64_t n, int64_t cap,
-                                 int64_t ntiles, int32_t base) {
+                                 uint16_t* recent_layer, int32_t* ntok_layer, int seq0, int nseq, int64_t n,
+                                 int64_t cap, int64_t ntiles, int32_t base) {
     const int64_t by_rows = (n + 3) / 4;
     const int64_t by_kv = kv_src ? (n * kKvRowU4 + 255) / 256 : 1;
     int gx = (int)std::min<int64_t>(std::max(by_rows, by_kv), 4096);
     if (gx < 1) gx = 1;
     hipLaunchKernelGGL(k_append_rows_c8, dim3(gx, nseq), dim3(256), 0, st, idx_src,
                        reinterpret_cast<const uint4*>(kv_src), reinterpret_cast<uint32_t*>(idx_layer),
-                       scales_layer, reinterpret_cast<uint4*>(pool_layer), ntok_layer, seq0, n, cap, ntiles,
-                       base);
+                       scales_layer, reinterpret_cast<uint4*>(pool_layer), reinterpret_cast<uint4*>(recent_layer),
+                       ntok_layer, seq0, n, cap, ntiles, base);
     return hipGetLastError();
 }
 

@@ -87,16 +87,18 @@ struct GatherEntry {
 };
 
 // Launchers.  All enqueue on `st`; none synchronizes.
+// recent_layer [B][576]: the device copy of each sequence's newest main-KV
+// row (written with the last appended row when kv_src is given).
 hipError_t launch_append_rows(hipStream_t st, const uint16_t* idx_src, const uint16_t* kv_src,
-                              uint16_t* idx_layer, uint16_t* pool_layer, int32_t* ntok_layer,
-                              int seq0, int nseq, int64_t n, int64_t cap, int64_t ntiles,
+                              uint16_t* idx_layer, uint16_t* pool_layer, uint16_t* recent_layer,
+                              int32_t* ntok_layer, int seq0, int nseq, int64_t n, int64_t cap, int64_t ntiles,
                               int32_t base);
 // The same for the int8 indexer: each bf16 indexer row is rotated and
 // quantized into its codes (idx_layer in the int8 layout) and fp16 scale.
 hipError_t launch_append_rows_c8(hipStream_t st, const uint16_t* idx_src, const uint16_t* kv_src,
                                  uint8_t* idx_layer, uint16_t* scales_layer, uint16_t* pool_layer,
-                                 int32_t* ntok_layer, int seq0, int nseq, int64_t n, int64_t cap,
-                                 int64_t ntiles, int32_t base);
+                                 uint16_t* recent_layer, int32_t* ntok_layer, int seq0, int nseq, int64_t n,
+                                 int64_t cap, int64_t ntiles, int32_t base);
 // keys may be null (keys are then not stored); candidates (key, token |
 // miss << 31) with first digit >= floor_layer[row] go to
 // pre[row][0 .. meta[row].pre_count).  scales_layer non-null: the int8
@@ -126,16 +128,19 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int B, int D, int top_k, int S, int64_t cap, int32_t t,
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
                             GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
-                            uint32_t* miss_bits, const uint16_t* pool_layer, uint16_t* stage_rows, int32_t* stage_idx,
-                            int32_t* stage_cnt, int64_t max_tokens_now);
+                            uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
+                            uint16_t* stage_rows, int32_t* stage_idx, int32_t* stage_cnt, int64_t max_tokens_now);
 // (miss_bits non-null: the launch also holds copy blocks that move the rows
 // marked in miss_bits [B][wpr] from the pool into stage_rows [B][D*k][576],
 // any order, record stage_idx[b][token], count into stage_cnt[b] and clear
-// the bits: the early miss copy, overlapping the LRU update.)
+// the bits: the early miss copy, overlapping the LRU update.)  In every copy
+// the newest token's row comes from recent_layer [B][576] instead of the
+// pool.
 // Late copy from the pool into the slots.  Work list: sequence b's entries
 // are glist[b * D*k + r], r < counts[b][2].
 hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const int32_t* counts,
-                                const uint16_t* pool_layer, uint16_t* hot_layer, int B, int mstride,
+                                const uint16_t* pool_layer, const uint16_t* recent_layer,
+                                const int32_t* ntok_layer, uint16_t* hot_layer, int B, int64_t cap, int mstride,
                                 int max_entries);
 // Resolves split threshold buckets, one row per block (for the early copy,
 // so that the miss bitmap is complete before the merge launch).
@@ -150,7 +155,8 @@ hipError_t launch_topk_refine(hipStream_t st, RowMeta* meta, const uint2* cand, 
 // the row into its slot, and stage_cnt is reset.
 hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_t* cache_slots_layer,
                                uint16_t* hot_layer, const uint16_t* q_attn, const uint16_t* pool_layer,
-                               const int32_t* ntok_layer, float* part_acc, float* part_ml,
+                               const uint16_t* recent_layer, const int32_t* ntok_layer, float* part_acc,
+                               float* part_ml,
                                int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
                                int rows_per_block, float scale, const uint16_t* stage_rows,
                                int32_t* stage_idx, int32_t* stage_cnt);
