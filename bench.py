@@ -56,6 +56,23 @@ def measure_h2d_ceiling(torch, nbytes: int = 1 << 30, reps: int = 5) -> float:
     return best
 
 
+def measure_hbm_copy(torch, nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Device-to-device copy rate (GB/s, bytes read + written) of a 1 GiB
+    buffer: a measured HBM ceiling beside the 8 TB/s vendor peak."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        best = max(best, 2 * nbytes / (time.perf_counter() - t0) / 1e9)
+    del src, dst
+    return best
+
+
 def calibration_copy(torch) -> None:
     """One plain device-to-device copy of CALIB_COPY_BYTES, so that a counter
     run of this script also holds a kernel with known bytes read and written
@@ -206,8 +223,12 @@ def main() -> int:
     # every stage bracketed by events (the per-stage breakdown; each event
     # pair costs device time, so the timed steps bracket only one stage).
     nstage = sko.sko_num_stages()
+    stats_cold0 = [h.stats(l) for l in range(L)]
+    torch.cuda.synchronize()
+    t_cold = time.perf_counter()
     run_step(0)
     torch.cuda.synchronize()
+    t_cold = time.perf_counter() - t_cold
     calib_stats0 = [h.stats(l) for l in range(L)]
     h.set_timing(0 if args.no_timing else (1 << nstage) - 1)
     for t in range(1, args.warmup):
@@ -273,6 +294,7 @@ def main() -> int:
         return {"late": "late", "fused": "fused"}.get(args.copy, "early")
 
     h2d_ceiling = measure_h2d_ceiling(torch)
+    hbm_copy = measure_hbm_copy(torch)
     calibration_copy(torch)
 
     def roof_entry(name, ms, n, model):
@@ -327,6 +349,11 @@ def main() -> int:
                                   if e.get("bound") == "host-link"), None),
         "miss_copy": copy_mode(calib) if calib else None,
         "h2d_ceiling_GBps": round(h2d_ceiling, 2),
+        "hbm_copy_GBps": round(hbm_copy, 1),
+        # the first step finds an empty shelf (every winner a miss); it is
+        # not in `value`
+        "cold_step": {"ms": round(t_cold * 1e3, 3), "layer_steps_per_s": round(L / t_cold, 1),
+                      "h2d_bytes_per_layer_step": int(deltas(stats_cold0, calib_stats0)["h2d_bytes"] / L)},
         "hit_rate": round(d["hits"] / max(1, d["unique"]), 4),
         "unique_misses_per_layer_step": round(d["misses"] / layer_steps, 1),
         "h2d_bytes_per_layer_step": int(d["h2d_bytes"] / layer_steps),
