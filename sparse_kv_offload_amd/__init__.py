@@ -50,6 +50,10 @@ EXPORTED = (
     "sko_create", "sko_set_stream", "sko_append_token", "sko_decode_step", "sko_read_step",
     "sko_read_table", "sko_get_stats", "sko_set_timing", "sko_get_timing", "sko_stage_name",
     "sko_num_stages", "sko_destroy", "sko_last_error", "sko_version",
+    # layerwise prefill offload (include/sko_prefill.h)
+    "sko_prefill_plan", "sko_prefill_create", "sko_prefill_destroy", "sko_prefill_host_pool",
+    "sko_prefill_set_tokens", "sko_prefill_begin_layer", "sko_prefill_end_layer", "sko_prefill_sync",
+    "sko_prefill_layer_timing", "sko_prefill_get_plan",
 )
 
 
@@ -68,6 +72,18 @@ class SkoConfig(ctypes.Structure):
         ("attn_scale", ctypes.c_float),
         ("device", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+    ]
+
+
+class SkoPrefillConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("shared_buffers", ctypes.c_int32),
+        ("lookahead", ctypes.c_int32),
+        ("row_bytes", ctypes.c_int32),
+        ("capacity_tokens", ctypes.c_int64),
+        ("device", ctypes.c_int32),
+        ("independent", ctypes.c_void_p),
     ]
 
 
@@ -110,6 +126,17 @@ def _load() -> ctypes.CDLL:
         "sko_destroy": (None, [vp]),
         "sko_last_error": (ctypes.c_char_p, []),
         "sko_version": (ctypes.c_char_p, []),
+        "sko_prefill_plan": (ctypes.c_int, [i32, vp, vp, i32, vp, vp, vp]),
+        "sko_prefill_create": (ctypes.c_int, [ctypes.POINTER(SkoPrefillConfig), vp, ctypes.POINTER(vp)]),
+        "sko_prefill_destroy": (ctypes.c_int, [vp]),
+        "sko_prefill_host_pool": (ctypes.c_int, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i64)]),
+        "sko_prefill_set_tokens": (ctypes.c_int, [vp, i32, i64]),
+        "sko_prefill_begin_layer": (ctypes.c_int, [vp, i32, ctypes.POINTER(vp)]),
+        "sko_prefill_end_layer": (ctypes.c_int, [vp, i32, i64]),
+        "sko_prefill_sync": (ctypes.c_int, [vp]),
+        "sko_prefill_layer_timing": (ctypes.c_int, [vp, i32, ctypes.POINTER(ctypes.c_float),
+                                                    ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
+        "sko_prefill_get_plan": (ctypes.c_int, [vp, vp, ctypes.POINTER(i32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -320,3 +347,128 @@ class SparseKVOffload:
 
 __all__ = [n for n in globals() if n.startswith(("sko_", "SKO_", "Sko"))] + [
     "SparseKVOffload", "make_config", "LIB_PATH", "EXPORTED"]
+
+
+# ------------------------------------------------------------ prefill offload
+
+def sko_prefill_plan(specs, independent, shared: int, layer_bytes):
+    """Buffer of every layer and the number of physical buffers."""
+    n = len(specs)
+    sp = np.ascontiguousarray(specs, dtype=np.int32)
+    ind = np.ascontiguousarray(independent, dtype=np.int32)
+    lb = np.ascontiguousarray(layer_bytes, dtype=np.int64)
+    if ind.size != n or lb.size != n:
+        raise ValueError("specs, independent and layer_bytes need one entry per layer")
+    out = np.zeros(max(n, 1), dtype=np.int32)
+    nphys = ctypes.c_int32(0)
+    _check(_lib.sko_prefill_plan(n, _addr(sp), _addr(ind), int(shared), _addr(lb), _addr(out),
+                                 ctypes.byref(nphys)), "sko_prefill_plan")
+    return out[:n].copy(), int(nphys.value)
+
+
+def sko_prefill_create(cfg: SkoPrefillConfig, stream=None) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(_lib.sko_prefill_create(ctypes.byref(cfg), _stream_handle(stream), ctypes.byref(h)),
+           "sko_prefill_create")
+    return h
+
+
+def sko_prefill_destroy(h) -> None:
+    _lib.sko_prefill_destroy(h)
+
+
+def sko_prefill_host_pool(h, layer: int):
+    """(host address of the layer's rows, tokens held)."""
+    p, t = ctypes.c_void_p(), ctypes.c_int64()
+    _check(_lib.sko_prefill_host_pool(h, layer, ctypes.byref(p), ctypes.byref(t)), "sko_prefill_host_pool")
+    return int(p.value), int(t.value)
+
+
+def sko_prefill_set_tokens(h, layer: int, tokens: int) -> None:
+    _check(_lib.sko_prefill_set_tokens(h, layer, tokens), "sko_prefill_set_tokens")
+
+
+def sko_prefill_begin_layer(h, layer: int) -> int:
+    p = ctypes.c_void_p()
+    _check(_lib.sko_prefill_begin_layer(h, layer, ctypes.byref(p)), "sko_prefill_begin_layer")
+    return int(p.value)
+
+
+def sko_prefill_end_layer(h, layer: int, new_tokens: int) -> None:
+    _check(_lib.sko_prefill_end_layer(h, layer, new_tokens), "sko_prefill_end_layer")
+
+
+def sko_prefill_sync(h) -> None:
+    _check(_lib.sko_prefill_sync(h), "sko_prefill_sync")
+
+
+def sko_prefill_layer_timing(h, layer: int):
+    a, w, c = ctypes.c_float(), ctypes.c_float(), ctypes.c_float()
+    _check(_lib.sko_prefill_layer_timing(h, layer, ctypes.byref(a), ctypes.byref(w), ctypes.byref(c)),
+           "sko_prefill_layer_timing")
+    return float(a.value), float(w.value), float(c.value)
+
+
+def sko_prefill_get_plan(h, num_layers: int):
+    out = np.zeros(num_layers, dtype=np.int32)
+    n = ctypes.c_int32(0)
+    _check(_lib.sko_prefill_get_plan(h, _addr(out), ctypes.byref(n)), "sko_prefill_get_plan")
+    return out, int(n.value)
+
+
+class PrefillOffload:
+    """Owns one sko_prefill_handle (include/sko_prefill.h)."""
+
+    def __init__(self, num_layers: int, shared_buffers: int, lookahead: int, row_bytes: int,
+                 capacity_tokens: int, independent=None, stream=None, device: int = 0):
+        self._ind = None if independent is None else np.ascontiguousarray(independent, dtype=np.int32)
+        cfg = SkoPrefillConfig(num_layers, shared_buffers, lookahead, row_bytes, capacity_tokens, device,
+                               None if self._ind is None else self._ind.ctypes.data)
+        self.handle = sko_prefill_create(cfg, stream)
+        self.num_layers, self.row_bytes, self.capacity = num_layers, row_bytes, capacity_tokens
+
+    def close(self) -> None:
+        if self.handle:
+            sko_prefill_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def host_pool(self, layer: int) -> np.ndarray:
+        """The layer's pinned host rows as a numpy view [capacity][row_bytes] (uint8)."""
+        addr, _ = sko_prefill_host_pool(self.handle, layer)
+        buf = (ctypes.c_uint8 * (self.capacity * self.row_bytes)).from_address(addr)
+        return np.frombuffer(buf, dtype=np.uint8).reshape(self.capacity, self.row_bytes)
+
+    def tokens(self, layer: int) -> int:
+        return sko_prefill_host_pool(self.handle, layer)[1]
+
+    def set_tokens(self, layer: int, tokens: int) -> None:
+        sko_prefill_set_tokens(self.handle, layer, tokens)
+
+    def begin_layer(self, layer: int) -> int:
+        """Device address of the layer's buffer (its KV first)."""
+        return sko_prefill_begin_layer(self.handle, layer)
+
+    def end_layer(self, layer: int, new_tokens: int) -> None:
+        sko_prefill_end_layer(self.handle, layer, new_tokens)
+
+    def sync(self) -> None:
+        sko_prefill_sync(self.handle)
+
+    def layer_timing(self, layer: int):
+        """(load_ms, exposed_ms, compute_ms) of the layer in the last pass."""
+        return sko_prefill_layer_timing(self.handle, layer)
+
+    def plan(self):
+        return sko_prefill_get_plan(self.handle, self.num_layers)

@@ -38,6 +38,18 @@ int set_err(int code, const char* fmt, ...) {
     return code;
 }
 
+}  // namespace
+
+namespace sko {
+// The library's last error message (also for the prefill calls).
+int set_error(int code, const char* msg) {
+    g_err = msg;
+    return code;
+}
+}  // namespace sko
+
+namespace {
+
 enum Stage {
     ST_APPEND = 0,
     ST_SCORE,

@@ -52,6 +52,9 @@ __host__ __device__ inline size_t idx_c8_tile_u4(size_t seq_tiles_base, int64_t 
            (size_t)(token % kIdxTile);
 }
 
+// Sets the message sko_last_error() returns; returns code.
+int set_error(int code, const char* msg);
+
 // Per (seq, position) row of the top-k selection.
 struct RowMeta {
     int32_t bucket;        // first-digit bucket holding the k-th largest key (-1: none)
