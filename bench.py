@@ -140,6 +140,83 @@ def cpu_baseline(w, target_s: float) -> dict:
                       f"(cold step included), {elapsed:.1f} s single-threaded"}
 
 
+class _DeviceBytes:
+    """A device address seen by torch as a uint8 tensor (no copy)."""
+
+    def __init__(self, ptr: int, nbytes: int):
+        self.__cuda_array_interface__ = {"shape": (nbytes,), "typestr": "|u1", "data": (ptr, False),
+                                         "version": 3, "strides": None, "stream": None}
+
+
+def prefill_bench(args) -> int:
+    """Layerwise prefill offload: N layers, B0 bound to layer 0, three
+    rotating trays; each pass loads every layer's cached prefix (host ->
+    device), runs a stand-in for the layer's compute of a chosen duration on
+    the compute stream (a timed spin kernel), writes the chunk's new rows and
+    saves them (device -> host).  Reports the measured exposed delay per
+    layer next to the model max(0, load - compute of the previous layer)."""
+    import torch
+    import sparse_kv_offload_amd as sko
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    N, row, prefix, chunk = args.prefill_layers, 1152, args.prefill_prefix, args.prefill_chunk
+    passes = 2
+    cap = prefix + passes * chunk
+    # calibrate the spin kernel: cycles per millisecond
+    torch.cuda._sleep(1000000)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    torch.cuda._sleep(50000000)
+    torch.cuda.synchronize()
+    cyc_per_ms = 50000000 / ((time.perf_counter() - t0) * 1e3)
+    rows = torch.randint(0, 256, (chunk * row,), dtype=torch.uint8, device="cuda")
+    results = []
+    with sko.PrefillOffload(N, 3, 1, row, cap, independent=[1] + [0] * (N - 1), stream=stream) as pf:
+        rng = np.random.default_rng(5)
+        pat = rng.integers(0, 256, size=(min(prefix, 4096), row), dtype=np.uint8)
+        for l in range(N):
+            hp = pf.host_pool(l)
+            for r0 in range(0, prefix, pat.shape[0]):
+                m = min(pat.shape[0], prefix - r0)
+                hp[r0:r0 + m] = pat[:m]
+            pf.set_tokens(l, prefix)
+        load_ms_est = prefix * row / 55e9 * 1e3
+        for frac in args.prefill_compute:
+            comp_ms = frac * load_ms_est
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for l in range(N):
+                ptr = pf.begin_layer(l)
+                if comp_ms > 0:
+                    torch.cuda._sleep(int(comp_ms * cyc_per_ms))
+                P_l = pf.tokens(l)
+                buf = torch.as_tensor(_DeviceBytes(ptr, cap * row), device="cuda")
+                buf[P_l * row:(P_l + chunk) * row].copy_(rows)
+                pf.end_layer(l, chunk)
+            pf.sync()
+            wall = time.perf_counter() - t0
+            t = [pf.layer_timing(l) for l in range(N)]
+            load = [x[0] for x in t]
+            exp = [x[1] for x in t]
+            comp = [x[2] for x in t]
+            model = [max(0.0, load[l] - comp[l - 1]) if l > 0 else load[0] for l in range(N)]
+            results.append({"compute_ms_per_layer": round(float(np.mean(comp[1:])), 3),
+                            "load_ms_per_layer": round(float(np.mean(load[1:])), 3),
+                            "load_GBps": round(prefix * row / (np.mean(load[1:]) * 1e-3) / 1e9, 2),
+                            "exposed_ms_sum": round(float(sum(exp[1:])), 3),
+                            "model_exposed_ms_sum": round(float(sum(model[1:])), 3),
+                            "pass_ms": round(wall * 1e3, 2),
+                            "pass_ms_if_resident": round(float(sum(comp)), 2)})
+            # the next setting starts from the same prefix
+            for l in range(N):
+                pf.set_tokens(l, prefix)
+    print(json.dumps({"metric": "layerwise prefill offload: exposed transfer delay per pass",
+                      "unit": "ms", "layers": N, "row_bytes": row, "prefix_tokens": prefix,
+                      "chunk_tokens": chunk, "trays": "B0 bound to layer 0 + 3 rotating", "lookahead": 1,
+                      "tray_footprint_ratio": round(4 / N, 4), "settings": results}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,12 +235,21 @@ def main() -> int:
                     help="miss-copy arrangement: early (the default: by extra blocks of the LRU-update launch, "
                          "into staging), late (after the LRU update), fused (inside the attention launch; one "
                          "position, at most 16 heads)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="measure the layerwise prefill offload pipeline instead of the decode step")
+    ap.add_argument("--prefill-layers", type=int, default=78)
+    ap.add_argument("--prefill-prefix", type=int, default=32768)
+    ap.add_argument("--prefill-chunk", type=int, default=4096)
+    ap.add_argument("--prefill-compute", type=float, nargs="+", default=[0.0, 0.5, 1.0, 2.0],
+                    help="compute per layer as multiples of the estimated load time")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the offload step is "
               "per-GPU and this build has no multi-GPU path", file=sys.stderr)
         return 2
+    if args.prefill:
+        return prefill_bench(args)
 
     import torch
     import synth
