@@ -92,8 +92,9 @@ KERNEL_SOURCE = {"score_hist": "select.hip", "gather_misses": "gather.hip", "mer
 
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary of this kernel
-    and workload, or None when there is none or the kernel's source changed
-    since the counters were taken (the summary records the source digest)."""
+    and workload, or None when there is none or the kernel's source or the
+    runtime (its launch shape) changed since the counters were taken (the
+    summary records a digest of both)."""
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
@@ -106,8 +107,10 @@ def traffic_for(kernel: str, workload: str):
     entry = json.loads(m.group(1)).get(kernel)
     if not entry:
         return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if entry.get("source_sha256_16") != digest:
+    # the kernel's source and the runtime that sets its launch shape
+    h = hashlib.sha256(open(src, "rb").read())
+    h.update(open(os.path.join(ROOT, "sparse_kv_offload_amd", "csrc", "runtime.hip"), "rb").read())
+    if entry.get("source_sha256_16") != h.hexdigest()[:16]:
         return None
     return entry.get("hbm_bytes_per_launch")
 
