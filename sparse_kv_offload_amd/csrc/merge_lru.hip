@@ -555,9 +555,14 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
 // from the top on the 52-bit composite, 8 bits per pass, over the staged
 // bucket entries (in LDS when they fit); the entries with composite >= T
 // are appended to the row's winners and marked in the winner bitmap, and
-// in the miss bitmap when they are absent from the hot buffer.
+// in the miss bitmap when they are absent from the hot buffer.  The filter
+// launch has completed, so the row's winner count is final: a staged row
+// places its winners with one block scan (no global atomics), and its
+// entries are loaded all at once, before the row's counts are known
+// (clamped to the row, which holds cap entries).
 constexpr int kRefineThreads = 256;
-constexpr int kRefineStage = 4096;
+constexpr int kRefinePer = 16;
+constexpr int kRefineStage = kRefineThreads * kRefinePer;
 
 __global__ __launch_bounds__(kRefineThreads) void k_topk_refine(RowMeta* __restrict__ meta,
                                                                 const uint2* __restrict__ cand,
@@ -569,16 +574,28 @@ __global__ __launch_bounds__(kRefineThreads) void k_topk_refine(RowMeta* __restr
     __shared__ uint32_t hg[256];
     __shared__ uint64_t s_prefix, s_T;
     __shared__ int s_rem, s_done;
+    __shared__ int scratch[kRefineThreads / 64 + 1];
     const int row = blockIdx.x;
     const int b = row / D;
     const int tid = threadIdx.x, lane = tid & 63;
+    const uint2* __restrict__ cg = cand + (size_t)row * cap;
+    uint2 pre[kRefinePer];
+#pragma unroll
+    for (int j = 0; j < kRefinePer; ++j) {
+        const int64_t i = tid + (int64_t)kRefineThreads * j;
+        pre[j] = cg[i < cap ? i : cap - 1];
+    }
     const RowMeta m = meta[row];
     if (m.bucket < 0 || m.need <= 0 || m.need == m.bucket_count) return;  // block-uniform
     const int c = (int)std::min<int64_t>(m.cand_count, cap);
-    const uint2* __restrict__ cg = cand + (size_t)row * cap;
     const bool staged = c <= kRefineStage;
-    if (staged)
-        for (int i = tid; i < c; i += kRefineThreads) sg[i] = cg[i];
+    if (staged) {
+#pragma unroll
+        for (int j = 0; j < kRefinePer; ++j) {
+            const int i = tid + kRefineThreads * j;
+            if (i < c) sg[i] = pre[j];
+        }
+    }
     if (tid == 0) {
         s_prefix = 0;
         s_T = 0;
@@ -642,18 +659,34 @@ __global__ __launch_bounds__(kRefineThreads) void k_topk_refine(RowMeta* __restr
     const uint64_t T = s_T;
     uint32_t* __restrict__ wb = winners + (size_t)b * wpr;
     uint32_t* __restrict__ mb = miss_bits ? miss_bits + (size_t)b * wpr : nullptr;
+    auto take = [&](uint2 e, int pw) {
+        const uint32_t tok = e.y & 0x7FFFFFFFu;
+        if (pw < top_k) topk[(size_t)row * top_k + pw] = (int32_t)e.y;
+        atomicOr(&wb[tok >> 5], 1u << (tok & 31u));
+        if (mb && (e.y & 0x80000000u)) atomicOr(&mb[tok >> 5], 1u << (tok & 31u));
+    };
+    if (staged) {
+        uint32_t wmask = 0u;
+#pragma unroll
+        for (int j = 0; j < kRefinePer; ++j) {
+            const int i = tid + kRefineThreads * j;
+            if (i < c && refine_composite(pre[j]) >= T) wmask |= 1u << j;
+        }
+        int total;
+        int pw = m.out_count + block_exclusive_scan<kRefineThreads>(__popc(wmask), &total, scratch);
+#pragma unroll
+        for (int j = 0; j < kRefinePer; ++j)
+            if ((wmask >> j) & 1u) take(pre[j], pw++);
+        if (tid == 0) meta[row].out_count = m.out_count + total;
+        return;
+    }
     for (int base = 0; base < c; base += kRefineThreads) {
         const int i = base + tid;
         const bool valid = i < c;
-        const uint2 e = valid ? (staged ? sg[i] : cg[i]) : make_uint2(0u, 0u);
+        const uint2 e = valid ? cg[i] : make_uint2(0u, 0u);
         const bool win = valid && refine_composite(e) >= T;
         const int pw = wave_append(&meta[row].out_count, win);
-        if (win && pw < top_k) {
-            const uint32_t tok = e.y & 0x7FFFFFFFu;
-            topk[(size_t)row * top_k + pw] = (int32_t)e.y;
-            atomicOr(&wb[tok >> 5], 1u << (tok & 31u));
-            if (mb && (e.y & 0x80000000u)) atomicOr(&mb[tok >> 5], 1u << (tok & 31u));
-        }
+        if (win) take(e, pw);
     }
 }
 
