@@ -238,6 +238,9 @@ def main() -> int:
                     help="miss-copy arrangement: early (the default: by extra blocks of the LRU-update launch, "
                          "into staging), late (after the LRU update), fused (inside the attention launch; one "
                          "position, at most 16 heads)")
+    ap.add_argument("--hit-overlap", action="store_true",
+                    help="with the early copy: attend the resident rows on a side stream beside the copy launch, "
+                         "the missed rows after it")
     ap.add_argument("--prefill", action="store_true",
                     help="measure the layerwise prefill offload pipeline instead of the decode step")
     ap.add_argument("--prefill-layers", type=int, default=78)
@@ -274,6 +277,8 @@ def main() -> int:
               "fused": sko.SKO_FLAG_FUSED_COPY}[args.copy]
     if args.indexer == "c8":
         flags |= sko.SKO_FLAG_INDEXER_C8
+    if args.hit_overlap:
+        flags |= sko.SKO_FLAG_HIT_OVERLAP
     cfg = sko.make_config(num_layers=L, batch=B, max_tokens=w.capacity, num_heads=H, top_k=k,
                           hot_slots=w.hot_slots, mtp_positions=D, flags=flags)
     h = sko.SparseKVOffload(cfg, stream)
@@ -431,6 +436,7 @@ def main() -> int:
         "config": {"workload": w.name, "layers": L, "batch": B, "context": w.context,
                    "top_k": k, "hot_slots": w.hot_slots, "mtp_positions": D, "heads": H,
                    "parallelism": "none (1 GPU)", "pool": args.pool, "copy": args.copy,
+                   "hit_overlap": bool(args.hit_overlap),
                    "indexer": args.indexer},
         "tokens_per_s": round(B * K / elapsed, 2),
         "indexer_scan_GBps": rooflines.get("score_hist", {}).get("achieved"),

@@ -93,6 +93,18 @@ extern "C" {
  * int32 sum of code products; the selection, residency, LRU and attention
  * are unchanged.  Halves the indexer bytes the score pass reads. */
 #define SKO_FLAG_INDEXER_C8 0x80u
+/* With the early copy: the attention is split by residency at step start.
+ * The rows that were resident (hits) are attended on an internal stream,
+ * forked from the caller's stream once the selection is known, while the
+ * LRU-update launch copies the misses in (the overlap of the fused Copy-SFA
+ * operator of [LSO-zh] §4: attention on resident rows while the missing
+ * rows are in flight); the rows that missed are attended after that launch,
+ * and the combine, after the join, merges both phases' partials.  A hit's
+ * slot and row do not change during the step (victims are slots not hit at
+ * this step), so both phases read what the unsplit attention reads; the
+ * output differs only in fp32 summation order.  SKO_E_INVAL with
+ * SKO_FLAG_FUSED_COPY or SKO_FLAG_LATE_COPY. */
+#define SKO_FLAG_HIT_OVERLAP 0x100u
 
 typedef struct sko_handle sko_handle;
 
@@ -191,7 +203,9 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
  * -> remap -> attention ([LSO] §4 "Decode step" items 3-7).  The gather
  * is done early (by extra blocks of the LRU-update launch), late, or inside
  * the attention launch, see SKO_FLAG_EARLY_COPY.  Everything runs on the
- * caller's stream.
+ * caller's stream (with SKO_FLAG_HIT_OVERLAP, part of the attention runs on
+ * an internal stream that is forked from and joined back into it by events
+ * within the call's stream order).
  *   q_idx   device [B][D][64] bf16 indexer queries
  *   q_attn  device [B][D][H][576] bf16 attention queries
  *   out     device [B][D][H][512] fp32 attention output

@@ -49,7 +49,13 @@ __device__ __forceinline__ uint32_t dword_of(uint4 v, int m) {
 // How the launch gets the rows that missed into their slots.
 enum AttnCopy { kCopyNone = 0, kCopyPool = 1, kCopyStaged = 2 };
 
-template <int COPY>
+// Which rows of a chunk a launch attends: all of them, only those resident
+// at step start (hits), or only those that missed.  A split runs the hits
+// while the copy launch brings the misses in, and the misses after it; each
+// phase writes its own partials, the combine merges both.
+enum AttnPhase { kPhaseAll = 0, kPhaseHits = 1, kPhaseMisses = 2 };
+
+template <int COPY, int PHASE>
 __global__ __launch_bounds__(256) void k_attn_partial(
     const int32_t* __restrict__ topk, const int32_t* __restrict__ cache_slots_layer,
     uint4* __restrict__ hot_layer, const uint4* __restrict__ q_attn, const uint4* __restrict__ pool_layer,
@@ -57,11 +63,12 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     const int32_t* __restrict__ ntok_layer, float* __restrict__ part_acc,
     float* __restrict__ part_ml, int32_t* __restrict__ phys, const uint4* __restrict__ stage_rows,
     int32_t* __restrict__ stage_idx, int32_t* __restrict__ stage_cnt, int B, int D, int H, int HG,
-    int top_k, int S, int64_t cap, int rows_per_block, int nchunk, float scale_log2) {
+    int top_k, int S, int64_t cap, int rows_per_block, int nchunk, int pchunks, float scale_log2) {
     __shared__ uint4 rows[kAttnTileRows * kRowStrideU4];
     __shared__ int32_t slot_s[kAttnMaxRowsPerBlock];  // row read, relative to the sequence's hot rows
     __shared__ int32_t cp_s[kAttnMaxRowsPerBlock];    // copy: pool token (fused) or victim slot (staged), else -1
     __shared__ f32x4_t sp[4][2][64];  // per-wave partial S^T tiles
+    __shared__ int scratch[256 / 64 + 1];
 
     const int chunk = blockIdx.x, bp = blockIdx.y, hg = blockIdx.z;
     const int b = bp / D;
@@ -70,7 +77,9 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     const int kk = (int)std::min<int64_t>(top_k, Lt);
     const int r0 = chunk * rows_per_block;
     const int r1 = std::min(r0 + rows_per_block, kk);
-    const size_t pidx = ((size_t)bp * HG + hg) * nchunk + chunk;
+    // partials of the chunk: pchunks per (seq, position, head group), the
+    // misses phase after the hits phase's nchunk
+    const size_t pidx = ((size_t)bp * HG + hg) * pchunks + (PHASE == kPhaseMisses ? nchunk : 0) + chunk;
     float* __restrict__ acc_out = part_acc + pidx * kAttnHeadGroup * kVDim;
     float* __restrict__ ml_out = part_ml + pidx * kAttnHeadGroup * 2;
     constexpr bool fused_copy = COPY == kCopyPool;
@@ -95,9 +104,25 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     // staging area lies in the same allocation, after every layer's rows)
     const int64_t stage_base = staged ? (stage_rows - hb) / kKvRowU4 + (int64_t)b * D * top_k : 0;
 
-    // remap: logical winner -> hot slot, for the whole chunk
-    for (int j = tid; j < r1 - r0; j += 256) {
-        const int32_t packed = w[r0 + j];
+    // remap: logical winner -> hot slot, for the chunk's rows of this phase,
+    // compacted in winner order (rows 0 .. n-1 of the block)
+    constexpr int kRowsPerThread = kAttnMaxRowsPerBlock / 256;
+    int32_t pk[kRowsPerThread];
+    int nmine = 0;
+#pragma unroll
+    for (int u = 0; u < kRowsPerThread; ++u) {
+        const int j = tid * kRowsPerThread + u;
+        pk[u] = (j < r1 - r0) ? w[r0 + j] : 0;
+        const bool in = j < r1 - r0 && (PHASE == kPhaseAll || (PHASE == kPhaseHits) == (pk[u] >= 0));
+        nmine += in ? 1 : 0;
+    }
+    int n;
+    int q = block_exclusive_scan<256>(nmine, &n, scratch);
+#pragma unroll
+    for (int u = 0; u < kRowsPerThread; ++u) {
+        const int j = tid * kRowsPerThread + u;
+        const int32_t packed = pk[u];
+        if (!(j < r1 - r0 && (PHASE == kPhaseAll || (PHASE == kPhaseHits) == (packed >= 0)))) continue;
         const int32_t tok = packed & 0x7FFFFFFF;
         int32_t slot = (tok < cap) ? cs[tok] : -1;
         if (slot >= S) slot = -1;
@@ -111,9 +136,17 @@ __global__ __launch_bounds__(256) void k_attn_partial(
                 if (!(old & kStageClaimed)) cp = slot;
             }
         }
-        slot_s[j] = rd;
-        cp_s[j] = cp;
+        slot_s[q] = rd;
+        cp_s[q] = cp;
+        ++q;
         if (hg == 0) phys[(size_t)bp * top_k + r0 + j] = slot;
+    }
+    if (n == 0) {  // block-uniform: no rows of this phase in the chunk
+        if (tid < kAttnHeadGroup) {
+            ml_out[2 * tid] = -INFINITY;
+            ml_out[2 * tid + 1] = 0.0f;
+        }
+        return;
     }
 
     // Fused: the missed rows of this chunk are copied from the pool into
@@ -126,7 +159,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         __syncthreads();
         // one row in flight per wave: more outstanding host reads lowered
         // the link rate of this scattered access pattern
-        for (int j = wave; j < r1 - r0; j += 4) {
+        for (int j = wave; j < n; j += 4) {
             const int32_t c = cp_s[j];
             const int32_t dst = c >= 0 ? slot_s[j] : -1;
             // (the newest token's row from its device copy)
@@ -178,7 +211,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         const int idx = tid + 256 * u;                                              \
         const int rr = idx / kKvRowU4;                                              \
         const int j = (rbase) + rr;                                                 \
-        const int32_t slot = (j < r1) ? slot_s[j - r0] : -1;                        \
+        const int32_t slot = (j < n) ? slot_s[j] : -1;                              \
         const uint4 v = hb[(size_t)(slot >= 0 ? slot : 0) * kKvRowU4 + (idx - rr * kKvRowU4)]; \
         pre[u] = (slot >= 0) ? v : make_uint4(0u, 0u, 0u, 0u);                      \
     }
@@ -195,17 +228,17 @@ __global__ __launch_bounds__(256) void k_attn_partial(
             const int idx = tid + 256 * u;                                               \
             const int rr = idx / kKvRowU4;                                               \
             const int j = (rbase) + rr;                                                  \
-            const int32_t c = (j < r1) ? cp_s[j - r0] : -1;                              \
+            const int32_t c = (j < n) ? cp_s[j] : -1;                                    \
             if (c >= 0) hb[(size_t)c * kKvRowU4 + (idx - rr * kKvRowU4)] = pre[u];       \
         }                                                                                \
     }
-    SKO_FETCH(r0)
+    SKO_FETCH(0)
     SKO_STASH()
-    SKO_MOVE(r0)
+    SKO_MOVE(0)
     __syncthreads();
 
-    for (int r = r0; r < r1; r += kAttnTileRows) {
-        const bool more = r + kAttnTileRows < r1;
+    for (int r = 0; r < n; r += kAttnTileRows) {
+        const bool more = r + kAttnTileRows < n;
         if (more) {
             SKO_FETCH(r + kAttnTileRows)
         }
@@ -232,7 +265,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = r + half * 16 + 4 * g + i;
-                s[half][i] = (j < r1) ? c[i] * scale_log2 : -INFINITY;
+                s[half][i] = (j < n) ? c[i] * scale_log2 : -INFINITY;
             }
         }
         // online softmax per head over the 32 rows (lane groups g share a head)
@@ -377,24 +410,31 @@ hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_
                                float* part_ml,
                                int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
                                int rows_per_block, float scale, const uint16_t* stage_rows,
-                               int32_t* stage_idx, int32_t* stage_cnt) {
+                               int32_t* stage_idx, int32_t* stage_cnt, int phase) {
     const int HG = (H + kAttnHeadGroup - 1) / kAttnHeadGroup;
     const int nchunk = (top_k + rows_per_block - 1) / rows_per_block;
+    const int pchunks = phase == 0 ? nchunk : 2 * nchunk;
     const float scale_log2 = scale * 1.4426950408889634f;
-#define SKO_ATTN_LAUNCH(C)                                                                                  \
-    hipLaunchKernelGGL(k_attn_partial<C>, dim3(nchunk, B * D, HG), dim3(256), 0, st, topk, cache_slots_layer,  \
-                       reinterpret_cast<uint4*>(hot_layer), reinterpret_cast<const uint4*>(q_attn),             \
-                       reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<const uint4*>(recent_layer), \
-                       ntok_layer, part_acc, part_ml, phys,                                                     \
+#define SKO_ATTN_LAUNCH(C, P)                                                                                 \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_attn_partial<C, P>), dim3(nchunk, B * D, HG), dim3(256), 0, st, topk,     \
+                       cache_slots_layer, reinterpret_cast<uint4*>(hot_layer),                                   \
+                       reinterpret_cast<const uint4*>(q_attn), reinterpret_cast<const uint4*>(pool_layer),       \
+                       reinterpret_cast<const uint4*>(recent_layer), ntok_layer, part_acc, part_ml, phys,        \
                        reinterpret_cast<const uint4*>(stage_rows), stage_idx, stage_cnt, B, D, H, HG, top_k, S, \
-                       cap, rows_per_block, nchunk, scale_log2)
+                       cap, rows_per_block, nchunk, pchunks, scale_log2)
     if (pool_layer != nullptr && stage_rows != nullptr) return hipErrorInvalidValue;
-    if (pool_layer != nullptr) {
-        SKO_ATTN_LAUNCH(kCopyPool);
+    if (phase == 1) {
+        // the rows resident at step start: no copy of any kind
+        SKO_ATTN_LAUNCH(kCopyNone, kPhaseHits);
+    } else if (phase == 2) {
+        if (stage_rows == nullptr) return hipErrorInvalidValue;
+        SKO_ATTN_LAUNCH(kCopyStaged, kPhaseMisses);
+    } else if (pool_layer != nullptr) {
+        SKO_ATTN_LAUNCH(kCopyPool, kPhaseAll);
     } else if (stage_rows != nullptr) {
-        SKO_ATTN_LAUNCH(kCopyStaged);
+        SKO_ATTN_LAUNCH(kCopyStaged, kPhaseAll);
     } else {
-        SKO_ATTN_LAUNCH(kCopyNone);
+        SKO_ATTN_LAUNCH(kCopyNone, kPhaseAll);
     }
 #undef SKO_ATTN_LAUNCH
     return hipGetLastError();

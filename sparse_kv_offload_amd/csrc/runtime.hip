@@ -59,10 +59,12 @@ enum Stage {
     ST_ATTN,
     ST_COMBINE,
     ST_REFINE,
+    ST_ATTN_HITS,
     ST_COUNT
 };
 const char* const kStageNames[ST_COUNT] = {"append_rows",   "score_hist",   "topk_filter",  "merge_lru",
-                                           "gather_misses", "attn_partial", "attn_combine", "topk_refine"};
+                                           "gather_misses", "attn_partial", "attn_combine", "topk_refine",
+                                           "attn_hits"};
 
 struct DeviceGuard {
     int prev = -1;
@@ -96,6 +98,12 @@ struct sko_handle {
     uint16_t* idx_scale = nullptr;  // int8 indexer: fp16 scales [L][B][ntiles * 64]
     uint32_t* qc8 = nullptr;        // int8 indexer: quantized queries [B][D][kQc8Words]
     bool c8 = false;                // the int8 indexer (SKO_FLAG_INDEXER_C8)
+    // SKO_FLAG_HIT_OVERLAP: the attention over resident rows runs on `side`
+    // (forked from the caller's stream after the selection, joined before
+    // the combine) beside the copy launch
+    bool hit_overlap = false;
+    hipStream_t side = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     uint16_t* staging = nullptr;    // device rows for host-source appends
     uint16_t* hot = nullptr;        // [L][B][S][576]
     uint16_t* recent = nullptr;     // [L][B][576] device copy of each sequence's newest main-KV row
@@ -183,6 +191,11 @@ void free_all(sko_handle* h) {
         (void)hipEventDestroy(p.b);
     }
     for (auto e : h->spare) (void)hipEventDestroy(e);
+    if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+    if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+    if (h->side) (void)hipStreamDestroy(h->side);
+    h->ev_fork = h->ev_join = nullptr;
+    h->side = nullptr;
     for (void* p : h->dev_allocs) (void)hipFree(p);
     if (h->pool_host) (void)hipHostFree(h->pool_host);
     h->dev_allocs.clear();
@@ -249,7 +262,7 @@ int validate_config(const sko_config* c) {
         return set_err(SKO_E_INVAL, "attn_scale must be finite and > 0");
     if ((c->flags & ~(SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT | SKO_FLAG_KEEP_KEYS |
                       SKO_FLAG_SELECT_RESCAN | SKO_FLAG_FUSED_COPY | SKO_FLAG_LATE_COPY |
-                      SKO_FLAG_EARLY_COPY | SKO_FLAG_INDEXER_C8)) != 0 ||
+                      SKO_FLAG_EARLY_COPY | SKO_FLAG_INDEXER_C8 | SKO_FLAG_HIT_OVERLAP)) != 0 ||
         (c->flags & (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT)) ==
             (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT))
         return set_err(SKO_E_INVAL, "unknown or conflicting flags 0x%x", c->flags);
@@ -260,6 +273,8 @@ int validate_config(const sko_config* c) {
         if ((modes & SKO_FLAG_FUSED_COPY) && (c->mtp_positions != 1 || c->num_heads > kAttnHeadGroup))
             return set_err(SKO_E_INVAL, "SKO_FLAG_FUSED_COPY needs mtp_positions == 1 and num_heads <= %d",
                            kAttnHeadGroup);
+        if ((c->flags & SKO_FLAG_HIT_OVERLAP) && (modes & (SKO_FLAG_FUSED_COPY | SKO_FLAG_LATE_COPY)))
+            return set_err(SKO_E_INVAL, "SKO_FLAG_HIT_OVERLAP needs the early copy");
     }
     if (c->device < 0) return set_err(SKO_E_INVAL, "device must be >= 0");
     if (c->hot_slots > kMaxHotSlots)
@@ -347,6 +362,9 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     h->fused_copy = (cfg->flags & SKO_FLAG_FUSED_COPY) != 0;
     h->staged_copy = !h->fused_copy && !(cfg->flags & SKO_FLAG_LATE_COPY);
     h->c8 = (cfg->flags & SKO_FLAG_INDEXER_C8) != 0;
+    h->hit_overlap = h->staged_copy && (cfg->flags & SKO_FLAG_HIT_OVERLAP) != 0;
+    // the split attention writes the partials of both phases
+    const size_t pchunks = (size_t)h->nchunk * (h->hit_overlap ? 2 : 1);
 
     const size_t LB = (size_t)h->L * h->B;
     const size_t BD = (size_t)h->B * h->D;
@@ -408,12 +426,21 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     ok = ok && dev_alloc(h, (void**)&h->evict_old, BD * h->k * 4);
     ok = ok && dev_alloc(h, (void**)&h->counts, (size_t)h->B * 8 * 4);
     ok = ok && dev_alloc(h, (void**)&h->glist, BD * h->k * sizeof(GatherEntry));
-    ok = ok && dev_alloc(h, (void**)&h->part_acc, BD * h->HG * h->nchunk * kAttnHeadGroup * kVDim * 4);
-    ok = ok && dev_alloc(h, (void**)&h->part_ml, BD * h->HG * h->nchunk * kAttnHeadGroup * 2 * 4);
+    ok = ok && dev_alloc(h, (void**)&h->part_acc, BD * h->HG * pchunks * kAttnHeadGroup * kVDim * 4);
+    ok = ok && dev_alloc(h, (void**)&h->part_ml, BD * h->HG * pchunks * kAttnHeadGroup * 2 * 4);
     if (!ok) {
         free_all(h);
         delete h;
         return set_err(SKO_E_NOMEM, "device allocation failed");
+    }
+    if (h->hit_overlap &&
+        (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+         hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+         hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess)) {
+        (void)hipGetLastError();
+        free_all(h);
+        delete h;
+        return set_err(SKO_E_DEVICE, "creating the side stream of the hit attention failed");
     }
     // initial state: empty shelf, empty reverse index, no tokens
     hipError_t e = hipSuccess;
@@ -593,6 +620,15 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
                                                  D, k, cap);
                    })))
         return rc;
+    // split attention: the selection is complete, so the rows resident at
+    // step start (whose slots and data the LRU update and the copy leave
+    // alone) are attended on the side stream while the copy launch runs
+    const bool split = staged && h->hit_overlap;
+    if (split) {
+        hipError_t e = hipEventRecord(h->ev_fork, h->stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_fork, 0);
+        if (e != hipSuccess) return device_fail(h, e, "fork of the hit attention");
+    }
     if ((rc = run_stage(h, ST_MERGE_LRU, [&] {
              return launch_merge_lru(h->stream, h->winners, h->hist, h->meta, h->cand, h->topk, ntok, cs, st, lu,
                                      ring0, ring1, ring_pos, ring_state, B, D, k, S, cap, t, h->misses, h->victims,
@@ -608,15 +644,35 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
                                          B, cap, D * k, B * D * k);
          })))
         return rc;
+    if (split) {
+        if ((rc = run_stage(
+                 h, ST_ATTN_HITS,
+                 [&] {
+                     return launch_attn_partial(h->side, h->topk, cs, hot_layer, qa, nullptr, recent_layer, ntok,
+                                                h->part_acc, h->part_ml, h->phys, B, D, H, k, S, cap,
+                                                h->rows_per_block, h->cfg.attn_scale, h->stage_rows, h->stage_idx,
+                                                h->stage_cnt, 1);
+                 },
+                 h->side)))
+            return rc;
+        const hipError_t e = hipEventRecord(h->ev_join, h->side);
+        if (e != hipSuccess) return device_fail(h, e, "join of the hit attention");
+    }
     if ((rc = run_stage(h, ST_ATTN, [&] {
              return launch_attn_partial(h->stream, h->topk, cs, hot_layer, qa, fused_copy ? pool_layer : nullptr,
                                         recent_layer, ntok, h->part_acc, h->part_ml, h->phys, B, D, H, k, S, cap,
                                         h->rows_per_block, h->cfg.attn_scale, staged ? h->stage_rows : nullptr,
-                                        staged ? h->stage_idx : nullptr, staged ? h->stage_cnt : nullptr);
+                                        staged ? h->stage_idx : nullptr, staged ? h->stage_cnt : nullptr,
+                                        split ? 2 : 0);
          })))
         return rc;
+    if (split) {
+        const hipError_t e = hipStreamWaitEvent(h->stream, h->ev_join, 0);
+        if (e != hipSuccess) return device_fail(h, e, "join of the hit attention");
+    }
     if ((rc = run_stage(h, ST_COMBINE, [&] {
-             return launch_attn_combine(h->stream, h->part_acc, h->part_ml, out, B, D, H, h->nchunk);
+             return launch_attn_combine(h->stream, h->part_acc, h->part_ml, out, B, D, H,
+                                        h->nchunk * (split ? 2 : 1));
          })))
         return rc;
     h->step[layer] += 1;
@@ -777,6 +833,7 @@ void sko_destroy(sko_handle* h) {
     {
         DeviceGuard guard(h->cfg.device);
         (void)hipStreamSynchronize(h->stream);
+        if (h->side) (void)hipStreamSynchronize(h->side);
         free_all(h);
     }
     delete h;

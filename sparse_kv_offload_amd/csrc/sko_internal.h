@@ -162,7 +162,7 @@ hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_
                                float* part_ml,
                                int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
                                int rows_per_block, float scale, const uint16_t* stage_rows,
-                               int32_t* stage_idx, int32_t* stage_cnt);
+                               int32_t* stage_idx, int32_t* stage_cnt, int phase);
 hipError_t launch_attn_combine(hipStream_t st, const float* part_acc, const float* part_ml,
                                float* out, int B, int D, int H, int nchunk);
 // Rings of n_seqs sequences: ring0 = 0..S-1, pos = identity, head 0, tail S.

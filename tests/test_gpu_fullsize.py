@@ -81,3 +81,18 @@ def test_mtp3_full_shape_int8_indexer():
     w = synth.MTP3
     _run(w, layers=1, steps=8, chains=[(0, 9)], out_steps=[0, 7], tables_every=7,
          flags=sko.SKO_FLAG_INDEXER_C8)
+
+
+def test_mtp3_full_shape_hit_overlap():
+    """The split attention at the mtp3 shape (four positions, 16 sequences)."""
+    import sparse_kv_offload_amd as sko
+    w = synth.MTP3
+    _run(w, layers=1, steps=10, chains=[(0, 6)], out_steps=[0, 9], tables_every=9,
+         flags=sko.SKO_FLAG_HIT_OVERLAP)
+
+
+def test_small_full_hit_overlap():
+    import sparse_kv_offload_amd as sko
+    w = synth.SMALL
+    _run(w, layers=2, steps=24, chains=[(1, 5)], out_steps=[0, 23], tables_every=12,
+         flags=sko.SKO_FLAG_HIT_OVERLAP)

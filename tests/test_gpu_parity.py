@@ -309,6 +309,36 @@ def test_early_copy_three_positions():
     run_parity(w, check_keys=False, flags=0, log=log)
 
 
+@pytest.mark.parametrize("shape", ["d1", "d2_hg2", "d3", "d4_ragged"])
+def test_hit_overlap(shape):
+    """Attention split by residency (SKO_FLAG_HIT_OVERLAP): the resident
+    rows are attended on the side stream beside the copy launch, the missed
+    rows after it, and the combine merges both phases.  Everything the
+    oracle checks, hot-buffer bytes included, at one to four positions, two
+    head groups and a ragged batch."""
+    import sparse_kv_offload_amd as sko
+    shapes = {
+        "d1": dict(batch=3, context=12000, steps=8, top_k=300, hot_slots=700, positions=1, heads=16),
+        "d2_hg2": dict(batch=3, context=9000, steps=6, top_k=256, hot_slots=600, positions=2, heads=20),
+        "d3": dict(batch=6, context=5000, steps=5, top_k=128, hot_slots=500, positions=3, heads=4),
+        "d4_ragged": dict(batch=5, contexts=(3000, 1, 777, 2048, 150), context=3000, steps=6, top_k=200,
+                          hot_slots=900, positions=4, heads=16),
+    }
+    w = case("overlap_" + shape, **shapes[shape])
+    log(f"case hit overlap {shape}")
+    run_parity(w, check_keys=False, flags=sko.SKO_FLAG_HIT_OVERLAP, log=log)
+
+
+def test_hit_overlap_newest_token():
+    """The newest token at every step with the split attention (it is a miss
+    at its first selection, then a hit)."""
+    import sparse_kv_offload_amd as sko
+    w = NewestWins("newest_overlap", layers=2, batch=3, context=3000, steps=5, top_k=128, hot_slots=300,
+                   positions=2, heads=16, seed=12)
+    log("case newest token, hit overlap")
+    run_parity(w, check_keys=False, flags=sko.SKO_FLAG_HIT_OVERLAP, log=log)
+
+
 @pytest.mark.parametrize("shape", ["d1", "d4_ragged", "host_append", "zeroq", "rescan", "floor_drop"])
 def test_indexer_c8(shape):
     """The int8 indexer: codes and fp16 scales of every appended row, the
