@@ -104,25 +104,10 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     // staging area lies in the same allocation, after every layer's rows)
     const int64_t stage_base = staged ? (stage_rows - hb) / kKvRowU4 + (int64_t)b * D * top_k : 0;
 
-    // remap: logical winner -> hot slot, for the chunk's rows of this phase,
-    // compacted in winner order (rows 0 .. n-1 of the block)
-    constexpr int kRowsPerThread = kAttnMaxRowsPerBlock / 256;
-    int32_t pk[kRowsPerThread];
-    int nmine = 0;
-#pragma unroll
-    for (int u = 0; u < kRowsPerThread; ++u) {
-        const int j = tid * kRowsPerThread + u;
-        pk[u] = (j < r1 - r0) ? w[r0 + j] : 0;
-        const bool in = j < r1 - r0 && (PHASE == kPhaseAll || (PHASE == kPhaseHits) == (pk[u] >= 0));
-        nmine += in ? 1 : 0;
-    }
-    int n;
-    int q = block_exclusive_scan<256>(nmine, &n, scratch);
-#pragma unroll
-    for (int u = 0; u < kRowsPerThread; ++u) {
-        const int j = tid * kRowsPerThread + u;
-        const int32_t packed = pk[u];
-        if (!(j < r1 - r0 && (PHASE == kPhaseAll || (PHASE == kPhaseHits) == (packed >= 0)))) continue;
+    // remap: logical winner -> hot slot for the chunk's rows of this phase
+    // (a split phase keeps its rows compacted in winner order: rows 0 .. n-1
+    // of the block)
+    auto remap = [&](int j, int32_t packed, int q) {
         const int32_t tok = packed & 0x7FFFFFFF;
         int32_t slot = (tok < cap) ? cs[tok] : -1;
         if (slot >= S) slot = -1;
@@ -131,15 +116,38 @@ __global__ __launch_bounds__(256) void k_attn_partial(
             if (fused_copy) {
                 cp = tok;
             } else if (staged) {
-                const int32_t old = atomicOr(&stage_idx[(size_t)b * cap + tok], kStageClaimed);
+                // one position and one head group: this block is the row's
+                // only reader and moves it without a claim
+                const int32_t old = (D == 1 && HG == 1)
+                                        ? stage_idx[(size_t)b * cap + tok]
+                                        : atomicOr(&stage_idx[(size_t)b * cap + tok], kStageClaimed);
                 rd = (int32_t)(stage_base + min(max(old & ~kStageClaimed, 0), D * top_k - 1));
                 if (!(old & kStageClaimed)) cp = slot;
             }
         }
         slot_s[q] = rd;
         cp_s[q] = cp;
-        ++q;
         if (hg == 0) phys[(size_t)bp * top_k + r0 + j] = slot;
+    };
+    int n = r1 - r0;
+    if constexpr (PHASE == kPhaseAll) {
+        for (int j = tid; j < n; j += 256) remap(j, w[r0 + j], j);
+    } else {
+        constexpr int kRowsPerThread = kAttnMaxRowsPerBlock / 256;
+        int32_t pk[kRowsPerThread];
+        int nmine = 0;
+#pragma unroll
+        for (int u = 0; u < kRowsPerThread; ++u) {
+            const int j = tid * kRowsPerThread + u;
+            pk[u] = (j < r1 - r0) ? w[r0 + j] : 0;
+            nmine += (j < r1 - r0 && (PHASE == kPhaseHits) == (pk[u] >= 0)) ? 1 : 0;
+        }
+        int q = block_exclusive_scan<256>(nmine, &n, scratch);
+#pragma unroll
+        for (int u = 0; u < kRowsPerThread; ++u) {
+            const int j = tid * kRowsPerThread + u;
+            if (j < r1 - r0 && (PHASE == kPhaseHits) == (pk[u] >= 0)) remap(j, pk[u], q++);
+        }
     }
     if (n == 0) {  // block-uniform: no rows of this phase in the chunk
         if (tid < kAttnHeadGroup) {
