@@ -90,27 +90,36 @@ KERNEL_SOURCE = {"score_hist": "select.hip", "gather_misses": "gather.hip", "mer
                  "attn_partial": "attention.hip"}
 
 
-def traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter summary of this kernel
-    and workload, or None when there is none or the kernel's source or the
-    runtime (its launch shape) changed since the counters were taken (the
-    summary records a digest of both)."""
+def code_digest(kernel_file: str) -> str:
+    """Digest of a kernel's source file and of the runtime (which sets its
+    launch shape), with comments and whitespace removed: only code changes
+    alter it."""
     import hashlib
     import re
+    h = hashlib.sha256()
+    for f in (kernel_file, "runtime.hip"):
+        src = open(os.path.join(ROOT, "sparse_kv_offload_amd", "csrc", f)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary of this kernel
+    and workload, or None when there is none or the code of the kernel's
+    source or of the runtime changed since the counters were taken (the
+    summary records code_digest of both)."""
+    import re
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
-    src = os.path.join(ROOT, "sparse_kv_offload_amd", "csrc", KERNEL_SOURCE.get(kernel, ""))
-    if not os.path.isfile(path) or not os.path.isfile(src):
+    src = KERNEL_SOURCE.get(kernel)
+    if not src or not os.path.isfile(path):
         return None
     m = re.search(r"```json\n(.*?)```", open(path).read(), re.S)
     if not m:
         return None
     entry = json.loads(m.group(1)).get(kernel)
-    if not entry:
-        return None
-    # the kernel's source and the runtime that sets its launch shape
-    h = hashlib.sha256(open(src, "rb").read())
-    h.update(open(os.path.join(ROOT, "sparse_kv_offload_amd", "csrc", "runtime.hip"), "rb").read())
-    if entry.get("source_sha256_16") != h.hexdigest()[:16]:
+    if not entry or entry.get("source_sha256_16") != code_digest(src):
         return None
     return entry.get("hbm_bytes_per_launch")
 

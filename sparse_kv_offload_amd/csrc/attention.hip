@@ -16,8 +16,11 @@
 // the attention of the others and no separate copy kernel runs.  Otherwise
 // the rows were copied early into a staging area that follows the hot
 // buffer in memory: every block reads its missed rows from there, and the
-// first block to claim a row (a flag bit in its staging index) also writes
-// it into its victim slot for later steps.
+// first block to claim a row (a flag bit in its staging index; no claim when
+// one position and one head group make every block a row's only reader)
+// also writes it into its victim slot for later steps.  A split launch pair
+// attends the rows resident at step start and the missed rows separately
+// (AttnPhase below), each writing its own partials.
 //
 // Layout of the work: a block takes one (seq, position), one group of 16
 // heads and a chunk of winners.  Rows are staged 32 at a time in LDS (one
