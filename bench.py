@@ -397,6 +397,7 @@ def main() -> int:
         return {"late": "late", "fused": "fused"}.get(args.copy, "early")
 
     h2d_ceiling = measure_h2d_ceiling(torch)
+    zero_copy = sko.sko_link_read_rate(0, 1 << 30, 3)
     hbm_copy = measure_hbm_copy(torch)
     calibration_copy(torch)
 
@@ -453,6 +454,8 @@ def main() -> int:
                                   if e.get("bound") == "host-link"), None),
         "miss_copy": copy_mode(calib) if calib else None,
         "h2d_ceiling_GBps": round(h2d_ceiling, 2),
+        # a streaming kernel reading contiguous pinned host memory
+        "zero_copy_read_GBps": round(zero_copy, 2),
         "hbm_copy_GBps": round(hbm_copy, 1),
         # the first step finds an empty shelf (every winner a miss); it is
         # not in `value`

@@ -274,6 +274,21 @@ int sko_get_timing(sko_handle* h, double* total_ms, int64_t* launches, int32_t n
 const char* sko_stage_name(int32_t stage);
 int32_t sko_num_stages(void);
 
+/*
+ * sko_link_read_rate — the host-link read rate as kernels see it: a
+ * streaming kernel reads `bytes` of pinned, device-mapped host memory
+ * (contiguous 16-byte loads), timed by HIP events over `reps` launches at
+ * each of a few grid sizes; *gbps receives the best rate (1e9 bytes/s).
+ * The decode step moves only missed rows over that link ([LSO] §4 "Decode
+ * step"; the early, late and fused copies all read the pool this way), so
+ * this is their ceiling for contiguous data, beside the bulk hipMemcpy rate
+ * of the copy engines.  Allocates, uses and frees its own buffer on
+ * `device`; synchronous; independent of any handle.
+ * Errors: SKO_E_INVAL (NULL gbps, device < 0, bytes < 1 MiB or not a
+ * multiple of 16, reps < 1), SKO_E_NOMEM, SKO_E_DEVICE.
+ */
+int sko_link_read_rate(int32_t device, int64_t bytes, int32_t reps, float* gbps);
+
 /* Destroy: synchronize the stream, free everything. NULL is a no-op. */
 void sko_destroy(sko_handle* h);
 

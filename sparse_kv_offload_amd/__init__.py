@@ -50,7 +50,7 @@ SKO_TAB_INDEXER_SCALE = 8
 EXPORTED = (
     "sko_create", "sko_set_stream", "sko_append_token", "sko_decode_step", "sko_read_step",
     "sko_read_table", "sko_get_stats", "sko_set_timing", "sko_get_timing", "sko_stage_name",
-    "sko_num_stages", "sko_destroy", "sko_last_error", "sko_version",
+    "sko_num_stages", "sko_destroy", "sko_last_error", "sko_version", "sko_link_read_rate",
     # layerwise prefill offload (include/sko_prefill.h)
     "sko_prefill_plan", "sko_prefill_create", "sko_prefill_destroy", "sko_prefill_host_pool",
     "sko_prefill_set_tokens", "sko_prefill_begin_layer", "sko_prefill_end_layer", "sko_prefill_sync",
@@ -127,6 +127,7 @@ def _load() -> ctypes.CDLL:
         "sko_destroy": (None, [vp]),
         "sko_last_error": (ctypes.c_char_p, []),
         "sko_version": (ctypes.c_char_p, []),
+        "sko_link_read_rate": (ctypes.c_int, [i32, i64, i32, ctypes.POINTER(ctypes.c_float)]),
         "sko_prefill_plan": (ctypes.c_int, [i32, vp, vp, i32, vp, vp, vp]),
         "sko_prefill_create": (ctypes.c_int, [ctypes.POINTER(SkoPrefillConfig), vp, ctypes.POINTER(vp)]),
         "sko_prefill_destroy": (ctypes.c_int, [vp]),
@@ -191,6 +192,13 @@ def sko_last_error() -> str:
 
 def sko_version() -> str:
     return _lib.sko_version().decode()
+
+
+def sko_link_read_rate(device: int = 0, nbytes: int = 1 << 30, reps: int = 3) -> float:
+    """Host-link read rate (GB/s) of a streaming kernel over pinned host memory."""
+    v = ctypes.c_float()
+    _check(_lib.sko_link_read_rate(device, nbytes, reps, ctypes.byref(v)), "sko_link_read_rate")
+    return float(v.value)
 
 
 def sko_num_stages() -> int:

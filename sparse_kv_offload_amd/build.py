@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsko.so")
-SOURCES = ["runtime.hip", "select.hip", "merge_lru.hip", "gather.hip", "attention.hip", "prefill.hip"]
+SOURCES = ["runtime.hip", "select.hip", "merge_lru.hip", "gather.hip", "attention.hip", "prefill.hip",
+           "link_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("SKO_ARCH", "gfx950")

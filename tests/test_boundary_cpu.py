@@ -99,3 +99,12 @@ def test_stage_names():
     assert "gather_misses" in names and "attn_partial" in names
     assert sko.sko_stage_name(99) == ""
     assert "gfx950" in sko.sko_version()
+
+
+@pytest.mark.parametrize("args", [(-1, 1 << 20, 1), (0, 1 << 19, 1), (0, (1 << 20) + 8, 1), (0, 1 << 20, 0)])
+def test_link_read_rate_rejects_bad_arguments(args):
+    """Argument checks come before any device work (so they run without a GPU)."""
+    import sparse_kv_offload_amd as sko
+    with pytest.raises(sko.SkoError) as e:
+        sko.sko_link_read_rate(*args)
+    assert e.value.code == sko.SKO_E_INVAL
