@@ -537,9 +537,12 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
     // B merge blocks, then (early copy) B * copy_per_seq copy blocks of
     // copy_words bitmap words each, about kCopyBlocks in all
     const int64_t words = std::max<int64_t>(1, (max_tokens_now + 31) / 32);
-    const int copy_words =
-        (int)std::min<int64_t>(kLruThreads, std::max<int64_t>(32, (B * words + kCopyBlocks - 1) / kCopyBlocks));
-    const int copy_per_seq = miss_bits ? (int)((words + copy_words - 1) / copy_words) : 0;
+    const int64_t max_words =
+        std::min<int64_t>(kLruThreads, std::max<int64_t>(32, (B * words + kCopyBlocks - 1) / kCopyBlocks));
+    const int copy_per_seq = miss_bits ? (int)((words + max_words - 1) / max_words) : 0;
+    // equal parts (a remainder part would hold few tokens and leave its
+    // block nearly idle while the others carry its share)
+    const int copy_words = copy_per_seq ? (int)((words + copy_per_seq - 1) / copy_per_seq) : (int)max_words;
     hipLaunchKernelGGL(k_merge_lru, dim3(B + B * copy_per_seq), dim3(kLruThreads), 0, st, winners, hist, meta, cand, topk,
                        ntok_layer, cache_slots_layer, slot_token_layer, last_use_layer, ring0_layer,
                        ring1_layer, pos_layer, ring_state_layer, D, top_k, S, C, cap, wpr, t, misses, victims,
