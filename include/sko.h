@@ -31,7 +31,9 @@
  *    corruption, no retry).
  *  - A handle is not thread-safe: drive it from one host thread.
  *  - All device work is enqueued on the stream given at create (or set by
- *    sko_set_stream), in call order.
+ *    sko_set_stream), in call order (SKO_FLAG_HIT_OVERLAP also uses an
+ *    internal stream, forked from and joined back into that stream within
+ *    each decode step).  sko_link_read_rate is independent of any handle.
  */
 #ifndef SKO_H
 #define SKO_H
