@@ -16,8 +16,7 @@
 // the attention of the others and no separate copy kernel runs.  Otherwise
 // the rows were copied early into a staging area that follows the hot
 // buffer in memory: every block reads its missed rows from there, and the
-// first block to claim a row (a flag bit in its staging index; no claim when
-// one position and one head group make every block a row's only reader)
+// block whose entry the LRU-update launch designated for each missed row
 // also writes it into its victim slot for later steps.  A split launch pair
 // attends the rows resident at step start and the missed rows separately
 // (AttnPhase below), each writing its own partials.
@@ -65,7 +64,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     const uint4* __restrict__ recent_layer,
     const int32_t* __restrict__ ntok_layer, float* __restrict__ part_acc,
     float* __restrict__ part_ml, int32_t* __restrict__ phys, const uint4* __restrict__ stage_rows,
-    int32_t* __restrict__ stage_idx, int32_t* __restrict__ stage_cnt, int B, int D, int H, int HG,
+    const int2* __restrict__ rdcp, uint32_t* __restrict__ miss_bits, int64_t wpr, int B, int D, int H, int HG,
     int top_k, int S, int64_t cap, int rows_per_block, int nchunk, int pchunks, float scale_log2) {
     __shared__ uint4 rows[kAttnTileRows * kRowStrideU4];
     __shared__ int32_t slot_s[kAttnMaxRowsPerBlock];  // row read, relative to the sequence's hot rows
@@ -87,10 +86,6 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     float* __restrict__ ml_out = part_ml + pidx * kAttnHeadGroup * 2;
     constexpr bool fused_copy = COPY == kCopyPool;
     constexpr bool staged = COPY == kCopyStaged;
-    // the next step's staging starts empty (reset by the first block, which
-    // may have no rows when sequence 0 holds no tokens)
-    if (staged && chunk == 0 && bp == 0 && hg == 0)
-        for (int i = tid; i < B; i += 256) stage_cnt[i] = 0;
     if (r0 >= r1) {
         if (tid < kAttnHeadGroup) {
             ml_out[2 * tid] = -INFINITY;
@@ -107,30 +102,32 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     // staging area lies in the same allocation, after every layer's rows)
     const int64_t stage_base = staged ? (stage_rows - hb) / kKvRowU4 + (int64_t)b * D * top_k : 0;
 
-    // remap: logical winner -> hot slot for the chunk's rows of this phase
-    // (a split phase keeps its rows compacted in winner order: rows 0 .. n-1
-    // of the block)
+    // remap: logical winner -> the row to read for the chunk's rows of this
+    // phase (a split phase keeps its rows compacted in winner order: rows
+    // 0 .. n-1 of the block).  Staged: the LRU-update launch wrote, per
+    // winner, the row (slot >= 0, -(r + 2) for staging row r, -1 none) and
+    // the slot a missed row moves into (one entry per miss), and its hot
+    // slot into phys; the miss's bitmap word is cleared for the next step
+    // (several blocks may store the same zero).
+    const int2* __restrict__ rc = staged ? rdcp + (size_t)bp * top_k : nullptr;
+    uint32_t* __restrict__ mbw = staged ? miss_bits + (size_t)b * wpr : nullptr;
     auto remap = [&](int j, int32_t packed, int q) {
-        const int32_t tok = packed & 0x7FFFFFFF;
-        int32_t slot = (tok < cap) ? cs[tok] : -1;
-        if (slot >= S) slot = -1;
-        int32_t rd = slot, cp = -1;
-        if (packed < 0 && slot >= 0) {
-            if (fused_copy) {
-                cp = tok;
-            } else if (staged) {
-                // one position and one head group: this block is the row's
-                // only reader and moves it without a claim
-                const int32_t old = (D == 1 && HG == 1)
-                                        ? stage_idx[(size_t)b * cap + tok]
-                                        : atomicOr(&stage_idx[(size_t)b * cap + tok], kStageClaimed);
-                rd = (int32_t)(stage_base + min(max(old & ~kStageClaimed, 0), D * top_k - 1));
-                if (!(old & kStageClaimed)) cp = slot;
-            }
+        int32_t rd = -1, cp = -1;
+        if constexpr (staged) {
+            const int2 e = rc[r0 + j];
+            rd = e.x >= 0 ? e.x : (e.x <= -2 ? (int32_t)(stage_base + min(-e.x - 2, D * top_k - 1)) : -1);
+            cp = e.y;
+            if (packed < 0) mbw[(packed & 0x7FFFFFFF) >> 5] = 0u;
+        } else {
+            const int32_t tok = packed & 0x7FFFFFFF;
+            int32_t slot = (tok < cap) ? cs[tok] : -1;
+            if (slot >= S) slot = -1;
+            rd = slot;
+            if (fused_copy && packed < 0 && slot >= 0) cp = tok;
+            if (hg == 0) phys[(size_t)bp * top_k + r0 + j] = slot;
         }
         slot_s[q] = rd;
         cp_s[q] = cp;
-        if (hg == 0) phys[(size_t)bp * top_k + r0 + j] = slot;
     };
     int n = r1 - r0;
     if constexpr (PHASE == kPhaseAll) {
@@ -421,7 +418,7 @@ hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_
                                float* part_ml,
                                int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
                                int rows_per_block, float scale, const uint16_t* stage_rows,
-                               int32_t* stage_idx, int32_t* stage_cnt, int phase) {
+                               const int2* rdcp, uint32_t* miss_bits, int phase) {
     const int HG = (H + kAttnHeadGroup - 1) / kAttnHeadGroup;
     const int nchunk = (top_k + rows_per_block - 1) / rows_per_block;
     const int pchunks = phase == 0 ? nchunk : 2 * nchunk;
@@ -431,18 +428,19 @@ hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_
                        cache_slots_layer, reinterpret_cast<uint4*>(hot_layer),                                   \
                        reinterpret_cast<const uint4*>(q_attn), reinterpret_cast<const uint4*>(pool_layer),       \
                        reinterpret_cast<const uint4*>(recent_layer), ntok_layer, part_acc, part_ml, phys,        \
-                       reinterpret_cast<const uint4*>(stage_rows), stage_idx, stage_cnt, B, D, H, HG, top_k, S, \
-                       cap, rows_per_block, nchunk, pchunks, scale_log2)
+                       reinterpret_cast<const uint4*>(stage_rows), rdcp, miss_bits, winner_words(cap), B, D, H, HG, \
+                       top_k, S, cap, rows_per_block, nchunk, pchunks, scale_log2)
     if (pool_layer != nullptr && stage_rows != nullptr) return hipErrorInvalidValue;
     if (phase == 1) {
         // the rows resident at step start: no copy of any kind
         SKO_ATTN_LAUNCH(kCopyNone, kPhaseHits);
     } else if (phase == 2) {
-        if (stage_rows == nullptr) return hipErrorInvalidValue;
+        if (stage_rows == nullptr || rdcp == nullptr || miss_bits == nullptr) return hipErrorInvalidValue;
         SKO_ATTN_LAUNCH(kCopyStaged, kPhaseMisses);
     } else if (pool_layer != nullptr) {
         SKO_ATTN_LAUNCH(kCopyPool, kPhaseAll);
     } else if (stage_rows != nullptr) {
+        if (rdcp == nullptr || miss_bits == nullptr) return hipErrorInvalidValue;
         SKO_ATTN_LAUNCH(kCopyStaged, kPhaseAll);
     } else {
         SKO_ATTN_LAUNCH(kCopyNone, kPhaseAll);

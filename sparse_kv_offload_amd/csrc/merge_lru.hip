@@ -196,11 +196,13 @@ __device__ __forceinline__ void thread_run(int64_t n, int align, int64_t* r0, in
 // its miss set M; a winner's flag is its absence at step start), so the
 // host-link transfer runs while the merge blocks update the LRU state.
 // Copy block j of sequence b takes bitmap words [W j, W j + W): it
-// lists their tokens in LDS, clears the words for the next step, reserves
-// that many staging rows with one atomic, and its 16 waves copy the rows
-// (kCopyRowsPerWave in flight per wave), recording each token's staging row
-// in stage_idx.  Staging rows are in no particular order; the attention
-// launch after this one looks them up (and moves each into its victim slot).
+// lists their tokens in LDS and copies each row into staging row r, where r
+// is the token's rank among the sequence's misses in token order (the
+// misses in the words before its own are counted first).  The merge blocks
+// of the same launch compute the same ranks from their sorted miss list, so
+// no block waits for another and no row index is handed over.  The bitmap
+// is left as it is for the other blocks' counts (the attention launch
+// clears the words of the misses).
 // The launch holds about kCopyBlocks copy blocks in all (each block a run
 // of up to 1024 bitmap words, one per thread): on this link more blocks,
 // i.e. more host reads in flight, lowered the transfer rate (2x the blocks:
@@ -208,23 +210,28 @@ __device__ __forceinline__ void thread_run(int64_t n, int align, int64_t* r0, in
 constexpr int kCopyBlocks = 64;
 constexpr int kCopyRowsPerWave = 2;
 
-__device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, uint32_t* __restrict__ miss_bits,
+__device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, const uint32_t* __restrict__ miss_bits,
                                            const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
-                                           uint4* __restrict__ stage_rows,
-                                           int32_t* __restrict__ stage_idx, int32_t* __restrict__ stage_cnt,
-                                           const int32_t* __restrict__ ntok_layer, int64_t cap, int64_t wpr,
-                                           int mstride, int32_t* toks, int* scratch, int* s_base) {
+                                           uint4* __restrict__ stage_rows, const int32_t* __restrict__ ntok_layer,
+                                           int64_t cap, int64_t wpr, int mstride, int32_t* toks, int* scratch) {
     const int b = cb / nper;
     const int part = cb - b * nper;
     const int64_t words_now = (ntok_layer[b] + 31) / 32;
     const int32_t newest = ntok_layer[b] - 1;  // its row is read from the device copy
-    const int64_t wi = (int64_t)part * copy_words + threadIdx.x;
-    uint32_t* __restrict__ mb = miss_bits + (size_t)b * wpr;
-    uint32_t bits = 0u;
-    if ((int)threadIdx.x < copy_words && wi < words_now) {
-        bits = mb[wi];
-        if (bits) mb[wi] = 0u;
+    const uint32_t* __restrict__ mb = miss_bits + (size_t)b * wpr;
+    // misses before this part (copy_words is a multiple of 4 and rows are
+    // 16-byte aligned, so the count reads whole 16-byte words)
+    const int64_t w_begin = (int64_t)part * copy_words;
+    int before = 0;
+    for (int64_t q = threadIdx.x; 4 * q < w_begin; q += kLruThreads) {
+        const uint4 v = reinterpret_cast<const uint4*>(mb)[q];
+        before += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
     }
+    int base;
+    (void)block_exclusive_scan<kLruThreads>(before, &base, scratch);
+    const int64_t wi = w_begin + threadIdx.x;
+    uint32_t bits = 0u;
+    if ((int)threadIdx.x < copy_words && wi < words_now) bits = mb[wi];
     int total;
     int pos = block_exclusive_scan<kLruThreads>(__popc(bits), &total, scratch);
     if (total == 0) return;  // block-uniform
@@ -233,9 +240,7 @@ __device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, uin
         bits &= bits - 1u;
         toks[pos++] = (int32_t)(wi * 32 + e);
     }
-    if (threadIdx.x == 0) *s_base = atomicAdd(&stage_cnt[b], total);
     __syncthreads();
-    const int base = *s_base;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int i0 = wave * kCopyRowsPerWave; i0 < total; i0 += (kLruThreads / 64) * kCopyRowsPerWave) {
         uint4 a[kCopyRowsPerWave], t8[kCopyRowsPerWave];
@@ -255,7 +260,6 @@ __device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, uin
             uint4* dst = stage_rows + ((int64_t)b * mstride + base + i) * kKvRowU4;
             dst[lane] = a[r];
             if (lane < kKvRowU4 - 64) dst[64 + lane] = t8[r];
-            if (lane == 0) stage_idx[(size_t)b * cap + toks[i]] = base + i;
         }
     }
 }
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     int32_t* __restrict__ evict_old, int32_t* __restrict__ counts, GatherEntry* __restrict__ glist,
     unsigned long long* __restrict__ layer_stats, int do_refine, int nseq, int copy_per_seq, int copy_words,
     uint32_t* __restrict__ miss_bits, const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
-    uint4* __restrict__ stage_rows, int32_t* __restrict__ stage_idx, int32_t* __restrict__ stage_cnt) {
+    uint4* __restrict__ stage_rows, int2* __restrict__ rdcp, int32_t* __restrict__ phys) {
     __shared__ uint32_t touched[kMaxHotSlots / 32];
     // [0, kMaxMerge): misses; [kMaxMerge, 2 kMaxMerge): the union, later the
     // victims.  Before the merge the whole area stages refine candidates.
@@ -286,11 +290,8 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     uint2* cstage = reinterpret_cast<uint2*>(lists);
 
     if ((int)blockIdx.x >= nseq) {
-        __shared__ int s_base;
         copy_block((int)blockIdx.x - nseq, copy_per_seq, copy_words, miss_bits, pool_layer, recent_layer,
-                   stage_rows, stage_idx,
-                   stage_cnt,
-                   ntok_layer, cap, wpr, D * top_k, lists, scratch, &s_base);
+                   stage_rows, ntok_layer, cap, wpr, D * top_k, lists, scratch);
         return;
     }
     const int b = blockIdx.x;
@@ -497,6 +498,45 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
         if (tid == 0) ring_state_layer[b] = RingState{head, tail + ntouched, cur, {0, 0, 0}};
     }
 
+    // 7. (early copy) what the attention reads for each winner of this
+    //    sequence: a hit's slot, or for a miss its staging row (its rank r
+    //    in the sorted miss list, the row the copy blocks fill) and, for
+    //    exactly one of the entries holding it, the victim slot it moves
+    //    into; rd = slot (>= 0), -(r + 2) for a staged row, -1 for none
+    if (rdcp != nullptr) {
+        const bool assigned = nM > 0 && sane && avail >= nM;
+        __syncthreads();  // the ring maintenance above is done with `touched`
+        for (int i = tid; i < (nM + 31) / 32; i += kLruThreads) touched[i] = 0u;
+        __syncthreads();
+        for (int e = tid; e < D * kk; e += kLruThreads) {
+            const int p = e / kk;
+            const size_t at = ((size_t)b * D + p) * top_k + (e - p * kk);
+            const int32_t packed = topk[at];
+            const int32_t tok = packed & 0x7FFFFFFF;
+            int32_t rd = -1, cp = -1, slot = -1;
+            if (packed >= 0) {
+                slot = tok < cap ? cs[tok] : -1;
+                if (slot >= S) slot = -1;
+                rd = slot;
+            } else if (assigned) {
+                int lo = 0, hi = nM;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (mlist[mid] < tok) lo = mid + 1;
+                    else hi = mid;
+                }
+                if (lo < nM && mlist[lo] == tok && lo < mstride && vlist[lo] >= 0 && vlist[lo] < S) {
+                    slot = vlist[lo];
+                    rd = -(lo + 2);
+                    const uint32_t bit = 1u << (lo & 31);
+                    if (!(atomicOr(&touched[lo >> 5], bit) & bit)) cp = slot;
+                }
+            }
+            rdcp[at] = make_int2(rd, cp);
+            phys[at] = slot;
+        }
+    }
+
     // 6. counters (rows that were rescanned); clear this sequence's selection
     // scratch for the next step
     __shared__ int s_rescans;
@@ -531,25 +571,26 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
                             GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
                             uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
-                            uint16_t* stage_rows, int32_t* stage_idx, int32_t* stage_cnt, int64_t max_tokens_now) {
+                            uint16_t* stage_rows, int2* rdcp, int32_t* phys, int64_t max_tokens_now) {
     const int64_t C = ring_capacity(S, D, top_k);
     const int64_t wpr = winner_words(cap);
     // B merge blocks, then (early copy) B * copy_per_seq copy blocks of
-    // copy_words bitmap words each, about kCopyBlocks in all
+    // copy_words bitmap words each (a multiple of 4), about kCopyBlocks in all
     const int64_t words = std::max<int64_t>(1, (max_tokens_now + 31) / 32);
     const int64_t max_words =
         std::min<int64_t>(kLruThreads, std::max<int64_t>(32, (B * words + kCopyBlocks - 1) / kCopyBlocks));
     const int copy_per_seq = miss_bits ? (int)((words + max_words - 1) / max_words) : 0;
     // equal parts (a remainder part would hold few tokens and leave its
     // block nearly idle while the others carry its share)
-    const int copy_words = copy_per_seq ? (int)((words + copy_per_seq - 1) / copy_per_seq) : (int)max_words;
+    const int copy_words =
+        copy_per_seq ? (int)(((words + copy_per_seq - 1) / copy_per_seq + 3) / 4 * 4) : (int)max_words;
     hipLaunchKernelGGL(k_merge_lru, dim3(B + B * copy_per_seq), dim3(kLruThreads), 0, st, winners, hist, meta, cand, topk,
                        ntok_layer, cache_slots_layer, slot_token_layer, last_use_layer, ring0_layer,
                        ring1_layer, pos_layer, ring_state_layer, D, top_k, S, C, cap, wpr, t, misses, victims,
                        evict_old, counts, glist, layer_stats, do_refine ? 1 : 0, B, copy_per_seq, copy_words,
                        miss_bits,
                        reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<const uint4*>(recent_layer),
-                       reinterpret_cast<uint4*>(stage_rows), stage_idx, stage_cnt);
+                       reinterpret_cast<uint4*>(stage_rows), miss_bits ? rdcp : nullptr, phys);
     return hipGetLastError();
 }
 

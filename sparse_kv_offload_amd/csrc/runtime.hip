@@ -128,8 +128,7 @@ struct sko_handle {
     bool staged_copy = false;       // early copy into staging
     uint32_t* miss_bits = nullptr;  // [B][wpr]
     uint16_t* stage_rows = nullptr; // [B][D*k][576] miss rows copied early (inside the hot allocation)
-    int32_t* stage_idx = nullptr;   // [B][cap]
-    int32_t* stage_cnt = nullptr;   // [B]
+    int2* rdcp = nullptr;           // [B][D][k]: per winner, the row the attention reads and the slot a missed row moves into
     int32_t* floor = nullptr;       // [L][B][D] candidate floor (first-digit bin)
     uint32_t* hist = nullptr;       // [B][D][4096]
     RowMeta* meta = nullptr;        // [B][D]
@@ -412,8 +411,7 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     ok = ok && dev_alloc(h, (void**)&h->floor, LB * h->D * 4);
     if (h->staged_copy) {
         ok = ok && dev_alloc(h, (void**)&h->miss_bits, (size_t)h->B * h->wpr * 4);
-        ok = ok && dev_alloc(h, (void**)&h->stage_idx, (size_t)h->B * h->cap * 4);
-        ok = ok && dev_alloc(h, (void**)&h->stage_cnt, (size_t)h->B * 4);
+        ok = ok && dev_alloc(h, (void**)&h->rdcp, BD * h->k * sizeof(int2));
     }
     ok = ok && dev_alloc(h, (void**)&h->winners, (size_t)h->B * h->wpr * 4);
     ok = ok && dev_alloc(h, (void**)&h->hist, BD * kHistBins * 4);
@@ -457,8 +455,7 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     if (e == hipSuccess) e = hipMemsetAsync(h->hist, 0, BD * kHistBins * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->meta, 0, BD * sizeof(RowMeta), h->stream);
     if (e == hipSuccess && h->staged_copy) e = hipMemsetAsync(h->miss_bits, 0, (size_t)h->B * h->wpr * 4, h->stream);
-    if (e == hipSuccess && h->staged_copy) e = hipMemsetAsync(h->stage_cnt, 0, (size_t)h->B * 4, h->stream);
-    if (e == hipSuccess && h->staged_copy) e = hipMemsetAsync(h->stage_idx, 0, (size_t)h->B * h->cap * 4, h->stream);
+    if (e == hipSuccess && h->staged_copy) e = hipMemsetAsync(h->rdcp, 0xFF, BD * h->k * sizeof(int2), h->stream);
     if (e == hipSuccess) {
         // first step: every key is a candidate (or none, to force the rescan path)
         const std::vector<int32_t> fl(LB * h->D, (cfg->flags & SKO_FLAG_SELECT_RESCAN) ? kFloorRescanAll : 0);
@@ -634,7 +631,7 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
                                      ring0, ring1, ring_pos, ring_state, B, D, k, S, cap, t, h->misses, h->victims,
                                      h->evict_old, h->counts, h->glist, h->stats + (size_t)layer * 8, !staged,
                                      staged ? h->miss_bits : nullptr, pool_layer, recent_layer, h->stage_rows,
-                                     h->stage_idx, h->stage_cnt, max_now);
+                                     staged ? h->rdcp : nullptr, h->phys, max_now);
          })))
         return rc;
     // late copy: its own gather from the pool; fused or early: the attention
@@ -650,8 +647,8 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
                  [&] {
                      return launch_attn_partial(h->side, h->topk, cs, hot_layer, qa, nullptr, recent_layer, ntok,
                                                 h->part_acc, h->part_ml, h->phys, B, D, H, k, S, cap,
-                                                h->rows_per_block, h->cfg.attn_scale, h->stage_rows, h->stage_idx,
-                                                h->stage_cnt, 1);
+                                                h->rows_per_block, h->cfg.attn_scale, h->stage_rows, nullptr,
+                                                nullptr, 1);
                  },
                  h->side)))
             return rc;
@@ -662,7 +659,7 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
              return launch_attn_partial(h->stream, h->topk, cs, hot_layer, qa, fused_copy ? pool_layer : nullptr,
                                         recent_layer, ntok, h->part_acc, h->part_ml, h->phys, B, D, H, k, S, cap,
                                         h->rows_per_block, h->cfg.attn_scale, staged ? h->stage_rows : nullptr,
-                                        staged ? h->stage_idx : nullptr, staged ? h->stage_cnt : nullptr,
+                                        staged ? h->rdcp : nullptr, staged ? h->miss_bits : nullptr,
                                         split ? 2 : 0);
          })))
         return rc;

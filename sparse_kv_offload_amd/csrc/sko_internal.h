@@ -21,7 +21,6 @@ constexpr int kMaxHotSlots = 1 << 18;        // S limit (LDS bitmap of touched s
 constexpr int kAttnHeadGroup = 16;           // heads per MFMA tile (M = 16)
 constexpr int kAttnTileRows = 32;            // rows per attention tile
 constexpr int kAttnMaxRowsPerBlock = 512;    // rows of one attention block (remap table)
-constexpr int32_t kStageClaimed = 1 << 30;   // staging index flag: row already moved into its slot
 constexpr int kFilterKeysPerThread = 16;
 constexpr int kFilterSpan = 256 * kFilterKeysPerThread;  // keys per block pass
 constexpr int kPreStage = 128;               // per-wave LDS staging of candidates
@@ -132,13 +131,16 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
                             GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
                             uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
-                            uint16_t* stage_rows, int32_t* stage_idx, int32_t* stage_cnt, int64_t max_tokens_now);
+                            uint16_t* stage_rows, int2* rdcp, int32_t* phys, int64_t max_tokens_now);
 // (miss_bits non-null: the launch also holds copy blocks that move the rows
 // marked in miss_bits [B][wpr] from the pool into stage_rows [B][D*k][576],
-// any order, record stage_idx[b][token], count into stage_cnt[b] and clear
-// the bits: the early miss copy, overlapping the LRU update.)  In every copy
-// the newest token's row comes from recent_layer [B][576] instead of the
-// pool.
+// the r-th miss of a sequence in token order into its row r, and the merge
+// blocks write rdcp and phys [B][D][k] for the attention: per winner, the
+// row to read (slot >= 0, -(r + 2) for staged row r, -1 for none) and for
+// one entry of each miss the victim slot to move it into (else -1); the
+// early miss copy, overlapping the LRU update.  The bits stay set; the
+// attention launch clears them.)  In every copy the newest token's row
+// comes from recent_layer [B][576] instead of the pool.
 // Late copy from the pool into the slots.  Work list: sequence b's entries
 // are glist[b * D*k + r], r < counts[b][2].
 hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const int32_t* counts,
@@ -153,16 +155,16 @@ hipError_t launch_topk_refine(hipStream_t st, RowMeta* meta, const uint2* cand, 
 // topk entries < 0) from the pool into their slots; only valid when each
 // row is read by one block (one position, at most 16 heads).  stage_rows
 // non-null instead (it must lie in the allocation of hot_layer, at a row
-// boundary after it): missed rows are read from stage_rows[b][stage_idx[b]
-// [token]], the first block to set kStageClaimed in that index also moves
-// the row into its slot, and stage_cnt is reset.
+// boundary after it): the rows and moves come from rdcp (written by the
+// LRU-update launch), staged rows are moved into their victim slots, and
+// the misses' words of miss_bits [B][wpr] are cleared.
 hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_t* cache_slots_layer,
                                uint16_t* hot_layer, const uint16_t* q_attn, const uint16_t* pool_layer,
                                const uint16_t* recent_layer, const int32_t* ntok_layer, float* part_acc,
                                float* part_ml,
                                int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
                                int rows_per_block, float scale, const uint16_t* stage_rows,
-                               int32_t* stage_idx, int32_t* stage_cnt, int phase);
+                               const int2* rdcp, uint32_t* miss_bits, int phase);
 hipError_t launch_attn_combine(hipStream_t st, const float* part_acc, const float* part_ml,
                                float* out, int B, int D, int H, int nchunk);
 // Rings of n_seqs sequences: ring0 = 0..S-1, pos = identity, head 0, tail S.
