@@ -558,8 +558,17 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
         atomicAdd(&layer_stats[2], (unsigned long long)nH);
         atomicAdd(&layer_stats[3], (unsigned long long)nM);
         atomicAdd(&layer_stats[4], (unsigned long long)nEv);
-        if (b == 0) atomicAdd(&layer_stats[0], 1ull);
     }
+}
+
+void copy_shape(int B, int64_t max_tokens_now, int* copy_per_seq, int* copy_words) {
+    const int64_t words = std::max<int64_t>(1, (max_tokens_now + 31) / 32);
+    const int64_t max_words =
+        std::min<int64_t>(kLruThreads, std::max<int64_t>(32, (B * words + kCopyBlocks - 1) / kCopyBlocks));
+    *copy_per_seq = (int)((words + max_words - 1) / max_words);
+    // equal parts (a remainder part would hold few tokens and leave its
+    // block nearly idle while the others carry its share)
+    *copy_words = (int)(((words + *copy_per_seq - 1) / *copy_per_seq + 3) / 4 * 4);
 }
 
 hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, RowMeta* meta,
@@ -576,14 +585,9 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
     const int64_t wpr = winner_words(cap);
     // B merge blocks, then (early copy) B * copy_per_seq copy blocks of
     // copy_words bitmap words each (a multiple of 4), about kCopyBlocks in all
-    const int64_t words = std::max<int64_t>(1, (max_tokens_now + 31) / 32);
-    const int64_t max_words =
-        std::min<int64_t>(kLruThreads, std::max<int64_t>(32, (B * words + kCopyBlocks - 1) / kCopyBlocks));
-    const int copy_per_seq = miss_bits ? (int)((words + max_words - 1) / max_words) : 0;
-    // equal parts (a remainder part would hold few tokens and leave its
-    // block nearly idle while the others carry its share)
-    const int copy_words =
-        copy_per_seq ? (int)(((words + copy_per_seq - 1) / copy_per_seq + 3) / 4 * 4) : (int)max_words;
+    int copy_per_seq = 0, copy_words = 0;
+    copy_shape(B, max_tokens_now, &copy_per_seq, &copy_words);
+    if (!miss_bits) copy_per_seq = 0;
     hipLaunchKernelGGL(k_merge_lru, dim3(B + B * copy_per_seq), dim3(kLruThreads), 0, st, winners, hist, meta, cand, topk,
                        ntok_layer, cache_slots_layer, slot_token_layer, last_use_layer, ring0_layer,
                        ring1_layer, pos_layer, ring_state_layer, D, top_k, S, C, cap, wpr, t, misses, victims,

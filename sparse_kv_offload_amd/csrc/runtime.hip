@@ -772,7 +772,7 @@ int sko_get_stats(sko_handle* h, int32_t layer, sko_layer_stats* out) {
     hipError_t e = hipStreamSynchronize(h->stream);
     if (e == hipSuccess) e = hipMemcpy(v, h->stats + (size_t)layer * 8, sizeof(v), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return device_fail(h, e, "read stats");
-    out->steps = (int64_t)v[0];
+    out->steps = h->step[layer];
     out->unique = (int64_t)v[1];
     out->hits = (int64_t)v[2];
     out->misses = (int64_t)v[3];
