@@ -1,0 +1,141 @@
+"""The handle's stream and instrumentation calls on the GPU: decoding on a
+non-default stream, and switching streams with sko_set_stream, gives the
+same residency, hot-buffer bytes and counts as the default stream (and the
+attention within the parity bar: the order of winners, and so the
+attention's rounding, follows the order of atomic appends); the per-stage
+timing counts one launch per layer-step for each stage of the copy
+arrangement; the step counters follow the calls."""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_kv_offload_amd  # noqa: F401
+    yield
+
+
+W = synth.Workload("api", layers=2, batch=3, context=4000, steps=5, top_k=128, hot_slots=300, positions=2,
+                   heads=16, seed=77)
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda")
+
+
+def run(stream_plan, flags=0):
+    """Decode W on a fresh handle; stream_plan(step) gives the stream for
+    that step (None: the default stream).  Returns the outputs and tables."""
+    import torch
+    import sparse_kv_offload_amd as sko
+    w = W
+    cfg = sko.make_config(num_layers=w.layers, batch=w.batch, max_tokens=w.capacity, num_heads=w.heads,
+                          top_k=w.top_k, hot_slots=w.hot_slots, mtp_positions=w.positions, flags=flags)
+    first = stream_plan(0)
+    outs, tabs, counts = [], [], []
+    with sko.SparseKVOffload(cfg, first) as h:
+        for l in range(w.layers):
+            for b in range(w.batch):
+                h.append(l, b, w.index_rows(l, b, 0, w.context), w.kv_rows(l, b, 0, w.context))
+        torch.cuda.synchronize()
+        qch = {(l, b): w.index_queries(l, b, w.steps) for l in range(w.layers) for b in range(w.batch)}
+        for t in range(w.steps):
+            st = stream_plan(t)
+            sko.sko_set_stream(h.handle, st)
+            ctx = torch.cuda.stream(st) if st is not None else torch.cuda.stream(torch.cuda.current_stream())
+            with ctx:
+                for l in range(w.layers):
+                    ni = dev(np.concatenate([w.index_rows(l, b, w.context + t, 1) for b in range(w.batch)]))
+                    nk = dev(np.concatenate([w.kv_rows(l, b, w.context + t, 1) for b in range(w.batch)]))
+                    qi = dev(np.stack([qch[(l, b)][t] for b in range(w.batch)]))
+                    qa = dev(np.stack([w.attn_queries(l, b, t) for b in range(w.batch)]))
+                    out = torch.empty((w.batch, w.positions, w.heads, synth.V_DIM), dtype=torch.float32,
+                                      device="cuda")
+                    sko.sko_append_token(h.handle, l, sko.SKO_ALL_SEQS, ni, nk, 1, True)
+                    sko.sko_decode_step(h.handle, l, qi, qa, out)
+                    torch.cuda.synchronize()
+                    outs.append(out.cpu().numpy())
+                    counts.append(h.step_buffer(sko.SKO_BUF_COUNTS).copy())
+        for l in range(w.layers):
+            for b in range(w.batch):
+                tabs.append(h.table(l, b, sko.SKO_TAB_CACHE_SLOTS).copy())
+                tabs.append(h.table(l, b, sko.SKO_TAB_HOT).copy())
+        steps = [h.stats(l).steps for l in range(w.layers)]
+    return outs, tabs, counts, steps
+
+
+@pytest.mark.parametrize("flags_name", ["early", "late"])
+def test_streams_give_the_same_results(flags_name):
+    import torch
+    import sparse_kv_offload_amd as sko
+    flags = {"early": 0, "late": sko.SKO_FLAG_LATE_COPY}[flags_name]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    log(f"streams {flags_name}: default stream")
+    ref = run(lambda t: None, flags)
+    log(f"streams {flags_name}: one side stream")
+    one = run(lambda t: s1, flags)
+    log(f"streams {flags_name}: switching streams every step")
+    alt = run(lambda t: s1 if t % 2 == 0 else s2, flags)
+    for other in (one, alt):
+        # residency tables, hot-buffer bytes and per-step counts: exact
+        for a, b in zip(ref[1], other[1]):
+            assert np.array_equal(a, b)
+        for a, b in zip(ref[2], other[2]):
+            assert np.array_equal(a, b)
+        # attention: the order of winners in a top-k list follows the order
+        # of atomic appends, which sets the attention's split over rows and
+        # so its rounding; the parity bar applies
+        for a, b in zip(ref[0], other[0]):
+            assert np.abs(a - b).max() <= 2e-2
+            assert np.sqrt(np.mean((a - b) ** 2)) <= 1e-2 * max(np.sqrt(np.mean(a ** 2)), 1e-6)
+    assert ref[3] == [W.steps] * W.layers == one[3] == alt[3]
+
+
+def test_timing_counts_one_launch_per_layer_step():
+    import torch
+    import sparse_kv_offload_amd as sko
+    w = W
+    cfg = sko.make_config(num_layers=w.layers, batch=w.batch, max_tokens=w.capacity, num_heads=w.heads,
+                          top_k=w.top_k, hot_slots=w.hot_slots, mtp_positions=w.positions)
+    with sko.SparseKVOffload(cfg, torch.cuda.current_stream()) as h:
+        for l in range(w.layers):
+            for b in range(w.batch):
+                h.append(l, b, w.index_rows(l, b, 0, w.context), w.kv_rows(l, b, 0, w.context))
+        h.set_timing((1 << sko.sko_num_stages()) - 1)
+        qch = {(l, b): w.index_queries(l, b, w.steps) for l in range(w.layers) for b in range(w.batch)}
+        out = torch.empty((w.batch, w.positions, w.heads, synth.V_DIM), dtype=torch.float32, device="cuda")
+        n = 3
+        for t in range(n):
+            for l in range(w.layers):
+                ni = dev(np.concatenate([w.index_rows(l, b, w.context + t, 1) for b in range(w.batch)]))
+                nk = dev(np.concatenate([w.kv_rows(l, b, w.context + t, 1) for b in range(w.batch)]))
+                qi = dev(np.stack([qch[(l, b)][t] for b in range(w.batch)]))
+                qa = dev(np.stack([w.attn_queries(l, b, t) for b in range(w.batch)]))
+                sko.sko_append_token(h.handle, l, sko.SKO_ALL_SEQS, ni, nk, 1, True)
+                h.decode_step(l, qi, qa, out)
+        tm = h.timing()
+        log(f"timing: {tm}")
+        layer_steps = n * w.layers
+        # the early copy's stages, one launch each per layer-step
+        for stage in ("append_rows", "score_hist", "topk_filter", "topk_refine", "merge_lru", "attn_partial",
+                      "attn_combine"):
+            ms, launches = tm[stage]
+            assert launches == layer_steps, (stage, launches)
+            assert ms > 0.0
+        assert tm.get("gather_misses", (0.0, 0))[1] == 0  # no late gather in this mode
+        # clearing the mask clears the totals
+        h.set_timing(0)
+        assert all(c == 0 for _, c in h.timing().values())
+        assert [h.stats(l).steps for l in range(w.layers)] == [n] * w.layers
