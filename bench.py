@@ -261,7 +261,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the offload step is "
-              "per-GPU and this build has no multi-GPU path", file=sys.stderr)
+              "per-GPU and this library has no multi-GPU path", file=sys.stderr)
         return 2
     if args.prefill:
         return prefill_bench(args)
