@@ -217,6 +217,12 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
  * set half an octave of score below the previous step's threshold; when
  * fewer than k keys reach it the row is rescanned from the indexer.  Both
  * paths give the same winners (the first step of a layer keeps every key).
+ * Reproducible: the LRU-update launch puts each position's winners in token
+ * order before the attention reads them, so the same inputs give the same
+ * output bits on any stream and in any run (with at most 16 positions and
+ * without SKO_FLAG_HIT_OVERLAP, whose hit attention reads the lists while
+ * that launch runs; there the winners keep the order in which the selection
+ * appended them and only the output's rounding varies).
  * Errors: SKO_E_INVAL (bad layer or NULL pointer), SKO_E_STATE, SKO_E_DEVICE.
  */
 int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void* q_attn,
@@ -224,7 +230,8 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
 
 /* Buffers of the most recent sko_decode_step (any layer), for inspection. */
 enum sko_step_buffer {
-    SKO_BUF_TOPK = 1,      /* int32 [B][D][k]: packed winners (bit31 = miss), first `selected` valid, any order */
+    SKO_BUF_TOPK = 1,      /* int32 [B][D][k]: packed winners (bit31 = miss), first `selected` valid, token order
+                              (the selection's order with SKO_FLAG_HIT_OVERLAP or more than 16 positions) */
     SKO_BUF_PHYS = 2,      /* int32 [B][D][k]: hot slot of each TOPK entry, same order */
     SKO_BUF_COUNTS = 3,    /* sko_seq_counts [B] */
     SKO_BUF_MISSES = 4,    /* int32 [B][D*k]: miss tokens ascending, first `misses` valid */

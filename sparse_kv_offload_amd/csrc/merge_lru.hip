@@ -275,11 +275,12 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     int32_t* __restrict__ evict_old, int32_t* __restrict__ counts, GatherEntry* __restrict__ glist,
     unsigned long long* __restrict__ layer_stats, int do_refine, int nseq, int copy_per_seq, int copy_words,
     uint32_t* __restrict__ miss_bits, const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
-    uint4* __restrict__ stage_rows, int2* __restrict__ rdcp, int32_t* __restrict__ phys) {
+    uint4* __restrict__ stage_rows, int2* __restrict__ rdcp, int32_t* __restrict__ phys, int sort_winners) {
     __shared__ uint32_t touched[kMaxHotSlots / 32];
     // [0, kMaxMerge): misses; [kMaxMerge, 2 kMaxMerge): the union, later the
     // victims.  Before the merge the whole area stages refine candidates.
     __shared__ int32_t lists[2 * kMaxMerge];
+    __shared__ uint32_t marks[kMaxMerge];  // per union entry: positions holding it (sorting)
     __shared__ uint32_t hgrp[4][256];
     __shared__ RefineGroup rgrp[4];
     __shared__ int scratch[kLruThreads / 64 + 1];
@@ -351,6 +352,49 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     }
     __syncthreads();
     nU = std::min(nU, kMaxMerge);
+
+    // 1b. (sort_winners, at most 16 positions) each position's winners are
+    //     rewritten in token order, so the attention's grouping of rows into
+    //     chunks does not depend on the order in which the selection
+    //     appended them: every entry finds its token in U (binary search)
+    //     and marks it with its position (bit p, and bit 16 + p where the
+    //     entry is a miss); a position's list is then U's entries marked p,
+    //     placed by one scan.  A position whose marks do not add up to its
+    //     count (which a well-formed list never gives) keeps its order.
+    const bool sorted_lists = sort_winners && D <= 16;
+    if (sorted_lists) {
+        for (int i = tid; i < nU; i += kLruThreads) marks[i] = 0u;
+        __syncthreads();
+        for (int e = tid; e < D * kk; e += kLruThreads) {
+            const int p = e / kk;
+            const int32_t packed = topk[((size_t)b * D + p) * top_k + (e - p * kk)];
+            const int32_t tok = packed & 0x7FFFFFFF;
+            int lo = 0, hi = nU;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (ulist[mid] < tok) lo = mid + 1;
+                else hi = mid;
+            }
+            if (lo < nU && ulist[lo] == tok) atomicOr(&marks[lo], (1u << p) | (packed < 0 ? 1u << (16 + p) : 0u));
+        }
+        __syncthreads();
+        int64_t r0, r1;
+        thread_run(nU, 1, &r0, &r1);
+        for (int p = 0; p < D; ++p) {
+            int n_loc = 0;
+            for (int64_t u = r0; u < r1; ++u) n_loc += (int)((marks[u] >> p) & 1u);
+            int total;
+            int o = block_exclusive_scan<kLruThreads>(n_loc, &total, scratch);
+            if (total == kk) {
+                int32_t* __restrict__ row = topk + ((size_t)b * D + p) * top_k;
+                for (int64_t u = r0; u < r1; ++u) {
+                    const uint32_t m = marks[u];
+                    if ((m >> p) & 1u) row[o++] = ulist[u] | (int32_t)(((m >> (16 + p)) & 1u) << 31);
+                }
+            }
+        }
+        __syncthreads();
+    }
 
     // 2. hits and misses: every thread looks up its contiguous run of U at
     //    once; misses listed in token order, hits stamped t and marked
@@ -502,15 +546,15 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     //    sequence: a hit's slot, or for a miss its staging row (its rank r
     //    in the sorted miss list, the row the copy blocks fill) and, for
     //    exactly one of the entries holding it, the victim slot it moves
-    //    into; rd = slot (>= 0), -(r + 2) for a staged row, -1 for none
+    //    into; rd = slot (>= 0), -(r + 2) for a staged row, -1 for none.
+    //    With sorted lists the positions are taken in turn, so the entry
+    //    that moves a missed row is the one of its first position.
     if (rdcp != nullptr) {
         const bool assigned = nM > 0 && sane && avail >= nM;
         __syncthreads();  // the ring maintenance above is done with `touched`
         for (int i = tid; i < (nM + 31) / 32; i += kLruThreads) touched[i] = 0u;
         __syncthreads();
-        for (int e = tid; e < D * kk; e += kLruThreads) {
-            const int p = e / kk;
-            const size_t at = ((size_t)b * D + p) * top_k + (e - p * kk);
+        auto emit = [&](size_t at) {
             const int32_t packed = topk[at];
             const int32_t tok = packed & 0x7FFFFFFF;
             int32_t rd = -1, cp = -1, slot = -1;
@@ -534,6 +578,17 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
             }
             rdcp[at] = make_int2(rd, cp);
             phys[at] = slot;
+        };
+        if (sorted_lists) {
+            for (int p = 0; p < D; ++p) {
+                for (int j = tid; j < kk; j += kLruThreads) emit(((size_t)b * D + p) * top_k + j);
+                __syncthreads();  // this position's claims before the next one's
+            }
+        } else {
+            for (int e = tid; e < D * kk; e += kLruThreads) {
+                const int p = e / kk;
+                emit(((size_t)b * D + p) * top_k + (e - p * kk));
+            }
         }
     }
 
@@ -580,7 +635,8 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
                             GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
                             uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
-                            uint16_t* stage_rows, int2* rdcp, int32_t* phys, int64_t max_tokens_now) {
+                            uint16_t* stage_rows, int2* rdcp, int32_t* phys, bool sort_winners,
+                            int64_t max_tokens_now) {
     const int64_t C = ring_capacity(S, D, top_k);
     const int64_t wpr = winner_words(cap);
     // B merge blocks, then (early copy) B * copy_per_seq copy blocks of
@@ -594,7 +650,7 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                        evict_old, counts, glist, layer_stats, do_refine ? 1 : 0, B, copy_per_seq, copy_words,
                        miss_bits,
                        reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<const uint4*>(recent_layer),
-                       reinterpret_cast<uint4*>(stage_rows), miss_bits ? rdcp : nullptr, phys);
+                       reinterpret_cast<uint4*>(stage_rows), miss_bits ? rdcp : nullptr, phys, sort_winners ? 1 : 0);
     return hipGetLastError();
 }
 

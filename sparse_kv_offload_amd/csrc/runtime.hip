@@ -631,7 +631,9 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
                                      ring0, ring1, ring_pos, ring_state, B, D, k, S, cap, t, h->misses, h->victims,
                                      h->evict_old, h->counts, h->glist, h->stats + (size_t)layer * 8, !staged,
                                      staged ? h->miss_bits : nullptr, pool_layer, recent_layer, h->stage_rows,
-                                     staged ? h->rdcp : nullptr, h->phys, max_now);
+                                     staged ? h->rdcp : nullptr, h->phys,
+                                     /* the split attention reads the lists during this launch */ !h->hit_overlap,
+                                     max_now);
          })))
         return rc;
     // late copy: its own gather from the pool; fused or early: the attention

@@ -131,7 +131,8 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
                             GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
                             uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
-                            uint16_t* stage_rows, int2* rdcp, int32_t* phys, int64_t max_tokens_now);
+                            uint16_t* stage_rows, int2* rdcp, int32_t* phys, bool sort_winners,
+                            int64_t max_tokens_now);
 // Copy blocks of the early copy: copy_per_seq per sequence, each owning
 // copy_words bitmap words (a multiple of 4, at most 1024).
 void copy_shape(int B, int64_t max_tokens_now, int* copy_per_seq, int* copy_words);
@@ -143,7 +144,9 @@ void copy_shape(int B, int64_t max_tokens_now, int* copy_per_seq, int* copy_word
 // one entry of each miss the victim slot to move it into (else -1); the
 // early miss copy, overlapping the LRU update.  The bits stay set; the
 // attention launch clears them.)  In every copy the newest token's row
-// comes from recent_layer [B][576] instead of the pool.
+// comes from recent_layer [B][576] instead of the pool.  With sort_winners
+// (and at most 16 positions) the merge blocks first rewrite each
+// position's top-k list in token order, in every copy arrangement.
 // Late copy from the pool into the slots.  Work list: sequence b's entries
 // are glist[b * D*k + r], r < counts[b][2].
 hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const int32_t* counts,
