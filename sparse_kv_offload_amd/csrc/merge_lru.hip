@@ -361,8 +361,11 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     //     entry is a miss); a position's list is then U's entries marked p,
     //     placed by one scan.  A position whose marks do not add up to its
     //     count (which a well-formed list never gives) keeps its order.
+    //     With one position U is the list itself: step 2 writes it back,
+    //     with the residency bit that the selection packed (cs == -1 then
+    //     as now, since only this launch changes cs).
     const bool sorted_lists = sort_winners && D <= 16;
-    if (sorted_lists) {
+    if (sorted_lists && D > 1) {
         for (int i = tid; i < nU; i += kLruThreads) marks[i] = 0u;
         __syncthreads();
         for (int e = tid; e < D * kk; e += kLruThreads) {
@@ -409,6 +412,12 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     }
 #pragma unroll
     for (int q = 0; q < kMaxPer; ++q) nm_loc += (u0 + q < u1 && slot_of[q] < 0) ? 1 : 0;
+    if (sorted_lists && D == 1 && nU == kk) {
+        int32_t* __restrict__ row = topk + (size_t)b * top_k;
+#pragma unroll
+        for (int q = 0; q < kMaxPer; ++q)
+            if (u0 + q < u1) row[u0 + q] = ulist[u0 + q] | (slot_of[q] == -1 ? (int32_t)0x80000000u : 0);
+    }
     int nM;
     int mo = block_exclusive_scan<kLruThreads>(nm_loc, &nM, scratch);
 #pragma unroll
