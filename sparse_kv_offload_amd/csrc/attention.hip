@@ -372,23 +372,36 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* _
     const int hg = h / kAttnHeadGroup, hl = h - hg * kAttnHeadGroup;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const size_t pbase = ((size_t)bp * HG + hg) * nchunk;
+    // each thread's (m, l) pairs stay in registers between the max and the
+    // weights (nchunk <= kMaxChunks: at most kCombinePer per thread)
+    constexpr int kCombinePer = kMaxChunks / kCombineThreads;
+    float mv[kCombinePer], lv[kCombinePer];
     float mloc = -INFINITY;
-    for (int c = tid; c < nchunk; c += kCombineThreads) {
-        const float m = part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2];
-        const float l = part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2 + 1];
-        if (l > 0.0f) mloc = fmaxf(mloc, m);
+#pragma unroll
+    for (int i = 0; i < kCombinePer; ++i) {
+        const int c = tid + i * kCombineThreads;
+        mv[i] = -INFINITY;
+        lv[i] = 0.0f;
+        if (c < nchunk) {
+            const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((pbase + c) * kAttnHeadGroup + hl) * 2);
+            mv[i] = ml.x;
+            lv[i] = ml.y;
+            if (ml.y > 0.0f) mloc = fmaxf(mloc, ml.x);
+        }
     }
     for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
     if (lane == 0) red[wid] = mloc;
     __syncthreads();
     const float M = fmaxf(red[0], red[1]);
     float lsum = 0.0f;
-    for (int c = tid; c < nchunk; c += kCombineThreads) {
-        const float m = part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2];
-        const float l = part_ml[((pbase + c) * kAttnHeadGroup + hl) * 2 + 1];
-        const float wc = (l > 0.0f) ? exp2f(m - M) : 0.0f;
-        wgt[c] = wc;
-        lsum += wc * l;
+#pragma unroll
+    for (int i = 0; i < kCombinePer; ++i) {
+        const int c = tid + i * kCombineThreads;
+        if (c < nchunk) {
+            const float wc = (lv[i] > 0.0f) ? exp2f(mv[i] - M) : 0.0f;
+            wgt[c] = wc;
+            lsum += wc * lv[i];
+        }
     }
     for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
     if (lane == 0) red[2 + wid] = lsum;
