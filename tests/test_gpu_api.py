@@ -99,6 +99,11 @@ def test_streams_give_the_same_results(flags_name):
         for a, b in zip(ref[0], other[0]):
             assert np.array_equal(a, b), float(np.abs(a - b).max())
     assert ref[3] == [W.steps] * W.layers == one[3] == alt[3]
+    # two positions: each position's list in token order, the same on every stream
+    for top, t1, t2 in zip(ref[4], one[4], alt[4]):
+        assert np.array_equal(top, t1) and np.array_equal(top, t2)
+        tok = (top & 0x7FFFFFFF).astype(np.int64)
+        assert (np.diff(tok, axis=-1) > 0).all()
 
 
 W1 = synth.Workload("api1", layers=2, batch=3, context=3000, steps=4, top_k=128, hot_slots=200, positions=1,
