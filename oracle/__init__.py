@@ -44,6 +44,9 @@ MUTATIONS = {
     "c8_query_not_rotated": 14,
     "c8_scale_255": 15,
     "c8_no_query_scale": 16,
+    "step_victim_slot_desc": 17,
+    "step_miss_desc": 18,
+    "append_offset": 19,
 }
 
 
@@ -200,7 +203,8 @@ class LRUState:
                                       _p(self.last_use), self.S, self.t, _p(sel), n,
                                       _p(misses), _p(victims), _p(old), _p(nh))
         if nm < 0:
-            raise RuntimeError("oracle LRU failed: not enough victims")
+            raise RuntimeError(f"oracle LRU failed ({nm}: -5 = not enough victims, "
+                               "-7 = a residency flag disagrees with the table)")
         self.t += 1
         return {"misses": misses[:nm].copy(), "victims": victims[:nm].copy(),
                 "evict_old": old[:nm].copy(), "hits": int(nh[0])}

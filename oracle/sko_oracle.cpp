@@ -51,9 +51,13 @@
 //     score (keys, top-k order, residency, LRU, attention) is unchanged.
 //
 // Parity status: every function below is pinned by tests/test_oracle_pins.py
-// (closed forms, brute force, a hand-simulated LRU trace and invariants);
-// the per-step statistics (hit rate, miss count) have no printed values on
-// the pages and are pinned only by the invariants.
+// (closed forms, brute force, a hand-simulated LRU trace, an independent
+// recency-list formulation and invariants).  The decode step and the
+// scripted LRU entry point run one merge-and-update routine, and the whole
+// step is also replayed against the pinned parts (keys from the per-row
+// score, winners by a full sort, misses / victims / tables from the
+// recency-list formulation).  The per-step statistics (hit rate, miss count)
+// have no printed values on the pages and are pinned only by the invariants.
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -88,6 +92,11 @@ enum Mutation {
     MUT_C8_QUERY_NOT_ROTATED = 14, // keys rotated, the query not
     MUT_C8_SCALE_255 = 15,         // s = a / 255 (codes saturate)
     MUT_C8_NO_QUERY_SCALE = 16,    // score misses the factor s_q
+    // slips confined to the decode step's own path (the scripted LRU entry
+    // point and the pin functions stay correct)
+    MUT_STEP_VICTIM_SLOT_DESC = 17, // decode step: victims in descending slot order
+    MUT_STEP_MISS_DESC = 18,        // decode step: misses paired with victims in descending order
+    MUT_APPEND_OFFSET = 19,         // append: indexer rows stored one place later
 };
 
 inline float bf16_to_f32(uint16_t h) {
@@ -263,10 +272,69 @@ std::vector<int32_t> topk_indices(const std::vector<float>& s, int k) {
 }
 
 // Packed int32 candidate: token index with the residency read from cache_slots.
-inline int32_t pack_candidate(int32_t token, const std::vector<int32_t>& cache_slots) {
+inline int32_t pack_candidate(int32_t token, const int32_t* cache_slots) {
     bool miss = cache_slots[token] == -1;
     if (g_mutation == MUT_FLAG_INVERTED) miss = !miss;
     return (int32_t)((uint32_t)token | (miss ? 0x80000000u : 0u));
+}
+
+// What one residency update did to one (layer, seq) table.
+struct LruStep {
+    int32_t n_union = 0, n_hits = 0;
+    std::vector<int32_t> misses, victims, evict_old;  // r-th miss -> r-th victim, its old owner
+};
+
+// Merge the position lists and update the residency table: the one routine
+// behind both the decode step and the scripted LRU entry point.
+//   packed: every position's winners, concatenated, each carrying its
+//           residency flag (bit 31 = absent at step start).
+// U = the distinct tokens, ascending; H = those flagged resident, M = those
+// flagged absent (both ascending).  Hits are stamped t; the victims are the
+// slots whose stamp is below t in ascending (last_use, slot) order; the r-th
+// miss takes the r-th victim and evicts its previous owner.
+// Returns 0, -5 when the slots run out (impossible when S >= D k), or -7 when
+// a flag disagrees with the table.
+int merge_and_update(int32_t* cache_slots, int32_t* slot_token, int32_t* last_use, int S, int32_t t,
+                     std::vector<int32_t> U, bool from_step, LruStep& out) {
+    std::sort(U.begin(), U.end(), [](int32_t a, int32_t x) { return (a & 0x7FFFFFFF) < (x & 0x7FFFFFFF); });
+    if (g_mutation != MUT_NO_DEDUPE)
+        U.erase(std::unique(U.begin(), U.end(), [](int32_t a, int32_t x) {
+                    return (a & 0x7FFFFFFF) == (x & 0x7FFFFFFF);
+                }), U.end());
+    std::vector<int32_t> Hs, Ms;
+    for (int32_t v : U) {
+        const int32_t tok = v & 0x7FFFFFFF;
+        if ((v < 0) != (cache_slots[tok] == -1)) return -7;
+        (v < 0 ? Ms : Hs).push_back(tok);
+    }
+    if (from_step && g_mutation == MUT_STEP_MISS_DESC) std::reverse(Ms.begin(), Ms.end());
+    if (g_mutation != MUT_HITS_NOT_STAMPED)
+        for (int32_t tok : Hs) last_use[cache_slots[tok]] = t;
+    std::vector<std::pair<int32_t, int32_t>> order;  // (last_use, slot)
+    for (int s = 0; s < S; ++s)
+        if (last_use[s] < t) order.push_back({last_use[s], s});
+    if (g_mutation == MUT_VICTIM_SLOT_DESC || (from_step && g_mutation == MUT_STEP_VICTIM_SLOT_DESC))
+        std::sort(order.begin(), order.end(), [](auto a, auto x) {
+            return a.first != x.first ? a.first < x.first : a.second > x.second;
+        });
+    else if (g_mutation == MUT_VICTIM_IGNORE_STAMP)
+        std::sort(order.begin(), order.end(), [](auto a, auto x) { return a.second < x.second; });
+    else
+        std::sort(order.begin(), order.end());
+    if (Ms.size() > order.size()) return -5;
+    for (size_t r = 0; r < Ms.size(); ++r) {
+        const int32_t v = order[r].second, m = Ms[r], old = slot_token[v];
+        if (old >= 0 && g_mutation != MUT_EVICT_KEEPS_OLD) cache_slots[old] = -1;
+        cache_slots[m] = v;
+        slot_token[v] = m;
+        last_use[v] = t;
+        out.misses.push_back(m);
+        out.victims.push_back(v);
+        out.evict_old.push_back(old);
+    }
+    out.n_union = (int32_t)U.size();
+    out.n_hits = (int32_t)Hs.size();
+    return 0;
 }
 
 // Step 7: softmax attention over the selected rows (fp64).
@@ -338,7 +406,14 @@ int oracle_append(void* h, int layer, int seq, const uint16_t* idx_rows, const u
     if (layer < 0 || layer >= o->L || seq < 0 || seq >= o->B || n < 0) return -1;
     Chain& c = o->at(layer, seq);
     if (c.ntok + n > o->cap) return -4;
-    std::memcpy(&c.kidx[(size_t)c.ntok * IDX_DIM], idx_rows, (size_t)n * IDX_DIM * 2);
+    if (g_mutation == MUT_APPEND_OFFSET) {
+        for (int64_t r = 0; r < n; ++r)
+            if (c.ntok + r + 1 < o->cap)
+                std::memcpy(&c.kidx[(size_t)(c.ntok + r + 1) * IDX_DIM], idx_rows + (size_t)r * IDX_DIM,
+                            IDX_DIM * 2);
+    } else {
+        std::memcpy(&c.kidx[(size_t)c.ntok * IDX_DIM], idx_rows, (size_t)n * IDX_DIM * 2);
+    }
     if (o->c8) {
         if (c.kidx8.empty()) {
             c.kidx8.assign((size_t)o->cap * IDX_DIM, 0);
@@ -388,67 +463,36 @@ int oracle_decode_step(void* h, int layer, const uint16_t* q_idx, const uint16_t
             if (keys)
                 for (int64_t i = 0; i < Lt; ++i) keys[((size_t)b * D + p) * o->cap + i] = ordered_key(s[i]);
             std::vector<int32_t> sel = topk_indices(s, k);
-            for (int32_t tok : sel) W[p].push_back(pack_candidate(tok, c.cache_slots));
+            for (int32_t tok : sel) W[p].push_back(pack_candidate(tok, c.cache_slots.data()));
             if (topk) {
                 int32_t* dst = topk + ((size_t)b * D + p) * k;
                 for (int j = 0; j < k; ++j) dst[j] = j < kk ? W[p][j] : 0;
             }
         }
 
-        // Merge the D position lists and deduplicate: U ascending; split by
-        // the packed flag into hits H and misses M (both ascending).
+        // Merge the D position lists, deduplicate and update the residency
+        // table (the one routine the scripted LRU entry point also runs);
+        // then step 5: copy only the missed rows, host pool -> hot buffer.
         std::vector<int32_t> U;
         for (int p = 0; p < D; ++p)
             for (int32_t v : W[p]) U.push_back(v);
-        std::sort(U.begin(), U.end(), [](int32_t a, int32_t x) {
-            return (a & 0x7FFFFFFF) < (x & 0x7FFFFFFF);
-        });
-        if (g_mutation != MUT_NO_DEDUPE)
-            U.erase(std::unique(U.begin(), U.end(), [](int32_t a, int32_t x) {
-                        return (a & 0x7FFFFFFF) == (x & 0x7FFFFFFF);
-                    }), U.end());
-        std::vector<int32_t> Hs, Ms;
-        for (int32_t v : U) {
-            int32_t tok = v & 0x7FFFFFFF;
-            if (v < 0) Ms.push_back(tok); else Hs.push_back(tok);
-        }
-
-        // Step 4: LRU residency update.  Hits keep their slot and are stamped
-        // with t; the misses take the least recently used other slots.
-        if (g_mutation != MUT_HITS_NOT_STAMPED)
-            for (int32_t tok : Hs) c.last_use[c.cache_slots[tok]] = t;
-        std::vector<std::pair<int32_t, int32_t>> order;  // (last_use, slot)
-        for (int s = 0; s < S; ++s)
-            if (c.last_use[s] < t) order.push_back({c.last_use[s], s});
-        if (g_mutation == MUT_VICTIM_SLOT_DESC)
-            std::sort(order.begin(), order.end(), [](auto a, auto x) {
-                return a.first != x.first ? a.first < x.first : a.second > x.second;
-            });
-        else if (g_mutation == MUT_VICTIM_IGNORE_STAMP)
-            std::sort(order.begin(), order.end(), [](auto a, auto x) { return a.second < x.second; });
-        else
-            std::sort(order.begin(), order.end());
+        LruStep st;
+        const int rc = merge_and_update(c.cache_slots.data(), c.slot_token.data(), c.last_use.data(),
+                                        S, t, U, true, st);
+        if (rc < 0) return rc;
+        const int nM = (int)st.misses.size();
         int nEv = 0;
-        const int nM = (int)Ms.size();
-        if ((size_t)nM > order.size()) return -5;  // cannot happen when S >= D*k
         for (int r = 0; r < nM; ++r) {
-            int32_t v = order[r].second, m = Ms[r], old = c.slot_token[v];
-            if (old >= 0) {
-                if (g_mutation != MUT_EVICT_KEEPS_OLD) c.cache_slots[old] = -1;
-                ++nEv;
-            }
-            c.cache_slots[m] = v;
-            c.slot_token[v] = m;
-            c.last_use[v] = t;
-            // Step 5: copy only the missed row, host pool -> hot buffer.
+            const int32_t v = st.victims[r], m = st.misses[r];
+            if (st.evict_old[r] >= 0) ++nEv;
             std::memcpy(&c.hot[(size_t)v * KV_DIM], &c.pool[(size_t)m * KV_DIM], KV_DIM * 2);
             if (misses) misses[(size_t)b * D * k + r] = m;
             if (victims) victims[(size_t)b * D * k + r] = v;
-            if (evict_old) evict_old[(size_t)b * D * k + r] = old;
+            if (evict_old) evict_old[(size_t)b * D * k + r] = st.evict_old[r];
         }
         if (counts) {
             int32_t* cn = counts + (size_t)b * 8;
-            cn[0] = (int32_t)U.size(); cn[1] = (int32_t)Hs.size(); cn[2] = nM; cn[3] = nEv;
+            cn[0] = st.n_union; cn[1] = st.n_hits; cn[2] = nM; cn[3] = nEv;
             cn[4] = kk; cn[5] = (int32_t)Lt; cn[6] = t; cn[7] = 0;
         }
 
@@ -536,42 +580,22 @@ int oracle_topk(const float* s, int64_t n, int k, int32_t* out_idx) {
 int oracle_lru_apply(int32_t* cache_slots, int64_t cap, int32_t* slot_token, int32_t* last_use,
                      int S, int32_t t, const int32_t* sel, int n,
                      int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* n_hits) {
-    std::vector<int32_t> cs(cache_slots, cache_slots + cap);
-    std::vector<int32_t> U;
-    for (int i = 0; i < n; ++i) U.push_back(pack_candidate(sel[i] & 0x7FFFFFFF, cs));
-    std::sort(U.begin(), U.end(), [](int32_t a, int32_t x) { return (a & 0x7FFFFFFF) < (x & 0x7FFFFFFF); });
-    if (g_mutation != MUT_NO_DEDUPE)
-        U.erase(std::unique(U.begin(), U.end(), [](int32_t a, int32_t x) {
-                    return (a & 0x7FFFFFFF) == (x & 0x7FFFFFFF);
-                }), U.end());
-    std::vector<int32_t> Hs, Ms;
-    for (int32_t v : U) (v < 0 ? Ms : Hs).push_back(v & 0x7FFFFFFF);
-    if (g_mutation != MUT_HITS_NOT_STAMPED)
-        for (int32_t tok : Hs) last_use[cache_slots[tok]] = t;
-    std::vector<std::pair<int32_t, int32_t>> order;
-    for (int s = 0; s < S; ++s)
-        if (last_use[s] < t) order.push_back({last_use[s], s});
-    if (g_mutation == MUT_VICTIM_SLOT_DESC)
-        std::sort(order.begin(), order.end(), [](auto a, auto x) {
-            return a.first != x.first ? a.first < x.first : a.second > x.second;
-        });
-    else if (g_mutation == MUT_VICTIM_IGNORE_STAMP)
-        std::sort(order.begin(), order.end(), [](auto a, auto x) { return a.second < x.second; });
-    else
-        std::sort(order.begin(), order.end());
-    if (Ms.size() > order.size()) return -5;
-    for (size_t r = 0; r < Ms.size(); ++r) {
-        int32_t v = order[r].second, m = Ms[r], old = slot_token[v];
-        if (old >= 0 && g_mutation != MUT_EVICT_KEEPS_OLD) cache_slots[old] = -1;
-        cache_slots[m] = v;
-        slot_token[v] = m;
-        last_use[v] = t;
-        misses[r] = m;
-        victims[r] = v;
-        evict_old[r] = old;
+    std::vector<int32_t> packed;
+    for (int i = 0; i < n; ++i) {
+        const int32_t tok = sel[i] & 0x7FFFFFFF;
+        if (tok >= cap) return -1;
+        packed.push_back(pack_candidate(tok, cache_slots));
     }
-    if (n_hits) *n_hits = (int32_t)Hs.size();
-    return (int)Ms.size();
+    LruStep st;
+    const int rc = merge_and_update(cache_slots, slot_token, last_use, S, t, packed, false, st);
+    if (rc < 0) return rc;
+    for (size_t r = 0; r < st.misses.size(); ++r) {
+        misses[r] = st.misses[r];
+        victims[r] = st.victims[r];
+        evict_old[r] = st.evict_old[r];
+    }
+    if (n_hits) *n_hits = st.n_hits;
+    return (int)st.misses.size();
 }
 
 // Attention over explicit rows (for the closed-form pins).

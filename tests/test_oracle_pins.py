@@ -142,12 +142,16 @@ def pin_lru_golden_trace():
 class ListLRU:
     """Independent formulation: an explicit recency list of slots.  Slots
     touched this step (hits and refilled victims) move to the back in slot
-    order; victims come from the front, skipping this step's hit slots."""
+    order; victims come from the front, skipping this step's hit slots.  The
+    step number of each slot's last touch is kept only for comparison; the
+    list order alone decides the victims."""
 
     def __init__(self, S):
         self.order = list(range(S))
         self.slot_of = {}
         self.owner = [-1] * S
+        self.stamp = [-1] * S
+        self.t = 0
 
     def apply(self, selected):
         U = sorted(set(int(x) for x in selected))
@@ -166,6 +170,9 @@ class ListLRU:
             self.owner[v] = m
         touched = sorted(hit_slots | set(victims))
         self.order = [s for s in self.order if s not in set(touched)] + touched
+        for s in touched:
+            self.stamp[s] = self.t
+        self.t += 1
         return misses, victims, olds, len(hits)
 
 
@@ -313,6 +320,84 @@ def pin_dedupe():
         assert a["counts"][0, 0] == w2.top_k
         assert a["counts"][0, 2] == b["counts"][0, 2]
         assert np.array_equal(a["misses"][0, :a["counts"][0, 2]], b["misses"][0, :b["counts"][0, 2]])
+
+
+def replay_decode_steps(c8):
+    """The whole decode step, replayed step by step from the pinned parts:
+    every token's key is the ordered key of the per-row score (score_one, or
+    the int8 pipeline of quantize_row / hadamard_rotate / c8_score) of the
+    synthetic rows regenerated on their own, the winners are a full sort on
+    (key desc, index asc), the flags are residency at step start, misses /
+    victims / evicted owners / hits and the whole tables come from the
+    recency-list formulation fed with that step's winners, the remap is its
+    slot map, and the attention of every (seq, position) is the textbook
+    softmax (numpy, fp64) over the pool rows of those winners."""
+    w = small_workload(D=2, H=2, B=2, steps=10, ctx=180, k=20)
+    o = oracle.Oracle(w.layers, w.batch, w.capacity, w.top_k, w.hot_slots, w.positions, w.heads,
+                      1.0 / 24.0, indexer_c8=c8)
+    lrus = [ListLRU(w.hot_slots) for _ in range(w.batch)]
+    # sequence 0: i.i.d. rows; sequence 1 repeats its first 40 indexer rows,
+    # so every step has tied scores across the top-k boundary
+    idx = [w.index_rows(0, b, 0, w.capacity) for b in range(w.batch)]
+    idx[1][40:] = idx[1][np.arange(40, w.capacity) % 40]
+    kv = [w.kv_rows(0, b, 0, w.capacity) for b in range(w.batch)]
+    for b in range(w.batch):
+        o.append(0, b, idx[b][:w.context], kv[b][:w.context])
+    qs = [w.index_queries(0, b) for b in range(w.batch)]
+    scale = np.float64(np.float32(1.0 / 24.0))
+    for t in range(w.steps):
+        for b in range(w.batch):
+            o.append(0, b, idx[b][w.context + t:w.context + t + 1], kv[b][w.context + t:w.context + t + 1])
+        qi = np.stack([qs[b][t] for b in range(w.batch)])
+        qa = np.stack([w.attn_queries(0, b, t) for b in range(w.batch)])
+        r = o.decode_step(0, qi, qa, want_keys=True)
+        for b in range(w.batch):
+            n = w.context + t + 1
+            kk = min(w.top_k, n)
+            rows, pool = idx[b][:n], kv[b][:n]
+            if c8:
+                kq = [oracle.quantize_row(oracle.hadamard_rotate(rows[i])) for i in range(n)]
+            sel_all, lru = [], lrus[b]
+            for p in range(w.positions):
+                if c8:
+                    q8, sq = oracle.quantize_row(oracle.hadamard_rotate(qi[b, p]))
+                    sc = [oracle.c8_score(q8, sq, kq[i][0], kq[i][1]) for i in range(n)]
+                else:
+                    sc = [oracle.score_one(qi[b, p], rows[i]) for i in range(n)]
+                keys = np.array([oracle.ordered_key(v) for v in sc], np.uint32)
+                assert np.array_equal(r["keys"][b, p, :n], keys), (t, b, p)
+                order = sorted(range(n), key=lambda i: (-int(keys[i]), i))[:kk]
+                W = r["topk"][b, p, :kk]
+                assert (W & 0x7FFFFFFF).tolist() == order, (t, b, p)
+                assert [bool(x < 0) for x in W] == [i not in lru.slot_of for i in order], (t, b, p)
+                sel_all += order
+            nU = len(set(sel_all))
+            m, v, old, nh = lru.apply(sel_all)
+            nM = len(m)
+            assert r["counts"][b, :5].tolist() == [nU, nh, nM, sum(x >= 0 for x in old), kk], (t, b)
+            assert r["misses"][b, :nM].tolist() == m and r["victims"][b, :nM].tolist() == v
+            assert r["evict_old"][b, :nM].tolist() == old
+            st = o.state(0, b)
+            cs = np.full(w.capacity, -1, np.int32)
+            for tok, slot in lru.slot_of.items():
+                cs[tok] = slot
+            assert np.array_equal(st["cache_slots"], cs) and st["slot_token"].tolist() == lru.owner
+            assert st["last_use"].tolist() == lru.stamp
+            for p in range(w.positions):
+                toks = (r["topk"][b, p, :kk] & 0x7FFFFFFF)
+                assert r["phys"][b, p, :kk].tolist() == [lru.slot_of[int(x)] for x in toks]
+                z = (f(qa[b, p]) @ f(pool[toks]).T) * scale
+                want = softmax(z, axis=1) @ f(pool[toks, :512])
+                assert np.allclose(r["out"][b, p], want, rtol=1e-11, atol=1e-13), (t, b, p)
+    o.close()
+
+
+def pin_bf16_decode_replay():
+    replay_decode_steps(False)
+
+
+def pin_c8_decode_replay():
+    replay_decode_steps(True)
 
 
 # ------------------------------------------------- int8 indexer (LIM C8)
@@ -470,7 +555,29 @@ PINS = [pin_score_error_bound, pin_score_special_cases, pin_score_order, pin_ord
         pin_lru_matches_list_formulation, pin_attention_single_row, pin_attention_uniform_mean,
         pin_attention_textbook, pin_attention_peaked, pin_step_invariants, pin_dedupe,
         pin_f16_conversion, pin_hadamard_closed_form, pin_hadamard_error_bound, pin_quantize_row,
-        pin_c8_score_bound, pin_c8_decode_consistent]
+        pin_c8_score_bound, pin_c8_decode_consistent, pin_bf16_decode_replay, pin_c8_decode_replay]
+
+# Slips that the whole-step replay must reject by itself.  It recomputes the
+# step from the part functions (score, ordered key, the int8 pipeline), so
+# slips inside those are left to their own pins; everything the step adds on
+# top (which rows it scores, the order of winners, dedupe, flags, victim
+# order, the miss <-> victim pairing, stamps, evictions, remap, attention
+# wiring) is covered here.
+MUST_CATCH = {
+    "append_offset": "pin_bf16_decode_replay",
+    "step_victim_slot_desc": "pin_bf16_decode_replay",
+    "step_miss_desc": "pin_bf16_decode_replay",
+    "victim_slot_desc": "pin_bf16_decode_replay",
+    "victim_ignore_stamp": "pin_bf16_decode_replay",
+    "hits_not_stamped": "pin_bf16_decode_replay",
+    "evict_keeps_old": "pin_bf16_decode_replay",
+    "no_dedupe": "pin_bf16_decode_replay",
+    "flag_inverted": "pin_bf16_decode_replay",
+    "tie_larger_index": "pin_bf16_decode_replay",
+    "scale_512": "pin_bf16_decode_replay",
+    "v_wrong_slice": "pin_bf16_decode_replay",
+    "c8_query_not_rotated": "pin_c8_decode_replay",
+}
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -491,5 +598,7 @@ def test_planted_mistakes(mutation):
             except (AssertionError, RuntimeError):
                 caught.append(pin.__name__)
         assert caught, f"no pin rejects mutation {mutation}"
+        if mutation in MUST_CATCH:
+            assert MUST_CATCH[mutation] in caught, (mutation, caught)
     finally:
         oracle.set_mutation(0)
