@@ -124,32 +124,112 @@ def traffic_for(kernel: str, workload: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, target_s: float) -> dict:
-    """The oracle as it stands, single-threaded, on layer 0 of the workload,
-    all sequences, for as many decode steps as fit in about target_s."""
+def host_cpu() -> dict:
+    """The host's CPU: logical CPUs, the CPUs this process may run on, and
+    the model name the kernel reports."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def _oracle_chains(w, seqs, nsteps, time_limit, barrier, results):
+    """Worker of the CPU baseline: the oracle as it stands on layer 0 of the
+    workload for the sequences `seqs` (chains are independent per (layer,
+    sequence)), decode steps 0, 1, ... until nsteps are done or time_limit
+    seconds have been spent in them.  Each step's inputs are generated before
+    its timed region; only append + decode_step are timed.  Returns (steps,
+    seconds inside the timed regions, wall clock at the start, at the end)."""
     import oracle
-    o = oracle.Oracle(1, w.batch, w.capacity, w.top_k, w.hot_slots, w.positions, w.heads, 1.0 / 24.0)
-    for b in range(w.batch):
+    o = oracle.Oracle(1, len(seqs), w.capacity, w.top_k, w.hot_slots, w.positions, w.heads, 1.0 / 24.0)
+    for j, b in enumerate(seqs):
         n = w.seq_context(b)
-        o.append(0, b, w.index_rows(0, b, 0, n), w.kv_rows(0, b, 0, n))
-    qs = [w.index_queries(0, b) for b in range(w.batch)]
-    steps, elapsed = 0, 0.0
-    while elapsed < target_s and steps < w.steps:
-        t = steps
-        rows_i = [w.index_rows(0, b, w.seq_context(b) + t, 1) for b in range(w.batch)]
-        rows_k = [w.kv_rows(0, b, w.seq_context(b) + t, 1) for b in range(w.batch)]
-        qi = np.stack([qs[b][t] for b in range(w.batch)])
-        qa = np.stack([w.attn_queries(0, b, t) for b in range(w.batch)])
+        o.append(0, j, w.index_rows(0, b, 0, n), w.kv_rows(0, b, 0, n))
+    qs = [w.index_queries(0, b, nsteps) for b in seqs]
+
+    def inputs(t):
+        return ([w.index_rows(0, b, w.seq_context(b) + t, 1) for b in seqs],
+                [w.kv_rows(0, b, w.seq_context(b) + t, 1) for b in seqs],
+                np.stack([q[t] for q in qs]),
+                np.stack([w.attn_queries(0, b, t) for b in seqs]))
+
+    # a worker of the all-core run holds every step's inputs before the
+    # common start, so its wall time is oracle work only
+    ready = [inputs(t) for t in range(nsteps)] if barrier is not None else [inputs(0)]
+    if barrier is not None:
+        barrier.wait()
+    wall0, busy, t = time.time(), 0.0, 0
+    while t < nsteps and busy < time_limit:
+        rows_i, rows_k, qi, qa = ready[t] if barrier is not None else ready[0]
         t0 = time.perf_counter()
-        for b in range(w.batch):
-            o.append(0, b, rows_i[b], rows_k[b])
+        for j in range(len(seqs)):
+            o.append(0, j, rows_i[j], rows_k[j])
         o.decode_step(0, qi, qa)
-        elapsed += time.perf_counter() - t0
-        steps += 1
+        busy += time.perf_counter() - t0
+        t += 1
+        if barrier is None and t < nsteps:
+            ready[0] = inputs(t)
+    wall1 = time.time()
     o.close()
-    return {"value": steps / elapsed, "unit": "layer-steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"layer 0 of '{w.name}', all {w.batch} sequences, decode steps 0..{steps - 1} "
-                      f"(cold step included), {elapsed:.1f} s single-threaded"}
+    if results is not None:
+        results.put((t, busy, wall0, wall1))
+    return t, busy, wall0, wall1
+
+
+def cpu_baseline(w, target_s: float, max_workers: int = 16) -> dict:
+    """The oracle as it stands, timed on the host cores on layer 0 of the
+    workload, all sequences, decode steps from the cold step on.  First on one
+    thread, for about target_s; then with the independent sequence chains
+    spread over worker processes (one oracle per worker, sequences dealt
+    round-robin) on every CPU this process may use, at most max_workers, for
+    about target_s of wall time.  The oracle's arithmetic is the same in both;
+    the all-core rate is the step count over the wall time from the common
+    start to the last worker's end."""
+    import multiprocessing as mp
+    host = host_cpu()
+    n1, busy, _, _ = _oracle_chains(w, list(range(w.batch)), w.steps, target_s, None, None)
+    single = {"value": round(n1 / busy, 4), "unit": "layer-steps/s", "cores": 1, "kind": "oracle",
+              "sample": f"layer 0 of '{w.name}', all {w.batch} sequences, decode steps 0..{n1 - 1} "
+                        f"(cold step included), {busy:.1f} s on one thread"}
+    workers = max(1, min(w.batch, host["affinity"], max_workers))
+    per_worker = -(-w.batch // workers)
+    # steps that fill about target_s on the slowest worker (it holds per_worker chains)
+    nsteps = max(1, min(w.steps, int(target_s * n1 / busy * w.batch / per_worker)))
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(workers)
+    results = ctx.Queue()
+    procs = [ctx.Process(target=_oracle_chains,
+                         args=(w, list(range(j, w.batch, workers)), nsteps, float("inf"), barrier, results))
+             for j in range(workers)]
+    # one thread per worker: the input generator's own OpenMP pool would
+    # otherwise oversubscribe the cores the workers share
+    omp = os.environ.get("OMP_NUM_THREADS")
+    os.environ["OMP_NUM_THREADS"] = "1"
+    try:
+        for pr in procs:
+            pr.start()
+    finally:
+        if omp is None:
+            del os.environ["OMP_NUM_THREADS"]
+        else:
+            os.environ["OMP_NUM_THREADS"] = omp
+    got = [results.get() for _ in procs]
+    for pr in procs:
+        pr.join()
+    if any(pr.exitcode != 0 for pr in procs):
+        raise RuntimeError("an oracle worker failed")
+    wall = max(g[3] for g in got) - min(g[2] for g in got)
+    return {"value": round(nsteps / wall, 4), "unit": "layer-steps/s", "cores": workers, "kind": "oracle",
+            "sample": f"layer 0 of '{w.name}', all {w.batch} sequences dealt over {workers} worker processes "
+                      f"(one oracle each), decode steps 0..{nsteps - 1} (cold step included), "
+                      f"{wall:.1f} s wall",
+            "single_thread": single, "host": host}
 
 
 class _DeviceBytes:
@@ -204,6 +284,8 @@ def prefill_bench(args) -> int:
                 P_l = pf.tokens(l)
                 buf = torch.as_tensor(_DeviceBytes(ptr, cap * row), device="cuda")
                 buf[P_l * row:(P_l + chunk) * row].copy_(rows)
+                # the alias of the library's buffer ends with the layer
+                del buf
                 pf.end_layer(l, chunk)
             pf.sync()
             wall = time.perf_counter() - t0
@@ -222,6 +304,12 @@ def prefill_bench(args) -> int:
             # the next setting starts from the same prefix
             for l in range(N):
                 pf.set_tokens(l, prefix)
+        # nothing queued on any stream may touch the library's buffers once
+        # the handle is destroyed
+        torch.cuda.synchronize()
+        pf.sync()
+    del rows
+    torch.cuda.synchronize()
     print(json.dumps({"metric": "layerwise prefill offload: exposed transfer delay per pass",
                       "unit": "ms", "layers": N, "row_bytes": row, "prefix_tokens": prefix,
                       "chunk_tokens": chunk, "trays": "B0 bound to layer 0 + 3 rotating", "lookahead": 1,
@@ -234,9 +322,12 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=56)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="small")
+    ap.add_argument("--workload", default="shelf_ctx8",
+                    help="tiny, small, mtp3, shelf_ctx8 (the largest single-GPU workload; default), "
+                         "shelf_ctx4 or long")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
-    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
+                    help="about this long for each of the two oracle timings (one thread, all cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="time without per-stage events")
     ap.add_argument("--indexer", choices=["bf16", "c8"], default="bf16",
@@ -266,15 +357,24 @@ def main() -> int:
     if args.prefill:
         return prefill_bench(args)
 
-    import torch
     import synth
-    import sparse_kv_offload_amd as sko
 
     w = synth.WORKLOADS[args.workload]
     L = args.layers or w.layers
     T = args.warmup + args.steps
     if T > w.steps:
         w = w.replace(steps=T)
+    # The oracle's timing runs first, in worker processes started before this
+    # process touches the GPU.
+    cpu_base = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host cores ...")
+        cpu_base = cpu_baseline(w, args.cpu_baseline_seconds)
+        log(f"oracle: {cpu_base['single_thread']['value']} layer-steps/s on 1 thread, "
+            f"{cpu_base['value']} on {cpu_base['cores']}")
+
+    import torch
+    import sparse_kv_offload_amd as sko
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     B, D, H, k = w.batch, w.positions, w.heads, w.top_k
@@ -482,9 +582,8 @@ def main() -> int:
     }
     h.close()
     del new_idx, new_kv, q_idx, q_attn
-    if not args.no_cpu_baseline:
-        log("timing the oracle on the host cores ...")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_baseline_seconds)
+    if cpu_base is not None:
+        result["cpu_baseline"] = cpu_base
     print(json.dumps(result), flush=True)
     return 0
 

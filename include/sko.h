@@ -28,7 +28,12 @@
  *    leaving partial data; section 7 of the same page).
  *  - A HIP runtime failure after validation marks the handle FAILED; every
  *    later call except sko_destroy returns SKO_E_STATE (no silent
- *    corruption, no retry).
+ *    corruption, no retry).  So does a broken residency invariant that a
+ *    decode step found on the device (a miss with no victim slot left, a
+ *    slot or token out of range: that step's rows are incomplete): the
+ *    kernel counts it, and the next synchronizing read (sko_read_step,
+ *    sko_read_table, sko_get_stats) marks the handle FAILED and returns
+ *    SKO_E_STATE.
  *  - A handle is not thread-safe: drive it from one host thread.
  *  - All device work is enqueued on the stream given at create (or set by
  *    sko_set_stream), in call order (SKO_FLAG_HIT_OVERLAP also uses an
@@ -49,7 +54,7 @@ extern "C" {
 #define SKO_E_NOMEM (-2)       /* host pinned or device allocation failed */
 #define SKO_E_DEVICE (-3)      /* HIP runtime error (handle is now FAILED) */
 #define SKO_E_CAPACITY (-4)    /* append beyond max_tokens */
-#define SKO_E_STATE (-5)       /* handle FAILED by an earlier device error */
+#define SKO_E_STATE (-5)       /* handle FAILED (device error or broken invariant), or state not kept */
 #define SKO_E_UNSUPPORTED (-6) /* valid but outside what the kernels support */
 
 #define SKO_ALL_SEQS (-1)
@@ -107,6 +112,10 @@ extern "C" {
  * output differs only in fp32 summation order.  SKO_E_INVAL with
  * SKO_FLAG_FUSED_COPY or SKO_FLAG_LATE_COPY. */
 #define SKO_FLAG_HIT_OVERLAP 0x100u
+/* Testing only: the LRU-update launch reports a broken residency invariant
+ * for sequence 0 at every step while doing its normal work, so that the
+ * reporting path below can be exercised without a real fault. */
+#define SKO_FLAG_TEST_VIOLATION 0x200u
 
 typedef struct sko_handle sko_handle;
 
@@ -171,7 +180,14 @@ typedef struct sko_layer_stats {
  */
 int sko_create(const sko_config* cfg, void* stream, sko_handle** out);
 
-/* Replace the stream used for later calls (caller-owned hipStream_t). */
+/*
+ * Replace the stream used for later calls (caller-owned hipStream_t).  The
+ * new stream is made to wait (by an event) for everything already enqueued
+ * on the old one, so no host synchronization is needed around a switch, and
+ * later synchronizing calls (reads, sko_destroy) cover the work of both.
+ * The old stream must stay valid until this call returns.
+ * Errors: SKO_E_INVAL (NULL handle), SKO_E_STATE, SKO_E_DEVICE.
+ */
 int sko_set_stream(sko_handle* h, void* stream);
 
 /*

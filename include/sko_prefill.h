@@ -78,7 +78,9 @@ typedef struct sko_prefill_config {
  */
 int sko_prefill_create(const sko_prefill_config* cfg, void* compute_stream, sko_prefill_handle** out);
 
-/* sko_prefill_destroy — synchronize and free everything (NULL: no-op). */
+/* sko_prefill_destroy — synchronize the load, save and compute streams, then
+ * free everything (NULL: no-op).  Device aliases of the layer buffers that
+ * begin_layer handed out are invalid afterwards. */
 int sko_prefill_destroy(sko_prefill_handle* h);
 
 /*

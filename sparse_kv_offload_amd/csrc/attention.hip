@@ -31,7 +31,7 @@
 // 128 of the 512 output columns (M = 16 columns, N = 16 heads, K = 32
 // rows).  P enters the MFMA in bf16; accumulation is fp32.  Each block
 // writes (m, l, acc) partials; k_attn_combine merges them.
-#include "sko_common.cuh"
+#include "sko_common.h"
 #include "sko_internal.h"
 
 namespace sko {

@@ -8,7 +8,7 @@
 // into their victim slots of the hot buffer.  The work list (source row,
 // destination row) of every sequence comes from the LRU kernel, with the
 // per-sequence miss counts on the device, so no host sync is needed.
-#include "sko_common.cuh"
+#include "sko_common.h"
 #include "sko_internal.h"
 
 namespace sko {

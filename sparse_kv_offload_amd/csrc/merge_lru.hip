@@ -29,7 +29,7 @@
 // top-k of its D rows whose threshold bucket had to be split (exact radix
 // select on the staged candidates); after it, it clears its rows' histograms
 // and records for the next step.
-#include "sko_common.cuh"
+#include "sko_common.h"
 #include "sko_internal.h"
 
 namespace sko {
@@ -275,7 +275,8 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     int32_t* __restrict__ evict_old, int32_t* __restrict__ counts, GatherEntry* __restrict__ glist,
     unsigned long long* __restrict__ layer_stats, int do_refine, int nseq, int copy_per_seq, int copy_words,
     uint32_t* __restrict__ miss_bits, const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
-    uint4* __restrict__ stage_rows, int2* __restrict__ rdcp, int32_t* __restrict__ phys, int sort_winners) {
+    uint4* __restrict__ stage_rows, int2* __restrict__ rdcp, int32_t* __restrict__ phys, int sort_winners,
+    int test_violation) {
     __shared__ uint32_t touched[kMaxHotSlots / 32];
     // [0, kMaxMerge): misses; [kMaxMerge, 2 kMaxMerge): the union, later the
     // victims.  Before the merge the whole area stages refine candidates.
@@ -618,6 +619,12 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
         if (Lt > 0 && cs[Lt - 1] >= 0) atomicAdd(&layer_stats[6], 1ull);
         cnt[0] = nU; cnt[1] = nH; cnt[2] = nM; cnt[3] = nEv;
         cnt[4] = kk; cnt[5] = (int32_t)Lt; cnt[6] = t;
+        // a broken residency invariant (a miss without a victim, or a slot
+        // or token out of range) is counted per layer, and the host refuses
+        // further reads of the handle; the test switch raises the flag for
+        // sequence 0 without changing any other work
+        if (test_violation && b == 0) cnt[7] = 1;
+        if (cnt[7]) atomicAdd(&layer_stats[7], 1ull);
         atomicAdd(&layer_stats[1], (unsigned long long)nU);
         atomicAdd(&layer_stats[2], (unsigned long long)nH);
         atomicAdd(&layer_stats[3], (unsigned long long)nM);
@@ -645,7 +652,7 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
                             uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
                             uint16_t* stage_rows, int2* rdcp, int32_t* phys, bool sort_winners,
-                            int64_t max_tokens_now) {
+                            int64_t max_tokens_now, bool test_violation) {
     const int64_t C = ring_capacity(S, D, top_k);
     const int64_t wpr = winner_words(cap);
     // B merge blocks, then (early copy) B * copy_per_seq copy blocks of
@@ -659,7 +666,8 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                        evict_old, counts, glist, layer_stats, do_refine ? 1 : 0, B, copy_per_seq, copy_words,
                        miss_bits,
                        reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<const uint4*>(recent_layer),
-                       reinterpret_cast<uint4*>(stage_rows), miss_bits ? rdcp : nullptr, phys, sort_winners ? 1 : 0);
+                       reinterpret_cast<uint4*>(stage_rows), miss_bits ? rdcp : nullptr, phys, sort_winners ? 1 : 0,
+                       test_violation ? 1 : 0);
     return hipGetLastError();
 }
 

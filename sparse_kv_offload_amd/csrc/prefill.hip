@@ -265,6 +265,9 @@ int sko_prefill_create(const sko_prefill_config* cfg, void* compute_stream, sko_
 int sko_prefill_destroy(sko_prefill_handle* h) {
     if (!h) return SKO_OK;
     Guard g(h->cfg.device);
+    // the caller's compute stream may still wait on the library's events or
+    // write into its buffers: drain it too before anything is freed
+    (void)hipStreamSynchronize(h->compute);
     if (h->load) (void)hipStreamSynchronize(h->load);
     if (h->save) (void)hipStreamSynchronize(h->save);
     free_all(h);

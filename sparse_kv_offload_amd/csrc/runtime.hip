@@ -104,6 +104,7 @@ struct sko_handle {
     bool hit_overlap = false;
     hipStream_t side = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    hipEvent_t ev_switch = nullptr;  // orders the old stream's work before the new one's (sko_set_stream)
     uint16_t* staging = nullptr;    // device rows for host-source appends
     uint16_t* hot = nullptr;        // [L][B][S][576]
     uint16_t* recent = nullptr;     // [L][B][576] device copy of each sequence's newest main-KV row
@@ -192,6 +193,8 @@ void free_all(sko_handle* h) {
     for (auto e : h->spare) (void)hipEventDestroy(e);
     if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
     if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+    if (h->ev_switch) (void)hipEventDestroy(h->ev_switch);
+    h->ev_switch = nullptr;
     if (h->side) (void)hipStreamDestroy(h->side);
     h->ev_fork = h->ev_join = nullptr;
     h->side = nullptr;
@@ -241,7 +244,26 @@ int run_stage(sko_handle* h, int stage, F&& launch) {
 
 int check_handle(sko_handle* h) {
     if (!h) return set_err(SKO_E_INVAL, "NULL handle");
-    if (h->failed) return set_err(SKO_E_STATE, "handle is FAILED after an earlier device error");
+    if (h->failed) return set_err(SKO_E_STATE, "handle is FAILED after an earlier device error or a broken invariant");
+    return SKO_OK;
+}
+
+// After a stream synchronize: a merge launch that found a residency
+// invariant broken (a miss without a victim, a slot or token out of range)
+// counted it in its layer's statistics.  The results of that step are
+// incomplete, so the handle is marked FAILED and the read is refused.
+int check_invariants(sko_handle* h) {
+    std::vector<unsigned long long> v((size_t)h->L * 8);
+    const hipError_t e = hipMemcpy(v.data(), h->stats, v.size() * 8, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return device_fail(h, e, "read invariant flags");
+    for (int l = 0; l < h->L; ++l)
+        if (v[(size_t)l * 8 + 7] != 0) {
+            h->failed = true;
+            return set_err(SKO_E_STATE,
+                           "layer %d: %llu sequence-steps broke a residency invariant (a miss without a "
+                           "victim, or a slot or token out of range); the handle is FAILED",
+                           l, v[(size_t)l * 8 + 7]);
+        }
     return SKO_OK;
 }
 
@@ -261,7 +283,8 @@ int validate_config(const sko_config* c) {
         return set_err(SKO_E_INVAL, "attn_scale must be finite and > 0");
     if ((c->flags & ~(SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT | SKO_FLAG_KEEP_KEYS |
                       SKO_FLAG_SELECT_RESCAN | SKO_FLAG_FUSED_COPY | SKO_FLAG_LATE_COPY |
-                      SKO_FLAG_EARLY_COPY | SKO_FLAG_INDEXER_C8 | SKO_FLAG_HIT_OVERLAP)) != 0 ||
+                      SKO_FLAG_EARLY_COPY | SKO_FLAG_INDEXER_C8 | SKO_FLAG_HIT_OVERLAP |
+                      SKO_FLAG_TEST_VIOLATION)) != 0 ||
         (c->flags & (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT)) ==
             (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT))
         return set_err(SKO_E_INVAL, "unknown or conflicting flags 0x%x", c->flags);
@@ -431,6 +454,13 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
         delete h;
         return set_err(SKO_E_NOMEM, "device allocation failed");
     }
+    if (hipEventCreateWithFlags(&h->ev_switch, hipEventDisableTiming) != hipSuccess) {
+        (void)hipGetLastError();
+        h->ev_switch = nullptr;
+        free_all(h);
+        delete h;
+        return set_err(SKO_E_DEVICE, "creating the stream-switch event failed");
+    }
     if (h->hit_overlap &&
         (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
          hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
@@ -480,7 +510,17 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
 int sko_set_stream(sko_handle* h, void* stream) {
     int rc = check_handle(h);
     if (rc != SKO_OK) return rc;
-    h->stream = (hipStream_t)stream;
+    const hipStream_t ns = (hipStream_t)stream;
+    if (ns == h->stream) return SKO_OK;
+    // Every step reads and writes the same handle state, so the new stream
+    // waits for whatever is queued on the old one; later synchronizations
+    // (reads, destroy) then cover both.
+    DeviceGuard guard(h->cfg.device);
+    if (!guard.ok) return device_fail(h, hipErrorInvalidDevice, "hipSetDevice");
+    hipError_t e = hipEventRecord(h->ev_switch, h->stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ns, h->ev_switch, 0);
+    if (e != hipSuccess) return device_fail(h, e, "ordering the new stream after the old one");
+    h->stream = ns;
     return SKO_OK;
 }
 
@@ -633,7 +673,7 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
                                      staged ? h->miss_bits : nullptr, pool_layer, recent_layer, h->stage_rows,
                                      staged ? h->rdcp : nullptr, h->phys,
                                      /* the split attention reads the lists during this launch */ !h->hit_overlap,
-                                     max_now);
+                                     max_now, (h->cfg.flags & SKO_FLAG_TEST_VIOLATION) != 0);
          })))
         return rc;
     // late copy: its own gather from the pool; fused or early: the attention
@@ -703,7 +743,9 @@ int sko_read_step(sko_handle* h, int32_t which, void* dst, int64_t bytes) {
     if ((size_t)bytes != size) return set_err(SKO_E_INVAL, "buffer %d holds %zu bytes, got %lld", which, size, (long long)bytes);
     DeviceGuard guard(h->cfg.device);
     hipError_t e = hipStreamSynchronize(h->stream);
-    if (e == hipSuccess && which == SKO_BUF_KEYS)
+    if (e != hipSuccess) return device_fail(h, e, "read step sync");
+    if ((rc = check_invariants(h)) != SKO_OK) return rc;
+    if (which == SKO_BUF_KEYS)
         e = hipMemcpy2D(dst, (size_t)h->cap * 4, src, (size_t)h->kcap * 4, (size_t)h->cap * 4, BD,
                         hipMemcpyDeviceToHost);
     else if (e == hipSuccess)
@@ -743,6 +785,7 @@ int sko_read_table(sko_handle* h, int32_t layer, int32_t seq, int32_t which, voi
     DeviceGuard guard(h->cfg.device);
     hipError_t e = hipStreamSynchronize(h->stream);
     if (e != hipSuccess) return device_fail(h, e, "read table sync");
+    if ((rc = check_invariants(h)) != SKO_OK) return rc;
     if (which == SKO_TAB_NTOK) {
         int64_t v = h->ntok[lb];
         std::memcpy(dst, &v, 8);
@@ -772,7 +815,9 @@ int sko_get_stats(sko_handle* h, int32_t layer, sko_layer_stats* out) {
     DeviceGuard guard(h->cfg.device);
     unsigned long long v[8];
     hipError_t e = hipStreamSynchronize(h->stream);
-    if (e == hipSuccess) e = hipMemcpy(v, h->stats + (size_t)layer * 8, sizeof(v), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return device_fail(h, e, "read stats sync");
+    if ((rc = check_invariants(h)) != SKO_OK) return rc;
+    e = hipMemcpy(v, h->stats + (size_t)layer * 8, sizeof(v), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return device_fail(h, e, "read stats");
     out->steps = h->step[layer];
     out->unique = (int64_t)v[1];

@@ -31,7 +31,7 @@
 
 #include <utility>
 
-#include "sko_common.cuh"
+#include "sko_common.h"
 #include "sko_internal.h"
 
 namespace sko {

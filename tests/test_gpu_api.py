@@ -166,3 +166,99 @@ def test_timing_counts_one_launch_per_layer_step():
         h.set_timing(0)
         assert all(c == 0 for _, c in h.timing().values())
         assert [h.stats(l).steps for l in range(w.layers)] == [n] * w.layers
+
+
+def run_unsynced(stream_plan, flags=0, w=W):
+    """Decode w with every input and output buffer prepared up front and no
+    host synchronization between calls: stream_plan(t, l) gives the stream
+    for layer l at step t, set by sko_set_stream, which alone orders the
+    handle's work across the switch.  Returns every step's output and the
+    final tables, counts and step counters."""
+    import torch
+    import sparse_kv_offload_amd as sko
+    cfg = sko.make_config(num_layers=w.layers, batch=w.batch, max_tokens=w.capacity, num_heads=w.heads,
+                          top_k=w.top_k, hot_slots=w.hot_slots, mtp_positions=w.positions, flags=flags)
+    qch = {(l, b): w.index_queries(l, b, w.steps) for l in range(w.layers) for b in range(w.batch)}
+    ins = [[(dev(np.concatenate([w.index_rows(l, b, w.context + t, 1) for b in range(w.batch)])),
+             dev(np.concatenate([w.kv_rows(l, b, w.context + t, 1) for b in range(w.batch)])),
+             dev(np.stack([qch[(l, b)][t] for b in range(w.batch)])),
+             dev(np.stack([w.attn_queries(l, b, t) for b in range(w.batch)])))
+            for l in range(w.layers)] for t in range(w.steps)]
+    outs = [[torch.zeros((w.batch, w.positions, w.heads, synth.V_DIM), dtype=torch.float32, device="cuda")
+             for _ in range(w.layers)] for _ in range(w.steps)]
+    torch.cuda.synchronize()
+    with sko.SparseKVOffload(cfg, None) as h:
+        for l in range(w.layers):
+            for b in range(w.batch):
+                h.append(l, b, w.index_rows(l, b, 0, w.context), w.kv_rows(l, b, 0, w.context))
+        for t in range(w.steps):
+            for l in range(w.layers):
+                sko.sko_set_stream(h.handle, stream_plan(t, l))
+                ni, nk, qi, qa = ins[t][l]
+                sko.sko_append_token(h.handle, l, sko.SKO_ALL_SEQS, ni, nk, 1, True)
+                sko.sko_decode_step(h.handle, l, qi, qa, outs[t][l])
+        # the read calls synchronize only the last stream
+        tabs = [h.table(l, b, which).copy() for l in range(w.layers) for b in range(w.batch)
+                for which in (sko.SKO_TAB_CACHE_SLOTS, sko.SKO_TAB_SLOT_TOKEN, sko.SKO_TAB_LAST_USE,
+                              sko.SKO_TAB_HOT)]
+        counts = h.step_buffer(sko.SKO_BUF_COUNTS).copy()
+        steps = [h.stats(l).steps for l in range(w.layers)]
+        torch.cuda.synchronize()
+        res = [o.cpu().numpy() for row in outs for o in row]
+    return res, tabs, counts, steps
+
+
+@pytest.mark.parametrize("flags_name", ["early", "late", "hit_overlap"])
+def test_stream_switch_without_host_sync(flags_name):
+    """Switching streams at every layer-step with no host synchronization
+    gives the default stream's output bits, tables and counts."""
+    import torch
+    import sparse_kv_offload_amd as sko
+    flags = {"early": 0, "late": sko.SKO_FLAG_LATE_COPY, "hit_overlap": sko.SKO_FLAG_HIT_OVERLAP}[flags_name]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    log(f"unsynced {flags_name}: default stream")
+    ref = run_unsynced(lambda t, l: None, flags)
+    log(f"unsynced {flags_name}: a new stream at every layer-step")
+    alt = run_unsynced(lambda t, l: streams[(t * W.layers + l) % 3], flags)
+    for a, b in zip(ref[1], alt[1]):
+        assert np.array_equal(a, b)
+    assert np.array_equal(ref[2], alt[2])
+    assert ref[3] == alt[3] == [W.steps] * W.layers
+    for a, b in zip(ref[0], alt[0]):
+        if flags_name == "hit_overlap":  # list order varies with the split attention: rounding only
+            assert np.abs(a - b).max() <= 2e-3
+        else:
+            assert np.array_equal(a, b), float(np.abs(a - b).max())
+
+
+def test_broken_invariant_fails_the_handle():
+    """A residency invariant the merge kernel finds broken is counted on the
+    device and makes the next synchronizing read mark the handle FAILED
+    (forced here by the test switch, which leaves every kernel's work
+    unchanged)."""
+    import torch
+    import sparse_kv_offload_amd as sko
+    w = W1
+    for flags, broken in ((0, False), (sko.SKO_FLAG_TEST_VIOLATION, True)):
+        cfg = sko.make_config(num_layers=1, batch=w.batch, max_tokens=w.capacity, num_heads=w.heads,
+                              top_k=w.top_k, hot_slots=w.hot_slots, mtp_positions=w.positions, flags=flags)
+        with sko.SparseKVOffload(cfg, None) as h:
+            for b in range(w.batch):
+                h.append(0, b, w.index_rows(0, b, 0, w.context + 1), w.kv_rows(0, b, 0, w.context + 1))
+            qi = dev(np.stack([w.index_queries(0, b)[0] for b in range(w.batch)]))
+            qa = dev(np.stack([w.attn_queries(0, b, 0) for b in range(w.batch)]))
+            out = torch.zeros((w.batch, w.positions, w.heads, synth.V_DIM), dtype=torch.float32, device="cuda")
+            h.decode_step(0, qi, qa, out)
+            if not broken:
+                assert h.stats(0).steps == 1
+                continue
+            with pytest.raises(sko.SkoError) as e:
+                h.stats(0)
+            assert e.value.code == sko.SKO_E_STATE and "invariant" in str(e.value)
+            # the handle stays FAILED for every later call
+            with pytest.raises(sko.SkoError) as e:
+                h.decode_step(0, qi, qa, out)
+            assert e.value.code == sko.SKO_E_STATE
+            with pytest.raises(sko.SkoError):
+                h.step_buffer(sko.SKO_BUF_COUNTS)
+        torch.cuda.synchronize()
