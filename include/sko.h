@@ -244,6 +244,29 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
 int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void* q_attn,
                      float* out);
 
+/*
+ * sko_decode_step_static — sko_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same step, arguments and results,
+ * but the kernels' per-step scratch (selection histograms and row records,
+ * candidate lists, winner and miss bitmaps, the per-winner row pairs, the
+ * gather list, the split-K attention partials, the int8 query codes) comes
+ * from one static device array of the library, SKO_STATIC_SCRATCH_BYTES
+ * (160 MiB), instead of the handle's own.  The call allocates nothing.
+ * Each device the library runs on holds that array until the process ends;
+ * its address is looked up at sko_create.  Every call on a device shares
+ * the array, which keeps the last call's contents (the call clears what
+ * must start cleared): calls that can overlap on one device (two handles,
+ * or streams not ordered against each other) race.  No stage timing.
+ * Errors: as sko_decode_step, plus SKO_E_UNSUPPORTED when the handle's step
+ * needs more scratch than the array holds (about 16 B per token of
+ * capacity per sequence and position, plus the attention partials), and
+ * SKO_E_DEVICE when the array's address could not be found at create.
+ */
+#define SKO_STATIC_SCRATCH_BYTES (160ull << 20)
+int sko_decode_step_static(sko_handle* h, int32_t layer, const void* q_idx, const void* q_attn,
+                            float* out);
+
 /* Buffers of the most recent sko_decode_step (any layer), for inspection. */
 enum sko_step_buffer {
     SKO_BUF_TOPK = 1,      /* int32 [B][D][k]: packed winners (bit31 = miss), first `selected` valid, token order

@@ -49,7 +49,8 @@ SKO_TAB_HOT, SKO_TAB_INDEXER, SKO_TAB_POOL, SKO_TAB_NTOK = 4, 5, 6, 7
 SKO_TAB_INDEXER_SCALE = 8
 
 EXPORTED = (
-    "sko_create", "sko_set_stream", "sko_append_token", "sko_decode_step", "sko_read_step",
+    "sko_create", "sko_set_stream", "sko_append_token", "sko_decode_step", "sko_decode_step_static",
+    "sko_read_step",
     "sko_read_table", "sko_get_stats", "sko_set_timing", "sko_get_timing", "sko_stage_name",
     "sko_num_stages", "sko_destroy", "sko_last_error", "sko_version", "sko_link_read_rate",
     # layerwise prefill offload (include/sko_prefill.h)
@@ -117,6 +118,7 @@ def _load() -> ctypes.CDLL:
         "sko_set_stream": (ctypes.c_int, [vp, vp]),
         "sko_append_token": (ctypes.c_int, [vp, i32, i32, vp, vp, i64, i32]),
         "sko_decode_step": (ctypes.c_int, [vp, i32, vp, vp, vp]),
+        "sko_decode_step_static": (ctypes.c_int, [vp, i32, vp, vp, vp]),
         "sko_read_step": (ctypes.c_int, [vp, i32, vp, i64]),
         "sko_read_table": (ctypes.c_int, [vp, i32, i32, i32, vp, i64]),
         "sko_get_stats": (ctypes.c_int, [vp, i32, ctypes.POINTER(SkoLayerStats)]),
@@ -229,6 +231,11 @@ def sko_append_token(h: int, layer: int, seq: int, idx_rows, kv_rows, n: int,
 
 def sko_decode_step(h: int, layer: int, q_idx, q_attn, out) -> None:
     _check(_lib.sko_decode_step(h, layer, _addr(q_idx), _addr(q_attn), _addr(out)), "sko_decode_step")
+
+
+def sko_decode_step_static(h: int, layer: int, q_idx, q_attn, out) -> None:
+    _check(_lib.sko_decode_step_static(h, layer, _addr(q_idx), _addr(q_attn), _addr(out)),
+           "sko_decode_step_static")
 
 
 def sko_read_step(h: int, which: int, dst: np.ndarray) -> np.ndarray:

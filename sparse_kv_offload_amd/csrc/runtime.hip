@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -329,6 +330,222 @@ int attn_rows_per_block(int k, int rows_total_pairs) {
 
 }  // namespace
 
+namespace {
+
+// Per-step scratch of the decode step's kernels.  None of it carries state
+// from one step to the next: the kernels leave the histograms, row records,
+// winner and miss bitmaps cleared for the next step, and everything else is
+// written before it is read within the step.
+struct StepScratch {
+    uint2* pre = nullptr;           // [B][D][cap] candidates at or above the floor
+    uint2* cand = nullptr;          // [B][D][cap] staged bucket keys
+    uint32_t* hist = nullptr;       // [B][D][4096]
+    RowMeta* meta = nullptr;        // [B][D]
+    uint32_t* winners = nullptr;    // [B][wpr]
+    uint32_t* miss_bits = nullptr;  // [B][wpr] (early copy)
+    int2* rdcp = nullptr;           // [B][D][k] (early copy)
+    GatherEntry* glist = nullptr;   // [B*D*k]
+    float* part_acc = nullptr;      // [B*D][HG][nchunk][16][512]
+    float* part_ml = nullptr;       // [B*D][HG][nchunk][16][2]
+    uint32_t* qc8 = nullptr;        // [B][D][kQc8Words] (int8 indexer)
+};
+
+int validate_decode(sko_handle* h, int32_t layer, const void* q_idx, const void* q_attn, const float* out) {
+    int rc = check_handle(h);
+    if (rc != SKO_OK) return rc;
+    if (layer < 0 || layer >= h->L) return set_err(SKO_E_INVAL, "layer %d out of range [0, %d)", layer, h->L);
+    if (!q_idx || !q_attn || !out) return set_err(SKO_E_INVAL, "NULL query or output pointer");
+    return SKO_OK;
+}
+
+// One decode step of `layer` (arguments already validated, device current),
+// with the per-step scratch `sc`.
+int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void* q_attn, float* out,
+                     const StepScratch& sc) {
+    int rc = SKO_OK;
+
+    const int B = h->B, D = h->D, k = h->k, S = h->S, H = h->H;
+    const int64_t cap = h->cap;
+    int64_t max_now = 0;
+    for (int b = 0; b < B; ++b) max_now = std::max(max_now, h->ntok[h->lb(layer, b)]);
+    const int32_t t = h->step[layer];
+    const size_t LBc = (size_t)layer * B * cap;
+    const size_t LBs = (size_t)layer * B * S;
+    const void* idx_layer = reinterpret_cast<const uint8_t*>(h->idx) + (size_t)layer * B * h->idx_seq_bytes();
+    const uint16_t* scale_layer = h->c8 ? h->idx_scale + (size_t)layer * B * h->ntiles * kIdxTile : nullptr;
+    const uint16_t* pool_layer = h->pool_dev + LBc * kKvDim;
+    const uint16_t* recent_layer = h->recent + (size_t)layer * B * kKvDim;
+    uint16_t* hot_layer = h->hot + LBs * kKvDim;
+    int32_t* cs = h->cache_slots + LBc;
+    int32_t* st = h->slot_token + LBs;
+    int32_t* lu = h->last_use + LBs;
+    const int32_t* ntok = h->ntok_dev + (size_t)layer * B;
+    const uint16_t* qi = static_cast<const uint16_t*>(q_idx);
+    const uint16_t* qa = static_cast<const uint16_t*>(q_attn);
+
+    int32_t* ring0 = h->ring[0] + (size_t)layer * B * h->C;
+    int32_t* ring1 = h->ring[1] + (size_t)layer * B * h->C;
+    int32_t* ring_pos = h->ring_pos + LBs;
+    RingState* ring_state = h->ring_state + (size_t)layer * B;
+    int32_t* floor_layer = h->floor + (size_t)layer * B * D;
+
+    if ((rc = run_stage(h, ST_SCORE, [&] {
+             return launch_score_hist(h->stream, idx_layer, qi, ntok, h->keys, sc.hist, floor_layer, sc.pre,
+                                      sc.meta, cs, B, D, h->kcap, cap, h->ntiles, max_now, h->cu_count, scale_layer,
+                                      sc.qc8);
+         })))
+        return rc;
+    const bool fused_copy = h->fused_copy;
+    const bool staged = h->staged_copy;
+    if ((rc = run_stage(h, ST_FILTER, [&] {
+             return launch_topk_filter(h->stream, sc.hist, sc.meta, sc.pre, sc.cand, h->topk, cs, ntok, sc.winners,
+                                       staged ? sc.miss_bits : nullptr, idx_layer, qi, floor_layer,
+                                       (h->cfg.flags & SKO_FLAG_SELECT_RESCAN) != 0, B, D, cap, h->ntiles, k,
+                                       max_now, scale_layer, h->c8 ? sc.qc8 : nullptr);
+         })))
+        return rc;
+    if (staged && (rc = run_stage(h, ST_REFINE, [&] {
+                       // the split buckets first, so that the miss set is complete
+                       // when the merge launch starts copying
+                       return launch_topk_refine(h->stream, sc.meta, sc.cand, h->topk, sc.winners, sc.miss_bits, B,
+                                                 D, k, cap);
+                   })))
+        return rc;
+    // split attention: the selection is complete, so the rows resident at
+    // step start (whose slots and data the LRU update and the copy leave
+    // alone) are attended on the side stream while the copy launch runs
+    const bool split = staged && h->hit_overlap;
+    if (split) {
+        hipError_t e = hipEventRecord(h->ev_fork, h->stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_fork, 0);
+        if (e != hipSuccess) return device_fail(h, e, "fork of the hit attention");
+    }
+    if ((rc = run_stage(h, ST_MERGE_LRU, [&] {
+             return launch_merge_lru(h->stream, sc.winners, sc.hist, sc.meta, sc.cand, h->topk, ntok, cs, st, lu,
+                                     ring0, ring1, ring_pos, ring_state, B, D, k, S, cap, t, h->misses, h->victims,
+                                     h->evict_old, h->counts, sc.glist, h->stats + (size_t)layer * 8, !staged,
+                                     staged ? sc.miss_bits : nullptr, pool_layer, recent_layer, h->stage_rows,
+                                     staged ? sc.rdcp : nullptr, h->phys,
+                                     /* the split attention reads the lists during this launch */ !h->hit_overlap,
+                                     max_now, (h->cfg.flags & SKO_FLAG_TEST_VIOLATION) != 0);
+         })))
+        return rc;
+    // late copy: its own gather from the pool; fused or early: the attention
+    // launch puts the missed rows into their slots itself
+    if (!fused_copy && !staged && (rc = run_stage(h, ST_GATHER, [&] {
+             return launch_gather_misses(h->stream, sc.glist, h->counts, pool_layer, recent_layer, ntok, hot_layer,
+                                         B, cap, D * k, B * D * k);
+         })))
+        return rc;
+    if (split) {
+        if ((rc = run_stage(
+                 h, ST_ATTN_HITS,
+                 [&] {
+                     return launch_attn_partial(h->side, h->topk, cs, hot_layer, qa, nullptr, recent_layer, ntok,
+                                                sc.part_acc, sc.part_ml, h->phys, B, D, H, k, S, cap,
+                                                h->rows_per_block, h->cfg.attn_scale, h->stage_rows, nullptr,
+                                                nullptr, 1);
+                 },
+                 h->side)))
+            return rc;
+        const hipError_t e = hipEventRecord(h->ev_join, h->side);
+        if (e != hipSuccess) return device_fail(h, e, "join of the hit attention");
+    }
+    if ((rc = run_stage(h, ST_ATTN, [&] {
+             return launch_attn_partial(h->stream, h->topk, cs, hot_layer, qa, fused_copy ? pool_layer : nullptr,
+                                        recent_layer, ntok, sc.part_acc, sc.part_ml, h->phys, B, D, H, k, S, cap,
+                                        h->rows_per_block, h->cfg.attn_scale, staged ? h->stage_rows : nullptr,
+                                        staged ? sc.rdcp : nullptr, staged ? sc.miss_bits : nullptr,
+                                        split ? 2 : 0);
+         })))
+        return rc;
+    if (split) {
+        const hipError_t e = hipStreamWaitEvent(h->stream, h->ev_join, 0);
+        if (e != hipSuccess) return device_fail(h, e, "join of the hit attention");
+    }
+    if ((rc = run_stage(h, ST_COMBINE, [&] {
+             return launch_attn_combine(h->stream, sc.part_acc, sc.part_ml, out, B, D, H,
+                                        h->nchunk * (split ? 2 : 1));
+         })))
+        return rc;
+    h->step[layer] += 1;
+    h->last_layer = layer;
+    return SKO_OK;
+}
+
+
+// ---- the decode step without any allocation ---------------------------------
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid it):
+// sko_decode_step_static takes the per-step scratch from this file-scope
+// array instead of the handle's own.  Each device that runs it holds one
+// copy until the process ends.  In host code the name `scratch` is only a
+// stand-in: its device address is looked up once per device at sko_create
+// (hipGetSymbolAddress) and only that address is ever used.
+constexpr size_t kStaticScratchBytes = (size_t)SKO_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};   // device address of `scratch` per device
+int g_scratch_state[kMaxDevices] = {};    // 0: not looked up, 1: found, -1: lookup failed
+
+// Called at sko_create with `device` current.
+void resolve_static_scratch(int device) {
+    if (device < 0 || device >= kMaxDevices) return;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_state[device] != 0) return;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+        (void)hipGetLastError();
+        g_scratch_state[device] = -1;
+        return;
+    }
+    g_scratch_addr[device] = ptr;
+    g_scratch_state[device] = 1;
+}
+
+// Lays the step scratch of `h` out from `base` (256-byte aligned pieces);
+// returns the bytes it needs (base may be null to only measure).
+size_t layout_step_scratch(const sko_handle* h, unsigned char* base, StepScratch* sc, size_t* zero_bytes) {
+    const size_t BD = (size_t)h->B * h->D;
+    const size_t pchunks = (size_t)h->nchunk * (h->hit_overlap ? 2 : 1);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        unsigned char* p = base ? base + off : nullptr;
+        off += (bytes + 255) / 256 * 256;
+        return p;
+    };
+    // the parts that must start at zero come first, in one run
+    sc->hist = reinterpret_cast<uint32_t*>(take(BD * kHistBins * 4));
+    sc->meta = reinterpret_cast<RowMeta*>(take(BD * sizeof(RowMeta)));
+    sc->winners = reinterpret_cast<uint32_t*>(take((size_t)h->B * h->wpr * 4));
+    sc->miss_bits = h->staged_copy ? reinterpret_cast<uint32_t*>(take((size_t)h->B * h->wpr * 4)) : nullptr;
+    *zero_bytes = off;
+    sc->rdcp = h->staged_copy ? reinterpret_cast<int2*>(take(BD * h->k * sizeof(int2))) : nullptr;
+    sc->pre = reinterpret_cast<uint2*>(take(BD * h->cap * sizeof(uint2)));
+    sc->cand = reinterpret_cast<uint2*>(take(BD * h->cap * sizeof(uint2)));
+    sc->glist = reinterpret_cast<GatherEntry*>(take(BD * h->k * sizeof(GatherEntry)));
+    sc->part_acc = reinterpret_cast<float*>(take(BD * h->HG * pchunks * kAttnHeadGroup * kVDim * 4));
+    sc->part_ml = reinterpret_cast<float*>(take(BD * h->HG * pchunks * kAttnHeadGroup * 2 * 4));
+    sc->qc8 = h->c8 ? reinterpret_cast<uint32_t*>(take(BD * kQc8Words * 4)) : nullptr;
+    return off;
+}
+
+// Clears the first nz words of `z` and sets the first nf words of `f` to all
+// ones (a kernel, not a memset, so the call can sit inside a captured graph).
+__global__ __launch_bounds__(256) void k_clear_scratch(uint32_t* __restrict__ z, int64_t nz,
+                                                       uint32_t* __restrict__ f, int64_t nf) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nz + nf; i += stride) {
+        if (i < nz) z[i] = 0u;
+        else f[i - nz] = 0xFFFFFFFFu;
+    }
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* sko_last_error(void) { return g_err.c_str(); }
@@ -503,6 +720,8 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
         delete h;
         return SKO_E_DEVICE;
     }
+    // set-up of the no-allocation decode step on this device (once per device)
+    resolve_static_scratch(cfg->device);
     *out = h;
     return SKO_OK;
 }
@@ -603,120 +822,58 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
 }
 
 int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void* q_attn, float* out) {
-    int rc = check_handle(h);
+    int rc = validate_decode(h, layer, q_idx, q_attn, out);
     if (rc != SKO_OK) return rc;
-    if (layer < 0 || layer >= h->L) return set_err(SKO_E_INVAL, "layer %d out of range [0, %d)", layer, h->L);
-    if (!q_idx || !q_attn || !out) return set_err(SKO_E_INVAL, "NULL query or output pointer");
     DeviceGuard guard(h->cfg.device);
     if (!guard.ok) return device_fail(h, hipErrorInvalidDevice, "hipSetDevice");
+    StepScratch sc;
+    sc.pre = h->pre;
+    sc.cand = h->cand;
+    sc.hist = h->hist;
+    sc.meta = h->meta;
+    sc.winners = h->winners;
+    sc.miss_bits = h->miss_bits;
+    sc.rdcp = h->rdcp;
+    sc.glist = h->glist;
+    sc.part_acc = h->part_acc;
+    sc.part_ml = h->part_ml;
+    sc.qc8 = h->qc8;
+    return decode_step_impl(h, layer, q_idx, q_attn, out, sc);
+}
 
-    const int B = h->B, D = h->D, k = h->k, S = h->S, H = h->H;
-    const int64_t cap = h->cap;
-    int64_t max_now = 0;
-    for (int b = 0; b < B; ++b) max_now = std::max(max_now, h->ntok[h->lb(layer, b)]);
-    const int32_t t = h->step[layer];
-    const size_t LBc = (size_t)layer * B * cap;
-    const size_t LBs = (size_t)layer * B * S;
-    const void* idx_layer = reinterpret_cast<const uint8_t*>(h->idx) + (size_t)layer * B * h->idx_seq_bytes();
-    const uint16_t* scale_layer = h->c8 ? h->idx_scale + (size_t)layer * B * h->ntiles * kIdxTile : nullptr;
-    const uint16_t* pool_layer = h->pool_dev + LBc * kKvDim;
-    const uint16_t* recent_layer = h->recent + (size_t)layer * B * kKvDim;
-    uint16_t* hot_layer = h->hot + LBs * kKvDim;
-    int32_t* cs = h->cache_slots + LBc;
-    int32_t* st = h->slot_token + LBs;
-    int32_t* lu = h->last_use + LBs;
-    const int32_t* ntok = h->ntok_dev + (size_t)layer * B;
-    const uint16_t* qi = static_cast<const uint16_t*>(q_idx);
-    const uint16_t* qa = static_cast<const uint16_t*>(q_attn);
-
-    int32_t* ring0 = h->ring[0] + (size_t)layer * B * h->C;
-    int32_t* ring1 = h->ring[1] + (size_t)layer * B * h->C;
-    int32_t* ring_pos = h->ring_pos + LBs;
-    RingState* ring_state = h->ring_state + (size_t)layer * B;
-    int32_t* floor_layer = h->floor + (size_t)layer * B * D;
-
-    if ((rc = run_stage(h, ST_SCORE, [&] {
-             return launch_score_hist(h->stream, idx_layer, qi, ntok, h->keys, h->hist, floor_layer, h->pre,
-                                      h->meta, cs, B, D, h->kcap, cap, h->ntiles, max_now, h->cu_count, scale_layer,
-                                      h->qc8);
-         })))
-        return rc;
-    const bool fused_copy = h->fused_copy;
-    const bool staged = h->staged_copy;
-    if ((rc = run_stage(h, ST_FILTER, [&] {
-             return launch_topk_filter(h->stream, h->hist, h->meta, h->pre, h->cand, h->topk, cs, ntok, h->winners,
-                                       staged ? h->miss_bits : nullptr, idx_layer, qi, floor_layer,
-                                       (h->cfg.flags & SKO_FLAG_SELECT_RESCAN) != 0, B, D, cap, h->ntiles, k,
-                                       max_now, scale_layer, h->c8 ? h->qc8 : nullptr);
-         })))
-        return rc;
-    if (staged && (rc = run_stage(h, ST_REFINE, [&] {
-                       // the split buckets first, so that the miss set is complete
-                       // when the merge launch starts copying
-                       return launch_topk_refine(h->stream, h->meta, h->cand, h->topk, h->winners, h->miss_bits, B,
-                                                 D, k, cap);
-                   })))
-        return rc;
-    // split attention: the selection is complete, so the rows resident at
-    // step start (whose slots and data the LRU update and the copy leave
-    // alone) are attended on the side stream while the copy launch runs
-    const bool split = staged && h->hit_overlap;
-    if (split) {
-        hipError_t e = hipEventRecord(h->ev_fork, h->stream);
-        if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_fork, 0);
-        if (e != hipSuccess) return device_fail(h, e, "fork of the hit attention");
-    }
-    if ((rc = run_stage(h, ST_MERGE_LRU, [&] {
-             return launch_merge_lru(h->stream, h->winners, h->hist, h->meta, h->cand, h->topk, ntok, cs, st, lu,
-                                     ring0, ring1, ring_pos, ring_state, B, D, k, S, cap, t, h->misses, h->victims,
-                                     h->evict_old, h->counts, h->glist, h->stats + (size_t)layer * 8, !staged,
-                                     staged ? h->miss_bits : nullptr, pool_layer, recent_layer, h->stage_rows,
-                                     staged ? h->rdcp : nullptr, h->phys,
-                                     /* the split attention reads the lists during this launch */ !h->hit_overlap,
-                                     max_now, (h->cfg.flags & SKO_FLAG_TEST_VIOLATION) != 0);
-         })))
-        return rc;
-    // late copy: its own gather from the pool; fused or early: the attention
-    // launch puts the missed rows into their slots itself
-    if (!fused_copy && !staged && (rc = run_stage(h, ST_GATHER, [&] {
-             return launch_gather_misses(h->stream, h->glist, h->counts, pool_layer, recent_layer, ntok, hot_layer,
-                                         B, cap, D * k, B * D * k);
-         })))
-        return rc;
-    if (split) {
-        if ((rc = run_stage(
-                 h, ST_ATTN_HITS,
-                 [&] {
-                     return launch_attn_partial(h->side, h->topk, cs, hot_layer, qa, nullptr, recent_layer, ntok,
-                                                h->part_acc, h->part_ml, h->phys, B, D, H, k, S, cap,
-                                                h->rows_per_block, h->cfg.attn_scale, h->stage_rows, nullptr,
-                                                nullptr, 1);
-                 },
-                 h->side)))
-            return rc;
-        const hipError_t e = hipEventRecord(h->ev_join, h->side);
-        if (e != hipSuccess) return device_fail(h, e, "join of the hit attention");
-    }
-    if ((rc = run_stage(h, ST_ATTN, [&] {
-             return launch_attn_partial(h->stream, h->topk, cs, hot_layer, qa, fused_copy ? pool_layer : nullptr,
-                                        recent_layer, ntok, h->part_acc, h->part_ml, h->phys, B, D, H, k, S, cap,
-                                        h->rows_per_block, h->cfg.attn_scale, staged ? h->stage_rows : nullptr,
-                                        staged ? h->rdcp : nullptr, staged ? h->miss_bits : nullptr,
-                                        split ? 2 : 0);
-         })))
-        return rc;
-    if (split) {
-        const hipError_t e = hipStreamWaitEvent(h->stream, h->ev_join, 0);
-        if (e != hipSuccess) return device_fail(h, e, "join of the hit attention");
-    }
-    if ((rc = run_stage(h, ST_COMBINE, [&] {
-             return launch_attn_combine(h->stream, h->part_acc, h->part_ml, out, B, D, H,
-                                        h->nchunk * (split ? 2 : 1));
-         })))
-        return rc;
-    h->step[layer] += 1;
-    h->last_layer = layer;
-    return SKO_OK;
+int sko_decode_step_static(sko_handle* h, int32_t layer, const void* q_idx, const void* q_attn, float* out) {
+    int rc = validate_decode(h, layer, q_idx, q_attn, out);
+    if (rc != SKO_OK) return rc;
+    const int dev = h->cfg.device;
+    if (dev >= kMaxDevices || g_scratch_state[dev] != 1)
+        return set_err(SKO_E_DEVICE, "the static scratch area of device %d is not available", dev);
+    StepScratch sc;
+    size_t zero_bytes = 0;
+    const size_t need = layout_step_scratch(h, nullptr, &sc, &zero_bytes);
+    if (need > kStaticScratchBytes)
+        return set_err(SKO_E_UNSUPPORTED,
+                       "sko_decode_step_static: this handle's step needs %zu bytes of scratch, the static area "
+                       "holds %zu (use sko_decode_step)",
+                       need, kStaticScratchBytes);
+    DeviceGuard guard(dev);
+    if (!guard.ok) return device_fail(h, hipErrorInvalidDevice, "hipSetDevice");
+    unsigned char* base = static_cast<unsigned char*>(g_scratch_addr[dev]);
+    (void)layout_step_scratch(h, base, &sc, &zero_bytes);
+    // the area keeps the last call's contents (any handle's): clear what the
+    // step expects to start cleared
+    const int64_t nz = (int64_t)(zero_bytes / 4);
+    const int64_t nf = sc.rdcp ? (int64_t)((size_t)h->B * h->D * h->k * sizeof(int2) / 4) : 0;
+    const int64_t blocks = std::min<int64_t>(1024, std::max<int64_t>(1, (nz + nf + 255) / 256));
+    hipLaunchKernelGGL(k_clear_scratch, dim3((unsigned)blocks), dim3(256), 0, h->stream,
+                       reinterpret_cast<uint32_t*>(base), nz, reinterpret_cast<uint32_t*>(sc.rdcp), nf);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return device_fail(h, e, "clearing the static scratch");
+    // no stage timing here: its events are created on demand
+    const uint32_t mask = h->timing_mask;
+    h->timing_mask = 0;
+    rc = decode_step_impl(h, layer, q_idx, q_attn, out, sc);
+    h->timing_mask = mask;
+    return rc;
 }
 
 int sko_read_step(sko_handle* h, int32_t which, void* dst, int64_t bytes) {
