@@ -7,10 +7,11 @@ alone is the full workload restricted to it).  Every step is compared
 bit-exactly on selection, counts, misses and evictions; attention is checked
 on a few steps; residency tables and hot-buffer bytes every few steps.
 
-Layer counts are reduced where the full count only repeats identical
-launches on more memory (mtp3: 2 of 4, shelf: 2 of 8); step counts are cut
-to what the oracle replays in well under a minute, always including the
-cold first step.
+Long horizons are covered: shelf_ctx8 runs one chain through all 256 steps
+(topic jumps at 64, 128 and 192, so the ring compaction and the candidate
+floor are exercised after each jump), mtp3 runs all 4 layers for 64 steps
+with two chains, long runs all 64 steps.  The GPU runs 2 of shelf's 8
+layers (the other layers repeat identical launches on more memory).
 """
 import pytest
 
@@ -47,24 +48,26 @@ def test_small_full():
          tables_every=16)
 
 
-def test_mtp3_full_shape():
+def test_mtp3_full_all_layers():
     w = synth.MTP3
-    _run(w, layers=2, steps=24, chains=[(0, 3), (1, 15)], out_steps=[0, 23], tables_every=8)
+    _run(w, layers=4, steps=64, chains=[(0, 3), (3, 15)], out_steps=range(0, 64, 16), tables_every=16)
 
 
-def test_shelf_ctx8_across_topic_jump():
+def test_shelf_ctx8_all_steps_across_topic_jumps():
     w = synth.SHELF8
-    _run(w, layers=2, steps=70, chains=[(1, 31)], out_steps=[0, 64, 69], tables_every=32)
+    _run(w, layers=2, steps=w.steps, chains=[(1, 31)], out_steps=list(range(0, 256, 32)) + [255],
+         tables_every=32)
 
 
 def test_shelf_ctx4_full_shape():
     w = synth.SHELF4
-    _run(w, layers=1, steps=20, chains=[(0, 5)], out_steps=[0, 19], tables_every=10)
+    _run(w, layers=1, steps=70, chains=[(0, 5)], out_steps=[0, 64, 69], tables_every=32)
 
 
-def test_long_full_shape():
+def test_long_all_steps():
     w = synth.LONG
-    _run(w, layers=2, steps=10, chains=[(1, 1)], out_steps=[0, 9], tables_every=5)
+    _run(w, layers=2, steps=w.steps, chains=[(1, 1)], out_steps=list(range(0, 64, 16)) + [63],
+         tables_every=16)
 
 
 def test_long_full_shape_int8_indexer():
