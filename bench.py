@@ -453,6 +453,9 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     timing = h.timing() if timed_mask else {}
+    # block stamps of the timed LRU-update launches (early copy): how long the
+    # copy blocks ran beside the LRU update
+    overlap = h.copy_overlap() if timed_mask else None
     h.set_timing(0)
     stats1 = [h.stats(l) for l in range(L)]
 
@@ -571,6 +574,20 @@ def main() -> int:
         if d["h2d_bytes"] else None,
         "frac_of_link_bound": round(value * d["h2d_bytes"] / (h2d_ceiling * 1e9 * layer_steps), 4)
         if d["h2d_bytes"] else None,
+        # the miss transfer against the rest of the step: the copy span and the
+        # LRU-update span of each timed copy launch and their intersection
+        # (the share of the copy during which other step work runs), and the
+        # part of a layer-step not covered by the link at its measured rate
+        "copy_overlap": ({
+            "launches": overlap["launches"],
+            "copy_span_us": round(overlap["copy_ms"] / overlap["launches"] * 1e3, 2),
+            "merge_span_us": round(overlap["merge_ms"] / overlap["launches"] * 1e3, 2),
+            "overlapped_us": round(overlap["overlap_ms"] / overlap["launches"] * 1e3, 2),
+            "overlap_frac_of_copy": round(overlap["overlap_ms"] / overlap["copy_ms"], 4),
+            "link_time_us_per_layer_step": round(d["h2d_bytes"] / layer_steps / (h2d_ceiling * 1e9) * 1e6, 2),
+            "exposed_non_link_us_per_layer_step": round(
+                elapsed / layer_steps * 1e6 - d["h2d_bytes"] / layer_steps / (h2d_ceiling * 1e9) * 1e6, 2),
+        } if overlap and overlap["launches"] and overlap["copy_ms"] > 0 else None),
         "selection_rescans": d["rescans"],
         "newest_rows_from_device": d["direct_rows"],
         "roofline": roof,

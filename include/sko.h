@@ -319,6 +319,22 @@ int sko_get_stats(sko_handle* h, int32_t layer, sko_layer_stats* out);
  */
 int sko_set_timing(sko_handle* h, uint32_t stage_mask);
 int sko_get_timing(sko_handle* h, double* total_ms, int64_t* launches, int32_t n);
+
+/*
+ * sko_get_copy_overlap — how long the early copy ran beside the LRU update
+ * (the overlap of the miss transfer with other step work; the explainer's
+ * decode paragraphs report 90-98 % of miss loads overlapped at batch >= 16).
+ * While the stage "merge_lru" is timed (sko_set_timing) and the early copy
+ * is in use, every block of the LRU-update launch records its start and end
+ * on the device's constant-rate clock.  Per launch: the copy span (first copy
+ * block's start to last copy block's end), the merge span (the same over the
+ * LRU-update blocks) and their intersection.  Returns the sums (ms) and the
+ * number of launches recorded since the last sko_set_timing; synchronizes.
+ * At most 1024 launches are recorded between two reads (sko_get_timing also
+ * reads); later ones are skipped.
+ */
+int sko_get_copy_overlap(sko_handle* h, double* copy_ms, double* merge_ms, double* overlap_ms,
+                         int64_t* launches);
 const char* sko_stage_name(int32_t stage);
 int32_t sko_num_stages(void);
 

@@ -51,7 +51,8 @@ SKO_TAB_INDEXER_SCALE = 8
 EXPORTED = (
     "sko_create", "sko_set_stream", "sko_append_token", "sko_decode_step", "sko_decode_step_static",
     "sko_read_step",
-    "sko_read_table", "sko_get_stats", "sko_set_timing", "sko_get_timing", "sko_stage_name",
+    "sko_read_table", "sko_get_stats", "sko_set_timing", "sko_get_timing", "sko_get_copy_overlap",
+    "sko_stage_name",
     "sko_num_stages", "sko_destroy", "sko_last_error", "sko_version", "sko_link_read_rate",
     # layerwise prefill offload (include/sko_prefill.h)
     "sko_prefill_plan", "sko_prefill_create", "sko_prefill_destroy", "sko_prefill_host_pool",
@@ -125,6 +126,8 @@ def _load() -> ctypes.CDLL:
         "sko_set_timing": (ctypes.c_int, [vp, ctypes.c_uint32]),
         "sko_get_timing": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int64), i32]),
+        "sko_get_copy_overlap": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                                ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
         "sko_stage_name": (ctypes.c_char_p, [i32]),
         "sko_num_stages": (i32, []),
         "sko_destroy": (None, [vp]),
@@ -276,6 +279,15 @@ def sko_get_timing(h: int) -> dict:
     return {sko_stage_name(i): (float(ms[i]), int(cnt[i])) for i in range(n)}
 
 
+def sko_get_copy_overlap(h: int) -> dict:
+    """Sums over the recorded LRU-update launches: copy span, merge span and
+    their overlap (ms), and the number of launches."""
+    c, m, o, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+    _check(_lib.sko_get_copy_overlap(h, ctypes.byref(c), ctypes.byref(m), ctypes.byref(o), ctypes.byref(n)),
+           "sko_get_copy_overlap")
+    return {"copy_ms": c.value, "merge_ms": m.value, "overlap_ms": o.value, "launches": n.value}
+
+
 def sko_destroy(h: int) -> None:
     if h:
         _lib.sko_destroy(h)
@@ -360,6 +372,9 @@ class SparseKVOffload:
 
     def timing(self) -> dict:
         return sko_get_timing(self.handle)
+
+    def copy_overlap(self) -> dict:
+        return sko_get_copy_overlap(self.handle)
 
 
 __all__ = [n for n in globals() if n.startswith(("sko_", "SKO_", "Sko"))] + [

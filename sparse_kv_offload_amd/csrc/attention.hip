@@ -43,6 +43,14 @@ constexpr int kRowStrideU4 = kKvRowU4 + 1;  // 16-byte pad per staged row
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// v if keep, else zero: a bit mask rather than a select, so that a load
+// feeding it is issued unconditionally (a select of a load becomes a branch
+// around the load, and a wait for it inside the branch)
+__device__ __forceinline__ uint4 keep_if(uint4 v, bool keep) {
+    const uint32_t m = keep ? 0xFFFFFFFFu : 0u;
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
 // dword holding bf16 element m (0..7) of a 16-byte vector
 __device__ __forceinline__ uint32_t dword_of(uint4 v, int m) {
     return (m >> 1) == 0 ? v.x : (m >> 1) == 1 ? v.y : (m >> 1) == 2 ? v.z : v.w;
@@ -75,17 +83,56 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     const int chunk = blockIdx.x, bp = blockIdx.y, hg = blockIdx.z;
     const int b = bp / D;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t Lt = ntok_layer[b];
-    const int kk = (int)std::min<int64_t>(top_k, Lt);
+    const int n16 = lane & 15, g = lane >> 4;
+    const int h = hg * kAttnHeadGroup + n16;
+    constexpr bool fused_copy = COPY == kCopyPool;
+    constexpr bool staged = COPY == kCopyStaged;
     const int r0 = chunk * rows_per_block;
-    const int r1 = std::min(r0 + rows_per_block, kk);
+    // list entries this chunk can hold (known without the token count)
+    const int rcap = std::min(r0 + rows_per_block, top_k);
+    const int32_t* __restrict__ w = topk + (size_t)bp * top_k;
+    const int2* __restrict__ rc = staged ? rdcp + (size_t)bp * top_k : nullptr;
+
+    // The loads that depend on nothing else are issued together, before any
+    // of them is waited for: the token count, the chunk's list entries and
+    // the query operand.
+    const int64_t Lt = ntok_layer[b];
+    constexpr int kRowsPerThread = kAttnMaxRowsPerBlock / 256;
+    int32_t pk[kRowsPerThread];
+    int2 pe[kRowsPerThread];
+#pragma unroll
+    for (int u = 0; u < kRowsPerThread; ++u) {
+        // all rows: thread t takes entries t, t + 256; a split phase keeps
+        // the rows in order, so a thread takes two consecutive entries
+        const int j = PHASE == kPhaseAll ? tid + 256 * u : tid * kRowsPerThread + u;
+        // read in bounds (clamped) and used only below the chunk's row count
+        const int jc = std::min(r0 + j, top_k - 1);
+        pk[u] = w[jc];
+        pe[u] = make_int2(-1, -1);
+        if constexpr (staged) pe[u] = rc[jc];
+    }
+    // The 18 k-steps (32 columns each) of S^T = K Q^T are split over the 4
+    // waves (5, 5, 4, 4); wave w holds the B operand Q^T of its k-steps:
+    // lane (n16, g) holds Q[h][32ks + 8g .. +7].
+    const int ks0 = wave < 2 ? 5 * wave : 10 + 4 * (wave - 2);
+    const int nks = wave < 2 ? 5 : 4;
+    uint4 qv[5];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+        // loads stay in bounds (clamped head and step); the select zeroes
+        // padding heads and the fifth step of waves that own four
+        const int hq = h < H ? h : H - 1;
+        const int kq = q < nks ? ks0 + q : ks0;
+        qv[q] = keep_if(q_attn[((size_t)bp * H + hq) * kKvRowU4 + 4 * kq + g], h < H && q < nks);
+    }
+
+    const int kk = (int)std::min<int64_t>(top_k, Lt);
+    const int r1 = std::min(rcap, kk);
     // partials of the chunk: pchunks per (seq, position, head group), the
     // misses phase after the hits phase's nchunk
     const size_t pidx = ((size_t)bp * HG + hg) * pchunks + (PHASE == kPhaseMisses ? nchunk : 0) + chunk;
     float* __restrict__ acc_out = part_acc + pidx * kAttnHeadGroup * kVDim;
     float* __restrict__ ml_out = part_ml + pidx * kAttnHeadGroup * 2;
-    constexpr bool fused_copy = COPY == kCopyPool;
-    constexpr bool staged = COPY == kCopyStaged;
     if (r0 >= r1) {
         if (tid < kAttnHeadGroup) {
             ml_out[2 * tid] = -INFINITY;
@@ -93,9 +140,6 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         }
         return;
     }
-    const int n16 = lane & 15, g = lane >> 4;
-    const int h = hg * kAttnHeadGroup + n16;
-    const int32_t* __restrict__ w = topk + (size_t)bp * top_k;
     const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
     uint4* __restrict__ hb = hot_layer + (size_t)b * S * kKvRowU4;
     // staging rows of this sequence, as row numbers relative to hb (the
@@ -108,13 +152,13 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     // winner, the row (slot >= 0, -(r + 2) for staging row r, -1 none) and
     // the slot a missed row moves into (one entry per miss), and its hot
     // slot into phys; the miss's bitmap word is cleared for the next step
-    // (several blocks may store the same zero).
-    const int2* __restrict__ rc = staged ? rdcp + (size_t)bp * top_k : nullptr;
+    // (several blocks may store the same zero).  A row that resolves to no
+    // slot (only possible with a broken invariant, which the LRU-update
+    // launch reports) reads row 0 instead of leaving the buffer.
     uint32_t* __restrict__ mbw = staged ? miss_bits + (size_t)b * wpr : nullptr;
-    auto remap = [&](int j, int32_t packed, int q) {
+    auto remap = [&](int j, int32_t packed, int2 e, int q) {
         int32_t rd = -1, cp = -1;
         if constexpr (staged) {
-            const int2 e = rc[r0 + j];
             rd = e.x >= 0 ? e.x : (e.x <= -2 ? (int32_t)(stage_base + min(-e.x - 2, D * top_k - 1)) : -1);
             cp = e.y;
             if (packed < 0) mbw[(packed & 0x7FFFFFFF) >> 5] = 0u;
@@ -126,27 +170,28 @@ __global__ __launch_bounds__(256) void k_attn_partial(
             if (fused_copy && packed < 0 && slot >= 0) cp = tok;
             if (hg == 0) phys[(size_t)bp * top_k + r0 + j] = slot;
         }
-        slot_s[q] = rd;
+        slot_s[q] = rd >= 0 ? rd : 0;
         cp_s[q] = cp;
     };
     int n = r1 - r0;
     if constexpr (PHASE == kPhaseAll) {
-        for (int j = tid; j < n; j += 256) remap(j, w[r0 + j], j);
+#pragma unroll
+        for (int u = 0; u < kRowsPerThread; ++u) {
+            const int j = tid + 256 * u;
+            if (j < n) remap(j, pk[u], pe[u], j);
+        }
     } else {
-        constexpr int kRowsPerThread = kAttnMaxRowsPerBlock / 256;
-        int32_t pk[kRowsPerThread];
         int nmine = 0;
 #pragma unroll
         for (int u = 0; u < kRowsPerThread; ++u) {
             const int j = tid * kRowsPerThread + u;
-            pk[u] = (j < r1 - r0) ? w[r0 + j] : 0;
             nmine += (j < r1 - r0 && (PHASE == kPhaseHits) == (pk[u] >= 0)) ? 1 : 0;
         }
         int q = block_exclusive_scan<256>(nmine, &n, scratch);
 #pragma unroll
         for (int u = 0; u < kRowsPerThread; ++u) {
             const int j = tid * kRowsPerThread + u;
-            if (j < r1 - r0 && (PHASE == kPhaseHits) == (pk[u] >= 0)) remap(j, pk[u], q++);
+            if (j < r1 - r0 && (PHASE == kPhaseHits) == (pk[u] >= 0)) remap(j, pk[u], pe[u], q++);
         }
     }
     if (n == 0) {  // block-uniform: no rows of this phase in the chunk
@@ -155,6 +200,13 @@ __global__ __launch_bounds__(256) void k_attn_partial(
             ml_out[2 * tid + 1] = 0.0f;
         }
         return;
+    }
+    // rows past the chunk's own, up to the last tile's end, read a real row
+    // (row 0: finite data) whose scores the softmax masks, so the tile
+    // loads need no condition
+    for (int j = n + tid; j < (n + kAttnTileRows - 1) / kAttnTileRows * kAttnTileRows; j += 256) {
+        slot_s[j] = 0;
+        cp_s[j] = -1;
     }
 
     // Fused: the missed rows of this chunk are copied from the pool into
@@ -187,22 +239,6 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         __threadfence_block();
     }
 
-    // The 18 k-steps (32 columns each) of S^T = K Q^T are split over the 4
-    // waves (5, 5, 4, 4); wave w holds the B operand Q^T of its k-steps:
-    // lane (n16, g) holds Q[h][32ks + 8g .. +7].
-    const int ks0 = wave < 2 ? 5 * wave : 10 + 4 * (wave - 2);
-    const int nks = wave < 2 ? 5 : 4;
-    uint4 qv[5];
-#pragma unroll
-    for (int q = 0; q < 5; ++q) {
-        // loads stay in bounds (clamped head and step); the select zeroes
-        // padding heads and the fifth step of waves that own four
-        const int hq = h < H ? h : H - 1;
-        const int kq = q < nks ? ks0 + q : ks0;
-        const uint4 v = q_attn[((size_t)bp * H + hq) * kKvRowU4 + 4 * kq + g];
-        qv[q] = (h < H && q < nks) ? v : make_uint4(0u, 0u, 0u, 0u);
-    }
-
     f32x4_t acc[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -212,37 +248,44 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     // rows of a tile: 32 x 72 chunks of 16 bytes, 9 per thread; the next
     // tile is fetched into registers while the current one is computed
     constexpr int kPer = kAttnTileRows * kKvRowU4 / 256;
-    uint4 pre[kPer];
-    // 16-byte chunk u of this thread: row rr_u, part pt_u of the tile
-#define SKO_FETCH(rbase)                                                             \
-    _Pragma("unroll") for (int u = 0; u < kPer; ++u) {                              \
-        const int idx = tid + 256 * u;                                              \
-        const int rr = idx / kKvRowU4;                                              \
-        const int j = (rbase) + rr;                                                 \
-        const int32_t slot = (j < n) ? slot_s[j] : -1;                              \
-        const uint4 v = hb[(size_t)(slot >= 0 ? slot : 0) * kKvRowU4 + (idx - rr * kKvRowU4)]; \
-        pre[u] = (slot >= 0) ? v : make_uint4(0u, 0u, 0u, 0u);                      \
+    // the nine 16-byte chunks of this thread, as named registers (an array
+    // here was kept in private memory by the compiler)
+    static_assert(kPer == 9, "a tile is 9 chunks of 16 bytes per thread");
+    uint4 pre0, pre1, pre2, pre3, pre4, pre5, pre6, pre7, pre8;
+#define SKO_FETCH1(u, rbase)                                                                   \
+    {                                                                                          \
+        const int idx = tid + 256 * u;                                                         \
+        const int rr = idx / kKvRowU4;                                                         \
+        pre##u = hb[(size_t)slot_s[(rbase) + rr] * kKvRowU4 + (idx - rr * kKvRowU4)];          \
     }
-#define SKO_STASH()                                                   \
-    _Pragma("unroll") for (int u = 0; u < kPer; ++u) {               \
-        const int idx = tid + 256 * u;                               \
-        const int rr = idx / kKvRowU4;                               \
-        rows[rr * kRowStrideU4 + (idx - rr * kKvRowU4)] = pre[u];    \
+#define SKO_FETCH(rbase)                                                                       \
+    SKO_FETCH1(0, rbase) SKO_FETCH1(1, rbase) SKO_FETCH1(2, rbase) SKO_FETCH1(3, rbase)        \
+    SKO_FETCH1(4, rbase) SKO_FETCH1(5, rbase) SKO_FETCH1(6, rbase) SKO_FETCH1(7, rbase)        \
+    SKO_FETCH1(8, rbase)
+#define SKO_STASH1(u)                                                                          \
+    {                                                                                          \
+        const int idx = tid + 256 * u;                                                         \
+        const int rr = idx / kKvRowU4;                                                         \
+        rows[rr * kRowStrideU4 + (idx - rr * kKvRowU4)] = pre##u;                              \
     }
-    // staged: a tile row this block claimed is also stored into its slot
-#define SKO_MOVE(rbase)                                                                   \
-    if (staged) {                                                                         \
-        _Pragma("unroll") for (int u = 0; u < kPer; ++u) {                               \
-            const int idx = tid + 256 * u;                                               \
-            const int rr = idx / kKvRowU4;                                               \
-            const int j = (rbase) + rr;                                                  \
-            const int32_t c = (j < n) ? cp_s[j] : -1;                                    \
-            if (c >= 0) hb[(size_t)c * kKvRowU4 + (idx - rr * kKvRowU4)] = pre[u];       \
-        }                                                                                \
+#define SKO_STASH()                                                                            \
+    SKO_STASH1(0) SKO_STASH1(1) SKO_STASH1(2) SKO_STASH1(3) SKO_STASH1(4) SKO_STASH1(5)        \
+    SKO_STASH1(6) SKO_STASH1(7) SKO_STASH1(8)
+    // staged: a tile row this block claimed is also stored into its slot,
+    // from LDS after the tile is complete there (the prefetch registers are
+    // then never the data of a pending store, so the next tile's loads need
+    // not wait for these stores)
+#define SKO_MOVE(rbase)                                                                              \
+    if (staged) {                                                                                    \
+        _Pragma("unroll") for (int u = 0; u < kPer; ++u) {                                          \
+            const int idx = tid + 256 * u;                                                          \
+            const int rr = idx / kKvRowU4;                                                          \
+            const int32_t c = cp_s[(rbase) + rr];                                                   \
+            if (c >= 0) hb[(size_t)c * kKvRowU4 + (idx - rr * kKvRowU4)] = rows[rr * kRowStrideU4 + (idx - rr * kKvRowU4)]; \
+        }                                                                                           \
     }
     SKO_FETCH(0)
     SKO_STASH()
-    SKO_MOVE(0)
     __syncthreads();
 
     for (int r = 0; r < n; r += kAttnTileRows) {
@@ -250,6 +293,9 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         if (more) {
             SKO_FETCH(r + kAttnTileRows)
         }
+        // the claimed rows of this tile go to their slots once the next
+        // tile's loads are in flight
+        SKO_MOVE(r)
 
         // S^T tiles for rows r..r+15 and r+16..r+31; lane holds head n16,
         // rows 4g+i (+16).  Each wave forms its k-steps' partial sums; the
@@ -331,11 +377,12 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         __syncthreads();
         if (more) {
             SKO_STASH()
-            SKO_MOVE(r + kAttnTileRows)
             __syncthreads();
         }
     }
+#undef SKO_FETCH1
 #undef SKO_FETCH
+#undef SKO_STASH1
 #undef SKO_STASH
 #undef SKO_MOVE
 

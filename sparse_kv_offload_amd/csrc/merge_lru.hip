@@ -276,7 +276,11 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     unsigned long long* __restrict__ layer_stats, int do_refine, int nseq, int copy_per_seq, int copy_words,
     uint32_t* __restrict__ miss_bits, const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
     uint4* __restrict__ stage_rows, int2* __restrict__ rdcp, int32_t* __restrict__ phys, int sort_winners,
-    int test_violation) {
+    int test_violation, uint64_t* __restrict__ stamps) {
+    // instrumentation (stamps != nullptr): each block records when it
+    // started and ended on the chip's constant-rate clock, so the host can
+    // tell how long the copy blocks ran beside the LRU update
+    const uint64_t t_start = stamps ? __builtin_amdgcn_s_memrealtime() : 0ull;
     __shared__ uint32_t touched[kMaxHotSlots / 32];
     // [0, kMaxMerge): misses; [kMaxMerge, 2 kMaxMerge): the union, later the
     // victims.  Before the merge the whole area stages refine candidates.
@@ -294,6 +298,13 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     if ((int)blockIdx.x >= nseq) {
         copy_block((int)blockIdx.x - nseq, copy_per_seq, copy_words, miss_bits, pool_layer, recent_layer,
                    stage_rows, ntok_layer, cap, wpr, D * top_k, lists, scratch);
+        if (stamps) {
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                stamps[2 * blockIdx.x] = t_start;
+                stamps[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+            }
+        }
         return;
     }
     const int b = blockIdx.x;
@@ -630,6 +641,13 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
         atomicAdd(&layer_stats[3], (unsigned long long)nM);
         atomicAdd(&layer_stats[4], (unsigned long long)nEv);
     }
+    if (stamps) {
+        __syncthreads();
+        if (tid == 0) {
+            stamps[2 * blockIdx.x] = t_start;
+            stamps[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+        }
+    }
 }
 
 void copy_shape(int B, int64_t max_tokens_now, int* copy_per_seq, int* copy_words) {
@@ -652,7 +670,7 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
                             uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
                             uint16_t* stage_rows, int2* rdcp, int32_t* phys, bool sort_winners,
-                            int64_t max_tokens_now, bool test_violation) {
+                            int64_t max_tokens_now, bool test_violation, uint64_t* stamps) {
     const int64_t C = ring_capacity(S, D, top_k);
     const int64_t wpr = winner_words(cap);
     // B merge blocks, then (early copy) B * copy_per_seq copy blocks of
@@ -667,7 +685,7 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                        miss_bits,
                        reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<const uint4*>(recent_layer),
                        reinterpret_cast<uint4*>(stage_rows), miss_bits ? rdcp : nullptr, phys, sort_winners ? 1 : 0,
-                       test_violation ? 1 : 0);
+                       test_violation ? 1 : 0, stamps);
     return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@ using namespace sko;
 namespace {
 
 constexpr int64_t kStagingRows = 65536;  // indexer rows per host-append piece
+constexpr int kStampLaunches = 1024;     // timed LRU-update launches recorded between reads
 
 thread_local std::string g_err;
 
@@ -159,6 +160,18 @@ struct sko_handle {
     std::vector<hipEvent_t> spare;
     double total_ms[ST_COUNT] = {};
     int64_t launches[ST_COUNT] = {};
+    // block start / end stamps of timed LRU-update launches (early copy):
+    // [kStampLaunches][stamp_blocks][2] on the device clock
+    uint64_t* stamps = nullptr;
+    int stamp_blocks = 0;        // most blocks one LRU-update launch can hold
+    int stamp_next = 0;
+    struct StampLaunch {
+        int slot, nmerge, nblocks;
+    };
+    std::vector<StampLaunch> stamp_pending;
+    double clock_khz = 100000.0;  // device wall clock (s_memrealtime)
+    double ovl_copy_ms = 0.0, ovl_merge_ms = 0.0, ovl_both_ms = 0.0;
+    int64_t ovl_launches = 0;
 
     std::vector<void*> dev_allocs;
 
@@ -246,6 +259,41 @@ int run_stage(sko_handle* h, int stage, F&& launch) {
 int check_handle(sko_handle* h) {
     if (!h) return set_err(SKO_E_INVAL, "NULL handle");
     if (h->failed) return set_err(SKO_E_STATE, "handle is FAILED after an earlier device error or a broken invariant");
+    return SKO_OK;
+}
+
+// After a stream synchronize: fold the recorded block stamps of timed
+// LRU-update launches into the overlap totals.  Per launch, the copy span
+// runs from the first copy block's start to the last one's end, the merge
+// span likewise over the merge blocks, and the overlap is their
+// intersection.
+int collect_stamps(sko_handle* h) {
+    if (h->stamp_pending.empty()) return SKO_OK;
+    std::vector<uint64_t> v((size_t)h->stamp_blocks * 2);
+    for (const auto& p : h->stamp_pending) {
+        const hipError_t e = hipMemcpy(v.data(), h->stamps + (size_t)p.slot * h->stamp_blocks * 2,
+                                       (size_t)p.nblocks * 2 * 8, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return device_fail(h, e, "read block stamps");
+        uint64_t m0 = ~0ull, m1 = 0, c0 = ~0ull, c1 = 0;
+        for (int i = 0; i < p.nblocks; ++i) {
+            const uint64_t a = v[2 * (size_t)i], b = v[2 * (size_t)i + 1];
+            if (i < p.nmerge) {
+                m0 = std::min(m0, a);
+                m1 = std::max(m1, b);
+            } else {
+                c0 = std::min(c0, a);
+                c1 = std::max(c1, b);
+            }
+        }
+        if (p.nblocks <= p.nmerge || m1 < m0 || c1 < c0) continue;
+        const double tick_ms = 1.0 / h->clock_khz;
+        h->ovl_copy_ms += (double)(c1 - c0) * tick_ms;
+        h->ovl_merge_ms += (double)(m1 - m0) * tick_ms;
+        const uint64_t lo = std::max(m0, c0), hi = std::min(m1, c1);
+        h->ovl_both_ms += hi > lo ? (double)(hi - lo) * tick_ms : 0.0;
+        h->ovl_launches += 1;
+    }
+    h->stamp_pending.clear();
     return SKO_OK;
 }
 
@@ -420,6 +468,20 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
         if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_fork, 0);
         if (e != hipSuccess) return device_fail(h, e, "fork of the hit attention");
     }
+    // timed early-copy launches also record their blocks' start and end
+    uint64_t* stamps = nullptr;
+    if (staged && h->stamps && ((h->timing_mask >> ST_MERGE_LRU) & 1u) &&
+        (int)h->stamp_pending.size() < kStampLaunches) {
+        int cps = 0, cw = 0;
+        copy_shape(B, max_now, &cps, &cw);
+        // the record holds stamp_blocks blocks (the launch at full capacity);
+        // a launch with more blocks is not recorded
+        if (B + B * cps <= h->stamp_blocks) {
+            const int slot = h->stamp_next++ % kStampLaunches;
+            stamps = h->stamps + (size_t)slot * h->stamp_blocks * 2;
+            h->stamp_pending.push_back({slot, B, B + B * cps});
+        }
+    }
     if ((rc = run_stage(h, ST_MERGE_LRU, [&] {
              return launch_merge_lru(h->stream, sc.winners, sc.hist, sc.meta, sc.cand, h->topk, ntok, cs, st, lu,
                                      ring0, ring1, ring_pos, ring_state, B, D, k, S, cap, t, h->misses, h->victims,
@@ -427,7 +489,7 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
                                      staged ? sc.miss_bits : nullptr, pool_layer, recent_layer, h->stage_rows,
                                      staged ? sc.rdcp : nullptr, h->phys,
                                      /* the split attention reads the lists during this launch */ !h->hit_overlap,
-                                     max_now, (h->cfg.flags & SKO_FLAG_TEST_VIOLATION) != 0);
+                                     max_now, (h->cfg.flags & SKO_FLAG_TEST_VIOLATION) != 0, stamps);
          })))
         return rc;
     // late copy: its own gather from the pool; fused or early: the attention
@@ -666,6 +728,17 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     ok = ok && dev_alloc(h, (void**)&h->glist, BD * h->k * sizeof(GatherEntry));
     ok = ok && dev_alloc(h, (void**)&h->part_acc, BD * h->HG * pchunks * kAttnHeadGroup * kVDim * 4);
     ok = ok && dev_alloc(h, (void**)&h->part_ml, BD * h->HG * pchunks * kAttnHeadGroup * 2 * 4);
+    if (h->staged_copy) {
+        int cps = 0, cw = 0;
+        copy_shape(h->B, h->cap, &cps, &cw);
+        h->stamp_blocks = h->B + h->B * cps;
+        ok = ok && dev_alloc(h, (void**)&h->stamps, (size_t)kStampLaunches * h->stamp_blocks * 2 * 8);
+    }
+    {
+        int khz = 0;
+        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, cfg->device) == hipSuccess && khz > 0)
+            h->clock_khz = khz;
+    }
     if (!ok) {
         free_all(h);
         delete h;
@@ -1001,6 +1074,9 @@ int sko_set_timing(sko_handle* h, uint32_t stage_mask) {
         h->total_ms[i] = 0.0;
         h->launches[i] = 0;
     }
+    h->stamp_pending.clear();
+    h->ovl_copy_ms = h->ovl_merge_ms = h->ovl_both_ms = 0.0;
+    h->ovl_launches = 0;
     h->timing_mask = stage_mask;
     return SKO_OK;
 }
@@ -1022,10 +1098,27 @@ int sko_get_timing(sko_handle* h, double* total_ms, int64_t* launches, int32_t n
         h->spare.push_back(p.b);
     }
     h->pending.clear();
+    if ((rc = collect_stamps(h)) != SKO_OK) return rc;
     for (int i = 0; i < n && i < ST_COUNT; ++i) {
         total_ms[i] = h->total_ms[i];
         launches[i] = h->launches[i];
     }
+    return SKO_OK;
+}
+
+int sko_get_copy_overlap(sko_handle* h, double* copy_ms, double* merge_ms, double* overlap_ms,
+                         int64_t* launches) {
+    int rc = check_handle(h);
+    if (rc != SKO_OK) return rc;
+    if (!copy_ms || !merge_ms || !overlap_ms || !launches) return set_err(SKO_E_INVAL, "NULL output");
+    DeviceGuard guard(h->cfg.device);
+    const hipError_t e = hipStreamSynchronize(h->stream);
+    if (e != hipSuccess) return device_fail(h, e, "overlap sync");
+    if ((rc = collect_stamps(h)) != SKO_OK) return rc;
+    *copy_ms = h->ovl_copy_ms;
+    *merge_ms = h->ovl_merge_ms;
+    *overlap_ms = h->ovl_both_ms;
+    *launches = h->ovl_launches;
     return SKO_OK;
 }
 

@@ -132,7 +132,7 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
                             uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
                             uint16_t* stage_rows, int2* rdcp, int32_t* phys, bool sort_winners,
-                            int64_t max_tokens_now, bool test_violation);
+                            int64_t max_tokens_now, bool test_violation, uint64_t* stamps);
 // Copy blocks of the early copy: copy_per_seq per sequence, each owning
 // copy_words bitmap words (a multiple of 4, at most 1024).
 void copy_shape(int B, int64_t max_tokens_now, int* copy_per_seq, int* copy_words);

@@ -162,9 +162,17 @@ def test_timing_counts_one_launch_per_layer_step():
             assert launches == layer_steps, (stage, launches)
             assert ms > 0.0
         assert tm.get("gather_misses", (0.0, 0))[1] == 0  # no late gather in this mode
+        # block stamps of the timed LRU-update launches: a copy span and a
+        # merge span per launch, their overlap no longer than either
+        ov = h.copy_overlap()
+        log(f"copy overlap: {ov}")
+        assert ov["launches"] == layer_steps
+        assert ov["copy_ms"] > 0.0 and ov["merge_ms"] > 0.0
+        assert 0.0 <= ov["overlap_ms"] <= min(ov["copy_ms"], ov["merge_ms"]) + 1e-9
         # clearing the mask clears the totals
         h.set_timing(0)
         assert all(c == 0 for _, c in h.timing().values())
+        assert h.copy_overlap()["launches"] == 0
         assert [h.stats(l).steps for l in range(w.layers)] == [n] * w.layers
 
 
