@@ -375,9 +375,77 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t r_begin = (int64_t)blockIdx.x * total_tiles / gridDim.x;
     const int64_t r_end = ((int64_t)blockIdx.x + 1) * total_tiles / gridDim.x;
+    // query terms of positions p0.. of row0's sequence, staged in LDS (the
+    // caller synchronizes).  qbits: this thread's bf16 term (thread t holds
+    // term t % 64 of position t / 64).  The int8 indexer quantizes each
+    // position's rotated query (waves 0..NP-1, one row each) into sq8 and
+    // qc8; otherwise the terms go to sq as binary32, where each chain loads
+    // its position's terms 16 per register (replicated in the four 16-lane
+    // rows): register m, lane l holds term 16*m + (l % 16).
+    auto stage_query = [&](size_t row0, uint32_t qbits) {
+        if constexpr (C8) {
+            if (wave < NP) {
+                uint32_t sc;
+                const int code = quant_row_wave(__uint_as_float(qbits << 16), &sc);
+                const uint32_t word = pack_codes4(code);
+                uint32_t* qg = qc8 + (row0 + wave) * kQc8Words;
+                uint32_t* ql = reinterpret_cast<uint32_t*>(&sq8[wave][0]);
+                if ((lane & 3) == 0) {
+                    ql[lane >> 2] = word;
+                    qg[lane >> 2] = word;
+                }
+                if (lane == 0) {
+                    ql[kIdxDim / 4] = sc;
+                    qg[kIdxDim / 4] = sc;
+                }
+            }
+        } else if constexpr (NP > 1) {
+            static_assert(NP == 1 || score_threads<NP>() >= NP * kIdxDim, "one query term per thread");
+            if ((int)threadIdx.x < NP * kIdxDim) sq[threadIdx.x] = __uint_as_float(qbits << 16);
+        }
+    };
+    // this thread's query term (clamped in bounds; used by threads below
+    // NP * 64 only)
+    auto query_bits = [&](size_t row0) -> uint32_t {
+        return (uint32_t)reinterpret_cast<const uint16_t*>(q_idx)[row0 * kIdxDim +
+                                                                  std::min<int>(threadIdx.x, NP * kIdxDim - 1)];
+    };
+    // Two register tiles per wave (ping-pong, below).  The wave's first tile
+    // of the block's first segment is requested before the block's set-up
+    // (query staging, histogram clear), so its latency overlaps that work.
+    // Every block has at least one tile of the flattened space (the launch
+    // holds at most as many blocks as tiles), and the loads below are
+    // unconditional on clamped indexes, so the set-up waits only for the
+    // query term, not for the tile.
+    uint4 ra[RU], rb[RU];
+    uint32_t sa = 0u, sb = 0u;  // C8: the lane's token scales
+    const int b_first = (int)(r_begin / tiles_now);
+    const size_t row0_first = (size_t)b_first * D + p0;
+    const uint32_t qpre = (NP > 1 || C8) ? query_bits(row0_first) : 0u;
+    // keep the query load ahead of the tile loads: loads complete in order,
+    // so waiting for it then leaves the tile in flight
+    __builtin_amdgcn_sched_barrier(0);
+    bool preloaded;  // ra holds this wave's first tile of the first segment
+    {
+        const int64_t tile0 = r_begin - (int64_t)b_first * tiles_now;
+        const int64_t tile_end = std::min<int64_t>(std::min<int64_t>(r_end, ((int64_t)b_first + 1) * tiles_now) -
+                                                       (int64_t)b_first * tiles_now,
+                                                   (ntok_layer[b_first] + kIdxTile - 1) / kIdxTile);
+        const int64_t tile = tile0 + wave;
+        preloaded = tile < tile_end;
+        // a wave without a tile reads an in-range one it does not use
+        const int64_t tl = std::max<int64_t>(0, std::min<int64_t>(tile, tile_end - 1));
+        const uint4* __restrict__ st = idx_layer + (size_t)b_first * ntiles * RU * kIdxTile + lane;
+#pragma unroll
+        for (int c = 0; c < RU; ++c) ra[c] = load_nt_u4(st + (tl * RU + c) * kIdxTile);
+        if constexpr (C8) sa = scales_layer[(size_t)b_first * ntiles * kIdxTile + lane + tl * kIdxTile];
+    }
+    // the first segment's queries while its first tiles are in flight
+    stage_query(row0_first, qpre);
     for (int i = threadIdx.x; i < NP * kHistBins; i += blockDim.x) sh[i] = 0u;
     __syncthreads();
     for (int64_t seg = r_begin; seg < r_end;) {
+        const bool first_segment = seg == r_begin;
         const int b = (int)(seg / tiles_now);
         const int64_t seg_end = std::min<int64_t>(r_end, ((int64_t)b + 1) * tiles_now);
         const int64_t Lt = ntok_layer[b];
@@ -392,31 +460,8 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
         const uint4* __restrict__ seq_tiles = idx_layer + (size_t)b * ntiles * RU * kIdxTile + lane;
         const uint16_t* __restrict__ seq_scales = C8 ? scales_layer + (size_t)b * ntiles * kIdxTile + lane : nullptr;
         const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
-        // query terms of positions p0.. as binary32 in LDS; each chain loads
-        // its position's terms 16 per register (replicated in the four
-        // 16-lane rows): register m, lane l holds term 16*m + (l % 16)
-        if constexpr (C8) {
-            if (wave < NP) {
-                const uint16_t* qh = reinterpret_cast<const uint16_t*>(q_idx) + (row0 + wave) * kIdxDim;
-                uint32_t sc;
-                const int code = quant_row_wave(__uint_as_float((uint32_t)qh[lane] << 16), &sc);
-                const uint32_t word = pack_codes4(code);
-                uint32_t* qg = qc8 + (row0 + wave) * kQc8Words;
-                uint32_t* ql = reinterpret_cast<uint32_t*>(&sq8[wave][0]);
-                if ((lane & 3) == 0) {
-                    ql[lane >> 2] = word;
-                    qg[lane >> 2] = word;
-                }
-                if (lane == 0) {
-                    ql[kIdxDim / 4] = sc;
-                    qg[kIdxDim / 4] = sc;
-                }
-            }
-            __syncthreads();
-        } else if constexpr (NP > 1) {
-            const uint16_t* qh = reinterpret_cast<const uint16_t*>(q_idx) + row0 * kIdxDim;
-            for (int i = threadIdx.x; i < NP * kIdxDim; i += blockDim.x)
-                sq[i] = __uint_as_float((uint32_t)qh[i] << 16);
+        if ((NP > 1 || C8) && !first_segment) {
+            stage_query(row0, query_bits(row0));
             __syncthreads();
         }
 
@@ -520,11 +565,10 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
                 }
             }
         };
-        uint4 ra[RU], rb[RU];
-        uint32_t sa = 0u, sb = 0u;  // C8: the lane's token scales
         int64_t tile = tile0 + wave;
         if (tile < tile_end) {
-            load_tile(ra, sa, tile);
+            // (the first segment's first tile was requested at the start)
+            if (!(first_segment && preloaded)) load_tile(ra, sa, tile);
             for (; tile < tile_end; tile += 2 * nw) {
                 load_tile(rb, sb, tile + nw);
                 score_tile(ra, sa, tile);
