@@ -317,6 +317,25 @@ def prefill_bench(args) -> int:
     return 0
 
 
+def cache_management(calib, overlap):
+    """Selection (score pass, filter, refine) plus the LRU update of one
+    layer-step, in µs, from the event-timed warm-up stages.  With the late or
+    fused copy the LRU-update launch does no copy and its stage time is the
+    update itself; with the early copy the launch also holds the copy blocks,
+    and the update is the span of its merge blocks (block stamps), which run
+    beside the copy."""
+    if not calib:
+        return None
+    per = {n: ms / c * 1e3 for n, (ms, c) in calib.items() if c}
+    sel = sum(per.get(n, 0.0) for n in ("score_hist", "topk_filter", "topk_refine"))
+    if overlap is None or not overlap["launches"] or overlap["copy_ms"] <= 0:
+        lru, src = per.get("merge_lru", 0.0), "merge_lru stage (no copy blocks in the launch)"
+    else:
+        lru, src = overlap["merge_ms"] / overlap["launches"] * 1e3, "merge blocks' span beside the copy blocks"
+    return {"selection_us": round(sel, 2), "lru_update_us": round(lru, 2), "total_us": round(sel + lru, 2),
+            "lru_update_source": src}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,8 +354,8 @@ def main() -> int:
     ap.add_argument("--pool", choices=["default", "coherent", "noncoherent"], default="default",
                     help="host-pool allocation mode")
     ap.add_argument("--copy", choices=["default", "early", "late", "fused"], default="default",
-                    help="miss-copy arrangement: early (the default: by extra blocks of the LRU-update launch, "
-                         "into staging), late (after the LRU update), fused (inside the attention launch; one "
+                    help="miss-copy arrangement: early (the default: by extra blocks of the LRU-update launch), "
+                         "late (after the LRU update), fused (inside the attention launch; one "
                          "position, at most 16 heads)")
     ap.add_argument("--hit-overlap", action="store_true",
                     help="with the early copy: attend the resident rows on a side stream beside the copy launch, "
@@ -473,10 +492,10 @@ def main() -> int:
         """Algorithmic bytes per launch of the modelled kernels, averaged over
         decode steps first_step .. first_step + nsteps - 1.  The launch that
         reads the missed rows over the host link is bound by it: the
-        attention (mode "fused"), the staging copy of the merge launch
-        ("early"; the attention then reads missed rows from the staging area
-        and writes each into its slot once, on top of its reads of the
-        winners), or the gather ("late")."""
+        attention (mode "fused"), the copy blocks of the merge launch
+        ("early") or the gather ("late"); each missed row is written once,
+        into the row its slot takes over, and the attention reads the
+        winners' rows."""
         avg_lt = w.context + first_step + (nsteps + 1) / 2.0  # tokens present after each append
         ls = L * nsteps
         per = h2d_bytes / ls if ls else 0.0
@@ -490,7 +509,6 @@ def main() -> int:
         attn = KV_ROW * B * D * min(k, avg_lt)
         if mode == "early":
             m["merge_lru"] = copy  # its copy blocks read the missed rows from the host
-            attn += per
         else:
             m["gather_misses"] = copy
         m["attn_partial"] = (attn, "hbm", HBM_PEAK_GBPS)
@@ -588,6 +606,9 @@ def main() -> int:
             "exposed_non_link_us_per_layer_step": round(
                 elapsed / layer_steps * 1e6 - d["h2d_bytes"] / layer_steps / (h2d_ceiling * 1e9) * 1e6, 2),
         } if overlap and overlap["launches"] and overlap["copy_ms"] > 0 else None),
+        # the selection and LRU bookkeeping of a layer-step, the miss copy
+        # excluded (the pages' "cache management" per indexer layer)
+        "cache_management_us_per_layer_step": cache_management(calib, overlap),
         "selection_rescans": d["rescans"],
         "newest_rows_from_device": d["direct_rows"],
         "roofline": roof,

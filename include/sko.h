@@ -75,16 +75,16 @@ extern "C" {
  * path (same results, slower). */
 #define SKO_FLAG_SELECT_RESCAN 0x8u
 /* How the rows that missed reach the device (at most one of these three;
- * all give the same results).  Default (SKO_FLAG_EARLY_COPY): as soon as
- * the selection is known, extra blocks of the LRU-update launch copy the
- * misses from the pool into a staging area, concurrently with the update;
- * the attention reads them from there and stores each into its slot.
- * SKO_FLAG_LATE_COPY: one kernel after the LRU update copies them from the
- * pool into their slots.  SKO_FLAG_FUSED_COPY: the attention launch reads
- * each missed row from the pool and stores it into its slot before
- * attending (the fused Copy-SFA operator of [LSO-zh] §4); only with one
- * position and at most 16 heads, where each row is read by one attention
- * block (SKO_E_INVAL otherwise). */
+ * all give the same results).  Each missed row is copied once, into the
+ * device row its victim slot takes over (see the hot buffer at
+ * sko_create).  Default (SKO_FLAG_EARLY_COPY): as soon as the selection is
+ * known, extra blocks of the LRU-update launch copy the misses from the
+ * pool, concurrently with the update.  SKO_FLAG_LATE_COPY: one kernel after
+ * the LRU update copies them.  SKO_FLAG_FUSED_COPY: the attention launch
+ * reads each missed row from the pool and stores it before attending (the
+ * fused Copy-SFA operator of [LSO-zh] §4); only with one position and at
+ * most 16 heads, where each row is read by one attention block
+ * (SKO_E_INVAL otherwise). */
 #define SKO_FLAG_FUSED_COPY 0x10u
 #define SKO_FLAG_LATE_COPY 0x20u
 #define SKO_FLAG_EARLY_COPY 0x40u
@@ -167,7 +167,14 @@ typedef struct sko_layer_stats {
  * offload state:
  *   host pool     pinned, device-mapped  [L][B][cap][576] bf16
  *   indexer cache device                 [L][B][cap][64]  bf16
- *   hot buffer    device                 [L][B][S][576]   bf16 (zeroed)
+ *   hot buffer    device                 [L][B][S+D*k][576] bf16 (zeroed):
+ *                 S rows hold the S slots, the other D*k are spare; a
+ *                 step copies its r-th miss (token order) into its r-th
+ *                 spare row, the r-th victim slot takes that row over and
+ *                 the victim's old row becomes spare.  Which row holds a
+ *                 slot is internal: the slot contents ([LSO] §4, the
+ *                 fixed-size hot buffer of S slots) are what
+ *                 sko_read_table(SKO_TAB_HOT) returns.
  *   cache_slots   device                 [L][B][cap] int32 = -1
  *   slot_token    device                 [L][B][S]   int32 = -1
  *   last_use      device                 [L][B][S]   int32 = -1
@@ -176,7 +183,9 @@ typedef struct sko_layer_stats {
  * Errors: SKO_E_INVAL (NULL pointer, a dimension other than 64/576/512,
  * L/B/H/k/D < 1, S < D*k, cap out of range, bad scale, unknown or
  * conflicting flags),
- * SKO_E_UNSUPPORTED (D*k > SKO_MAX_MERGE), SKO_E_NOMEM, SKO_E_DEVICE.
+ * SKO_E_UNSUPPORTED (D*k > SKO_MAX_MERGE, L*B*(S+D*k) hot rows or
+ * B*max_tokens or B*S at or beyond the int32/uint32 row-number range),
+ * SKO_E_NOMEM, SKO_E_DEVICE.
  */
 int sko_create(const sko_config* cfg, void* stream, sko_handle** out);
 
@@ -291,11 +300,14 @@ enum sko_table {
     SKO_TAB_CACHE_SLOTS = 1, /* int32 [cap] */
     SKO_TAB_SLOT_TOKEN = 2,  /* int32 [S] */
     SKO_TAB_LAST_USE = 3,    /* int32 [S] */
-    SKO_TAB_HOT = 4,         /* bf16 [S][576] */
+    SKO_TAB_HOT = 4,         /* bf16 [S][576]: the row of each slot, in slot order */
     SKO_TAB_INDEXER = 5,     /* bf16 [cap][64]; with SKO_FLAG_INDEXER_C8 int8 codes [cap][64] */
     SKO_TAB_POOL = 6,        /* bf16 [cap][576] (host pool) */
     SKO_TAB_NTOK = 7,        /* int64 [1] tokens present */
-    SKO_TAB_INDEXER_SCALE = 8 /* fp16 [cap] scales; only with SKO_FLAG_INDEXER_C8, else SKO_E_STATE */
+    SKO_TAB_INDEXER_SCALE = 8, /* fp16 [cap] scales; only with SKO_FLAG_INDEXER_C8, else SKO_E_STATE */
+    SKO_TAB_SLOT_ROW = 9,    /* int32 [S]: the device row holding each slot (0 <= row < S + D*k) */
+    SKO_TAB_SPARE_ROWS = 10  /* int32 [D*k]: the spare rows the layer's next step copies its misses into;
+                                with SKO_TAB_SLOT_ROW a permutation of 0 .. S + D*k - 1 */
 };
 
 /*

@@ -47,6 +47,7 @@ SKO_BUF_MISSES, SKO_BUF_VICTIMS, SKO_BUF_EVICT_OLD, SKO_BUF_KEYS = 4, 5, 6, 7
 SKO_TAB_CACHE_SLOTS, SKO_TAB_SLOT_TOKEN, SKO_TAB_LAST_USE = 1, 2, 3
 SKO_TAB_HOT, SKO_TAB_INDEXER, SKO_TAB_POOL, SKO_TAB_NTOK = 4, 5, 6, 7
 SKO_TAB_INDEXER_SCALE = 8
+SKO_TAB_SLOT_ROW, SKO_TAB_SPARE_ROWS = 9, 10
 
 EXPORTED = (
     "sko_create", "sko_set_stream", "sko_append_token", "sko_decode_step", "sko_decode_step_static",
@@ -360,6 +361,8 @@ class SparseKVOffload:
             SKO_TAB_POOL: ((c.max_tokens, SKO_KV_DIM), np.uint16),
             SKO_TAB_NTOK: ((1,), np.int64),
             SKO_TAB_INDEXER_SCALE: ((c.max_tokens,), np.uint16),
+            SKO_TAB_SLOT_ROW: ((c.hot_slots,), np.int32),
+            SKO_TAB_SPARE_ROWS: ((c.mtp_positions * c.top_k,), np.int32),
         }
         shape, dt = shapes[which]
         return sko_read_table(self.handle, layer, seq, which, np.zeros(shape, dtype=dt))

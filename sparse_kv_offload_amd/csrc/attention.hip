@@ -8,18 +8,19 @@
 //     out = sum_j softmax(z)_j * V_j  over the first 512 (latent) columns,
 // j running over the min(k, L_t) winners of that position.
 //
-// The launch also puts the rows that missed into their victim slots.  With
-// one query position and one group of 16 heads every winner row is read by
-// exactly one block, which can read a missed row straight from the pinned
-// host pool (device-mapped) and write it into its slot (the Copy-SFA fusion
-// of the Chinese revision), so the host-link transfer of one block overlaps
-// the attention of the others and no separate copy kernel runs.  Otherwise
-// the rows were copied early into a staging area that follows the hot
-// buffer in memory: every block reads its missed rows from there, and the
-// block whose entry the LRU-update launch designated for each missed row
-// also writes it into its victim slot for later steps.  A split launch pair
-// attends the rows resident at step start and the missed rows separately
-// (AttnPhase below), each writing its own partials.
+// Every slot lives in a physical hot row (slot_row), and the misses of a
+// step arrive in spare rows that their victim slots then take over, so the
+// rows of a step never move.  Which row a winner reads comes either from the
+// list the LRU-update launch wrote (wrow: the default, with the copy done
+// early by that launch or late by its own kernel) or from the tables
+// (slot_row[cache_slots[token]]).  With one query position and one group of
+// 16 heads every winner row is read by exactly one block, which can also
+// read a missed row straight from the pinned host pool (device-mapped) and
+// write it into its row (the Copy-SFA fusion of the Chinese revision), so
+// the host-link transfer of one block overlaps the attention of the others
+// and no separate copy kernel runs.  A split launch pair attends the rows
+// resident at step start and the missed rows separately (AttnPhase below),
+// each writing its own partials.
 //
 // Layout of the work: a block takes one (seq, position), one group of 16
 // heads and a chunk of winners.  Rows are staged 32 at a time in LDS (one
@@ -37,7 +38,9 @@
 namespace sko {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kRowStrideU4 = kKvRowU4 + 1;  // 16-byte pad per staged row
 
@@ -56,8 +59,131 @@ __device__ __forceinline__ uint32_t dword_of(uint4 v, int m) {
     return (m >> 1) == 0 ? v.x : (m >> 1) == 1 ? v.y : (m >> 1) == 2 ? v.z : v.w;
 }
 
+// ---- per-tile compute, shared by both attention kernels ---------------------
+// Four compute waves, lanes (n16, g): n16 = head within the group, g = lane
+// / 16.  The 18 k-steps (32 columns each) of S^T = K Q^T for a 32-row tile
+// are split over the waves (5, 5, 4, 4); wave w holds the B operand Q^T of
+// its k-steps in qv (lane (n16, g): Q[h][32ks + 8g .. +7]).
+
+// This wave's partial S^T tiles of the tile in `rows` (LDS, padded rows)
+// for rows 0..15 and 16..31, written to sp[wave].
+__device__ __forceinline__ void tile_scores(const uint4* rows, const uint4 (&qv)[5], int ks0, int nks, int n16,
+                                            int g, int lane, int wave, f32x4_t (*sp)[2][64]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+        const uint4* rp = rows + (half * 16 + n16) * kRowStrideU4 + g;
+#pragma unroll
+        for (int q = 0; q < 5; ++q)
+            if (q < nks)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rp[4 * (ks0 + q)]), as_bf16x8(qv[q]), c, 0, 0,
+                                                            0);
+        sp[wave][half][lane] = c;
+    }
+}
+
+// Once every wave's partial tiles are in sp: the scores of the tile's rows
+// r .. r+31 (the four partials added in wave order; rows at or past n
+// masked), the online-softmax update of (m_run, l_run) per head (exp2 of
+// scaled scores), and O^T += V^T P^T for this wave's 128 output columns
+// (P in bf16, fp32 accumulation).
+__device__ __forceinline__ void tile_softmax_pv(const uint4* rows, const f32x4_t (*sp)[2][64], int r, int n,
+                                                float scale_log2, int n16, int g, int lane, int wave, float& m_run,
+                                                float& l_run, f32x4_t (&acc)[8]) {
+    float s[2][4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const f32x4_t c = ((sp[0][half][lane] + sp[1][half][lane]) + sp[2][half][lane]) + sp[3][half][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = r + half * 16 + 4 * g + i;
+            s[half][i] = (j < n) ? c[i] * scale_log2 : -INFINITY;
+        }
+    }
+    // online softmax per head over the 32 rows (lane groups g share a head)
+    float mt = s[0][0];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[half][i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    // v_exp_f32 directly: arguments are <= 0 (or -inf: 0), results that
+    // would be binary32 subnormals flush to zero
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float p[2][4];
+    float ls = 0.0f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[half][i] = __builtin_amdgcn_exp2f(s[half][i] - m_new);
+            ls += p[half][i];
+        }
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+    // once the running maxima settle, most tiles leave every head's maximum
+    // unchanged (alpha exactly 1): the rescale is skipped for the wave
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m] *= alpha;
+    }
+
+    // B operand of O^T = V^T P^T: k-slot s of group g is row 4g+s (s<4)
+    // or 16+4g+s-4 (s>=4), i.e. exactly the rows this lane's p covers;
+    // P rounded to bf16 (nearest even) two at a time
+    uint4 pb;
+    pb.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){p[0][0], p[0][1]}, bf16x2_t));
+    pb.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){p[0][2], p[0][3]}, bf16x2_t));
+    pb.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){p[1][0], p[1][1]}, bf16x2_t));
+    pb.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){p[1][2], p[1][3]}, bf16x2_t));
+
+    // A operand: V^T.  Lane reads 8 columns (cb + 8*n16 .. +7) of each of
+    // its 8 rows; column cb + 8*n16 + m feeds MFMA m.
+    uint4 vr[8];
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+        const int R = (sl < 4) ? (4 * g + sl) : (16 + 4 * g + sl - 4);
+        vr[sl] = rows[R * kRowStrideU4 + wave * 16 + n16];
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        // element m of each row: the low half of dword m/2 for even m, the
+        // high half for odd m; two rows' elements per dword (v_perm_b32
+        // byte select: 0..3 = bytes of the second operand, 4..7 = first)
+        const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t d[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d[q] = __builtin_amdgcn_perm(dword_of(vr[2 * q + 1], m), dword_of(vr[2 * q], m), sel);
+        const uint4 a = make_uint4(d[0], d[1], d[2], d[3]);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pb), acc[m], 0, 0, 0);
+    }
+}
+
+// This wave's (m, l, acc) partials: acc of 16 heads x its 128 columns, and
+// (m, l) per head from wave 0.
+__device__ __forceinline__ void write_partials(float* acc_out, float* ml_out, const f32x4_t (&acc)[8], float m_run,
+                                               float l_run, int h, int H, int n16, int g, int wave) {
+    float lt = l_run + __shfl_xor(l_run, 16);
+    lt += __shfl_xor(lt, 32);
+    const int cb = wave * 128;
+    if (h < H) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc_out[n16 * kVDim + cb + 8 * (4 * g + i) + m] = acc[m][i];
+    }
+    if (wave == 0 && g == 0) {
+        ml_out[2 * n16] = m_run;
+        ml_out[2 * n16 + 1] = lt;
+    }
+}
+
 // How the launch gets the rows that missed into their slots.
-enum AttnCopy { kCopyNone = 0, kCopyPool = 1, kCopyStaged = 2 };
+// Where a launch finds each winner's row: the tables, the tables plus the
+// fused copy of the misses, or the LRU-update launch's row list.
+enum AttnRows { kRowsTables = 0, kRowsFusedCopy = 1, kRowsGiven = 2 };
 
 // Which rows of a chunk a launch attends: all of them, only those resident
 // at step start (hits), or only those that missed.  A split runs the hits
@@ -65,18 +191,18 @@ enum AttnCopy { kCopyNone = 0, kCopyPool = 1, kCopyStaged = 2 };
 // phase writes its own partials, the combine merges both.
 enum AttnPhase { kPhaseAll = 0, kPhaseHits = 1, kPhaseMisses = 2 };
 
-template <int COPY, int PHASE>
+template <int ROWS, int PHASE>
 __global__ __launch_bounds__(256) void k_attn_partial(
     const int32_t* __restrict__ topk, const int32_t* __restrict__ cache_slots_layer,
-    uint4* __restrict__ hot_layer, const uint4* __restrict__ q_attn, const uint4* __restrict__ pool_layer,
-    const uint4* __restrict__ recent_layer,
-    const int32_t* __restrict__ ntok_layer, float* __restrict__ part_acc,
-    float* __restrict__ part_ml, int32_t* __restrict__ phys, const uint4* __restrict__ stage_rows,
-    const int2* __restrict__ rdcp, uint32_t* __restrict__ miss_bits, int64_t wpr, int B, int D, int H, int HG,
-    int top_k, int S, int64_t cap, int rows_per_block, int nchunk, int pchunks, float scale_log2) {
+    const int32_t* __restrict__ slot_row_layer, uint4* __restrict__ hot_layer, const uint4* __restrict__ q_attn,
+    const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
+    const int32_t* __restrict__ ntok_layer, float* __restrict__ part_acc, float* __restrict__ part_ml,
+    int32_t* __restrict__ phys, const int32_t* __restrict__ wrow, uint32_t* __restrict__ miss_bits, int64_t wpr,
+    int D, int H, int HG, int top_k, int S, int R, int64_t cap, int rows_per_block, int nchunk, int pchunks,
+    float scale_log2) {
     __shared__ uint4 rows[kAttnTileRows * kRowStrideU4];
     __shared__ int32_t slot_s[kAttnMaxRowsPerBlock];  // row read, relative to the sequence's hot rows
-    __shared__ int32_t cp_s[kAttnMaxRowsPerBlock];    // copy: pool token (fused) or victim slot (staged), else -1
+    __shared__ int32_t cp_s[kAttnMaxRowsPerBlock];    // fused copy: pool token of a missed row, else -1
     __shared__ f32x4_t sp[4][2][64];  // per-wave partial S^T tiles
     __shared__ int scratch[256 / 64 + 1];
 
@@ -85,21 +211,19 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15, g = lane >> 4;
     const int h = hg * kAttnHeadGroup + n16;
-    constexpr bool fused_copy = COPY == kCopyPool;
-    constexpr bool staged = COPY == kCopyStaged;
+    constexpr bool fused_copy = ROWS == kRowsFusedCopy;
+    constexpr bool given = ROWS == kRowsGiven;
     const int r0 = chunk * rows_per_block;
     // list entries this chunk can hold (known without the token count)
     const int rcap = std::min(r0 + rows_per_block, top_k);
     const int32_t* __restrict__ w = topk + (size_t)bp * top_k;
-    const int2* __restrict__ rc = staged ? rdcp + (size_t)bp * top_k : nullptr;
 
     // The loads that depend on nothing else are issued together, before any
-    // of them is waited for: the token count, the chunk's list entries and
-    // the query operand.
+    // of them is waited for: the token count, the chunk's list entries (and
+    // rows) and the query operand.
     const int64_t Lt = ntok_layer[b];
     constexpr int kRowsPerThread = kAttnMaxRowsPerBlock / 256;
-    int32_t pk[kRowsPerThread];
-    int2 pe[kRowsPerThread];
+    int32_t pk[kRowsPerThread], pr[kRowsPerThread];
 #pragma unroll
     for (int u = 0; u < kRowsPerThread; ++u) {
         // all rows: thread t takes entries t, t + 256; a split phase keeps
@@ -108,8 +232,8 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         // read in bounds (clamped) and used only below the chunk's row count
         const int jc = std::min(r0 + j, top_k - 1);
         pk[u] = w[jc];
-        pe[u] = make_int2(-1, -1);
-        if constexpr (staged) pe[u] = rc[jc];
+        pr[u] = -1;
+        if constexpr (given) pr[u] = wrow[(size_t)bp * top_k + jc];
     }
     // The 18 k-steps (32 columns each) of S^T = K Q^T are split over the 4
     // waves (5, 5, 4, 4); wave w holds the B operand Q^T of its k-steps:
@@ -141,33 +265,32 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         return;
     }
     const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
-    uint4* __restrict__ hb = hot_layer + (size_t)b * S * kKvRowU4;
-    // staging rows of this sequence, as row numbers relative to hb (the
-    // staging area lies in the same allocation, after every layer's rows)
-    const int64_t stage_base = staged ? (stage_rows - hb) / kKvRowU4 + (int64_t)b * D * top_k : 0;
+    const int32_t* __restrict__ srow = slot_row_layer + (size_t)b * S;
+    uint4* __restrict__ hb = hot_layer + (size_t)b * R * kKvRowU4;
 
     // remap: logical winner -> the row to read for the chunk's rows of this
     // phase (a split phase keeps its rows compacted in winner order: rows
-    // 0 .. n-1 of the block).  Staged: the LRU-update launch wrote, per
-    // winner, the row (slot >= 0, -(r + 2) for staging row r, -1 none) and
-    // the slot a missed row moves into (one entry per miss), and its hot
-    // slot into phys; the miss's bitmap word is cleared for the next step
-    // (several blocks may store the same zero).  A row that resolves to no
-    // slot (only possible with a broken invariant, which the LRU-update
-    // launch reports) reads row 0 instead of leaving the buffer.
-    uint32_t* __restrict__ mbw = staged ? miss_bits + (size_t)b * wpr : nullptr;
-    auto remap = [&](int j, int32_t packed, int2 e, int q) {
+    // 0 .. n-1 of the block).  Given rows come with the list; otherwise the
+    // winner's slot (cache_slots) and the slot's row (slot_row).  With the
+    // given list the miss's bitmap word is cleared for the next step
+    // (several blocks may store the same zero).  A row that resolves to none
+    // (only possible with a broken invariant, which the LRU-update launch
+    // reports) reads row 0 instead of leaving the buffer.
+    uint32_t* __restrict__ mbw = miss_bits != nullptr ? miss_bits + (size_t)b * wpr : nullptr;
+    auto remap = [&](int j, int32_t packed, int32_t given_row, int q) {
         int32_t rd = -1, cp = -1;
-        if constexpr (staged) {
-            rd = e.x >= 0 ? e.x : (e.x <= -2 ? (int32_t)(stage_base + min(-e.x - 2, D * top_k - 1)) : -1);
-            cp = e.y;
-            if (packed < 0) mbw[(packed & 0x7FFFFFFF) >> 5] = 0u;
+        if constexpr (given) {
+            rd = given_row;
+            if (mbw != nullptr && packed < 0) mbw[(packed & 0x7FFFFFFF) >> 5] = 0u;
         } else {
             const int32_t tok = packed & 0x7FFFFFFF;
             int32_t slot = (tok < cap) ? cs[tok] : -1;
             if (slot >= S) slot = -1;
-            rd = slot;
-            if (fused_copy && packed < 0 && slot >= 0) cp = tok;
+            if (slot >= 0) {
+                rd = srow[slot];
+                if (rd >= R) rd = -1;
+            }
+            if (fused_copy && packed < 0 && rd >= 0) cp = tok;
             if (hg == 0) phys[(size_t)bp * top_k + r0 + j] = slot;
         }
         slot_s[q] = rd >= 0 ? rd : 0;
@@ -178,7 +301,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(
 #pragma unroll
         for (int u = 0; u < kRowsPerThread; ++u) {
             const int j = tid + 256 * u;
-            if (j < n) remap(j, pk[u], pe[u], j);
+            if (j < n) remap(j, pk[u], pr[u], j);
         }
     } else {
         int nmine = 0;
@@ -191,7 +314,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(
 #pragma unroll
         for (int u = 0; u < kRowsPerThread; ++u) {
             const int j = tid * kRowsPerThread + u;
-            if (j < r1 - r0 && (PHASE == kPhaseHits) == (pk[u] >= 0)) remap(j, pk[u], pe[u], q++);
+            if (j < r1 - r0 && (PHASE == kPhaseHits) == (pk[u] >= 0)) remap(j, pk[u], pr[u], q++);
         }
     }
     if (n == 0) {  // block-uniform: no rows of this phase in the chunk
@@ -210,11 +333,9 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     }
 
     // Fused: the missed rows of this chunk are copied from the pool into
-    // their slots first (wave w takes rows w, w+4, ...; lanes 0..63 move
+    // their rows first (wave w takes rows w, w+4, ...; lanes 0..63 move
     // 16-byte chunks 0..63 of a row, lanes 0..7 chunks 64..71), and the
-    // attention below reads the slots.  (Staged: the attention reads the
-    // staging rows, and the tile loads below also store the claimed ones
-    // into their slots.)
+    // attention below reads them there.
     if (fused_copy) {
         __syncthreads();
         // one row in flight per wave: more outstanding host reads lowered
@@ -271,19 +392,6 @@ __global__ __launch_bounds__(256) void k_attn_partial(
 #define SKO_STASH()                                                                            \
     SKO_STASH1(0) SKO_STASH1(1) SKO_STASH1(2) SKO_STASH1(3) SKO_STASH1(4) SKO_STASH1(5)        \
     SKO_STASH1(6) SKO_STASH1(7) SKO_STASH1(8)
-    // staged: a tile row this block claimed is also stored into its slot,
-    // from LDS after the tile is complete there (the prefetch registers are
-    // then never the data of a pending store, so the next tile's loads need
-    // not wait for these stores)
-#define SKO_MOVE(rbase)                                                                              \
-    if (staged) {                                                                                    \
-        _Pragma("unroll") for (int u = 0; u < kPer; ++u) {                                          \
-            const int idx = tid + 256 * u;                                                          \
-            const int rr = idx / kKvRowU4;                                                          \
-            const int32_t c = cp_s[(rbase) + rr];                                                   \
-            if (c >= 0) hb[(size_t)c * kKvRowU4 + (idx - rr * kKvRowU4)] = rows[rr * kRowStrideU4 + (idx - rr * kKvRowU4)]; \
-        }                                                                                           \
-    }
     SKO_FETCH(0)
     SKO_STASH()
     __syncthreads();
@@ -293,87 +401,9 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         if (more) {
             SKO_FETCH(r + kAttnTileRows)
         }
-        // the claimed rows of this tile go to their slots once the next
-        // tile's loads are in flight
-        SKO_MOVE(r)
-
-        // S^T tiles for rows r..r+15 and r+16..r+31; lane holds head n16,
-        // rows 4g+i (+16).  Each wave forms its k-steps' partial sums; the
-        // four partials are added in wave order (the same in every wave).
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-            const uint4* rp = rows + (half * 16 + n16) * kRowStrideU4 + g;
-#pragma unroll
-            for (int q = 0; q < 5; ++q)
-                if (q < nks)
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rp[4 * (ks0 + q)]), as_bf16x8(qv[q]), c,
-                                                                0, 0, 0);
-            sp[wave][half][lane] = c;
-        }
+        tile_scores(rows, qv, ks0, nks, n16, g, lane, wave, sp);
         __syncthreads();
-        float s[2][4];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const f32x4_t c = ((sp[0][half][lane] + sp[1][half][lane]) + sp[2][half][lane]) + sp[3][half][lane];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = r + half * 16 + 4 * g + i;
-                s[half][i] = (j < n) ? c[i] * scale_log2 : -INFINITY;
-            }
-        }
-        // online softmax per head over the 32 rows (lane groups g share a head)
-        float mt = s[0][0];
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[half][i]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = exp2f(m_run - m_new);
-        float p[2][4];
-        float ls = 0.0f;
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[half][i] = exp2f(s[half][i] - m_new);
-                ls += p[half][i];
-            }
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) acc[m] *= alpha;
-
-        // B operand of O^T = V^T P^T: k-slot s of group g is row 4g+s (s<4)
-        // or 16+4g+s-4 (s>=4), i.e. exactly the rows this lane's p covers
-        uint4 pb;
-        pb.x = f32_to_bf16_bits(p[0][0]) | (f32_to_bf16_bits(p[0][1]) << 16);
-        pb.y = f32_to_bf16_bits(p[0][2]) | (f32_to_bf16_bits(p[0][3]) << 16);
-        pb.z = f32_to_bf16_bits(p[1][0]) | (f32_to_bf16_bits(p[1][1]) << 16);
-        pb.w = f32_to_bf16_bits(p[1][2]) | (f32_to_bf16_bits(p[1][3]) << 16);
-
-        // A operand: V^T.  Lane reads 8 columns (cb + 8*n16 .. +7) of each of
-        // its 8 rows; column cb + 8*n16 + m feeds MFMA m.
-        uint4 vr[8];
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-            const int R = (sl < 4) ? (4 * g + sl) : (16 + 4 * g + sl - 4);
-            vr[sl] = rows[R * kRowStrideU4 + wave * 16 + n16];
-        }
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            // element m of each row: low half of dword m/2 for even m, high half for odd m
-            uint32_t d[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t w0 = dword_of(vr[2 * q], m), w1 = dword_of(vr[2 * q + 1], m);
-                d[q] = (m & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
-            }
-            const uint4 a = make_uint4(d[0], d[1], d[2], d[3]);
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pb), acc[m], 0, 0, 0);
-        }
+        tile_softmax_pv(rows, sp, r, n, scale_log2, n16, g, lane, wave, m_run, l_run, acc);
         __syncthreads();
         if (more) {
             SKO_STASH()
@@ -384,21 +414,8 @@ __global__ __launch_bounds__(256) void k_attn_partial(
 #undef SKO_FETCH
 #undef SKO_STASH1
 #undef SKO_STASH
-#undef SKO_MOVE
 
-    float lt = l_run + __shfl_xor(l_run, 16);
-    lt += __shfl_xor(lt, 32);
-    const int cb = wave * 128;
-    if (h < H) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc_out[n16 * kVDim + cb + 8 * (4 * g + i) + m] = acc[m][i];
-    }
-    if (wave == 0 && g == 0) {
-        ml_out[2 * n16] = m_run;
-        ml_out[2 * n16 + 1] = lt;
-    }
+    write_partials(acc_out, ml_out, acc, m_run, l_run, h, H, n16, g, wave);
 }
 
 // Merge of the per-chunk partials (m, l, acc) of one (seq, position, head):
@@ -473,39 +490,56 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* _
 }
 
 hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_t* cache_slots_layer,
-                               uint16_t* hot_layer, const uint16_t* q_attn, const uint16_t* pool_layer,
-                               const uint16_t* recent_layer, const int32_t* ntok_layer, float* part_acc,
-                               float* part_ml,
-                               int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
-                               int rows_per_block, float scale, const uint16_t* stage_rows,
-                               const int2* rdcp, uint32_t* miss_bits, int phase) {
+                               const int32_t* slot_row_layer, uint16_t* hot_layer, int R, const uint16_t* q_attn,
+                               const uint16_t* pool_layer, const uint16_t* recent_layer, const int32_t* ntok_layer,
+                               float* part_acc, float* part_ml, int32_t* phys, int B, int D, int H, int top_k, int S,
+                               int64_t cap, int rows_per_block, float scale, const int32_t* wrow,
+                               uint32_t* miss_bits, int phase) {
     const int HG = (H + kAttnHeadGroup - 1) / kAttnHeadGroup;
     const int nchunk = (top_k + rows_per_block - 1) / rows_per_block;
     const int pchunks = phase == 0 ? nchunk : 2 * nchunk;
     const float scale_log2 = scale * 1.4426950408889634f;
-#define SKO_ATTN_LAUNCH(C, P)                                                                                 \
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_attn_partial<C, P>), dim3(nchunk, B * D, HG), dim3(256), 0, st, topk,     \
-                       cache_slots_layer, reinterpret_cast<uint4*>(hot_layer),                                   \
+#define SKO_ATTN_LAUNCH(W, P)                                                                                 \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_attn_partial<W, P>), dim3(nchunk, B * D, HG), dim3(256), 0, st, topk,     \
+                       cache_slots_layer, slot_row_layer, reinterpret_cast<uint4*>(hot_layer),                   \
                        reinterpret_cast<const uint4*>(q_attn), reinterpret_cast<const uint4*>(pool_layer),       \
-                       reinterpret_cast<const uint4*>(recent_layer), ntok_layer, part_acc, part_ml, phys,        \
-                       reinterpret_cast<const uint4*>(stage_rows), rdcp, miss_bits, winner_words(cap), B, D, H, HG, \
-                       top_k, S, cap, rows_per_block, nchunk, pchunks, scale_log2)
-    if (pool_layer != nullptr && stage_rows != nullptr) return hipErrorInvalidValue;
+                       reinterpret_cast<const uint4*>(recent_layer), ntok_layer, part_acc, part_ml, phys, wrow,  \
+                       miss_bits, winner_words(cap), D, H, HG, top_k, S, R, cap, rows_per_block, nchunk, pchunks, \
+                       scale_log2)
+    if (pool_layer != nullptr && wrow != nullptr) return hipErrorInvalidValue;
     if (phase == 1) {
         // the rows resident at step start: no copy of any kind
-        SKO_ATTN_LAUNCH(kCopyNone, kPhaseHits);
+        SKO_ATTN_LAUNCH(kRowsTables, kPhaseHits);
     } else if (phase == 2) {
-        if (stage_rows == nullptr || rdcp == nullptr || miss_bits == nullptr) return hipErrorInvalidValue;
-        SKO_ATTN_LAUNCH(kCopyStaged, kPhaseMisses);
+        if (wrow == nullptr) return hipErrorInvalidValue;
+        SKO_ATTN_LAUNCH(kRowsGiven, kPhaseMisses);
     } else if (pool_layer != nullptr) {
-        SKO_ATTN_LAUNCH(kCopyPool, kPhaseAll);
-    } else if (stage_rows != nullptr) {
-        if (rdcp == nullptr || miss_bits == nullptr) return hipErrorInvalidValue;
-        SKO_ATTN_LAUNCH(kCopyStaged, kPhaseAll);
+        SKO_ATTN_LAUNCH(kRowsFusedCopy, kPhaseAll);
+    } else if (wrow != nullptr) {
+        SKO_ATTN_LAUNCH(kRowsGiven, kPhaseAll);
     } else {
-        SKO_ATTN_LAUNCH(kCopyNone, kPhaseAll);
+        SKO_ATTN_LAUNCH(kRowsTables, kPhaseAll);
     }
 #undef SKO_ATTN_LAUNCH
+    return hipGetLastError();
+}
+
+// One sequence's rows in slot order (for reading the hot buffer by slot):
+// block s copies row slot_row[s] (lanes: 16-byte chunks).
+__global__ __launch_bounds__(128) void k_gather_slots(const uint4* __restrict__ hot_seq,
+                                                      const int32_t* __restrict__ slot_row_seq, int R,
+                                                      uint4* __restrict__ dst) {
+    const int s = blockIdx.x;
+    const int32_t row = slot_row_seq[s];
+    if (row < 0 || row >= R) return;  // never with intact tables
+    for (int c = threadIdx.x; c < kKvRowU4; c += 128) dst[(size_t)s * kKvRowU4 + c] = hot_seq[(size_t)row * kKvRowU4 + c];
+}
+
+hipError_t launch_gather_slots(hipStream_t st, const uint16_t* hot_seq, const int32_t* slot_row_seq, int S, int R,
+                               uint16_t* dst) {
+    if (S < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_gather_slots, dim3(S), dim3(128), 0, st, reinterpret_cast<const uint4*>(hot_seq),
+                       slot_row_seq, R, reinterpret_cast<uint4*>(dst));
     return hipGetLastError();
 }
 

@@ -191,18 +191,19 @@ __device__ __forceinline__ void thread_run(int64_t n, int align, int64_t* r0, in
 }
 
 // Early miss copy inside the merge launch: blocks past the B merge blocks
-// copy, from the pool into the staging area, the rows of the misses marked
-// in the miss bitmap (the union of the miss-flagged winners of a sequence is
-// its miss set M; a winner's flag is its absence at step start), so the
-// host-link transfer runs while the merge blocks update the LRU state.
-// Copy block j of sequence b takes bitmap words [W j, W j + W): it
-// lists their tokens in LDS and copies each row into staging row r, where r
-// is the token's rank among the sequence's misses in token order (the
-// misses in the words before its own are counted first).  The merge blocks
-// of the same launch compute the same ranks from their sorted miss list, so
-// no block waits for another and no row index is handed over.  The bitmap
-// is left as it is for the other blocks' counts (the attention launch
-// clears the words of the misses).
+// copy, from the pool into the sequence's spare hot rows, the rows of the
+// misses marked in the miss bitmap (the union of the miss-flagged winners of
+// a sequence is its miss set M; a winner's flag is its absence at step
+// start), so the host-link transfer runs while the merge blocks update the
+// LRU state.  Copy block j of sequence b takes bitmap words [W j, W j + W):
+// it lists their tokens in LDS and copies each row into spare row r of the
+// step's generation, where r is the token's rank among the sequence's
+// misses in token order (the misses in the words before its own are counted
+// first).  The merge blocks of the same launch compute the same ranks from
+// their sorted miss list and give the r-th miss's victim slot that spare
+// row, so no block waits for another.  The bitmap is left as it is for the
+// other blocks' counts (the attention launch clears the words of the
+// misses).
 // The launch holds about kCopyBlocks copy blocks in all (each block a run
 // of up to 1024 bitmap words, one per thread): on this link more blocks,
 // i.e. more host reads in flight, lowered the transfer rate (2x the blocks:
@@ -212,9 +213,12 @@ constexpr int kCopyRowsPerWave = 2;
 
 __device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, const uint32_t* __restrict__ miss_bits,
                                            const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
-                                           uint4* __restrict__ stage_rows, const int32_t* __restrict__ ntok_layer,
+                                           uint4* __restrict__ hot_layer, const int32_t* __restrict__ spare_layer,
+                                           int gen, int R, const int32_t* __restrict__ ntok_layer,
                                            int64_t cap, int64_t wpr, int mstride, int32_t* toks, int* scratch) {
     const int b = cb / nper;
+    // this step's spare rows of the sequence (each < R)
+    const int32_t* __restrict__ spare = spare_layer + ((size_t)b * 2 + gen) * mstride;
     const int part = cb - b * nper;
     const int64_t words_now = (ntok_layer[b] + 31) / 32;
     const int32_t newest = ntok_layer[b] - 1;  // its row is read from the device copy
@@ -257,7 +261,9 @@ __device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, con
         for (int r = 0; r < kCopyRowsPerWave; ++r) {
             const int i = i0 + r;
             if (i >= total || base + i >= mstride) break;
-            uint4* dst = stage_rows + ((int64_t)b * mstride + base + i) * kKvRowU4;
+            const int32_t row = spare[base + i];
+            if (row < 0 || row >= R) continue;  // never with intact tables
+            uint4* dst = hot_layer + ((int64_t)b * R + row) * kKvRowU4;
             dst[lane] = a[r];
             if (lane < kKvRowU4 - 64) dst[64 + lane] = t8[r];
         }
@@ -275,7 +281,8 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     int32_t* __restrict__ evict_old, int32_t* __restrict__ counts, GatherEntry* __restrict__ glist,
     unsigned long long* __restrict__ layer_stats, int do_refine, int nseq, int copy_per_seq, int copy_words,
     uint32_t* __restrict__ miss_bits, const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
-    uint4* __restrict__ stage_rows, int2* __restrict__ rdcp, int32_t* __restrict__ phys, int sort_winners,
+    uint4* __restrict__ hot_layer, int32_t* __restrict__ slot_row_layer, int32_t* __restrict__ spare_layer, int R,
+    int32_t* __restrict__ wrow, int32_t* __restrict__ phys, int sort_winners,
     int test_violation, uint64_t* __restrict__ stamps) {
     // instrumentation (stamps != nullptr): each block records when it
     // started and ended on the chip's constant-rate clock, so the host can
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
 
     if ((int)blockIdx.x >= nseq) {
         copy_block((int)blockIdx.x - nseq, copy_per_seq, copy_words, miss_bits, pool_layer, recent_layer,
-                   stage_rows, ntok_layer, cap, wpr, D * top_k, lists, scratch);
+                   hot_layer, spare_layer, t & 1, R, ntok_layer, cap, wpr, D * top_k, lists, scratch);
         if (stamps) {
             __syncthreads();
             if (threadIdx.x == 0) {
@@ -322,6 +329,12 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     int32_t* __restrict__ cnt = counts + (size_t)b * 8;
     const int mstride = D * top_k;
     const int SW = (S + 31) / 32;
+    // physical hot rows: slot s of the sequence lives in row P[s]; the
+    // step's generation of spare rows (rows holding no slot) is Fc, the next
+    // step's is Fn (both < R)
+    int32_t* __restrict__ P = slot_row_layer + (size_t)b * S;
+    const int32_t* __restrict__ Fc = spare_layer + ((size_t)b * 2 + (t & 1)) * mstride;
+    int32_t* __restrict__ Fn = spare_layer + ((size_t)b * 2 + ((t & 1) ^ 1)) * mstride;
 
     // 0. finish the top-k of rows whose threshold bucket is split (unless
     //    k_topk_refine already did)
@@ -481,13 +494,16 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
             if (s >= 0 && s < S) atomicOr(&touched[s >> 5], 1u << (s & 31));
         }
         __syncthreads();
-        // 4. assignment: r-th miss -> r-th victim
+        // 4. assignment: r-th miss -> r-th victim.  The miss's row is spare
+        //    row r of this step (where the copy puts it); the victim's old
+        //    row becomes spare row r of the next step.
         int ev_loc = 0;
         for (int r = tid; r < nM; r += kLruThreads) {
             const int32_t v = vlist[r];
             const int32_t m = mlist[r];
             if (avail < nM || v < 0 || v >= S || m < 0 || m >= cap) {
                 cnt[7] = 1;  // invariant violated; reported in the counts record
+                Fn[r] = Fc[r];
                 continue;
             }
             const int32_t old = st[v];
@@ -498,16 +514,24 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
             cs[m] = v;
             st[v] = m;
             lu[v] = t;
+            const int32_t row = Fc[r];
+            Fn[r] = P[v];
+            P[v] = row;
             misses[(size_t)b * mstride + r] = m;
             victims[(size_t)b * mstride + r] = v;
             evict_old[(size_t)b * mstride + r] = old;
-            glist[(size_t)b * mstride + r] = GatherEntry{(uint32_t)((int64_t)b * cap + m), (uint32_t)((int64_t)b * S + v)};
+            glist[(size_t)b * mstride + r] = GatherEntry{(uint32_t)((int64_t)b * cap + m), (uint32_t)((int64_t)b * R + row)};
         }
         int ev_total;
         (void)block_exclusive_scan<kLruThreads>(ev_loc, &ev_total, scratch);
         nEv = ev_total;
     } else if (nM > 0) {
         if (tid == 0) cnt[7] = 1;
+    }
+    {
+        // spare rows no miss took stay spare
+        const int taken = (nM > 0 && sane) ? std::min(nM, mstride) : 0;
+        for (int r = taken + tid; r < mstride; r += kLruThreads) Fn[r] = Fc[r];
     }
     __syncthreads();
 
@@ -563,26 +587,21 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
         if (tid == 0) ring_state_layer[b] = RingState{head, tail + ntouched, cur, {0, 0, 0}};
     }
 
-    // 7. (early copy) what the attention reads for each winner of this
-    //    sequence: a hit's slot, or for a miss its staging row (its rank r
-    //    in the sorted miss list, the row the copy blocks fill) and, for
-    //    exactly one of the entries holding it, the victim slot it moves
-    //    into; rd = slot (>= 0), -(r + 2) for a staged row, -1 for none.
-    //    With sorted lists the positions are taken in turn, so the entry
-    //    that moves a missed row is the one of its first position.
-    if (rdcp != nullptr) {
+    // 7. the row the attention reads for each winner of this sequence, a
+    //    hit's P[slot] or a miss's spare row (-1: none, only with a broken
+    //    invariant), and the winner's slot in phys
+    if (wrow != nullptr) {
         const bool assigned = nM > 0 && sane && avail >= nM;
-        __syncthreads();  // the ring maintenance above is done with `touched`
-        for (int i = tid; i < (nM + 31) / 32; i += kLruThreads) touched[i] = 0u;
-        __syncthreads();
-        auto emit = [&](size_t at) {
+        for (int e = tid; e < D * kk; e += kLruThreads) {
+            const int p = e / kk;
+            const size_t at = ((size_t)b * D + p) * top_k + (e - p * kk);
             const int32_t packed = topk[at];
             const int32_t tok = packed & 0x7FFFFFFF;
-            int32_t rd = -1, cp = -1, slot = -1;
+            int32_t rd = -1, slot = -1;
             if (packed >= 0) {
                 slot = tok < cap ? cs[tok] : -1;
                 if (slot >= S) slot = -1;
-                rd = slot;
+                rd = slot >= 0 ? P[slot] : -1;
             } else if (assigned) {
                 int lo = 0, hi = nM;
                 while (lo < hi) {
@@ -592,24 +611,11 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
                 }
                 if (lo < nM && mlist[lo] == tok && lo < mstride && vlist[lo] >= 0 && vlist[lo] < S) {
                     slot = vlist[lo];
-                    rd = -(lo + 2);
-                    const uint32_t bit = 1u << (lo & 31);
-                    if (!(atomicOr(&touched[lo >> 5], bit) & bit)) cp = slot;
+                    rd = Fc[lo];
                 }
             }
-            rdcp[at] = make_int2(rd, cp);
+            wrow[at] = (rd >= 0 && rd < R) ? rd : -1;
             phys[at] = slot;
-        };
-        if (sorted_lists) {
-            for (int p = 0; p < D; ++p) {
-                for (int j = tid; j < kk; j += kLruThreads) emit(((size_t)b * D + p) * top_k + j);
-                __syncthreads();  // this position's claims before the next one's
-            }
-        } else {
-            for (int e = tid; e < D * kk; e += kLruThreads) {
-                const int p = e / kk;
-                emit(((size_t)b * D + p) * top_k + (e - p * kk));
-            }
         }
     }
 
@@ -669,7 +675,8 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
                             GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
                             uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
-                            uint16_t* stage_rows, int2* rdcp, int32_t* phys, bool sort_winners,
+                            uint16_t* hot_layer, int32_t* slot_row_layer, int32_t* spare_layer, int R,
+                            int32_t* wrow, int32_t* phys, bool sort_winners,
                             int64_t max_tokens_now, bool test_violation, uint64_t* stamps) {
     const int64_t C = ring_capacity(S, D, top_k);
     const int64_t wpr = winner_words(cap);
@@ -684,8 +691,8 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                        evict_old, counts, glist, layer_stats, do_refine ? 1 : 0, B, copy_per_seq, copy_words,
                        miss_bits,
                        reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<const uint4*>(recent_layer),
-                       reinterpret_cast<uint4*>(stage_rows), miss_bits ? rdcp : nullptr, phys, sort_winners ? 1 : 0,
-                       test_violation ? 1 : 0, stamps);
+                       reinterpret_cast<uint4*>(hot_layer), slot_row_layer, spare_layer, R, wrow, phys,
+                       sort_winners ? 1 : 0, test_violation ? 1 : 0, stamps);
     return hipGetLastError();
 }
 
@@ -837,21 +844,28 @@ hipError_t launch_topk_refine(hipStream_t st, RowMeta* meta, const uint2* cand, 
 }
 
 __global__ void k_init_rings(int32_t* __restrict__ ring0, int32_t* __restrict__ pos,
-                             RingState* __restrict__ state, int64_t n_seqs, int S, int64_t C) {
+                             RingState* __restrict__ state, int32_t* __restrict__ slot_row,
+                             int32_t* __restrict__ spare, int64_t n_seqs, int S, int64_t C, int M) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (int64_t i = i0; i < n_seqs * C; i += stride) {
         const int64_t e = i % C;
         ring0[i] = e < S ? (int32_t)e : -1;
     }
-    for (int64_t i = i0; i < n_seqs * S; i += stride) pos[i] = (int32_t)(i % S);
+    for (int64_t i = i0; i < n_seqs * S; i += stride) {
+        pos[i] = (int32_t)(i % S);
+        slot_row[i] = (int32_t)(i % S);  // slot s in row s
+    }
+    // both generations of spare rows: rows S .. S+M-1
+    for (int64_t i = i0; i < n_seqs * 2 * M; i += stride) spare[i] = S + (int32_t)(i % M);
     for (int64_t i = i0; i < n_seqs; i += stride) state[i] = RingState{0, S, 0, {0, 0, 0}};
 }
 
-hipError_t launch_init_rings(hipStream_t st, int32_t* ring0, int32_t* pos, RingState* state, int64_t n_seqs,
-                             int S, int64_t C) {
+hipError_t launch_init_rings(hipStream_t st, int32_t* ring0, int32_t* pos, RingState* state, int32_t* slot_row,
+                             int32_t* spare, int64_t n_seqs, int S, int64_t C, int M) {
     const int g = (int)std::min<int64_t>((n_seqs * C + 255) / 256, 4096);
-    hipLaunchKernelGGL(k_init_rings, dim3(std::max(g, 1)), dim3(256), 0, st, ring0, pos, state, n_seqs, S, C);
+    hipLaunchKernelGGL(k_init_rings, dim3(std::max(g, 1)), dim3(256), 0, st, ring0, pos, state, slot_row, spare,
+                       n_seqs, S, C, M);
     return hipGetLastError();
 }
 

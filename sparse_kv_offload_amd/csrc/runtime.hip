@@ -108,7 +108,14 @@ struct sko_handle {
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     hipEvent_t ev_switch = nullptr;  // orders the old stream's work before the new one's (sko_set_stream)
     uint16_t* staging = nullptr;    // device rows for host-source appends
-    uint16_t* hot = nullptr;        // [L][B][S][576]
+    // hot rows: [L][B][R][576], R = S + D*k; slot s of (layer, seq) lives in
+    // row slot_row[s], the other D*k rows are spare (two generations of the
+    // spare list, the step's one chosen by the layer's step stamp)
+    uint16_t* hot = nullptr;
+    int R = 0;                      // physical rows per (layer, seq)
+    int M = 0;                      // spare rows per (layer, seq) = D*k
+    int32_t* slot_row = nullptr;    // [L][B][S]
+    int32_t* spare_rows = nullptr;  // [L][B][2][M]
     uint16_t* recent = nullptr;     // [L][B][576] device copy of each sequence's newest main-KV row
     int32_t* cache_slots = nullptr; // [L][B][cap]
     int32_t* slot_token = nullptr;  // [L][B][S]
@@ -128,10 +135,9 @@ struct sko_handle {
     // blocks of the merge launch move the misses into staging while the
     // merge blocks update the LRU state
     bool fused_copy = false;        // the attention launch copies the misses
-    bool staged_copy = false;       // early copy into staging
+    bool staged_copy = false;       // early copy (copy blocks in the LRU-update launch)
     uint32_t* miss_bits = nullptr;  // [B][wpr]
-    uint16_t* stage_rows = nullptr; // [B][D*k][576] miss rows copied early (inside the hot allocation)
-    int2* rdcp = nullptr;           // [B][D][k]: per winner, the row the attention reads and the slot a missed row moves into
+    int32_t* wrow = nullptr;        // [B][D][k]: per winner, the row the attention reads (not with the fused copy)
     int32_t* floor = nullptr;       // [L][B][D] candidate floor (first-digit bin)
     uint32_t* hist = nullptr;       // [B][D][4096]
     RowMeta* meta = nullptr;        // [B][D]
@@ -354,10 +360,11 @@ int validate_config(const sko_config* c) {
         return set_err(SKO_E_UNSUPPORTED, "mtp_positions*top_k above %d", SKO_MAX_MERGE);
     if ((int64_t)c->batch * c->max_tokens >= 0xFFFFFFFFLL || (int64_t)c->batch * c->hot_slots >= 0xFFFFFFFFLL)
         return set_err(SKO_E_UNSUPPORTED, "batch*max_tokens and batch*hot_slots must stay below 2^32");
-    // hot rows of every layer plus the staging rows are addressed by int32 row numbers
-    if ((int64_t)c->num_layers * c->batch * c->hot_slots + (int64_t)c->batch * c->mtp_positions * c->top_k >=
+    // the hot rows of every layer (S slot rows and D*k spare rows per
+    // sequence) are addressed by int32 row numbers
+    if ((int64_t)c->num_layers * c->batch * ((int64_t)c->hot_slots + (int64_t)c->mtp_positions * c->top_k) >=
         0x7FFFFFFFLL)
-        return set_err(SKO_E_UNSUPPORTED, "num_layers*batch*hot_slots must stay below 2^31");
+        return set_err(SKO_E_UNSUPPORTED, "num_layers*batch*(hot_slots + mtp_positions*top_k) must stay below 2^31");
     return SKO_OK;
 }
 
@@ -391,7 +398,7 @@ struct StepScratch {
     RowMeta* meta = nullptr;        // [B][D]
     uint32_t* winners = nullptr;    // [B][wpr]
     uint32_t* miss_bits = nullptr;  // [B][wpr] (early copy)
-    int2* rdcp = nullptr;           // [B][D][k] (early copy)
+    int32_t* wrow = nullptr;        // [B][D][k] (early or late copy)
     GatherEntry* glist = nullptr;   // [B*D*k]
     float* part_acc = nullptr;      // [B*D][HG][nchunk][16][512]
     float* part_ml = nullptr;       // [B*D][HG][nchunk][16][2]
@@ -419,11 +426,14 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
     const int32_t t = h->step[layer];
     const size_t LBc = (size_t)layer * B * cap;
     const size_t LBs = (size_t)layer * B * S;
+    const int R = h->R;
     const void* idx_layer = reinterpret_cast<const uint8_t*>(h->idx) + (size_t)layer * B * h->idx_seq_bytes();
     const uint16_t* scale_layer = h->c8 ? h->idx_scale + (size_t)layer * B * h->ntiles * kIdxTile : nullptr;
     const uint16_t* pool_layer = h->pool_dev + LBc * kKvDim;
     const uint16_t* recent_layer = h->recent + (size_t)layer * B * kKvDim;
-    uint16_t* hot_layer = h->hot + LBs * kKvDim;
+    uint16_t* hot_layer = h->hot + (size_t)layer * B * R * kKvDim;
+    int32_t* slot_row_layer = h->slot_row + LBs;
+    int32_t* spare_layer = h->spare_rows + (size_t)layer * B * 2 * h->M;
     int32_t* cs = h->cache_slots + LBc;
     int32_t* st = h->slot_token + LBs;
     int32_t* lu = h->last_use + LBs;
@@ -486,14 +496,15 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
              return launch_merge_lru(h->stream, sc.winners, sc.hist, sc.meta, sc.cand, h->topk, ntok, cs, st, lu,
                                      ring0, ring1, ring_pos, ring_state, B, D, k, S, cap, t, h->misses, h->victims,
                                      h->evict_old, h->counts, sc.glist, h->stats + (size_t)layer * 8, !staged,
-                                     staged ? sc.miss_bits : nullptr, pool_layer, recent_layer, h->stage_rows,
-                                     staged ? sc.rdcp : nullptr, h->phys,
+                                     staged ? sc.miss_bits : nullptr, pool_layer, recent_layer, hot_layer,
+                                     slot_row_layer, spare_layer, R, fused_copy ? nullptr : sc.wrow, h->phys,
                                      /* the split attention reads the lists during this launch */ !h->hit_overlap,
                                      max_now, (h->cfg.flags & SKO_FLAG_TEST_VIOLATION) != 0, stamps);
          })))
         return rc;
-    // late copy: its own gather from the pool; fused or early: the attention
-    // launch puts the missed rows into their slots itself
+    // late copy: its own gather from the pool into the misses' rows; early:
+    // the copy blocks of the LRU-update launch did it; fused: the attention
+    // launch copies them itself
     if (!fused_copy && !staged && (rc = run_stage(h, ST_GATHER, [&] {
              return launch_gather_misses(h->stream, sc.glist, h->counts, pool_layer, recent_layer, ntok, hot_layer,
                                          B, cap, D * k, B * D * k);
@@ -503,10 +514,9 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
         if ((rc = run_stage(
                  h, ST_ATTN_HITS,
                  [&] {
-                     return launch_attn_partial(h->side, h->topk, cs, hot_layer, qa, nullptr, recent_layer, ntok,
-                                                sc.part_acc, sc.part_ml, h->phys, B, D, H, k, S, cap,
-                                                h->rows_per_block, h->cfg.attn_scale, h->stage_rows, nullptr,
-                                                nullptr, 1);
+                     return launch_attn_partial(h->side, h->topk, cs, slot_row_layer, hot_layer, R, qa, nullptr,
+                                                recent_layer, ntok, sc.part_acc, sc.part_ml, h->phys, B, D, H, k,
+                                                S, cap, h->rows_per_block, h->cfg.attn_scale, nullptr, nullptr, 1);
                  },
                  h->side)))
             return rc;
@@ -514,11 +524,11 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
         if (e != hipSuccess) return device_fail(h, e, "join of the hit attention");
     }
     if ((rc = run_stage(h, ST_ATTN, [&] {
-             return launch_attn_partial(h->stream, h->topk, cs, hot_layer, qa, fused_copy ? pool_layer : nullptr,
-                                        recent_layer, ntok, sc.part_acc, sc.part_ml, h->phys, B, D, H, k, S, cap,
-                                        h->rows_per_block, h->cfg.attn_scale, staged ? h->stage_rows : nullptr,
-                                        staged ? sc.rdcp : nullptr, staged ? sc.miss_bits : nullptr,
-                                        split ? 2 : 0);
+             return launch_attn_partial(h->stream, h->topk, cs, slot_row_layer, hot_layer, R, qa,
+                                        fused_copy ? pool_layer : nullptr, recent_layer, ntok, sc.part_acc,
+                                        sc.part_ml, h->phys, B, D, H, k, S, cap, h->rows_per_block,
+                                        h->cfg.attn_scale, fused_copy ? nullptr : sc.wrow,
+                                        staged ? sc.miss_bits : nullptr, split ? 2 : 0);
          })))
         return rc;
     if (split) {
@@ -585,7 +595,7 @@ size_t layout_step_scratch(const sko_handle* h, unsigned char* base, StepScratch
     sc->winners = reinterpret_cast<uint32_t*>(take((size_t)h->B * h->wpr * 4));
     sc->miss_bits = h->staged_copy ? reinterpret_cast<uint32_t*>(take((size_t)h->B * h->wpr * 4)) : nullptr;
     *zero_bytes = off;
-    sc->rdcp = h->staged_copy ? reinterpret_cast<int2*>(take(BD * h->k * sizeof(int2))) : nullptr;
+    sc->wrow = h->fused_copy ? nullptr : reinterpret_cast<int32_t*>(take(BD * h->k * 4));
     sc->pre = reinterpret_cast<uint2*>(take(BD * h->cap * sizeof(uint2)));
     sc->cand = reinterpret_cast<uint2*>(take(BD * h->cap * sizeof(uint2)));
     sc->glist = reinterpret_cast<GatherEntry*>(take(BD * h->k * sizeof(GatherEntry)));
@@ -645,6 +655,8 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     h->ntiles = (h->cap + kIdxTile - 1) / kIdxTile;
     h->kcap = (h->cap + 15) / 16 * 16;
     h->C = ring_capacity(h->S, h->D, h->k);
+    h->M = h->D * h->k;
+    h->R = h->S + h->M;
     h->wpr = winner_words(h->cap);
     h->ntok.assign((size_t)h->L * h->B, 0);
     h->step.assign((size_t)h->L, 0);
@@ -653,8 +665,6 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
         if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, cfg->device) == hipSuccess && ncu > 0)
             h->cu_count = ncu;
     }
-    h->rows_per_block = attn_rows_per_block(h->k, h->B * h->D * h->HG);
-    h->nchunk = (h->k + h->rows_per_block - 1) / h->rows_per_block;
     // Early copy by default: extra blocks of the LRU-update launch read the
     // misses into staging while the update runs, so neither the update nor
     // the attention waits on the host link (measured against copying inside
@@ -664,6 +674,8 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     h->staged_copy = !h->fused_copy && !(cfg->flags & SKO_FLAG_LATE_COPY);
     h->c8 = (cfg->flags & SKO_FLAG_INDEXER_C8) != 0;
     h->hit_overlap = h->staged_copy && (cfg->flags & SKO_FLAG_HIT_OVERLAP) != 0;
+    h->rows_per_block = attn_rows_per_block(h->k, h->B * h->D * h->HG);
+    h->nchunk = (h->k + h->rows_per_block - 1) / h->rows_per_block;
     // the split attention writes the partials of both phases
     const size_t pchunks = (size_t)h->nchunk * (h->hit_overlap ? 2 : 1);
 
@@ -693,11 +705,11 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
         ok = ok && dev_alloc(h, (void**)&h->qc8, (size_t)h->B * h->D * kQc8Words * 4);
     }
     ok = ok && dev_alloc(h, (void**)&h->staging, (size_t)kStagingRows * kIdxDim * 2);
-    // the staging rows of the early copy follow the hot rows of every layer
-    // in one allocation (the attention addresses both from one base)
-    const size_t stage_rows_n = h->staged_copy ? BD * h->k : 0;
-    ok = ok && dev_alloc(h, (void**)&h->hot, (LB * h->S + stage_rows_n) * (size_t)kKvRowBytes);
-    if (ok && h->staged_copy) h->stage_rows = h->hot + LB * h->S * kKvDim;
+    // the hot rows of every (layer, seq): its S slots' rows and D*k spare
+    // rows, which take the misses of a step
+    ok = ok && dev_alloc(h, (void**)&h->hot, LB * h->R * (size_t)kKvRowBytes);
+    ok = ok && dev_alloc(h, (void**)&h->slot_row, LB * h->S * 4);
+    ok = ok && dev_alloc(h, (void**)&h->spare_rows, LB * 2 * h->M * 4);
     ok = ok && dev_alloc(h, (void**)&h->recent, LB * (size_t)kKvRowBytes);
     ok = ok && dev_alloc(h, (void**)&h->cache_slots, LB * h->cap * 4);
     ok = ok && dev_alloc(h, (void**)&h->slot_token, LB * h->S * 4);
@@ -711,10 +723,8 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     if (cfg->flags & SKO_FLAG_KEEP_KEYS) ok = ok && dev_alloc(h, (void**)&h->keys, BD * h->kcap * 4);
     ok = ok && dev_alloc(h, (void**)&h->pre, BD * h->cap * sizeof(uint2));
     ok = ok && dev_alloc(h, (void**)&h->floor, LB * h->D * 4);
-    if (h->staged_copy) {
-        ok = ok && dev_alloc(h, (void**)&h->miss_bits, (size_t)h->B * h->wpr * 4);
-        ok = ok && dev_alloc(h, (void**)&h->rdcp, BD * h->k * sizeof(int2));
-    }
+    if (h->staged_copy) ok = ok && dev_alloc(h, (void**)&h->miss_bits, (size_t)h->B * h->wpr * 4);
+    if (!h->fused_copy) ok = ok && dev_alloc(h, (void**)&h->wrow, BD * h->k * 4);
     ok = ok && dev_alloc(h, (void**)&h->winners, (size_t)h->B * h->wpr * 4);
     ok = ok && dev_alloc(h, (void**)&h->hist, BD * kHistBins * 4);
     ok = ok && dev_alloc(h, (void**)&h->meta, BD * sizeof(RowMeta));
@@ -766,7 +776,7 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     if (e == hipSuccess) e = hipMemsetAsync(h->slot_token, 0xFF, LB * h->S * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->last_use, 0xFF, LB * h->S * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->ntok_dev, 0, LB * 4, h->stream);
-    if (e == hipSuccess) e = hipMemsetAsync(h->hot, 0, LB * h->S * (size_t)kKvRowBytes, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->hot, 0, LB * h->R * (size_t)kKvRowBytes, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->stats, 0, (size_t)h->L * 8 * 8, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->topk, 0, BD * h->k * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->counts, 0, (size_t)h->B * 8 * 4, h->stream);
@@ -775,7 +785,7 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     if (e == hipSuccess) e = hipMemsetAsync(h->hist, 0, BD * kHistBins * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->meta, 0, BD * sizeof(RowMeta), h->stream);
     if (e == hipSuccess && h->staged_copy) e = hipMemsetAsync(h->miss_bits, 0, (size_t)h->B * h->wpr * 4, h->stream);
-    if (e == hipSuccess && h->staged_copy) e = hipMemsetAsync(h->rdcp, 0xFF, BD * h->k * sizeof(int2), h->stream);
+    if (e == hipSuccess && h->wrow) e = hipMemsetAsync(h->wrow, 0xFF, BD * h->k * 4, h->stream);
     if (e == hipSuccess) {
         // first step: every key is a candidate (or none, to force the rescan path)
         const std::vector<int32_t> fl(LB * h->D, (cfg->flags & SKO_FLAG_SELECT_RESCAN) ? kFloorRescanAll : 0);
@@ -785,7 +795,8 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     if (e == hipSuccess) e = hipMemsetAsync(h->idx, 0, LB * h->idx_seq_bytes(), h->stream);
     if (e == hipSuccess && h->c8) e = hipMemsetAsync(h->idx_scale, 0, LB * h->ntiles * kIdxTile * 2, h->stream);
     if (e == hipSuccess && h->c8) e = hipMemsetAsync(h->qc8, 0, (size_t)h->B * h->D * kQc8Words * 4, h->stream);
-    if (e == hipSuccess) e = launch_init_rings(h->stream, h->ring[0], h->ring_pos, h->ring_state, (int64_t)LB, h->S, h->C);
+    if (e == hipSuccess) e = launch_init_rings(h->stream, h->ring[0], h->ring_pos, h->ring_state, h->slot_row, h->spare_rows,
+                                                   (int64_t)LB, h->S, h->C, h->M);
     if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
     if (e != hipSuccess) {
         set_err(SKO_E_DEVICE, "initialising state: %s", hipGetErrorString(e));
@@ -906,7 +917,7 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
     sc.meta = h->meta;
     sc.winners = h->winners;
     sc.miss_bits = h->miss_bits;
-    sc.rdcp = h->rdcp;
+    sc.wrow = h->wrow;
     sc.glist = h->glist;
     sc.part_acc = h->part_acc;
     sc.part_ml = h->part_ml;
@@ -935,10 +946,10 @@ int sko_decode_step_static(sko_handle* h, int32_t layer, const void* q_idx, cons
     // the area keeps the last call's contents (any handle's): clear what the
     // step expects to start cleared
     const int64_t nz = (int64_t)(zero_bytes / 4);
-    const int64_t nf = sc.rdcp ? (int64_t)((size_t)h->B * h->D * h->k * sizeof(int2) / 4) : 0;
+    const int64_t nf = sc.wrow ? (int64_t)((size_t)h->B * h->D * h->k) : 0;
     const int64_t blocks = std::min<int64_t>(1024, std::max<int64_t>(1, (nz + nf + 255) / 256));
     hipLaunchKernelGGL(k_clear_scratch, dim3((unsigned)blocks), dim3(256), 0, h->stream,
-                       reinterpret_cast<uint32_t*>(base), nz, reinterpret_cast<uint32_t*>(sc.rdcp), nf);
+                       reinterpret_cast<uint32_t*>(base), nz, reinterpret_cast<uint32_t*>(sc.wrow), nf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return device_fail(h, e, "clearing the static scratch");
     // no stage timing here: its events are created on demand
@@ -997,7 +1008,7 @@ int sko_read_table(sko_handle* h, int32_t layer, int32_t seq, int32_t which, voi
         case SKO_TAB_CACHE_SLOTS: src = h->cache_slots + lb * h->cap; size = (size_t)h->cap * 4; break;
         case SKO_TAB_SLOT_TOKEN: src = h->slot_token + lb * h->S; size = (size_t)h->S * 4; break;
         case SKO_TAB_LAST_USE: src = h->last_use + lb * h->S; size = (size_t)h->S * 4; break;
-        case SKO_TAB_HOT: src = h->hot + lb * h->S * kKvDim; size = (size_t)h->S * kKvRowBytes; break;
+        case SKO_TAB_HOT: src = h->hot + lb * h->R * kKvDim; size = (size_t)h->S * kKvRowBytes; break;
         case SKO_TAB_INDEXER:
             src = reinterpret_cast<const uint8_t*>(h->idx) + lb * h->idx_seq_bytes();
             size = (size_t)h->cap * (h->c8 ? kIdxDim : kIdxDim * 2);
@@ -1009,6 +1020,12 @@ int sko_read_table(sko_handle* h, int32_t layer, int32_t seq, int32_t which, voi
             break;
         case SKO_TAB_POOL: src = h->pool_host + lb * h->cap * kKvDim; size = (size_t)h->cap * kKvRowBytes; host = true; break;
         case SKO_TAB_NTOK: size = 8; break;
+        case SKO_TAB_SLOT_ROW: src = h->slot_row + lb * h->S; size = (size_t)h->S * 4; break;
+        case SKO_TAB_SPARE_ROWS:
+            // the generation the layer's next step (stamp step[layer]) uses
+            src = h->spare_rows + (lb * 2 + (h->step[layer] & 1)) * h->M;
+            size = (size_t)h->M * 4;
+            break;
         default: return set_err(SKO_E_INVAL, "unknown table %d", which);
     }
     if ((size_t)bytes != size) return set_err(SKO_E_INVAL, "table %d holds %zu bytes, got %lld", which, size, (long long)bytes);
@@ -1029,6 +1046,20 @@ int sko_read_table(sko_handle* h, int32_t layer, int32_t seq, int32_t which, voi
         for (int64_t tok = 0; tok < h->cap; ++tok)
             for (int c = 0; c < ru; ++c)
                 o[tok * ru + c] = tiles[h->c8 ? idx_c8_tile_u4(0, tok, c) : idx_tile_u4(0, tok, c)];
+    } else if (which == SKO_TAB_HOT) {
+        // the slots' rows in slot order (slot s lives in row slot_row[s])
+        void* tmp = nullptr;
+        e = hipMalloc(&tmp, size);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return set_err(SKO_E_NOMEM, "read table: %zu bytes of device memory", size);
+        }
+        e = launch_gather_slots(h->stream, static_cast<const uint16_t*>(src), h->slot_row + lb * h->S, h->S, h->R,
+                                static_cast<uint16_t*>(tmp));
+        if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+        if (e == hipSuccess) e = hipMemcpy(dst, tmp, size, hipMemcpyDeviceToHost);
+        (void)hipFree(tmp);
+        if (e != hipSuccess) return device_fail(h, e, "read table");
     } else if (host) {
         std::memcpy(dst, src, size);
     } else {

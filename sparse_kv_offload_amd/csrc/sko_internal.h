@@ -131,24 +131,30 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int32_t* misses, int32_t* victims, int32_t* evict_old, int32_t* counts,
                             GatherEntry* glist, unsigned long long* layer_stats, bool do_refine,
                             uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
-                            uint16_t* stage_rows, int2* rdcp, int32_t* phys, bool sort_winners,
+                            uint16_t* hot_layer, int32_t* slot_row_layer, int32_t* spare_layer, int R,
+                            int32_t* wrow, int32_t* phys, bool sort_winners,
                             int64_t max_tokens_now, bool test_violation, uint64_t* stamps);
 // Copy blocks of the early copy: copy_per_seq per sequence, each owning
 // copy_words bitmap words (a multiple of 4, at most 1024).
 void copy_shape(int B, int64_t max_tokens_now, int* copy_per_seq, int* copy_words);
-// (miss_bits non-null: the launch also holds copy blocks that move the rows
-// marked in miss_bits [B][wpr] from the pool into stage_rows [B][D*k][576],
-// the r-th miss of a sequence in token order into its row r, and the merge
-// blocks write rdcp and phys [B][D][k] for the attention: per winner, the
-// row to read (slot >= 0, -(r + 2) for staged row r, -1 for none) and for
-// one entry of each miss the victim slot to move it into (else -1); the
-// early miss copy, overlapping the LRU update.  The bits stay set; the
-// attention launch clears them.)  In every copy the newest token's row
-// comes from recent_layer [B][576] instead of the pool.  With sort_winners
-// (and at most 16 positions) the merge blocks first rewrite each
-// position's top-k list in token order, in every copy arrangement.
-// Late copy from the pool into the slots.  Work list: sequence b's entries
-// are glist[b * D*k + r], r < counts[b][2].
+// Physical hot rows: each (layer, seq) has R = S + D*k rows; slot s lives
+// in row slot_row[s], and the other D*k rows are spare, listed in
+// spare [2][D*k] (two generations, the step's one chosen by t & 1).  The
+// r-th miss of a step (in token order) is copied into spare row r of the
+// step's generation, and the merge blocks give the r-th victim slot that
+// row; the victim's old row becomes spare row r of the next generation.
+// (miss_bits non-null: the launch also holds copy blocks that copy the rows
+// marked in miss_bits [B][wpr] from the pool into those spare rows while the
+// merge blocks update the LRU state; the bits stay set, the attention launch
+// clears them.)  wrow non-null: the merge blocks write, per winner, the row
+// the attention reads (-1: none) into wrow [B][D][k], and its slot into
+// phys.  In every copy the newest token's row comes from recent_layer
+// [B][576] instead of the pool.  With sort_winners (and at most 16
+// positions) the merge blocks first rewrite each position's top-k list in
+// token order, in every copy arrangement.
+// Late copy from the pool into the misses' rows.  Work list: sequence b's
+// entries are glist[b * D*k + r], r < counts[b][2] (destinations are row
+// numbers from hot_layer).
 hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const int32_t* counts,
                                 const uint16_t* pool_layer, const uint16_t* recent_layer,
                                 const int32_t* ntok_layer, uint16_t* hot_layer, int B, int64_t cap, int mstride,
@@ -157,24 +163,29 @@ hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const 
 // so that the miss bitmap is complete before the merge launch).
 hipError_t launch_topk_refine(hipStream_t st, RowMeta* meta, const uint2* cand, int32_t* topk, uint32_t* winners,
                               uint32_t* miss_bits, int B, int D, int top_k, int64_t cap);
-// pool_layer non-null: the launch also copies the rows that missed (packed
-// topk entries < 0) from the pool into their slots; only valid when each
-// row is read by one block (one position, at most 16 heads).  stage_rows
-// non-null instead (it must lie in the allocation of hot_layer, at a row
-// boundary after it): the rows and moves come from rdcp (written by the
-// LRU-update launch), staged rows are moved into their victim slots, and
-// the misses' words of miss_bits [B][wpr] are cleared.
+// The row each winner's attention reads: wrow non-null, the list the
+// LRU-update launch wrote (the misses' words of miss_bits [B][wpr] are then
+// cleared for the next step when miss_bits is non-null); otherwise
+// slot_row[cache_slots[token]] (and with pool_layer non-null the launch
+// also copies the rows that missed, packed topk entries < 0, from the pool
+// into their rows; only valid when each row is read by one block: one
+// position, at most 16 heads).  phase 1 attends only the rows resident at
+// step start (tables), phase 2 only the misses (wrow).
 hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_t* cache_slots_layer,
-                               uint16_t* hot_layer, const uint16_t* q_attn, const uint16_t* pool_layer,
-                               const uint16_t* recent_layer, const int32_t* ntok_layer, float* part_acc,
-                               float* part_ml,
-                               int32_t* phys, int B, int D, int H, int top_k, int S, int64_t cap,
-                               int rows_per_block, float scale, const uint16_t* stage_rows,
-                               const int2* rdcp, uint32_t* miss_bits, int phase);
+                               const int32_t* slot_row_layer, uint16_t* hot_layer, int R, const uint16_t* q_attn,
+                               const uint16_t* pool_layer, const uint16_t* recent_layer, const int32_t* ntok_layer,
+                               float* part_acc, float* part_ml, int32_t* phys, int B, int D, int H, int top_k, int S,
+                               int64_t cap, int rows_per_block, float scale, const int32_t* wrow,
+                               uint32_t* miss_bits, int phase);
 hipError_t launch_attn_combine(hipStream_t st, const float* part_acc, const float* part_ml,
                                float* out, int B, int D, int H, int nchunk);
-// Rings of n_seqs sequences: ring0 = 0..S-1, pos = identity, head 0, tail S.
-hipError_t launch_init_rings(hipStream_t st, int32_t* ring0, int32_t* pos, RingState* state, int64_t n_seqs,
-                             int S, int64_t C);
+// Rings of n_seqs sequences: ring0 = 0..S-1, pos = identity, head 0, tail S;
+// slot_row = identity, both spare generations S .. S+M-1.
+hipError_t launch_init_rings(hipStream_t st, int32_t* ring0, int32_t* pos, RingState* state, int32_t* slot_row,
+                             int32_t* spare, int64_t n_seqs, int S, int64_t C, int M);
+// Rows slot_row[0 .. S) of one sequence's hot rows, in slot order, into dst
+// [S][576] (device).
+hipError_t launch_gather_slots(hipStream_t st, const uint16_t* hot_seq, const int32_t* slot_row_seq, int S, int R,
+                               uint16_t* dst);
 
 }  // namespace sko

@@ -120,6 +120,11 @@ class GpuSide:
              "slot_token": self.h.table(layer, seq, sko.SKO_TAB_SLOT_TOKEN),
              "last_use": self.h.table(layer, seq, sko.SKO_TAB_LAST_USE),
              "hot": self.h.table(layer, seq, sko.SKO_TAB_HOT)}
+        # the device rows: each slot in its own row, the rest spare
+        rows = np.concatenate([self.h.table(layer, seq, sko.SKO_TAB_SLOT_ROW),
+                               self.h.table(layer, seq, sko.SKO_TAB_SPARE_ROWS)])
+        assert np.array_equal(np.sort(rows), np.arange(rows.size)), \
+            f"layer {layer} seq {seq}: slot and spare rows are not a permutation of the device rows"
         if self.h.cfg.flags & sko.SKO_FLAG_INDEXER_C8:
             t["idx_codes"] = self.h.table(layer, seq, sko.SKO_TAB_INDEXER)
             t["idx_scales"] = self.h.table(layer, seq, sko.SKO_TAB_INDEXER_SCALE)

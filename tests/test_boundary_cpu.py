@@ -70,8 +70,8 @@ def test_create_rejects_unsupported_merge_width():
 
 
 def test_create_rejects_hot_rows_beyond_int32():
-    """Hot rows of every layer plus the staging rows are addressed by int32
-    row numbers: 2^14 layers x 2^9 sequences x 2^8 slots is refused."""
+    """Hot rows of every layer (slot rows plus spare rows) are addressed by
+    int32 row numbers: 2^14 layers x 2^9 sequences x 2^8 slots is refused."""
     import sparse_kv_offload_amd as sko
     with pytest.raises(sko.SkoError) as e:
         sko.sko_create(good_cfg(sko, num_layers=1 << 14, batch=1 << 9, hot_slots=1 << 8))

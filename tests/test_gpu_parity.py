@@ -166,7 +166,7 @@ def test_empty_sequence_gives_zero_output():
 
 def test_early_copy_with_empty_first_sequence():
     """Early copy while sequence 0 holds no tokens (its attention blocks have
-    no rows): the per-step staging state must still be reset, so over
+    no rows): the per-step copy state must still be reset, so over
     several steps with new misses the results equal the late copy's
     (selection and hot-buffer rows bit for bit)."""
     import torch
@@ -290,7 +290,7 @@ def test_keys_need_keep_flag():
 
 @pytest.mark.parametrize("mode", ["early", "fused", "late"])
 def test_copy_modes_one_position(mode):
-    """One position, 16 heads: the early copy (staging, the default), the
+    """One position, 16 heads: the early copy (the default), the
     copy inside the attention launch and the late copy all give the oracle's
     results, hot-buffer bytes included."""
     import sparse_kv_offload_amd as sko
@@ -303,9 +303,8 @@ def test_copy_modes_one_position(mode):
 @pytest.mark.parametrize("mode", ["late", "early"])
 def test_copy_modes_positions_and_head_groups(mode):
     """Two positions and two head groups: a missed row is read by several
-    attention blocks.  Late copy, and early copy (forced by its flag), where
-    the blocks read the staging row and exactly one of them moves it into
-    its slot."""
+    attention blocks.  Late copy, and early copy (forced by its flag): the
+    blocks read the one row the copy wrote."""
     import sparse_kv_offload_amd as sko
     w = case(mode, batch=3, context=9000, steps=6, top_k=256, hot_slots=600, positions=2, heads=20)
     log(f"case {mode} D=2 H=20")
