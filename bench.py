@@ -519,6 +519,13 @@ def main() -> int:
 
     h2d_ceiling = measure_h2d_ceiling(torch)
     zero_copy = sko.sko_link_read_rate(0, 1 << 30, 3)
+    # the attention's access pattern (random whole rows, cold) at this
+    # workload's shape, B*D lists of k rows, each list over its own region
+    # of up to 4k rows: the practical HBM ceiling of the attention
+    gather_rows = min(k, w.context) // 128 * 128
+    gather_slots = max(gather_rows, min(w.hot_slots, 4 * gather_rows))
+    gather_ceiling = sko.sko_hbm_gather_rate(0, B * D, gather_slots, gather_rows, 2) \
+        if gather_rows >= 128 and B * D * gather_slots <= (1 << 22) else None
     hbm_copy = measure_hbm_copy(torch)
     calibration_copy(torch)
 
@@ -532,6 +539,9 @@ def main() -> int:
         if bound == "host-link":
             e["measured_ceiling"] = round(h2d_ceiling, 2)
             e["frac_of_measured"] = round(ach / h2d_ceiling, 4)
+        elif name == "attn_partial" and gather_ceiling:
+            e["measured_ceiling"] = round(gather_ceiling, 1)
+            e["frac_of_measured"] = round(ach / gather_ceiling, 4)
         return e
 
     rooflines = {}
@@ -577,6 +587,8 @@ def main() -> int:
         "h2d_ceiling_GBps": round(h2d_ceiling, 2),
         # a streaming kernel reading contiguous pinned host memory
         "zero_copy_read_GBps": round(zero_copy, 2),
+        # random whole-row gathers from HBM (the attention's access pattern)
+        "hbm_row_gather_GBps": round(gather_ceiling, 1) if gather_ceiling else None,
         "hbm_copy_GBps": round(hbm_copy, 1),
         # the first step finds an empty shelf (every winner a miss); it is
         # not in `value`

@@ -38,7 +38,8 @@
  *  - All device work is enqueued on the stream given at create (or set by
  *    sko_set_stream), in call order (SKO_FLAG_HIT_OVERLAP also uses an
  *    internal stream, forked from and joined back into that stream within
- *    each decode step).  sko_link_read_rate is independent of any handle.
+ *    each decode step).  sko_link_read_rate and sko_hbm_gather_rate are
+ *    independent of any handle.
  */
 #ifndef SKO_H
 #define SKO_H
@@ -364,6 +365,24 @@ int32_t sko_num_stages(void);
  * multiple of 16, reps < 1), SKO_E_NOMEM, SKO_E_DEVICE.
  */
 int sko_link_read_rate(int32_t device, int64_t bytes, int32_t reps, float* gbps);
+
+/*
+ * sko_hbm_gather_rate — the HBM read rate of the attention's access pattern:
+ * whole 1152-byte rows at random distinct slots of `seqs` sequences of
+ * `slots` rows each, `rows_per_seq` rows per sequence, gathered by blocks of
+ * 128 rows one 32-row tile at a time (the attention reads the selected rows
+ * of the hot buffer this way, [LSO] §4 "Decode step" item 7).  Eight copies
+ * of the rows are read in rotation, so a launch finds little of its rows in
+ * the on-die caches; *gbps receives the average over reps x 8 timed
+ * launches (1e9 bytes/s).  Allocates 8 x seqs x slots x 1152 bytes of device
+ * memory, uses and frees it on `device`; synchronous; independent of any
+ * handle.
+ * Errors: SKO_E_INVAL (NULL gbps, device < 0, seqs < 1, rows_per_seq not a
+ * positive multiple of 128, slots < rows_per_seq, seqs*slots or
+ * seqs*rows_per_seq above 2^22, reps < 1), SKO_E_NOMEM, SKO_E_DEVICE.
+ */
+int sko_hbm_gather_rate(int32_t device, int32_t seqs, int32_t slots, int32_t rows_per_seq, int32_t reps,
+                        float* gbps);
 
 /* Destroy: synchronize the stream, free everything. NULL is a no-op. */
 void sko_destroy(sko_handle* h);

@@ -113,3 +113,13 @@ def test_link_read_rate_rejects_bad_arguments(args):
     with pytest.raises(sko.SkoError) as e:
         sko.sko_link_read_rate(*args)
     assert e.value.code == sko.SKO_E_INVAL
+
+
+@pytest.mark.parametrize("args", [(-1, 32, 8192, 2048, 1), (0, 0, 8192, 2048, 1), (0, 32, 8192, 100, 1),
+                                  (0, 32, 1000, 2048, 1), (0, 32, 8192, 2048, 0), (0, 1024, 8192, 2048, 1)])
+def test_hbm_gather_rate_rejects_bad_arguments(args):
+    """Argument checks come before any device work (so they run without a GPU)."""
+    import sparse_kv_offload_amd as sko
+    with pytest.raises(sko.SkoError) as e:
+        sko.sko_hbm_gather_rate(*args)
+    assert e.value.code == sko.SKO_E_INVAL

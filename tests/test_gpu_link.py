@@ -1,6 +1,7 @@
-"""The host-link read probe on the GPU: a plausible rate for a PCIe 5.0 x16
-link (above 1 GB/s, below the link's 64 GB/s per direction plus a margin),
-and the bulk-copy comparison the benchmark reports beside it."""
+"""The bandwidth probes on the GPU: a plausible host-link read rate for a
+PCIe 5.0 x16 link (above 1 GB/s, below the link's 64 GB/s per direction plus
+a margin), and a plausible HBM rate for random whole-row gathers (above
+0.5 TB/s, below the 8 TB/s HBM3E peak plus a margin)."""
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -19,3 +20,10 @@ def test_link_read_rate_is_plausible():
     rate = sko.sko_link_read_rate(0, 256 << 20, 1)
     print(f"zero-copy read {rate:.1f} GB/s", flush=True)
     assert 1.0 < rate < 80.0
+
+
+def test_hbm_gather_rate_is_plausible():
+    import sparse_kv_offload_amd as sko
+    rate = sko.sko_hbm_gather_rate(0, 8, 4096, 1024, 1)
+    print(f"row gather {rate:.0f} GB/s", flush=True)
+    assert 500.0 < rate < 9000.0
