@@ -371,15 +371,17 @@ int validate_config(const sko_config* c) {
 int attn_rows_per_block(int k, int rows_total_pairs) {
     // Two 32-row tiles per block (a block overlaps one tile's load with the
     // other's compute, and the split-K partials, as large as 32 rows at 16
-    // heads, are halved), doubled while the launch would hold more than one
-    // round of blocks (two per CU at this kernel's occupancy).  Tiny launches
-    // keep single tiles to have more blocks.  Measured against a floor of
-    // 1024 blocks: small 4 880 -> 4 970, shelf 2 612 -> 2 670, long 4 190 ->
-    // 4 245 layer-steps/s.
+    // heads, are halved), doubled up to 256 rows while the launch would hold
+    // more than one block per CU.  Tiny launches keep single tiles to have
+    // more blocks.  Measured (layer-steps/s, one box): at most 512 blocks
+    // against at most 256: shelf_ctx8 2 714 -> 2 727 (256 rows per block:
+    // attention 22.6 -> 22.3 us, combine 5.8 -> 4.6 us); mtp3 with 512 rows
+    // per block (256 blocks) lost (attention 28.9 -> 34.6 us), so blocks stay
+    // at 256 rows; at most 1024 blocks lost everywhere (shelf_ctx8 2 642).
     auto blocks = [&](int64_t rpb) { return (int64_t)((k + rpb - 1) / rpb) * rows_total_pairs; };
     int rpb = 2 * kAttnTileRows;
     if (blocks(rpb) < 64) return kAttnTileRows;
-    while (rpb < kAttnMaxRowsPerBlock && blocks(rpb) > 512) rpb *= 2;
+    while (rpb < 8 * kAttnTileRows && blocks(rpb) > 256) rpb *= 2;
     return rpb;
 }
 
