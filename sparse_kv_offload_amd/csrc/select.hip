@@ -817,7 +817,14 @@ hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* met
                               int64_t max_tokens_now, const uint16_t* scales_layer, const uint32_t* qc8) {
     const int64_t wpr = winner_words(cap);
     const int64_t now = std::max<int64_t>(1, max_tokens_now);
-    const int per_row = (int)std::min<int64_t>(32, std::max<int64_t>(4, (now + kFilterSpan - 1) / kFilterSpan));
+    // blocks per row: one per kFilterSpan tokens of the longest sequence
+    // (the rescan path's share), 4 to 32, and at most 1024 blocks in all:
+    // most blocks of a row find no candidates and only cost their launch
+    // (mtp3, 64 rows: 32 per row 18.3 us, 16 per row 12.4 us; long, 8 rows,
+    // keeps 32: 16 per row took 10.9 against 8.0 us)
+    const int rows = B * D;
+    int per_row = (int)std::min<int64_t>(32, std::max<int64_t>(4, (now + kFilterSpan - 1) / kFilterSpan));
+    per_row = std::min(per_row, std::max(4, 1024 / std::max(rows, 1)));
     const dim3 grid((unsigned)per_row, (unsigned)(B * D));
     hipLaunchKernelGGL(k_topk_filter, grid, dim3(256), 0, st, hist, meta, pre, cand, topk, cache_slots_layer,
                        ntok_layer, winners, miss_bits, reinterpret_cast<const uint4*>(idx_layer),
