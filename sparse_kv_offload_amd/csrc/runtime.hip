@@ -131,9 +131,8 @@ struct sko_handle {
     // per-step scratch (shared by all layers; steps are stream-ordered)
     uint32_t* keys = nullptr;       // [B][D][kcap], only with SKO_FLAG_KEEP_KEYS
     uint2* pre = nullptr;           // [B][D][cap] candidates at or above the floor
-    // early miss copy (several positions or head groups, small batch): copy
-    // blocks of the merge launch move the misses into staging while the
-    // merge blocks update the LRU state
+    // early miss copy: copy blocks of the merge launch copy the misses into
+    // their spare hot rows while the merge blocks update the LRU state
     bool fused_copy = false;        // the attention launch copies the misses
     bool staged_copy = false;       // early copy (copy blocks in the LRU-update launch)
     uint32_t* miss_bits = nullptr;  // [B][wpr]
@@ -667,9 +666,9 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
         if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, cfg->device) == hipSuccess && ncu > 0)
             h->cu_count = ncu;
     }
-    // Early copy by default: extra blocks of the LRU-update launch read the
-    // misses into staging while the update runs, so neither the update nor
-    // the attention waits on the host link (measured against copying inside
+    // Early copy by default: extra blocks of the LRU-update launch copy the
+    // misses into their spare hot rows while the update runs, so neither the
+    // update nor the attention waits on the host link (measured against copying inside
     // the attention at one position: tiny +18 %, small +4.5 %, shelf even;
     // against the late copy: long +20 %, mtp3 +2 %).
     h->fused_copy = (cfg->flags & SKO_FLAG_FUSED_COPY) != 0;

@@ -88,8 +88,7 @@ def test_five_positions():
 @pytest.mark.parametrize("positions", [16, 17])
 def test_many_positions(positions):
     """16 positions: the largest count whose lists the LRU update puts in
-    token order; 17: the lists keep the selection's order and the early
-    copy's claims are taken over all positions at once."""
+    token order; 17: the lists keep the selection's order."""
     w = case(f"d{positions}", batch=2, context=1500, steps=6, top_k=24, hot_slots=positions * 24 + 40,
              positions=positions, heads=4)
     log(f"case d{positions}")
