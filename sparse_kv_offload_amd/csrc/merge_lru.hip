@@ -209,7 +209,15 @@ __device__ __forceinline__ void thread_run(int64_t n, int align, int64_t* r0, in
 // i.e. more host reads in flight, lowered the transfer rate (2x the blocks:
 // -15 %, 4x: -25 % at long context) and fewer left it idle (small).
 constexpr int kCopyBlocks = 64;
-constexpr int kCopyRowsPerWave = 2;
+// One row in flight per wave (about 1 000 rows over the launch, some 1.2 MB,
+// several times the link's bandwidth-delay product).  Two rows per wave
+// copied no faster and slowed everything else on the chip more: host reads
+// in flight hold the memory system, so the LRU update beside them and any
+// kernel on another stream wait longer (one box, layer-steps/s, two rows ->
+// one: shelf_ctx8 2 724 -> 2 736, mtp3 1 225 -> 1 243, small 4 989 -> 5 045,
+// long 4 335 -> 4 363; with eight waves of one row each the copy itself
+// slowed, 270 -> 279 us at shelf_ctx8).
+constexpr int kCopyRowsPerWave = 1;
 
 __device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, const uint32_t* __restrict__ miss_bits,
                                            const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
