@@ -526,6 +526,9 @@ def main() -> int:
     gather_slots = max(gather_rows, min(w.hot_slots, 4 * gather_rows))
     gather_ceiling = sko.sko_hbm_gather_rate(0, B * D, gather_slots, gather_rows, 2) \
         if gather_rows >= 128 and B * D * gather_slots <= (1 << 22) else None
+    # a plain streaming read of 256 MiB (cold): the practical HBM ceiling of
+    # the indexer score pass, which reads every indexer row once
+    stream_ceiling = sko.sko_hbm_read_rate(0, 1 << 28, 5)
     hbm_copy = measure_hbm_copy(torch)
     calibration_copy(torch)
 
@@ -542,6 +545,9 @@ def main() -> int:
         elif name == "attn_partial" and gather_ceiling:
             e["measured_ceiling"] = round(gather_ceiling, 1)
             e["frac_of_measured"] = round(ach / gather_ceiling, 4)
+        elif name == "score_hist" and stream_ceiling:
+            e["measured_ceiling"] = round(stream_ceiling, 1)
+            e["frac_of_measured"] = round(ach / stream_ceiling, 4)
         return e
 
     rooflines = {}
@@ -589,6 +595,8 @@ def main() -> int:
         "zero_copy_read_GBps": round(zero_copy, 2),
         # random whole-row gathers from HBM (the attention's access pattern)
         "hbm_row_gather_GBps": round(gather_ceiling, 1) if gather_ceiling else None,
+        # a plain streaming read of HBM (the score pass's access pattern)
+        "hbm_stream_read_GBps": round(stream_ceiling, 1),
         "hbm_copy_GBps": round(hbm_copy, 1),
         # the first step finds an empty shelf (every winner a miss); it is
         # not in `value`

@@ -38,8 +38,8 @@
  *  - All device work is enqueued on the stream given at create (or set by
  *    sko_set_stream), in call order (SKO_FLAG_HIT_OVERLAP also uses an
  *    internal stream, forked from and joined back into that stream within
- *    each decode step).  sko_link_read_rate and sko_hbm_gather_rate are
- *    independent of any handle.
+ *    each decode step).  sko_link_read_rate, sko_hbm_gather_rate and
+ *    sko_hbm_read_rate are independent of any handle.
  */
 #ifndef SKO_H
 #define SKO_H
@@ -383,6 +383,22 @@ int sko_link_read_rate(int32_t device, int64_t bytes, int32_t reps, float* gbps)
  */
 int sko_hbm_gather_rate(int32_t device, int32_t seqs, int32_t slots, int32_t rows_per_seq, int32_t reps,
                         float* gbps);
+
+/*
+ * sko_hbm_read_rate — the HBM rate of a plain streaming read, the access
+ * pattern of the indexer score pass (every indexer row of the layer read
+ * once per step, [LSO] §4 "Decode step" item 1): `bytes` bytes read with
+ * 16-byte loads, one block per compute unit, each block a contiguous part.
+ * Four buffers of `bytes` bytes are read in rotation, so a launch finds
+ * little of its buffer in the on-die caches; *gbps receives the median of
+ * reps x 4 launches each timed on its own (1e9 bytes/s).  Allocates 4 x
+ * bytes of device memory, uses and frees it on `device`; synchronous;
+ * independent of any handle.
+ * Errors: SKO_E_INVAL (NULL gbps, device < 0, bytes below 1 MiB, above
+ * 2 GiB or not a multiple of 16, reps outside 1..64), SKO_E_NOMEM,
+ * SKO_E_DEVICE.
+ */
+int sko_hbm_read_rate(int32_t device, int64_t bytes, int32_t reps, float* gbps);
 
 /* Destroy: synchronize the stream, free everything. NULL is a no-op. */
 void sko_destroy(sko_handle* h);

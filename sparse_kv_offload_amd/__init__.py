@@ -55,6 +55,7 @@ EXPORTED = (
     "sko_read_table", "sko_get_stats", "sko_set_timing", "sko_get_timing", "sko_get_copy_overlap",
     "sko_stage_name",
     "sko_num_stages", "sko_destroy", "sko_last_error", "sko_version", "sko_link_read_rate", "sko_hbm_gather_rate",
+    "sko_hbm_read_rate",
     # layerwise prefill offload (include/sko_prefill.h)
     "sko_prefill_plan", "sko_prefill_create", "sko_prefill_destroy", "sko_prefill_host_pool",
     "sko_prefill_set_tokens", "sko_prefill_begin_layer", "sko_prefill_end_layer", "sko_prefill_sync",
@@ -136,6 +137,7 @@ def _load() -> ctypes.CDLL:
         "sko_version": (ctypes.c_char_p, []),
         "sko_link_read_rate": (ctypes.c_int, [i32, i64, i32, ctypes.POINTER(ctypes.c_float)]),
         "sko_hbm_gather_rate": (ctypes.c_int, [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_float)]),
+        "sko_hbm_read_rate": (ctypes.c_int, [i32, i64, i32, ctypes.POINTER(ctypes.c_float)]),
         "sko_prefill_plan": (ctypes.c_int, [i32, vp, vp, i32, vp, vp, vp]),
         "sko_prefill_create": (ctypes.c_int, [ctypes.POINTER(SkoPrefillConfig), vp, ctypes.POINTER(vp)]),
         "sko_prefill_destroy": (ctypes.c_int, [vp]),
@@ -215,6 +217,13 @@ def sko_hbm_gather_rate(device: int = 0, seqs: int = 32, slots: int = 8192, rows
     v = ctypes.c_float()
     _check(_lib.sko_hbm_gather_rate(device, seqs, slots, rows_per_seq, reps, ctypes.byref(v)),
            "sko_hbm_gather_rate")
+    return float(v.value)
+
+
+def sko_hbm_read_rate(device: int = 0, nbytes: int = 1 << 28, reps: int = 5) -> float:
+    """HBM rate (GB/s) of a plain streaming read, the indexer score pass's pattern."""
+    v = ctypes.c_float()
+    _check(_lib.sko_hbm_read_rate(device, nbytes, reps, ctypes.byref(v)), "sko_hbm_read_rate")
     return float(v.value)
 
 

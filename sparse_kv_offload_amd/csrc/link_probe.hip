@@ -3,12 +3,16 @@
 // kind of access the miss copy makes, without its scatter), timed with HIP
 // events.  It is the reference for the miss copy's link rate beside the
 // bulk hipMemcpy rate (the copy engines), which kernels cannot reach.
+// Two device-memory probes sit beside it, the measured ceilings of the two
+// HBM-bound kernels: random whole-row gathers as the attention makes them,
+// and a plain streaming read as the indexer score pass makes it.
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <vector>
 
 #include "sko.h"
+#include "sko_common.h"
 #include "sko_internal.h"
 
 namespace sko {
@@ -66,8 +70,100 @@ __global__ __launch_bounds__(256) void k_gather_rows(const uint4* __restrict__ r
     if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// Streaming read of n 16-byte words: block j reads the contiguous part
+// [j n / g, (j + 1) n / g) of the buffer, every thread kStreamUnroll
+// nontemporal 16-byte loads at a time (a sweep of block size, blocks per CU
+// and loads in flight per thread put this shape at the top).
+constexpr int kStreamThreads = 512;
+constexpr int kStreamUnroll = 4;
+__global__ __launch_bounds__(kStreamThreads) void k_stream_read(const uint4* __restrict__ src, int64_t n,
+                                                                uint32_t* __restrict__ sink) {
+    const int64_t b0 = (int64_t)blockIdx.x * n / gridDim.x;
+    const int64_t b1 = ((int64_t)blockIdx.x + 1) * n / gridDim.x;
+    uint32_t acc = 0u;
+    int64_t i = b0 + threadIdx.x;
+    for (; i + (int64_t)(kStreamUnroll - 1) * kStreamThreads < b1; i += (int64_t)kStreamUnroll * kStreamThreads) {
+        uint4 v[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) v[u] = load_nt_u4(src + i + (int64_t)u * kStreamThreads);
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < b1; i += kStreamThreads) {
+        const uint4 v = load_nt_u4(src + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 }  // namespace
 }  // namespace sko
+
+extern "C" int sko_hbm_read_rate(int32_t device, int64_t bytes, int32_t reps, float* gbps) {
+    using namespace sko;
+    const char* fn = "sko_hbm_read_rate";
+    if (!gbps) return fail(SKO_E_INVAL, "NULL result pointer", hipSuccess, fn);
+    *gbps = 0.0f;
+    constexpr int kRot = 4;  // buffers in rotation: each launch starts cold in the device-side caches
+    if (device < 0 || bytes < (1 << 20) || bytes > ((int64_t)1 << 31) || bytes % 16 != 0 || reps < 1 || reps > 64)
+        return fail(SKO_E_INVAL, "needs device >= 0, 1 MiB <= bytes <= 2 GiB and a multiple of 16, 1 <= reps <= 64",
+                    hipSuccess, fn);
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    hipError_t e = hipSetDevice(device);
+    if (e != hipSuccess) return fail(SKO_E_DEVICE, "hipSetDevice", e, fn);
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1) cus = 256;
+    const int64_t n = bytes / 16;
+    uint4* buf = nullptr;
+    uint32_t* sink = nullptr;
+    hipStream_t st = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    int rc = SKO_OK;
+    if (hipMalloc((void**)&buf, (size_t)kRot * bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        rc = fail(SKO_E_NOMEM, "device buffers", hipSuccess, fn);
+    }
+    if (rc == SKO_OK) {
+        e = hipMemset(buf, 0, (size_t)kRot * bytes);
+        if (e == hipSuccess) e = hipMalloc((void**)&sink, 4);
+        if (e == hipSuccess) e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreate(&a);
+        if (e == hipSuccess) e = hipEventCreate(&b);
+        if (e != hipSuccess) rc = fail(SKO_E_DEVICE, "set-up", e, fn);
+    }
+    // one warm-up launch per buffer, then reps * kRot launches, each timed
+    // on its own (the median is reported)
+    std::vector<float> times;
+    for (int w = 0; rc == SKO_OK && w < kRot * (reps + 1); ++w) {
+        const uint4* src = buf + (size_t)(w % kRot) * n;
+        const bool timed = w >= kRot;
+        if (timed) e = hipEventRecord(a, st);
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(k_stream_read, dim3(cus), dim3(kStreamThreads), 0, st, src, n, sink);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess && timed) e = hipEventRecord(b, st);
+        if (e == hipSuccess && timed) e = hipEventSynchronize(b);
+        float ms = 0.0f;
+        if (e == hipSuccess && timed) e = hipEventElapsedTime(&ms, a, b);
+        if (e != hipSuccess) rc = fail(SKO_E_DEVICE, "timed read", e, fn);
+        else if (timed) times.push_back(ms);
+    }
+    if (st) (void)hipStreamSynchronize(st);
+    if (a) (void)hipEventDestroy(a);
+    if (b) (void)hipEventDestroy(b);
+    if (st) (void)hipStreamDestroy(st);
+    if (sink) (void)hipFree(sink);
+    if (buf) (void)hipFree(buf);
+    if (prev >= 0) (void)hipSetDevice(prev);
+    if (rc == SKO_OK && !times.empty()) {
+        std::sort(times.begin(), times.end());
+        const float ms = times[times.size() / 2];
+        if (ms > 0.0f) *gbps = (float)((double)bytes / (ms * 1e-3) / 1e9);
+    }
+    return rc;
+}
 
 extern "C" int sko_link_read_rate(int32_t device, int64_t bytes, int32_t reps, float* gbps) {
     using namespace sko;

@@ -57,7 +57,6 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* scra
     return res;
 }
 
-// bf16 pair in one dword -> two floats (exact widening).
 // 16-byte load marked nontemporal: data streamed once per step (the
 // indexer scan) is not kept in the caches, which lets the loads reach a
 // higher share of HBM bandwidth than ordinary loads.
@@ -67,6 +66,7 @@ __device__ __forceinline__ uint4 load_nt_u4(const uint4* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// bf16 pair in one dword -> two floats (exact widening).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -123,3 +123,13 @@ def test_hbm_gather_rate_rejects_bad_arguments(args):
     with pytest.raises(sko.SkoError) as e:
         sko.sko_hbm_gather_rate(*args)
     assert e.value.code == sko.SKO_E_INVAL
+
+
+@pytest.mark.parametrize("args", [(-1, 1 << 28, 1), (0, 1000, 1), (0, (1 << 20) + 8, 1), (0, 1 << 28, 0),
+                                  (0, (1 << 31) + 16, 1), (0, 1 << 28, 65)])
+def test_hbm_read_rate_rejects_bad_arguments(args):
+    """Argument checks come before any device work (so they run without a GPU)."""
+    import sparse_kv_offload_amd as sko
+    with pytest.raises(sko.SkoError) as e:
+        sko.sko_hbm_read_rate(*args)
+    assert e.value.code == sko.SKO_E_INVAL
