@@ -353,6 +353,9 @@ def main() -> int:
                     help="indexer cache: bf16 rows, or int8 codes with fp16 scales after a Hadamard rotation")
     ap.add_argument("--pool", choices=["default", "coherent", "noncoherent"], default="default",
                     help="host-pool allocation mode")
+    ap.add_argument("--append", choices=["fused", "separate"], default="fused",
+                    help="append each step's token inside the decode call (sko_decode_step_append) or with "
+                         "its own call (sko_append_token, then sko_decode_step)")
     ap.add_argument("--copy", choices=["default", "early", "late", "fused"], default="default",
                     help="miss-copy arrangement: early (the default: by extra blocks of the LRU-update launch), "
                          "late (after the LRU update), fused (inside the attention launch; one "
@@ -438,8 +441,14 @@ def main() -> int:
 
     def run_step(t):
         for l in range(L):
-            sko.sko_append_token(h.handle, l, sko.SKO_ALL_SEQS, new_idx[t][l], new_kv[t][l], 1, True)
-            sko.sko_decode_step(h.handle, l, q_idx[t][l], q_attn[t][l], out)
+            if args.append == "fused":
+                # the new token's rows go in with the decode call (one launch
+                # fewer per layer-step; same results as the two calls)
+                sko.sko_decode_step_append(h.handle, l, new_idx[t][l], new_kv[t][l], q_idx[t][l], q_attn[t][l],
+                                           out)
+            else:
+                sko.sko_append_token(h.handle, l, sko.SKO_ALL_SEQS, new_idx[t][l], new_kv[t][l], 1, True)
+                sko.sko_decode_step(h.handle, l, q_idx[t][l], q_attn[t][l], out)
 
     # Warm-up: the cold step untimed, then the remaining warm-up steps with
     # every stage bracketed by events (the per-stage breakdown; each event
@@ -583,7 +592,7 @@ def main() -> int:
         "config": {"workload": w.name, "layers": L, "batch": B, "context": w.context,
                    "top_k": k, "hot_slots": w.hot_slots, "mtp_positions": D, "heads": H,
                    "parallelism": "none (1 GPU)", "pool": args.pool, "copy": args.copy,
-                   "hit_overlap": bool(args.hit_overlap),
+                   "hit_overlap": bool(args.hit_overlap), "append": args.append,
                    "indexer": args.indexer},
         "tokens_per_s": round(B * K / elapsed, 2),
         "indexer_scan_GBps": rooflines.get("score_hist", {}).get("achieved"),

@@ -255,6 +255,26 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
                      float* out);
 
 /*
+ * sko_decode_step_append — sko_append_token of one new token for every
+ * sequence (rows on the device) followed by sko_decode_step, in one call
+ * with one launch fewer ([LSO] §4 "Decode step": the new token's rows are
+ * written, then the step runs over every token including it).  The score
+ * launch scores the new token from idx_rows and writes its indexer row to
+ * the device cache and its main-KV row to the device copy of the newest
+ * row; the LRU-update launch writes that row to the host pool.  Results,
+ * tables and pool contents are those of the two calls.
+ *   idx_rows  device [B][64] bf16, kv_rows device [B][576] bf16, read in
+ *             stream order (keep them live until the stream passes this
+ *             call)
+ *   q_idx, q_attn, out  as for sko_decode_step
+ * Errors: SKO_E_INVAL (bad layer or NULL pointer), SKO_E_CAPACITY (any
+ * sequence at max_tokens; checked before any work), SKO_E_STATE,
+ * SKO_E_DEVICE.
+ */
+int sko_decode_step_append(sko_handle* h, int32_t layer, const void* idx_rows, const void* kv_rows,
+                           const void* q_idx, const void* q_attn, float* out);
+
+/*
  * sko_decode_step_static — sko_decode_step for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): the same step, arguments and results,

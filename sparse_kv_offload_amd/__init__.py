@@ -51,6 +51,7 @@ SKO_TAB_SLOT_ROW, SKO_TAB_SPARE_ROWS = 9, 10
 
 EXPORTED = (
     "sko_create", "sko_set_stream", "sko_append_token", "sko_decode_step", "sko_decode_step_static",
+    "sko_decode_step_append",
     "sko_read_step",
     "sko_read_table", "sko_get_stats", "sko_set_timing", "sko_get_timing", "sko_get_copy_overlap",
     "sko_stage_name",
@@ -122,6 +123,7 @@ def _load() -> ctypes.CDLL:
         "sko_append_token": (ctypes.c_int, [vp, i32, i32, vp, vp, i64, i32]),
         "sko_decode_step": (ctypes.c_int, [vp, i32, vp, vp, vp]),
         "sko_decode_step_static": (ctypes.c_int, [vp, i32, vp, vp, vp]),
+        "sko_decode_step_append": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp]),
         "sko_read_step": (ctypes.c_int, [vp, i32, vp, i64]),
         "sko_read_table": (ctypes.c_int, [vp, i32, i32, i32, vp, i64]),
         "sko_get_stats": (ctypes.c_int, [vp, i32, ctypes.POINTER(SkoLayerStats)]),
@@ -256,6 +258,12 @@ def sko_decode_step(h: int, layer: int, q_idx, q_attn, out) -> None:
     _check(_lib.sko_decode_step(h, layer, _addr(q_idx), _addr(q_attn), _addr(out)), "sko_decode_step")
 
 
+def sko_decode_step_append(h: int, layer: int, idx_rows, kv_rows, q_idx, q_attn, out) -> None:
+    """Append one token per sequence (device rows) and decode, in one call."""
+    _check(_lib.sko_decode_step_append(h, layer, _addr(idx_rows), _addr(kv_rows), _addr(q_idx), _addr(q_attn),
+                                       _addr(out)), "sko_decode_step_append")
+
+
 def sko_decode_step_static(h: int, layer: int, q_idx, q_attn, out) -> None:
     _check(_lib.sko_decode_step_static(h, layer, _addr(q_idx), _addr(q_attn), _addr(out)),
            "sko_decode_step_static")
@@ -353,6 +361,9 @@ class SparseKVOffload:
 
     def decode_step(self, layer: int, q_idx, q_attn, out) -> None:
         sko_decode_step(self.handle, layer, q_idx, q_attn, out)
+
+    def decode_step_append(self, layer: int, idx_rows, kv_rows, q_idx, q_attn, out) -> None:
+        sko_decode_step_append(self.handle, layer, idx_rows, kv_rows, q_idx, q_attn, out)
 
     # ---- inspection ----
     def step_buffer(self, which: int) -> np.ndarray:

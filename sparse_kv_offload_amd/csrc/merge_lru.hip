@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     uint32_t* __restrict__ miss_bits, const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
     uint4* __restrict__ hot_layer, int32_t* __restrict__ slot_row_layer, int32_t* __restrict__ spare_layer, int R,
     int32_t* __restrict__ wrow, int32_t* __restrict__ phys, int sort_winners,
-    int test_violation, uint64_t* __restrict__ stamps) {
+    int test_violation, uint64_t* __restrict__ stamps, uint4* __restrict__ pool_newest) {
     // instrumentation (stamps != nullptr): each block records when it
     // started and ended on the chip's constant-rate clock, so the host can
     // tell how long the copy blocks ran beside the LRU update
@@ -325,6 +325,11 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t Lt = ntok_layer[b];
+    // the fused append: the newest token's row, which the score launch put in
+    // its device copy, also goes to the host pool (no kernel of this step
+    // reads it there: every copy takes the newest row from the device copy)
+    if (pool_newest != nullptr && Lt > 0 && tid < kKvRowU4)
+        pool_newest[((size_t)b * cap + (size_t)(Lt - 1)) * kKvRowU4 + tid] = recent_layer[(size_t)b * kKvRowU4 + tid];
     const int kk = (int)std::min<int64_t>(top_k, Lt);
     int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
     int32_t* __restrict__ st = slot_token_layer + (size_t)b * S;
@@ -685,7 +690,8 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
                             uint16_t* hot_layer, int32_t* slot_row_layer, int32_t* spare_layer, int R,
                             int32_t* wrow, int32_t* phys, bool sort_winners,
-                            int64_t max_tokens_now, bool test_violation, uint64_t* stamps) {
+                            int64_t max_tokens_now, bool test_violation, uint64_t* stamps,
+                            uint16_t* pool_newest) {
     const int64_t C = ring_capacity(S, D, top_k);
     const int64_t wpr = winner_words(cap);
     // B merge blocks, then (early copy) B * copy_per_seq copy blocks of
@@ -700,7 +706,7 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                        miss_bits,
                        reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<const uint4*>(recent_layer),
                        reinterpret_cast<uint4*>(hot_layer), slot_row_layer, spare_layer, R, wrow, phys,
-                       sort_winners ? 1 : 0, test_violation ? 1 : 0, stamps);
+                       sort_winners ? 1 : 0, test_violation ? 1 : 0, stamps, reinterpret_cast<uint4*>(pool_newest));
     return hipGetLastError();
 }
 

@@ -123,7 +123,14 @@ struct sko_handle {
     int32_t* ring[2] = {nullptr, nullptr};  // [L][B][C] recency rings (one live per sequence)
     int32_t* ring_pos = nullptr;            // [L][B][S] ring index of each slot
     RingState* ring_state = nullptr;        // [L][B]
-    int32_t* ntok_dev = nullptr;    // [L][B]
+    // [L][2][B] device token counts, two buffers per layer: ntok_sel[layer]
+    // picks the current one.  The fused append and decode step reads the
+    // current buffer in its score launch, which writes the counts after the
+    // append into the other buffer; the step's later kernels read that one,
+    // and the host then flips ntok_sel, so no kernel reads a count that
+    // another kernel of the same launch writes.
+    int32_t* ntok_dev = nullptr;
+    std::vector<uint8_t> ntok_sel;  // [L]
     unsigned long long* stats = nullptr;  // [L][8]
     std::vector<int64_t> ntok;      // host mirror [L][B]
     std::vector<int32_t> step;      // [L]
@@ -181,6 +188,7 @@ struct sko_handle {
     std::vector<void*> dev_allocs;
 
     size_t lb(int layer, int b) const { return (size_t)layer * B + b; }
+    int32_t* ntok_buf(int layer, int which) const { return ntok_dev + ((size_t)layer * 2 + which) * B; }
     // indexer cache bytes of one (layer, seq): 128 B (bf16) or 64 B (int8) per token slot
     size_t idx_seq_bytes() const { return (size_t)ntiles * kIdxTile * (c8 ? kIdxDim : kIdxDim * 2); }
 };
@@ -415,13 +423,18 @@ int validate_decode(sko_handle* h, int32_t layer, const void* q_idx, const void*
 }
 
 // One decode step of `layer` (arguments already validated, device current),
-// with the per-step scratch `sc`.
+// with the per-step scratch `sc`.  app_idx / app_kv non-null: the fused
+// append, one new token per sequence (rows on the device, capacity already
+// checked), appended inside the step.
 int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void* q_attn, float* out,
-                     const StepScratch& sc) {
+                     const StepScratch& sc, const void* app_idx = nullptr, const void* app_kv = nullptr) {
     int rc = SKO_OK;
 
     const int B = h->B, D = h->D, k = h->k, S = h->S, H = h->H;
     const int64_t cap = h->cap;
+    const bool fused_append = app_idx != nullptr;
+    if (fused_append)
+        for (int b = 0; b < B; ++b) h->ntok[h->lb(layer, b)] += 1;
     int64_t max_now = 0;
     for (int b = 0; b < B; ++b) max_now = std::max(max_now, h->ntok[h->lb(layer, b)]);
     const int32_t t = h->step[layer];
@@ -438,7 +451,20 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
     int32_t* cs = h->cache_slots + LBc;
     int32_t* st = h->slot_token + LBs;
     int32_t* lu = h->last_use + LBs;
-    const int32_t* ntok = h->ntok_dev + (size_t)layer * B;
+    // the counts every kernel after the score launch reads: with the fused
+    // append, the other buffer, which the score launch fills
+    const int sel = h->ntok_sel[layer];
+    const int32_t* ntok_in = h->ntok_buf(layer, sel);
+    const int32_t* ntok = h->ntok_buf(layer, fused_append ? sel ^ 1 : sel);
+    ScoreAppend app;
+    if (fused_append) {
+        app.idx = static_cast<const uint16_t*>(app_idx);
+        app.kv = static_cast<const uint4*>(app_kv);
+        app.idx_cache = reinterpret_cast<uint8_t*>(h->idx) + (size_t)layer * B * h->idx_seq_bytes();
+        app.scales = h->c8 ? h->idx_scale + (size_t)layer * B * h->ntiles * kIdxTile : nullptr;
+        app.recent = reinterpret_cast<uint4*>(h->recent + (size_t)layer * B * kKvDim);
+        app.ntok_out = h->ntok_buf(layer, sel ^ 1);
+    }
     const uint16_t* qi = static_cast<const uint16_t*>(q_idx);
     const uint16_t* qa = static_cast<const uint16_t*>(q_attn);
 
@@ -449,9 +475,9 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
     int32_t* floor_layer = h->floor + (size_t)layer * B * D;
 
     if ((rc = run_stage(h, ST_SCORE, [&] {
-             return launch_score_hist(h->stream, idx_layer, qi, ntok, h->keys, sc.hist, floor_layer, sc.pre,
+             return launch_score_hist(h->stream, idx_layer, qi, ntok_in, h->keys, sc.hist, floor_layer, sc.pre,
                                       sc.meta, cs, B, D, h->kcap, cap, h->ntiles, max_now, h->cu_count, scale_layer,
-                                      sc.qc8);
+                                      sc.qc8, app);
          })))
         return rc;
     const bool fused_copy = h->fused_copy;
@@ -500,7 +526,8 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
                                      staged ? sc.miss_bits : nullptr, pool_layer, recent_layer, hot_layer,
                                      slot_row_layer, spare_layer, R, fused_copy ? nullptr : sc.wrow, h->phys,
                                      /* the split attention reads the lists during this launch */ !h->hit_overlap,
-                                     max_now, (h->cfg.flags & SKO_FLAG_TEST_VIOLATION) != 0, stamps);
+                                     max_now, (h->cfg.flags & SKO_FLAG_TEST_VIOLATION) != 0, stamps,
+                                     fused_append ? h->pool_dev + LBc * kKvDim : nullptr);
          })))
         return rc;
     // late copy: its own gather from the pool into the misses' rows; early:
@@ -543,7 +570,25 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
         return rc;
     h->step[layer] += 1;
     h->last_layer = layer;
+    if (fused_append) h->ntok_sel[layer] ^= 1;
     return SKO_OK;
+}
+
+// The step scratch the handle owns (sko_decode_step, sko_decode_step_append).
+StepScratch handle_scratch(const sko_handle* h) {
+    StepScratch sc;
+    sc.pre = h->pre;
+    sc.cand = h->cand;
+    sc.hist = h->hist;
+    sc.meta = h->meta;
+    sc.winners = h->winners;
+    sc.miss_bits = h->miss_bits;
+    sc.wrow = h->wrow;
+    sc.glist = h->glist;
+    sc.part_acc = h->part_acc;
+    sc.part_ml = h->part_ml;
+    sc.qc8 = h->qc8;
+    return sc;
 }
 
 
@@ -660,6 +705,7 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     h->R = h->S + h->M;
     h->wpr = winner_words(h->cap);
     h->ntok.assign((size_t)h->L * h->B, 0);
+    h->ntok_sel.assign((size_t)h->L, 0);
     h->step.assign((size_t)h->L, 0);
     {
         int ncu = 0;
@@ -719,7 +765,7 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     ok = ok && dev_alloc(h, (void**)&h->ring[1], LB * h->C * 4);
     ok = ok && dev_alloc(h, (void**)&h->ring_pos, LB * h->S * 4);
     ok = ok && dev_alloc(h, (void**)&h->ring_state, LB * sizeof(RingState));
-    ok = ok && dev_alloc(h, (void**)&h->ntok_dev, LB * 4);
+    ok = ok && dev_alloc(h, (void**)&h->ntok_dev, LB * 2 * 4);
     ok = ok && dev_alloc(h, (void**)&h->stats, (size_t)h->L * 8 * 8);
     if (cfg->flags & SKO_FLAG_KEEP_KEYS) ok = ok && dev_alloc(h, (void**)&h->keys, BD * h->kcap * 4);
     ok = ok && dev_alloc(h, (void**)&h->pre, BD * h->cap * sizeof(uint2));
@@ -776,7 +822,7 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     if (e == hipSuccess) e = hipMemsetAsync(h->cache_slots, 0xFF, LB * h->cap * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->slot_token, 0xFF, LB * h->S * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->last_use, 0xFF, LB * h->S * 4, h->stream);
-    if (e == hipSuccess) e = hipMemsetAsync(h->ntok_dev, 0, LB * 4, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->ntok_dev, 0, LB * 2 * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->hot, 0, LB * h->R * (size_t)kKvRowBytes, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->stats, 0, (size_t)h->L * 8 * 8, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->topk, 0, BD * h->k * 4, h->stream);
@@ -852,7 +898,7 @@ int sko_append_token(sko_handle* h, int32_t layer, int32_t seq, const void* idx_
     uint16_t* scale_layer = h->c8 ? h->idx_scale + (size_t)layer * h->B * h->ntiles * kIdxTile : nullptr;
     uint16_t* pool_layer_dev = h->pool_dev + (size_t)layer * h->B * h->cap * kKvDim;
     uint16_t* recent_layer = h->recent + (size_t)layer * h->B * kKvDim;
-    int32_t* ntok_layer = h->ntok_dev + (size_t)layer * h->B;
+    int32_t* ntok_layer = h->ntok_buf(layer, h->ntok_sel[layer]);
     // bf16 indexer rows are stored as they are, or rotated and quantized
     auto append_rows = [&](const uint16_t* is, const uint16_t* ks, uint16_t* pool, int b0, int nb, int64_t m,
                            int64_t base) {
@@ -911,19 +957,21 @@ int sko_decode_step(sko_handle* h, int32_t layer, const void* q_idx, const void*
     if (rc != SKO_OK) return rc;
     DeviceGuard guard(h->cfg.device);
     if (!guard.ok) return device_fail(h, hipErrorInvalidDevice, "hipSetDevice");
-    StepScratch sc;
-    sc.pre = h->pre;
-    sc.cand = h->cand;
-    sc.hist = h->hist;
-    sc.meta = h->meta;
-    sc.winners = h->winners;
-    sc.miss_bits = h->miss_bits;
-    sc.wrow = h->wrow;
-    sc.glist = h->glist;
-    sc.part_acc = h->part_acc;
-    sc.part_ml = h->part_ml;
-    sc.qc8 = h->qc8;
-    return decode_step_impl(h, layer, q_idx, q_attn, out, sc);
+    return decode_step_impl(h, layer, q_idx, q_attn, out, handle_scratch(h));
+}
+
+int sko_decode_step_append(sko_handle* h, int32_t layer, const void* idx_rows, const void* kv_rows,
+                           const void* q_idx, const void* q_attn, float* out) {
+    int rc = validate_decode(h, layer, q_idx, q_attn, out);
+    if (rc != SKO_OK) return rc;
+    if (!idx_rows || !kv_rows) return set_err(SKO_E_INVAL, "NULL row pointer");
+    for (int b = 0; b < h->B; ++b)
+        if (h->ntok[h->lb(layer, b)] + 1 > h->cap)
+            return set_err(SKO_E_CAPACITY, "seq %d: %lld + 1 tokens exceed max_tokens %lld", b,
+                           (long long)h->ntok[h->lb(layer, b)], (long long)h->cap);
+    DeviceGuard guard(h->cfg.device);
+    if (!guard.ok) return device_fail(h, hipErrorInvalidDevice, "hipSetDevice");
+    return decode_step_impl(h, layer, q_idx, q_attn, out, handle_scratch(h), idx_rows, kv_rows);
 }
 
 int sko_decode_step_static(sko_handle* h, int32_t layer, const void* q_idx, const void* q_attn, float* out) {

@@ -361,7 +361,7 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
     const int32_t* __restrict__ floor_layer, uint2* __restrict__ pre, RowMeta* __restrict__ meta,
     const int32_t* __restrict__ cache_slots_layer, int D, int p0, int64_t kcap, int64_t cap, int64_t ntiles,
     int64_t tiles_now, int64_t total_tiles, const uint16_t* __restrict__ scales_layer,
-    uint32_t* __restrict__ qc8) {
+    uint32_t* __restrict__ qc8, ScoreAppend app) {
     constexpr int nw = score_threads<NP>() / 64;
     constexpr int RU = C8 ? kIdxC8RowU4 : kIdxRowU4;  // 16-byte loads per token
     __shared__ uint32_t sh[NP * kHistBins];
@@ -372,6 +372,12 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
     __shared__ int s_cnt[nw][NP];
     __shared__ float sq[NP > 1 ? NP * kIdxDim : 1];
     __shared__ int s_base[NP];
+    // the fused append: the new token's indexer row of the segment's
+    // sequence as the cache holds it (bf16: 32 words; int8: 16 words of
+    // codes, then the scale bits)
+    __shared__ uint4 snew4[kIdxRowU4];
+    uint32_t* const snew = reinterpret_cast<uint32_t*>(snew4);
+    const int add = app.idx != nullptr ? 1 : 0;  // tokens appended by this launch, per sequence
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t r_begin = (int64_t)blockIdx.x * total_tiles / gridDim.x;
     const int64_t r_end = ((int64_t)blockIdx.x + 1) * total_tiles / gridDim.x;
@@ -404,6 +410,29 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
             if ((int)threadIdx.x < NP * kIdxDim) sq[threadIdx.x] = __uint_as_float(qbits << 16);
         }
     };
+    // the fused append: wave NP stages the new token's row (element `elem`
+    // of it per lane), quantized for the int8 indexer (the caller
+    // synchronizes)
+    auto stage_new = [&](uint32_t elem) {
+        if (wave == NP) {
+            if constexpr (C8) {
+                uint32_t sc;
+                const int code = quant_row_wave(__uint_as_float(elem << 16), &sc);
+                const uint32_t word = pack_codes4(code);
+                if ((lane & 3) == 0) snew[lane >> 2] = word;
+                if (lane == 0) snew[kIdxDim / 4] = sc;
+            } else {
+                reinterpret_cast<uint16_t*>(snew)[lane] = (uint16_t)elem;
+            }
+        }
+    };
+    // this lane's element of sequence b's new row (any valid row when there
+    // is none, so that the load needs no branch)
+    auto new_elem = [&](int b) -> uint32_t {
+        const uint16_t* src = add ? app.idx + (size_t)b * kIdxDim
+                                  : reinterpret_cast<const uint16_t*>(q_idx) + (size_t)b * D * kIdxDim;
+        return src[lane];
+    };
     // this thread's query term (clamped in bounds; used by threads below
     // NP * 64 only)
     auto query_bits = [&](size_t row0) -> uint32_t {
@@ -422,6 +451,7 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
     const int b_first = (int)(r_begin / tiles_now);
     const size_t row0_first = (size_t)b_first * D + p0;
     const uint32_t qpre = (NP > 1 || C8) ? query_bits(row0_first) : 0u;
+    const uint32_t npre = new_elem(b_first);
     // keep the query load ahead of the tile loads: loads complete in order,
     // so waiting for it then leaves the tile in flight
     __builtin_amdgcn_sched_barrier(0);
@@ -442,26 +472,32 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
     }
     // the first segment's queries while its first tiles are in flight
     stage_query(row0_first, qpre);
+    if (add) stage_new(npre);
     for (int i = threadIdx.x; i < NP * kHistBins; i += blockDim.x) sh[i] = 0u;
     __syncthreads();
     for (int64_t seg = r_begin; seg < r_end;) {
         const bool first_segment = seg == r_begin;
         const int b = (int)(seg / tiles_now);
         const int64_t seg_end = std::min<int64_t>(r_end, ((int64_t)b + 1) * tiles_now);
+        // Lt: the tokens the cache holds at launch (the tile loop's tokens);
+        // the fused append adds token Lt, which the block whose range holds
+        // its tile scores on its own, from the staged row
         const int64_t Lt = ntok_layer[b];
         const int64_t tile0 = seg - (int64_t)b * tiles_now;
         const int64_t tile_end = std::min<int64_t>(seg_end - (int64_t)b * tiles_now,
                                                    (Lt + kIdxTile - 1) / kIdxTile);
+        const bool own_new = add && Lt / kIdxTile >= tile0 && Lt / kIdxTile < seg_end - (int64_t)b * tiles_now;
         seg = seg_end;
-        if (tile0 >= tile_end) continue;  // block-uniform: nothing of this sequence here
+        if (tile0 >= tile_end && !own_new) continue;  // block-uniform: nothing of this sequence here
         const size_t row0 = (size_t)b * D + p0;
         const uint32_t* __restrict__ qb = q_idx + row0 * (kIdxDim / 2);
         uint32_t* __restrict__ keyrow = keys + row0 * kcap;
         const uint4* __restrict__ seq_tiles = idx_layer + (size_t)b * ntiles * RU * kIdxTile + lane;
         const uint16_t* __restrict__ seq_scales = C8 ? scales_layer + (size_t)b * ntiles * kIdxTile + lane : nullptr;
         const int32_t* __restrict__ cs = cache_slots_layer + (size_t)b * cap;
-        if ((NP > 1 || C8) && !first_segment) {
+        if ((NP > 1 || C8 || add) && !first_segment) {
             stage_query(row0, query_bits(row0));
+            if (add) stage_new(new_elem(b));
             __syncthreads();
         }
 
@@ -471,6 +507,71 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
         for (int p = 0; p < NP; ++p) {
             floor_bin[p] = (uint32_t)floor_layer[row0 + p];
             nstage[p] = 0;
+        }
+        if (own_new) {  // block-uniform
+            // the layer's first launch writes the appended token: its
+            // indexer row to the cache (int8: codes and scale), its main-KV
+            // row to the device copy of the newest row, the token count
+            if (app.write) {
+                const int t = threadIdx.x;
+                if (t < kKvRowU4) {
+                    app.recent[(size_t)b * kKvRowU4 + t] = app.kv[(size_t)b * kKvRowU4 + t];
+                } else if (t < kKvRowU4 + RU) {
+                    const int c = t - kKvRowU4;
+                    uint4* cache = static_cast<uint4*>(app.idx_cache);
+                    if constexpr (C8) cache[idx_c8_tile_u4((size_t)b * ntiles, Lt, c)] = snew4[c];
+                    else cache[idx_tile_u4((size_t)b * ntiles, Lt, c)] = snew4[c];
+                } else if (t == kKvRowU4 + RU) {
+                    if constexpr (C8) app.scales[(size_t)b * ntiles * kIdxTile + Lt] = (uint16_t)snew[kIdxDim / 4];
+                    app.ntok_out[b] = (int32_t)(Lt + 1);
+                }
+            }
+            // wave NP scores it for every position (lane 0, the same
+            // arithmetic as the tile loop) and counts and stages its keys
+            if (wave == NP) {
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    uint32_t key = 0u;
+                    if (lane == 0) {
+                        float acc;
+                        if constexpr (C8) {
+                            int dot = 0;
+#pragma unroll
+                            for (int c = 0; c < kIdxC8RowU4; ++c) {
+                                const uint4 qv = sq8[p][c];
+                                dot = __builtin_amdgcn_sdot4((int)snew[4 * c + 0], (int)qv.x, dot, false);
+                                dot = __builtin_amdgcn_sdot4((int)snew[4 * c + 1], (int)qv.y, dot, false);
+                                dot = __builtin_amdgcn_sdot4((int)snew[4 * c + 2], (int)qv.z, dot, false);
+                                dot = __builtin_amdgcn_sdot4((int)snew[4 * c + 3], (int)qv.w, dot, false);
+                            }
+                            const float sq = __half2float(__ushort_as_half((uint16_t)sq8[p][4].x));
+                            acc = (float)dot * __half2float(__ushort_as_half((uint16_t)snew[kIdxDim / 4]));
+                            acc = acc * sq;
+                        } else {
+                            acc = 0.0f;
+                            const uint32_t* __restrict__ qr = qb + (size_t)p * (kIdxDim / 2);
+#pragma unroll
+                            for (int j = 0; j < kIdxDim / 2; ++j) {
+                                const uint32_t qw = qr[j];
+                                acc = __builtin_fmaf(bf16_lo(qw), bf16_lo(snew[j]), acc);
+                                acc = __builtin_fmaf(bf16_hi(qw), bf16_hi(snew[j]), acc);
+                            }
+                        }
+                        acc += 0.0f;
+                        key = score_key(acc);
+                    }
+                    key = __shfl(key, 0);
+                    const uint32_t bin = key >> (32 - kHistBits);
+                    if (lane == 0) {
+                        if constexpr (KEEP) keyrow[(size_t)p * kcap + Lt] = key;
+                        atomicAdd(&sh[p * kHistBins + bin], 1u);
+                    }
+                    if (bin >= floor_bin[p]) {  // wave-uniform
+                        if (lane == 0) stage[wave][p][0] = make_uint2(key, (uint32_t)Lt);
+                        nstage[p] = 1;
+                    }
+                }
+            }
         }
         // append this wave's staged candidates of position p to pre[row]
         auto flush = [&](int p) {
@@ -635,7 +736,7 @@ hipError_t launch_score_hist(hipStream_t st, const void* idx_layer, const uint16
                              const int32_t* floor_layer, uint2* pre, RowMeta* meta,
                              const int32_t* cache_slots_layer, int B, int D, int64_t kcap, int64_t cap,
                              int64_t ntiles, int64_t max_tokens_now, int cu_count,
-                             const uint16_t* scales_layer, uint32_t* qc8) {
+                             const uint16_t* scales_layer, uint32_t* qc8, const ScoreAppend& app) {
     const int64_t tiles_now = std::max<int64_t>(1, (max_tokens_now + kIdxTile - 1) / kIdxTile);
     const int64_t total = (int64_t)B * tiles_now;
     const uint4* kb = reinterpret_cast<const uint4*>(idx_layer);
@@ -652,10 +753,13 @@ hipError_t launch_score_hist(hipStream_t st, const void* idx_layer, const uint16
         int64_t nb = std::min<int64_t>((int64_t)cu_count * per_cu, (total + nw - 1) / nw);
         nb = std::max<int64_t>(nb, 1);
         const dim3 grid((unsigned)nb);
+        // every launch scores the appended token; the first one writes it
+        ScoreAppend ap = app;
+        ap.write = (app.idx != nullptr && p0 == 0) ? 1 : 0;
 #define SKO_SCORE_LAUNCH1(N, K, C)                                                                         \
     hipLaunchKernelGGL(HIP_KERNEL_NAME(k_score_hist<N, K, C>), grid, dim3(score_threads<N>()), 0, st, kb, q,      \
                        ntok_layer, keys, hist, floor_layer, pre, meta, cache_slots_layer, D, p0, kcap, cap, ntiles, \
-                       tiles_now, total, scales_layer, qc8)
+                       tiles_now, total, scales_layer, qc8, ap)
 #define SKO_SCORE_LAUNCH(N)                                   \
     do {                                                      \
         if (scales_layer) {                                   \

@@ -101,6 +101,25 @@ hipError_t launch_append_rows_c8(hipStream_t st, const uint16_t* idx_src, const 
                                  uint8_t* idx_layer, uint16_t* scales_layer, uint16_t* pool_layer,
                                  uint16_t* recent_layer, int32_t* ntok_layer, int seq0, int nseq, int64_t n,
                                  int64_t cap, int64_t ntiles, int32_t base);
+// The new token of every sequence, appended by the score launch itself
+// (the fused append and decode step): its bf16 indexer row idx [B][64] and
+// main-KV row kv [B][576], both on the device.  The launch scores the token
+// from idx (its tile in the cache does not hold it yet); with `write` (the
+// layer's first score launch) the block holding the token's tile also
+// writes the indexer row to the cache (int8 indexer: its codes and scale),
+// the main-KV row to recent, and ntok_out[b] = ntok_layer[b] + 1.  The host
+// pool receives the main-KV row from the LRU-update launch.  idx null: no
+// append.
+struct ScoreAppend {
+    const uint16_t* idx = nullptr;
+    const uint4* kv = nullptr;
+    void* idx_cache = nullptr;   // the layer's indexer cache (bf16 rows, or int8 codes)
+    uint16_t* scales = nullptr;  // the layer's int8 indexer scales
+    uint4* recent = nullptr;     // [B][72] the newest main-KV row of each sequence
+    int32_t* ntok_out = nullptr;
+    int write = 0;
+};
+
 // keys may be null (keys are then not stored); candidates (key, token |
 // miss << 31) with first digit >= floor_layer[row] go to
 // pre[row][0 .. meta[row].pre_count).  scales_layer non-null: the int8
@@ -111,7 +130,7 @@ hipError_t launch_score_hist(hipStream_t st, const void* idx_layer, const uint16
                              const int32_t* floor_layer, uint2* pre, RowMeta* meta,
                              const int32_t* cache_slots_layer, int B, int D, int64_t kcap, int64_t cap,
                              int64_t ntiles, int64_t max_tokens_now, int cu_count,
-                             const uint16_t* scales_layer, uint32_t* qc8);
+                             const uint16_t* scales_layer, uint32_t* qc8, const ScoreAppend& app);
 // Also sets floor_layer for the next step (kFloorRescanAll when rescan_all).
 // scales_layer / qc8 non-null: the int8 indexer (for the rescan path).
 hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* meta, const uint2* pre,
@@ -121,7 +140,10 @@ hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* met
                               bool rescan_all, int B, int D, int64_t cap, int64_t ntiles, int top_k,
                               int64_t max_tokens_now, const uint16_t* scales_layer, const uint32_t* qc8);
 // Also finishes the top-k (split buckets) and clears the histograms and row
-// records for the next step.
+// records for the next step.  pool_newest non-null (the fused append): the
+// merge block of each sequence also copies the newest token's main-KV row
+// from recent_layer into pool_newest (the host pool of the layer, through
+// its device mapping).
 hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, RowMeta* meta,
                             const uint2* cand, int32_t* topk, const int32_t* ntok_layer,
                             int32_t* cache_slots_layer, int32_t* slot_token_layer,
@@ -133,7 +155,8 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             uint32_t* miss_bits, const uint16_t* pool_layer, const uint16_t* recent_layer,
                             uint16_t* hot_layer, int32_t* slot_row_layer, int32_t* spare_layer, int R,
                             int32_t* wrow, int32_t* phys, bool sort_winners,
-                            int64_t max_tokens_now, bool test_violation, uint64_t* stamps);
+                            int64_t max_tokens_now, bool test_violation, uint64_t* stamps,
+                            uint16_t* pool_newest);
 // Copy blocks of the early copy: copy_per_seq per sequence, each owning
 // copy_words bitmap words (a multiple of 4, at most 1024).
 void copy_shape(int B, int64_t max_tokens_now, int* copy_per_seq, int* copy_words);

@@ -68,7 +68,7 @@ class GpuSide:
     """The HIP path through the C ABI (all sequences of the workload)."""
 
     def __init__(self, w: synth.Workload, layers: int, device_append: bool = True,
-                 prefix_chunk: int = 65536, flags: int = 0):
+                 prefix_chunk: int = 65536, flags: int = 0, fused_append: bool = False):
         import sparse_kv_offload_amd as sko
         torch = torch_mod()
         self.sko, self.torch, self.w = sko, torch, w
@@ -80,6 +80,10 @@ class GpuSide:
         self.h = sko.SparseKVOffload(cfg, self.stream)
         self.device_append = device_append
         self.prefix_chunk = prefix_chunk
+        # fused_append: each step's token goes in with the decode call
+        # (sko_decode_step_append) instead of sko_append_token
+        self.fused_append = fused_append
+        self.pending = {}
 
     def close(self):
         self.h.close()
@@ -94,7 +98,9 @@ class GpuSide:
         w = self.w
         idx = np.concatenate([w.index_rows(layer, b, w.seq_context(b) + t, 1) for b in range(w.batch)])
         kv = np.concatenate([w.kv_rows(layer, b, w.seq_context(b) + t, 1) for b in range(w.batch)])
-        if self.device_append:
+        if self.fused_append:
+            self.pending[layer] = (to_device_u16(idx), to_device_u16(kv))
+        elif self.device_append:
             self.h.append(layer, self.sko.SKO_ALL_SEQS, to_device_u16(idx), to_device_u16(kv), 1)
         else:
             self.h.append(layer, self.sko.SKO_ALL_SEQS, idx, kv, 1)
@@ -104,7 +110,11 @@ class GpuSide:
         w = self.w
         qi, qa = to_device_u16(q_idx), to_device_u16(q_attn)
         out = torch.empty((w.batch, w.positions, w.heads, synth.V_DIM), dtype=torch.float32, device="cuda")
-        self.h.decode_step(layer, qi, qa, out)
+        if layer in self.pending:
+            idx, kv = self.pending.pop(layer)
+            self.h.decode_step_append(layer, idx, kv, qi, qa, out)
+        else:
+            self.h.decode_step(layer, qi, qa, out)
         torch.cuda.synchronize()
         r = StepResult(topk=self.h.step_buffer(sko.SKO_BUF_TOPK), phys=self.h.step_buffer(sko.SKO_BUF_PHYS),
                        counts=self.h.step_buffer(sko.SKO_BUF_COUNTS), misses=self.h.step_buffer(sko.SKO_BUF_MISSES),
@@ -223,7 +233,7 @@ def compare_tables(gt: Dict[str, np.ndarray], ot: Dict[str, np.ndarray], where: 
 def run_parity(w: synth.Workload, layers: Optional[int] = None, steps: Optional[int] = None,
                chains: Optional[List[tuple]] = None, check_tables_every: int = 1,
                check_keys: bool = False, device_append: bool = True, out_steps=None,
-               log=None, flags: int = 0) -> Dict[str, float]:
+               log=None, flags: int = 0, fused_append: bool = False) -> Dict[str, float]:
     """Run the full workload on the GPU; check the sampled chains on the CPU."""
     L = w.layers if layers is None else layers
     T = w.steps if steps is None else steps
@@ -231,7 +241,7 @@ def run_parity(w: synth.Workload, layers: Optional[int] = None, steps: Optional[
     inputs = Inputs(w, sorted({c[0] for c in chains} | set(range(L))), T)
     import sparse_kv_offload_amd as sko
     gpu = GpuSide(w, L, device_append=device_append,
-                  flags=flags | (sko.SKO_FLAG_KEEP_KEYS if check_keys else 0))
+                  flags=flags | (sko.SKO_FLAG_KEEP_KEYS if check_keys else 0), fused_append=fused_append)
     ora = OracleSide(w, chains, indexer_c8=bool(flags & sko.SKO_FLAG_INDEXER_C8))
     worst = {"abs": 0.0, "rel_rms": 0.0, "rescans": 0}
     try:

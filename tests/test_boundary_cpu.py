@@ -85,6 +85,7 @@ def test_calls_on_null_handle_fail_cleanly():
     assert lib.sko_append_token(None, 0, 0, None, None, 0, 0) == sko.SKO_E_INVAL
     assert lib.sko_decode_step(None, 0, None, None, None) == sko.SKO_E_INVAL
     assert lib.sko_decode_step_static(None, 0, None, None, None) == sko.SKO_E_INVAL
+    assert lib.sko_decode_step_append(None, 0, None, None, None, None, None) == sko.SKO_E_INVAL
     buf = np.zeros(4, dtype=np.int32)
     assert lib.sko_read_step(None, 1, buf.ctypes.data, buf.nbytes) == sko.SKO_E_INVAL
     assert lib.sko_read_table(None, 0, 0, 1, buf.ctypes.data, buf.nbytes) == sko.SKO_E_INVAL
