@@ -360,6 +360,10 @@ def main() -> int:
                     help="miss-copy arrangement: early (the default: by extra blocks of the LRU-update launch), "
                          "late (after the LRU update), fused (inside the attention launch; one "
                          "position, at most 16 heads)")
+    ap.add_argument("--micro-batches", type=int, default=1,
+                    help="split the batch into this many handles on as many streams, kept off the copy XCD")
+    ap.add_argument("--xcd-split", action="store_true",
+                    help="keep the step's kernels off the copy blocks' XCD even with one micro-batch")
     ap.add_argument("--hit-overlap", action="store_true",
                     help="with the early copy: attend the resident rows on a side stream beside the copy launch, "
                          "the missed rows after it")
@@ -410,16 +414,30 @@ def main() -> int:
         flags |= sko.SKO_FLAG_INDEXER_C8
     if args.hit_overlap:
         flags |= sko.SKO_FLAG_HIT_OVERLAP
-    cfg = sko.make_config(num_layers=L, batch=B, max_tokens=w.capacity, num_heads=H, top_k=k,
-                          hot_slots=w.hot_slots, mtp_positions=D, flags=flags)
-    h = sko.SparseKVOffload(cfg, stream)
+    # Micro-batches: the batch is split into NMB contiguous groups of
+    # sequences, one handle and one stream each, every handle kept off the
+    # XCD of the copy blocks, so that one group's selection and attention run
+    # while another group's misses cross the host link.  Each layer-step
+    # issues every group's call for the layer before the next layer's.
+    nmb = max(1, min(args.micro_batches, B))
+    if nmb > 1 or args.xcd_split:
+        flags |= sko.SKO_FLAG_XCD_SPLIT
+    groups = [list(range(g * B // nmb, (g + 1) * B // nmb)) for g in range(nmb)]
+    streams = [stream] if nmb == 1 else [torch.cuda.Stream() for _ in range(nmb)]
+    hs = []
+    for g, seqs in enumerate(groups):
+        cfg = sko.make_config(num_layers=L, batch=len(seqs), max_tokens=w.capacity, num_heads=H, top_k=k,
+                              hot_slots=w.hot_slots, mtp_positions=D, flags=flags)
+        hs.append(sko.SparseKVOffload(cfg, streams[g]))
     chunk = 65536
-    for l in range(L):
-        for b in range(B):
-            n = w.seq_context(b)
-            for r0 in range(0, n, chunk):
-                m = min(chunk, n - r0)
-                h.append(l, b, w.index_rows(l, b, r0, m), w.kv_rows(l, b, r0, m))
+    for h, seqs in zip(hs, groups):
+        for l in range(L):
+            for j, b in enumerate(seqs):
+                n = w.seq_context(b)
+                for r0 in range(0, n, chunk):
+                    m = min(chunk, n - r0)
+                    h.append(l, j, w.index_rows(l, b, r0, m), w.kv_rows(l, b, r0, m))
+    torch.cuda.synchronize()
     log(f"prefix loaded: {L}x{B}x{w.context} tokens in {time.perf_counter() - t_setup:.1f}s")
 
     def dev(a):
@@ -428,64 +446,90 @@ def main() -> int:
     # per-step inputs, resident on the device before timing
     new_idx, new_kv, q_idx, q_attn = [], [], [], []
     qchains = {(l, b): w.index_queries(l, b, T) for l in range(L) for b in range(B)}
+    # [t][l][group]
     for t in range(T):
-        new_idx.append([dev(np.concatenate([w.index_rows(l, b, w.seq_context(b) + t, 1) for b in range(B)]))
-                        for l in range(L)])
-        new_kv.append([dev(np.concatenate([w.kv_rows(l, b, w.seq_context(b) + t, 1) for b in range(B)]))
+        new_idx.append([[dev(np.concatenate([w.index_rows(l, b, w.seq_context(b) + t, 1) for b in seqs]))
+                         for seqs in groups] for l in range(L)])
+        new_kv.append([[dev(np.concatenate([w.kv_rows(l, b, w.seq_context(b) + t, 1) for b in seqs]))
+                        for seqs in groups] for l in range(L)])
+        q_idx.append([[dev(np.stack([qchains[(l, b)][t] for b in seqs])) for seqs in groups] for l in range(L)])
+        q_attn.append([[dev(np.stack([w.attn_queries(l, b, t) for b in seqs])) for seqs in groups]
                        for l in range(L)])
-        q_idx.append([dev(np.stack([qchains[(l, b)][t] for b in range(B)])) for l in range(L)])
-        q_attn.append([dev(np.stack([w.attn_queries(l, b, t) for b in range(B)])) for l in range(L)])
-    out = torch.empty((B, D, H, synth.V_DIM), dtype=torch.float32, device="cuda")
+    outs = [torch.empty((len(seqs), D, H, synth.V_DIM), dtype=torch.float32, device="cuda") for seqs in groups]
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t_setup:.1f}s")
 
     def run_step(t):
         for l in range(L):
-            if args.append == "fused":
-                # the new token's rows go in with the decode call (one launch
-                # fewer per layer-step; same results as the two calls)
-                sko.sko_decode_step_append(h.handle, l, new_idx[t][l], new_kv[t][l], q_idx[t][l], q_attn[t][l],
-                                           out)
-            else:
-                sko.sko_append_token(h.handle, l, sko.SKO_ALL_SEQS, new_idx[t][l], new_kv[t][l], 1, True)
-                sko.sko_decode_step(h.handle, l, q_idx[t][l], q_attn[t][l], out)
+            for g, h in enumerate(hs):
+                if args.append == "fused":
+                    # the new token's rows go in with the decode call (one
+                    # launch fewer per layer-step; same results as the two calls)
+                    sko.sko_decode_step_append(h.handle, l, new_idx[t][l][g], new_kv[t][l][g], q_idx[t][l][g],
+                                               q_attn[t][l][g], outs[g])
+                else:
+                    sko.sko_append_token(h.handle, l, sko.SKO_ALL_SEQS, new_idx[t][l][g], new_kv[t][l][g], 1, True)
+                    sko.sko_decode_step(h.handle, l, q_idx[t][l][g], q_attn[t][l][g], outs[g])
+
+    def all_stats():
+        # per (group, layer); the counters are summed over both
+        return [h.stats(l) for h in hs for l in range(L)]
+
+    def set_timing(mask):
+        for h in hs:
+            h.set_timing(mask)
+
+    def merged_timing():
+        m = {}
+        for h in hs:
+            for name, (ms, c) in h.timing().items():
+                a = m.get(name, (0.0, 0))
+                m[name] = (a[0] + ms, a[1] + c)
+        return m
+
+    def merged_overlap():
+        m = None
+        for h in hs:
+            o = h.copy_overlap()
+            m = dict(o) if m is None else {key: m[key] + o[key] for key in m}
+        return m
 
     # Warm-up: the cold step untimed, then the remaining warm-up steps with
     # every stage bracketed by events (the per-stage breakdown; each event
     # pair costs device time, so the timed steps bracket only one stage).
     nstage = sko.sko_num_stages()
-    stats_cold0 = [h.stats(l) for l in range(L)]
+    stats_cold0 = all_stats()
     torch.cuda.synchronize()
     t_cold = time.perf_counter()
     run_step(0)
     torch.cuda.synchronize()
     t_cold = time.perf_counter() - t_cold
-    calib_stats0 = [h.stats(l) for l in range(L)]
-    h.set_timing(0 if args.no_timing else (1 << nstage) - 1)
+    calib_stats0 = all_stats()
+    set_timing(0 if args.no_timing else (1 << nstage) - 1)
     for t in range(1, args.warmup):
         run_step(t)
     torch.cuda.synchronize()
-    calib = h.timing() if (not args.no_timing and args.warmup > 1) else {}
-    stats0 = [h.stats(l) for l in range(L)]
+    calib = merged_timing() if (not args.no_timing and args.warmup > 1) else {}
+    stats0 = all_stats()
     calib_steps = args.warmup - 1
 
     dominant = None
     if calib:
         dominant = max(calib.items(), key=lambda kv: kv[1][0])[0]
     timed_mask = 0 if dominant is None else (1 << sko.sko_stage_index(dominant))
-    h.set_timing(timed_mask)
+    set_timing(timed_mask)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for t in range(args.warmup, T):
         run_step(t)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    timing = h.timing() if timed_mask else {}
+    timing = merged_timing() if timed_mask else {}
     # block stamps of the timed LRU-update launches (early copy): how long the
     # copy blocks ran beside the LRU update
-    overlap = h.copy_overlap() if timed_mask else None
-    h.set_timing(0)
-    stats1 = [h.stats(l) for l in range(L)]
+    overlap = merged_overlap() if timed_mask else None
+    set_timing(0)
+    stats1 = all_stats()
 
     K = args.steps
     layer_steps = L * K
@@ -506,16 +550,17 @@ def main() -> int:
         into the row its slot takes over, and the attention reads the
         winners' rows."""
         avg_lt = w.context + first_step + (nsteps + 1) / 2.0  # tokens present after each append
-        ls = L * nsteps
+        ls = L * nsteps * nmb  # launches of each kernel (one per group and layer-step)
         per = h2d_bytes / ls if ls else 0.0
+        Bg = B / nmb  # sequences per launch
         copy = (per, "host-link", HOST_LINK_PEAK_GBPS)
         # the query rows are read as bf16 in both modes
         idx_row = IDX_ROW_C8 if args.indexer == "c8" else IDX_ROW
-        m = {"score_hist": (idx_row * B * avg_lt + IDX_ROW * B * D, "hbm", HBM_PEAK_GBPS)}
+        m = {"score_hist": (idx_row * Bg * avg_lt + IDX_ROW * Bg * D, "hbm", HBM_PEAK_GBPS)}
         if mode == "fused":
             m["attn_partial"] = copy
             return m
-        attn = KV_ROW * B * D * min(k, avg_lt)
+        attn = KV_ROW * Bg * D * min(k, avg_lt)
         if mode == "early":
             m["merge_lru"] = copy  # its copy blocks read the missed rows from the host
         else:
@@ -541,12 +586,16 @@ def main() -> int:
     hbm_copy = measure_hbm_copy(torch)
     calibration_copy(torch)
 
+    # the counter summary of this configuration under profiles/
+    profile_name = (w.name + ("_c8" if args.indexer == "c8" else "") + (f"_mb{nmb}" if nmb > 1 else "")
+                    + ("_xcd" if nmb == 1 and args.xcd_split else ""))
+
     def roof_entry(name, ms, n, model):
         nbytes, bound, peak = model[name]
         avg = ms / n
         ach = nbytes / (avg * 1e-3) / 1e9 if avg > 0 else 0.0
         e = {"bound": bound, "achieved": round(ach, 2), "peak": round(peak, 2), "unit": "GB/s",
-             "frac": round(ach / peak, 4), "traffic": traffic_for(name, w.name + ("_c8" if args.indexer == "c8" else "")), "kernel": name,
+             "frac": round(ach / peak, 4), "traffic": traffic_for(name, profile_name), "kernel": name,
              "avg_ms": round(avg, 5), "launches": n, "bytes_per_launch": int(nbytes)}
         if bound == "host-link":
             e["measured_ceiling"] = round(h2d_ceiling, 2)
@@ -593,7 +642,8 @@ def main() -> int:
                    "top_k": k, "hot_slots": w.hot_slots, "mtp_positions": D, "heads": H,
                    "parallelism": "none (1 GPU)", "pool": args.pool, "copy": args.copy,
                    "hit_overlap": bool(args.hit_overlap), "append": args.append,
-                   "indexer": args.indexer},
+                   "indexer": args.indexer, "micro_batches": nmb,
+                   "xcd_split": bool(flags & sko.SKO_FLAG_XCD_SPLIT)},
         "tokens_per_s": round(B * K / elapsed, 2),
         "indexer_scan_GBps": rooflines.get("score_hist", {}).get("achieved"),
         "miss_gather_GBps": next((e["achieved"] for e in [roof or {}] + list(rooflines.values())
@@ -647,7 +697,8 @@ def main() -> int:
                               f"event-timed; the timed steps bracket only '{dominant}'")
         if calib else None,
     }
-    h.close()
+    for h in hs:
+        h.close()
     del new_idx, new_kv, q_idx, q_attn
     if cpu_base is not None:
         result["cpu_baseline"] = cpu_base

@@ -117,6 +117,21 @@ extern "C" {
  * for sequence 0 at every step while doing its normal work, so that the
  * reporting path below can be exercised without a real fault. */
 #define SKO_FLAG_TEST_VIOLATION 0x200u
+/* Kept off one XCD (for two or more handles whose steps overlap, each on its
+ * own stream, e.g. the two halves of a batch): the copy blocks of the
+ * LRU-update launch run only on XCD 0, one block per CU, and every other
+ * block of the decode step runs on the other seven XCDs.  A kernel's HBM
+ * loads on a CU that also has host reads in flight wait behind them (the
+ * kernel takes several times as long), so only with the host reads on CUs
+ * of their own can one handle's selection and attention run while another
+ * handle's misses cross the host link ([FO] decode paragraphs: miss loads
+ * overlapped with the other work of the step).  Results are those of the
+ * default early copy, bit for bit.  sko_create checks that the device deals
+ * the blocks of a launch to 8 XCDs in a fixed stripe (block i on XCD
+ * (i + o) mod 8) and fails with SKO_E_UNSUPPORTED otherwise; SKO_E_INVAL
+ * with SKO_FLAG_FUSED_COPY, SKO_FLAG_LATE_COPY or SKO_FLAG_HIT_OVERLAP.
+ * sko_append_token's own launch is not kept off XCD 0. */
+#define SKO_FLAG_XCD_SPLIT 0x400u
 
 typedef struct sko_handle sko_handle;
 

@@ -41,6 +41,7 @@ SKO_FLAG_EARLY_COPY = 0x40
 SKO_FLAG_INDEXER_C8 = 0x80
 SKO_FLAG_HIT_OVERLAP = 0x100
 SKO_FLAG_TEST_VIOLATION = 0x200
+SKO_FLAG_XCD_SPLIT = 0x400
 
 SKO_BUF_TOPK, SKO_BUF_PHYS, SKO_BUF_COUNTS = 1, 2, 3
 SKO_BUF_MISSES, SKO_BUF_VICTIMS, SKO_BUF_EVICT_OLD, SKO_BUF_KEYS = 4, 5, 6, 7

@@ -199,14 +199,17 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     const int32_t* __restrict__ ntok_layer, float* __restrict__ part_acc, float* __restrict__ part_ml,
     int32_t* __restrict__ phys, const int32_t* __restrict__ wrow, uint32_t* __restrict__ miss_bits, int64_t wpr,
     int D, int H, int HG, int top_k, int S, int R, int64_t cap, int rows_per_block, int nchunk, int pchunks,
-    float scale_log2) {
+    float scale_log2, int nbp, int xc) {
     __shared__ uint4 rows[kAttnTileRows * kRowStrideU4];
     __shared__ int32_t slot_s[kAttnMaxRowsPerBlock];  // row read, relative to the sequence's hot rows
     __shared__ int32_t cp_s[kAttnMaxRowsPerBlock];    // fused copy: pool token of a missed row, else -1
     __shared__ f32x4_t sp[4][2][64];  // per-wave partial S^T tiles
     __shared__ int scratch[256 / 64 + 1];
 
-    const int chunk = blockIdx.x, bp = blockIdx.y, hg = blockIdx.z;
+    // work block (chunk, bp, hg), chunk fastest
+    const int wk = split_block(blockIdx.x, xc);
+    if (wk < 0 || wk >= nchunk * nbp * HG) return;  // block-uniform
+    const int chunk = wk % nchunk, bp = (wk / nchunk) % nbp, hg = wk / (nchunk * nbp);
     const int b = bp / D;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15, g = lane >> 4;
@@ -428,10 +431,13 @@ constexpr int kMaxChunks = 1024;
 __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* __restrict__ part_acc,
                                                                   const float* __restrict__ part_ml,
                                                                   float* __restrict__ out, int H,
-                                                                  int HG, int nchunk) {
+                                                                  int HG, int nchunk, int nbph, int xc) {
     __shared__ float wgt[kMaxChunks];
     __shared__ float red[2 * kCombineThreads / 64];
-    const int bph = blockIdx.x;
+    // work block (bph, column block), bph fastest
+    const int wk = split_block(blockIdx.x, xc);
+    if (wk < 0 || wk >= nbph * (kVDim / kCombineThreads)) return;  // block-uniform
+    const int bph = wk % nbph, cblk = wk / nbph;
     const int bp = bph / H, h = bph - bp * H;
     const int hg = h / kAttnHeadGroup, hl = h - hg * kAttnHeadGroup;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -471,7 +477,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* _
     if (lane == 0) red[2 + wid] = lsum;
     __syncthreads();
     const float L = red[2] + red[3];
-    const int col = blockIdx.y * kCombineThreads + tid;
+    const int col = cblk * kCombineThreads + tid;
     const float* __restrict__ src = part_acc + (pbase * kAttnHeadGroup + hl) * kVDim + col;
     const size_t cstride = (size_t)kAttnHeadGroup * kVDim;
     float acc = 0.0f;
@@ -494,18 +500,19 @@ hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_
                                const uint16_t* pool_layer, const uint16_t* recent_layer, const int32_t* ntok_layer,
                                float* part_acc, float* part_ml, int32_t* phys, int B, int D, int H, int top_k, int S,
                                int64_t cap, int rows_per_block, float scale, const int32_t* wrow,
-                               uint32_t* miss_bits, int phase) {
+                               uint32_t* miss_bits, int phase, int xc) {
     const int HG = (H + kAttnHeadGroup - 1) / kAttnHeadGroup;
     const int nchunk = (top_k + rows_per_block - 1) / rows_per_block;
     const int pchunks = phase == 0 ? nchunk : 2 * nchunk;
     const float scale_log2 = scale * 1.4426950408889634f;
 #define SKO_ATTN_LAUNCH(W, P)                                                                                 \
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_attn_partial<W, P>), dim3(nchunk, B * D, HG), dim3(256), 0, st, topk,     \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_attn_partial<W, P>), dim3(split_grid((int64_t)nchunk * B * D * HG, xc)), \
+                       dim3(256), 0, st, topk,                                                                   \
                        cache_slots_layer, slot_row_layer, reinterpret_cast<uint4*>(hot_layer),                   \
                        reinterpret_cast<const uint4*>(q_attn), reinterpret_cast<const uint4*>(pool_layer),       \
                        reinterpret_cast<const uint4*>(recent_layer), ntok_layer, part_acc, part_ml, phys, wrow,  \
                        miss_bits, winner_words(cap), D, H, HG, top_k, S, R, cap, rows_per_block, nchunk, pchunks, \
-                       scale_log2)
+                       scale_log2, B * D, xc)
     if (pool_layer != nullptr && wrow != nullptr) return hipErrorInvalidValue;
     if (phase == 1) {
         // the rows resident at step start: no copy of any kind
@@ -544,11 +551,12 @@ hipError_t launch_gather_slots(hipStream_t st, const uint16_t* hot_seq, const in
 }
 
 hipError_t launch_attn_combine(hipStream_t st, const float* part_acc, const float* part_ml,
-                               float* out, int B, int D, int H, int nchunk) {
+                               float* out, int B, int D, int H, int nchunk, int xc) {
     const int HG = (H + kAttnHeadGroup - 1) / kAttnHeadGroup;
     if (nchunk > kMaxChunks) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_attn_combine, dim3(B * D * H, kVDim / kCombineThreads), dim3(kCombineThreads), 0,
-                       st, part_acc, part_ml, out, H, HG, nchunk);
+    const int nbph = B * D * H;
+    hipLaunchKernelGGL(k_attn_combine, dim3(split_grid((int64_t)nbph * (kVDim / kCombineThreads), xc)),
+                       dim3(kCombineThreads), 0, st, part_acc, part_ml, out, H, HG, nchunk, nbph, xc);
     return hipGetLastError();
 }
 

@@ -234,8 +234,12 @@ __device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, con
     // misses before this part (copy_words is a multiple of 4 and rows are
     // 16-byte aligned, so the count reads whole 16-byte words)
     const int64_t w_begin = (int64_t)part * copy_words;
+    // no bit is set at or past the sequence's token count (a part may begin
+    // there), and the bitmap row holds at least that many words rounded up
+    // to 4
+    const int64_t w_count = std::min(w_begin, words_now);
     int before = 0;
-    for (int64_t q = threadIdx.x; 4 * q < w_begin; q += kLruThreads) {
+    for (int64_t q = threadIdx.x; 4 * q < w_count; q += kLruThreads) {
         const uint4 v = reinterpret_cast<const uint4*>(mb)[q];
         before += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
     }
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     uint32_t* __restrict__ miss_bits, const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
     uint4* __restrict__ hot_layer, int32_t* __restrict__ slot_row_layer, int32_t* __restrict__ spare_layer, int R,
     int32_t* __restrict__ wrow, int32_t* __restrict__ phys, int sort_winners,
-    int test_violation, uint64_t* __restrict__ stamps, uint4* __restrict__ pool_newest) {
+    int test_violation, uint64_t* __restrict__ stamps, uint4* __restrict__ pool_newest, int ncopy, int xc) {
     // instrumentation (stamps != nullptr): each block records when it
     // started and ended on the chip's constant-rate clock, so the host can
     // tell how long the copy blocks ran beside the LRU update
@@ -310,19 +314,34 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     int32_t* vlist = lists + kMaxMerge;
     uint2* cstage = reinterpret_cast<uint2*>(lists);
 
-    if ((int)blockIdx.x >= nseq) {
-        copy_block((int)blockIdx.x - nseq, copy_per_seq, copy_words, miss_bits, pool_layer, recent_layer,
+    // the block's part: merge block rb < nseq, or copy block rb - nseq.  Kept
+    // off XCD xc (xc >= 0), the copy blocks are the launch's blocks on XCD
+    // xc (copy block i / 8 for block i) and the merge blocks are work blocks
+    // of the other XCDs, so the host reads never share a CU or an XCD with
+    // other kernels' HBM accesses
+    int rb = blockIdx.x;
+    if (xc >= 0) {
+        if (xcc_id() == xc) {
+            rb = (int)(blockIdx.x >> 3) < ncopy ? nseq + (int)(blockIdx.x >> 3) : -1;
+        } else {
+            rb = split_block(blockIdx.x, xc);
+            if (rb >= nseq) rb = -1;
+        }
+        if (rb < 0) return;  // block-uniform
+    }
+    if (rb >= nseq) {
+        copy_block(rb - nseq, copy_per_seq, copy_words, miss_bits, pool_layer, recent_layer,
                    hot_layer, spare_layer, t & 1, R, ntok_layer, cap, wpr, D * top_k, lists, scratch);
         if (stamps) {
             __syncthreads();
             if (threadIdx.x == 0) {
-                stamps[2 * blockIdx.x] = t_start;
-                stamps[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+                stamps[2 * rb] = t_start;
+                stamps[2 * rb + 1] = __builtin_amdgcn_s_memrealtime();
             }
         }
         return;
     }
-    const int b = blockIdx.x;
+    const int b = rb;
     const int tid = threadIdx.x;
     const int64_t Lt = ntok_layer[b];
     // the fused append: the newest token's row, which the score launch put in
@@ -663,17 +682,26 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     if (stamps) {
         __syncthreads();
         if (tid == 0) {
-            stamps[2 * blockIdx.x] = t_start;
-            stamps[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+            stamps[2 * b] = t_start;
+            stamps[2 * b + 1] = __builtin_amdgcn_s_memrealtime();
         }
     }
 }
 
-void copy_shape(int B, int64_t max_tokens_now, int* copy_per_seq, int* copy_words) {
+void copy_shape(int B, int64_t max_tokens_now, int* copy_per_seq, int* copy_words, int xcd_cus) {
     const int64_t words = std::max<int64_t>(1, (max_tokens_now + 31) / 32);
-    const int64_t max_words =
-        std::min<int64_t>(kLruThreads, std::max<int64_t>(32, (B * words + kCopyBlocks - 1) / kCopyBlocks));
-    *copy_per_seq = (int)((words + max_words - 1) / max_words);
+    if (xcd_cus > 0) {
+        // the copy blocks of one XCD: about one per CU (a copy block holds a
+        // CU's LDS), each part at most kLruThreads words and, unless that
+        // forces more, at least 32
+        *copy_per_seq = (int)std::max<int64_t>(
+            (words + kLruThreads - 1) / kLruThreads,
+            std::min<int64_t>((xcd_cus + B - 1) / B, (words + 31) / 32));
+    } else {
+        const int64_t max_words =
+            std::min<int64_t>(kLruThreads, std::max<int64_t>(32, (B * words + kCopyBlocks - 1) / kCopyBlocks));
+        *copy_per_seq = (int)((words + max_words - 1) / max_words);
+    }
     // equal parts (a remainder part would hold few tokens and leave its
     // block nearly idle while the others carry its share)
     *copy_words = (int)(((words + *copy_per_seq - 1) / *copy_per_seq + 3) / 4 * 4);
@@ -691,22 +719,28 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             uint16_t* hot_layer, int32_t* slot_row_layer, int32_t* spare_layer, int R,
                             int32_t* wrow, int32_t* phys, bool sort_winners,
                             int64_t max_tokens_now, bool test_violation, uint64_t* stamps,
-                            uint16_t* pool_newest) {
+                            uint16_t* pool_newest, int xc, int xcd_cus) {
     const int64_t C = ring_capacity(S, D, top_k);
     const int64_t wpr = winner_words(cap);
     // B merge blocks, then (early copy) B * copy_per_seq copy blocks of
     // copy_words bitmap words each (a multiple of 4), about kCopyBlocks in all
     int copy_per_seq = 0, copy_words = 0;
-    copy_shape(B, max_tokens_now, &copy_per_seq, &copy_words);
+    copy_shape(B, max_tokens_now, &copy_per_seq, &copy_words, xc >= 0 ? xcd_cus : 0);
     if (!miss_bits) copy_per_seq = 0;
-    hipLaunchKernelGGL(k_merge_lru, dim3(B + B * copy_per_seq), dim3(kLruThreads), 0, st, winners, hist, meta, cand, topk,
+    const int ncopy = B * copy_per_seq;
+    // kept off XCD xc: the copy blocks are the blocks on it, one per group
+    // of 8, and the merge blocks are work blocks of the other seven
+    const unsigned grid = xc < 0 ? (unsigned)(B + ncopy)
+                                 : (unsigned)(kXcds * std::max<int64_t>(ncopy, (B + kXcds - 2) / (kXcds - 1)));
+    hipLaunchKernelGGL(k_merge_lru, dim3(grid), dim3(kLruThreads), 0, st, winners, hist, meta, cand, topk,
                        ntok_layer, cache_slots_layer, slot_token_layer, last_use_layer, ring0_layer,
                        ring1_layer, pos_layer, ring_state_layer, D, top_k, S, C, cap, wpr, t, misses, victims,
                        evict_old, counts, glist, layer_stats, do_refine ? 1 : 0, B, copy_per_seq, copy_words,
                        miss_bits,
                        reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<const uint4*>(recent_layer),
                        reinterpret_cast<uint4*>(hot_layer), slot_row_layer, spare_layer, R, wrow, phys,
-                       sort_winners ? 1 : 0, test_violation ? 1 : 0, stamps, reinterpret_cast<uint4*>(pool_newest));
+                       sort_winners ? 1 : 0, test_violation ? 1 : 0, stamps, reinterpret_cast<uint4*>(pool_newest),
+                       ncopy, xc);
     return hipGetLastError();
 }
 
@@ -729,13 +763,15 @@ __global__ __launch_bounds__(kRefineThreads) void k_topk_refine(RowMeta* __restr
                                                                 int32_t* __restrict__ topk,
                                                                 uint32_t* __restrict__ winners,
                                                                 uint32_t* __restrict__ miss_bits, int D,
-                                                                int top_k, int64_t cap, int64_t wpr) {
+                                                                int top_k, int64_t cap, int64_t wpr, int nrows,
+                                                                int xc) {
     __shared__ uint2 sg[kRefineStage];
     __shared__ uint32_t hg[256];
     __shared__ uint64_t s_prefix, s_T;
     __shared__ int s_rem, s_done;
     __shared__ int scratch[kRefineThreads / 64 + 1];
-    const int row = blockIdx.x;
+    const int row = split_block(blockIdx.x, xc);
+    if (row < 0 || row >= nrows) return;  // block-uniform
     const int b = row / D;
     const int tid = threadIdx.x, lane = tid & 63;
     const uint2* __restrict__ cg = cand + (size_t)row * cap;
@@ -851,9 +887,9 @@ __global__ __launch_bounds__(kRefineThreads) void k_topk_refine(RowMeta* __restr
 }
 
 hipError_t launch_topk_refine(hipStream_t st, RowMeta* meta, const uint2* cand, int32_t* topk, uint32_t* winners,
-                              uint32_t* miss_bits, int B, int D, int top_k, int64_t cap) {
-    hipLaunchKernelGGL(k_topk_refine, dim3(B * D), dim3(kRefineThreads), 0, st, meta, cand, topk, winners,
-                       miss_bits, D, top_k, cap, winner_words(cap));
+                              uint32_t* miss_bits, int B, int D, int top_k, int64_t cap, int xc) {
+    hipLaunchKernelGGL(k_topk_refine, dim3(split_grid(B * D, xc)), dim3(kRefineThreads), 0, st, meta, cand, topk,
+                       winners, miss_bits, D, top_k, cap, winner_words(cap), B * D, xc);
     return hipGetLastError();
 }
 

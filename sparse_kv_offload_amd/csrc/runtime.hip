@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "../../include/sko.h"
+#include "sko_common.h"
 #include "sko_internal.h"
 
 using namespace sko;
@@ -160,6 +161,10 @@ struct sko_handle {
     float* part_ml = nullptr;       // [B*D][HG][nchunk][16][2]
     int rows_per_block = 32, nchunk = 1;
     int cu_count = 256;  // compute units of the device (launch sizing)
+    // SKO_FLAG_XCD_SPLIT: the XCD of the copy blocks (every other block of
+    // the step stays off it) and its CUs; -1 / 0 without the flag
+    int xc = -1;
+    int xcd_cus = 0;
     int last_layer = -1;
 
     // timing
@@ -346,7 +351,7 @@ int validate_config(const sko_config* c) {
     if ((c->flags & ~(SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT | SKO_FLAG_KEEP_KEYS |
                       SKO_FLAG_SELECT_RESCAN | SKO_FLAG_FUSED_COPY | SKO_FLAG_LATE_COPY |
                       SKO_FLAG_EARLY_COPY | SKO_FLAG_INDEXER_C8 | SKO_FLAG_HIT_OVERLAP |
-                      SKO_FLAG_TEST_VIOLATION)) != 0 ||
+                      SKO_FLAG_TEST_VIOLATION | SKO_FLAG_XCD_SPLIT)) != 0 ||
         (c->flags & (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT)) ==
             (SKO_FLAG_POOL_COHERENT | SKO_FLAG_POOL_NONCOHERENT))
         return set_err(SKO_E_INVAL, "unknown or conflicting flags 0x%x", c->flags);
@@ -359,6 +364,9 @@ int validate_config(const sko_config* c) {
                            kAttnHeadGroup);
         if ((c->flags & SKO_FLAG_HIT_OVERLAP) && (modes & (SKO_FLAG_FUSED_COPY | SKO_FLAG_LATE_COPY)))
             return set_err(SKO_E_INVAL, "SKO_FLAG_HIT_OVERLAP needs the early copy");
+        if ((c->flags & SKO_FLAG_XCD_SPLIT) &&
+            ((modes & (SKO_FLAG_FUSED_COPY | SKO_FLAG_LATE_COPY)) || (c->flags & SKO_FLAG_HIT_OVERLAP)))
+            return set_err(SKO_E_INVAL, "SKO_FLAG_XCD_SPLIT needs the early copy without SKO_FLAG_HIT_OVERLAP");
     }
     if (c->device < 0) return set_err(SKO_E_INVAL, "device must be >= 0");
     if (c->hot_slots > kMaxHotSlots)
@@ -477,7 +485,7 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
     if ((rc = run_stage(h, ST_SCORE, [&] {
              return launch_score_hist(h->stream, idx_layer, qi, ntok_in, h->keys, sc.hist, floor_layer, sc.pre,
                                       sc.meta, cs, B, D, h->kcap, cap, h->ntiles, max_now, h->cu_count, scale_layer,
-                                      sc.qc8, app);
+                                      sc.qc8, app, h->xc);
          })))
         return rc;
     const bool fused_copy = h->fused_copy;
@@ -486,14 +494,14 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
              return launch_topk_filter(h->stream, sc.hist, sc.meta, sc.pre, sc.cand, h->topk, cs, ntok, sc.winners,
                                        staged ? sc.miss_bits : nullptr, idx_layer, qi, floor_layer,
                                        (h->cfg.flags & SKO_FLAG_SELECT_RESCAN) != 0, B, D, cap, h->ntiles, k,
-                                       max_now, scale_layer, h->c8 ? sc.qc8 : nullptr);
+                                       max_now, scale_layer, h->c8 ? sc.qc8 : nullptr, h->xc);
          })))
         return rc;
     if (staged && (rc = run_stage(h, ST_REFINE, [&] {
                        // the split buckets first, so that the miss set is complete
                        // when the merge launch starts copying
                        return launch_topk_refine(h->stream, sc.meta, sc.cand, h->topk, sc.winners, sc.miss_bits, B,
-                                                 D, k, cap);
+                                                 D, k, cap, h->xc);
                    })))
         return rc;
     // split attention: the selection is complete, so the rows resident at
@@ -510,7 +518,7 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
     if (staged && h->stamps && ((h->timing_mask >> ST_MERGE_LRU) & 1u) &&
         (int)h->stamp_pending.size() < kStampLaunches) {
         int cps = 0, cw = 0;
-        copy_shape(B, max_now, &cps, &cw);
+        copy_shape(B, max_now, &cps, &cw, h->xcd_cus);
         // the record holds stamp_blocks blocks (the launch at full capacity);
         // a launch with more blocks is not recorded
         if (B + B * cps <= h->stamp_blocks) {
@@ -527,7 +535,7 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
                                      slot_row_layer, spare_layer, R, fused_copy ? nullptr : sc.wrow, h->phys,
                                      /* the split attention reads the lists during this launch */ !h->hit_overlap,
                                      max_now, (h->cfg.flags & SKO_FLAG_TEST_VIOLATION) != 0, stamps,
-                                     fused_append ? h->pool_dev + LBc * kKvDim : nullptr);
+                                     fused_append ? h->pool_dev + LBc * kKvDim : nullptr, h->xc, h->xcd_cus);
          })))
         return rc;
     // late copy: its own gather from the pool into the misses' rows; early:
@@ -556,7 +564,7 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
                                         fused_copy ? pool_layer : nullptr, recent_layer, ntok, sc.part_acc,
                                         sc.part_ml, h->phys, B, D, H, k, S, cap, h->rows_per_block,
                                         h->cfg.attn_scale, fused_copy ? nullptr : sc.wrow,
-                                        staged ? sc.miss_bits : nullptr, split ? 2 : 0);
+                                        staged ? sc.miss_bits : nullptr, split ? 2 : 0, h->xc);
          })))
         return rc;
     if (split) {
@@ -565,7 +573,7 @@ int decode_step_impl(sko_handle* h, int32_t layer, const void* q_idx, const void
     }
     if ((rc = run_stage(h, ST_COMBINE, [&] {
              return launch_attn_combine(h->stream, sc.part_acc, sc.part_ml, out, B, D, H,
-                                        h->nchunk * (split ? 2 : 1));
+                                        h->nchunk * (split ? 2 : 1), h->xc);
          })))
         return rc;
     h->step[layer] += 1;
@@ -651,6 +659,52 @@ size_t layout_step_scratch(const sko_handle* h, unsigned char* base, StepScratch
     return off;
 }
 
+// The XCD each block of a launch runs on (HW_REG_XCC_ID), for the check of
+// SKO_FLAG_XCD_SPLIT at creation.
+__global__ __launch_bounds__(64) void k_xcc_of_blocks(int32_t* __restrict__ out) {
+    if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
+}
+
+// True when launches on `st` deal their blocks to the 8 XCDs in a fixed
+// stripe: block i on XCD (i + o) mod 8 with one o per launch, every XCD
+// taking part.  Launch sizes that are and are not multiples of 8.
+bool xcd_stripe_holds(hipStream_t st) {
+    const int sizes[] = {256, 61, 1000, 8};
+    int total = 0;
+    for (int n : sizes) total += n;
+    int32_t* d = nullptr;
+    if (hipMalloc((void**)&d, (size_t)total * 4) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    bool ok = true;
+    int off = 0;
+    for (int n : sizes) {
+        hipLaunchKernelGGL(k_xcc_of_blocks, dim3(n), dim3(64), 0, st, d + off);
+        if (hipGetLastError() != hipSuccess) ok = false;
+        off += n;
+    }
+    std::vector<int32_t> x(total, -1);
+    if (ok && hipMemcpyAsync(x.data(), d, (size_t)total * 4, hipMemcpyDeviceToHost, st) != hipSuccess) ok = false;
+    if (ok && hipStreamSynchronize(st) != hipSuccess) ok = false;
+    (void)hipFree(d);
+    (void)hipGetLastError();
+    off = 0;
+    for (int n : sizes) {
+        if (!ok) break;
+        const int o = (x[off] % kXcds + kXcds) % kXcds;
+        unsigned seen = 0;
+        for (int i = 0; i < n; ++i) {
+            const int v = x[off + i];
+            if (v < 0 || v >= kXcds || ((v - i) % kXcds + kXcds) % kXcds != o) ok = false;
+            else seen |= 1u << v;
+        }
+        if (n >= kXcds && seen != (1u << kXcds) - 1) ok = false;
+        off += n;
+    }
+    return ok;
+}
+
 // Clears the first nz words of `z` and sets the first nf words of `f` to all
 // ones (a kernel, not a memset, so the call can sit inside a captured graph).
 __global__ __launch_bounds__(256) void k_clear_scratch(uint32_t* __restrict__ z, int64_t nz,
@@ -721,6 +775,15 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     h->staged_copy = !h->fused_copy && !(cfg->flags & SKO_FLAG_LATE_COPY);
     h->c8 = (cfg->flags & SKO_FLAG_INDEXER_C8) != 0;
     h->hit_overlap = h->staged_copy && (cfg->flags & SKO_FLAG_HIT_OVERLAP) != 0;
+    if (cfg->flags & SKO_FLAG_XCD_SPLIT) {
+        if (h->cu_count % kXcds != 0 || !xcd_stripe_holds(h->stream)) {
+            delete h;
+            return set_err(SKO_E_UNSUPPORTED,
+                           "SKO_FLAG_XCD_SPLIT: the device does not deal launch blocks to 8 XCDs in a fixed stripe");
+        }
+        h->xc = 0;
+        h->xcd_cus = h->cu_count / kXcds;
+    }
     h->rows_per_block = attn_rows_per_block(h->k, h->B * h->D * h->HG);
     h->nchunk = (h->k + h->rows_per_block - 1) / h->rows_per_block;
     // the split attention writes the partials of both phases
@@ -787,7 +850,7 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
     ok = ok && dev_alloc(h, (void**)&h->part_ml, BD * h->HG * pchunks * kAttnHeadGroup * 2 * 4);
     if (h->staged_copy) {
         int cps = 0, cw = 0;
-        copy_shape(h->B, h->cap, &cps, &cw);
+        copy_shape(h->B, h->cap, &cps, &cw, h->xcd_cus);
         h->stamp_blocks = h->B + h->B * cps;
         ok = ok && dev_alloc(h, (void**)&h->stamps, (size_t)kStampLaunches * h->stamp_blocks * 2 * 8);
     }

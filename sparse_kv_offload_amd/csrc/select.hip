@@ -361,7 +361,7 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
     const int32_t* __restrict__ floor_layer, uint2* __restrict__ pre, RowMeta* __restrict__ meta,
     const int32_t* __restrict__ cache_slots_layer, int D, int p0, int64_t kcap, int64_t cap, int64_t ntiles,
     int64_t tiles_now, int64_t total_tiles, const uint16_t* __restrict__ scales_layer,
-    uint32_t* __restrict__ qc8, ScoreAppend app) {
+    uint32_t* __restrict__ qc8, ScoreAppend app, int nwork, int xc) {
     constexpr int nw = score_threads<NP>() / 64;
     constexpr int RU = C8 ? kIdxC8RowU4 : kIdxRowU4;  // 16-byte loads per token
     __shared__ uint32_t sh[NP * kHistBins];
@@ -379,8 +379,11 @@ __global__ __launch_bounds__(score_threads<NP>()) void k_score_hist(
     uint32_t* const snew = reinterpret_cast<uint32_t*>(snew4);
     const int add = app.idx != nullptr ? 1 : 0;  // tokens appended by this launch, per sequence
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t r_begin = (int64_t)blockIdx.x * total_tiles / gridDim.x;
-    const int64_t r_end = ((int64_t)blockIdx.x + 1) * total_tiles / gridDim.x;
+    // nwork work blocks, each a contiguous range of the (seq, tile) space
+    const int wb = split_block(blockIdx.x, xc);
+    if (wb < 0 || wb >= nwork) return;  // block-uniform
+    const int64_t r_begin = (int64_t)wb * total_tiles / nwork;
+    const int64_t r_end = ((int64_t)wb + 1) * total_tiles / nwork;
     // query terms of positions p0.. of row0's sequence, staged in LDS (the
     // caller synchronizes).  qbits: this thread's bf16 term (thread t holds
     // term t % 64 of position t / 64).  The int8 indexer quantizes each
@@ -736,7 +739,7 @@ hipError_t launch_score_hist(hipStream_t st, const void* idx_layer, const uint16
                              const int32_t* floor_layer, uint2* pre, RowMeta* meta,
                              const int32_t* cache_slots_layer, int B, int D, int64_t kcap, int64_t cap,
                              int64_t ntiles, int64_t max_tokens_now, int cu_count,
-                             const uint16_t* scales_layer, uint32_t* qc8, const ScoreAppend& app) {
+                             const uint16_t* scales_layer, uint32_t* qc8, const ScoreAppend& app, int xc) {
     const int64_t tiles_now = std::max<int64_t>(1, (max_tokens_now + kIdxTile - 1) / kIdxTile);
     const int64_t total = (int64_t)B * tiles_now;
     const uint4* kb = reinterpret_cast<const uint4*>(idx_layer);
@@ -749,17 +752,19 @@ hipError_t launch_score_hist(hipStream_t st, const void* idx_layer, const uint16
                                : (np == 1 ? score_blocks_per_cu<1, false>() : np == 2 ? score_blocks_per_cu<2, false>()
                                   : np == 3 ? score_blocks_per_cu<3, false>() : score_blocks_per_cu<4, false>());
         const int nw = (np == 1 ? score_threads<1>() : score_threads<4>()) / 64;
-        // one resident round of blocks, at least one tile per wave
-        int64_t nb = std::min<int64_t>((int64_t)cu_count * per_cu, (total + nw - 1) / nw);
+        // one resident round of blocks (on the CUs the launch may use), at
+        // least one tile per wave
+        const int64_t cus = xc < 0 ? cu_count : (int64_t)cu_count * (kXcds - 1) / kXcds;
+        int64_t nb = std::min<int64_t>(cus * per_cu, (total + nw - 1) / nw);
         nb = std::max<int64_t>(nb, 1);
-        const dim3 grid((unsigned)nb);
+        const dim3 grid(split_grid(nb, xc));
         // every launch scores the appended token; the first one writes it
         ScoreAppend ap = app;
         ap.write = (app.idx != nullptr && p0 == 0) ? 1 : 0;
 #define SKO_SCORE_LAUNCH1(N, K, C)                                                                         \
     hipLaunchKernelGGL(HIP_KERNEL_NAME(k_score_hist<N, K, C>), grid, dim3(score_threads<N>()), 0, st, kb, q,      \
                        ntok_layer, keys, hist, floor_layer, pre, meta, cache_slots_layer, D, p0, kcap, cap, ntiles, \
-                       tiles_now, total, scales_layer, qc8, ap)
+                       tiles_now, total, scales_layer, qc8, ap, (int)nb, xc)
 #define SKO_SCORE_LAUNCH(N)                                   \
     do {                                                      \
         if (scales_layer) {                                   \
@@ -814,11 +819,15 @@ __global__ __launch_bounds__(256) void k_topk_filter(
     const int32_t* __restrict__ ntok_layer, uint32_t* __restrict__ winners, uint32_t* __restrict__ miss_bits,
     const uint4* __restrict__ idx_layer, const uint32_t* __restrict__ q_idx, int32_t* __restrict__ floor_layer,
     int rescan_all, int D, int64_t cap, int64_t ntiles, int64_t wpr, int top_k,
-    const uint16_t* __restrict__ scales_layer, const uint32_t* __restrict__ qc8) {
+    const uint16_t* __restrict__ scales_layer, const uint32_t* __restrict__ qc8, int per_row, int nwork, int xc) {
     __shared__ int scratch[8];
     __shared__ int s_bw, s_bs, s_floor;
     __shared__ RowMeta s_res;
-    const int row = blockIdx.y;
+    // work block wk: block bx of row `row` (per_row blocks per row)
+    const int wk = split_block(blockIdx.x, xc);
+    if (wk < 0 || wk >= nwork) return;  // block-uniform
+    const int row = wk / per_row;
+    const int bx = wk - row * per_row;
     const int b = row / D;
     const int64_t Lt = ntok_layer[b];
     const int kk = (int)std::min<int64_t>(top_k, Lt);
@@ -829,7 +838,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(
     uint2 e0[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int64_t j = (int64_t)blockIdx.x * kFilterSpanC + 256 * u + threadIdx.x;
+        const int64_t j = (int64_t)bx * kFilterSpanC + 256 * u + threadIdx.x;
         e0[u] = pr[j < cap ? j : cap - 1];
     }
     const bool rescan = npre < kk;
@@ -837,10 +846,10 @@ __global__ __launch_bounds__(256) void k_topk_filter(
     const int span = rescan ? kFilterSpan : kFilterSpanC;
     // a block without items leaves at once (block 0 stays: it records the
     // threshold and the floor)
-    if (blockIdx.x != 0 && (int64_t)blockIdx.x * span >= n_items) return;
-    threshold_row(hist + (size_t)row * kHistBins, blockIdx.x == 0 ? meta + row : nullptr, kk, scratch, &s_res,
+    if (bx != 0 && (int64_t)bx * span >= n_items) return;
+    threshold_row(hist + (size_t)row * kHistBins, bx == 0 ? meta + row : nullptr, kk, scratch, &s_res,
                   &s_floor);
-    if (blockIdx.x == 0 && threadIdx.x == 0) floor_layer[row] = rescan_all ? kFloorRescanAll : s_floor;
+    if (bx == 0 && threadIdx.x == 0) floor_layer[row] = rescan_all ? kFloorRescanAll : s_floor;
     const RowMeta m = s_res;
     if (m.bucket < 0) return;
     const bool take_bucket = m.need == m.bucket_count;
@@ -850,7 +859,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(
     int32_t* __restrict__ w = topk + (size_t)row * top_k;
     uint2* __restrict__ cr = cand + (size_t)row * cap;
     const uint32_t* __restrict__ qrow = q_idx + (size_t)row * (kIdxDim / 2);
-    for (int64_t base = (int64_t)blockIdx.x * span; base < n_items; base += (int64_t)gridDim.x * span) {
+    for (int64_t base = (int64_t)bx * span; base < n_items; base += (int64_t)per_row * span) {
         uint32_t kv[kFilterKeysPerThread], tk[kFilterKeysPerThread];  // tk: packed winner value
         uint32_t wmask = 0, smask = 0;
         if (rescan) {
@@ -876,7 +885,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(
             for (int u = 0; u < 4; ++u) {
                 const int64_t j = base + 256 * u + threadIdx.x;
                 uint2 v = e0[u];
-                if (base != (int64_t)blockIdx.x * kFilterSpanC) v = pr[j < cap ? j : cap - 1];
+                if (base != (int64_t)bx * kFilterSpanC) v = pr[j < cap ? j : cap - 1];
                 kv[u] = v.x;
                 tk[u] = v.y;
                 if (j < n_items) {
@@ -918,7 +927,7 @@ hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* met
                               const int32_t* ntok_layer, uint32_t* winners, uint32_t* miss_bits,
                               const void* idx_layer, const uint16_t* q_idx, int32_t* floor_layer,
                               bool rescan_all, int B, int D, int64_t cap, int64_t ntiles, int top_k,
-                              int64_t max_tokens_now, const uint16_t* scales_layer, const uint32_t* qc8) {
+                              int64_t max_tokens_now, const uint16_t* scales_layer, const uint32_t* qc8, int xc) {
     const int64_t wpr = winner_words(cap);
     const int64_t now = std::max<int64_t>(1, max_tokens_now);
     // blocks per row: one per kFilterSpan tokens of the longest sequence
@@ -929,11 +938,12 @@ hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* met
     const int rows = B * D;
     int per_row = (int)std::min<int64_t>(32, std::max<int64_t>(4, (now + kFilterSpan - 1) / kFilterSpan));
     per_row = std::min(per_row, std::max(4, 1024 / std::max(rows, 1)));
-    const dim3 grid((unsigned)per_row, (unsigned)(B * D));
-    hipLaunchKernelGGL(k_topk_filter, grid, dim3(256), 0, st, hist, meta, pre, cand, topk, cache_slots_layer,
-                       ntok_layer, winners, miss_bits, reinterpret_cast<const uint4*>(idx_layer),
+    // one linear grid, block bx of row r at r * per_row + bx
+    const int nwork = per_row * rows;
+    hipLaunchKernelGGL(k_topk_filter, dim3(split_grid(nwork, xc)), dim3(256), 0, st, hist, meta, pre, cand, topk,
+                       cache_slots_layer, ntok_layer, winners, miss_bits, reinterpret_cast<const uint4*>(idx_layer),
                        reinterpret_cast<const uint32_t*>(q_idx), floor_layer, rescan_all ? 1 : 0, D, cap, ntiles,
-                       wpr, top_k, scales_layer, qc8);
+                       wpr, top_k, scales_layer, qc8, per_row, nwork, xc);
     return hipGetLastError();
 }
 

@@ -83,4 +83,35 @@ __device__ __forceinline__ uint32_t score_key(float s) {
     return (u & 0x80000000u) ? ~u : (u ^ 0x80000000u);
 }
 
+// ---- launches kept off one XCD ------------------------------------------
+// MI355X deals the blocks of a launch to its 8 XCDs in a fixed stripe:
+// block i (linear id, x fastest) runs on XCD (i + o) mod 8, with one offset
+// o per launch (the handle checks this at creation).  A launch that must
+// stay off XCD `xc` has 8 * ceil(n / 7) blocks for its n work blocks: the
+// blocks of the stripe slot that falls on XCD xc leave at once, and the
+// others take work blocks 0, 1, ... in order, 7 per group of 8.  xc < 0:
+// no split, block i is work block i.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcc_id() {
+    int v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(v));
+    return v;
+}
+
+// Work block of linear block `lin`, or -1 for a block on XCD xc.
+__device__ __forceinline__ int split_block(int lin, int xc) {
+    if (xc < 0) return lin;
+    const int x = xcc_id();
+    if (x == xc) return -1;
+    const int slot = lin & (kXcds - 1);
+    const int cslot = (xc - x + slot) & (kXcds - 1);  // the slot on XCD xc
+    return (lin >> 3) * (kXcds - 1) + ((slot - cslot - 1) & (kXcds - 1));
+}
+
+// Blocks of a launch of n work blocks (n >= 1).
+__host__ __device__ inline unsigned split_grid(int64_t n, int xc) {
+    return xc < 0 ? (unsigned)n : (unsigned)((n + kXcds - 2) / (kXcds - 1) * kXcds);
+}
+
 }  // namespace sko

@@ -130,7 +130,7 @@ hipError_t launch_score_hist(hipStream_t st, const void* idx_layer, const uint16
                              const int32_t* floor_layer, uint2* pre, RowMeta* meta,
                              const int32_t* cache_slots_layer, int B, int D, int64_t kcap, int64_t cap,
                              int64_t ntiles, int64_t max_tokens_now, int cu_count,
-                             const uint16_t* scales_layer, uint32_t* qc8, const ScoreAppend& app);
+                             const uint16_t* scales_layer, uint32_t* qc8, const ScoreAppend& app, int xc = -1);
 // Also sets floor_layer for the next step (kFloorRescanAll when rescan_all).
 // scales_layer / qc8 non-null: the int8 indexer (for the rescan path).
 hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* meta, const uint2* pre,
@@ -138,7 +138,8 @@ hipError_t launch_topk_filter(hipStream_t st, const uint32_t* hist, RowMeta* met
                               const int32_t* ntok_layer, uint32_t* winners, uint32_t* miss_bits,
                               const void* idx_layer, const uint16_t* q_idx, int32_t* floor_layer,
                               bool rescan_all, int B, int D, int64_t cap, int64_t ntiles, int top_k,
-                              int64_t max_tokens_now, const uint16_t* scales_layer, const uint32_t* qc8);
+                              int64_t max_tokens_now, const uint16_t* scales_layer, const uint32_t* qc8,
+                              int xc = -1);
 // Also finishes the top-k (split buckets) and clears the histograms and row
 // records for the next step.  pool_newest non-null (the fused append): the
 // merge block of each sequence also copies the newest token's main-KV row
@@ -156,10 +157,11 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             uint16_t* hot_layer, int32_t* slot_row_layer, int32_t* spare_layer, int R,
                             int32_t* wrow, int32_t* phys, bool sort_winners,
                             int64_t max_tokens_now, bool test_violation, uint64_t* stamps,
-                            uint16_t* pool_newest);
+                            uint16_t* pool_newest, int xc = -1, int xcd_cus = 0);
 // Copy blocks of the early copy: copy_per_seq per sequence, each owning
-// copy_words bitmap words (a multiple of 4, at most 1024).
-void copy_shape(int B, int64_t max_tokens_now, int* copy_per_seq, int* copy_words);
+// copy_words bitmap words (a multiple of 4, at most 1024).  xcd_cus > 0:
+// the copy blocks run on one XCD of xcd_cus CUs (at least one block per CU).
+void copy_shape(int B, int64_t max_tokens_now, int* copy_per_seq, int* copy_words, int xcd_cus = 0);
 // Physical hot rows: each (layer, seq) has R = S + D*k rows; slot s lives
 // in row slot_row[s], and the other D*k rows are spare, listed in
 // spare [2][D*k] (two generations, the step's one chosen by t & 1).  The
@@ -185,7 +187,7 @@ hipError_t launch_gather_misses(hipStream_t st, const GatherEntry* glist, const 
 // Resolves split threshold buckets, one row per block (for the early copy,
 // so that the miss bitmap is complete before the merge launch).
 hipError_t launch_topk_refine(hipStream_t st, RowMeta* meta, const uint2* cand, int32_t* topk, uint32_t* winners,
-                              uint32_t* miss_bits, int B, int D, int top_k, int64_t cap);
+                              uint32_t* miss_bits, int B, int D, int top_k, int64_t cap, int xc = -1);
 // The row each winner's attention reads: wrow non-null, the list the
 // LRU-update launch wrote (the misses' words of miss_bits [B][wpr] are then
 // cleared for the next step when miss_bits is non-null); otherwise
@@ -199,9 +201,9 @@ hipError_t launch_attn_partial(hipStream_t st, const int32_t* topk, const int32_
                                const uint16_t* pool_layer, const uint16_t* recent_layer, const int32_t* ntok_layer,
                                float* part_acc, float* part_ml, int32_t* phys, int B, int D, int H, int top_k, int S,
                                int64_t cap, int rows_per_block, float scale, const int32_t* wrow,
-                               uint32_t* miss_bits, int phase);
+                               uint32_t* miss_bits, int phase, int xc = -1);
 hipError_t launch_attn_combine(hipStream_t st, const float* part_acc, const float* part_ml,
-                               float* out, int B, int D, int H, int nchunk);
+                               float* out, int B, int D, int H, int nchunk, int xc = -1);
 // Rings of n_seqs sequences: ring0 = 0..S-1, pos = identity, head 0, tail S;
 // slot_row = identity, both spare generations S .. S+M-1.
 hipError_t launch_init_rings(hipStream_t st, int32_t* ring0, int32_t* pos, RingState* state, int32_t* slot_row,

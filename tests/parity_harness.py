@@ -65,18 +65,22 @@ class Inputs:
 
 
 class GpuSide:
-    """The HIP path through the C ABI (all sequences of the workload)."""
+    """The HIP path through the C ABI: one handle over the workload's
+    sequences `seqs` (all of them by default; the handle's sequence j is the
+    workload's seqs[j]), on `stream` (the current one by default)."""
 
     def __init__(self, w: synth.Workload, layers: int, device_append: bool = True,
-                 prefix_chunk: int = 65536, flags: int = 0, fused_append: bool = False):
+                 prefix_chunk: int = 65536, flags: int = 0, fused_append: bool = False,
+                 seqs: Optional[List[int]] = None, stream=None):
         import sparse_kv_offload_amd as sko
         torch = torch_mod()
         self.sko, self.torch, self.w = sko, torch, w
         self.L = layers
-        cfg = sko.make_config(num_layers=layers, batch=w.batch, max_tokens=w.capacity,
+        self.seqs = list(range(w.batch)) if seqs is None else list(seqs)
+        cfg = sko.make_config(num_layers=layers, batch=len(self.seqs), max_tokens=w.capacity,
                               num_heads=w.heads, top_k=w.top_k, hot_slots=w.hot_slots,
                               mtp_positions=w.positions, attn_scale=SCALE, flags=flags)
-        self.stream = torch.cuda.current_stream()
+        self.stream = torch.cuda.current_stream() if stream is None else stream
         self.h = sko.SparseKVOffload(cfg, self.stream)
         self.device_append = device_append
         self.prefix_chunk = prefix_chunk
@@ -84,38 +88,56 @@ class GpuSide:
         # (sko_decode_step_append) instead of sko_append_token
         self.fused_append = fused_append
         self.pending = {}
+        self._keep = []
 
     def close(self):
         self.h.close()
 
     def load_prefix(self, layer: int, seq: int, n: Optional[int] = None) -> None:
-        n = self.w.seq_context(seq) if n is None else n
+        """Prefix of the handle's sequence `seq` (workload sequence seqs[seq])."""
+        ws = self.seqs[seq]
+        n = self.w.seq_context(ws) if n is None else n
         for r0 in range(0, n, self.prefix_chunk):
             m = min(self.prefix_chunk, n - r0)
-            self.h.append(layer, seq, self.w.index_rows(layer, seq, r0, m), self.w.kv_rows(layer, seq, r0, m))
+            self.h.append(layer, seq, self.w.index_rows(layer, ws, r0, m), self.w.kv_rows(layer, ws, r0, m))
 
     def append_token(self, layer: int, t: int) -> None:
         w = self.w
-        idx = np.concatenate([w.index_rows(layer, b, w.seq_context(b) + t, 1) for b in range(w.batch)])
-        kv = np.concatenate([w.kv_rows(layer, b, w.seq_context(b) + t, 1) for b in range(w.batch)])
+        idx = np.concatenate([w.index_rows(layer, b, w.seq_context(b) + t, 1) for b in self.seqs])
+        kv = np.concatenate([w.kv_rows(layer, b, w.seq_context(b) + t, 1) for b in self.seqs])
         if self.fused_append:
             self.pending[layer] = (to_device_u16(idx), to_device_u16(kv))
         elif self.device_append:
-            self.h.append(layer, self.sko.SKO_ALL_SEQS, to_device_u16(idx), to_device_u16(kv), 1)
+            di, dk = to_device_u16(idx), to_device_u16(kv)
+            self.stream.wait_stream(self.torch.cuda.current_stream())
+            self.h.append(layer, self.sko.SKO_ALL_SEQS, di, dk, 1)
+            self._keep.append((di, dk))
         else:
             self.h.append(layer, self.sko.SKO_ALL_SEQS, idx, kv, 1)
 
-    def decode(self, layer: int, q_idx: np.ndarray, q_attn: np.ndarray, want_keys=False) -> StepResult:
-        torch, sko = self.torch, self.sko
+    def issue(self, layer: int, q_idx: np.ndarray, q_attn: np.ndarray):
+        """Queues the decode step of `layer` (queries of the handle's
+        sequences) without waiting for it; returns its output tensor."""
+        torch = self.torch
         w = self.w
         qi, qa = to_device_u16(q_idx), to_device_u16(q_attn)
-        out = torch.empty((w.batch, w.positions, w.heads, synth.V_DIM), dtype=torch.float32, device="cuda")
+        out = torch.empty((len(self.seqs), w.positions, w.heads, synth.V_DIM), dtype=torch.float32, device="cuda")
+        # inputs made on the current stream are complete before the step
+        self.stream.wait_stream(torch.cuda.current_stream())
         if layer in self.pending:
             idx, kv = self.pending.pop(layer)
             self.h.decode_step_append(layer, idx, kv, qi, qa, out)
+            self._keep.append((idx, kv))
         else:
             self.h.decode_step(layer, qi, qa, out)
-        torch.cuda.synchronize()
+        # the inputs stay alive until the device has synchronized
+        self._keep.append((qi, qa))
+        return out
+
+    def result(self, out, want_keys=False) -> StepResult:
+        """The last step's results (after a device synchronize)."""
+        sko = self.sko
+        self._keep.clear()
         r = StepResult(topk=self.h.step_buffer(sko.SKO_BUF_TOPK), phys=self.h.step_buffer(sko.SKO_BUF_PHYS),
                        counts=self.h.step_buffer(sko.SKO_BUF_COUNTS), misses=self.h.step_buffer(sko.SKO_BUF_MISSES),
                        victims=self.h.step_buffer(sko.SKO_BUF_VICTIMS),
@@ -123,6 +145,11 @@ class GpuSide:
         if want_keys:
             r.keys = self.h.step_buffer(sko.SKO_BUF_KEYS)
         return r
+
+    def decode(self, layer: int, q_idx: np.ndarray, q_attn: np.ndarray, want_keys=False) -> StepResult:
+        out = self.issue(layer, q_idx, q_attn)
+        self.torch.cuda.synchronize()
+        return self.result(out, want_keys)
 
     def tables(self, layer: int, seq: int) -> Dict[str, np.ndarray]:
         sko = self.sko
@@ -277,4 +304,94 @@ def run_parity(w: synth.Workload, layers: Optional[int] = None, steps: Optional[
             assert worst["rescans"] == L * rows, (worst["rescans"], L * rows)
     finally:
         gpu.close()
+    return worst
+
+
+def run_parity_micro(w: synth.Workload, nmb: int = 2, layers: Optional[int] = None, steps: Optional[int] = None,
+                     chains: Optional[List[tuple]] = None, check_tables_every: int = 1,
+                     fused_append: bool = True, out_steps=None, flags: int = 0, sync_each_layer: bool = True,
+                     log=None) -> Dict[str, float]:
+    """The batch split into nmb handles (contiguous groups of sequences), each
+    kept off the copy blocks' XCD (SKO_FLAG_XCD_SPLIT) and on its own stream.
+    Every layer-step queues all groups' calls before waiting, so the groups'
+    steps overlap on the device.  With sync_each_layer every step of every
+    sampled chain is checked against the oracle; without it the whole run is
+    queued with no wait at all and the last step and the tables at the end
+    are checked."""
+    import sparse_kv_offload_amd as sko
+    torch = torch_mod()
+    L = w.layers if layers is None else layers
+    T = w.steps if steps is None else steps
+    chains = [(l, b) for l in range(L) for b in range(w.batch)] if chains is None else chains
+    chain_set = set(chains)
+    inputs = Inputs(w, sorted({c[0] for c in chains} | set(range(L))), T)
+    groups = [list(range(g * w.batch // nmb, (g + 1) * w.batch // nmb)) for g in range(nmb)]
+    assert all(groups), "every group needs a sequence"
+    streams = [torch.cuda.Stream() for _ in groups]
+    gpus = []
+    worst = {"abs": 0.0, "rel_rms": 0.0}
+    try:
+        for grp, st in zip(groups, streams):
+            gpus.append(GpuSide(w, L, flags=flags | sko.SKO_FLAG_XCD_SPLIT, fused_append=fused_append,
+                                seqs=grp, stream=st))
+        for gs in gpus:
+            for l in range(L):
+                for j in range(len(gs.seqs)):
+                    gs.load_prefix(l, j)
+        torch.cuda.synchronize()
+        ora = OracleSide(w, chains, indexer_c8=bool(flags & sko.SKO_FLAG_INDEXER_C8))
+        for c in chains:
+            ora.load_prefix(*c)
+
+        def check(gs, out, l, t, tables_now):
+            g = gs.result(out)
+            for j, b in enumerate(gs.seqs):
+                if (l, b) not in chain_set:
+                    continue
+                want_out = out_steps is None or t in out_steps
+                o = ora.decode(l, b, inputs.q_idx[(l, b)][t], inputs.w.attn_queries(l, b, t), want_out=want_out)
+                s_ = compare_step(w, g, j, o, check_out=want_out, where=f"[{w.name} micro{nmb} l={l} b={b} t={t}]")
+                for k_, v in s_.items():
+                    worst[k_] = max(worst[k_], v)
+                if tables_now:
+                    compare_tables(gs.tables(l, j), ora.tables(l, b), where=f"[{w.name} micro{nmb} l={l} b={b} t={t}]")
+
+        for t in range(T):
+            for l in range(L):
+                outs = []
+                for gs in gpus:
+                    gs.append_token(l, t)
+                    outs.append(gs.issue(l, inputs.q_idx_step(l, t, gs.seqs), inputs.q_attn_step(l, t, gs.seqs)))
+                if sync_each_layer:
+                    torch.cuda.synchronize()
+                    for gs, out in zip(gpus, outs):
+                        for b in gs.seqs:
+                            if (l, b) in chain_set:
+                                ora.append_token(l, b, t)
+                        tables_now = bool(check_tables_every) and (t % check_tables_every == 0 or t == T - 1)
+                        check(gs, out, l, t, tables_now)
+                else:
+                    last = outs
+                    for b in range(w.batch):
+                        if (l, b) in chain_set:
+                            ora.append_token(l, b, t)
+                            if not (t == T - 1 and l == L - 1):
+                                ora.decode(l, b, inputs.q_idx[(l, b)][t], inputs.w.attn_queries(l, b, t),
+                                           want_out=False)
+            if log:
+                log(f"{w.name} micro{nmb}: step {t + 1}/{T} queued")
+        if not sync_each_layer:
+            torch.cuda.synchronize()
+            for gs, out in zip(gpus, last):
+                check(gs, out, L - 1, T - 1, True)
+            # every other layer's tables after the whole run
+            for gs in gpus:
+                for j, b in enumerate(gs.seqs):
+                    for l in range(L - 1):
+                        if (l, b) in chain_set:
+                            compare_tables(gs.tables(l, j), ora.tables(l, b), where=f"[{w.name} micro{nmb} end l={l} b={b}]")
+    finally:
+        torch.cuda.synchronize()
+        for gs in gpus:
+            gs.close()
     return worst

@@ -49,9 +49,11 @@ def good_cfg(sko, **kw):
     dict(index_dim=32), dict(kv_dim=512), dict(v_dim=576), dict(num_layers=0), dict(batch=0),
     dict(num_heads=0), dict(top_k=0), dict(mtp_positions=0), dict(max_tokens=0),
     dict(max_tokens=2 ** 31), dict(hot_slots=127), dict(attn_scale=0.0),
-    dict(attn_scale=float("inf")), dict(attn_scale=float("nan")), dict(flags=0x400), dict(flags=0x60), dict(flags=0x110), dict(flags=0x120),
+    dict(attn_scale=float("inf")), dict(attn_scale=float("nan")), dict(flags=0x800), dict(flags=0x60), dict(flags=0x110), dict(flags=0x120),
     dict(flags=0x30), dict(flags=0x50), dict(flags=0x80000000), dict(flags=3),
     dict(flags=0x10, mtp_positions=2), dict(flags=0x10, mtp_positions=1, num_heads=17),
+    # the XCD split needs the early copy without the hit/miss split
+    dict(flags=0x420), dict(flags=0x410), dict(flags=0x500),
     dict(device=-1),
 ])
 def test_create_rejects_bad_config(bad):

@@ -1,0 +1,98 @@
+"""The step kept off the copy blocks' XCD (SKO_FLAG_XCD_SPLIT), alone and as
+micro-batches: the batch split into handles on their own streams whose steps
+overlap on the device.
+
+Every case checks the oracle's chains element by element (packed winners,
+slots, counts, miss lists, evictions, residency tables and hot-buffer bytes
+bit-exactly; attention within 2e-2 absolute and 1e-2 relative RMS).  The
+split changes only where blocks run: the copy blocks on one XCD, every other
+block on the other seven.  The grids cover a launch smaller than one group of
+eight blocks, launches that are not multiples of seven work blocks, several
+score blocks per sequence, head groups, up to five positions, a ragged batch
+with an empty sequence, and the full shelf_ctx8 shape in the benchmark's
+micro-batch configuration.
+"""
+import pytest
+
+import synth
+from parity_harness import run_parity, run_parity_micro
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_kv_offload_amd  # noqa: F401  (raises if libsko.so is missing)
+    yield
+
+
+def case(name, **kw):
+    base = dict(layers=1, batch=2, context=1500, steps=8, top_k=64, hot_slots=160, positions=1,
+                heads=16, seed=4321)
+    base.update(kw)
+    return synth.Workload(name, **base)
+
+
+@pytest.mark.parametrize("shape", ["tiny", "tiles_d2_hg2", "ragged_d3", "d5"])
+@pytest.mark.parametrize("fused_append", [False, True])
+def test_split_one_handle(shape, fused_append):
+    """One handle with the split: the oracle's results, score keys included."""
+    import sparse_kv_offload_amd as sko
+    shapes = {
+        "tiny": dict(batch=1, context=700, steps=6, top_k=32, hot_slots=96, positions=1, heads=16),
+        "tiles_d2_hg2": dict(batch=4, context=20000, steps=6, top_k=512, hot_slots=1100, positions=2,
+                             heads=20),
+        "ragged_d3": dict(batch=3, contexts=(3001, 0, 777), context=3001, steps=7, top_k=100,
+                          hot_slots=337, positions=3, heads=5),
+        "d5": dict(batch=2, context=9000, steps=5, top_k=200, hot_slots=1000, positions=5, heads=16),
+    }
+    w = case(f"xcd_{shape}", **shapes[shape])
+    log(f"case xcd split one handle {shape} fused_append={fused_append}: {w}")
+    worst = run_parity(w, check_keys=True, flags=sko.SKO_FLAG_XCD_SPLIT, fused_append=fused_append, log=log)
+    log(f"worst {worst}")
+
+
+@pytest.mark.parametrize("shape,nmb", [("d1", 2), ("d4", 2), ("ragged_d2", 3)])
+def test_micro_batches_each_layer(shape, nmb):
+    """nmb handles on nmb streams, every layer's calls of all handles queued
+    before one wait: each handle's results against the oracle at every step."""
+    shapes = {
+        "d1": dict(batch=4, context=12000, steps=8, top_k=300, hot_slots=700, positions=1, heads=16),
+        "d4": dict(batch=4, layers=2, context=9000, steps=6, top_k=256, hot_slots=1100, positions=4,
+                   heads=16),
+        "ragged_d2": dict(batch=5, contexts=(2000, 0, 4100, 63, 64), context=4100, steps=6, top_k=64,
+                          hot_slots=200, positions=2, heads=20),
+    }
+    w = case(f"micro_{shape}", **shapes[shape])
+    log(f"case micro-batches {nmb} {shape}: {w}")
+    worst = run_parity_micro(w, nmb=nmb, log=log)
+    log(f"worst {worst}")
+
+
+def test_micro_batches_queued_without_waits():
+    """Two handles, two layers, the whole run queued with no wait between
+    steps (layer l + 1 of one handle overlaps layer l of the other): the last
+    step and every table at the end against the oracle."""
+    w = case("micro_async", batch=4, layers=2, context=8000, steps=10, top_k=256, hot_slots=600,
+             positions=2, heads=16)
+    log(f"case micro-batches queued: {w}")
+    worst = run_parity_micro(w, nmb=2, sync_each_layer=False, log=log)
+    log(f"worst {worst}")
+
+
+def test_micro_batches_shelf_ctx8_full_shape():
+    """shelf_ctx8 at full shape (B = 32 in two handles of 16, 64K context,
+    k 2048, S 8192) in the benchmark's launch configuration: one layer, 24
+    steps, one chain in each handle."""
+    w = synth.SHELF8
+    log(f"fullsize shelf_ctx8 micro-batches 2: {w}")
+    worst = run_parity_micro(w, nmb=2, layers=1, steps=24, chains=[(0, 3), (0, 30)],
+                             out_steps={0, 1, 12, 23}, check_tables_every=8, log=log)
+    log(f"worst {worst}")
