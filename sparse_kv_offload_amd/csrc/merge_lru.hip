@@ -67,7 +67,7 @@ struct RefineGroup {
 __device__ __forceinline__ void refine_rows(int b, int D, RowMeta* __restrict__ meta, const uint2* __restrict__ cand,
                                             int32_t* __restrict__ topk,
                                             uint32_t* __restrict__ wb, int top_k, int64_t cap, uint2* stage,
-                                            uint32_t (*hg)[256], RefineGroup* gs) {
+                                            int stage_cap, uint32_t (*hg)[256], RefineGroup* gs) {
     const int NG = D < 4 ? D : 4;
     const int gsize = (kLruThreads / NG) & ~63;  // whole waves per group
     const int tid = threadIdx.x;
@@ -76,7 +76,7 @@ __device__ __forceinline__ void refine_rows(int b, int D, RowMeta* __restrict__ 
     const int gl = gt & 63;
     const bool in_group = g < NG;
     const int gi = in_group ? g : 0;  // a valid index for threads outside any group
-    const int stage_per = kMaxMerge / NG;
+    const int stage_per = stage_cap / NG;
     for (int p0 = 0; p0 < D; p0 += NG) {
         if (in_group && gt == 0) {
             const int p = p0 + g;
@@ -223,7 +223,8 @@ __device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, con
                                            const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
                                            uint4* __restrict__ hot_layer, const int32_t* __restrict__ spare_layer,
                                            int gen, int R, const int32_t* __restrict__ ntok_layer,
-                                           int64_t cap, int64_t wpr, int mstride, int32_t* toks, int* scratch) {
+                                           int64_t cap, int64_t wpr, int mstride, int32_t* toks, int toks_cap,
+                                           int* scratch) {
     const int b = cb / nper;
     // this step's spare rows of the sequence (each < R)
     const int32_t* __restrict__ spare = spare_layer + ((size_t)b * 2 + gen) * mstride;
@@ -251,10 +252,14 @@ __device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, con
     int total;
     int pos = block_exclusive_scan<kLruThreads>(__popc(bits), &total, scratch);
     if (total == 0) return;  // block-uniform
+    // a sequence has at most D*k misses, which toks holds (a larger count
+    // would be a broken invariant: the rows past it are not copied)
+    total = std::min(total, toks_cap);
     while (bits) {
         const int e = __ffs((int)bits) - 1;
         bits &= bits - 1u;
-        toks[pos++] = (int32_t)(wi * 32 + e);
+        if (pos < toks_cap) toks[pos] = (int32_t)(wi * 32 + e);
+        ++pos;
     }
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -295,23 +300,30 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     uint32_t* __restrict__ miss_bits, const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
     uint4* __restrict__ hot_layer, int32_t* __restrict__ slot_row_layer, int32_t* __restrict__ spare_layer, int R,
     int32_t* __restrict__ wrow, int32_t* __restrict__ phys, int sort_winners,
-    int test_violation, uint64_t* __restrict__ stamps, uint4* __restrict__ pool_newest, int ncopy, int xc) {
+    int test_violation, uint64_t* __restrict__ stamps, uint4* __restrict__ pool_newest, int ncopy, int xc,
+    int tw, int mcap) {
     // instrumentation (stamps != nullptr): each block records when it
     // started and ended on the chip's constant-rate clock, so the host can
     // tell how long the copy blocks ran beside the LRU update
     const uint64_t t_start = stamps ? __builtin_amdgcn_s_memrealtime() : 0ull;
-    __shared__ uint32_t touched[kMaxHotSlots / 32];
-    // [0, kMaxMerge): misses; [kMaxMerge, 2 kMaxMerge): the union, later the
-    // victims.  Before the merge the whole area stages refine candidates.
-    __shared__ int32_t lists[2 * kMaxMerge];
-    __shared__ uint32_t marks[kMaxMerge];  // per union entry: positions holding it (sorting)
+    // Sized for the handle (dynamic LDS, so that at small shelves and one
+    // position a block leaves room on its CU for other kernels' blocks):
+    //   touched [tw] words: the slots hit or taken at this step (tw >= S/32);
+    //   lists [2 mcap] (mcap = D*k): [0, mcap) the misses, [mcap, 2 mcap) the
+    //     union, later the victims; before the merge the whole area stages
+    //     refine candidates (a copy block lists its part's misses there);
+    //   marks [mcap]: per union entry, the positions holding it (sorting).
+    extern __shared__ __align__(16) uint32_t lru_lds[];
+    uint32_t* const touched = lru_lds;
+    int32_t* const lists = reinterpret_cast<int32_t*>(lru_lds + tw);
+    uint32_t* const marks = lru_lds + tw + 2 * mcap;
     __shared__ uint32_t hgrp[4][256];
     __shared__ RefineGroup rgrp[4];
     __shared__ int scratch[kLruThreads / 64 + 1];
     __shared__ int64_t s_newhead;
     int32_t* mlist = lists;
-    int32_t* ulist = lists + kMaxMerge;
-    int32_t* vlist = lists + kMaxMerge;
+    int32_t* ulist = lists + mcap;
+    int32_t* vlist = lists + mcap;
     uint2* cstage = reinterpret_cast<uint2*>(lists);
 
     // the block's part: merge block rb < nseq, or copy block rb - nseq.  Kept
@@ -330,8 +342,8 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
         if (rb < 0) return;  // block-uniform
     }
     if (rb >= nseq) {
-        copy_block(rb - nseq, copy_per_seq, copy_words, miss_bits, pool_layer, recent_layer,
-                   hot_layer, spare_layer, t & 1, R, ntok_layer, cap, wpr, D * top_k, lists, scratch);
+        copy_block(rb - nseq, copy_per_seq, copy_words, miss_bits, pool_layer, recent_layer, hot_layer,
+                   spare_layer, t & 1, R, ntok_layer, cap, wpr, D * top_k, lists, 2 * mcap, scratch);
         if (stamps) {
             __syncthreads();
             if (threadIdx.x == 0) {
@@ -370,7 +382,7 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
 
     // 0. finish the top-k of rows whose threshold bucket is split (unless
     //    k_topk_refine already did)
-    if (do_refine) refine_rows(b, D, meta, cand, topk, wb, top_k, cap, cstage, hgrp, rgrp);
+    if (do_refine) refine_rows(b, D, meta, cand, topk, wb, top_k, cap, cstage, mcap, hgrp, rgrp);
 
     for (int i = tid; i < SW; i += kLruThreads) touched[i] = 0u;
     if (tid == 0) cnt[7] = 0;
@@ -401,14 +413,14 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 for (uint32_t x = wv[q]; x; x &= x - 1u) {
-                    if (uo < kMaxMerge) ulist[uo] = (int32_t)((w + q) * 32 + (__ffs((int)x) - 1));
+                    if (uo < mcap) ulist[uo] = (int32_t)((w + q) * 32 + (__ffs((int)x) - 1));
                     ++uo;
                 }
             *reinterpret_cast<uint4*>(wb + w) = make_uint4(0u, 0u, 0u, 0u);
         }
     }
     __syncthreads();
-    nU = std::min(nU, kMaxMerge);
+    nU = std::min(nU, mcap);
 
     // 1b. (sort_winners, at most 16 positions) each position's winners are
     //     rewritten in token order, so the attention's grouping of rows into
@@ -688,12 +700,27 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     }
 }
 
+int merge_lru_touched_words(int S) { return ((S + 31) / 32 + 3) / 4 * 4; }
+
+size_t merge_lru_lds_bytes(int S, int D, int top_k) {
+    return 4 * ((size_t)merge_lru_touched_words(S) + 3 * (size_t)D * top_k);
+}
+
+hipError_t prepare_merge_lru(size_t lds_bytes) {
+    // the attribute is the kernel's limit for every launch: it is set to the
+    // largest size any handle can need (S and D*k at their limits), never
+    // lowered
+    const size_t most = merge_lru_lds_bytes(kMaxHotSlots, 1, kMaxMerge);
+    if (lds_bytes > most) return hipErrorInvalidValue;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_merge_lru), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)most);
+}
+
 void copy_shape(int B, int64_t max_tokens_now, int* copy_per_seq, int* copy_words, int xcd_cus) {
     const int64_t words = std::max<int64_t>(1, (max_tokens_now + 31) / 32);
     if (xcd_cus > 0) {
-        // the copy blocks of one XCD: about one per CU (a copy block holds a
-        // CU's LDS), each part at most kLruThreads words and, unless that
-        // forces more, at least 32
+        // the copy blocks of one XCD: about one per CU, each part at most
+        // kLruThreads words and, unless that forces more, at least 32
         *copy_per_seq = (int)std::max<int64_t>(
             (words + kLruThreads - 1) / kLruThreads,
             std::min<int64_t>((xcd_cus + B - 1) / B, (words + 31) / 32));
@@ -728,11 +755,13 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
     copy_shape(B, max_tokens_now, &copy_per_seq, &copy_words, xc >= 0 ? xcd_cus : 0);
     if (!miss_bits) copy_per_seq = 0;
     const int ncopy = B * copy_per_seq;
+    const int tw = merge_lru_touched_words(S);
+    const size_t lds = merge_lru_lds_bytes(S, D, top_k);
     // kept off XCD xc: the copy blocks are the blocks on it, one per group
     // of 8, and the merge blocks are work blocks of the other seven
     const unsigned grid = xc < 0 ? (unsigned)(B + ncopy)
                                  : (unsigned)(kXcds * std::max<int64_t>(ncopy, (B + kXcds - 2) / (kXcds - 1)));
-    hipLaunchKernelGGL(k_merge_lru, dim3(grid), dim3(kLruThreads), 0, st, winners, hist, meta, cand, topk,
+    hipLaunchKernelGGL(k_merge_lru, dim3(grid), dim3(kLruThreads), lds, st, winners, hist, meta, cand, topk,
                        ntok_layer, cache_slots_layer, slot_token_layer, last_use_layer, ring0_layer,
                        ring1_layer, pos_layer, ring_state_layer, D, top_k, S, C, cap, wpr, t, misses, victims,
                        evict_old, counts, glist, layer_stats, do_refine ? 1 : 0, B, copy_per_seq, copy_words,
@@ -740,7 +769,7 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                        reinterpret_cast<const uint4*>(pool_layer), reinterpret_cast<const uint4*>(recent_layer),
                        reinterpret_cast<uint4*>(hot_layer), slot_row_layer, spare_layer, R, wrow, phys,
                        sort_winners ? 1 : 0, test_violation ? 1 : 0, stamps, reinterpret_cast<uint4*>(pool_newest),
-                       ncopy, xc);
+                       ncopy, xc, tw, D * top_k);
     return hipGetLastError();
 }
 

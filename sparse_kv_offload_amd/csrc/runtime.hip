@@ -784,6 +784,13 @@ int sko_create(const sko_config* cfg, void* stream, sko_handle** out) {
         h->xc = 0;
         h->xcd_cus = h->cu_count / kXcds;
     }
+    // the LRU-update launch's LDS, sized for S and D*k
+    if (prepare_merge_lru(merge_lru_lds_bytes(h->S, h->D, h->k)) != hipSuccess) {
+        (void)hipGetLastError();
+        delete h;
+        return set_err(SKO_E_DEVICE, "the LRU-update kernel cannot take %zu bytes of LDS",
+                       merge_lru_lds_bytes(h->S, h->D, h->k));
+    }
     h->rows_per_block = attn_rows_per_block(h->k, h->B * h->D * h->HG);
     h->nchunk = (h->k + h->rows_per_block - 1) / h->rows_per_block;
     // the split attention writes the partials of both phases

@@ -158,6 +158,12 @@ hipError_t launch_merge_lru(hipStream_t st, uint32_t* winners, uint32_t* hist, R
                             int32_t* wrow, int32_t* phys, bool sort_winners,
                             int64_t max_tokens_now, bool test_violation, uint64_t* stamps,
                             uint16_t* pool_newest, int xc = -1, int xcd_cus = 0);
+// Dynamic LDS of the LRU-update launch for S slots and D*k winners (the
+// touched-slot bitmap, the miss/union/victim lists and the sort marks), and
+// the call that lets that kernel take it (before its first launch).
+int merge_lru_touched_words(int S);
+size_t merge_lru_lds_bytes(int S, int D, int top_k);
+hipError_t prepare_merge_lru(size_t lds_bytes);
 // Copy blocks of the early copy: copy_per_seq per sequence, each owning
 // copy_words bitmap words (a multiple of 4, at most 1024).  xcd_cus > 0:
 // the copy blocks run on one XCD of xcd_cus CUs (at least one block per CU).
