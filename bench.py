@@ -360,8 +360,9 @@ def main() -> int:
                     help="miss-copy arrangement: early (the default: by extra blocks of the LRU-update launch), "
                          "late (after the LRU update), fused (inside the attention launch; one "
                          "position, at most 16 heads)")
-    ap.add_argument("--micro-batches", type=int, default=1,
-                    help="split the batch into this many handles on as many streams, kept off the copy XCD")
+    ap.add_argument("--micro-batches", type=int, default=0,
+                    help="split the batch into this many handles on as many streams, kept off the copy XCD "
+                         "(0: two when the batch has at least 4 sequences, else one)")
     ap.add_argument("--xcd-split", action="store_true",
                     help="keep the step's kernels off the copy blocks' XCD even with one micro-batch")
     ap.add_argument("--hit-overlap", action="store_true",
@@ -419,7 +420,11 @@ def main() -> int:
     # XCD of the copy blocks, so that one group's selection and attention run
     # while another group's misses cross the host link.  Each layer-step
     # issues every group's call for the layer before the next layer's.
-    nmb = max(1, min(args.micro_batches, B))
+    # two micro-batches wherever each gets at least two sequences (measured,
+    # layer-steps/s, one handle -> two: shelf_ctx8 2 682 -> 3 269, mtp3
+    # 1 235 -> 1 398, small 5 035 -> 5 275; long, B = 2, 4 300 -> 4 262)
+    nmb = args.micro_batches if args.micro_batches > 0 else (2 if B >= 4 else 1)
+    nmb = max(1, min(nmb, B))
     if nmb > 1 or args.xcd_split:
         flags |= sko.SKO_FLAG_XCD_SPLIT
     groups = [list(range(g * B // nmb, (g + 1) * B // nmb)) for g in range(nmb)]
@@ -625,6 +630,13 @@ def main() -> int:
             roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": None, "traffic": None, "kernel": dominant, "avg_ms": round(ms / n, 5)}
 
+    if roof is not None and roof.get("bound") == "host-link" and elapsed > 0:
+        # with micro-batches the copy launches of the handles overlap and
+        # share the link, so a launch's own rate is a share of it; the link's
+        # rate over the timed steps is the copied bytes over the wall time
+        roof["concurrent_handles"] = nmb
+        roof["link_rate_over_timed_steps_GBps"] = round(d["h2d_bytes"] / elapsed / 1e9, 2)
+        roof["link_rate_frac_of_measured"] = round(d["h2d_bytes"] / elapsed / 1e9 / h2d_ceiling, 4)
     result = {
         "metric": "sparse-offload decode layer-steps/s",
         "value": round(value, 2),

@@ -9,8 +9,8 @@ split changes only where blocks run: the copy blocks on one XCD, every other
 block on the other seven.  The grids cover a launch smaller than one group of
 eight blocks, launches that are not multiples of seven work blocks, several
 score blocks per sequence, head groups, up to five positions, a ragged batch
-with an empty sequence, and the full shelf_ctx8 shape in the benchmark's
-micro-batch configuration.
+with an empty sequence, and the full shelf_ctx8, small and mtp3 shapes in
+the benchmark's micro-batch configuration (two handles).
 """
 import pytest
 
@@ -95,4 +95,26 @@ def test_micro_batches_shelf_ctx8_full_shape():
     log(f"fullsize shelf_ctx8 micro-batches 2: {w}")
     worst = run_parity_micro(w, nmb=2, layers=1, steps=24, chains=[(0, 3), (0, 30)],
                              out_steps={0, 1, 12, 23}, check_tables_every=8, log=log)
+    log(f"worst {worst}")
+
+
+def test_micro_batches_small_full_shape():
+    """small at full shape (B = 8 in two handles of 4, 32K context, k 2048,
+    S 4096, 4 layers), the benchmark's default for it: 12 steps, a chain in
+    each handle on different layers."""
+    w = synth.SMALL
+    log(f"fullsize small micro-batches 2: {w}")
+    worst = run_parity_micro(w, nmb=2, layers=4, steps=12, chains=[(0, 1), (3, 6)],
+                             out_steps={0, 1, 11}, check_tables_every=4, log=log)
+    log(f"worst {worst}")
+
+
+def test_micro_batches_mtp3_full_shape():
+    """mtp3 at full shape (B = 16 in two handles of 8, 128K context, four
+    positions, k 2048, S 16384), the benchmark's default for it: one layer,
+    12 steps, a chain in each handle."""
+    w = synth.MTP3
+    log(f"fullsize mtp3 micro-batches 2: {w}")
+    worst = run_parity_micro(w, nmb=2, layers=1, steps=12, chains=[(0, 2), (0, 13)],
+                             out_steps={0, 1, 11}, check_tables_every=4, log=log)
     log(f"worst {worst}")
