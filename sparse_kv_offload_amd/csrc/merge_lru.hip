@@ -218,13 +218,18 @@ constexpr int kCopyBlocks = 64;
 // long 4 335 -> 4 363; with eight waves of one row each the copy itself
 // slowed, 270 -> 279 us at shelf_ctx8).
 constexpr int kCopyRowsPerWave = 1;
+// Kept off an XCD, the copy blocks of two handles' launches share the copy
+// XCD; each copies with this many of its waves (one box, layer-steps/s, 16
+// waves -> 8: shelf_ctx8 3 291 -> 3 311, small 5 284 -> 5 381; 4 waves lost
+// 10 %).
+constexpr int kSplitCopyWaves = 8;
 
 __device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, const uint32_t* __restrict__ miss_bits,
                                            const uint4* __restrict__ pool_layer, const uint4* __restrict__ recent_layer,
                                            uint4* __restrict__ hot_layer, const int32_t* __restrict__ spare_layer,
                                            int gen, int R, const int32_t* __restrict__ ntok_layer,
                                            int64_t cap, int64_t wpr, int mstride, int32_t* toks, int toks_cap,
-                                           int* scratch) {
+                                           int copy_waves, int* scratch) {
     const int b = cb / nper;
     // this step's spare rows of the sequence (each < R)
     const int32_t* __restrict__ spare = spare_layer + ((size_t)b * 2 + gen) * mstride;
@@ -263,7 +268,7 @@ __device__ __forceinline__ void copy_block(int cb, int nper, int copy_words, con
     }
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int i0 = wave * kCopyRowsPerWave; i0 < total; i0 += (kLruThreads / 64) * kCopyRowsPerWave) {
+    for (int i0 = wave * kCopyRowsPerWave; wave < copy_waves && i0 < total; i0 += copy_waves * kCopyRowsPerWave) {
         uint4 a[kCopyRowsPerWave], t8[kCopyRowsPerWave];
 #pragma unroll
         for (int r = 0; r < kCopyRowsPerWave; ++r) {
@@ -343,7 +348,8 @@ __global__ __launch_bounds__(kLruThreads) void k_merge_lru(
     }
     if (rb >= nseq) {
         copy_block(rb - nseq, copy_per_seq, copy_words, miss_bits, pool_layer, recent_layer, hot_layer,
-                   spare_layer, t & 1, R, ntok_layer, cap, wpr, D * top_k, lists, 2 * mcap, scratch);
+                   spare_layer, t & 1, R, ntok_layer, cap, wpr, D * top_k, lists, 2 * mcap,
+                   xc >= 0 ? kSplitCopyWaves : kLruThreads / 64, scratch);
         if (stamps) {
             __syncthreads();
             if (threadIdx.x == 0) {
