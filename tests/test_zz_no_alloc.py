@@ -108,7 +108,7 @@ def test_static_scratch_matches_the_allocating_step():
 def test_static_scratch_in_every_copy_mode():
     import sparse_kv_offload_amd as sko
     for name, flags in (("late", sko.SKO_FLAG_LATE_COPY), ("fused", sko.SKO_FLAG_FUSED_COPY),
-                        ("c8", sko.SKO_FLAG_INDEXER_C8)):
+                        ("c8", sko.SKO_FLAG_INDEXER_C8), ("xcd_split", sko.SKO_FLAG_XCD_SPLIT)):
         log(f"no-alloc: {name}")
         compare_workload(SMALL.replace(name=f"noalloc_{name}"), flags)
 
