@@ -362,7 +362,7 @@ def main() -> int:
                          "position, at most 16 heads)")
     ap.add_argument("--micro-batches", type=int, default=0,
                     help="split the batch into this many handles on as many streams, kept off the copy XCD "
-                         "(0: two when the batch has at least 4 sequences, else one)")
+                         "(0: two when the batch has at least 2 sequences, else one)")
     ap.add_argument("--xcd-split", action="store_true",
                     help="keep the step's kernels off the copy blocks' XCD even with one micro-batch")
     ap.add_argument("--hit-overlap", action="store_true",
@@ -420,10 +420,11 @@ def main() -> int:
     # XCD of the copy blocks, so that one group's selection and attention run
     # while another group's misses cross the host link.  Each layer-step
     # issues every group's call for the layer before the next layer's.
-    # two micro-batches wherever each gets at least two sequences (measured,
-    # layer-steps/s, one handle -> two: shelf_ctx8 2 682 -> 3 269, mtp3
-    # 1 235 -> 1 398, small 5 035 -> 5 275; long, B = 2, 4 300 -> 4 262)
-    nmb = args.micro_batches if args.micro_batches > 0 else (2 if B >= 4 else 1)
+    # two micro-batches wherever the batch has two sequences or more
+    # (measured, one box each, layer-steps/s, one handle -> two: shelf_ctx8
+    # 2 743 -> 3 402, mtp3 1 239 -> 1 403, small 5 007 -> 5 371, long
+    # 4 363 -> 4 767)
+    nmb = args.micro_batches if args.micro_batches > 0 else (2 if B >= 2 else 1)
     nmb = max(1, min(nmb, B))
     if nmb > 1 or args.xcd_split:
         flags |= sko.SKO_FLAG_XCD_SPLIT

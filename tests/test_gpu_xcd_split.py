@@ -9,8 +9,8 @@ split changes only where blocks run: the copy blocks on one XCD, every other
 block on the other seven.  The grids cover a launch smaller than one group of
 eight blocks, launches that are not multiples of seven work blocks, several
 score blocks per sequence, head groups, up to five positions, a ragged batch
-with an empty sequence, and the full shelf_ctx8, small and mtp3 shapes in
-the benchmark's micro-batch configuration (two handles).
+with an empty sequence, and the full shelf_ctx8, small, mtp3 and long shapes
+in the benchmark's micro-batch configuration (two handles).
 """
 import pytest
 
@@ -117,4 +117,15 @@ def test_micro_batches_mtp3_full_shape():
     log(f"fullsize mtp3 micro-batches 2: {w}")
     worst = run_parity_micro(w, nmb=2, layers=1, steps=12, chains=[(0, 2), (0, 13)],
                              out_steps={0, 1, 11}, check_tables_every=4, log=log)
+    log(f"worst {worst}")
+
+
+def test_micro_batches_long_full_shape():
+    """long at full shape (B = 2 in two handles of one sequence, 1M-token
+    context, four positions, k 2048, S 131072), the benchmark's default for
+    it: one layer, 8 steps, both chains."""
+    w = synth.LONG
+    log(f"fullsize long micro-batches 2: {w}")
+    worst = run_parity_micro(w, nmb=2, layers=1, steps=8, chains=[(0, 0), (0, 1)],
+                             out_steps={0, 1, 7}, check_tables_every=4, log=log)
     log(f"worst {worst}")
