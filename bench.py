@@ -431,10 +431,25 @@ def main() -> int:
     groups = [list(range(g * B // nmb, (g + 1) * B // nmb)) for g in range(nmb)]
     streams = [stream] if nmb == 1 else [torch.cuda.Stream() for _ in range(nmb)]
     hs = []
+    split_note = None
     for g, seqs in enumerate(groups):
         cfg = sko.make_config(num_layers=L, batch=len(seqs), max_tokens=w.capacity, num_heads=H, top_k=k,
                               hot_slots=w.hot_slots, mtp_positions=D, flags=flags)
-        hs.append(sko.SparseKVOffload(cfg, streams[g]))
+        try:
+            hs.append(sko.SparseKVOffload(cfg, streams[g]))
+        except sko.SkoError as e:
+            if not (flags & sko.SKO_FLAG_XCD_SPLIT) or e.code != sko.SKO_E_UNSUPPORTED or hs:
+                raise
+            # a device that does not deal launch blocks in the fixed stripe:
+            # one handle over the whole batch, without the split
+            split_note = f"XCD split unsupported on this device ({e}); one handle"
+            log(split_note)
+            flags &= ~sko.SKO_FLAG_XCD_SPLIT
+            nmb, groups, streams = 1, [list(range(B))], [stream]
+            cfg = sko.make_config(num_layers=L, batch=B, max_tokens=w.capacity, num_heads=H, top_k=k,
+                                  hot_slots=w.hot_slots, mtp_positions=D, flags=flags)
+            hs.append(sko.SparseKVOffload(cfg, stream))
+            break
     chunk = 65536
     for h, seqs in zip(hs, groups):
         for l in range(L):
@@ -656,7 +671,8 @@ def main() -> int:
                    "parallelism": "none (1 GPU)", "pool": args.pool, "copy": args.copy,
                    "hit_overlap": bool(args.hit_overlap), "append": args.append,
                    "indexer": args.indexer, "micro_batches": nmb,
-                   "xcd_split": bool(flags & sko.SKO_FLAG_XCD_SPLIT)},
+                   "xcd_split": bool(flags & sko.SKO_FLAG_XCD_SPLIT),
+                   **({"note": split_note} if split_note else {})},
         "tokens_per_s": round(B * K / elapsed, 2),
         "indexer_scan_GBps": rooflines.get("score_hist", {}).get("achieved"),
         "miss_gather_GBps": next((e["achieved"] for e in [roof or {}] + list(rooflines.values())

@@ -29,7 +29,15 @@ def _gpu():
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    import sparse_kv_offload_amd  # noqa: F401  (raises if libsko.so is missing)
+    import sparse_kv_offload_amd as sko  # raises if libsko.so is missing
+    cfg = sko.make_config(num_layers=1, batch=1, max_tokens=64, num_heads=1, top_k=4, hot_slots=8,
+                          flags=sko.SKO_FLAG_XCD_SPLIT)
+    try:
+        sko.SparseKVOffload(cfg, None).close()
+    except sko.SkoError as e:
+        if e.code == sko.SKO_E_UNSUPPORTED:
+            pytest.skip(f"the device does not deal launch blocks to 8 XCDs in a fixed stripe: {e}")
+        raise
     yield
 
 
