@@ -549,12 +549,35 @@ def main() -> int:
     # block stamps of the timed LRU-update launches (early copy): how long the
     # copy blocks ran beside the LRU update
     overlap = merged_overlap() if timed_mask else None
+    # the copy spans of every timed LRU-update launch of every handle, on the
+    # device clock: their union is the time during which any missed row is
+    # being copied over the host link
+    span_list, span_khz = [], None
+    if timed_mask and dominant == "merge_lru":
+        for h in hs:
+            sp, span_khz = h.copy_spans()
+            span_list.append(sp)
     set_timing(0)
     stats1 = all_stats()
 
     K = args.steps
     layer_steps = L * K
     value = layer_steps / elapsed
+
+    def union_s(spans_per_handle, khz):
+        """Total length (s) of the union of [start, end) spans in ticks."""
+        iv = sorted((int(a), int(b)) for sp in spans_per_handle for a, b in sp if b > a)
+        tot, cur = 0, None
+        for a, b in iv:
+            if cur is None or a > cur[1]:
+                if cur:
+                    tot += cur[1] - cur[0]
+                cur = [a, b]
+            else:
+                cur[1] = max(cur[1], b)
+        if cur:
+            tot += cur[1] - cur[0]
+        return tot / (khz * 1e3)
 
     def deltas(s0, s1):
         return {f: sum(getattr(b, f) - getattr(a, f) for a, b in zip(s0, s1))
@@ -646,6 +669,9 @@ def main() -> int:
             roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": None, "traffic": None, "kernel": dominant, "avg_ms": round(ms / n, 5)}
 
+    copy_union_s = None
+    if span_list and span_khz and sum(len(sp) for sp in span_list) == layer_steps * nmb:
+        copy_union_s = union_s(span_list, span_khz) or None
     if roof is not None and roof.get("bound") == "host-link" and elapsed > 0:
         # with micro-batches the copy launches of the handles overlap and
         # share the link, so a launch's own rate is a share of it; the link's
@@ -675,8 +701,21 @@ def main() -> int:
                    **({"note": split_note} if split_note else {})},
         "tokens_per_s": round(B * K / elapsed, 2),
         "indexer_scan_GBps": rooflines.get("score_hist", {}).get("achieved"),
-        "miss_gather_GBps": next((e["achieved"] for e in [roof or {}] + list(rooflines.values())
-                                  if e.get("bound") == "host-link"), None),
+        # the miss gather's host-link rate: copied bytes over the time during
+        # which any copy block runs (the union of every handle's copy spans;
+        # with one handle, the copy blocks' own time), when every timed launch
+        # was recorded; else the per-launch rate of the roofline
+        "miss_gather_GBps": (round(d["h2d_bytes"] / copy_union_s / 1e9, 2) if copy_union_s else
+                             next((e["achieved"] for e in [roof or {}] + list(rooflines.values())
+                                   if e.get("bound") == "host-link"), None)),
+        "miss_gather": ({"GBps": round(d["h2d_bytes"] / copy_union_s / 1e9, 2),
+                         "frac_of_measured": round(d["h2d_bytes"] / copy_union_s / 1e9 / h2d_ceiling, 4),
+                         "copy_busy_us_per_layer_step": round(copy_union_s / layer_steps * 1e6, 2),
+                         "copy_busy_frac_of_wall": round(copy_union_s / elapsed, 4),
+                         "launches": int(sum(len(sp) for sp in span_list)),
+                         "definition": "copied bytes / union of all handles' copy spans (first copy block start "
+                                       "to last copy block end of each LRU-update launch, device clock)"}
+                        if copy_union_s else None),
         "miss_copy": copy_mode(calib) if calib else None,
         "h2d_ceiling_GBps": round(h2d_ceiling, 2),
         # a streaming kernel reading contiguous pinned host memory

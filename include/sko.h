@@ -383,6 +383,20 @@ int sko_get_timing(sko_handle* h, double* total_ms, int64_t* launches, int32_t n
  */
 int sko_get_copy_overlap(sko_handle* h, double* copy_ms, double* merge_ms, double* overlap_ms,
                          int64_t* launches);
+
+/*
+ * sko_get_copy_spans — the copy span of every launch recorded as for
+ * sko_get_copy_overlap (the first copy block's start and the last copy
+ * block's end, in ticks of the device's constant-rate clock, which all
+ * handles on the device share), in recording order: spans[2 i], spans[2 i +
+ * 1] for launch i.  With two or more handles whose steps overlap (the two
+ * micro-batches of SKO_FLAG_XCD_SPLIT), the union of all handles' spans is
+ * the time during which any miss row is being copied over the host link.
+ * Writes at most max_spans pairs; *n_spans receives the number recorded
+ * (which may be larger), *clock_khz the clock's rate.  Synchronizes.
+ * SKO_E_INVAL for NULL outputs or max_spans < 0.
+ */
+int sko_get_copy_spans(sko_handle* h, uint64_t* spans, int32_t max_spans, int32_t* n_spans, double* clock_khz);
 const char* sko_stage_name(int32_t stage);
 int32_t sko_num_stages(void);
 

@@ -55,7 +55,7 @@ EXPORTED = (
     "sko_decode_step_append",
     "sko_read_step",
     "sko_read_table", "sko_get_stats", "sko_set_timing", "sko_get_timing", "sko_get_copy_overlap",
-    "sko_stage_name",
+    "sko_get_copy_spans", "sko_stage_name",
     "sko_num_stages", "sko_destroy", "sko_last_error", "sko_version", "sko_link_read_rate", "sko_hbm_gather_rate",
     "sko_hbm_read_rate",
     # layerwise prefill offload (include/sko_prefill.h)
@@ -133,6 +133,7 @@ def _load() -> ctypes.CDLL:
                                           ctypes.POINTER(ctypes.c_int64), i32]),
         "sko_get_copy_overlap": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
+        "sko_get_copy_spans": (ctypes.c_int, [vp, vp, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]),
         "sko_stage_name": (ctypes.c_char_p, [i32]),
         "sko_num_stages": (i32, []),
         "sko_destroy": (None, [vp]),
@@ -317,6 +318,16 @@ def sko_get_copy_overlap(h: int) -> dict:
     return {"copy_ms": c.value, "merge_ms": m.value, "overlap_ms": o.value, "launches": n.value}
 
 
+def sko_get_copy_spans(h: int) -> tuple:
+    """(spans [n][2] uint64 device-clock ticks, clock_khz) of the recorded
+    LRU-update launches' copy spans."""
+    n, khz = ctypes.c_int32(), ctypes.c_double()
+    _check(_lib.sko_get_copy_spans(h, None, 0, ctypes.byref(n), ctypes.byref(khz)), "sko_get_copy_spans")
+    a = np.zeros((max(n.value, 1), 2), dtype=np.uint64)
+    _check(_lib.sko_get_copy_spans(h, _addr(a), n.value, ctypes.byref(n), ctypes.byref(khz)), "sko_get_copy_spans")
+    return a[:n.value].copy(), khz.value
+
+
 def sko_destroy(h: int) -> None:
     if h:
         _lib.sko_destroy(h)
@@ -409,6 +420,9 @@ class SparseKVOffload:
 
     def copy_overlap(self) -> dict:
         return sko_get_copy_overlap(self.handle)
+
+    def copy_spans(self):
+        return sko_get_copy_spans(self.handle)
 
 
 __all__ = [n for n in globals() if n.startswith(("sko_", "SKO_", "Sko"))] + [

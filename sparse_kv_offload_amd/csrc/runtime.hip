@@ -189,6 +189,9 @@ struct sko_handle {
     double clock_khz = 100000.0;  // device wall clock (s_memrealtime)
     double ovl_copy_ms = 0.0, ovl_merge_ms = 0.0, ovl_both_ms = 0.0;
     int64_t ovl_launches = 0;
+    // the copy span (first copy block's start, last copy block's end) of each
+    // recorded launch, on the device clock, in recording order
+    std::vector<uint64_t> copy_spans;
 
     std::vector<void*> dev_allocs;
 
@@ -310,6 +313,8 @@ int collect_stamps(sko_handle* h) {
         const uint64_t lo = std::max(m0, c0), hi = std::min(m1, c1);
         h->ovl_both_ms += hi > lo ? (double)(hi - lo) * tick_ms : 0.0;
         h->ovl_launches += 1;
+        h->copy_spans.push_back(c0);
+        h->copy_spans.push_back(c1);
     }
     h->stamp_pending.clear();
     return SKO_OK;
@@ -1227,6 +1232,7 @@ int sko_set_timing(sko_handle* h, uint32_t stage_mask) {
     h->stamp_pending.clear();
     h->ovl_copy_ms = h->ovl_merge_ms = h->ovl_both_ms = 0.0;
     h->ovl_launches = 0;
+    h->copy_spans.clear();
     h->timing_mask = stage_mask;
     return SKO_OK;
 }
@@ -1269,6 +1275,23 @@ int sko_get_copy_overlap(sko_handle* h, double* copy_ms, double* merge_ms, doubl
     *merge_ms = h->ovl_merge_ms;
     *overlap_ms = h->ovl_both_ms;
     *launches = h->ovl_launches;
+    return SKO_OK;
+}
+
+int sko_get_copy_spans(sko_handle* h, uint64_t* spans, int32_t max_spans, int32_t* n_spans, double* clock_khz) {
+    int rc = check_handle(h);
+    if (rc != SKO_OK) return rc;
+    if (!n_spans || !clock_khz || max_spans < 0 || (max_spans > 0 && !spans))
+        return set_err(SKO_E_INVAL, "bad copy-span output");
+    DeviceGuard guard(h->cfg.device);
+    const hipError_t e = hipStreamSynchronize(h->stream);
+    if (e != hipSuccess) return device_fail(h, e, "copy-span sync");
+    if ((rc = collect_stamps(h)) != SKO_OK) return rc;
+    const int32_t n = (int32_t)(h->copy_spans.size() / 2);
+    const int32_t m = std::min(n, max_spans);
+    if (m > 0) std::memcpy(spans, h->copy_spans.data(), (size_t)m * 2 * sizeof(uint64_t));
+    *n_spans = n;
+    *clock_khz = h->clock_khz;
     return SKO_OK;
 }
 

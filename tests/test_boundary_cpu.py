@@ -92,6 +92,8 @@ def test_calls_on_null_handle_fail_cleanly():
     assert lib.sko_read_step(None, 1, buf.ctypes.data, buf.nbytes) == sko.SKO_E_INVAL
     assert lib.sko_read_table(None, 0, 0, 1, buf.ctypes.data, buf.nbytes) == sko.SKO_E_INVAL
     assert lib.sko_set_timing(None, 1) == sko.SKO_E_INVAL
+    n32, khz = ctypes.c_int32(), ctypes.c_double()
+    assert lib.sko_get_copy_spans(None, None, 0, ctypes.byref(n32), ctypes.byref(khz)) == sko.SKO_E_INVAL
     d = ctypes.c_double()
     n = ctypes.c_int64()
     assert lib.sko_get_copy_overlap(None, ctypes.byref(d), ctypes.byref(d), ctypes.byref(d),
