@@ -169,10 +169,17 @@ def test_timing_counts_one_launch_per_layer_step():
         assert ov["launches"] == layer_steps
         assert ov["copy_ms"] > 0.0 and ov["merge_ms"] > 0.0
         assert 0.0 <= ov["overlap_ms"] <= min(ov["copy_ms"], ov["merge_ms"]) + 1e-9
+        # the same launches' copy spans, one per launch, on the device clock:
+        # ordered within each span, and summing to the copy time above
+        spans, khz = h.copy_spans()
+        assert spans.shape == (layer_steps, 2) and khz > 0
+        assert (spans[:, 1] > spans[:, 0]).all()
+        assert abs(float((spans[:, 1] - spans[:, 0]).sum()) / khz - ov["copy_ms"]) <= 1e-6 * ov["copy_ms"] + 1e-9
         # clearing the mask clears the totals
         h.set_timing(0)
         assert all(c == 0 for _, c in h.timing().values())
         assert h.copy_overlap()["launches"] == 0
+        assert h.copy_spans()[0].shape == (0, 2)
         assert [h.stats(l).steps for l in range(w.layers)] == [n] * w.layers
 
 
