@@ -762,7 +762,10 @@ def main() -> int:
         "rooflines": rooflines,
         "stage_ms_per_launch": {n: round(ms / c, 5) for n, (ms, c) in calib.items() if c},
         "stage_timing_note": (f"stage breakdown from warm-up steps 1..{args.warmup - 1} with every stage "
-                              f"event-timed; the timed steps bracket only '{dominant}'")
+                              f"event-timed" + (f", the {nmb} handles' steps overlapping as in the timed steps (a "
+                                                f"stage's time includes waiting behind the other handle's kernels)"
+                                                if nmb > 1 else "") +
+                              f"; the timed steps bracket only '{dominant}'")
         if calib else None,
     }
     for h in hs:
