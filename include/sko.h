@@ -393,7 +393,8 @@ int sko_get_copy_overlap(sko_handle* h, double* copy_ms, double* merge_ms, doubl
  * micro-batches of SKO_FLAG_XCD_SPLIT), the union of all handles' spans is
  * the time during which any miss row is being copied over the host link.
  * Writes at most max_spans pairs; *n_spans receives the number recorded
- * (which may be larger), *clock_khz the clock's rate.  Synchronizes.
+ * (which may be larger; at most 65 536 are kept between two
+ * sko_set_timing calls), *clock_khz the clock's rate.  Synchronizes.
  * SKO_E_INVAL for NULL outputs or max_spans < 0.
  */
 int sko_get_copy_spans(sko_handle* h, uint64_t* spans, int32_t max_spans, int32_t* n_spans, double* clock_khz);

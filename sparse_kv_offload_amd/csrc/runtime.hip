@@ -26,6 +26,7 @@ using namespace sko;
 namespace {
 
 constexpr int64_t kStagingRows = 65536;  // indexer rows per host-append piece
+constexpr int kMaxCopySpans = 1 << 16;  // copy spans kept between two sko_set_timing calls
 constexpr int kStampLaunches = 1024;     // timed LRU-update launches recorded between reads
 
 thread_local std::string g_err;
@@ -313,8 +314,10 @@ int collect_stamps(sko_handle* h) {
         const uint64_t lo = std::max(m0, c0), hi = std::min(m1, c1);
         h->ovl_both_ms += hi > lo ? (double)(hi - lo) * tick_ms : 0.0;
         h->ovl_launches += 1;
-        h->copy_spans.push_back(c0);
-        h->copy_spans.push_back(c1);
+        if (h->copy_spans.size() < 2 * (size_t)kMaxCopySpans) {
+            h->copy_spans.push_back(c0);
+            h->copy_spans.push_back(c1);
+        }
     }
     h->stamp_pending.clear();
     return SKO_OK;
