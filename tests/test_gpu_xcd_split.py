@@ -67,6 +67,18 @@ def test_split_one_handle(shape, fused_append):
     log(f"worst {worst}")
 
 
+@pytest.mark.parametrize("extra", ["c8", "rescan"])
+def test_split_one_handle_int8_and_rescan(extra):
+    """The split with the int8 indexer (its codes and scales bit-exact) and
+    with every row selected through the filter's rescan path."""
+    import sparse_kv_offload_amd as sko
+    w = case(f"xcd_{extra}", batch=3, context=9000, steps=5, top_k=256, hot_slots=1100, positions=4, heads=16)
+    f = sko.SKO_FLAG_XCD_SPLIT | {"c8": sko.SKO_FLAG_INDEXER_C8, "rescan": sko.SKO_FLAG_SELECT_RESCAN}[extra]
+    log(f"case xcd split + {extra}: {w}")
+    worst = run_parity(w, check_keys=True, flags=f, fused_append=True, log=log)
+    log(f"worst {worst}")
+
+
 @pytest.mark.parametrize("shape,nmb", [("d1", 2), ("d4", 2), ("ragged_d2", 3)])
 def test_micro_batches_each_layer(shape, nmb):
     """nmb handles on nmb streams, every layer's calls of all handles queued
