@@ -8,7 +8,7 @@ bit-exactly; attention within 2e-2 absolute and 1e-2 relative RMS).  The
 split changes only where blocks run: the copy blocks on one XCD, every other
 block on the other seven.  The grids cover a launch smaller than one group of
 eight blocks, launches that are not multiples of seven work blocks, several
-score blocks per sequence, head groups, up to five positions, a ragged batch
+score blocks per sequence, head groups, up to 17 positions, a ragged batch
 with an empty sequence, and the full shelf_ctx8, small, mtp3 and long shapes
 in the benchmark's micro-batch configuration (two handles).
 """
@@ -79,7 +79,21 @@ def test_split_one_handle_int8_and_rescan(extra):
     log(f"worst {worst}")
 
 
-@pytest.mark.parametrize("shape,nmb", [("d1", 2), ("d4", 2), ("ragged_d2", 3)])
+@pytest.mark.parametrize("positions", [16, 17])
+def test_split_many_positions(positions):
+    """The split with four and five score launches per step (16 and 17
+    positions, four positions per launch) and the LRU update over D * k
+    entries: 16 is the largest count whose lists the LRU update puts in
+    token order, with 17 the lists keep the selection's order."""
+    import sparse_kv_offload_amd as sko
+    w = case(f"xcd_d{positions}", batch=3, context=1500, steps=6, top_k=24, hot_slots=positions * 24 + 40,
+             positions=positions, heads=4)
+    log(f"case xcd split d{positions}: {w}")
+    worst = run_parity(w, check_keys=True, flags=sko.SKO_FLAG_XCD_SPLIT, fused_append=True, log=log)
+    log(f"worst {worst}")
+
+
+@pytest.mark.parametrize("shape,nmb", [("d1", 2), ("d4", 2), ("ragged_d2", 3), ("d5", 2)])
 def test_micro_batches_each_layer(shape, nmb):
     """nmb handles on nmb streams, every layer's calls of all handles queued
     before one wait: each handle's results against the oracle at every step."""
@@ -89,6 +103,8 @@ def test_micro_batches_each_layer(shape, nmb):
                    heads=16),
         "ragged_d2": dict(batch=5, contexts=(2000, 0, 4100, 63, 64), context=4100, steps=6, top_k=64,
                           hot_slots=200, positions=2, heads=20),
+        # two score launches per step in each handle
+        "d5": dict(batch=4, context=6000, steps=6, top_k=128, hot_slots=900, positions=5, heads=16),
     }
     w = case(f"micro_{shape}", **shapes[shape])
     log(f"case micro-batches {nmb} {shape}: {w}")
